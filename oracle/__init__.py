@@ -1,0 +1,29 @@
+"""CPU oracle for the batched, rank-specialized LoRA-delta apply.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports, calls or
+links anything in this package: only the test suite, the smoke check and the
+benchmark's CPU-baseline leg do.  It shares no code with the HIP library.
+
+Every function is a plain, slow, obviously-correct restatement of what the
+sources define (float64 unless stated, Python loops over tokens):
+
+* ``segment_ref``  - stable grouping of tokens by adapter id
+* ``shrink_ref``   - h = A_a x per token
+* ``apply_ref``    - y = y0 + s_a B_a (A_a x) per token
+* ``brute_force``  - the same in exact rational arithmetic, two association
+                     orders, for tiny inputs
+* ``bf16_round_ref`` - round-to-nearest-even onto bfloat16, used where a
+                     floating-point result is compared bit for bit
+
+Parity status: every function here is pinned by tests in
+``tests/test_oracle.py`` (closed forms, invariants, brute force, library
+routines, a hand-worked example); none is "parity unpinned".
+"""
+from .lora_ref import (  # noqa: F401
+    apply_ref,
+    bf16_round_ref,
+    brute_force,
+    segment_ref,
+    shrink_ref,
+    shrink_error_bound,
+)

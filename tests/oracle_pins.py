@@ -1,0 +1,211 @@
+"""Pins for the CPU oracle: checks against what the sources and the
+mathematics fix, independent of the oracle's own code.
+
+Each check takes the function under test as an argument so that the same
+checks can be run on deliberately broken copies of the oracle
+(tests/test_oracle_mutations.py) to show that they catch plausible mistakes.
+Each check raises AssertionError on failure.
+"""
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+from workloads import make_config, make_random_workload
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def load_worked_example():
+    with open(os.path.join(GOLDEN, "worked_example.json")) as f:
+        ex = json.load(f)
+    A = [np.array(a, dtype=np.float32).reshape(r, ex["d_in"]) for a, r in zip(ex["A"], ex["ranks"])]
+    B = [np.array(b, dtype=np.float32).reshape(ex["d_out"], r) for b, r in zip(ex["B"], ex["ranks"])]
+    return ex, A, B
+
+
+# ---------------------------------------------------------------- apply pins
+
+def pin_worked_example(apply_fn):
+    """Hand-worked example from the LoRA definition (tests/golden)."""
+    ex, A, B = load_worked_example()
+    y = apply_fn(np.array(ex["x"], np.float32), np.array(ex["ids"], np.int32), A, B,
+                 np.array(ex["scales"], np.float32), np.array(ex["y0"], np.float32))
+    assert np.array_equal(np.asarray(y, np.float64), np.array(ex["expected_y"], np.float64)), y
+
+
+def pin_merged_weight(apply_fn, wl=None, seed=0):
+    """With y0 = 0 the delta equals x (W + s B A)^T - x W^T for any W
+    (merged form W0 -> W0 + B_i A_i versus the separate branch, Compress then
+    Serve section 11).  The merged form is built with dense numpy products."""
+    wl = wl or make_config("1")
+    m = wl.module
+    rng = np.random.default_rng(seed)
+    W = rng.normal(size=(m.d_out, m.d_in))
+    x = wl.x.astype(np.float64)
+    ref = np.zeros((wl.T, m.d_out))
+    for t in range(wl.T):
+        a = int(wl.ids[t])
+        if not 0 <= a < m.n:
+            continue
+        merged = W + float(m.scales[a]) * (m.B[a].astype(np.float64) @ m.A[a].astype(np.float64))
+        ref[t] = merged @ x[t] - W @ x[t]
+    y = np.asarray(apply_fn(wl.x, wl.ids, m.A, m.B, m.scales), np.float64)
+    scale = max(np.abs(ref).max(), 1e-300)
+    assert np.abs(y - ref).max() <= 1e-10 * scale, np.abs(y - ref).max() / scale
+
+
+def pin_rank_zero(apply_fn):
+    """An adapter with retained rank 0 contributes an exactly zero delta."""
+    wl = make_random_workload(1, 24, 3, 16, 8, [0, 2, 0], dtype="fp32")
+    m = wl.module
+    y = np.asarray(apply_fn(wl.x, wl.ids, m.A, m.B, m.scales), np.float64)
+    for t in range(wl.T):
+        if m.ranks[wl.ids[t]] == 0:
+            assert np.all(y[t] == 0.0), (t, y[t])
+    assert np.any(y != 0.0)
+
+
+def pin_scale_linearity(apply_fn):
+    """The delta is linear in s: doubling s doubles it exactly; s1 + s2 adds."""
+    wl = make_random_workload(2, 20, 4, 32, 24, [1, 3, 5, 2], dtype="bf16")
+    m = wl.module
+    y1 = np.asarray(apply_fn(wl.x, wl.ids, m.A, m.B, m.scales), np.float64)
+    y2 = np.asarray(apply_fn(wl.x, wl.ids, m.A, m.B, m.scales * 2), np.float64)
+    assert np.array_equal(y2, 2 * y1)
+    s2 = np.full(m.n, 0.375, np.float32)
+    y3 = np.asarray(apply_fn(wl.x, wl.ids, m.A, m.B, s2), np.float64)
+    y4 = np.asarray(apply_fn(wl.x, wl.ids, m.A, m.B, m.scales + s2), np.float64)
+    assert np.abs(y4 - (y1 + y3)).max() <= 1e-12 * max(np.abs(y4).max(), 1e-300)
+
+
+def pin_zero_padding(apply_fn):
+    """Appending zero rows to A_a and zero columns to B_a (any larger rank)
+    leaves the result unchanged: padding is neutral, only wasteful."""
+    wl = make_random_workload(3, 30, 5, 40, 24, [1, 2, 3, 4, 7], dtype="bf16")
+    m = wl.module
+    rng = np.random.default_rng(3)
+    Ap, Bp = [], []
+    for a in range(m.n):
+        r = int(m.ranks[a]) + int(rng.integers(1, 9))
+        A = np.zeros((r, m.d_in), np.float32)
+        B = np.zeros((m.d_out, r), np.float32)
+        A[: m.ranks[a]] = m.A[a]
+        B[:, : m.ranks[a]] = m.B[a]
+        Ap.append(A)
+        Bp.append(B)
+    y = np.asarray(apply_fn(wl.x, wl.ids, m.A, m.B, m.scales), np.float64)
+    yp = np.asarray(apply_fn(wl.x, wl.ids, Ap, Bp, m.scales), np.float64)
+    assert np.abs(y - yp).max() <= 1e-13 * max(np.abs(y).max(), 1e-300)
+
+
+def pin_brute_force(apply_fn, brute_fn):
+    """Exact rational triple loops on tiny inputs, both association orders."""
+    for seed, (T, n, di, do, ranks) in enumerate([(5, 2, 3, 4, [1, 2]), (7, 3, 4, 3, [2, 0, 3])]):
+        wl = make_random_workload(10 + seed, T, n, di, do, ranks, dtype="bf16", y0=True,
+                                  invalid_frac=0.2)
+        m = wl.module
+        exact = brute_fn(wl.x, wl.ids, m.A, m.B, m.scales, wl.y0, form="B(Ax)")
+        merged = brute_fn(wl.x, wl.ids, m.A, m.B, m.scales, wl.y0, form="(BA)x")
+        assert exact == merged
+        y = np.asarray(apply_fn(wl.x, wl.ids, m.A, m.B, m.scales, wl.y0), np.float64)
+        ref = np.array([[float(v) for v in row] for row in exact])
+        assert np.abs(y - ref).max() <= 1e-13 * max(np.abs(ref).max(), 1.0)
+
+
+def pin_integer_exact(apply_fn, brute_fn):
+    """Integer inputs and power-of-two scales: the float64 result is exact."""
+    wl = make_random_workload(20, 9, 3, 6, 5, [2, 3, 1], dtype="fp32", integer=True,
+                              scales=[0.5, 2.0, 1.0])
+    m = wl.module
+    exact = brute_fn(wl.x, wl.ids, m.A, m.B, m.scales)
+    y = np.asarray(apply_fn(wl.x, wl.ids, m.A, m.B, m.scales), np.float64)
+    assert all(Fraction(float(y[t, o])) == exact[t][o] for t in range(wl.T) for o in range(m.d_out))
+
+
+def pin_token_permutation(apply_fn):
+    """Tokens are independent: permuting tokens permutes outputs exactly."""
+    wl = make_random_workload(4, 33, 4, 24, 16, [3, 1, 4, 2], dtype="bf16", y0=True,
+                              invalid_frac=0.1)
+    m = wl.module
+    p = np.random.default_rng(4).permutation(wl.T)
+    y = np.asarray(apply_fn(wl.x, wl.ids, m.A, m.B, m.scales, wl.y0), np.float64)
+    yp = np.asarray(apply_fn(wl.x[p], wl.ids[p], m.A, m.B, m.scales, wl.y0[p]), np.float64)
+    assert np.array_equal(yp, y[p])
+
+
+def pin_per_segment(apply_fn):
+    """Per adapter group: delta = s_a (X_seg A_a^T) B_a^T with numpy products
+    (the stacked-bmm form of Compress then Serve section 11)."""
+    wl = make_random_workload(5, 64, 6, 48, 40, [1, 2, 4, 8, 3, 5], dtype="bf16", id_mode="zipf")
+    m = wl.module
+    y = np.asarray(apply_fn(wl.x, wl.ids, m.A, m.B, m.scales), np.float64)
+    for a in range(m.n):
+        rows = np.nonzero(wl.ids == a)[0]
+        if len(rows) == 0:
+            continue
+        X = wl.x[rows].astype(np.float64)
+        d = float(m.scales[a]) * ((X @ m.A[a].astype(np.float64).T) @ m.B[a].astype(np.float64).T)
+        assert np.abs(y[rows] - d).max() <= 1e-12 * max(np.abs(d).max(), 1e-300)
+
+
+def pin_no_adapter_tokens(apply_fn):
+    """Tokens with id -1 keep y0 exactly."""
+    wl = make_random_workload(6, 40, 3, 16, 16, [2, 2, 2], dtype="bf16", y0=True, invalid_frac=0.4)
+    m = wl.module
+    y = np.asarray(apply_fn(wl.x, wl.ids, m.A, m.B, m.scales, wl.y0), np.float64)
+    mask = wl.ids < 0
+    assert mask.any()
+    assert np.array_equal(y[mask], wl.y0[mask].astype(np.float64))
+    assert not np.array_equal(y[~mask], wl.y0[~mask].astype(np.float64))
+
+
+APPLY_PINS = (pin_worked_example, pin_merged_weight, pin_rank_zero, pin_scale_linearity,
+              pin_zero_padding, pin_token_permutation, pin_per_segment, pin_no_adapter_tokens)
+
+
+# -------------------------------------------------------------- segment pins
+
+def pin_segment_worked_example(segment_fn):
+    ex, _, _ = load_worked_example()
+    seg_off, perm, n_inv = segment_fn(ex["ids"], ex["n"])
+    assert list(seg_off) == ex["expected_seg_off"], seg_off
+    assert list(perm) == ex["expected_perm"], perm
+    assert n_inv == 0
+
+
+def pin_segment_vs_stable_argsort(segment_fn):
+    """perm equals numpy's stable argsort of ids (out-of-range ids mapped to
+    n); seg_off equals the cumulative bincount."""
+    rng = np.random.default_rng(7)
+    for T, n in [(0, 3), (1, 1), (17, 4), (200, 16), (513, 300), (64, 1)]:
+        ids = rng.integers(-1, n, size=T).astype(np.int32)
+        if T > 3:
+            ids[rng.integers(0, T, size=2)] = [n + 5, -7]
+        key = np.where((ids >= 0) & (ids < n), ids, n)
+        seg_off, perm, n_inv = segment_fn(ids, n)
+        assert list(perm) == list(np.argsort(key, kind="stable"))
+        exp_off = np.concatenate([[0], np.cumsum(np.bincount(key, minlength=n + 1))])
+        assert list(seg_off) == list(exp_off)
+        assert n_inv == int(np.sum((ids != -1) & ((ids < 0) | (ids >= n))))
+
+
+def pin_segment_invariants(segment_fn):
+    """perm is a permutation, ids[perm] is non-decreasing, positions increase
+    inside each group, empty groups have zero length."""
+    ids = np.array([3, 3, 0, 5, 3, 0, 0, 5, 5, 5], np.int32)
+    seg_off, perm, _ = segment_fn(ids, 7)
+    assert sorted(perm) == list(range(len(ids)))
+    g = ids[np.array(perm)]
+    assert np.all(np.diff(g) >= 0)
+    for a in range(7):
+        members = perm[seg_off[a]:seg_off[a + 1]]
+        assert list(members) == sorted(members)
+        assert all(ids[t] == a for t in members)
+    assert seg_off[1] - seg_off[0] == 3 and seg_off[2] == seg_off[1] and seg_off[-1] == len(ids)
+
+
+SEGMENT_PINS = (pin_segment_worked_example, pin_segment_vs_stable_argsort, pin_segment_invariants)

@@ -1,0 +1,103 @@
+"""Plant plausible mistakes in copies of the oracle (CPU only) and check
+that the pins catch every one of them."""
+import numpy as np
+import pytest
+
+from oracle import apply_ref, segment_ref
+
+import oracle_pins as P
+
+
+def _apply_mutant(kind):
+    def fn(x, ids, A_list, B_list, scales, y0=None):
+        x64 = np.asarray(x, np.float64)
+        T = x64.shape[0]
+        n = len(A_list)
+        d_out = np.asarray(B_list[0]).shape[0]
+        y = np.zeros((T, d_out)) if y0 is None else np.asarray(y0, np.float64).copy()
+        if kind == "drop_y0" and y0 is not None:
+            y = np.zeros_like(y)
+        for t in range(T):
+            a = int(ids[t])
+            if not 0 <= a < n:
+                if kind == "invalid_uses_adapter0":
+                    a = 0
+                else:
+                    continue
+            if kind == "off_by_one_adapter":
+                a = (a + 1) % n
+            A = np.asarray(A_list[a], np.float64)
+            B = np.asarray(B_list[a], np.float64)
+            s = float(scales[a])
+            if kind == "drop_scale":
+                s = 1.0
+            if kind == "neg_sign":
+                s = -s
+            if kind == "transpose_B" and B.shape[0] == B.shape[1]:
+                B = B.T
+            if kind == "truncate_rank" and A.shape[0] > 1:
+                A, B = A[:-1], B[:, :-1]
+            if kind == "scale_squared":
+                s = s * s
+            h = A @ x64[t]
+            if kind == "relu_h":
+                h = np.maximum(h, 0)
+            y[t] += s * (B @ h)
+        return y
+    return fn
+
+
+APPLY_MUTANTS = ["drop_y0", "invalid_uses_adapter0", "off_by_one_adapter", "drop_scale", "neg_sign",
+                 "transpose_B", "truncate_rank", "scale_squared", "relu_h"]
+
+
+@pytest.mark.parametrize("kind", APPLY_MUTANTS)
+def test_apply_mutant_is_caught(kind):
+    fn = _apply_mutant(kind)
+    caught = []
+    for pin in P.APPLY_PINS:
+        try:
+            pin(fn)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"mutant {kind} passed every pin"
+
+
+def test_unmutated_copy_passes():
+    fn = _apply_mutant("none")
+    for pin in P.APPLY_PINS:
+        pin(fn)
+
+
+def _segment_mutant(kind):
+    def fn(ids, n):
+        seg_off, perm, n_inv = segment_ref(ids, n)
+        perm = list(perm)
+        seg_off = list(seg_off)
+        if kind == "unstable" and len(perm) > 1:
+            # reverse the order inside each group
+            for g in range(n + 1):
+                perm[seg_off[g]:seg_off[g + 1]] = perm[seg_off[g]:seg_off[g + 1]][::-1]
+        elif kind == "invalid_first":
+            key = [n if not 0 <= int(v) < n else int(v) for v in ids]
+            order = sorted(range(len(ids)), key=lambda t: (-1 if key[t] == n else key[t], t))
+            perm = order
+        elif kind == "inclusive_offsets":
+            seg_off = seg_off[1:] + [seg_off[-1]]
+        elif kind == "count_minus_one_as_invalid":
+            n_inv = sum(1 for v in ids if not 0 <= int(v) < n)
+        return seg_off, perm, n_inv
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["unstable", "invalid_first", "inclusive_offsets",
+                                  "count_minus_one_as_invalid"])
+def test_segment_mutant_is_caught(kind):
+    fn = _segment_mutant(kind)
+    caught = []
+    for pin in P.SEGMENT_PINS:
+        try:
+            pin(fn)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"segment mutant {kind} passed every pin"
