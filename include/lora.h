@@ -1,0 +1,240 @@
+/*
+ * lora.h - C ABI of the batched, rank-specialized LoRA-delta apply on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  A batch of T tokens x[t] (rows of d_in values) each names
+ * an adapter a = ids[t]; every adapter keeps its own retained rank r_a.  The
+ * library adds the LoRA branch of each token's adapter into the output:
+ *
+ *     y[t] += s_a * B_a (A_a x[t])        A_a: r_a x d_in,  B_a: d_out x r_a
+ *
+ * Sources:
+ *  - "Compress then Serve: Serving Thousands of LoRA Adapters with Little
+ *    Overhead" (arXiv 2407.00066): section 3 defines the LoRA-updated layer
+ *    (W0 + B A) x with B of shape d_B x r and A of shape r x d_A; section 11
+ *    computes W0 x once and adds the per-request branch B_i A_i x; section 2
+ *    describes grouping the requests that use the same adapter (segmented
+ *    gather); section 13.4 gives the two-step form used here: A applied with
+ *    scale 1 into a float32 buffer of shape [tokens, R], then B applied with
+ *    the scale and added into a slice (offset, width) of y.
+ *  - "LoRAForge: Co-Designing Compression and Execution for More Efficient
+ *    Multi-LoRA Serving", section "LoRAForge's Core Design: Explicit
+ *    Retained-Rank Representation and Dual Strategies": execution runs on
+ *    each adapter's retained factors at its own rank, without padding or
+ *    re-expansion; rank-specialized kernels are compiled for specific rank
+ *    values.  The abstract page of the same title names padding, factor
+ *    access and generic kernels as what hides the retained low rank.
+ *
+ * Conventions shared by every entry point.
+ *  - Pointers are DEVICE pointers unless the parameter name ends in _host.
+ *  - The caller owns every buffer.  The library never allocates or frees
+ *    device memory.  Only lora_pack_retained synchronizes (its stream, once,
+ *    at the end, so the host staging it used can be released).
+ *  - Every call enqueues work on `stream` (a hipStream_t; NULL = the null
+ *    stream) and returns; results are visible after the stream reaches that
+ *    point.  Calls are stateless; concurrent calls on different streams are
+ *    safe when their outputs (and workspaces) are disjoint.
+ *  - Return value: LORA_OK, or an error code.  On LORA_ERR_INVALID_ARG and
+ *    LORA_ERR_UNSUPPORTED nothing has been enqueued.  On LORA_ERR_HIP a HIP
+ *    call failed; lora_last_hip_error() returns its hipError_t (per thread).
+ *  - dtype: LORA_DTYPE_BF16 (x, factors and y are bfloat16) or
+ *    LORA_DTYPE_F32 (all float32).  Accumulation is float32 in both.
+ *  - Row strides (ldx, ldy, ldh) are in elements.  x and y rows must start on
+ *    16-byte boundaries: base pointers 16-byte aligned, strides a multiple of
+ *    8 elements (bf16) or 4 elements (f32).  d_in and d_out must be
+ *    multiples of 8 (bf16) or 4 (f32).  Violations: LORA_ERR_UNSUPPORTED.
+ *  - Aliasing: x, y, h and the workspaces must not overlap one another.
+ */
+#ifndef RANK_SPECIALIZED_LORA_H
+#define RANK_SPECIALIZED_LORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum lora_status {
+  LORA_OK = 0,
+  LORA_ERR_INVALID_ARG = 1, /* a null pointer, negative size, inconsistent sizes */
+  LORA_ERR_UNSUPPORTED = 2, /* valid, but outside the kernels' envelope */
+  LORA_ERR_HIP = 3          /* a HIP runtime call failed; see lora_last_hip_error */
+};
+
+enum lora_dtype { LORA_DTYPE_F32 = 0, LORA_DTYPE_BF16 = 1 };
+
+/* Largest retained (or padded) rank the kernels accept. */
+#define LORA_MAX_RANK 64
+/* Tokens per work tile (a run of one adapter's tokens in grouped order). */
+#define LORA_TILE_TOKENS 64
+/* Largest T and n that lora_segment accepts (single-workgroup sort). */
+#define LORA_SEGMENT_MAX_T 16384
+#define LORA_SEGMENT_MAX_N 16382
+
+/*
+ * The retained-rank store: every adapter's factors laid end to end at its
+ * own rank (pad_to = 0), or every adapter padded with zero rows to pad_to
+ * (the rank-padded comparison variant, the stacked [b, r, n] / [b, m, r]
+ * layout of "Compress then Serve" section 11).
+ *
+ *   A_pack  [R, d_in]   row row_off[a] + j = row j of A_a
+ *   Bt_pack [R, d_out]  row row_off[a] + j = column j of B_a
+ *   row_off [n + 1]     int32, exclusive scan of the stored ranks
+ *   rank    [n]         int32, stored rank of each adapter (r_a, or pad_to)
+ *   scale   [n]         float32, s_a
+ *
+ * A plain struct filled by lora_pack_retained.  Its device pointers point
+ * into the caller's buffers; its lifetime is the caller's.
+ */
+typedef struct lora_store {
+  int32_t n;           /* adapters */
+  int32_t d_in;        /* input features */
+  int32_t d_out;       /* output features */
+  int32_t dtype;       /* enum lora_dtype */
+  int32_t r_max;       /* largest stored rank */
+  int32_t R;           /* total stored rows = row_off[n] */
+  int32_t pad_to;      /* 0 = rank-specialized; otherwise every rank padded to this */
+  int32_t reserved;
+  const void* A_pack;
+  const void* Bt_pack;
+  const int32_t* row_off;
+  const int32_t* rank;
+  const float* scale;
+} lora_store;
+
+/* Human-readable name of a status code (static string). */
+const char* lora_status_string(int status);
+
+/* hipError_t of the last failed HIP call on this thread (0 if none). */
+int lora_last_hip_error(void);
+
+/* ABI version; bumps on any incompatible change of this header. */
+int lora_abi_version(void);
+
+/*
+ * Size query for a store (host only, nothing enqueued).
+ *   n, d_in, d_out, dtype : as in lora_store.
+ *   ranks_host [n]        : retained rank of each adapter, 0 <= r_a.
+ *   pad_to                : 0 for the rank-specialized store; otherwise every
+ *                           adapter is stored with pad_to rows (pad_to >= max r_a).
+ * Out (host): bytes needed for A_pack, Bt_pack and meta.
+ * Errors: INVALID_ARG (null outputs, n < 0, d <= 0, r_a < 0, pad_to below a
+ * rank, total rows overflowing int32); UNSUPPORTED (stored rank above
+ * LORA_MAX_RANK, d not a multiple of 8 (bf16) / 4 (f32), unknown dtype).
+ */
+int lora_store_bytes(int n, int d_in, int d_out, int dtype, const int32_t* ranks_host, int pad_to,
+                     size_t* a_bytes_host, size_t* bt_bytes_host, size_t* meta_bytes_host);
+
+/*
+ * Pack retained factors into a store.
+ *   A_ptrs_host [n] : host array of device pointers; A_a is r_a x d_in,
+ *                     row-major (rows of d_in contiguous elements).
+ *   B_ptrs_host [n] : host array of device pointers; B_a is d_out x r_a,
+ *                     row-major.  Either pointer may be NULL when r_a = 0.
+ *   scales_host [n] : s_a.
+ *   A_pack, Bt_pack, meta : caller buffers of at least the sizes that
+ *                     lora_store_bytes returns, 16-byte aligned.
+ *   out_host        : filled on success (references A_pack, Bt_pack, meta).
+ * Copies the factors (bit-exact), writes zero rows where pad_to pads, and
+ * writes row_off / rank / scale into meta.  Synchronizes `stream` before
+ * returning.  Errors: as lora_store_bytes, plus INVALID_ARG for null buffers
+ * or a null factor pointer with r_a > 0.
+ */
+int lora_pack_retained(lora_store* out_host, int n, int d_in, int d_out, int dtype,
+                       const int32_t* ranks_host, const float* scales_host,
+                       const void* const* A_ptrs_host, const void* const* B_ptrs_host,
+                       void* A_pack, void* Bt_pack, void* meta, int pad_to, void* stream);
+
+/*
+ * Workspace of lora_segment / lora_segment_from_offsets: the tile plan that
+ * lora_shrink and lora_expand read (runs of at most LORA_TILE_TOKENS tokens
+ * of one adapter).  Host only.  Returns 0 for T < 0 or n < 0.
+ */
+size_t lora_segment_ws_bytes(int T, int n);
+
+/*
+ * Group tokens by adapter: a stable counting sort of ids.
+ *   ids [T]         : int32 adapter id per token.  -1 = no adapter; any other
+ *                     id outside [0, n) is treated as -1 and counted.
+ *   seg_off [n + 2] : out.  Adapter a's tokens occupy grouped positions
+ *                     seg_off[a] .. seg_off[a+1]-1; group n holds the tokens
+ *                     without an adapter; seg_off[n+1] = T.
+ *   perm [T]        : out.  perm[i] = original token index at grouped
+ *                     position i.  Adapters ascend; inside a group tokens
+ *                     keep ascending index (unique result).
+ *   n_invalid       : optional (NULL) device int32; receives the count of
+ *                     ids that are neither -1 nor in [0, n).
+ *   ws              : lora_segment_ws_bytes(T, n) bytes; receives the plan.
+ * T = 0 is a no-op apart from writing seg_off (all zero) and the plan.
+ * Errors: INVALID_ARG (null pointers, T < 0, n < 1, ws too small);
+ * UNSUPPORTED (T > LORA_SEGMENT_MAX_T or n > LORA_SEGMENT_MAX_N).
+ */
+int lora_segment(const int32_t* ids, int T, int n, int32_t* seg_off, int32_t* perm,
+                 int32_t* n_invalid, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Build the tile plan in ws from a caller-supplied grouping (seg_off as
+ * lora_segment writes it).  For callers that group tokens themselves, or
+ * reuse one grouping across many stores (every module of a layer stack).
+ */
+int lora_segment_from_offsets(const int32_t* seg_off, int T, int n, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/*
+ * Shrink (step 1 of "Compress then Serve" section 13.4):
+ *   h[i, j] = sum_k A_a[j, k] * x[perm[i], k]    for j < r_a, a = adapter of
+ *                                                grouped position i
+ *   x   [T, ldx] : dtype of the store, token order.
+ *   h   [T, ldh] : float32, GROUPED order (row i = grouped position i),
+ *                  ldh >= r_max.  Columns >= r_a and rows of tokens without an
+ *                  adapter are not written.  Products are accumulated in
+ *                  float32 (bf16 products are exact in float32).
+ *   seg_off, perm, seg_ws : from lora_segment (or lora_segment_from_offsets)
+ *                  for the same T and store->n.
+ * Errors: INVALID_ARG (null pointers, T < 0, ldx < d_in, ldh < r_max, ws too
+ * small); UNSUPPORTED (alignment, see conventions).
+ */
+int lora_shrink(const lora_store* store_host, const void* x, int64_t ldx, int T,
+                const int32_t* seg_off, const int32_t* perm, const void* seg_ws, size_t seg_ws_bytes,
+                float* h, int64_t ldh, void* stream);
+
+/*
+ * Expand (step 3 of "Compress then Serve" section 13.4):
+ *   y[perm[i], o] += s_a * sum_{j < r_a} B_a[o, j] * h[i, j]
+ * accumulated in float32 and rounded once to the output dtype (bf16: round
+ * to nearest, ties to even).  y [T, ldy] in token order, ldy >= d_out; y may
+ * be a column slice of a wider buffer (pass the slice's first column and the
+ * wider row stride) - the y_offset / y_slice_size of the same section.
+ * Rows of tokens without an adapter (and of adapters with r_a = 0) are left
+ * untouched.  Errors as lora_shrink.
+ */
+int lora_expand(const lora_store* store_host, const float* h, int64_t ldh, int T,
+                const int32_t* seg_off, const int32_t* perm, const void* seg_ws, size_t seg_ws_bytes,
+                void* y, int64_t ldy, void* stream);
+
+/*
+ * Workspace of lora_apply_batched for T tokens on this store (host only).
+ * with_segmentation = 1: room for seg_off, perm and the plan (ids path);
+ * 0: only the float32 intermediate h (caller passes a grouping).
+ */
+size_t lora_apply_ws_bytes(const lora_store* store_host, int T, int with_segmentation);
+
+/*
+ * The batched apply:  y[t] += s_a * B_a (A_a x[t])  for every token.
+ * Either ids (then the grouping is computed into ws), or ids = NULL and
+ * seg_off / perm / seg_ws from a previous lora_segment (one grouping reused
+ * across many stores, e.g. every projection of a decode step).
+ * Equivalent to lora_segment (when ids is given), lora_shrink, lora_expand.
+ * Errors: union of those calls'.
+ */
+int lora_apply_batched(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy,
+                       int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm,
+                       const void* seg_ws, size_t seg_ws_bytes, void* ws, size_t ws_bytes,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RANK_SPECIALIZED_LORA_H */

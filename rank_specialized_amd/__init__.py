@@ -1,0 +1,239 @@
+"""Batched, rank-specialized LoRA-delta apply on AMD Instinct MI355X.
+
+Thin PyTorch binding over the C ABI (include/lora.h).  Torch provides device
+memory and the current stream; every step of the apply runs in the HIP
+kernels of librank_specialized.so.  The entry points keep the C names:
+
+    store = lora_pack_retained(A_list, B_list, scales)        # pack
+    seg   = lora_segment(ids, store.n)                        # group tokens
+    h     = lora_shrink(store, x, seg)                        # h = A_a x (grouped rows)
+    lora_expand(store, h, seg, y)                             # y += s_a B_a h
+    lora_apply_batched(store, x, y, ids=ids)                  # all of the above
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import _lib as L
+from ._lib import LoraError, lora_store  # noqa: F401
+
+__all__ = [
+    "Store", "Segmentation", "LoraError", "lora_store_bytes", "lora_pack_retained",
+    "lora_segment_ws_bytes", "lora_segment", "lora_segment_from_offsets", "lora_shrink",
+    "lora_expand", "lora_apply_ws_bytes", "lora_apply_batched", "load_library",
+]
+
+_DTYPES = {torch.bfloat16: L.LORA_DTYPE_BF16, torch.float32: L.LORA_DTYPE_F32}
+
+
+def load_library():
+    """Load librank_specialized.so (raises ImportError if it was not built)."""
+    return L.lib()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None or t.numel() == 0 else t.data_ptr()
+
+
+def _rows(t: torch.Tensor, name: str):
+    if t.dim() != 2 or (t.shape[0] > 0 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+    return t.stride(0) if t.shape[0] > 0 else t.shape[1]
+
+
+@dataclass
+class Store:
+    """A packed retained-rank store: the C struct plus the buffers it references."""
+
+    c: lora_store
+    A_pack: torch.Tensor
+    Bt_pack: torch.Tensor
+    meta: torch.Tensor
+    ranks: List[int]
+    dtype: torch.dtype
+
+    @property
+    def n(self) -> int:
+        return self.c.n
+
+    @property
+    def d_in(self) -> int:
+        return self.c.d_in
+
+    @property
+    def d_out(self) -> int:
+        return self.c.d_out
+
+    @property
+    def r_max(self) -> int:
+        return self.c.r_max
+
+    @property
+    def pad_to(self) -> int:
+        return self.c.pad_to
+
+    def ref(self):
+        return C.byref(self.c)
+
+    def clone(self) -> "Store":
+        """An independent copy in fresh device memory (same layout)."""
+        A, Bt, meta = self.A_pack.clone(), self.Bt_pack.clone(), self.meta.clone()
+        c = lora_store.from_buffer_copy(self.c)
+        n = self.c.n
+        c.A_pack, c.Bt_pack = A.data_ptr(), Bt.data_ptr()
+        c.row_off = meta.data_ptr()
+        c.rank = meta.data_ptr() + (n + 1) * 4
+        c.scale = meta.data_ptr() + (2 * n + 1) * 4
+        return Store(c, A, Bt, meta, list(self.ranks), self.dtype)
+
+    def device_meta(self):
+        """(row_off, rank, scale) as device tensors (views of the meta buffer)."""
+        n = self.n
+        i32 = self.meta[: (3 * n + 1) * 4].view(torch.int32)
+        return i32[: n + 1], i32[n + 1: 2 * n + 1], i32[2 * n + 1: 3 * n + 1].view(torch.float32)
+
+
+def lora_store_bytes(n: int, d_in: int, d_out: int, dtype: torch.dtype, ranks: Sequence[int],
+                     pad_to: int = 0):
+    r = (C.c_int32 * max(n, 1))(*[int(v) for v in ranks])
+    a, b, m = C.c_size_t(), C.c_size_t(), C.c_size_t()
+    L.check("lora_store_bytes", L.lib().lora_store_bytes(n, d_in, d_out, _DTYPES[dtype], r, pad_to,
+                                                         C.byref(a), C.byref(b), C.byref(m)))
+    return a.value, b.value, m.value
+
+
+def lora_pack_retained(A_list: Sequence[torch.Tensor], B_list: Sequence[torch.Tensor], scales,
+                       pad_to: int = 0) -> Store:
+    """Pack per-adapter factors (A_a [r_a, d_in], B_a [d_out, r_a], device tensors,
+    row-major contiguous, one dtype) into a store.  pad_to > 0 builds the
+    rank-padded comparison store."""
+    n = len(A_list)
+    if n == 0 or len(B_list) != n:
+        raise ValueError("need one A and one B per adapter")
+    dtype = A_list[0].dtype
+    device = A_list[0].device
+    d_in = A_list[0].shape[1]
+    d_out = B_list[0].shape[0]
+    ranks = [int(a.shape[0]) for a in A_list]
+    for a, b, r in zip(A_list, B_list, ranks):
+        if a.dtype != dtype or b.dtype != dtype or a.shape != (r, d_in) or b.shape != (d_out, r):
+            raise ValueError("factor shapes/dtypes are inconsistent")
+        if not (a.is_contiguous() and b.is_contiguous()):
+            raise ValueError("factors must be contiguous")
+    a_bytes, b_bytes, m_bytes = lora_store_bytes(n, d_in, d_out, dtype, ranks, pad_to)
+    A_pack = torch.empty(max(a_bytes, 16), dtype=torch.uint8, device=device)
+    Bt_pack = torch.empty(max(b_bytes, 16), dtype=torch.uint8, device=device)
+    meta = torch.empty(m_bytes, dtype=torch.uint8, device=device)
+    r_arr = (C.c_int32 * n)(*ranks)
+    s_arr = (C.c_float * n)(*[float(v) for v in scales])
+    a_ptrs = (C.c_void_p * n)(*[_p(a) for a in A_list])
+    b_ptrs = (C.c_void_p * n)(*[_p(b) for b in B_list])
+    st = lora_store()
+    L.check("lora_pack_retained", L.lib().lora_pack_retained(
+        C.byref(st), n, d_in, d_out, _DTYPES[dtype], r_arr, s_arr, a_ptrs, b_ptrs,
+        A_pack.data_ptr(), Bt_pack.data_ptr(), meta.data_ptr(), pad_to, _stream(meta)))
+    return Store(st, A_pack, Bt_pack, meta, ranks, dtype)
+
+
+def lora_segment_ws_bytes(T: int, n: int) -> int:
+    return int(L.lib().lora_segment_ws_bytes(T, n))
+
+
+@dataclass
+class Segmentation:
+    """Grouped order of T tokens over n adapters plus the tile plan."""
+
+    T: int
+    n: int
+    seg_off: torch.Tensor  # int32 [n + 2]
+    perm: torch.Tensor  # int32 [T]
+    ws: torch.Tensor  # uint8 plan
+    n_invalid: Optional[torch.Tensor] = None
+
+    @property
+    def ws_bytes(self) -> int:
+        return self.ws.numel()
+
+
+def lora_segment(ids: torch.Tensor, n: int, *, seg: Optional[Segmentation] = None) -> Segmentation:
+    """Stable grouping of tokens by adapter id (ids: int32 device tensor [T])."""
+    if ids.dtype != torch.int32 or ids.dim() != 1 or not ids.is_contiguous():
+        raise ValueError("ids must be a contiguous int32 vector")
+    T = ids.shape[0]
+    dev = ids.device
+    if seg is None:
+        seg = Segmentation(T, n, torch.empty(n + 2, dtype=torch.int32, device=dev),
+                           torch.empty(max(T, 1), dtype=torch.int32, device=dev)[:T],
+                           torch.empty(max(lora_segment_ws_bytes(T, n), 16), dtype=torch.uint8,
+                                       device=dev),
+                           torch.empty(1, dtype=torch.int32, device=dev))
+    L.check("lora_segment", L.lib().lora_segment(
+        _p(ids), T, n, seg.seg_off.data_ptr(), _p(seg.perm), seg.n_invalid.data_ptr(),
+        seg.ws.data_ptr(), seg.ws.numel(), _stream(seg.ws)))
+    return seg
+
+
+def lora_segment_from_offsets(seg_off: torch.Tensor, perm: torch.Tensor, n: int) -> Segmentation:
+    """Plan for a caller-supplied grouping (seg_off [n+2], perm [T], int32)."""
+    T = perm.shape[0]
+    ws = torch.empty(max(lora_segment_ws_bytes(T, n), 16), dtype=torch.uint8, device=seg_off.device)
+    L.check("lora_segment_from_offsets", L.lib().lora_segment_from_offsets(
+        seg_off.data_ptr(), T, n, ws.data_ptr(), ws.numel(), _stream(ws)))
+    return Segmentation(T, n, seg_off, perm, ws)
+
+
+def lora_shrink(store: Store, x: torch.Tensor, seg: Segmentation, h: Optional[torch.Tensor] = None
+                ) -> torch.Tensor:
+    """h[i, :r_a] = A_a x[perm[i]] in float32 (grouped rows).  Columns >= r_a
+    and rows of tokens without an adapter are left as they were in ``h``."""
+    T = x.shape[0]
+    if h is None:
+        h = torch.zeros(T, max(store.r_max, 1), dtype=torch.float32, device=x.device)
+    L.check("lora_shrink", L.lib().lora_shrink(
+        store.ref(), _p(x), _rows(x, "x"), T, seg.seg_off.data_ptr(), _p(seg.perm),
+        seg.ws.data_ptr(), seg.ws_bytes, _p(h), _rows(h, "h"), _stream(x)))
+    return h
+
+
+def lora_expand(store: Store, h: torch.Tensor, seg: Segmentation, y: torch.Tensor) -> torch.Tensor:
+    """y[perm[i]] += s_a B_a h[i] in place."""
+    T = y.shape[0]
+    L.check("lora_expand", L.lib().lora_expand(
+        store.ref(), _p(h), _rows(h, "h"), T, seg.seg_off.data_ptr(), _p(seg.perm),
+        seg.ws.data_ptr(), seg.ws_bytes, _p(y), _rows(y, "y"), _stream(y)))
+    return y
+
+
+def lora_apply_ws_bytes(store: Store, T: int, with_segmentation: bool = True) -> int:
+    return int(L.lib().lora_apply_ws_bytes(store.ref(), T, 1 if with_segmentation else 0))
+
+
+def lora_apply_batched(store: Store, x: torch.Tensor, y: torch.Tensor, *,
+                       ids: Optional[torch.Tensor] = None, seg: Optional[Segmentation] = None,
+                       ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[t] += s_a B_a (A_a x[t]) in place, for ids (grouped here) or a prior grouping."""
+    T = x.shape[0]
+    if (ids is None) == (seg is None):
+        raise ValueError("pass exactly one of ids or seg")
+    need = lora_apply_ws_bytes(store, T, ids is not None)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    if seg is not None:
+        so, pm, sw, swb = seg.seg_off.data_ptr(), _p(seg.perm), seg.ws.data_ptr(), seg.ws_bytes
+    else:
+        if ids.dtype != torch.int32 or not ids.is_contiguous():
+            raise ValueError("ids must be a contiguous int32 vector")
+        so = pm = sw = None
+        swb = 0
+    L.check("lora_apply_batched", L.lib().lora_apply_batched(
+        store.ref(), _p(x), _rows(x, "x"), _p(y), _rows(y, "y"), T, _p(ids) if ids is not None else None,
+        so, pm, sw, swb, ws.data_ptr(), ws.numel(), _stream(x)))
+    return y

@@ -1,0 +1,218 @@
+// C ABI of the batched, rank-specialized LoRA-delta apply (include/lora.h).
+// Host dispatch only: validate, size grids, launch on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <vector>
+
+#include "kernels.h"
+#include "validate.h"
+
+namespace lora {
+static thread_local int g_last_hip = 0;
+static int hip_fail(hipError_t e) {
+  g_last_hip = (int)e;
+  return LORA_ERR_HIP;
+}
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+}  // namespace lora
+
+using namespace lora;
+
+extern "C" {
+
+const char* lora_status_string(int status) {
+  switch (status) {
+    case LORA_OK: return "ok";
+    case LORA_ERR_INVALID_ARG: return "invalid argument";
+    case LORA_ERR_UNSUPPORTED: return "unsupported (outside the kernels' envelope)";
+    case LORA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int lora_last_hip_error(void) { return g_last_hip; }
+
+int lora_abi_version(void) { return 1; }
+
+int lora_store_bytes(int n, int d_in, int d_out, int dtype, const int32_t* ranks_host, int pad_to,
+                     size_t* a_bytes_host, size_t* bt_bytes_host, size_t* meta_bytes_host) {
+  if (!a_bytes_host || !bt_bytes_host || !meta_bytes_host) return LORA_ERR_INVALID_ARG;
+  int r_max = 0;
+  int64_t rows = 0;
+  int st = check_store_shape(n, d_in, d_out, dtype, ranks_host, pad_to, &r_max, &rows);
+  if (st != LORA_OK) return st;
+  const size_t eb = (size_t)elem_bytes(dtype);
+  *a_bytes_host = (size_t)rows * d_in * eb;
+  *bt_bytes_host = (size_t)rows * d_out * eb;
+  *meta_bytes_host = meta_bytes(n);
+  return LORA_OK;
+}
+
+int lora_pack_retained(lora_store* out_host, int n, int d_in, int d_out, int dtype,
+                       const int32_t* ranks_host, const float* scales_host,
+                       const void* const* A_ptrs_host, const void* const* B_ptrs_host, void* A_pack,
+                       void* Bt_pack, void* meta, int pad_to, void* stream) {
+  if (!out_host || !scales_host || !meta) return LORA_ERR_INVALID_ARG;
+  if (n < 1) return LORA_ERR_INVALID_ARG;
+  int r_max = 0;
+  int64_t rows = 0;
+  int st = check_store_shape(n, d_in, d_out, dtype, ranks_host, pad_to, &r_max, &rows);
+  if (st != LORA_OK) return st;
+  if (!A_ptrs_host || !B_ptrs_host) return LORA_ERR_INVALID_ARG;
+  if (rows > 0 && (!A_pack || !Bt_pack)) return LORA_ERR_INVALID_ARG;
+  if (!aligned16(meta) || (A_pack && !aligned16(A_pack)) || (Bt_pack && !aligned16(Bt_pack)))
+    return LORA_ERR_UNSUPPORTED;
+  for (int a = 0; a < n; ++a)
+    if (ranks_host[a] > 0 && (!A_ptrs_host[a] || !B_ptrs_host[a])) return LORA_ERR_INVALID_ARG;
+
+  // Host image of the meta buffer.
+  std::vector<char> img(meta_bytes(n), 0);
+  int32_t* row_off = reinterpret_cast<int32_t*>(img.data());
+  int32_t* rank = row_off + (n + 1);
+  float* scale = reinterpret_cast<float*>(rank + n);
+  int32_t* true_rank = reinterpret_cast<int32_t*>(scale + n);
+  const void** ptrs = reinterpret_cast<const void**>(img.data() + meta_ptr_offset(n));
+  row_off[0] = 0;
+  for (int a = 0; a < n; ++a) {
+    const int stored = pad_to > 0 ? pad_to : ranks_host[a];
+    rank[a] = stored;
+    true_rank[a] = ranks_host[a];
+    scale[a] = scales_host[a];
+    row_off[a + 1] = row_off[a] + stored;
+    ptrs[a] = A_ptrs_host[a];
+    ptrs[n + a] = B_ptrs_host[a];
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(meta, img.data(), img.size(), hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e);
+  e = launch_pack(dtype, meta, n, d_in, d_out, (int)rows, A_pack, Bt_pack, s);
+  if (e != hipSuccess) return hip_fail(e);
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e);
+
+  lora_store st_out;
+  std::memset(&st_out, 0, sizeof(st_out));
+  st_out.n = n;
+  st_out.d_in = d_in;
+  st_out.d_out = d_out;
+  st_out.dtype = dtype;
+  st_out.r_max = r_max;
+  st_out.R = (int32_t)rows;
+  st_out.pad_to = pad_to;
+  st_out.A_pack = A_pack;
+  st_out.Bt_pack = Bt_pack;
+  st_out.row_off = reinterpret_cast<const int32_t*>(meta);
+  st_out.rank = st_out.row_off + (n + 1);
+  st_out.scale = reinterpret_cast<const float*>(st_out.rank + n);
+  *out_host = st_out;
+  return LORA_OK;
+}
+
+size_t lora_segment_ws_bytes(int T, int n) { return plan_bytes(T, n); }
+
+int lora_segment(const int32_t* ids, int T, int n, int32_t* seg_off, int32_t* perm, int32_t* n_invalid,
+                 void* ws, size_t ws_bytes, void* stream) {
+  int st = check_segment_args(ids, T, n, seg_off, perm, ws, ws_bytes);
+  if (st != LORA_OK) return st;
+  int max_lds = 0;
+  hipError_t e = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, 0);
+  if (e != hipSuccess) return hip_fail(e);
+  if (segment_lds_bytes(T, n) > (size_t)max_lds) return LORA_ERR_UNSUPPORTED;
+  e = launch_segment(ids, T, n, seg_off, perm, n_invalid, ws, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LORA_OK : hip_fail(e);
+}
+
+int lora_segment_from_offsets(const int32_t* seg_off, int T, int n, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (T < 0 || n < 1 || !seg_off || !ws) return LORA_ERR_INVALID_ARG;
+  if (ws_bytes < plan_bytes(T, n)) return LORA_ERR_INVALID_ARG;
+  if (!aligned16(ws)) return LORA_ERR_UNSUPPORTED;
+  if (n > LORA_SEGMENT_MAX_N) return LORA_ERR_UNSUPPORTED;
+  hipError_t e = launch_plan_from_offsets(seg_off, T, n, ws, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LORA_OK : hip_fail(e);
+}
+
+int lora_shrink(const lora_store* store_host, const void* x, int64_t ldx, int T, const int32_t* seg_off,
+                const int32_t* perm, const void* seg_ws, size_t seg_ws_bytes, float* h, int64_t ldh,
+                void* stream) {
+  int st = check_store(store_host);
+  if (st != LORA_OK) return st;
+  if ((st = check_plan_args(store_host, T, seg_off, perm, seg_ws, seg_ws_bytes)) != LORA_OK) return st;
+  if ((st = check_rows(x, ldx, store_host->d_in, store_host->dtype, T)) != LORA_OK) return st;
+  if ((st = check_h(h, ldh, store_host, T)) != LORA_OK) return st;
+  if (T == 0) return LORA_OK;
+  hipError_t e = launch_shrink(*store_host, x, ldx, T, perm, seg_ws, h, ldh,
+                               reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LORA_OK : hip_fail(e);
+}
+
+int lora_expand(const lora_store* store_host, const float* h, int64_t ldh, int T, const int32_t* seg_off,
+                const int32_t* perm, const void* seg_ws, size_t seg_ws_bytes, void* y, int64_t ldy,
+                void* stream) {
+  int st = check_store(store_host);
+  if (st != LORA_OK) return st;
+  if ((st = check_plan_args(store_host, T, seg_off, perm, seg_ws, seg_ws_bytes)) != LORA_OK) return st;
+  if ((st = check_rows(y, ldy, store_host->d_out, store_host->dtype, T)) != LORA_OK) return st;
+  if ((st = check_h(h, ldh, store_host, T)) != LORA_OK) return st;
+  if (T == 0) return LORA_OK;
+  hipError_t e = launch_expand(*store_host, h, ldh, T, perm, seg_ws, y, ldy,
+                               reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LORA_OK : hip_fail(e);
+}
+
+// Workspace layout of lora_apply_batched (each part 256-byte aligned):
+//   [plan | seg_off (n+2) | perm (T)]   (only with segmentation)   then h.
+static size_t apply_seg_bytes(int T, int n) {
+  return align_up(plan_bytes(T, n), 256) + align_up((size_t)(n + 2) * 4, 256) +
+         align_up((size_t)T * 4, 256);
+}
+
+size_t lora_apply_ws_bytes(const lora_store* store_host, int T, int with_segmentation) {
+  if (!store_host || T < 0 || store_host->n < 1) return 0;
+  size_t hb = align_up((size_t)T * (size_t)apply_ldh(store_host->r_max) * 4, 256);
+  return hb + (with_segmentation ? apply_seg_bytes(T, store_host->n) : 0);
+}
+
+int lora_apply_batched(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy,
+                       int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm,
+                       const void* seg_ws, size_t seg_ws_bytes, void* ws, size_t ws_bytes,
+                       void* stream) {
+  int st = check_store(store_host);
+  if (st != LORA_OK) return st;
+  const lora_store& s = *store_host;
+  if (T < 0) return LORA_ERR_INVALID_ARG;
+  if ((st = check_rows(x, ldx, s.d_in, s.dtype, T)) != LORA_OK) return st;
+  if ((st = check_rows(y, ldy, s.d_out, s.dtype, T)) != LORA_OK) return st;
+  if (T == 0) return LORA_OK;  // nothing to group or apply
+  const bool segment = ids != nullptr;
+  if (!ws || ws_bytes < lora_apply_ws_bytes(store_host, T, segment ? 1 : 0)) return LORA_ERR_INVALID_ARG;
+  if (!aligned16(ws)) return LORA_ERR_UNSUPPORTED;
+  char* base = reinterpret_cast<char*>(ws);
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  const void* plan = seg_ws;
+  if (segment) {
+    if (T > LORA_SEGMENT_MAX_T || s.n > LORA_SEGMENT_MAX_N) return LORA_ERR_UNSUPPORTED;
+    void* plan_w = base;
+    int32_t* so = reinterpret_cast<int32_t*>(base + align_up(plan_bytes(T, s.n), 256));
+    int32_t* pm = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(so) +
+                                             align_up((size_t)(s.n + 2) * 4, 256));
+    base += apply_seg_bytes(T, s.n);
+    st = lora_segment(ids, T, s.n, so, pm, nullptr, plan_w, plan_bytes(T, s.n), stream);
+    if (st != LORA_OK) return st;
+    seg_off = so;
+    perm = pm;
+    plan = plan_w;
+    seg_ws_bytes = plan_bytes(T, s.n);
+  } else {
+    if ((st = check_plan_args(store_host, T, seg_off, perm, seg_ws, seg_ws_bytes)) != LORA_OK) return st;
+  }
+  float* h = reinterpret_cast<float*>(base);
+  const int64_t ldh = apply_ldh(s.r_max);
+  hipError_t e = launch_shrink(s, x, ldx, T, perm, plan, h, ldh, strm);
+  if (e != hipSuccess) return hip_fail(e);
+  e = launch_expand(s, h, ldh, T, perm, plan, y, ldy, strm);
+  return e == hipSuccess ? LORA_OK : hip_fail(e);
+}
+
+}  // extern "C"

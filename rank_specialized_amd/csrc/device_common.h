@@ -1,0 +1,105 @@
+// Device-side helpers shared by the kernels (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.h"
+
+namespace lora {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bfloat16
+// bfloat16 is the top half of a binary32 word: widening is a 16-bit shift.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// binary32 -> bfloat16 bits, round to nearest, ties to even: add 0x7fff plus
+// the lowest kept bit, then drop the low 16 bits.  NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// ------------------------------------------------------------ element types
+// Each lane moves 16 bytes at a time: 8 bf16 or 4 f32 values.
+struct BF16 {
+  static constexpr int kVec = 8;
+  static constexpr int kBytes = 2;
+  typedef uint16_t storage;
+  __device__ static __forceinline__ void widen(const uint4& v, float* f) {
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+  }
+  __device__ static __forceinline__ uint4 narrow(const float* f) {
+    return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                      pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
+  }
+};
+struct F32 {
+  static constexpr int kVec = 4;
+  static constexpr int kBytes = 4;
+  typedef float storage;
+  __device__ static __forceinline__ void widen(const uint4& v, float* f) {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  }
+  __device__ static __forceinline__ uint4 narrow(const float* f) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
+                      __float_as_uint(f[2]), __float_as_uint(f[3]));
+  }
+};
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// ------------------------------------------------------------------- MFMA
+// 16x16 output tile, float32 accumulate.  Operand convention (both
+// operands): lane l supplies row/column (l % 16) of its matrix and the
+// K-slice owned by lane group (l / 16).  Output: lane l holds column l % 16,
+// rows 4 * (l / 16) + 0..3.
+__device__ __forceinline__ f32x4_t mfma_bf16_16x16x32(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_f32_16x16x4(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// One 16-byte K-chunk of both operands: 1 bf16 MFMA (K = 32 over the wave)
+// or 4 f32 MFMAs (K = 4 each).
+template <typename E>
+__device__ __forceinline__ f32x4_t mfma_chunk(const uint4& a, const uint4& b, f32x4_t c);
+template <>
+__device__ __forceinline__ f32x4_t mfma_chunk<BF16>(const uint4& a, const uint4& b, f32x4_t c) {
+  return mfma_bf16_16x16x32(a, b, c);
+}
+template <>
+__device__ __forceinline__ f32x4_t mfma_chunk<F32>(const uint4& a, const uint4& b, f32x4_t c) {
+  c = mfma_f32_16x16x4(__uint_as_float(a.x), __uint_as_float(b.x), c);
+  c = mfma_f32_16x16x4(__uint_as_float(a.y), __uint_as_float(b.y), c);
+  c = mfma_f32_16x16x4(__uint_as_float(a.z), __uint_as_float(b.z), c);
+  c = mfma_f32_16x16x4(__uint_as_float(a.w), __uint_as_float(b.w), c);
+  return c;
+}
+
+// ------------------------------------------------------------------ plan
+struct Plan {
+  const int32_t* count;  // header[0]
+  const int4* tiles;     // {adapter, first grouped position, tokens, 0}
+};
+__host__ __device__ inline Plan plan_view(const void* ws) {
+  Plan p;
+  p.count = reinterpret_cast<const int32_t*>(ws);
+  p.tiles = reinterpret_cast<const int4*>(reinterpret_cast<const char*>(ws) + kPlanHeaderBytes);
+  return p;
+}
+
+}  // namespace lora

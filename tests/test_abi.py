@@ -1,0 +1,204 @@
+"""The C ABI on the CPU: the library loads, exports every symbol that
+include/lora.h declares, and rejects bad arguments before touching the GPU.
+No compute call is made here."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from rank_specialized_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lora.h")
+
+FAKE = 0x10000  # a 16-byte aligned non-null address; never dereferenced on error paths
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    src = "\n".join(line for line in src.splitlines() if not line.lstrip().startswith("#"))
+    return sorted(set(re.findall(r"\b(lora_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.lib()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ["lora_pack_retained", "lora_segment", "lora_shrink", "lora_expand",
+                 "lora_apply_batched", "lora_store_bytes", "lora_status_string"]:
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in L.SIGNATURES, f"binding lacks {name}"
+
+
+def test_binding_matches_header():
+    assert set(L.SIGNATURES) == set(declared_functions())
+
+
+def test_status_strings(lib):
+    assert lib.lora_status_string(0) == b"ok"
+    assert b"invalid" in lib.lora_status_string(1)
+    assert b"unsupported" in lib.lora_status_string(2)
+    assert b"HIP" in lib.lora_status_string(3)
+    assert lib.lora_abi_version() == 1
+    assert lib.lora_last_hip_error() == 0
+
+
+def _sizes(lib, n, d_in, d_out, dtype, ranks, pad_to=0):
+    r = (C.c_int32 * max(n, 1))(*ranks)
+    a, b, m = C.c_size_t(), C.c_size_t(), C.c_size_t()
+    st = lib.lora_store_bytes(n, d_in, d_out, dtype, r, pad_to, C.byref(a), C.byref(b), C.byref(m))
+    return st, a.value, b.value, m.value
+
+
+def test_store_bytes(lib):
+    st, a, b, m = _sizes(lib, 3, 64, 32, L.LORA_DTYPE_BF16, [1, 0, 5])
+    assert st == 0 and a == 6 * 64 * 2 and b == 6 * 32 * 2
+    assert m >= (4 * 3 + 1) * 4 + 16 * 3
+    st, a, b, _ = _sizes(lib, 3, 64, 32, L.LORA_DTYPE_F32, [1, 0, 5], pad_to=8)
+    assert st == 0 and a == 24 * 64 * 4 and b == 24 * 32 * 4
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-1, 64, 64, 1, [1]), 1),
+    ((1, 0, 64, 1, [1]), 1),
+    ((1, 64, -8, 1, [1]), 1),
+    ((2, 64, 64, 1, [1, -2]), 1),
+    ((1, 64, 64, 1, [65]), 2),          # above LORA_MAX_RANK
+    ((1, 60, 64, 1, [4]), 2),           # d_in not a multiple of 8 (bf16)
+    ((1, 64, 66, 0, [4]), 2),           # d_out not a multiple of 4 (f32)
+    ((1, 64, 64, 7, [4]), 2),           # unknown dtype
+])
+def test_store_bytes_errors(lib, args, status):
+    assert _sizes(lib, *args)[0] == status
+
+
+def test_store_bytes_pad_below_rank(lib):
+    assert _sizes(lib, 2, 64, 64, 1, [4, 9], pad_to=8)[0] == 1
+    assert _sizes(lib, 2, 64, 64, 1, [4, 9], pad_to=72)[0] == 2
+
+
+def test_store_bytes_null_outputs(lib):
+    r = (C.c_int32 * 1)(4)
+    assert lib.lora_store_bytes(1, 64, 64, 1, r, 0, None, None, None) == 1
+
+
+def test_pack_rejects_before_launch(lib):
+    st = L.lora_store()
+    r = (C.c_int32 * 2)(2, 3)
+    s = (C.c_float * 2)(1.0, 1.0)
+    ptrs = (C.c_void_p * 2)(FAKE, FAKE)
+    nulls = (C.c_void_p * 2)(FAKE, None)
+    f = lib.lora_pack_retained
+    assert f(None, 2, 64, 64, 1, r, s, ptrs, ptrs, FAKE, FAKE, FAKE, 0, None) == 1
+    assert f(C.byref(st), 0, 64, 64, 1, r, s, ptrs, ptrs, FAKE, FAKE, FAKE, 0, None) == 1
+    assert f(C.byref(st), 2, 64, 64, 1, r, s, ptrs, nulls, FAKE, FAKE, FAKE, 0, None) == 1
+    assert f(C.byref(st), 2, 64, 64, 1, r, s, ptrs, ptrs, None, FAKE, FAKE, 0, None) == 1
+    assert f(C.byref(st), 2, 64, 64, 1, r, s, ptrs, ptrs, FAKE, FAKE, None, 0, None) == 1
+    assert f(C.byref(st), 2, 64, 64, 1, r, s, ptrs, ptrs, FAKE + 4, FAKE, FAKE, 0, None) == 2
+    assert f(C.byref(st), 2, 64, 64, 1, r, s, ptrs, ptrs, FAKE, FAKE, FAKE, 2, None) == 1
+
+
+def test_segment_ws_bytes(lib):
+    assert lib.lora_segment_ws_bytes(0, 4) == 64
+    # T=100, n=3: at most (100 + 63*3)//64 = 4 tiles
+    assert lib.lora_segment_ws_bytes(100, 3) == 64 + 16 * 4
+    assert lib.lora_segment_ws_bytes(-1, 3) == 0
+
+
+def test_segment_rejects_before_launch(lib):
+    f = lib.lora_segment
+    big = 1 << 30
+    assert f(FAKE, -1, 4, FAKE, FAKE, None, FAKE, big, None) == 1
+    assert f(FAKE, 16, 0, FAKE, FAKE, None, FAKE, big, None) == 1
+    assert f(None, 16, 4, FAKE, FAKE, None, FAKE, big, None) == 1
+    assert f(FAKE, 16, 4, None, FAKE, None, FAKE, big, None) == 1
+    assert f(FAKE, 16, 4, FAKE, None, None, FAKE, big, None) == 1
+    assert f(FAKE, 16, 4, FAKE, FAKE, None, FAKE, 8, None) == 1          # ws too small
+    assert f(FAKE, 16, 4, FAKE, FAKE, None, FAKE + 8, big, None) == 2    # ws misaligned
+    assert f(FAKE, L.LORA_SEGMENT_MAX_T + 1, 4, FAKE, FAKE, None, FAKE, big, None) == 2
+    assert f(FAKE, 16, L.LORA_SEGMENT_MAX_N + 1, FAKE, FAKE, None, FAKE, big, None) == 2
+    assert lib.lora_segment_from_offsets(None, 16, 4, FAKE, big, None) == 1
+    assert lib.lora_segment_from_offsets(FAKE, 16, 4, FAKE, 8, None) == 1
+
+
+def _store(n=4, d_in=64, d_out=32, dtype=1, r_max=8, R=20):
+    st = L.lora_store()
+    st.n, st.d_in, st.d_out, st.dtype, st.r_max, st.R = n, d_in, d_out, dtype, r_max, R
+    st.A_pack = st.Bt_pack = st.row_off = st.rank = st.scale = FAKE
+    return st
+
+
+def test_shrink_expand_reject_before_launch(lib):
+    big = 1 << 30
+    for fn in (lib.lora_shrink, lib.lora_expand):
+        good = _store()
+        d = 64 if fn is lib.lora_shrink else 32
+
+        def call(st=good, p=FAKE, ld=d, T=16, so=FAKE, pm=FAKE, ws=FAKE, wsb=big, h=FAKE, ldh=8):
+            if fn is lib.lora_shrink:
+                return fn(C.byref(st) if st is not None else None, p, ld, T, so, pm, ws, wsb, h, ldh, None)
+            return fn(C.byref(st) if st is not None else None, h, ldh, T, so, pm, ws, wsb, p, ld, None)
+
+        assert call(T=0) == 0                       # no-op, nothing launched
+        assert call(st=None) == 1
+        assert call(st=_store(n=0)) == 1
+        assert call(st=_store(r_max=65)) == 2
+        assert call(st=_store(dtype=9)) == 2
+        assert call(st=_store(d_in=60, d_out=36)) == 2
+        assert call(T=-1) == 1
+        assert call(ld=d - 8) == 1                  # row stride below the row length
+        assert call(ld=d + 4) == 2                  # stride not a multiple of 8 bf16 elements
+        assert call(p=FAKE + 2) == 2                # misaligned rows
+        assert call(p=None) == 1
+        assert call(ldh=4) == 1                     # ldh < r_max
+        assert call(h=None) == 1
+        assert call(wsb=8) == 1
+        assert call(so=None) == 1
+        assert call(pm=None) == 1
+
+
+def test_apply_rejects_before_launch(lib):
+    big = 1 << 30
+    st = _store()
+    f = lib.lora_apply_batched
+
+    def call(T=16, ids=FAKE, so=None, pm=None, sw=None, swb=0, ws=FAKE, wsb=big, x=FAKE, y=FAKE,
+             ldx=64, ldy=32, s=st):
+        return f(C.byref(s) if s is not None else None, x, ldx, y, ldy, T, ids, so, pm, sw, swb, ws, wsb, None)
+
+    assert call(s=None) == 1
+    assert call(T=-3) == 1
+    assert call(x=None) == 1
+    assert call(ldy=16) == 1
+    assert call(ws=None) == 1
+    assert call(wsb=16) == 1
+    assert call(ws=FAKE + 8) == 2
+    assert call(T=L.LORA_SEGMENT_MAX_T + 1) == 2
+    # no ids: a grouping must be supplied
+    assert call(ids=None) == 1
+    assert call(ids=None, so=FAKE, pm=FAKE, sw=FAKE, swb=8) == 1
+    # T = 0: nothing to group or apply, with or without ids
+    assert call(T=0, ids=None, so=FAKE, pm=FAKE, sw=FAKE, swb=big) == 0
+    assert call(T=0, ids=None) == 0
+    assert call(T=0, x=None, y=None) == 0
+
+
+def test_apply_ws_bytes(lib):
+    st = _store(n=4, r_max=6)
+    T = 100
+    ldh = 8  # r_max rounded up to a multiple of 4
+    h_bytes = -(-T * ldh * 4 // 256) * 256
+    assert lib.lora_apply_ws_bytes(C.byref(st), T, 0) == h_bytes
+    assert lib.lora_apply_ws_bytes(C.byref(st), T, 1) > h_bytes
+    assert lib.lora_apply_ws_bytes(None, T, 1) == 0

@@ -1,0 +1,251 @@
+"""GPU parity of the HIP path against the CPU oracle.
+
+Float configs: max |y_gpu - y_ref| <= 2e-2 max |y_ref| (bf16) or 1e-5 max |y_ref|
+(f32) over the call, y0 = 0.  Integer configs (x, A, B integers in [-2, 2],
+power-of-two scales): every partial sum is an exact integer below 2**24, so
+the GPU result must equal the round-to-nearest-even bf16 of the exact result
+bit for bit, whatever the summation order.
+"""
+import numpy as np
+import pytest
+import torch
+
+import rank_specialized_amd as rs
+from oracle import apply_ref, bf16_round_ref, shrink_error_bound, shrink_ref
+from workloads import make_config, make_random_workload
+
+from gpu_helpers import (TOL, TORCH_DTYPE, device, hbits, inputs, note, pack, rel_err, to_dev,
+                         y_host)
+
+pytestmark = pytest.mark.gpu
+
+FLOAT_CONFIGS = ["1", "2", "3", "4"]
+FLEET_SAMPLES = [("5U", 0, 0), ("5U", 27, 6), ("5S", 3, 1), ("5S", 14, 4)]
+
+
+def _run_apply(wl, dev, pad_to=0, **kw):
+    store = pack(wl, dev, pad_to)
+    x, ids, y = inputs(wl, dev)
+    note(f"apply {wl.key} T={wl.T} n={wl.n} d={wl.module.d_in}->{wl.module.d_out} pad_to={pad_to}")
+    rs.lora_apply_batched(store, x, y, ids=ids, **kw)
+    torch.cuda.synchronize()
+    return store, x, ids, y
+
+
+def _ref(wl):
+    m = wl.module
+    return apply_ref(wl.x, wl.ids, m.A, m.B, m.scales, wl.y0)
+
+
+@pytest.mark.parametrize("key", FLOAT_CONFIGS)
+def test_apply_parity(key):
+    dev = device()
+    wl = make_config(key)
+    _, _, _, y = _run_apply(wl, dev)
+    err = rel_err(y_host(y), _ref(wl))
+    assert err <= TOL[wl.dtype], err
+
+
+@pytest.mark.parametrize("key,layer,proj", FLEET_SAMPLES)
+def test_apply_parity_fleet_module(key, layer, proj):
+    dev = device()
+    wl = make_config(key, layer=layer, proj=proj)
+    _, _, _, y = _run_apply(wl, dev)
+    err = rel_err(y_host(y), _ref(wl))
+    assert err <= TOL["bf16"], err
+
+
+@pytest.mark.parametrize("key", FLOAT_CONFIGS + ["5U", "5S"])
+def test_apply_integer_exact(key):
+    dev = device()
+    wl = make_config(key, integer=True, layer=2, proj=6) if key.startswith("5") else \
+        make_config(key, integer=True)
+    _, _, _, y = _run_apply(wl, dev)
+    ref = _ref(wl)
+    assert np.abs(ref).max() < 2 ** 24
+    want = bf16_round_ref(ref) if wl.dtype == "bf16" else ref
+    got = y_host(y)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, (len(bad), bad[:5], got[tuple(bad[0])], want[tuple(bad[0])])
+
+
+@pytest.mark.parametrize("key", ["1", "2", "3", "4"])
+def test_shrink_h_within_fp32_bound(key):
+    dev = device()
+    wl = make_config(key)
+    m = wl.module
+    store = pack(wl, dev)
+    x, ids, _ = inputs(wl, dev)
+    note(f"shrink {key}")
+    seg = rs.lora_segment(ids, m.n)
+    h = torch.full((wl.T, store.r_max), float("nan"), dtype=torch.float32, device=dev)
+    rs.lora_shrink(store, x, seg, h)
+    torch.cuda.synchronize()
+    hg = h.cpu().numpy().astype(np.float64)
+    perm = seg.perm.cpu().numpy()
+    href = shrink_ref(wl.x, wl.ids, m.A)
+    bound = shrink_error_bound(wl.x, wl.ids, m.A)
+    for i, t in enumerate(perm):
+        a = wl.ids[t]
+        r = m.ranks[a]
+        assert np.all(np.abs(hg[i, :r] - href[t]) <= bound[t] + 1e-30), (i, t)
+        assert np.all(np.isnan(hg[i, r:])), "columns beyond the rank must stay untouched"
+
+
+@pytest.mark.parametrize("key", ["1", "3", "4"])
+def test_shrink_then_expand_equals_apply(key):
+    dev = device()
+    wl = make_config(key)
+    store = pack(wl, dev)
+    x, ids, y1 = inputs(wl, dev)
+    y2 = y1.clone()
+    note(f"compose {key}")
+    rs.lora_apply_batched(store, x, y1, ids=ids)
+    seg = rs.lora_segment(ids, store.n)
+    h = rs.lora_shrink(store, x, seg)
+    rs.lora_expand(store, h, seg, y2)
+    torch.cuda.synchronize()
+    assert np.array_equal(hbits(y1), hbits(y2))
+
+
+@pytest.mark.parametrize("key", ["1", "3", "4"])
+def test_padded_equals_specialized(key):
+    """The rank-padded store (zero rows up to r_max) gives bit-identical y."""
+    dev = device()
+    for integer in (True, False):
+        wl = make_config(key, integer=integer)
+        _, _, _, y1 = _run_apply(wl, dev)
+        _, _, _, y2 = _run_apply(wl, dev, pad_to=int(wl.module.ranks.max()))
+        assert np.array_equal(hbits(y1), hbits(y2)), (key, integer)
+
+
+def test_deterministic():
+    dev = device()
+    wl = make_config("3")
+    store = pack(wl, dev)
+    x, ids, y = inputs(wl, dev)
+    ys = []
+    for _ in range(3):
+        yy = y.clone()
+        note("determinism run")
+        rs.lora_apply_batched(store, x, yy, ids=ids)
+        ys.append(hbits(yy))
+    assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[0], ys[2])
+
+
+def test_given_segmentation_equals_ids():
+    dev = device()
+    wl = make_config("3")
+    store = pack(wl, dev)
+    x, ids, y1 = inputs(wl, dev)
+    y2 = y1.clone()
+    note("given segmentation")
+    rs.lora_apply_batched(store, x, y1, ids=ids)
+    seg = rs.lora_segment(ids, store.n)
+    rs.lora_apply_batched(store, x, y2, seg=seg)
+    torch.cuda.synchronize()
+    assert np.array_equal(hbits(y1), hbits(y2))
+
+
+def test_accumulate_fp32():
+    dev = device()
+    wl = make_config("1", with_y0=True)
+    assert wl.y0 is not None and np.abs(wl.y0).max() > 0
+    _, _, _, y = _run_apply(wl, dev)
+    err = rel_err(y_host(y), _ref(wl))
+    assert err <= 1e-5, err
+
+
+def test_accumulate_bf16():
+    """y0 + delta rounded once to bf16: within half a bf16 ulp plus float32 slack."""
+    dev = device()
+    wl = make_config("2", with_y0=True)
+    _, _, _, y = _run_apply(wl, dev)
+    ref = _ref(wl)
+    got = y_host(y)
+    tol = np.abs(ref) * 2.0 ** -8 + 1e-3 * np.abs(ref).max() * 2.0 ** -8 + 1e-6
+    assert np.all(np.abs(got - ref) <= tol)
+
+
+def test_strided_y_slice_and_canaries():
+    """y as a column slice of a wider buffer (offset + row stride); everything
+    outside the slice, and rows of tokens without an adapter, stay untouched."""
+    dev = device()
+    wl = make_random_workload(50, 200, 7, 264, 136, [3, 9, 1, 0, 17, 33, 64], dtype="bf16",
+                              id_mode="zipf", invalid_frac=0.15)
+    store = pack(wl, dev)
+    x, ids, _ = inputs(wl, dev)
+    wide = torch.randn(wl.T, 136 + 64 + 16, device=dev).to(torch.bfloat16)
+    before = wide.clone()
+    y = wide[:, 64: 64 + 136]
+    note("strided y")
+    rs.lora_apply_batched(store, x, y, ids=ids)
+    torch.cuda.synchronize()
+    assert torch.equal(wide[:, :64], before[:, :64]) and torch.equal(wide[:, 200:], before[:, 200:])
+    invalid = torch.from_numpy(wl.ids < 0).to(dev)
+    assert torch.equal(wide[invalid], before[invalid])
+    zero_rank = torch.from_numpy(np.isin(wl.ids, [3])).to(dev)
+    assert torch.equal(wide[zero_rank], before[zero_rank])
+    m = wl.module
+    ref = apply_ref(wl.x, wl.ids, m.A, m.B, m.scales, y_host(before[:, 64:200]))
+    got = y_host(wide[:, 64:200])
+    tol = np.abs(ref) * 2.0 ** -8 + 2e-2 * np.abs(ref - y_host(before[:, 64:200])).max()
+    assert np.all(np.abs(got - ref) <= tol)
+
+
+def test_strided_x():
+    dev = device()
+    wl = make_random_workload(51, 90, 3, 128, 64, [5, 12, 2], dtype="bf16")
+    store = pack(wl, dev)
+    _, ids, y = inputs(wl, dev)
+    xw = torch.zeros(wl.T, 128 + 40, dtype=torch.bfloat16, device=dev)
+    xw[:, 8:136] = to_dev(wl.x, torch.bfloat16, dev)
+    note("strided x")
+    rs.lora_apply_batched(store, xw[:, 8:136], y, ids=ids)
+    torch.cuda.synchronize()
+    assert rel_err(y_host(y), _ref(wl)) <= TOL["bf16"]
+
+
+EDGE = {
+    "one_adapter_many_tiles": dict(seed=60, T=333, n=1, d_in=64, d_out=64, ranks=[7], id_mode="uniform"),
+    "tile_boundaries": dict(seed=61, T=64 + 65 + 1 + 128, n=4, d_in=96, d_out=40, ranks=[16, 32, 48, 64],
+                            id_mode="sorted"),
+    "ragged_dims": dict(seed=62, T=77, n=5, d_in=8, d_out=8, ranks=[1, 2, 3, 4, 8], id_mode="uniform"),
+    "wide_out": dict(seed=63, T=20, n=3, d_in=520, d_out=3000, ranks=[13, 27, 64], id_mode="uniform"),
+    "zero_ranks": dict(seed=64, T=50, n=4, d_in=64, d_out=64, ranks=[0, 5, 0, 2], id_mode="uniform"),
+    "all_invalid": dict(seed=65, T=40, n=3, d_in=64, d_out=64, ranks=[1, 2, 3], id_mode="uniform",
+                        invalid_frac=1.0),
+    "distinct": dict(seed=66, T=100, n=200, d_in=256, d_out=128, ranks=list(range(1, 65)) * 3 + [8] * 8,
+                     id_mode="distinct"),
+}
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_edge_cases(name, dtype):
+    dev = device()
+    kw = dict(EDGE[name])
+    wl = make_random_workload(kw.pop("seed"), kw.pop("T"), kw.pop("n"), kw.pop("d_in"), kw.pop("d_out"),
+                              kw.pop("ranks"), dtype=dtype, y0=True, **kw)
+    _, _, _, y = _run_apply(wl, dev)
+    ref = _ref(wl)
+    got = y_host(y)
+    y0 = wl.y0.astype(np.float64)
+    delta = np.abs(ref - y0).max()
+    if dtype == "fp32":
+        assert np.abs(got - ref).max() <= 1e-5 * max(np.abs(ref).max(), 1e-30)
+    else:
+        tol = np.abs(ref) * 2.0 ** -8 + 2e-2 * delta + 1e-30
+        assert np.all(np.abs(got - ref) <= tol)
+
+
+def test_empty_batch():
+    dev = device()
+    wl = make_random_workload(70, 0, 3, 64, 64, [1, 2, 3], dtype="bf16")
+    store = pack(wl, dev)
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(0, 64, dtype=torch.bfloat16, device=dev)
+    ids = torch.empty(0, dtype=torch.int32, device=dev)
+    note("empty batch")
+    rs.lora_apply_batched(store, x, y, ids=ids)
+    torch.cuda.synchronize()
