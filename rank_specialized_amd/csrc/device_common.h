@@ -60,6 +60,24 @@ struct F32 {
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
+// ----------------------------------------------------------- buffer loads
+// A buffer resource (base address and size in bytes) lets a load carry a
+// 32-bit offset instead of a 64-bit address, and an offset at or beyond the
+// size reads as zero.  Used for the per-adapter factor blocks (a few MB at
+// most), where rows past the retained rank then need no predicate.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // an offset that always reads as zero
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_ld16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t buf_ld2(rsrc_t r, uint32_t voff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0);
+}
+
 // ------------------------------------------------------------------- MFMA
 // 16x16 output tile, float32 accumulate.  Operand convention (both
 // operands): lane l supplies row/column (l % 16) of its matrix and the
@@ -92,13 +110,16 @@ __device__ __forceinline__ f32x4_t mfma_chunk<F32>(const uint4& a, const uint4& 
 
 // ------------------------------------------------------------------ plan
 struct Plan {
-  const int32_t* count;  // header[0]
-  const int4* tiles;     // {adapter, first grouped position, tokens, 0}
+  const int32_t* count;  // header: [0] tiles, [1] large tiles, [2] small tiles, [3] sub-tiles
+  const int4* tiles;     // expand tiles {adapter, first grouped position, tokens, 0}; large first
+  const int4* subtiles;  // shrink sub-tiles (<= kSubTile tokens)
 };
-__host__ __device__ inline Plan plan_view(const void* ws) {
+__host__ __device__ inline Plan plan_view(const void* ws, size_t subtile_offset) {
   Plan p;
-  p.count = reinterpret_cast<const int32_t*>(ws);
-  p.tiles = reinterpret_cast<const int4*>(reinterpret_cast<const char*>(ws) + kPlanHeaderBytes);
+  const char* b = reinterpret_cast<const char*>(ws);
+  p.count = reinterpret_cast<const int32_t*>(b);
+  p.tiles = reinterpret_cast<const int4*>(b + kPlanHeaderBytes);
+  p.subtiles = reinterpret_cast<const int4*>(b + subtile_offset);
   return p;
 }
 

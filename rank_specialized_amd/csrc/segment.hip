@@ -17,8 +17,8 @@
 //     wave-minor order, which places earlier waves first.
 //  3. perm = low bits of the sorted keys; seg_off[b] = lower_bound(b).
 //  4. Tile plan: every adapter group is cut into runs of at most kTile
-//     tokens; a block-wide exclusive scan over adapters gives each run's
-//     slot, so the plan is ordered by adapter, then position.
+//     tokens; block-wide exclusive scans over adapters give each run's slot
+//     in the large-tile or small-tile list.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -61,27 +61,52 @@ __device__ int block_exclusive_scan(int v, int* s_wsum, int* total) {
   return before + x - v;
 }
 
-// Tile plan from group offsets held in LDS (so[0..n]).
-__device__ void build_tiles(const int32_t* so, int n, void* plan_ws, int* s_wsum) {
+// Tile plan from group offsets held in LDS (so[0..n]).  Every adapter group
+// of c tokens is cut into runs of kTile tokens (expand tiles; runs of more
+// than kSmallTile tokens go to the "large" list, written first) and into runs
+// of kSubTile tokens (shrink sub-tiles).  Each list is ordered by adapter,
+// then position (one block scan each).
+__device__ void build_tiles(const int32_t* so, int n, void* plan_ws, size_t sub_off, int* s_wsum) {
   const int per = (n + kSegThreads - 1) / kSegThreads;
   const int a0 = threadIdx.x * per;
   const int a1 = min(n, a0 + per);
-  int cnt = 0;
-  for (int a = a0; a < a1; ++a) cnt += (so[a + 1] - so[a] + kTile - 1) / kTile;
-  int total;
-  int slot = block_exclusive_scan(cnt, s_wsum, &total);
-  int4* tiles = reinterpret_cast<int4*>(reinterpret_cast<char*>(plan_ws) + kPlanHeaderBytes);
+  int n_large = 0, n_small = 0, n_sub = 0;
+  for (int a = a0; a < a1; ++a) {
+    const int c = so[a + 1] - so[a];
+    const int rem = c % kTile;
+    n_large += c / kTile + (rem > kSmallTile ? 1 : 0);
+    n_small += (rem > 0 && rem <= kSmallTile) ? 1 : 0;
+    n_sub += (c + kSubTile - 1) / kSubTile;
+  }
+  int total_large, total_small, total_sub;
+  int slot_large = block_exclusive_scan(n_large, s_wsum, &total_large);
+  int slot_small = block_exclusive_scan(n_small, s_wsum, &total_small) + total_large;
+  int slot_sub = block_exclusive_scan(n_sub, s_wsum, &total_sub);
+  char* base = reinterpret_cast<char*>(plan_ws);
+  int4* tiles = reinterpret_cast<int4*>(base + kPlanHeaderBytes);
+  int4* subs = reinterpret_cast<int4*>(base + sub_off);
   for (int a = a0; a < a1; ++a) {
     const int start = so[a], c = so[a + 1] - so[a];
-    for (int k = 0; k < c; k += kTile) tiles[slot++] = make_int4(a, start + k, min(kTile, c - k), 0);
+    for (int k = 0; k < c; k += kTile) {
+      const int m = min(kTile, c - k);
+      const int4 t = make_int4(a, start + k, m, 0);
+      if (m > kSmallTile) tiles[slot_large++] = t; else tiles[slot_small++] = t;
+    }
+    for (int k = 0; k < c; k += kSubTile) subs[slot_sub++] = make_int4(a, start + k, min(kSubTile, c - k), 0);
   }
-  if (threadIdx.x == 0) reinterpret_cast<int32_t*>(plan_ws)[0] = total;
+  if (threadIdx.x == 0) {
+    int32_t* hdr = reinterpret_cast<int32_t*>(plan_ws);
+    hdr[0] = total_large + total_small;
+    hdr[1] = total_large;
+    hdr[2] = total_small;
+    hdr[3] = total_sub;
+  }
 }
 
 __global__ void __launch_bounds__(kSegThreads)
 segment_kernel(const int32_t* __restrict__ ids, int T, int n, int tbits, int passes, int cap,
                int32_t* __restrict__ seg_off, int32_t* __restrict__ perm,
-               int32_t* __restrict__ n_invalid, void* __restrict__ plan_ws) {
+               int32_t* __restrict__ n_invalid, void* __restrict__ plan_ws, size_t sub_off) {
   extern __shared__ uint32_t dyn[];
   __shared__ int s_cnt[kSegWaves][kDigits];
   __shared__ int s_base[kSegWaves][kDigits];
@@ -193,17 +218,18 @@ segment_kernel(const int32_t* __restrict__ ids, int T, int n, int tbits, int pas
   }
   if (tid == 0 && n_invalid != nullptr) *n_invalid = s_inval;
   __syncthreads();
-  build_tiles(so, n, plan_ws, s_wsum);
+  build_tiles(so, n, plan_ws, sub_off, s_wsum);
 }
 
 __global__ void __launch_bounds__(kSegThreads)
-plan_from_offsets_kernel(const int32_t* __restrict__ seg_off, int n, void* __restrict__ plan_ws) {
+plan_from_offsets_kernel(const int32_t* __restrict__ seg_off, int n, void* __restrict__ plan_ws,
+                         size_t sub_off) {
   extern __shared__ uint32_t dyn[];
   __shared__ int s_wsum[kSegWaves];
   int32_t* so = reinterpret_cast<int32_t*>(dyn);
   for (int b = threadIdx.x; b <= n; b += kSegThreads) so[b] = seg_off[b];
   __syncthreads();
-  build_tiles(so, n, plan_ws, s_wsum);
+  build_tiles(so, n, plan_ws, sub_off, s_wsum);
 }
 
 static int bits_for(int v) {  // smallest b >= 1 with 2^b > v
@@ -232,13 +258,12 @@ hipError_t launch_segment(const int32_t* ids, int T, int n, int32_t* seg_off, in
     raised = lds;
   }
   hipLaunchKernelGGL(segment_kernel, dim3(1), dim3(kSegThreads), lds, stream, ids, T, n, tbits, passes,
-                     cap, seg_off, perm, n_invalid, plan_ws);
+                     cap, seg_off, perm, n_invalid, plan_ws, plan_subtile_offset(T, n));
   return hipGetLastError();
 }
 
 hipError_t launch_plan_from_offsets(const int32_t* seg_off, int T, int n, void* plan_ws,
                                     hipStream_t stream) {
-  (void)T;
   const size_t lds = (size_t)(n + 2) * 4;
   static size_t raised = 64 * 1024;
   if (lds > raised) {
@@ -248,7 +273,7 @@ hipError_t launch_plan_from_offsets(const int32_t* seg_off, int T, int n, void* 
     raised = lds;
   }
   hipLaunchKernelGGL(plan_from_offsets_kernel, dim3(1), dim3(kSegThreads), lds, stream, seg_off, n,
-                     plan_ws);
+                     plan_ws, plan_subtile_offset(T, n));
   return hipGetLastError();
 }
 

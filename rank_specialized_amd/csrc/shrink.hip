@@ -5,142 +5,154 @@
 // 1 into a float32 buffer of shape [tokens, R]).  Rows of h follow the
 // grouped order, so one tile's rows are contiguous.
 //
-// One workgroup (4 waves) per tile (<= 64 tokens of one adapter).  The tile
-// is a skinny GEMM  H^T[r_a x m] = A_a[r_a x d_in] . X^T[d_in x m]  and runs
-// on 16x16 MFMA tiles whatever m is: the matrix core performs the d_in
-// reduction, so a one-token decode segment needs no cross-lane reduction;
-// rows j >= r_a and tokens >= m are never loaded (zero operands), so memory
-// traffic is exactly the retained rows plus the tile's x rows.
+// One workgroup of 16 waves per sub-tile (<= 16 tokens of one adapter).  A
+// sub-tile is the skinny GEMM  H^T[r_a x m] = A_a[r_a x d_in] . X^T[d_in x m]
+// on 16x16 MFMA tiles whatever m is: the matrix core does the d_in
+// reduction, so a one-token decode segment needs no cross-lane reduction.
+// Rows j >= r_a and tokens >= m are never loaded (zero operands): memory
+// traffic is the retained rows (once per sub-tile) plus the tile's x rows.
+// The 16 waves split d_in into 16 chunks, so even a decode batch of a few
+// hundred tokens spreads over thousands of waves, and a popular adapter's
+// tokens spread over several CUs (a CU's own bandwidth is the limit
+// otherwise).  The waves' float32 partial tiles are summed in LDS in a fixed
+// order (deterministic, no atomics) and written to h once.
 //
 // Rank specialization: NG = ceil(r_a / 16) row groups is a template
-// parameter, so each instantiation keeps exactly its accumulators and
-// issues its loads for several K-steps back to back.
+// parameter; each instantiation keeps exactly its accumulators and issues U
+// K-steps of loads back to back (U sized so the loads in flight fit the
+// register budget of a 1024-thread workgroup).
 //
-// K split: the 4 waves take consecutive quarters of d_in; inside a wave,
-// lane group g (lanes 16g..16g+15) owns a contiguous quarter of the wave's
-// range and walks it 16 bytes per step, so both operands of every MFMA
-// carry the same K indices (the contraction is a plain sum over K, so any
-// assignment of K indices to lane groups that is identical for the two
-// operands is exact).  The 4 partial tiles are summed in LDS in wave order
-// (deterministic).
+// Inside a wave, step s covers K indices [k0 + s * 32, +32) (bf16): lane
+// group g (lanes 16g..16g+15) takes the g-th 16 bytes of it, so the four lane
+// groups of a row read 64 contiguous bytes per instruction and two
+// consecutive steps consume whole 128-byte lines.  Both operands of every
+// MFMA carry the same K indices (the contraction is a plain sum over K, so
+// any K order that is identical for the two operands is exact).
 #include "device_common.h"
 #include "kernels.h"
 
 namespace lora {
 
-template <typename E, int NG>
-__device__ __forceinline__ void shrink_tile(const char* __restrict__ x, int64_t ldx_bytes,
-                                            const char* __restrict__ a_rows, int d_in, int r,
-                                            const int32_t* __restrict__ perm, int p0, int m,
-                                            float* __restrict__ h, int64_t ldh, f32x4_t* red) {
-  constexpr int V = E::kVec;
-  constexpr int KSTEP = 4 * V;              // K covered by one 16-byte chunk over the wave
-  constexpr int U = NG <= 1 ? 8 : (NG == 2 ? 4 : 2);  // K-steps issued back to back
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int i = lane & 15, g = lane >> 4;
-  const int steps_total = (d_in + KSTEP - 1) / KSTEP;
-  const int steps_w = (steps_total + 3) / 4;
-  const int k_lane0 = (w * steps_w * 4 + g * steps_w) * V;
-  const size_t a_row_bytes = (size_t)d_in * E::kBytes;
+constexpr int kShrinkWaves = 16;
+constexpr int kShrinkThreads = kShrinkWaves * kWave;
 
-  const char* arow[NG];
-  bool aval[NG];
+template <typename E, int NG>
+__device__ __forceinline__ void shrink_wave(const char* __restrict__ xrow, bool tval,
+                                            const char* __restrict__ a_rows, int d_in, int r, int k0,
+                                            int kc, f32x4_t* red_slot) {
+  constexpr int V = E::kVec;
+  constexpr int KSTEP = 4 * V;
+  constexpr int U = NG <= 2 ? 8 : 4;
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15, g = lane >> 4;
+  const int steps = kc / KSTEP;
+  const int kl = k0 + g * V;  // step s covers [k0 + s * KSTEP, +KSTEP): lane group g its g-th 16 bytes
+  const uint32_t a_row_bytes = (uint32_t)d_in * E::kBytes;
+  // The adapter's retained rows as one buffer: rows j >= r read as zero.
+  const rsrc_t ar = make_rsrc(a_rows, (uint32_t)r * a_row_bytes);
+  uint32_t aoff[NG];
 #pragma unroll
-  for (int q = 0; q < NG; ++q) {
-    const int j = q * 16 + i;
-    aval[q] = j < r;
-    arow[q] = a_rows + (size_t)(aval[q] ? j : 0) * a_row_bytes;
-  }
+  for (int q = 0; q < NG; ++q) aoff[q] = (uint32_t)(q * 16 + i) * a_row_bytes + (uint32_t)kl * E::kBytes;
+  f32x4_t acc[NG];
+#pragma unroll
+  for (int q = 0; q < NG; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const uint4 zero = make_uint4(0, 0, 0, 0);
-  const int nt = (m + 15) >> 4;
-  for (int u = 0; u < nt; ++u) {
-    const int tl = u * 16 + i;
-    const bool tval = tl < m;
-    const char* xrow = x + (int64_t)(tval ? perm[p0 + tl] : 0) * ldx_bytes;
-    f32x4_t acc[NG];
+  for (int s0 = 0; s0 < steps; s0 += U) {
+    uint4 bx[U], ba[U][NG];
 #pragma unroll
-    for (int q = 0; q < NG; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < steps_w; s0 += U) {
-      uint4 bx[U], ba[U][NG];
+    for (int uu = 0; uu < U; ++uu) {
+      const int s = s0 + uu;
+      const int k = kl + s * KSTEP;
+      const bool kv = s < steps && k < d_in;
+      bx[uu] = (tval && kv) ? ld16(xrow + (size_t)k * E::kBytes) : zero;
+      const uint32_t so = (uint32_t)(s * KSTEP * E::kBytes);
 #pragma unroll
-      for (int uu = 0; uu < U; ++uu) {
-        const int s = s0 + uu;
-        const int k = k_lane0 + s * V;
-        const bool kv = s < steps_w && k < d_in;
-        bx[uu] = (tval && kv) ? ld16(xrow + (size_t)k * E::kBytes) : zero;
-#pragma unroll
-        for (int q = 0; q < NG; ++q)
-          ba[uu][q] = (aval[q] && kv) ? ld16(arow[q] + (size_t)k * E::kBytes) : zero;
-      }
-#pragma unroll
-      for (int uu = 0; uu < U; ++uu)
-#pragma unroll
-        for (int q = 0; q < NG; ++q) acc[q] = mfma_chunk<E>(ba[uu][q], bx[uu], acc[q]);
+      for (int q = 0; q < NG; ++q) ba[uu][q] = buf_ld16(ar, kv ? aoff[q] + so : kOutOfRange, 0);
     }
-    if (w > 0) {
 #pragma unroll
-      for (int q = 0; q < NG; ++q) red[((w - 1) * NG + q) * 64 + lane] = acc[q];
-    }
-    __syncthreads();
-    if (w == 0) {
-      const int tok = u * 16 + i;  // output column of this lane
+    for (int uu = 0; uu < U; ++uu)
 #pragma unroll
-      for (int q = 0; q < NG; ++q) {
-        f32x4_t s = acc[q];
+      for (int q = 0; q < NG; ++q) acc[q] = mfma_chunk<E>(ba[uu][q], bx[uu], acc[q]);
+  }
 #pragma unroll
-        for (int ww = 1; ww < 4; ++ww) s += red[((ww - 1) * NG + q) * 64 + lane];
-        const int j0 = q * 16 + 4 * g;
-        if (tok < m && j0 < r) {
-          float* hr = h + (int64_t)(p0 + tok) * ldh + j0;
-          if (j0 + 0 < r) hr[0] = s[0];
-          if (j0 + 1 < r) hr[1] = s[1];
-          if (j0 + 2 < r) hr[2] = s[2];
-          if (j0 + 3 < r) hr[3] = s[3];
-        }
-      }
-    }
-    __syncthreads();
+  for (int q = 0; q < NG; ++q) red_slot[q * 64 + lane] = acc[q];
+}
+
+// red: [16 slots][ng_max][64 lanes] of f32x4; slot = wave = K chunk.
+template <typename E>
+__global__ void __launch_bounds__(kShrinkThreads)
+shrink_kernel(const char* __restrict__ x, int64_t ldx_bytes, const char* __restrict__ a_pack,
+              const int32_t* __restrict__ row_off, const int32_t* __restrict__ rank, int d_in, int ng_max,
+              const int32_t* __restrict__ perm, const void* __restrict__ plan_ws, size_t sub_off,
+              float* __restrict__ h, int64_t ldh) {
+  extern __shared__ f32x4_t red[];
+  constexpr int KSTEP = 4 * E::kVec;
+  const Plan pl = plan_view(plan_ws, sub_off);
+  const int t = blockIdx.x;  // grid = sub-tile capacity, so subtiles[t] is in bounds
+  const int4 tile = pl.subtiles[t];
+  const int count = pl.count[3];
+  if (t >= count) return;
+  const int a = tile.x, p0 = tile.y, m = tile.z;  // m <= kSubTile
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tl = lane & 15;
+  const bool tval = tl < m;
+  const int tok = tval ? perm[p0 + tl] : 0;
+  const int r = rank[a];
+  const int ro = row_off[a];
+  if (r <= 0) return;  // uniform over the workgroup
+  const int ng = (r + 15) >> 4;
+  int kc = (d_in + kShrinkWaves - 1) / kShrinkWaves;
+  kc = (kc + KSTEP - 1) / KSTEP * KSTEP;
+  const int k0 = w * kc;
+  const char* xrow = x + (int64_t)tok * ldx_bytes;
+  const char* a_rows = a_pack + (size_t)ro * d_in * E::kBytes;
+  f32x4_t* slot = red + w * ng_max * 64;
+  switch (ng) {
+    case 1: shrink_wave<E, 1>(xrow, tval, a_rows, d_in, r, k0, kc, slot); break;
+    case 2: shrink_wave<E, 2>(xrow, tval, a_rows, d_in, r, k0, kc, slot); break;
+    case 3: shrink_wave<E, 3>(xrow, tval, a_rows, d_in, r, k0, kc, slot); break;
+    default: shrink_wave<E, 4>(xrow, tval, a_rows, d_in, r, k0, kc, slot); break;
+  }
+  __syncthreads();
+  // Sum the 16 slots of each (row group, lane, accumulator row) in slot order
+  // and write h.  Lane l of a partial tile holds token l % 16 and rank rows
+  // 4 * (l / 16) + 0..3 of its row group.
+  const float* redf = reinterpret_cast<const float*>(red);
+  for (int c = threadIdx.x; c < ng * 256; c += kShrinkThreads) {
+    const int v = c & 3, l = (c >> 2) & 63, q = c >> 8;
+    const int tk = l & 15;
+    const int j = q * 16 + 4 * (l >> 4) + v;
+    if (tk >= m || j >= r) continue;
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < kShrinkWaves; ++k) s += redf[((k * ng_max + q) * 64 + l) * 4 + v];
+    h[(int64_t)(p0 + tk) * ldh + j] = s;
   }
 }
 
-template <typename E>
-__global__ void __launch_bounds__(256)
-shrink_kernel(const char* __restrict__ x, int64_t ldx_bytes, const char* __restrict__ a_pack,
-              const int32_t* __restrict__ row_off, const int32_t* __restrict__ rank, int d_in,
-              const int32_t* __restrict__ perm, const void* __restrict__ plan_ws,
-              float* __restrict__ h, int64_t ldh) {
-  __shared__ f32x4_t red[3 * 4 * 64];
-  const Plan pl = plan_view(plan_ws);
-  const int t = blockIdx.x;
-  if (t >= *pl.count) return;
-  const int4 tile = pl.tiles[t];
-  const int a = tile.x, p0 = tile.y, m = tile.z;
-  const int r = rank[a];
-  if (r <= 0) return;
-  const char* a_rows = a_pack + (size_t)row_off[a] * d_in * E::kBytes;
-  switch ((r + 15) >> 4) {
-    case 1: shrink_tile<E, 1>(x, ldx_bytes, a_rows, d_in, r, perm, p0, m, h, ldh, red); break;
-    case 2: shrink_tile<E, 2>(x, ldx_bytes, a_rows, d_in, r, perm, p0, m, h, ldh, red); break;
-    case 3: shrink_tile<E, 3>(x, ldx_bytes, a_rows, d_in, r, perm, p0, m, h, ldh, red); break;
-    default: shrink_tile<E, 4>(x, ldx_bytes, a_rows, d_in, r, perm, p0, m, h, ldh, red); break;
-  }
+size_t shrink_lds_bytes(int r_max) {
+  const int ng_max = r_max <= 0 ? 1 : (r_max + 15) / 16;
+  return (size_t)kShrinkWaves * ng_max * 64 * sizeof(float) * 4;
 }
 
 hipError_t launch_shrink(const lora_store& s, const void* x, int64_t ldx, int T, const int32_t* perm,
                          const void* plan_ws, float* h, int64_t ldh, hipStream_t stream) {
-  const int64_t grid = plan_max_tiles(T, s.n);
-  if (grid == 0) return hipSuccess;
+  const int64_t subs = plan_max_subtiles(T, s.n);
+  if (subs == 0) return hipSuccess;
+  const int ng_max = s.r_max <= 0 ? 1 : (s.r_max + 15) / 16;
+  const size_t lds = shrink_lds_bytes(s.r_max);
+  const size_t sub_off = plan_subtile_offset(T, s.n);
   const int eb = elem_bytes(s.dtype);
   if (s.dtype == LORA_DTYPE_BF16)
-    hipLaunchKernelGGL(shrink_kernel<BF16>, dim3((unsigned)grid), dim3(256), 0, stream,
+    hipLaunchKernelGGL(shrink_kernel<BF16>, dim3((unsigned)subs), dim3(kShrinkThreads), lds, stream,
                        reinterpret_cast<const char*>(x), ldx * eb,
-                       reinterpret_cast<const char*>(s.A_pack), s.row_off, s.rank, s.d_in, perm,
-                       plan_ws, h, ldh);
+                       reinterpret_cast<const char*>(s.A_pack), s.row_off, s.rank, s.d_in, ng_max, perm,
+                       plan_ws, sub_off, h, ldh);
   else
-    hipLaunchKernelGGL(shrink_kernel<F32>, dim3((unsigned)grid), dim3(256), 0, stream,
+    hipLaunchKernelGGL(shrink_kernel<F32>, dim3((unsigned)subs), dim3(kShrinkThreads), lds, stream,
                        reinterpret_cast<const char*>(x), ldx * eb,
-                       reinterpret_cast<const char*>(s.A_pack), s.row_off, s.rank, s.d_in, perm,
-                       plan_ws, h, ldh);
+                       reinterpret_cast<const char*>(s.A_pack), s.row_off, s.rank, s.d_in, ng_max, perm,
+                       plan_ws, sub_off, h, ldh);
   return hipGetLastError();
 }
 

@@ -111,8 +111,9 @@ def test_pack_rejects_before_launch(lib):
 
 def test_segment_ws_bytes(lib):
     assert lib.lora_segment_ws_bytes(0, 4) == 64
-    # T=100, n=3: at most (100 + 63*3)//64 = 4 tiles
-    assert lib.lora_segment_ws_bytes(100, 3) == 64 + 16 * 4
+    # T=100, n=3: at most (100 + 63*3)//64 = 4 expand tiles of <= 64 tokens
+    # and (100 + 15*3)//16 = 9 shrink sub-tiles of <= 16 tokens
+    assert lib.lora_segment_ws_bytes(100, 3) == 64 + 16 * 4 + 16 * 9
     assert lib.lora_segment_ws_bytes(-1, 3) == 0
 
 

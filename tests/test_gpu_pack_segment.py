@@ -59,18 +59,37 @@ def test_pack_roundtrip(case):
     assert np.array_equal(sc.cpu().numpy(), wl.module.scales)
 
 
+def _plan_offsets(T, n):
+    max_tiles = (T + 63 * min(n, T)) // 64 if T > 0 else 0
+    return 64, 64 + 16 * max_tiles
+
+
 def _check_plan(seg, n):
+    """Expand tiles (<= 64 tokens; tiles of more than 4 tokens first) and
+    shrink sub-tiles (<= 16 tokens) each cover every grouped token of a real
+    adapter exactly once; each list is in (adapter, position) order."""
     ws = seg.ws.cpu().numpy()
-    count = int(ws[:4].view(np.int32)[0])
-    tiles = ws[64: 64 + 16 * count].view(np.int32).reshape(count, 4)
+    hdr = ws[:64].view(np.int32)
+    count, n_large, n_small, n_sub = int(hdr[0]), int(hdr[1]), int(hdr[2]), int(hdr[3])
+    assert count == n_large + n_small
+    t_off, s_off = _plan_offsets(seg.T, n)
+    tiles = ws[t_off: t_off + 16 * count].view(np.int32).reshape(count, 4)
+    subs = ws[s_off: s_off + 16 * n_sub].view(np.int32).reshape(n_sub, 4)
     so = seg.seg_off.cpu().numpy()
-    covered = []
-    for a, p0, m, _ in tiles:
-        assert 0 <= a < n and 1 <= m <= rs._lib.LORA_TILE_TOKENS
-        assert so[a] <= p0 and p0 + m <= so[a + 1]
-        covered.extend(range(p0, p0 + m))
-    assert covered == list(range(int(so[n])))  # every grouped token of a real adapter, once, in order
-    return tiles
+    for lst, cap, large in ((tiles, rs._lib.LORA_TILE_TOKENS, n_large), (subs, 16, None)):
+        covered = []
+        for k, (a, p0, m, _) in enumerate(lst):
+            assert 0 <= a < n and 1 <= m <= cap
+            if large is not None:
+                assert (m > 4) == (k < large)
+            assert so[a] <= p0 and p0 + m <= so[a + 1]
+            assert (p0 - so[a]) % cap == 0
+            covered.extend(range(p0, p0 + m))
+        assert sorted(covered) == list(range(int(so[n])))
+    for part in (tiles[:n_large], tiles[n_large:], subs):
+        keys = [(int(a), int(p)) for a, p, _, _ in part]
+        assert keys == sorted(keys)
+    return np.concatenate([tiles.ravel(), subs.ravel()])
 
 
 def _segment_case(name):
