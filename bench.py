@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "LoRA-delta tokens/s and achieved HBM GB/s (% of ~8 TB/s peak), 1 MI355X"
 PEAK_GBPS = 8000.0
 COLD_BYTES = 2.0e9  # rotation set size: well past the 256 MB Infinity Cache
-KERNEL_SOURCES = ["shrink.hip", "expand.hip", "segment.hip", "device_common.h"]
+KERNEL_SOURCES = ["shrink.hip", "expand.hip", "segment.hip", "fused.hip", "tile_ops.h", "device_common.h"]
 
 WORKLOAD_NAMES = {
     "1": "tiny-fp32: d_in=d_out=256 f32, 4 adapters ranks {1,2,3,4}, T=16",

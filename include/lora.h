@@ -225,8 +225,12 @@ size_t lora_apply_ws_bytes(const lora_store* store_host, int T, int with_segment
  * Either ids (then the grouping is computed into ws), or ids = NULL and
  * seg_off / perm / seg_ws from a previous lora_segment (one grouping reused
  * across many stores, e.g. every projection of a decode step).
- * Equivalent to lora_segment (when ids is given), lora_shrink, lora_expand,
- * bit for bit.  Errors: union of those calls'.
+ * Computes what lora_segment (when ids is given), lora_shrink and
+ * lora_expand compute.  On decode-shaped batches (T <= 8 n) the shrink and
+ * expand of each sub-tile run fused in one workgroup with the float32
+ * intermediate kept on chip; float32 sums may then be formed in a different
+ * order than the separate calls (results agree to float32 rounding; exact
+ * integer-valued inputs give identical bits).  Errors: union of those calls'.
  */
 int lora_apply_batched(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy,
                        int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm,

@@ -118,7 +118,7 @@ int lora_segment(const int32_t* ids, int T, int n, int32_t* seg_off, int32_t* pe
   int max_lds = 0;
   hipError_t e = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, 0);
   if (e != hipSuccess) return hip_fail(e);
-  if (segment_lds_bytes(T, n) > (size_t)max_lds) return LORA_ERR_UNSUPPORTED;
+  if (segment_lds_bytes(T, n) + segment_static_lds_bytes() > (size_t)max_lds) return LORA_ERR_UNSUPPORTED;
   e = launch_segment(ids, T, n, seg_off, perm, n_invalid, ws, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? LORA_OK : hip_fail(e);
 }
@@ -207,11 +207,16 @@ int lora_apply_batched(const lora_store* store_host, const void* x, int64_t ldx,
   } else {
     if ((st = check_plan_args(store_host, T, seg_off, perm, seg_ws, seg_ws_bytes)) != LORA_OK) return st;
   }
-  float* h = reinterpret_cast<float*>(base);
-  const int64_t ldh = apply_ldh(s.r_max);
-  hipError_t e = launch_shrink(s, x, ldx, T, perm, plan, h, ldh, strm);
-  if (e != hipSuccess) return hip_fail(e);
-  e = launch_expand(s, h, ldh, T, perm, plan, y, ldy, strm);
+  hipError_t e;
+  if (use_fused_apply(T, s.n)) {
+    e = launch_apply_fused(s, x, ldx, T, perm, plan, y, ldy, strm);
+  } else {
+    float* h = reinterpret_cast<float*>(base);
+    const int64_t ldh = apply_ldh(s.r_max);
+    e = launch_shrink(s, x, ldx, T, perm, plan, h, ldh, strm);
+    if (e != hipSuccess) return hip_fail(e);
+    e = launch_expand(s, h, ldh, T, perm, plan, y, ldy, strm);
+  }
   return e == hipSuccess ? LORA_OK : hip_fail(e);
 }
 

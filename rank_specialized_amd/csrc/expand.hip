@@ -11,13 +11,13 @@
 // run of consecutive tiles: tiles of one popular adapter share that run's
 // Bt rows through the CU's cache.
 //  * Tiles of more than kSmallTile tokens (prefill segments, popular decode
-//    adapters) run on the matrix cores: for a run of 64 features,
-//    Y^T[o, t] = Bt^T[o, j] . H^T[j, t] on bf16 16x16x32 MFMA.  h is float32
-//    and is fed as the exact sum of two bf16 values (hi = nearest bf16 of h,
+//    adapters) run on the matrix cores: for a run of 128 features,
+//    Y[t, o] = H[t, j] . Bt[j, o] on bf16 16x16x32 MFMA.  h is float32 and
+//    is fed as the exact sum of two bf16 values (hi = nearest bf16 of h,
 //    lo = nearest bf16 of h - hi), so the product keeps about 16 significant
-//    bits of h instead of 8.  M rows are permuted so that each lane ends with
-//    16 consecutive features of one token: y is read and written with
-//    16-byte accesses.
+//    bits of h instead of 8.  N columns are permuted so that each lane ends
+//    with 16 consecutive bytes of features of 4 tokens: a y row is read and
+//    written as 256 contiguous bytes by 16 lanes.
 //  * Small tiles (decode: a few tokens per adapter) run on the vector ALUs
 //    over a run of 64 x 16 bytes of features: a lane owns 16 bytes of
 //    outputs; the tile's y rows and a rank chunk of Bt rows (one coalesced
@@ -31,92 +31,16 @@
 // loaded); the matrix path per number of 32-deep K steps (1 or 2).
 #include "device_common.h"
 #include "kernels.h"
+#include "tile_ops.h"
 
 namespace lora {
 
 constexpr int kExpandThreads = 256;
-constexpr int kLargeRun = 64;  // output features per matrix-path item
-
-// ------------------------------------------------------------ vector path
-template <typename E, int RB>
-__device__ __forceinline__ void expand_small(const char* __restrict__ bt_rows, int d_out, int r, float s,
-                                             const float* __restrict__ hrows, int64_t ldh,
-                                             const int32_t* __restrict__ perm, int p0, int m,
-                                             char* __restrict__ y, int64_t ldy_bytes, int o) {
-  constexpr int V = E::kVec;
-  constexpr int MT = kSmallTile;
-  constexpr int JN = RB < 16 ? RB : 16;
-  const bool active = o < d_out;
-  const uint32_t bt_row_bytes = (uint32_t)d_out * E::kBytes;
-  // The adapter's Bt rows as one buffer; inactive lanes read zeros.
-  const rsrc_t br = make_rsrc(bt_rows, (uint32_t)r * bt_row_bytes);
-  const uint32_t boff = active ? (uint32_t)o * E::kBytes : kOutOfRange;
-  const uint4 zero = make_uint4(0, 0, 0, 0);
-  uint4 yv[MT];
-  char* yp[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    yp[t] = (t < m) ? y + (int64_t)perm[p0 + t] * ldy_bytes + (size_t)o * E::kBytes : nullptr;
-    yv[t] = (active && t < m) ? ld16(yp[t]) : zero;
-  }
-  float acc[MT][V];
-#pragma unroll
-  for (int t = 0; t < MT; ++t)
-#pragma unroll
-    for (int e = 0; e < V; ++e) acc[t][e] = 0.f;
-#pragma unroll 1
-  for (int j0 = 0; j0 < RB; j0 += JN) {
-    if (j0 >= r) break;
-    uint4 b[JN];
-#pragma unroll
-    for (int jj = 0; jj < JN; ++jj)
-      b[jj] = (j0 + jj < r) ? buf_ld16(br, boff, (uint32_t)(j0 + jj) * bt_row_bytes) : zero;
-#pragma unroll
-    for (int jj = 0; jj < JN; ++jj) {
-      if (j0 + jj < r) {
-        float bf[V];
-        E::widen(b[jj], bf);
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          if (t < m) {
-            const float hv = hrows[(int64_t)t * ldh + j0 + jj];
-#pragma unroll
-            for (int e = 0; e < V; ++e) acc[t][e] += hv * bf[e];
-          }
-        }
-      }
-    }
-  }
-  if (!active) return;
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    if (t < m) {
-      float yf[V];
-      E::widen(yv[t], yf);
-#pragma unroll
-      for (int e = 0; e < V; ++e) yf[e] = yf[e] + s * acc[t][e];
-      st16(yp[t], E::narrow(yf));
-    }
-  }
-}
+constexpr int kLargeRun = 128;  // output features per matrix-path item (one wave)
 
 // ------------------------------------------------------------ matrix path
-// A-operand fragment of Bt^T for one output feature: Bt[jbase + e][o],
-// e = 0..7, from the adapter's Bt buffer (rows j >= r read as zero; voff =
-// byte offset of (jbase, o); the row step rides in the uniform offset).
-__device__ __forceinline__ uint4 bt_fragment(rsrc_t br, uint32_t voff, uint32_t row_bytes) {
-  uint32_t w[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(br, voff, (2 * p) * row_bytes, 0);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(br, voff, (2 * p + 1) * row_bytes, 0);
-    w[p] = lo | (hi << 16);
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
-// B-operand fragments of H^T from 8 consecutive float32 h values (columns
-// jbase..jbase+7 of one token): columns >= r are zeroed (the shrink leaves
+// A-operand fragment of H: 8 consecutive float32 h values (columns
+// jbase..jbase+7 of one token); columns >= r are zeroed (the shrink leaves
 // them unwritten), then each value is split into the exact pair hi + lo of
 // bf16 values.
 __device__ __forceinline__ void h_fragment(const uint4& q0, const uint4& q1, int r, int jbase, uint4& hi,
@@ -136,110 +60,132 @@ __device__ __forceinline__ void h_fragment(const uint4& q0, const uint4& q1, int
   lo = make_uint4(wl[0], wl[1], wl[2], wl[3]);
 }
 
-// One wave: 64 output features (4 M-tiles) of one tile, all of its tokens.
-// M-tile mm, row i holds output o_w + 16 (i / 4) + 4 mm + (i % 4), so the
-// accumulator rows 4 g + v of lane (i, g) are outputs o_w + 16 g + 4 mm + v:
-// 16 consecutive features of token i per lane.  The loads of NB token groups
-// (y and h) and the Bt fragments are issued before any MFMA, so a wave keeps
-// up to ~10 KB in flight.
+// Per-wave LDS slice of Bt: rows j < 64 of 128 features (256 bytes) plus 16
+// bytes of padding, so the four lane groups of a transposed read fall in
+// different banks.
+constexpr int kSliceStride = 272;
+constexpr int kSliceBytes = 64 * kSliceStride;
+
+// One wave: 128 output features of one tile, all of its tokens.
+//   D[token, feature] = H[token, j] . Bt[j, feature]  on bf16 16x16x32 MFMA,
+// eight N-tiles per 16-token M-tile.  N-tile nt, column n is feature
+// o_w + 8 n + nt, so lane (n, g) accumulates features o_w + 8n .. o_w + 8n + 7
+// (16 bytes) of tokens 4g .. 4g + 3 of the M-tile: a y row is read and written
+// as 256 contiguous bytes by 16 lanes.
+//   The Bt slice [r x 128] is staged in LDS with coalesced 16-byte loads and
+// read back transposed (8 rank indices of one feature per lane).
 template <int KS>
-__device__ __forceinline__ void expand_large(const uint16_t* __restrict__ bt, int d_out, int r, float s,
+__device__ __forceinline__ void expand_large(const char* __restrict__ bt_rows, int d_out, int r, float s,
                                              const float* __restrict__ hrows, int64_t ldh,
                                              const int32_t* __restrict__ perm, int p0, int m,
-                                             char* __restrict__ y, int64_t ldy_bytes, int o_w) {
-  constexpr int NB = KS == 1 ? 4 : 2;  // token groups of 16 whose loads are in flight together
+                                             char* __restrict__ y, int64_t ldy_bytes, int o_w,
+                                             char* __restrict__ slice) {
   const int lane = threadIdx.x & 63;
-  const int i = lane & 15, g = lane >> 4;
+  const int n = lane & 15, g = lane >> 4;
   const uint32_t row_bytes = (uint32_t)d_out * 2;
-  const rsrc_t br = make_rsrc(bt, (uint32_t)r * row_bytes);
+  const rsrc_t br = make_rsrc(bt_rows, (uint32_t)r * row_bytes);
+  const int col = o_w + 8 * n;  // first feature of this lane's 16 bytes
+  const bool cv = col < d_out;
+  // Stage Bt rows 0 .. 32 KS - 1 (rows >= r and features >= d_out as zeros).
+  {
+    uint4 v[8 * KS];
+#pragma unroll
+    for (int q = 0; q < 8 * KS; ++q) {
+      const int j = 4 * q + g;
+      v[q] = buf_ld16(br, (j < r && cv) ? (uint32_t)j * row_bytes + (uint32_t)col * 2 : kOutOfRange, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 8 * KS; ++q)
+      *reinterpret_cast<uint4*>(slice + (4 * q + g) * kSliceStride + 16 * n) = v[q];
+  }
+  __builtin_amdgcn_wave_barrier();
+  // B-operand fragments (rebuilt from LDS per M-tile and K step): lane
+  // (n, g), N-tile nt holds Bt[32 ks + 8 g + e][col(n) + nt], e = 0..7.
+  const uint16_t* sl = reinterpret_cast<const uint16_t*>(slice) + 8 * n;
+  auto bfrag = [&](int ks, int nt) {
+    uint32_t w[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int j = 32 * ks + 8 * g + 2 * p;
+      const uint32_t lo = sl[(j * kSliceStride) / 2 + nt];
+      const uint32_t hi = sl[((j + 1) * kSliceStride) / 2 + nt];
+      w[p] = lo | (hi << 16);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  };
   // The tile's h rows as one buffer: tokens >= m read as zero.
   const uint32_t h_row_bytes = (uint32_t)ldh * 4;
   const rsrc_t hr = make_rsrc(hrows, (uint32_t)m * h_row_bytes);
-  const int o_lane = o_w + 16 * g;
-  const bool ov0 = o_lane < d_out, ov1 = o_lane + 8 < d_out;
-  uint4 af[4][KS];
+  // The y rows this lane touches for NB token groups (tokens 16 u + 4 g + v)
+  // are loaded before any matrix work: 16 bytes x 4 NB rows per lane in flight.
+  constexpr int NB = KS == 1 ? 4 : 2;
   for (int u0 = 0; u0 < m; u0 += 16 * NB) {
-    // y rows and h of NB token groups.
-    int prow[NB];
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int tok = u0 + u * 16 + i;
-      prow[u] = tok < m ? perm[p0 + tok] : -1;
-    }
-    uint4 hq[NB][KS][2];
+    int prow[NB][4];
+    uint4 yv[NB][4];
 #pragma unroll
     for (int u = 0; u < NB; ++u)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint32_t voff = (uint32_t)(u0 + u * 16 + i) * h_row_bytes + (uint32_t)(32 * ks + 8 * g) * 4;
-        hq[u][ks][0] = buf_ld16(hr, voff, 0);
-        hq[u][ks][1] = buf_ld16(hr, voff + 16, 0);
+      for (int v = 0; v < 4; ++v) {
+        const int tok = u0 + 16 * u + 4 * g + v;
+        prow[u][v] = (tok < m && cv) ? perm[p0 + tok] : -1;
       }
-    char* yrow[NB];
-    uint4 y0[NB], y1[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        yv[u][v] = prow[u][v] >= 0 ? ld16(y + (int64_t)prow[u][v] * ldy_bytes + (size_t)col * 2)
+                                   : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int u = 0; u < NB; ++u) {
-      const bool tv = prow[u] >= 0;
-      yrow[u] = y + (int64_t)(tv ? prow[u] : 0) * ldy_bytes;
-      y0[u] = (tv && ov0) ? ld16(yrow[u] + (size_t)o_lane * 2) : make_uint4(0, 0, 0, 0);
-      y1[u] = (tv && ov1) ? ld16(yrow[u] + (size_t)(o_lane + 8) * 2) : make_uint4(0, 0, 0, 0);
-    }
-    if (u0 == 0) {
-#pragma unroll
-      for (int mm = 0; mm < 4; ++mm) {
-        const int o = o_w + 16 * (i >> 2) + 4 * mm + (i & 3);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const uint32_t voff = o < d_out ? (uint32_t)(32 * ks + 8 * g) * row_bytes + (uint32_t)o * 2
-                                          : kOutOfRange;
-          af[mm][ks] = bt_fragment(br, voff, row_bytes);
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      if (u0 + u * 16 >= m) break;
-      const bool tv = prow[u] >= 0;
-      f32x4_t acc[4];
-#pragma unroll
-      for (int mm = 0; mm < 4; ++mm) acc[mm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int t0 = u0 + 16 * u;
+      if (t0 >= m) break;
+      uint4 hq[KS][2];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        uint4 bh, bl;
-        h_fragment(hq[u][ks][0], hq[u][ks][1], r, 32 * ks + 8 * g, bh, bl);
+        const uint32_t voff = (uint32_t)(t0 + n) * h_row_bytes + (uint32_t)(32 * ks + 8 * g) * 4;
+        hq[ks][0] = buf_ld16(hr, voff, 0);
+        hq[ks][1] = buf_ld16(hr, voff + 16, 0);
+      }
+      f32x4_t acc[8];
 #pragma unroll
-        for (int mm = 0; mm < 4; ++mm) {
-          acc[mm] = mfma_bf16_16x16x32(af[mm][ks], bh, acc[mm]);
-          acc[mm] = mfma_bf16_16x16x32(af[mm][ks], bl, acc[mm]);
+      for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 ah, al;
+        h_fragment(hq[ks][0], hq[ks][1], r, 32 * ks + 8 * g, ah, al);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          const uint4 b = bfrag(ks, nt);
+          acc[nt] = mfma_bf16_16x16x32(ah, b, acc[nt]);
+          acc[nt] = mfma_bf16_16x16x32(al, b, acc[nt]);
         }
       }
-      if (tv && ov0) {
-        float f[8];
-        BF16::widen(y0[u], f);
+      // acc[nt][v] = feature col + nt of token t0 + 4 g + v.
 #pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = f[e] + s * acc[e >> 2][e & 3];
-        st16(yrow[u] + (size_t)o_lane * 2, BF16::narrow(f));
-      }
-      if (tv && ov1) {
-        float f[8];
-        BF16::widen(y1[u], f);
+      for (int v = 0; v < 4; ++v) {
+        if (prow[u][v] >= 0) {
+          float f[8];
+          BF16::widen(yv[u][v], f);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = f[e] + s * acc[2 + (e >> 2)][e & 3];
-        st16(yrow[u] + (size_t)(o_lane + 8) * 2, BF16::narrow(f));
+          for (int e = 0; e < 8; ++e) f[e] = f[e] + s * acc[e][v];
+          st16(y + (int64_t)prow[u][v] * ldy_bytes + (size_t)col * 2, BF16::narrow(f));
+        }
       }
     }
   }
+  __builtin_amdgcn_wave_barrier();  // the slice is rewritten by this wave's next item
 }
 
 // ------------------------------------------------------------------ kernel
 template <typename E>
 __global__ void __launch_bounds__(kExpandThreads)
-expand_kernel(const float* __restrict__ h, int64_t ldh, const char* __restrict__ bt_pack,
+__attribute__((amdgpu_waves_per_eu(2, 8))) expand_kernel(const float* __restrict__ h, int64_t ldh, const char* __restrict__ bt_pack,
               const int32_t* __restrict__ row_off, const int32_t* __restrict__ rank,
               const float* __restrict__ scale, int d_out, const int32_t* __restrict__ perm,
               const void* __restrict__ plan_ws, char* __restrict__ y, int64_t ldy_bytes) {
   constexpr int V = E::kVec;
   constexpr bool kMatrix = E::kBytes == 2;  // f32 stores always take the vector path
+  __shared__ __attribute__((aligned(16))) char slices[kMatrix ? 4 * kSliceBytes : 16];
   const Plan pl = plan_view(plan_ws, 0);  // expand tiles only
   const int n_all = pl.count[0];
   const int n_large = kMatrix ? pl.count[1] : 0;
@@ -252,12 +198,15 @@ expand_kernel(const float* __restrict__ h, int64_t ldh, const char* __restrict__
   const int64_t stride = (int64_t)gridDim.x * (kExpandThreads / 64);
   for (int64_t item = (int64_t)blockIdx.x * (kExpandThreads / 64) + (threadIdx.x >> 6); item < items;
        item += stride) {
-    const bool large = item < large_items;
-    int t, run;
-    if (large) {
-      run = (int)(item / n_large);
-      t = (int)(item - (int64_t)run * n_large);
-    } else {
+    const bool large = kMatrix && item < large_items;
+    int t = 0, run = 0;
+    if constexpr (kMatrix) {
+      if (large) {
+        run = (int)(item / n_large);
+        t = (int)(item - (int64_t)run * n_large);
+      }
+    }
+    if (!large) {
       const int64_t it = item - large_items;
       run = (int)(it / n_small);
       t = n_large + (int)(it - (int64_t)run * n_small);
@@ -271,10 +220,10 @@ expand_kernel(const float* __restrict__ h, int64_t ldh, const char* __restrict__
     const float* hrows = h + (int64_t)p0 * ldh;
     if (large) {
       if constexpr (kMatrix) {
-        const uint16_t* bt = reinterpret_cast<const uint16_t*>(bt_rows);
         const int o_w = run * kLargeRun;
-        if (r <= 32) expand_large<1>(bt, d_out, r, sc, hrows, ldh, perm, p0, m, y, ldy_bytes, o_w);
-        else expand_large<2>(bt, d_out, r, sc, hrows, ldh, perm, p0, m, y, ldy_bytes, o_w);
+        char* slice = slices + (threadIdx.x >> 6) * kSliceBytes;
+        if (r <= 32) expand_large<1>(bt_rows, d_out, r, sc, hrows, ldh, perm, p0, m, y, ldy_bytes, o_w, slice);
+        else expand_large<2>(bt_rows, d_out, r, sc, hrows, ldh, perm, p0, m, y, ldy_bytes, o_w, slice);
       }
     } else {
       const int o = (run * 64 + lane) * V;

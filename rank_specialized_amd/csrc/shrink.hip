@@ -30,53 +30,12 @@
 // any K order that is identical for the two operands is exact).
 #include "device_common.h"
 #include "kernels.h"
+#include "tile_ops.h"
 
 namespace lora {
 
 constexpr int kShrinkWaves = 16;
 constexpr int kShrinkThreads = kShrinkWaves * kWave;
-
-template <typename E, int NG>
-__device__ __forceinline__ void shrink_wave(const char* __restrict__ xrow, bool tval,
-                                            const char* __restrict__ a_rows, int d_in, int r, int k0,
-                                            int kc, f32x4_t* red_slot) {
-  constexpr int V = E::kVec;
-  constexpr int KSTEP = 4 * V;
-  constexpr int U = NG <= 2 ? 8 : 4;
-  const int lane = threadIdx.x & 63;
-  const int i = lane & 15, g = lane >> 4;
-  const int steps = kc / KSTEP;
-  const int kl = k0 + g * V;  // step s covers [k0 + s * KSTEP, +KSTEP): lane group g its g-th 16 bytes
-  const uint32_t a_row_bytes = (uint32_t)d_in * E::kBytes;
-  // The adapter's retained rows as one buffer: rows j >= r read as zero.
-  const rsrc_t ar = make_rsrc(a_rows, (uint32_t)r * a_row_bytes);
-  uint32_t aoff[NG];
-#pragma unroll
-  for (int q = 0; q < NG; ++q) aoff[q] = (uint32_t)(q * 16 + i) * a_row_bytes + (uint32_t)kl * E::kBytes;
-  f32x4_t acc[NG];
-#pragma unroll
-  for (int q = 0; q < NG; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const uint4 zero = make_uint4(0, 0, 0, 0);
-  for (int s0 = 0; s0 < steps; s0 += U) {
-    uint4 bx[U], ba[U][NG];
-#pragma unroll
-    for (int uu = 0; uu < U; ++uu) {
-      const int s = s0 + uu;
-      const int k = kl + s * KSTEP;
-      const bool kv = s < steps && k < d_in;
-      bx[uu] = (tval && kv) ? ld16(xrow + (size_t)k * E::kBytes) : zero;
-      const uint32_t so = (uint32_t)(s * KSTEP * E::kBytes);
-#pragma unroll
-      for (int q = 0; q < NG; ++q) ba[uu][q] = buf_ld16(ar, kv ? aoff[q] + so : kOutOfRange, 0);
-    }
-#pragma unroll
-    for (int uu = 0; uu < U; ++uu)
-#pragma unroll
-      for (int q = 0; q < NG; ++q) acc[q] = mfma_chunk<E>(ba[uu][q], bx[uu], acc[q]);
-  }
-#pragma unroll
-  for (int q = 0; q < NG; ++q) red_slot[q * 64 + lane] = acc[q];
-}
 
 // red: [16 slots][ng_max][64 lanes] of f32x4; slot = wave = K chunk.
 template <typename E>

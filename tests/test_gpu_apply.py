@@ -94,18 +94,42 @@ def test_shrink_h_within_fp32_bound(key):
 
 @pytest.mark.parametrize("key", ["1", "3", "4"])
 def test_shrink_then_expand_equals_apply(key):
+    """The separate calls and the batched apply compute the same result:
+    bit for bit on the separate-kernel (prefill) path, to float32 rounding on
+    the fused (decode) path, and bit for bit on exact integer inputs."""
     dev = device()
-    wl = make_config(key)
+    for integer in (False, True):
+        wl = make_config(key, integer=integer)
+        store = pack(wl, dev)
+        x, ids, y1 = inputs(wl, dev)
+        y2 = y1.clone()
+        note(f"compose {key} integer={integer}")
+        rs.lora_apply_batched(store, x, y1, ids=ids)
+        seg = rs.lora_segment(ids, store.n)
+        h = rs.lora_shrink(store, x, seg)
+        rs.lora_expand(store, h, seg, y2)
+        torch.cuda.synchronize()
+        fused = wl.T <= 8 * wl.n
+        if integer or not fused:
+            assert np.array_equal(hbits(y1), hbits(y2))
+        else:
+            a, b = y_host(y1), y_host(y2)
+            assert np.abs(a - b).max() <= 1e-5 * np.abs(b).max() + 1e-30 if wl.dtype == "fp32" else \
+                np.abs(a - b).max() <= 2.0 ** -7 * np.abs(b).max()
+
+
+def test_separate_kernels_integer_exact_decode():
+    """The standalone shrink + expand (not the fused path) on a decode shape."""
+    dev = device()
+    wl = make_config("3", integer=True)
     store = pack(wl, dev)
-    x, ids, y1 = inputs(wl, dev)
-    y2 = y1.clone()
-    note(f"compose {key}")
-    rs.lora_apply_batched(store, x, y1, ids=ids)
+    x, ids, y = inputs(wl, dev)
+    note("separate kernels decode integer")
     seg = rs.lora_segment(ids, store.n)
     h = rs.lora_shrink(store, x, seg)
-    rs.lora_expand(store, h, seg, y2)
+    rs.lora_expand(store, h, seg, y)
     torch.cuda.synchronize()
-    assert np.array_equal(hbits(y1), hbits(y2))
+    assert np.array_equal(y_host(y), bf16_round_ref(_ref(wl)))
 
 
 @pytest.mark.parametrize("key", ["1", "3", "4"])
