@@ -4,7 +4,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
 
 A step is one pass of the whole hot path over one batch: token grouping,
-shrink and expand, i.e. one lora_apply_batched call with adapter ids, on
+shrink and expand, i.e. one lora_apply_batched call with adapter ids (two
+kernels: the shrink, which also groups the tokens, and the expand), on
 inputs already resident in HBM.  Steps rotate through independent copies of
 (store, x, y) whose total size exceeds the 256 MB last-level cache, so every
 step reads its factors and activations from HBM (cold-HBM timing).
@@ -33,7 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "LoRA-delta tokens/s and achieved HBM GB/s (% of ~8 TB/s peak), 1 MI355X"
 PEAK_GBPS = 8000.0
 COLD_BYTES = 2.0e9  # rotation set size: well past the 256 MB Infinity Cache
-KERNEL_SOURCES = ["shrink.hip", "expand.hip", "segment.hip", "fused.hip", "tile_ops.h", "device_common.h"]
+KERNEL_SOURCES = ["shrink.hip", "expand.hip", "tile_ops.h", "device_common.h", "plan.h"]
 
 WORKLOAD_NAMES = {
     "1": "tiny-fp32: d_in=d_out=256 f32, 4 adapters ranks {1,2,3,4}, T=16",
@@ -68,9 +69,11 @@ def kernel_source_digest() -> str:
 # ------------------------------------------------------------------ bytes
 def algorithmic_bytes(ids: np.ndarray, ranks: np.ndarray, n: int, d_in: int, d_out: int, e: int):
     """Bytes the method itself must move per call (nothing for untouched
-    adapters or padding): each used adapter's factors once, each token's x
-    row once, each token's y row read and written once, the float32
-    intermediate written and read once, the index arrays."""
+    adapters or padding): the ids, each used adapter's factors once, each
+    token's x row once, each token's y row read and written once, and the
+    float32 intermediate h (sum of the tokens' ranks) written once and read
+    once.  The shrink kernel owns the ids, A, x and the h write; the expand
+    the h read, B and y."""
     valid = (ids >= 0) & (ids < n)
     tok_r = np.where(valid, ranks[np.clip(ids, 0, n - 1)], 0)
     active = valid & (tok_r > 0)
@@ -79,10 +82,9 @@ def algorithmic_bytes(ids: np.ndarray, ranks: np.ndarray, n: int, d_in: int, d_o
     Tv = int(active.sum())
     sum_r = int(tok_r.sum())
     T = len(ids)
-    seg = 4 * (2 * T + n + 2)
-    shrink = R_touched * d_in * e + Tv * d_in * e + 4 * sum_r + 4 * Tv
-    expand = R_touched * d_out * e + 2 * Tv * d_out * e + 4 * sum_r + 4 * Tv
-    return {"segment": seg, "shrink": shrink, "expand": expand, "total": seg + shrink + expand,
+    shrink = 4 * T + R_touched * d_in * e + Tv * d_in * e + 4 * sum_r
+    expand = R_touched * d_out * e + 2 * Tv * d_out * e + 4 * sum_r
+    return {"shrink": shrink, "expand": expand, "total": shrink + expand,
             "flops": 2 * sum_r * (d_in + d_out), "touched": int(len(touched)), "R_touched": R_touched}
 
 
@@ -105,7 +107,7 @@ def make_copies(rs, torch, wl, dev, pad_to: int, cold: bool):
     del A, B
     x = torch.from_numpy(wl.x).to(dev).to(dt)
     y = torch.from_numpy(wl.y0).to(dev).to(dt)
-    per_copy = store.A_pack.numel() + store.Bt_pack.numel() + x.numel() * x.element_size() \
+    per_copy = store.A_pack.numel() + store.B_pack.numel() + x.numel() * x.element_size() \
         + y.numel() * y.element_size()
     n_copies = 1 if not cold else int(min(512, max(1, math.ceil(COLD_BYTES / per_copy))))
     copies = [Copy(store, x, y)]
@@ -133,33 +135,21 @@ def time_apply(rs, torch, copies, ids, ws, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall
 
 
-def time_kernels(rs, torch, copies, ids, n, steps):
-    """Per-kernel average duration: HIP events recorded on the launch stream
-    around each segment / shrink / expand launch."""
-    c0 = copies[0]
-    seg = rs.lora_segment(ids, n)
-    T = ids.shape[0]
-    h = torch.empty(T, max(4, -(-c0.store.r_max // 4) * 4), dtype=torch.float32, device=ids.device)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+def time_kernels(rs, torch, copies, ids, ws, steps):
+    """Per-kernel average duration of the apply's two kernels: HIP events
+    recorded on the launch stream before the shrink, between the kernels and
+    after the expand, over the same rotation of copies as the timed steps."""
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for k in range(min(steps, 10)):  # warm the launch path
         c = copies[k % len(copies)]
-        rs.lora_segment(ids, n, seg=seg)
-        rs.lora_shrink(c.store, c.x, seg, h)
-        rs.lora_expand(c.store, h, seg, c.y)
+        rs.lora_apply_batched_timed(c.store, c.x, c.y, ev[k], ids=ids, ws=ws)
     torch.cuda.synchronize()
     for k in range(steps):
         c = copies[k % len(copies)]
-        e = ev[k]
-        e[0].record()
-        rs.lora_segment(ids, n, seg=seg)
-        e[1].record()
-        rs.lora_shrink(c.store, c.x, seg, h)
-        e[2].record()
-        rs.lora_expand(c.store, h, seg, c.y)
-        e[3].record()
+        rs.lora_apply_batched_timed(c.store, c.x, c.y, ev[k], ids=ids, ws=ws)
     torch.cuda.synchronize()
     out = {}
-    for i, name in enumerate(["segment", "shrink", "expand"]):
+    for i, name in enumerate(["shrink", "expand"]):
         ms = [ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(steps)]
         out[name] = {"avg_us": 1e3 * float(np.mean(ms)), "p10_us": 1e3 * float(np.percentile(ms, 10)),
                      "p90_us": 1e3 * float(np.percentile(ms, 90))}
@@ -230,9 +220,9 @@ def main():
     nbytes = algorithmic_bytes(wl.ids, m.ranks, m.n, m.d_in, m.d_out, e)
 
     copies, per_copy = make_copies(rs, torch, wl, dev, 0, not args.warm)
-    ws = torch.empty(rs.lora_apply_ws_bytes(copies[0].store, wl.T, True), dtype=torch.uint8, device=dev)
+    ws = torch.empty(rs.lora_workspace_bytes(copies[0].store, wl.T), dtype=torch.uint8, device=dev)
     ms, wall = time_apply(rs, torch, copies, ids, ws, args.steps, args.warmup)
-    kern = time_kernels(rs, torch, copies, ids, m.n, args.steps)
+    kern = time_kernels(rs, torch, copies, ids, ws, args.steps)
     gbps = nbytes["total"] / (ms * 1e-3) / 1e9
 
     dom = max(("shrink", "expand"), key=lambda k: kern[k]["avg_us"])
@@ -243,7 +233,7 @@ def main():
                 "kernel": f"{dom}_kernel<{'BF16' if e == 2 else 'F32'}>",
                 "algorithmic_bytes_per_launch": nbytes[dom],
                 "avg_launch_us": round(kern[dom]["avg_us"], 2)}
-    for k in ("segment", "shrink", "expand"):
+    for k in ("shrink", "expand"):
         kern[k]["algorithmic_bytes"] = nbytes[k]
         kern[k]["gbps"] = round(nbytes[k] / (kern[k]["avg_us"] * 1e-6) / 1e9, 1)
         kern[k] = {a: (round(b, 2) if isinstance(b, float) else b) for a, b in kern[k].items()}
@@ -261,7 +251,7 @@ def main():
             variants["pad8"] = p8
         for name, pad in variants.items():
             pc, _ = make_copies(rs, torch, wl, dev, pad, not args.warm)
-            pws = torch.empty(rs.lora_apply_ws_bytes(pc[0].store, wl.T, True), dtype=torch.uint8, device=dev)
+            pws = torch.empty(rs.lora_workspace_bytes(pc[0].store, wl.T), dtype=torch.uint8, device=dev)
             pms, _ = time_apply(rs, torch, pc, ids, pws, max(20, args.steps // 2), args.warmup)
             own = algorithmic_bytes(wl.ids, np.full(m.n, pad), m.n, m.d_in, m.d_out, e)["total"]
             padded[name] = {"pad_to": pad, "ms_per_step": round(pms, 5),

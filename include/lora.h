@@ -66,20 +66,23 @@ enum lora_dtype { LORA_DTYPE_F32 = 0, LORA_DTYPE_BF16 = 1 };
 
 /* Largest retained (or padded) rank the kernels accept. */
 #define LORA_MAX_RANK 64
-/* Tokens per work tile (a run of one adapter's tokens in grouped order). */
-#define LORA_TILE_TOKENS 64
-/* Largest T and n that lora_segment accepts (single-workgroup sort). */
+/* Largest T and n that lora_segment accepts (single-workgroup sort); the
+ * batched apply with ids accepts the same T. */
 #define LORA_SEGMENT_MAX_T 16384
 #define LORA_SEGMENT_MAX_N 16382
 
 /*
  * The retained-rank store: every adapter's factors laid end to end at its
- * own rank (pad_to = 0), or every adapter padded with zero rows to pad_to
- * (the rank-padded comparison variant, the stacked [b, r, n] / [b, m, r]
- * layout of "Compress then Serve" section 11).
+ * own rank (pad_to = 0), or every adapter padded with zeros to pad_to (the
+ * rank-padded comparison variant, the stacked [b, r, n] / [b, m, r] layout
+ * of "Compress then Serve" section 11).  Both factors keep the orientation
+ * of the section-3 definition (B: d_B x r, A: r x d_A):
  *
- *   A_pack  [R, d_in]   row row_off[a] + j = row j of A_a
- *   Bt_pack [R, d_out]  row row_off[a] + j = column j of B_a
+ *   A_pack  [R, d_in]   rows row_off[a] .. row_off[a] + rank[a] - 1: A_a
+ *                       (row-major), zero rows past r_a
+ *   B_pack  elements row_off[a] * d_out .. (row_off[a] + rank[a]) * d_out - 1:
+ *                       B_a as a [d_out, rank[a]] row-major block, zero
+ *                       columns past r_a
  *   row_off [n + 1]     int32, exclusive scan of the stored ranks
  *   rank    [n]         int32, stored rank of each adapter (r_a, or pad_to)
  *   scale   [n]         float32, s_a
@@ -93,11 +96,11 @@ typedef struct lora_store {
   int32_t d_out;       /* output features */
   int32_t dtype;       /* enum lora_dtype */
   int32_t r_max;       /* largest stored rank */
-  int32_t R;           /* total stored rows = row_off[n] */
+  int32_t R;           /* total stored rank = row_off[n] */
   int32_t pad_to;      /* 0 = rank-specialized; otherwise every rank padded to this */
   int32_t reserved;
   const void* A_pack;
-  const void* Bt_pack;
+  const void* B_pack;
   const int32_t* row_off;
   const int32_t* rank;
   const float* scale;
@@ -117,14 +120,14 @@ int lora_abi_version(void);
  *   n, d_in, d_out, dtype : as in lora_store.
  *   ranks_host [n]        : retained rank of each adapter, 0 <= r_a.
  *   pad_to                : 0 for the rank-specialized store; otherwise every
- *                           adapter is stored with pad_to rows (pad_to >= max r_a).
- * Out (host): bytes needed for A_pack, Bt_pack and meta.
+ *                           adapter is stored at rank pad_to (pad_to >= max r_a).
+ * Out (host): bytes needed for A_pack, B_pack and meta.
  * Errors: INVALID_ARG (null outputs, n < 0, d <= 0, r_a < 0, pad_to below a
- * rank, total rows overflowing int32); UNSUPPORTED (stored rank above
+ * rank, total rank overflowing int32); UNSUPPORTED (stored rank above
  * LORA_MAX_RANK, d not a multiple of 8 (bf16) / 4 (f32), unknown dtype).
  */
 int lora_store_bytes(int n, int d_in, int d_out, int dtype, const int32_t* ranks_host, int pad_to,
-                     size_t* a_bytes_host, size_t* bt_bytes_host, size_t* meta_bytes_host);
+                     size_t* a_bytes_host, size_t* b_bytes_host, size_t* meta_bytes_host);
 
 /*
  * Pack retained factors into a store.
@@ -133,10 +136,10 @@ int lora_store_bytes(int n, int d_in, int d_out, int dtype, const int32_t* ranks
  *   B_ptrs_host [n] : host array of device pointers; B_a is d_out x r_a,
  *                     row-major.  Either pointer may be NULL when r_a = 0.
  *   scales_host [n] : s_a.
- *   A_pack, Bt_pack, meta : caller buffers of at least the sizes that
+ *   A_pack, B_pack, meta : caller buffers of at least the sizes that
  *                     lora_store_bytes returns, 16-byte aligned.
- *   out_host        : filled on success (references A_pack, Bt_pack, meta).
- * Copies the factors (bit-exact), writes zero rows where pad_to pads, and
+ *   out_host        : filled on success (references A_pack, B_pack, meta).
+ * Copies the factors (bit-exact), writes zeros where pad_to pads, and
  * writes row_off / rank / scale into meta.  Synchronizes `stream` before
  * returning.  Errors: as lora_store_bytes, plus INVALID_ARG for null buffers
  * or a null factor pointer with r_a > 0.
@@ -144,17 +147,11 @@ int lora_store_bytes(int n, int d_in, int d_out, int dtype, const int32_t* ranks
 int lora_pack_retained(lora_store* out_host, int n, int d_in, int d_out, int dtype,
                        const int32_t* ranks_host, const float* scales_host,
                        const void* const* A_ptrs_host, const void* const* B_ptrs_host,
-                       void* A_pack, void* Bt_pack, void* meta, int pad_to, void* stream);
+                       void* A_pack, void* B_pack, void* meta, int pad_to, void* stream);
 
 /*
- * Workspace of lora_segment / lora_segment_from_offsets: the tile plan that
- * lora_shrink and lora_expand read (runs of at most LORA_TILE_TOKENS tokens
- * of one adapter).  Host only.  Returns 0 for T < 0 or n < 0.
- */
-size_t lora_segment_ws_bytes(int T, int n);
-
-/*
- * Group tokens by adapter: a stable counting sort of ids.
+ * Group tokens by adapter: a stable counting sort of ids (the grouping of
+ * requests that use the same adapter, "Compress then Serve" section 2).
  *   ids [T]         : int32 adapter id per token.  -1 = no adapter; any other
  *                     id outside [0, n) is treated as -1 and counted.
  *   seg_off [n + 2] : out.  Adapter a's tokens occupy grouped positions
@@ -165,77 +162,80 @@ size_t lora_segment_ws_bytes(int T, int n);
  *                     keep ascending index (unique result).
  *   n_invalid       : optional (NULL) device int32; receives the count of
  *                     ids that are neither -1 nor in [0, n).
- *   ws              : lora_segment_ws_bytes(T, n) bytes; receives the plan.
- * T = 0 is a no-op apart from writing seg_off (all zero) and the plan.
- * Errors: INVALID_ARG (null pointers, T < 0, n < 1, ws too small);
- * UNSUPPORTED (T > LORA_SEGMENT_MAX_T or n > LORA_SEGMENT_MAX_N).
+ * T = 0 writes seg_off (all zero).  Errors: INVALID_ARG (null pointers,
+ * T < 0, n < 1); UNSUPPORTED (T > LORA_SEGMENT_MAX_T or n > LORA_SEGMENT_MAX_N).
  */
-int lora_segment(const int32_t* ids, int T, int n, int32_t* seg_off, int32_t* perm,
-                 int32_t* n_invalid, void* ws, size_t ws_bytes, void* stream);
+int lora_segment(const int32_t* ids, int T, int n, int32_t* seg_off, int32_t* perm, int32_t* n_invalid,
+                 void* stream);
 
 /*
- * Build the tile plan in ws from a caller-supplied grouping (seg_off as
- * lora_segment writes it).  For callers that group tokens themselves, or
- * reuse one grouping across many stores (every module of a layer stack).
+ * Workspace of lora_shrink, lora_expand and lora_apply_batched for T tokens
+ * on this store (host only; 0 on invalid arguments).  It holds the work plan
+ * (sub-tiles of at most 16 tokens of one adapter) and the shrink's float32
+ * partial sums; the contents need no initialization and are scratch after
+ * the call.  One workspace must not be shared by calls in flight together.
  */
-int lora_segment_from_offsets(const int32_t* seg_off, int T, int n, void* ws, size_t ws_bytes,
-                              void* stream);
+size_t lora_workspace_bytes(const lora_store* store_host, int T);
 
 /*
  * Shrink (step 1 of "Compress then Serve" section 13.4):
  *   h[i, j] = sum_k A_a[j, k] * x[perm[i], k]    for j < r_a, a = adapter of
  *                                                grouped position i
  *   x   [T, ldx] : dtype of the store, token order.
+ *   seg_off, perm: a grouping as lora_segment writes it (for store->n).
  *   h   [T, ldh] : float32, GROUPED order (row i = grouped position i),
- *                  ldh >= r_max.  Columns >= r_a and rows of tokens without an
- *                  adapter are not written.  Products are accumulated in
- *                  float32 (bf16 products are exact in float32).
- *   seg_off, perm, seg_ws : from lora_segment (or lora_segment_from_offsets)
- *                  for the same T and store->n.
+ *                  ldh >= r_max.  Columns >= r_a and rows of tokens without
+ *                  an adapter (or with r_a = 0) are not written.  Products
+ *                  are accumulated in float32 (bf16 products are exact in
+ *                  float32); the sum over d_in is formed in a fixed order,
+ *                  so results are deterministic.
+ *   ws           : lora_workspace_bytes(store, T) bytes, 16-byte aligned.
  * Errors: INVALID_ARG (null pointers, T < 0, ldx < d_in, ldh < r_max, ws too
- * small); UNSUPPORTED (alignment, see conventions).
+ * small); UNSUPPORTED (alignment, see conventions; n > LORA_SEGMENT_MAX_N).
  */
-int lora_shrink(const lora_store* store_host, const void* x, int64_t ldx, int T,
-                const int32_t* seg_off, const int32_t* perm, const void* seg_ws, size_t seg_ws_bytes,
-                float* h, int64_t ldh, void* stream);
+int lora_shrink(const lora_store* store_host, const void* x, int64_t ldx, int T, const int32_t* seg_off,
+                const int32_t* perm, float* h, int64_t ldh, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Expand (step 3 of "Compress then Serve" section 13.4):
  *   y[perm[i], o] += s_a * sum_{j < r_a} B_a[o, j] * h[i, j]
  * accumulated in float32 and rounded once to the output dtype (bf16: round
- * to nearest, ties to even).  y [T, ldy] in token order, ldy >= d_out; y may
- * be a column slice of a wider buffer (pass the slice's first column and the
- * wider row stride) - the y_offset / y_slice_size of the same section.
- * Rows of tokens without an adapter (and of adapters with r_a = 0) are left
- * untouched.  Errors as lora_shrink.
+ * to nearest, ties to even).  h [T, ldh] float32 in grouped order (as
+ * lora_shrink writes it; columns >= r_a are not read).  y [T, ldy] in token
+ * order, ldy >= d_out; y may be a column slice of a wider buffer (pass the
+ * slice's first column and the wider row stride) - the y_offset /
+ * y_slice_size of the same section.  Rows of tokens without an adapter (and
+ * of adapters with r_a = 0) are left untouched.  Errors as lora_shrink.
  */
-int lora_expand(const lora_store* store_host, const float* h, int64_t ldh, int T,
-                const int32_t* seg_off, const int32_t* perm, const void* seg_ws, size_t seg_ws_bytes,
-                void* y, int64_t ldy, void* stream);
-
-/*
- * Workspace of lora_apply_batched for T tokens on this store (host only).
- * with_segmentation = 1: room for seg_off, perm and the plan (ids path);
- * 0: only the float32 intermediate h (caller passes a grouping).
- */
-size_t lora_apply_ws_bytes(const lora_store* store_host, int T, int with_segmentation);
+int lora_expand(const lora_store* store_host, const float* h, int64_t ldh, int T, const int32_t* seg_off,
+                const int32_t* perm, void* y, int64_t ldy, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * The batched apply:  y[t] += s_a * B_a (A_a x[t])  for every token.
- * Either ids (then the grouping is computed into ws), or ids = NULL and
- * seg_off / perm / seg_ws from a previous lora_segment (one grouping reused
- * across many stores, e.g. every projection of a decode step).
- * Computes what lora_segment (when ids is given), lora_shrink and
- * lora_expand compute.  On decode-shaped batches (T <= 8 n) the shrink and
- * expand of each sub-tile run fused in one workgroup with the float32
- * intermediate kept on chip; float32 sums may then be formed in a different
- * order than the separate calls (results agree to float32 rounding; exact
- * integer-valued inputs give identical bits).  Errors: union of those calls'.
+ * Either ids (the grouping is then formed inside the shrink), or ids = NULL
+ * and seg_off / perm from lora_segment (one grouping reused across many
+ * stores, e.g. every projection of a decode step).  Two kernels: the shrink
+ * (grouping + float32 partial sums over chunks of d_in, in the workspace)
+ * and the expand (partials summed in chunk order, then y updated).  The
+ * result equals lora_segment + lora_shrink + lora_expand bit for bit.
+ * Errors: union of those calls'.
  */
 int lora_apply_batched(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy,
-                       int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm,
-                       const void* seg_ws, size_t seg_ws_bytes, void* ws, size_t ws_bytes,
-                       void* stream);
+                       int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/*
+ * lora_apply_batched with timing marks, for measurement: events_host[0..2]
+ * are hipEvent_t handles (created by the caller) that are recorded on
+ * `stream` before the shrink kernel, between the shrink and the expand, and
+ * after the expand (when n > 4096 with ids, the sort runs after mark 0).
+ * Errors: as lora_apply_batched; INVALID_ARG for a null events_host or
+ * event.
+ */
+int lora_apply_batched_timed(const lora_store* store_host, const void* x, int64_t ldx, void* y,
+                             int64_t ldy, int T, const int32_t* ids, const int32_t* seg_off,
+                             const int32_t* perm, void* ws, size_t ws_bytes, void* stream,
+                             void* const* events_host);
 
 #ifdef __cplusplus
 }

@@ -9,6 +9,9 @@ kernels of librank_specialized.so.  The entry points keep the C names:
     h     = lora_shrink(store, x, seg)                        # h = A_a x (grouped rows)
     lora_expand(store, h, seg, y)                             # y += s_a B_a h
     lora_apply_batched(store, x, y, ids=ids)                  # all of the above
+
+Workspaces (lora_workspace_bytes) are allocated here with torch when the
+caller passes none.
 """
 from __future__ import annotations
 
@@ -23,8 +26,8 @@ from ._lib import LoraError, lora_store  # noqa: F401
 
 __all__ = [
     "Store", "Segmentation", "LoraError", "lora_store_bytes", "lora_pack_retained",
-    "lora_segment_ws_bytes", "lora_segment", "lora_segment_from_offsets", "lora_shrink",
-    "lora_expand", "lora_apply_ws_bytes", "lora_apply_batched", "load_library",
+    "lora_segment", "lora_workspace_bytes", "lora_shrink", "lora_expand", "lora_apply_batched",
+    "lora_apply_batched_timed", "load_library",
 ]
 
 _DTYPES = {torch.bfloat16: L.LORA_DTYPE_BF16, torch.float32: L.LORA_DTYPE_F32}
@@ -55,7 +58,7 @@ class Store:
 
     c: lora_store
     A_pack: torch.Tensor
-    Bt_pack: torch.Tensor
+    B_pack: torch.Tensor
     meta: torch.Tensor
     ranks: List[int]
     dtype: torch.dtype
@@ -85,14 +88,14 @@ class Store:
 
     def clone(self) -> "Store":
         """An independent copy in fresh device memory (same layout)."""
-        A, Bt, meta = self.A_pack.clone(), self.Bt_pack.clone(), self.meta.clone()
+        A, B, meta = self.A_pack.clone(), self.B_pack.clone(), self.meta.clone()
         c = lora_store.from_buffer_copy(self.c)
         n = self.c.n
-        c.A_pack, c.Bt_pack = A.data_ptr(), Bt.data_ptr()
+        c.A_pack, c.B_pack = A.data_ptr(), B.data_ptr()
         c.row_off = meta.data_ptr()
         c.rank = meta.data_ptr() + (n + 1) * 4
         c.scale = meta.data_ptr() + (2 * n + 1) * 4
-        return Store(c, A, Bt, meta, list(self.ranks), self.dtype)
+        return Store(c, A, B, meta, list(self.ranks), self.dtype)
 
     def device_meta(self):
         """(row_off, rank, scale) as device tensors (views of the meta buffer)."""
@@ -130,7 +133,7 @@ def lora_pack_retained(A_list: Sequence[torch.Tensor], B_list: Sequence[torch.Te
             raise ValueError("factors must be contiguous")
     a_bytes, b_bytes, m_bytes = lora_store_bytes(n, d_in, d_out, dtype, ranks, pad_to)
     A_pack = torch.empty(max(a_bytes, 16), dtype=torch.uint8, device=device)
-    Bt_pack = torch.empty(max(b_bytes, 16), dtype=torch.uint8, device=device)
+    B_pack = torch.empty(max(b_bytes, 16), dtype=torch.uint8, device=device)
     meta = torch.empty(m_bytes, dtype=torch.uint8, device=device)
     r_arr = (C.c_int32 * n)(*ranks)
     s_arr = (C.c_float * n)(*[float(v) for v in scales])
@@ -139,28 +142,19 @@ def lora_pack_retained(A_list: Sequence[torch.Tensor], B_list: Sequence[torch.Te
     st = lora_store()
     L.check("lora_pack_retained", L.lib().lora_pack_retained(
         C.byref(st), n, d_in, d_out, _DTYPES[dtype], r_arr, s_arr, a_ptrs, b_ptrs,
-        A_pack.data_ptr(), Bt_pack.data_ptr(), meta.data_ptr(), pad_to, _stream(meta)))
-    return Store(st, A_pack, Bt_pack, meta, ranks, dtype)
-
-
-def lora_segment_ws_bytes(T: int, n: int) -> int:
-    return int(L.lib().lora_segment_ws_bytes(T, n))
+        A_pack.data_ptr(), B_pack.data_ptr(), meta.data_ptr(), pad_to, _stream(meta)))
+    return Store(st, A_pack, B_pack, meta, ranks, dtype)
 
 
 @dataclass
 class Segmentation:
-    """Grouped order of T tokens over n adapters plus the tile plan."""
+    """Grouped order of T tokens over n adapters (as lora_segment writes it)."""
 
     T: int
     n: int
     seg_off: torch.Tensor  # int32 [n + 2]
     perm: torch.Tensor  # int32 [T]
-    ws: torch.Tensor  # uint8 plan
     n_invalid: Optional[torch.Tensor] = None
-
-    @property
-    def ws_bytes(self) -> int:
-        return self.ws.numel()
 
 
 def lora_segment(ids: torch.Tensor, n: int, *, seg: Optional[Segmentation] = None) -> Segmentation:
@@ -172,48 +166,45 @@ def lora_segment(ids: torch.Tensor, n: int, *, seg: Optional[Segmentation] = Non
     if seg is None:
         seg = Segmentation(T, n, torch.empty(n + 2, dtype=torch.int32, device=dev),
                            torch.empty(max(T, 1), dtype=torch.int32, device=dev)[:T],
-                           torch.empty(max(lora_segment_ws_bytes(T, n), 16), dtype=torch.uint8,
-                                       device=dev),
                            torch.empty(1, dtype=torch.int32, device=dev))
     L.check("lora_segment", L.lib().lora_segment(
-        _p(ids), T, n, seg.seg_off.data_ptr(), _p(seg.perm), seg.n_invalid.data_ptr(),
-        seg.ws.data_ptr(), seg.ws.numel(), _stream(seg.ws)))
+        _p(ids), T, n, seg.seg_off.data_ptr(), _p(seg.perm), seg.n_invalid.data_ptr(), _stream(seg.seg_off)))
     return seg
 
 
-def lora_segment_from_offsets(seg_off: torch.Tensor, perm: torch.Tensor, n: int) -> Segmentation:
-    """Plan for a caller-supplied grouping (seg_off [n+2], perm [T], int32)."""
-    T = perm.shape[0]
-    ws = torch.empty(max(lora_segment_ws_bytes(T, n), 16), dtype=torch.uint8, device=seg_off.device)
-    L.check("lora_segment_from_offsets", L.lib().lora_segment_from_offsets(
-        seg_off.data_ptr(), T, n, ws.data_ptr(), ws.numel(), _stream(ws)))
-    return Segmentation(T, n, seg_off, perm, ws)
+def lora_workspace_bytes(store: Store, T: int) -> int:
+    return int(L.lib().lora_workspace_bytes(store.ref(), T))
 
 
-def lora_shrink(store: Store, x: torch.Tensor, seg: Segmentation, h: Optional[torch.Tensor] = None
-                ) -> torch.Tensor:
+def _ws(store: Store, T: int, ws: Optional[torch.Tensor], device) -> torch.Tensor:
+    if ws is None:
+        ws = torch.empty(max(lora_workspace_bytes(store, T), 16), dtype=torch.uint8, device=device)
+    return ws
+
+
+def lora_shrink(store: Store, x: torch.Tensor, seg: Segmentation, h: Optional[torch.Tensor] = None,
+                ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """h[i, :r_a] = A_a x[perm[i]] in float32 (grouped rows).  Columns >= r_a
     and rows of tokens without an adapter are left as they were in ``h``."""
     T = x.shape[0]
     if h is None:
         h = torch.zeros(T, max(store.r_max, 1), dtype=torch.float32, device=x.device)
+    ws = _ws(store, T, ws, x.device)
     L.check("lora_shrink", L.lib().lora_shrink(
-        store.ref(), _p(x), _rows(x, "x"), T, seg.seg_off.data_ptr(), _p(seg.perm),
-        seg.ws.data_ptr(), seg.ws_bytes, _p(h), _rows(h, "h"), _stream(x)))
+        store.ref(), _p(x), _rows(x, "x"), T, seg.seg_off.data_ptr(), _p(seg.perm), _p(h), _rows(h, "h"),
+        ws.data_ptr(), ws.numel(), _stream(x)))
     return h
 
 
-def lora_expand(store: Store, h: torch.Tensor, seg: Segmentation, y: torch.Tensor) -> torch.Tensor:
+def lora_expand(store: Store, h: torch.Tensor, seg: Segmentation, y: torch.Tensor,
+                ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """y[perm[i]] += s_a B_a h[i] in place."""
     T = y.shape[0]
+    ws = _ws(store, T, ws, y.device)
     L.check("lora_expand", L.lib().lora_expand(
-        store.ref(), _p(h), _rows(h, "h"), T, seg.seg_off.data_ptr(), _p(seg.perm),
-        seg.ws.data_ptr(), seg.ws_bytes, _p(y), _rows(y, "y"), _stream(y)))
+        store.ref(), _p(h), _rows(h, "h"), T, seg.seg_off.data_ptr(), _p(seg.perm), _p(y), _rows(y, "y"),
+        ws.data_ptr(), ws.numel(), _stream(y)))
     return y
-
-
-def lora_apply_ws_bytes(store: Store, T: int, with_segmentation: bool = True) -> int:
-    return int(L.lib().lora_apply_ws_bytes(store.ref(), T, 1 if with_segmentation else 0))
 
 
 def lora_apply_batched(store: Store, x: torch.Tensor, y: torch.Tensor, *,
@@ -223,17 +214,39 @@ def lora_apply_batched(store: Store, x: torch.Tensor, y: torch.Tensor, *,
     T = x.shape[0]
     if (ids is None) == (seg is None):
         raise ValueError("pass exactly one of ids or seg")
-    need = lora_apply_ws_bytes(store, T, ids is not None)
-    if ws is None:
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    ws = _ws(store, T, ws, x.device)
     if seg is not None:
-        so, pm, sw, swb = seg.seg_off.data_ptr(), _p(seg.perm), seg.ws.data_ptr(), seg.ws_bytes
+        so, pm = seg.seg_off.data_ptr(), _p(seg.perm)
     else:
         if ids.dtype != torch.int32 or not ids.is_contiguous():
             raise ValueError("ids must be a contiguous int32 vector")
-        so = pm = sw = None
-        swb = 0
+        so = pm = None
     L.check("lora_apply_batched", L.lib().lora_apply_batched(
         store.ref(), _p(x), _rows(x, "x"), _p(y), _rows(y, "y"), T, _p(ids) if ids is not None else None,
-        so, pm, sw, swb, ws.data_ptr(), ws.numel(), _stream(x)))
+        so, pm, ws.data_ptr(), ws.numel(), _stream(x)))
+    return y
+
+
+def lora_apply_batched_timed(store: Store, x: torch.Tensor, y: torch.Tensor, events, *,
+                             ids: Optional[torch.Tensor] = None, seg: Optional[Segmentation] = None,
+                             ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """lora_apply_batched that also records three torch.cuda.Event objects on
+    the launch stream: before the shrink, between shrink and expand, after."""
+    T = x.shape[0]
+    if (ids is None) == (seg is None):
+        raise ValueError("pass exactly one of ids or seg")
+    if len(events) != 3:
+        raise ValueError("need three events")
+    for ev in events:  # make sure the HIP events exist
+        if ev.cuda_event == 0:
+            ev.record(torch.cuda.current_stream(x.device))
+    handles = (C.c_void_p * 3)(*[ev.cuda_event for ev in events])
+    ws = _ws(store, T, ws, x.device)
+    so = seg.seg_off.data_ptr() if seg is not None else None
+    pm = _p(seg.perm) if seg is not None else None
+    if ids is not None and (ids.dtype != torch.int32 or not ids.is_contiguous()):
+        raise ValueError("ids must be a contiguous int32 vector")
+    L.check("lora_apply_batched_timed", L.lib().lora_apply_batched_timed(
+        store.ref(), _p(x), _rows(x, "x"), _p(y), _rows(y, "y"), T, _p(ids) if ids is not None else None,
+        so, pm, ws.data_ptr(), ws.numel(), _stream(x), handles))
     return y

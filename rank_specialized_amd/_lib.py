@@ -18,7 +18,6 @@ LORA_ERR_HIP = 3
 LORA_DTYPE_F32 = 0
 LORA_DTYPE_BF16 = 1
 LORA_MAX_RANK = 64
-LORA_TILE_TOKENS = 64
 LORA_SEGMENT_MAX_T = 16384
 LORA_SEGMENT_MAX_N = 16382
 
@@ -27,7 +26,7 @@ class lora_store(C.Structure):
     _fields_ = [
         ("n", C.c_int32), ("d_in", C.c_int32), ("d_out", C.c_int32), ("dtype", C.c_int32),
         ("r_max", C.c_int32), ("R", C.c_int32), ("pad_to", C.c_int32), ("reserved", C.c_int32),
-        ("A_pack", C.c_void_p), ("Bt_pack", C.c_void_p), ("row_off", C.c_void_p),
+        ("A_pack", C.c_void_p), ("B_pack", C.c_void_p), ("row_off", C.c_void_p),
         ("rank", C.c_void_p), ("scale", C.c_void_p),
     ]
 
@@ -43,13 +42,13 @@ SIGNATURES = {
     "lora_abi_version": (I, []),
     "lora_store_bytes": (I, [I, I, I, I, P, I, C.POINTER(SZ), C.POINTER(SZ), C.POINTER(SZ)]),
     "lora_pack_retained": (I, [C.POINTER(lora_store), I, I, I, I, P, P, P, P, P, P, P, I, P]),
-    "lora_segment_ws_bytes": (SZ, [I, I]),
-    "lora_segment": (I, [P, I, I, P, P, P, P, SZ, P]),
-    "lora_segment_from_offsets": (I, [P, I, I, P, SZ, P]),
-    "lora_shrink": (I, [C.POINTER(lora_store), P, I64, I, P, P, P, SZ, P, I64, P]),
-    "lora_expand": (I, [C.POINTER(lora_store), P, I64, I, P, P, P, SZ, P, I64, P]),
-    "lora_apply_ws_bytes": (SZ, [C.POINTER(lora_store), I, I]),
-    "lora_apply_batched": (I, [C.POINTER(lora_store), P, I64, P, I64, I, P, P, P, P, SZ, P, SZ, P]),
+    "lora_segment": (I, [P, I, I, P, P, P, P]),
+    "lora_workspace_bytes": (SZ, [C.POINTER(lora_store), I]),
+    "lora_shrink": (I, [C.POINTER(lora_store), P, I64, I, P, P, P, I64, P, SZ, P]),
+    "lora_expand": (I, [C.POINTER(lora_store), P, I64, I, P, P, P, I64, P, SZ, P]),
+    "lora_apply_batched": (I, [C.POINTER(lora_store), P, I64, P, I64, I, P, P, P, P, SZ, P]),
+    "lora_apply_batched_timed": (I, [C.POINTER(lora_store), P, I64, P, I64, I, P, P, P, P, SZ, P,
+                                     C.POINTER(C.c_void_p)]),
 }
 
 _lib = None

@@ -33,18 +33,18 @@ const char* lora_status_string(int status) {
 
 int lora_last_hip_error(void) { return g_last_hip; }
 
-int lora_abi_version(void) { return 1; }
+int lora_abi_version(void) { return 2; }
 
 int lora_store_bytes(int n, int d_in, int d_out, int dtype, const int32_t* ranks_host, int pad_to,
-                     size_t* a_bytes_host, size_t* bt_bytes_host, size_t* meta_bytes_host) {
-  if (!a_bytes_host || !bt_bytes_host || !meta_bytes_host) return LORA_ERR_INVALID_ARG;
+                     size_t* a_bytes_host, size_t* b_bytes_host, size_t* meta_bytes_host) {
+  if (!a_bytes_host || !b_bytes_host || !meta_bytes_host) return LORA_ERR_INVALID_ARG;
   int r_max = 0;
   int64_t rows = 0;
   int st = check_store_shape(n, d_in, d_out, dtype, ranks_host, pad_to, &r_max, &rows);
   if (st != LORA_OK) return st;
   const size_t eb = (size_t)elem_bytes(dtype);
   *a_bytes_host = (size_t)rows * d_in * eb;
-  *bt_bytes_host = (size_t)rows * d_out * eb;
+  *b_bytes_host = (size_t)rows * d_out * eb;
   *meta_bytes_host = meta_bytes(n);
   return LORA_OK;
 }
@@ -52,7 +52,7 @@ int lora_store_bytes(int n, int d_in, int d_out, int dtype, const int32_t* ranks
 int lora_pack_retained(lora_store* out_host, int n, int d_in, int d_out, int dtype,
                        const int32_t* ranks_host, const float* scales_host,
                        const void* const* A_ptrs_host, const void* const* B_ptrs_host, void* A_pack,
-                       void* Bt_pack, void* meta, int pad_to, void* stream) {
+                       void* B_pack, void* meta, int pad_to, void* stream) {
   if (!out_host || !scales_host || !meta) return LORA_ERR_INVALID_ARG;
   if (n < 1) return LORA_ERR_INVALID_ARG;
   int r_max = 0;
@@ -60,8 +60,8 @@ int lora_pack_retained(lora_store* out_host, int n, int d_in, int d_out, int dty
   int st = check_store_shape(n, d_in, d_out, dtype, ranks_host, pad_to, &r_max, &rows);
   if (st != LORA_OK) return st;
   if (!A_ptrs_host || !B_ptrs_host) return LORA_ERR_INVALID_ARG;
-  if (rows > 0 && (!A_pack || !Bt_pack)) return LORA_ERR_INVALID_ARG;
-  if (!aligned16(meta) || (A_pack && !aligned16(A_pack)) || (Bt_pack && !aligned16(Bt_pack)))
+  if (rows > 0 && (!A_pack || !B_pack)) return LORA_ERR_INVALID_ARG;
+  if (!aligned16(meta) || (A_pack && !aligned16(A_pack)) || (B_pack && !aligned16(B_pack)))
     return LORA_ERR_UNSUPPORTED;
   for (int a = 0; a < n; ++a)
     if (ranks_host[a] > 0 && (!A_ptrs_host[a] || !B_ptrs_host[a])) return LORA_ERR_INVALID_ARG;
@@ -86,7 +86,7 @@ int lora_pack_retained(lora_store* out_host, int n, int d_in, int d_out, int dty
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipMemcpyAsync(meta, img.data(), img.size(), hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return hip_fail(e);
-  e = launch_pack(dtype, meta, n, d_in, d_out, (int)rows, A_pack, Bt_pack, s);
+  e = launch_pack(dtype, meta, n, d_in, d_out, (int)rows, A_pack, B_pack, s);
   if (e != hipSuccess) return hip_fail(e);
   e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e);
@@ -101,7 +101,7 @@ int lora_pack_retained(lora_store* out_host, int n, int d_in, int d_out, int dty
   st_out.R = (int32_t)rows;
   st_out.pad_to = pad_to;
   st_out.A_pack = A_pack;
-  st_out.Bt_pack = Bt_pack;
+  st_out.B_pack = B_pack;
   st_out.row_off = reinterpret_cast<const int32_t*>(meta);
   st_out.rank = st_out.row_off + (n + 1);
   st_out.scale = reinterpret_cast<const float*>(st_out.rank + n);
@@ -109,115 +109,103 @@ int lora_pack_retained(lora_store* out_host, int n, int d_in, int d_out, int dty
   return LORA_OK;
 }
 
-size_t lora_segment_ws_bytes(int T, int n) { return plan_bytes(T, n); }
-
 int lora_segment(const int32_t* ids, int T, int n, int32_t* seg_off, int32_t* perm, int32_t* n_invalid,
-                 void* ws, size_t ws_bytes, void* stream) {
-  int st = check_segment_args(ids, T, n, seg_off, perm, ws, ws_bytes);
+                 void* stream) {
+  int st = check_segment_args(ids, T, n, seg_off, perm);
   if (st != LORA_OK) return st;
   int max_lds = 0;
   hipError_t e = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, 0);
   if (e != hipSuccess) return hip_fail(e);
   if (segment_lds_bytes(T, n) + segment_static_lds_bytes() > (size_t)max_lds) return LORA_ERR_UNSUPPORTED;
-  e = launch_segment(ids, T, n, seg_off, perm, n_invalid, ws, reinterpret_cast<hipStream_t>(stream));
+  e = launch_segment(ids, T, n, seg_off, perm, n_invalid, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? LORA_OK : hip_fail(e);
 }
 
-int lora_segment_from_offsets(const int32_t* seg_off, int T, int n, void* ws, size_t ws_bytes,
-                              void* stream) {
-  if (T < 0 || n < 1 || !seg_off || !ws) return LORA_ERR_INVALID_ARG;
-  if (ws_bytes < plan_bytes(T, n)) return LORA_ERR_INVALID_ARG;
-  if (!aligned16(ws)) return LORA_ERR_UNSUPPORTED;
-  if (n > LORA_SEGMENT_MAX_N) return LORA_ERR_UNSUPPORTED;
-  hipError_t e = launch_plan_from_offsets(seg_off, T, n, ws, reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? LORA_OK : hip_fail(e);
+size_t lora_workspace_bytes(const lora_store* store_host, int T) {
+  if (check_store(store_host) != LORA_OK) return 0;
+  return workspace_bytes(store_host, T);
 }
 
 int lora_shrink(const lora_store* store_host, const void* x, int64_t ldx, int T, const int32_t* seg_off,
-                const int32_t* perm, const void* seg_ws, size_t seg_ws_bytes, float* h, int64_t ldh,
-                void* stream) {
+                const int32_t* perm, float* h, int64_t ldh, void* ws, size_t ws_bytes, void* stream) {
   int st = check_store(store_host);
   if (st != LORA_OK) return st;
-  if ((st = check_plan_args(store_host, T, seg_off, perm, seg_ws, seg_ws_bytes)) != LORA_OK) return st;
+  if ((st = check_grouping(store_host, T, seg_off, perm)) != LORA_OK) return st;
   if ((st = check_rows(x, ldx, store_host->d_in, store_host->dtype, T)) != LORA_OK) return st;
   if ((st = check_h(h, ldh, store_host, T)) != LORA_OK) return st;
+  if ((st = check_ws(store_host, T, ws, ws_bytes)) != LORA_OK) return st;
   if (T == 0) return LORA_OK;
-  hipError_t e = launch_shrink(*store_host, x, ldx, T, perm, seg_ws, h, ldh,
-                               reinterpret_cast<hipStream_t>(stream));
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_shrink(*store_host, nullptr, seg_off, perm, T, x, ldx, ws, strm);
+  if (e == hipSuccess) e = launch_reduce_partials(*store_host, T, ws, h, ldh, strm);
   return e == hipSuccess ? LORA_OK : hip_fail(e);
 }
 
 int lora_expand(const lora_store* store_host, const float* h, int64_t ldh, int T, const int32_t* seg_off,
-                const int32_t* perm, const void* seg_ws, size_t seg_ws_bytes, void* y, int64_t ldy,
-                void* stream) {
+                const int32_t* perm, void* y, int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
   int st = check_store(store_host);
   if (st != LORA_OK) return st;
-  if ((st = check_plan_args(store_host, T, seg_off, perm, seg_ws, seg_ws_bytes)) != LORA_OK) return st;
+  if ((st = check_grouping(store_host, T, seg_off, perm)) != LORA_OK) return st;
   if ((st = check_rows(y, ldy, store_host->d_out, store_host->dtype, T)) != LORA_OK) return st;
   if ((st = check_h(h, ldh, store_host, T)) != LORA_OK) return st;
+  if ((st = check_ws(store_host, T, ws, ws_bytes)) != LORA_OK) return st;
   if (T == 0) return LORA_OK;
-  hipError_t e = launch_expand(*store_host, h, ldh, T, perm, seg_ws, y, ldy,
-                               reinterpret_cast<hipStream_t>(stream));
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_plan(*store_host, seg_off, perm, T, ws, strm);
+  if (e == hipSuccess) e = launch_expand(*store_host, T, ws, h, ldh, y, ldy, strm);
   return e == hipSuccess ? LORA_OK : hip_fail(e);
 }
 
-// Workspace layout of lora_apply_batched (each part 256-byte aligned):
-//   [plan | seg_off (n+2) | perm (T)]   (only with segmentation)   then h.
-static size_t apply_seg_bytes(int T, int n) {
-  return align_up(plan_bytes(T, n), 256) + align_up((size_t)(n + 2) * 4, 256) +
-         align_up((size_t)T * 4, 256);
-}
-
-size_t lora_apply_ws_bytes(const lora_store* store_host, int T, int with_segmentation) {
-  if (!store_host || T < 0 || store_host->n < 1) return 0;
-  size_t hb = align_up((size_t)T * (size_t)apply_ldh(store_host->r_max) * 4, 256);
-  return hb + (with_segmentation ? apply_seg_bytes(T, store_host->n) : 0);
-}
-
-int lora_apply_batched(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy,
-                       int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm,
-                       const void* seg_ws, size_t seg_ws_bytes, void* ws, size_t ws_bytes,
-                       void* stream) {
+static int apply_impl(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy, int T,
+                      const int32_t* ids, const int32_t* seg_off, const int32_t* perm, void* ws, size_t ws_bytes,
+                      void* stream, void* const* events) {
   int st = check_store(store_host);
   if (st != LORA_OK) return st;
   const lora_store& s = *store_host;
   if (T < 0) return LORA_ERR_INVALID_ARG;
   if ((st = check_rows(x, ldx, s.d_in, s.dtype, T)) != LORA_OK) return st;
   if ((st = check_rows(y, ldy, s.d_out, s.dtype, T)) != LORA_OK) return st;
+  if ((st = check_ws(store_host, T, ws, ws_bytes)) != LORA_OK) return st;
+  if (ids != nullptr && (T > LORA_SEGMENT_MAX_T || s.n > LORA_SEGMENT_MAX_N)) return LORA_ERR_UNSUPPORTED;
+  if (events != nullptr && (!events[0] || !events[1] || !events[2])) return LORA_ERR_INVALID_ARG;
   if (T == 0) return LORA_OK;  // nothing to group or apply
-  const bool segment = ids != nullptr;
-  if (!ws || ws_bytes < lora_apply_ws_bytes(store_host, T, segment ? 1 : 0)) return LORA_ERR_INVALID_ARG;
-  if (!aligned16(ws)) return LORA_ERR_UNSUPPORTED;
-  char* base = reinterpret_cast<char*>(ws);
+  if (ids == nullptr && (st = check_grouping(store_host, T, seg_off, perm)) != LORA_OK) return st;
   hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
-  const void* plan = seg_ws;
-  if (segment) {
-    if (T > LORA_SEGMENT_MAX_T || s.n > LORA_SEGMENT_MAX_N) return LORA_ERR_UNSUPPORTED;
-    void* plan_w = base;
-    int32_t* so = reinterpret_cast<int32_t*>(base + align_up(plan_bytes(T, s.n), 256));
-    int32_t* pm = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(so) +
-                                             align_up((size_t)(s.n + 2) * 4, 256));
-    base += apply_seg_bytes(T, s.n);
-    st = lora_segment(ids, T, s.n, so, pm, nullptr, plan_w, plan_bytes(T, s.n), stream);
+  auto mark = [&](int k) -> hipError_t {
+    return events ? hipEventRecord(reinterpret_cast<hipEvent_t>(events[k]), strm) : hipSuccess;
+  };
+  hipError_t e = mark(0);
+  if (e != hipSuccess) return hip_fail(e);
+  if (ids != nullptr && s.n > kGroupMaxN) {
+    // Too many adapters for the in-shrink histogram: sort first, into ws.
+    const WsLayout L = ws_layout(T, s.n, s.d_in, s.r_max, s.dtype);
+    int32_t* so = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + L.seg_off);
+    int32_t* pm = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + L.perm);
+    st = lora_segment(ids, T, s.n, so, pm, nullptr, stream);
     if (st != LORA_OK) return st;
-    seg_off = so;
-    perm = pm;
-    plan = plan_w;
-    seg_ws_bytes = plan_bytes(T, s.n);
+    e = launch_shrink(s, nullptr, so, pm, T, x, ldx, ws, strm);
+  } else if (ids != nullptr) {
+    e = launch_shrink(s, ids, nullptr, nullptr, T, x, ldx, ws, strm);
   } else {
-    if ((st = check_plan_args(store_host, T, seg_off, perm, seg_ws, seg_ws_bytes)) != LORA_OK) return st;
+    e = launch_shrink(s, nullptr, seg_off, perm, T, x, ldx, ws, strm);
   }
-  hipError_t e;
-  if (use_fused_apply(T, s.n)) {
-    e = launch_apply_fused(s, x, ldx, T, perm, plan, y, ldy, strm);
-  } else {
-    float* h = reinterpret_cast<float*>(base);
-    const int64_t ldh = apply_ldh(s.r_max);
-    e = launch_shrink(s, x, ldx, T, perm, plan, h, ldh, strm);
-    if (e != hipSuccess) return hip_fail(e);
-    e = launch_expand(s, h, ldh, T, perm, plan, y, ldy, strm);
-  }
+  if (e == hipSuccess) e = mark(1);
+  if (e == hipSuccess) e = launch_expand(s, T, ws, nullptr, 0, y, ldy, strm);
+  if (e == hipSuccess) e = mark(2);
   return e == hipSuccess ? LORA_OK : hip_fail(e);
+}
+
+int lora_apply_batched(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy,
+                       int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm, void* ws,
+                       size_t ws_bytes, void* stream) {
+  return apply_impl(store_host, x, ldx, y, ldy, T, ids, seg_off, perm, ws, ws_bytes, stream, nullptr);
+}
+
+int lora_apply_batched_timed(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy,
+                             int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm, void* ws,
+                             size_t ws_bytes, void* stream, void* const* events_host) {
+  if (events_host == nullptr) return LORA_ERR_INVALID_ARG;
+  return apply_impl(store_host, x, ldx, y, ldy, T, ids, seg_off, perm, ws, ws_bytes, stream, events_host);
 }
 
 }  // extern "C"

@@ -74,6 +74,9 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ uint4 buf_ld16(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
+__device__ __forceinline__ uint32_t buf_ld4(rsrc_t r, uint32_t voff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
+}
 __device__ __forceinline__ uint32_t buf_ld2(rsrc_t r, uint32_t voff) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0);
 }
@@ -108,19 +111,37 @@ __device__ __forceinline__ f32x4_t mfma_chunk<F32>(const uint4& a, const uint4& 
   return c;
 }
 
-// ------------------------------------------------------------------ plan
-struct Plan {
-  const int32_t* count;  // header: [0] tiles, [1] large tiles, [2] small tiles, [3] sub-tiles
-  const int4* tiles;     // expand tiles {adapter, first grouped position, tokens, 0}; large first
-  const int4* subtiles;  // shrink sub-tiles (<= kSubTile tokens)
-};
-__host__ __device__ inline Plan plan_view(const void* ws, size_t subtile_offset) {
-  Plan p;
-  const char* b = reinterpret_cast<const char*>(ws);
-  p.count = reinterpret_cast<const int32_t*>(b);
-  p.tiles = reinterpret_cast<const int4*>(b + kPlanHeaderBytes);
-  p.subtiles = reinterpret_cast<const int4*>(b + subtile_offset);
-  return p;
+// ------------------------------------------------------------ block scan
+__device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << __lane_id()) - 1ull; }
+
+// Exclusive scan of one value per thread across a workgroup of W waves;
+// *total receives the sum over the workgroup.  Contains barriers: every
+// thread of the workgroup must call it.
+template <int W, typename V>
+__device__ V block_exclusive_scan(V v, V* s_wsum, V* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  V x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    V y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) s_wsum[w] = x;
+  __syncthreads();
+  if (w == 0) {
+    V s = lane < W ? s_wsum[lane] : V(0);
+#pragma unroll
+    for (int d = 1; d < W; d <<= 1) {
+      V y = __shfl_up(s, d);
+      if (lane >= d) s += y;
+    }
+    if (lane < W) s_wsum[lane] = s;
+  }
+  __syncthreads();
+  const V before = w > 0 ? s_wsum[w - 1] : V(0);
+  *total = s_wsum[W - 1];
+  __syncthreads();
+  return before + x - v;
 }
 
 }  // namespace lora

@@ -4,10 +4,14 @@
 // common padded rank for the comparison variant): the explicit retained-rank
 // representation of "LoRAForge: Co-Designing Compression and Execution for
 // More Efficient Multi-LoRA Serving" (section "LoRAForge's Core Design").
-//   A_pack  row row_off[a] + j  <-  row j of A_a         (j < r_a; zero above)
-//   Bt_pack row row_off[a] + j  <-  column j of B_a      (j < r_a; zero above)
-// B_a is stored transposed so that the expand reads, for one rank index j,
-// a contiguous run of output features.
+//   A_pack: rows row_off[a] .. row_off[a] + stored - 1 are the rows of A_a
+//           ([r_a, d_in] row-major), then zero rows up to the stored rank;
+//   B_pack: elements row_off[a] * d_out .. are B_a in its own [d_out, r_a]
+//           row-major orientation, each row widened with zeros to the
+//           stored rank.
+// Both factors keep the orientation the adapter was trained in, so packing
+// is a copy, and the expand reads a run of consecutive rows of B_a (all
+// ranks of 128 output features) as one contiguous block.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -48,38 +52,33 @@ __global__ void __launch_bounds__(256) pack_a_kernel(const int32_t* __restrict__
   }
 }
 
-// One block per (128-feature tile, adapter): stage B_a[o0:o0+128, :r_a] in
-// LDS (a contiguous run of B_a), then write rows of Bt_pack.
-constexpr int kPackTile = 128;
+// One block per (adapter, run of kPackRows rows of B_a): element (o, j) of
+// the adapter's block is B_a[o, j] for j < r_a and zero for the padded
+// columns r_a <= j < stored rank.
+constexpr int kPackRows = 256;
 
 template <typename E>
-__global__ void __launch_bounds__(256) pack_bt_kernel(const int32_t* __restrict__ row_off,
-                                                      const int32_t* __restrict__ true_rank,
-                                                      const void* const* __restrict__ b_ptrs,
-                                                      int d_out, void* __restrict__ bt_pack) {
+__global__ void __launch_bounds__(256) pack_b_kernel(const int32_t* __restrict__ row_off,
+                                                     const int32_t* __restrict__ true_rank,
+                                                     const void* const* __restrict__ b_ptrs,
+                                                     int d_out, void* __restrict__ b_pack) {
   typedef typename E::storage S;
-  __shared__ S tile[kPackTile * LORA_MAX_RANK];
   const int a = blockIdx.y;
-  const int o0 = blockIdx.x * kPackTile;
+  const int o0 = blockIdx.x * kPackRows;
   const int r = true_rank[a];
-  const int row0 = row_off[a];
-  const int stored = row_off[a + 1] - row0;
-  if (stored == 0) return;
-  const int ot = min(kPackTile, d_out - o0);
-  if (r > 0) {
-    const S* src = reinterpret_cast<const S*>(b_ptrs[a]) + (size_t)o0 * r;
-    for (int idx = threadIdx.x; idx < ot * r; idx += blockDim.x) tile[idx] = src[idx];
-  }
-  __syncthreads();
-  S* dst = reinterpret_cast<S*>(bt_pack);
-  const int o = threadIdx.x % kPackTile;
-  for (int j = threadIdx.x / kPackTile; j < stored; j += blockDim.x / kPackTile) {
-    if (o < ot) dst[(size_t)(row0 + j) * d_out + o0 + o] = j < r ? tile[o * r + j] : S(0);
+  const int stored = row_off[a + 1] - row_off[a];
+  if (stored == 0 || o0 >= d_out) return;
+  const int rows = min(kPackRows, d_out - o0);
+  const S* src = r > 0 ? reinterpret_cast<const S*>(b_ptrs[a]) + (size_t)o0 * r : nullptr;
+  S* dst = reinterpret_cast<S*>(b_pack) + (size_t)row_off[a] * d_out + (size_t)o0 * stored;
+  for (int idx = threadIdx.x; idx < rows * stored; idx += blockDim.x) {
+    const int o = idx / stored, j = idx - o * stored;
+    dst[idx] = j < r ? src[(size_t)o * r + j] : S(0);
   }
 }
 
 hipError_t launch_pack(int dtype, const void* meta, int n, int d_in, int d_out, int rows,
-                       void* a_pack, void* bt_pack, hipStream_t stream) {
+                       void* a_pack, void* b_pack, hipStream_t stream) {
   const char* m = reinterpret_cast<const char*>(meta);
   const int32_t* row_off = reinterpret_cast<const int32_t*>(m);
   const int32_t* true_rank = row_off + (n + 1) + 2 * n;
@@ -94,13 +93,13 @@ hipError_t launch_pack(int dtype, const void* meta, int n, int d_in, int d_out, 
                          a_ptrs, n, d_in, a_pack);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 grid((d_out + kPackTile - 1) / kPackTile, n);
+    dim3 grid((d_out + kPackRows - 1) / kPackRows, n);
     if (dtype == LORA_DTYPE_BF16)
-      hipLaunchKernelGGL(pack_bt_kernel<BF16>, grid, dim3(256), 0, stream, row_off, true_rank, b_ptrs,
-                         d_out, bt_pack);
+      hipLaunchKernelGGL(pack_b_kernel<BF16>, grid, dim3(256), 0, stream, row_off, true_rank, b_ptrs,
+                         d_out, b_pack);
     else
-      hipLaunchKernelGGL(pack_bt_kernel<F32>, grid, dim3(256), 0, stream, row_off, true_rank, b_ptrs,
-                         d_out, bt_pack);
+      hipLaunchKernelGGL(pack_b_kernel<F32>, grid, dim3(256), 0, stream, row_off, true_rank, b_ptrs,
+                         d_out, b_pack);
   }
   return hipGetLastError();
 }

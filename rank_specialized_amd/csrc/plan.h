@@ -1,5 +1,6 @@
-// Internal sizes shared by the host dispatcher and the validation code.
-// No HIP types: this header is also compiled by the host-only validator.
+// Internal sizes and layouts shared by the host dispatcher, the validation
+// code and the kernels.  No HIP types: also compiled by the host-only
+// validator.
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -8,14 +9,21 @@
 
 namespace lora {
 
-constexpr int kTile = LORA_TILE_TOKENS;  // tokens per work tile
-
-// Tiles of more than kSmallTile tokens take the matrix-core expand path;
-// smaller ones (decode) take the vector path.
-constexpr int kSmallTile = 4;
-// The shrink works on sub-tiles of at most kSubTile tokens (one MFMA column
-// block), so that every shrink workgroup moves a similar amount of data.
+// A sub-tile is a run of at most kSubTile tokens of one adapter in grouped
+// order: one 16-wide block of a matrix-core tile.
 constexpr int kSubTile = 16;
+
+// The shrink's workgroup: 16 waves share one (sub-tile, K chunk) item.
+constexpr int kShrinkWaves = 16;
+constexpr int kShrinkThreads = kShrinkWaves * 64;
+
+// The shrink groups tokens itself (histogram of the ids in LDS) when
+// n <= kGroupMaxN; beyond that the apply first runs the single-workgroup sort.
+constexpr int kGroupMaxN = 4096;
+
+// The expand's wave covers kExpandCols output features of one sub-tile.
+constexpr int kExpandCols = 128;
+constexpr int kExpandWaves = 4;  // waves per expand workgroup
 
 // Upper bound on the number of runs of at most `len` tokens that T tokens
 // over n adapters cut into: each non-empty group of c tokens gives
@@ -25,33 +33,79 @@ inline int64_t plan_max_runs(int T, int n, int len) {
   int64_t k = n < T ? n : T;
   return ((int64_t)T + (int64_t)(len - 1) * k) / len;
 }
-inline int64_t plan_max_tiles(int T, int n) { return plan_max_runs(T, n, kTile); }
 inline int64_t plan_max_subtiles(int T, int n) { return plan_max_runs(T, n, kSubTile); }
 
-// Plan layout: int32 header[16], then the expand tiles, then the shrink
-// sub-tiles; every entry is int4 {adapter, first grouped position, tokens, 0}.
-//   header[0] = expand tiles, header[1] = large ones (tokens > kSmallTile,
-//   listed first), header[2] = small ones, header[3] = shrink sub-tiles.
-constexpr size_t kPlanHeaderBytes = 64;
-inline size_t plan_subtile_offset(int T, int n) {
-  return kPlanHeaderBytes + 16 * (size_t)plan_max_tiles(T, n);
-}
+// The work plan: a 256-byte header (int32 [0] = number of sub-tiles), then
+// one 128-byte entry per sub-tile, in adapter order.  Written by the shrink
+// (or by the plan kernel) and read by the expand and the partial-sum reduce.
+struct TileEntry {
+  int32_t a;        // adapter
+  int32_t pos0;     // grouped position of the first token
+  int32_t m;        // tokens (1..kSubTile)
+  int32_t r;        // stored rank
+  int32_t row_off;  // first row of the adapter in the store
+  float scale;      // s_a
+  int32_t pad0[2];
+  int32_t tok[kSubTile];  // token indices, ascending
+  int32_t pad1[8];
+};
+static_assert(sizeof(TileEntry) == 128, "entry is one 128-byte line");
+constexpr size_t kPlanHeaderBytes = 256;
 inline size_t plan_bytes(int T, int n) {
-  if (T < 0 || n < 0) return 0;
-  return plan_subtile_offset(T, n) + 16 * (size_t)plan_max_subtiles(T, n);
+  return kPlanHeaderBytes + sizeof(TileEntry) * (size_t)plan_max_subtiles(T, n);
 }
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
-
 inline int elem_bytes(int dtype) { return dtype == LORA_DTYPE_BF16 ? 2 : 4; }
 inline int vec_elems(int dtype) { return dtype == LORA_DTYPE_BF16 ? 8 : 4; }  // 16-byte vectors
+
+// The shrink splits d_in into S chunks; each of the 16 waves of an item
+// takes `spw` consecutive K steps (a step is 4 x 16 bytes of K: 32 bf16 or
+// 16 f32 values).  spw is the per-batch step count the register budget
+// allows (4 for up to 32 retained ranks, 2 above), S at most 8 (more steps
+// per wave, in batches, for very wide inputs).
+struct ShrinkSplit {
+  int spw;     // K steps per wave
+  int S;       // K chunks (partial sums per output)
+  int kchunk;  // K elements per chunk = 16 * spw * step
+};
+inline ShrinkSplit shrink_split(int d_in, int r_max, int dtype) {
+  const int step = 4 * vec_elems(dtype);
+  const int steps = (d_in + step - 1) / step;
+  const int ng = r_max <= 16 ? 1 : (r_max + 15) / 16;
+  int spw = ng <= 2 ? 4 : 2;
+  int S = (steps + kShrinkWaves * spw - 1) / (kShrinkWaves * spw);
+  if (S > 8) {
+    spw = (steps + kShrinkWaves * 8 - 1) / (kShrinkWaves * 8);
+    S = (steps + kShrinkWaves * spw - 1) / (kShrinkWaves * spw);
+  }
+  return ShrinkSplit{spw, S, kShrinkWaves * spw * step};
+}
+
+// Row stride (floats) of the float32 partial sums: r_max rounded up to 8 so
+// that every 8-value rank chunk a lane reads lies inside its row.
+inline int64_t partial_ld(int r_max) { return (int64_t)align_up((size_t)(r_max < 1 ? 1 : r_max), 8); }
+
+// Workspace of shrink / expand / apply, each part 256-byte aligned:
+//   plan | partial sums [S][T][ldp] float32 | seg_off [n+2] | perm [T]
+// (the last two only when the apply has to sort: n > kGroupMaxN).
+struct WsLayout {
+  size_t plan, part, seg_off, perm, total;
+};
+inline WsLayout ws_layout(int T, int n, int d_in, int r_max, int dtype) {
+  WsLayout L;
+  const ShrinkSplit sp = shrink_split(d_in, r_max, dtype);
+  L.plan = 0;
+  L.part = align_up(plan_bytes(T, n), 256);
+  L.seg_off = L.part + align_up((size_t)sp.S * (size_t)T * (size_t)partial_ld(r_max) * 4, 256);
+  L.perm = L.seg_off + (n > kGroupMaxN ? align_up((size_t)(n + 2) * 4, 256) : 0);
+  L.total = L.perm + (n > kGroupMaxN ? align_up((size_t)T * 4, 256) : 0);
+  return L;
+}
 
 // Meta buffer of a store: row_off[n+1] | rank[n] (stored) | scale[n] |
 // true_rank[n] (before padding) | (16-aligned) A pointers[n] | B pointers[n].
 inline size_t meta_ptr_offset(int n) { return align_up((size_t)(4 * (size_t)n + 1) * 4, 16); }
 inline size_t meta_bytes(int n) { return meta_ptr_offset(n) + 16 * (size_t)n; }
-
-// h leading dimension used inside lora_apply_batched.
-inline int64_t apply_ldh(int r_max) { return r_max < 4 ? 4 : (int64_t)align_up((size_t)r_max, 4); }
 
 }  // namespace lora

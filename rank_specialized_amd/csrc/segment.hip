@@ -17,9 +17,6 @@
 //     wave) counts are scanned in digit-major, wave-minor order, which places
 //     earlier waves first.
 //  3. perm = low bits of the sorted keys; seg_off[b] = lower_bound(b).
-//  4. Tile plan: every adapter group is cut into expand tiles and shrink
-//     sub-tiles; one block scan (three counts packed in 64 bits) gives each
-//     run its slot.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -29,92 +26,11 @@ constexpr int kDigitBits = 8;
 constexpr int kDigits = 1 << kDigitBits;
 constexpr int kSmallSegT = 2048;  // T up to this uses the 4-wave variant
 
-__device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << __lane_id()) - 1ull; }
-
-// Exclusive scan of one value per thread across a block of W waves.
-template <int W, typename V>
-__device__ V block_exclusive_scan(V v, V* s_wsum, V* total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  V x = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    V y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) s_wsum[w] = x;
-  __syncthreads();
-  if (w == 0) {
-    V s = lane < W ? s_wsum[lane] : V(0);
-#pragma unroll
-    for (int d = 1; d < W; d <<= 1) {
-      V y = __shfl_up(s, d);
-      if (lane >= d) s += y;
-    }
-    if (lane < W) s_wsum[lane] = s;
-  }
-  __syncthreads();
-  const V before = w > 0 ? s_wsum[w - 1] : V(0);
-  *total = s_wsum[W - 1];
-  __syncthreads();
-  return before + x - v;
-}
-
-// Tile plan from group offsets held in LDS (so[0..n]).  Every adapter group
-// of c tokens is cut into runs of kTile tokens (expand tiles; runs of more
-// than kSmallTile tokens go to the "large" list, written first) and into runs
-// of kSubTile tokens (shrink sub-tiles).  Each list is ordered by adapter,
-// then position.
-template <int W>
-__device__ void build_tiles(const int32_t* so, int n, void* plan_ws, size_t sub_off,
-                            unsigned long long* s_wsum) {
-  constexpr int THREADS = W * 64;
-  const int per = (n + THREADS - 1) / THREADS;
-  const int a0 = threadIdx.x * per;
-  const int a1 = min(n, a0 + per);
-  // Three counts (each < 2^21) packed in one 64-bit value: large | small << 21 | sub << 42.
-  unsigned long long packed = 0;
-  for (int a = a0; a < a1; ++a) {
-    const int c = so[a + 1] - so[a];
-    const int rem = c % kTile;
-    const unsigned long long nl = (unsigned long long)(c / kTile + (rem > kSmallTile ? 1 : 0));
-    const unsigned long long ns = (rem > 0 && rem <= kSmallTile) ? 1ull : 0ull;
-    const unsigned long long nsub = (unsigned long long)((c + kSubTile - 1) / kSubTile);
-    packed += nl | (ns << 21) | (nsub << 42);
-  }
-  unsigned long long total;
-  const unsigned long long pre = block_exclusive_scan<W>(packed, s_wsum, &total);
-  const unsigned long long mask = (1ull << 21) - 1;
-  const int total_large = (int)(total & mask), total_small = (int)((total >> 21) & mask);
-  const int total_sub = (int)(total >> 42);
-  int slot_large = (int)(pre & mask);
-  int slot_small = (int)((pre >> 21) & mask) + total_large;
-  int slot_sub = (int)(pre >> 42);
-  char* base = reinterpret_cast<char*>(plan_ws);
-  int4* tiles = reinterpret_cast<int4*>(base + kPlanHeaderBytes);
-  int4* subs = reinterpret_cast<int4*>(base + sub_off);
-  for (int a = a0; a < a1; ++a) {
-    const int start = so[a], c = so[a + 1] - so[a];
-    for (int k = 0; k < c; k += kTile) {
-      const int m = min(kTile, c - k);
-      const int4 t = make_int4(a, start + k, m, 0);
-      if (m > kSmallTile) tiles[slot_large++] = t; else tiles[slot_small++] = t;
-    }
-    for (int k = 0; k < c; k += kSubTile) subs[slot_sub++] = make_int4(a, start + k, min(kSubTile, c - k), 0);
-  }
-  if (threadIdx.x == 0) {
-    int32_t* hdr = reinterpret_cast<int32_t*>(plan_ws);
-    hdr[0] = total_large + total_small;
-    hdr[1] = total_large;
-    hdr[2] = total_small;
-    hdr[3] = total_sub;
-  }
-}
-
 template <int W>
 __global__ void __launch_bounds__(W * 64)
 segment_kernel(const int32_t* __restrict__ ids, int T, int n, int tbits, int passes, int cap,
                int32_t* __restrict__ seg_off, int32_t* __restrict__ perm,
-               int32_t* __restrict__ n_invalid, void* __restrict__ plan_ws, size_t sub_off) {
+               int32_t* __restrict__ n_invalid) {
   constexpr int THREADS = W * 64;
   constexpr int MAXB = (W == 4 ? kSmallSegT : LORA_SEGMENT_MAX_T) / THREADS;  // batches of 64 per wave
   constexpr int PER = kDigits * W / THREADS;                                   // scan entries per thread
@@ -207,7 +123,6 @@ segment_kernel(const int32_t* __restrict__ ids, int T, int n, int tbits, int pas
 
   const uint32_t tmask = (1u << tbits) - 1u;
   for (int i = tid; i < T; i += THREADS) perm[i] = (int32_t)(in[i] & tmask);
-  int32_t* so = reinterpret_cast<int32_t*>(out);  // cap >= n + 2
   for (int b = tid; b <= n + 1; b += THREADS) {
     const uint32_t target = (uint32_t)b << tbits;
     int lo = 0, hi = T;
@@ -215,23 +130,10 @@ segment_kernel(const int32_t* __restrict__ ids, int T, int n, int tbits, int pas
       const int mid = (lo + hi) >> 1;
       if (in[mid] < target) lo = mid + 1; else hi = mid;
     }
-    so[b] = lo;
     seg_off[b] = lo;
   }
   __syncthreads();
   if (tid == 0 && n_invalid != nullptr) *n_invalid = s_inval;
-  build_tiles<W>(so, n, plan_ws, sub_off, s_wsum);
-}
-
-__global__ void __launch_bounds__(1024)
-plan_from_offsets_kernel(const int32_t* __restrict__ seg_off, int n, void* __restrict__ plan_ws,
-                         size_t sub_off) {
-  extern __shared__ uint32_t dyn[];
-  __shared__ unsigned long long s_wsum[16];
-  int32_t* so = reinterpret_cast<int32_t*>(dyn);
-  for (int b = threadIdx.x; b <= n; b += 1024) so[b] = seg_off[b];
-  __syncthreads();
-  build_tiles<16>(so, n, plan_ws, sub_off, s_wsum);
 }
 
 static int bits_for(int v) {  // smallest b >= 1 with 2^b > v
@@ -249,7 +151,7 @@ size_t segment_static_lds_bytes() { return 16 * kDigits * 4 + 16 * 8 + 16; }
 
 template <int W>
 static hipError_t launch_segment_w(const int32_t* ids, int T, int n, int32_t* seg_off, int32_t* perm,
-                                   int32_t* n_invalid, void* plan_ws, hipStream_t stream) {
+                                   int32_t* n_invalid, hipStream_t stream) {
   const int tbits = T > 1 ? bits_for(T - 1) : 1;
   const int gbits = bits_for(n);  // group ids 0..n
   const int passes = (gbits + kDigitBits - 1) / kDigitBits;
@@ -263,29 +165,14 @@ static hipError_t launch_segment_w(const int32_t* ids, int T, int n, int32_t* se
     raised = lds;
   }
   hipLaunchKernelGGL(segment_kernel<W>, dim3(1), dim3(W * 64), lds, stream, ids, T, n, tbits, passes, cap,
-                     seg_off, perm, n_invalid, plan_ws, plan_subtile_offset(T, n));
+                     seg_off, perm, n_invalid);
   return hipGetLastError();
 }
 
 hipError_t launch_segment(const int32_t* ids, int T, int n, int32_t* seg_off, int32_t* perm,
-                          int32_t* n_invalid, void* plan_ws, hipStream_t stream) {
-  if (T <= kSmallSegT) return launch_segment_w<4>(ids, T, n, seg_off, perm, n_invalid, plan_ws, stream);
-  return launch_segment_w<16>(ids, T, n, seg_off, perm, n_invalid, plan_ws, stream);
-}
-
-hipError_t launch_plan_from_offsets(const int32_t* seg_off, int T, int n, void* plan_ws,
-                                    hipStream_t stream) {
-  const size_t lds = (size_t)(n + 2) * 4;
-  static size_t raised = 48 * 1024;
-  if (lds > raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(plan_from_offsets_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    raised = lds;
-  }
-  hipLaunchKernelGGL(plan_from_offsets_kernel, dim3(1), dim3(1024), lds, stream, seg_off, n, plan_ws,
-                     plan_subtile_offset(T, n));
-  return hipGetLastError();
+                          int32_t* n_invalid, hipStream_t stream) {
+  if (T <= kSmallSegT) return launch_segment_w<4>(ids, T, n, seg_off, perm, n_invalid, stream);
+  return launch_segment_w<16>(ids, T, n, seg_off, perm, n_invalid, stream);
 }
 
 }  // namespace lora

@@ -1,117 +1,456 @@
 // Shrink: h[i, j] = sum_k A_a[j, k] x[perm[i], k]   (j < r_a), float32.
 //
 // Step 1 of the two-step branch in "Compress then Serve: Serving Thousands
-// of LoRA Adapters with Little Overhead", section 13.4 (A applied with scale
-// 1 into a float32 buffer of shape [tokens, R]).  Rows of h follow the
-// grouped order, so one tile's rows are contiguous.
+// of LoRA Adapters with Little Overhead", section 13.4: A applied with scale
+// 1 into a float32 buffer of shape [tokens, R].  Tokens are taken in groups
+// of one adapter (the segmented gather of its section 2), so each adapter's
+// retained rows are read once per sub-tile of at most 16 of its tokens.
 //
-// One workgroup of 16 waves per sub-tile (<= 16 tokens of one adapter).  A
-// sub-tile is the skinny GEMM  H^T[r_a x m] = A_a[r_a x d_in] . X^T[d_in x m]
-// on 16x16 MFMA tiles whatever m is: the matrix core does the d_in
-// reduction, so a one-token decode segment needs no cross-lane reduction.
-// Rows j >= r_a and tokens >= m are never loaded (zero operands): memory
-// traffic is the retained rows (once per sub-tile) plus the tile's x rows.
-// The 16 waves split d_in into 16 chunks, so even a decode batch of a few
-// hundred tokens spreads over thousands of waves, and a popular adapter's
-// tokens spread over several CUs (a CU's own bandwidth is the limit
-// otherwise).  The waves' float32 partial tiles are summed in LDS in a fixed
-// order (deterministic, no atomics) and written to h once.
+// Work item = (sub-tile, K chunk); one workgroup of 16 waves per item, a
+// grid-stride loop over the items.  A sub-tile is the skinny GEMM
+//   H^T[r_a x m] = A_a[r_a x d_in] . X^T[d_in x m]      (m <= 16)
+// on 16x16 MFMA tiles whatever m is.  d_in is cut into S chunks (S <= 8) so
+// that a popular or high-rank adapter's rows spread over several CUs; inside
+// an item each wave takes `spw` consecutive K steps and issues all of their
+// loads before the first MFMA.  The 16 waves' float32 tiles are summed in
+// LDS in wave order, and chunk kc's sum is written as partial kc; the
+// consumer adds the S partials in chunk order.  No atomics: results are
+// deterministic.
+//
+// Token grouping happens inside every workgroup, so no separate launch and
+// no round trip through memory precede the factor loads:
+//  * from ids (n <= 4096): a histogram of the ids in LDS, one block scan of
+//    (tokens, sub-tiles) per adapter, and for each item the sub-tile's
+//    tokens by a ballot rank over the ids (tokens keep ascending index);
+//  * from a grouping (seg_off, perm): the same scan over seg_off.
+// Every adapter's rank, row offset and scale are loaded while the histogram
+// forms (one load each per thread), so the item loop finds its adapter's
+// metadata in the cache.
+// Item 0 of each sub-tile writes the sub-tile's plan entry (adapter,
+// position, tokens, rank, row offset, scale) for the expand.
 //
 // Rank specialization: NG = ceil(r_a / 16) row groups is a template
-// parameter; each instantiation keeps exactly its accumulators and issues U
-// K-steps of loads back to back (U sized so the loads in flight fit the
-// register budget of a 1024-thread workgroup).
-//
-// Inside a wave, step s covers K indices [k0 + s * 32, +32) (bf16): lane
-// group g (lanes 16g..16g+15) takes the g-th 16 bytes of it, so the four lane
-// groups of a row read 64 contiguous bytes per instruction and two
-// consecutive steps consume whole 128-byte lines.  Both operands of every
-// MFMA carry the same K indices (the contraction is a plain sum over K, so
-// any K order that is identical for the two operands is exact).
+// parameter; rows j >= r_a and tokens >= m are never loaded.
 #include "device_common.h"
 #include "kernels.h"
 #include "tile_ops.h"
 
 namespace lora {
 
-constexpr int kShrinkWaves = 16;
-constexpr int kShrinkThreads = kShrinkWaves * kWave;
+constexpr int kMaxBlocks64 = LORA_SEGMENT_MAX_T / 64;  // 64-token blocks of the ids
 
-// red: [16 slots][ng_max][64 lanes] of f32x4; slot = wave = K chunk.
-template <typename E>
-__global__ void __launch_bounds__(kShrinkThreads)
-shrink_kernel(const char* __restrict__ x, int64_t ldx_bytes, const char* __restrict__ a_pack,
-              const int32_t* __restrict__ row_off, const int32_t* __restrict__ rank, int d_in, int ng_max,
-              const int32_t* __restrict__ perm, const void* __restrict__ plan_ws, size_t sub_off,
-              float* __restrict__ h, int64_t ldh) {
-  extern __shared__ f32x4_t red[];
+struct ShrinkArgs {
+  const int32_t* ids;      // ids mode
+  const int32_t* seg_off;  // grouping mode
+  const int32_t* perm;     // grouping mode
+  int T, n, max_sub;
+  const char* x;
+  int64_t ldx_bytes;
+  const char* a_pack;
+  const int32_t* row_off;
+  const int32_t* rank;
+  const float* scale;
+  int d_in, ng_max, spw, S, kchunk;
+  float* part;
+  int64_t ldp, pstride;  // floats: row stride, distance between partials
+  char* plan;
+  int warm_key;
+};
+
+template <typename E, bool kIds, int APT>
+__global__ void __launch_bounds__(kShrinkThreads) shrink_kernel(ShrinkArgs p) {
   constexpr int KSTEP = 4 * E::kVec;
-  const Plan pl = plan_view(plan_ws, sub_off);
-  const int t = blockIdx.x;  // grid = sub-tile capacity, so subtiles[t] is in bounds
-  const int4 tile = pl.subtiles[t];
-  const int count = pl.count[3];
-  if (t >= count) return;
-  const int a = tile.x, p0 = tile.y, m = tile.z;  // m <= kSubTile
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int tl = lane & 15;
-  const bool tval = tl < m;
-  const int tok = tval ? perm[p0 + tl] : 0;
-  const int r = rank[a];
-  const int ro = row_off[a];
-  if (r <= 0) return;  // uniform over the workgroup
-  const int ng = (r + 15) >> 4;
-  int kc = (d_in + kShrinkWaves - 1) / kShrinkWaves;
-  kc = (kc + KSTEP - 1) / KSTEP * KSTEP;
-  const int k0 = w * kc;
-  const char* xrow = x + (int64_t)tok * ldx_bytes;
-  const char* a_rows = a_pack + (size_t)ro * d_in * E::kBytes;
-  f32x4_t* slot = red + w * ng_max * 64;
-  switch (ng) {
-    case 1: shrink_wave<E, 1>(xrow, tval, a_rows, d_in, r, k0, kc, slot); break;
-    case 2: shrink_wave<E, 2>(xrow, tval, a_rows, d_in, r, k0, kc, slot); break;
-    case 3: shrink_wave<E, 3>(xrow, tval, a_rows, d_in, r, k0, kc, slot); break;
-    default: shrink_wave<E, 4>(xrow, tval, a_rows, d_in, r, k0, kc, slot); break;
+  extern __shared__ __align__(16) char dyn[];
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(dyn);  // [16 waves][ng_max][64 lanes]
+  int* cnt = reinterpret_cast<int*>(dyn + (size_t)p.ng_max * kShrinkWaves * 64 * 16);  // [n]
+  uint16_t* id16 = reinterpret_cast<uint16_t*>(cnt + ((p.n + 3) & ~3));                // [T]
+  __shared__ uint64_t s_wsum[kShrinkWaves];
+  __shared__ int s_tile[8];
+  __shared__ int s_tok[kSubTile];
+  __shared__ int s_bc[kMaxBlocks64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = p.n, T = p.T;
+
+  // 1. Tokens per adapter, and this thread's adapters [a0, a0 + APT).
+  if (kIds) {
+    for (int i = tid; i < n; i += kShrinkThreads) cnt[i] = 0;
+    __syncthreads();
+  }
+  const int a0 = tid * APT;
+  int cnt_[APT], rk_[APT];
+  // The row offsets and scales of this thread's adapters are loaded now and
+  // only folded into a value that is never stored in practice: the loads
+  // bring them into the cache while the histogram forms, so the item loop
+  // below finds its adapter's metadata there.
+  int warm = 0;
+#pragma unroll
+  for (int i = 0; i < APT; ++i) {
+    const int a = a0 + i;
+    const bool v = a < n;
+    rk_[i] = v ? p.rank[a] : 0;
+    if (v) warm ^= p.row_off[a] ^ __float_as_int(p.scale[a]);
+    cnt_[i] = (!kIds && v) ? p.seg_off[a + 1] - p.seg_off[a] : 0;
+  }
+  if (kIds) {
+    for (int t = tid; t < T; t += kShrinkThreads) {
+      const int v = p.ids[t];
+      const bool ok = (unsigned)v < (unsigned)n;
+      id16[t] = ok ? (uint16_t)v : (uint16_t)0xFFFFu;
+      if (ok) atomicAdd(&cnt[v], 1);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < APT; ++i) cnt_[i] = a0 + i < n ? cnt[a0 + i] : 0;
+  }
+  if (warm == p.warm_key) s_tile[7] = warm;  // warm_key is never produced by valid metadata
+  // 2. Exclusive scan of (tokens << 32 | sub-tiles) in adapter order; each
+  //    adapter's (tokens << 16 | sub-tiles) is kept for the item loop.
+  uint64_t mine = 0;
+  uint32_t cs_[APT];
+#pragma unroll
+  for (int i = 0; i < APT; ++i) {
+    const int c = cnt_[i] < 0 ? 0 : (cnt_[i] > T ? T : cnt_[i]);  // T < 2^16
+    const int sub = rk_[i] > 0 ? (c + kSubTile - 1) / kSubTile : 0;
+    cs_[i] = ((uint32_t)c << 16) | (uint32_t)sub;
+    mine += ((uint64_t)c << 32) | (uint64_t)sub;
+  }
+  uint64_t tot;
+  const uint64_t pre = block_exclusive_scan<kShrinkWaves>(mine, s_wsum, &tot);
+  const int total_sub = min((int)(tot & 0xffffffffu), p.max_sub);
+  if (blockIdx.x == 0 && tid == 0) *reinterpret_cast<int32_t*>(p.plan) = total_sub;
+  const int base_pos = kIds ? 0 : p.seg_off[0];
+  const int items = total_sub * p.S;
+  TileEntry* entries = reinterpret_cast<TileEntry*>(p.plan + kPlanHeaderBytes);
+
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    const int st = item / p.S, kc = item - st * p.S;
+    // 3. The adapter that owns sub-tile st.
+    {
+      int s = (int)(pre & 0xffffffffu), pos = base_pos + (int)(pre >> 32);
+#pragma unroll
+      for (int i = 0; i < APT; ++i) {
+        const int c = (int)(cs_[i] >> 16), sub = (int)(cs_[i] & 0xffffu);
+        if (st >= s && st < s + sub) {
+          const int j = st - s;
+          const int a = a0 + i;
+          s_tile[0] = a;
+          s_tile[1] = pos + j * kSubTile;
+          s_tile[2] = min(kSubTile, c - j * kSubTile);
+          s_tile[3] = p.rank[a];
+          s_tile[4] = p.row_off[a];
+          s_tile[5] = __float_as_int(p.scale[a]);
+          s_tile[6] = j;
+        }
+        s += sub;
+        pos += c;
+      }
+    }
+    __syncthreads();
+    const int a = s_tile[0], pos0 = s_tile[1], m = s_tile[2], r = s_tile[3], jt = s_tile[6];
+    const int ro = s_tile[4];
+    const float sc = __int_as_float(s_tile[5]);
+    // 4. The sub-tile's tokens: ranks [16 jt, 16 jt + 16) among the tokens of
+    //    adapter a, in token order.
+    if (kIds) {
+      const int nb = (T + 63) >> 6;
+      for (int b = w; b < nb; b += kShrinkWaves) {
+        const int t = b * 64 + lane;
+        const uint64_t bal = __ballot(t < T && id16[t] == (uint16_t)a);
+        if (lane == 0) s_bc[b] = __popcll(bal);
+      }
+      __syncthreads();
+      if (w == 0) {  // exclusive scan of the block counts (4 per lane)
+        int v[4], sum = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int idx = lane * 4 + q;
+          v[q] = idx < nb ? s_bc[idx] : 0;
+          sum += v[q];
+        }
+        int x = sum;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int y = __shfl_up(x, d);
+          if (lane >= d) x += y;
+        }
+        int run = x - sum;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int idx = lane * 4 + q;
+          if (idx < nb) s_bc[idx] = run;
+          run += v[q];
+        }
+      }
+      __syncthreads();
+      for (int b = w; b < nb; b += kShrinkWaves) {
+        const int t = b * 64 + lane;
+        const bool hit = t < T && id16[t] == (uint16_t)a;
+        const uint64_t bal = __ballot(hit);
+        const int rk = s_bc[b] + __popcll(bal & lanemask_lt()) - jt * kSubTile;
+        if (hit && rk >= 0 && rk < kSubTile) s_tok[rk] = t;
+      }
+    } else if (tid < m) {
+      const int q = pos0 + tid;
+      const int tk = (q >= 0 && q < T) ? p.perm[q] : -1;
+      s_tok[tid] = (unsigned)tk < (unsigned)T ? tk : -1;
+    }
+    __syncthreads();
+    // 5. This wave's K steps of chunk kc.
+    const int ng = (r + 15) >> 4;
+    {
+      const int tl = lane & 15;
+      const int tk = tl < m ? s_tok[tl] : -1;
+      const bool tval = tk >= 0;
+      const char* xrow = p.x + (int64_t)(tval ? tk : 0) * p.ldx_bytes;
+      const char* a_rows = p.a_pack + (size_t)ro * p.d_in * E::kBytes;
+      const int k0 = kc * p.kchunk + w * p.spw * KSTEP;
+      const int kw = p.spw * KSTEP;
+      f32x4_t* slot = red + w * p.ng_max * 64;
+      switch (ng) {
+        case 1: shrink_wave<E, 1, 4>(xrow, tval, a_rows, p.d_in, r, k0, kw, slot); break;
+        case 2: shrink_wave<E, 2, 4>(xrow, tval, a_rows, p.d_in, r, k0, kw, slot); break;
+        case 3: shrink_wave<E, 3, 2>(xrow, tval, a_rows, p.d_in, r, k0, kw, slot); break;
+        default: shrink_wave<E, 4, 2>(xrow, tval, a_rows, p.d_in, r, k0, kw, slot); break;
+      }
+    }
+    __syncthreads();
+    // 6. Sum the 16 waves' tiles in wave order; write partial kc.  Lane l of
+    //    row group q holds token l % 16, ranks 16 q + 4 (l / 16) + 0..3.
+    if (tid < ng * 64) {
+      const int q = tid >> 6, l = tid & 63;
+      f32x4_t s = red[q * 64 + l];
+#pragma unroll
+      for (int k = 1; k < kShrinkWaves; ++k) s += red[(k * p.ng_max + q) * 64 + l];
+      const int tk = l & 15;
+      const int j0 = q * 16 + 4 * (l >> 4);
+      const int row = pos0 + tk;
+      if (tk < m && row >= 0 && row < T) {
+        float* dst = p.part + (int64_t)kc * p.pstride + (int64_t)row * p.ldp + j0;
+        if (j0 + 3 < r) {
+          *reinterpret_cast<f32x4_t*>(dst) = s;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j0 + e < r) dst[e] = s[e];
+        }
+      }
+    }
+    if (kc == 0 && tid < 32) {
+      int v = 0;
+      if (tid == 0) v = a;
+      else if (tid == 1) v = pos0;
+      else if (tid == 2) v = m;
+      else if (tid == 3) v = r;
+      else if (tid == 4) v = ro;
+      else if (tid == 5) v = __float_as_int(sc);
+      else if (tid >= 8 && tid < 8 + kSubTile) v = tid - 8 < m ? s_tok[tid - 8] : -1;
+      reinterpret_cast<int32_t*>(entries + st)[tid] = v;
+    }
+    __syncthreads();  // s_tile, s_tok and red are rewritten by the next item
+  }
+}
+
+// ------------------------------------------------------------- reduce
+// h[pos, j] = partial 0 + partial 1 + ... (chunk order, as the expand sums
+// them), for every sub-tile of the plan.
+__global__ void __launch_bounds__(256)
+reduce_partials_kernel(const char* __restrict__ plan, int max_sub, const float* __restrict__ part,
+                       int64_t ldp, int64_t pstride, int S, int T, float* __restrict__ h, int64_t ldh) {
+  const int st = blockIdx.x;
+  const int count = min(*reinterpret_cast<const int32_t*>(plan), max_sub);
+  if (st >= count) return;
+  const TileEntry* e = reinterpret_cast<const TileEntry*>(plan + kPlanHeaderBytes) + st;
+  const int m = e->m, r = e->r, pos0 = e->pos0;
+  for (int idx = threadIdx.x; idx < m * r; idx += 256) {
+    const int i = idx / r, j = idx - i * r;
+    const int row = pos0 + i;
+    if (row < 0 || row >= T) continue;
+    const float* src = part + (int64_t)row * ldp + j;
+    float s = src[0];
+    for (int k = 1; k < S; ++k) s += src[(int64_t)k * pstride];
+    h[(int64_t)row * ldh + j] = s;
+  }
+}
+
+// --------------------------------------------------------------- plan
+// The plan of a caller-supplied grouping, for the standalone expand: one
+// workgroup scans the sub-tile counts, then writes the entries in parallel.
+template <int APT>
+__global__ void __launch_bounds__(1024)
+plan_kernel(const int32_t* __restrict__ seg_off, const int32_t* __restrict__ perm, int T, int n,
+            const int32_t* __restrict__ row_off, const int32_t* __restrict__ rank,
+            const float* __restrict__ scale, int max_sub, char* __restrict__ plan) {
+  extern __shared__ int s_sub[];  // [n + 1]: first sub-tile of each adapter
+  __shared__ uint64_t s_wsum[16];
+  const int tid = threadIdx.x;
+  const int a0 = tid * APT;
+  int sub_[APT];
+  uint64_t mine = 0;
+#pragma unroll
+  for (int i = 0; i < APT; ++i) {
+    const int a = a0 + i;
+    int c = a < n ? seg_off[a + 1] - seg_off[a] : 0;
+    c = c > 0 ? c : 0;
+    sub_[i] = (a < n && rank[a] > 0) ? (c + kSubTile - 1) / kSubTile : 0;
+    mine += (uint64_t)sub_[i];
+  }
+  uint64_t tot;
+  uint64_t s = block_exclusive_scan<16>(mine, s_wsum, &tot);
+#pragma unroll
+  for (int i = 0; i < APT; ++i) {
+    if (a0 + i < n) s_sub[a0 + i] = (int)s;
+    s += sub_[i];
+  }
+  const int total = min((int)tot, max_sub);
+  if (tid == 0) {
+    s_sub[n] = (int)tot;
+    *reinterpret_cast<int32_t*>(plan) = total;
   }
   __syncthreads();
-  // Sum the 16 slots of each (row group, lane, accumulator row) in slot order
-  // and write h.  Lane l of a partial tile holds token l % 16 and rank rows
-  // 4 * (l / 16) + 0..3 of its row group.
-  const float* redf = reinterpret_cast<const float*>(red);
-  for (int c = threadIdx.x; c < ng * 256; c += kShrinkThreads) {
-    const int v = c & 3, l = (c >> 2) & 63, q = c >> 8;
-    const int tk = l & 15;
-    const int j = q * 16 + 4 * (l >> 4) + v;
-    if (tk >= m || j >= r) continue;
-    float s = 0.f;
+  TileEntry* entries = reinterpret_cast<TileEntry*>(plan + kPlanHeaderBytes);
+  for (int st = tid; st < total; st += 1024) {
+    int lo = 0, hi = n;  // s_sub[lo] <= st < s_sub[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_sub[mid] <= st) lo = mid; else hi = mid;
+    }
+    const int a = lo, j = st - s_sub[a];
+    const int pos0 = seg_off[a] + j * kSubTile;
+    const int m = min(kSubTile, seg_off[a + 1] - pos0);
+    TileEntry e;
+    e.a = a;
+    e.pos0 = pos0;
+    e.m = m;
+    e.r = rank[a];
+    e.row_off = row_off[a];
+    e.scale = scale[a];
+    e.pad0[0] = e.pad0[1] = 0;
 #pragma unroll
-    for (int k = 0; k < kShrinkWaves; ++k) s += redf[((k * ng_max + q) * 64 + l) * 4 + v];
-    h[(int64_t)(p0 + tk) * ldh + j] = s;
+    for (int i = 0; i < kSubTile; ++i) {
+      const int q = pos0 + i;
+      const int tk = (i < m && q >= 0 && q < T) ? perm[q] : -1;
+      e.tok[i] = (unsigned)tk < (unsigned)T ? tk : -1;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) e.pad1[i] = 0;
+    entries[st] = e;
   }
 }
 
-size_t shrink_lds_bytes(int r_max) {
-  const int ng_max = r_max <= 0 ? 1 : (r_max + 15) / 16;
-  return (size_t)kShrinkWaves * ng_max * 64 * sizeof(float) * 4;
+// --------------------------------------------------------------- host
+static int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cached[dev] = v;
+  }
+  return cached[dev];
 }
 
-hipError_t launch_shrink(const lora_store& s, const void* x, int64_t ldx, int T, const int32_t* perm,
-                         const void* plan_ws, float* h, int64_t ldh, hipStream_t stream) {
-  const int64_t subs = plan_max_subtiles(T, s.n);
-  if (subs == 0) return hipSuccess;
-  const int ng_max = s.r_max <= 0 ? 1 : (s.r_max + 15) / 16;
-  const size_t lds = shrink_lds_bytes(s.r_max);
-  const size_t sub_off = plan_subtile_offset(T, s.n);
-  const int eb = elem_bytes(s.dtype);
-  if (s.dtype == LORA_DTYPE_BF16)
-    hipLaunchKernelGGL(shrink_kernel<BF16>, dim3((unsigned)subs), dim3(kShrinkThreads), lds, stream,
-                       reinterpret_cast<const char*>(x), ldx * eb,
-                       reinterpret_cast<const char*>(s.A_pack), s.row_off, s.rank, s.d_in, ng_max, perm,
-                       plan_ws, sub_off, h, ldh);
-  else
-    hipLaunchKernelGGL(shrink_kernel<F32>, dim3((unsigned)subs), dim3(kShrinkThreads), lds, stream,
-                       reinterpret_cast<const char*>(x), ldx * eb,
-                       reinterpret_cast<const char*>(s.A_pack), s.row_off, s.rank, s.d_in, ng_max, perm,
-                       plan_ws, sub_off, h, ldh);
+static int ng_of(int r_max) { return r_max <= 16 ? 1 : (r_max + 15) / 16; }
+
+size_t shrink_lds_bytes(int T, int n, int r_max, bool with_ids) {
+  size_t b = (size_t)ng_of(r_max) * kShrinkWaves * 64 * 16;
+  if (with_ids) b += (size_t)((n + 3) & ~3) * 4 + align_up((size_t)T * 2, 16);
+  return b;
+}
+
+template <typename E, bool kIds, int APT>
+static hipError_t launch_shrink_t(const ShrinkArgs& a, int grid, size_t lds, hipStream_t stream) {
+  auto fn = shrink_kernel<E, kIds, APT>;
+  static size_t raised = 48 * 1024;  // dynamic LDS above this needs the attribute
+  if (lds > raised) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    raised = lds;
+  }
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(kShrinkThreads), lds, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_shrink(const lora_store& s, const int32_t* ids, const int32_t* seg_off, const int32_t* perm,
+                         int T, const void* x, int64_t ldx, void* ws, hipStream_t stream) {
+  const ShrinkSplit sp = shrink_split(s.d_in, s.r_max, s.dtype);
+  const WsLayout L = ws_layout(T, s.n, s.d_in, s.r_max, s.dtype);
+  const int64_t max_sub = plan_max_subtiles(T, s.n);
+  if (max_sub == 0) return hipSuccess;
+  char* base = reinterpret_cast<char*>(ws);
+  ShrinkArgs a;
+  a.ids = ids;
+  a.seg_off = seg_off;
+  a.perm = perm;
+  a.T = T;
+  a.n = s.n;
+  a.max_sub = (int)max_sub;
+  a.x = reinterpret_cast<const char*>(x);
+  a.ldx_bytes = ldx * elem_bytes(s.dtype);
+  a.a_pack = reinterpret_cast<const char*>(s.A_pack);
+  a.row_off = s.row_off;
+  a.rank = s.rank;
+  a.scale = s.scale;
+  a.d_in = s.d_in;
+  a.ng_max = ng_of(s.r_max);
+  a.spw = sp.spw;
+  a.S = sp.S;
+  a.kchunk = sp.kchunk;
+  a.part = reinterpret_cast<float*>(base + L.part);
+  a.ldp = partial_ld(s.r_max);
+  a.pstride = (int64_t)T * a.ldp;
+  a.plan = base + L.plan;
+  a.warm_key = 0x7fc00001;  // a NaN pattern folded with row offsets: never equal in practice
+  const bool with_ids = ids != nullptr;
+  const size_t lds = shrink_lds_bytes(T, s.n, s.r_max, with_ids);
+  const int64_t items = max_sub * sp.S;
+  const int grid = (int)(items < 2LL * cu_count() ? items : 2LL * cu_count());
+  const bool bf = s.dtype == LORA_DTYPE_BF16;
+  if (with_ids)
+    return bf ? launch_shrink_t<BF16, true, 4>(a, grid, lds, stream)
+              : launch_shrink_t<F32, true, 4>(a, grid, lds, stream);
+  if (s.n <= kGroupMaxN)
+    return bf ? launch_shrink_t<BF16, false, 4>(a, grid, lds, stream)
+              : launch_shrink_t<F32, false, 4>(a, grid, lds, stream);
+  return bf ? launch_shrink_t<BF16, false, 16>(a, grid, lds, stream)
+            : launch_shrink_t<F32, false, 16>(a, grid, lds, stream);
+}
+
+hipError_t launch_reduce_partials(const lora_store& s, int T, const void* ws, float* h, int64_t ldh,
+                                  hipStream_t stream) {
+  const int64_t max_sub = plan_max_subtiles(T, s.n);
+  if (max_sub == 0) return hipSuccess;
+  const ShrinkSplit sp = shrink_split(s.d_in, s.r_max, s.dtype);
+  const WsLayout L = ws_layout(T, s.n, s.d_in, s.r_max, s.dtype);
+  const char* base = reinterpret_cast<const char*>(ws);
+  const int64_t ldp = partial_ld(s.r_max);
+  hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)max_sub), dim3(256), 0, stream, base + L.plan,
+                     (int)max_sub, reinterpret_cast<const float*>(base + L.part), ldp, (int64_t)T * ldp, sp.S,
+                     T, h, ldh);
+  return hipGetLastError();
+}
+
+hipError_t launch_plan(const lora_store& s, const int32_t* seg_off, const int32_t* perm, int T, void* ws,
+                       hipStream_t stream) {
+  const int64_t max_sub = plan_max_subtiles(T, s.n);
+  const WsLayout L = ws_layout(T, s.n, s.d_in, s.r_max, s.dtype);
+  char* plan = reinterpret_cast<char*>(ws) + L.plan;
+  const size_t lds = (size_t)(s.n + 1) * 4;
+  if (s.n <= kGroupMaxN) {
+    hipLaunchKernelGGL(plan_kernel<4>, dim3(1), dim3(1024), lds, stream, seg_off, perm, T, s.n, s.row_off,
+                       s.rank, s.scale, (int)max_sub, plan);
+  } else {
+    static size_t raised = 48 * 1024;
+    if (lds > raised) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(plan_kernel<16>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      raised = lds;
+    }
+    hipLaunchKernelGGL(plan_kernel<16>, dim3(1), dim3(1024), lds, stream, seg_off, perm, T, s.n, s.row_off,
+                       s.rank, s.scale, (int)max_sub, plan);
+  }
   return hipGetLastError();
 }
 

@@ -35,32 +35,40 @@ int check_store(const lora_store* s) {
   if (s->dtype != LORA_DTYPE_BF16 && s->dtype != LORA_DTYPE_F32) return LORA_ERR_UNSUPPORTED;
   if (s->r_max > LORA_MAX_RANK) return LORA_ERR_UNSUPPORTED;
   if (s->row_off == nullptr || s->rank == nullptr || s->scale == nullptr) return LORA_ERR_INVALID_ARG;
-  if (s->R > 0 && (s->A_pack == nullptr || s->Bt_pack == nullptr)) return LORA_ERR_INVALID_ARG;
+  if (s->R > 0 && (s->A_pack == nullptr || s->B_pack == nullptr)) return LORA_ERR_INVALID_ARG;
   int v = vec_elems(s->dtype);
   if (s->d_in % v != 0 || s->d_out % v != 0) return LORA_ERR_UNSUPPORTED;
-  if ((s->A_pack && !aligned16(s->A_pack)) || (s->Bt_pack && !aligned16(s->Bt_pack)))
+  if ((s->A_pack && !aligned16(s->A_pack)) || (s->B_pack && !aligned16(s->B_pack)))
     return LORA_ERR_UNSUPPORTED;
   return LORA_OK;
 }
 
-int check_segment_args(const int32_t* ids, int T, int n, const int32_t* seg_off, const int32_t* perm,
-                       const void* ws, size_t ws_bytes) {
+int check_segment_args(const int32_t* ids, int T, int n, const int32_t* seg_off, const int32_t* perm) {
   if (T < 0 || n < 1) return LORA_ERR_INVALID_ARG;
-  if (seg_off == nullptr || ws == nullptr) return LORA_ERR_INVALID_ARG;
+  if (seg_off == nullptr) return LORA_ERR_INVALID_ARG;
   if (T > 0 && (ids == nullptr || perm == nullptr)) return LORA_ERR_INVALID_ARG;
-  if (ws_bytes < plan_bytes(T, n)) return LORA_ERR_INVALID_ARG;
-  if (!aligned16(ws)) return LORA_ERR_UNSUPPORTED;
   if (T > LORA_SEGMENT_MAX_T || n > LORA_SEGMENT_MAX_N) return LORA_ERR_UNSUPPORTED;
   return LORA_OK;
 }
 
-int check_plan_args(const lora_store* s, int T, const int32_t* seg_off, const int32_t* perm,
-                    const void* seg_ws, size_t seg_ws_bytes) {
+int check_grouping(const lora_store* s, int T, const int32_t* seg_off, const int32_t* perm) {
   if (T < 0) return LORA_ERR_INVALID_ARG;
-  if (seg_off == nullptr || seg_ws == nullptr) return LORA_ERR_INVALID_ARG;
+  if (seg_off == nullptr) return LORA_ERR_INVALID_ARG;
   if (T > 0 && perm == nullptr) return LORA_ERR_INVALID_ARG;
-  if (seg_ws_bytes < plan_bytes(T, s->n)) return LORA_ERR_INVALID_ARG;
-  if (!aligned16(seg_ws)) return LORA_ERR_UNSUPPORTED;
+  if (s->n > LORA_SEGMENT_MAX_N) return LORA_ERR_UNSUPPORTED;
+  return LORA_OK;
+}
+
+size_t workspace_bytes(const lora_store* s, int T) {
+  if (s == nullptr || T < 0 || s->n < 1 || s->d_in <= 0 || s->r_max < 0) return 0;
+  return ws_layout(T, s->n, s->d_in, s->r_max, s->dtype).total;
+}
+
+int check_ws(const lora_store* s, int T, const void* ws, size_t ws_bytes) {
+  if (T == 0) return LORA_OK;  // nothing is launched
+  if (ws == nullptr) return LORA_ERR_INVALID_ARG;
+  if (ws_bytes < workspace_bytes(s, T)) return LORA_ERR_INVALID_ARG;
+  if (ws && !aligned16(ws)) return LORA_ERR_UNSUPPORTED;
   return LORA_OK;
 }
 

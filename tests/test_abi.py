@@ -50,7 +50,7 @@ def test_status_strings(lib):
     assert b"invalid" in lib.lora_status_string(1)
     assert b"unsupported" in lib.lora_status_string(2)
     assert b"HIP" in lib.lora_status_string(3)
-    assert lib.lora_abi_version() == 1
+    assert lib.lora_abi_version() == 2
     assert lib.lora_last_hip_error() == 0
 
 
@@ -109,34 +109,21 @@ def test_pack_rejects_before_launch(lib):
     assert f(C.byref(st), 2, 64, 64, 1, r, s, ptrs, ptrs, FAKE, FAKE, FAKE, 2, None) == 1
 
 
-def test_segment_ws_bytes(lib):
-    assert lib.lora_segment_ws_bytes(0, 4) == 64
-    # T=100, n=3: at most (100 + 63*3)//64 = 4 expand tiles of <= 64 tokens
-    # and (100 + 15*3)//16 = 9 shrink sub-tiles of <= 16 tokens
-    assert lib.lora_segment_ws_bytes(100, 3) == 64 + 16 * 4 + 16 * 9
-    assert lib.lora_segment_ws_bytes(-1, 3) == 0
-
-
 def test_segment_rejects_before_launch(lib):
     f = lib.lora_segment
-    big = 1 << 30
-    assert f(FAKE, -1, 4, FAKE, FAKE, None, FAKE, big, None) == 1
-    assert f(FAKE, 16, 0, FAKE, FAKE, None, FAKE, big, None) == 1
-    assert f(None, 16, 4, FAKE, FAKE, None, FAKE, big, None) == 1
-    assert f(FAKE, 16, 4, None, FAKE, None, FAKE, big, None) == 1
-    assert f(FAKE, 16, 4, FAKE, None, None, FAKE, big, None) == 1
-    assert f(FAKE, 16, 4, FAKE, FAKE, None, FAKE, 8, None) == 1          # ws too small
-    assert f(FAKE, 16, 4, FAKE, FAKE, None, FAKE + 8, big, None) == 2    # ws misaligned
-    assert f(FAKE, L.LORA_SEGMENT_MAX_T + 1, 4, FAKE, FAKE, None, FAKE, big, None) == 2
-    assert f(FAKE, 16, L.LORA_SEGMENT_MAX_N + 1, FAKE, FAKE, None, FAKE, big, None) == 2
-    assert lib.lora_segment_from_offsets(None, 16, 4, FAKE, big, None) == 1
-    assert lib.lora_segment_from_offsets(FAKE, 16, 4, FAKE, 8, None) == 1
+    assert f(FAKE, -1, 4, FAKE, FAKE, None, None) == 1
+    assert f(FAKE, 16, 0, FAKE, FAKE, None, None) == 1
+    assert f(None, 16, 4, FAKE, FAKE, None, None) == 1
+    assert f(FAKE, 16, 4, None, FAKE, None, None) == 1
+    assert f(FAKE, 16, 4, FAKE, None, None, None) == 1
+    assert f(FAKE, L.LORA_SEGMENT_MAX_T + 1, 4, FAKE, FAKE, None, None) == 2
+    assert f(FAKE, 16, L.LORA_SEGMENT_MAX_N + 1, FAKE, FAKE, None, None) == 2
 
 
 def _store(n=4, d_in=64, d_out=32, dtype=1, r_max=8, R=20):
     st = L.lora_store()
     st.n, st.d_in, st.d_out, st.dtype, st.r_max, st.R = n, d_in, d_out, dtype, r_max, R
-    st.A_pack = st.Bt_pack = st.row_off = st.rank = st.scale = FAKE
+    st.A_pack = st.B_pack = st.row_off = st.rank = st.scale = FAKE
     return st
 
 
@@ -148,8 +135,8 @@ def test_shrink_expand_reject_before_launch(lib):
 
         def call(st=good, p=FAKE, ld=d, T=16, so=FAKE, pm=FAKE, ws=FAKE, wsb=big, h=FAKE, ldh=8):
             if fn is lib.lora_shrink:
-                return fn(C.byref(st) if st is not None else None, p, ld, T, so, pm, ws, wsb, h, ldh, None)
-            return fn(C.byref(st) if st is not None else None, h, ldh, T, so, pm, ws, wsb, p, ld, None)
+                return fn(C.byref(st) if st is not None else None, p, ld, T, so, pm, h, ldh, ws, wsb, None)
+            return fn(C.byref(st) if st is not None else None, h, ldh, T, so, pm, p, ld, ws, wsb, None)
 
         assert call(T=0) == 0                       # no-op, nothing launched
         assert call(st=None) == 1
@@ -165,8 +152,11 @@ def test_shrink_expand_reject_before_launch(lib):
         assert call(ldh=4) == 1                     # ldh < r_max
         assert call(h=None) == 1
         assert call(wsb=8) == 1
+        assert call(ws=None) == 1
+        assert call(ws=FAKE + 8) == 2
         assert call(so=None) == 1
         assert call(pm=None) == 1
+        assert call(st=_store(n=L.LORA_SEGMENT_MAX_N + 1)) == 2
 
 
 def test_apply_rejects_before_launch(lib):
@@ -174,9 +164,8 @@ def test_apply_rejects_before_launch(lib):
     st = _store()
     f = lib.lora_apply_batched
 
-    def call(T=16, ids=FAKE, so=None, pm=None, sw=None, swb=0, ws=FAKE, wsb=big, x=FAKE, y=FAKE,
-             ldx=64, ldy=32, s=st):
-        return f(C.byref(s) if s is not None else None, x, ldx, y, ldy, T, ids, so, pm, sw, swb, ws, wsb, None)
+    def call(T=16, ids=FAKE, so=None, pm=None, ws=FAKE, wsb=big, x=FAKE, y=FAKE, ldx=64, ldy=32, s=st):
+        return f(C.byref(s) if s is not None else None, x, ldx, y, ldy, T, ids, so, pm, ws, wsb, None)
 
     assert call(s=None) == 1
     assert call(T=-3) == 1
@@ -188,18 +177,51 @@ def test_apply_rejects_before_launch(lib):
     assert call(T=L.LORA_SEGMENT_MAX_T + 1) == 2
     # no ids: a grouping must be supplied
     assert call(ids=None) == 1
-    assert call(ids=None, so=FAKE, pm=FAKE, sw=FAKE, swb=8) == 1
+    assert call(ids=None, so=FAKE) == 1
     # T = 0: nothing to group or apply, with or without ids
-    assert call(T=0, ids=None, so=FAKE, pm=FAKE, sw=FAKE, swb=big) == 0
+    assert call(T=0, ids=None, so=FAKE, pm=FAKE) == 0
     assert call(T=0, ids=None) == 0
-    assert call(T=0, x=None, y=None) == 0
+    assert call(T=0, x=None, y=None, ws=None, wsb=0) == 0
 
 
-def test_apply_ws_bytes(lib):
-    st = _store(n=4, r_max=6)
-    T = 100
-    ldh = 8  # r_max rounded up to a multiple of 4
-    h_bytes = -(-T * ldh * 4 // 256) * 256
-    assert lib.lora_apply_ws_bytes(C.byref(st), T, 0) == h_bytes
-    assert lib.lora_apply_ws_bytes(C.byref(st), T, 1) > h_bytes
-    assert lib.lora_apply_ws_bytes(None, T, 1) == 0
+def _layout_bytes(T, n, d_in, r_max, e):
+    """The workspace layout restated: plan (256-byte header + one 128-byte
+    entry per possible sub-tile of <= 16 tokens), float32 partial sums for
+    S chunks of d_in at row stride r_max rounded up to 8, and seg_off + perm
+    when n exceeds the in-kernel histogram's 4096 adapters; 256-byte aligned."""
+    up = lambda v: -(-v // 256) * 256
+    max_sub = (T + 15 * min(n, T)) // 16 if T > 0 else 0
+    step = 64 // e  # K values per 64 bytes
+    steps = -(-d_in // step)
+    ng = 1 if r_max <= 16 else -(-r_max // 16)
+    spw = 4 if ng <= 2 else 2
+    S = -(-steps // (16 * spw))
+    if S > 8:
+        spw = -(-steps // 128)
+        S = -(-steps // (16 * spw))
+    ldp = -(-max(r_max, 1) // 8) * 8
+    total = up(256 + 128 * max_sub) + up(S * T * ldp * 4)
+    if n > 4096:
+        total += up((n + 2) * 4) + up(T * 4)
+    return total
+
+
+@pytest.mark.parametrize("T,n,d_in,r_max,dtype", [(100, 4, 64, 6, 1), (2048, 512, 3584, 64, 1),
+                                                  (4096, 1024, 18944, 16, 1), (16, 4, 256, 4, 0),
+                                                  (300, 5000, 4096, 8, 1), (0, 3, 64, 4, 1)])
+def test_workspace_bytes(lib, T, n, d_in, r_max, dtype):
+    st = _store(n=n, d_in=d_in, r_max=r_max, dtype=dtype)
+    assert lib.lora_workspace_bytes(C.byref(st), T) == _layout_bytes(T, n, d_in, r_max, 2 if dtype == 1 else 4)
+    assert lib.lora_workspace_bytes(None, T) == 0
+    assert lib.lora_workspace_bytes(C.byref(st), -1) == 0
+
+
+def test_apply_timed_rejects_before_launch(lib):
+    st = _store()
+    f = lib.lora_apply_batched_timed
+    evs = (C.c_void_p * 3)(FAKE, FAKE, None)
+    good = (C.c_void_p * 3)(FAKE, FAKE, FAKE)
+    assert f(C.byref(st), FAKE, 64, FAKE, 32, 16, FAKE, None, None, FAKE, 1 << 30, None, None) == 1
+    assert f(C.byref(st), FAKE, 64, FAKE, 32, 16, FAKE, None, None, FAKE, 1 << 30, None, evs) == 1
+    assert f(None, FAKE, 64, FAKE, 32, 16, FAKE, None, None, FAKE, 1 << 30, None, good) == 1
+    assert f(C.byref(st), FAKE, 64, FAKE, 32, 0, FAKE, None, None, FAKE, 1 << 30, None, good) == 0

@@ -1,4 +1,5 @@
-"""GPU: the packed store and the token grouping, both bit-exact."""
+"""GPU: the packed store, the token grouping and the work plan the shrink
+builds from ids, all bit-exact."""
 import zlib
 
 import numpy as np
@@ -15,19 +16,22 @@ pytestmark = pytest.mark.gpu
 
 
 def _expected_store(wl, pad_to=0):
+    """A_pack rows and B_pack blocks as the store layout defines them: A_a
+    ([r, d_in]) then zero rows, B_a ([d_out, r]) widened with zero columns,
+    to the stored rank; adapters end to end."""
     m = wl.module
-    rows_a, rows_b, row_off = [], [], [0]
+    rows_a, blocks_b, row_off = [], [], [0]
     for a in range(m.n):
         r = int(m.ranks[a])
         stored = pad_to if pad_to else r
         A = np.zeros((stored, m.d_in), np.float32)
-        Bt = np.zeros((stored, m.d_out), np.float32)
+        B = np.zeros((m.d_out, stored), np.float32)
         A[:r] = m.A[a]
-        Bt[:r] = m.B[a].T
+        B[:, :r] = m.B[a]
         rows_a.append(A)
-        rows_b.append(Bt)
+        blocks_b.append(B.ravel())
         row_off.append(row_off[-1] + stored)
-    return np.concatenate(rows_a), np.concatenate(rows_b), np.array(row_off, np.int32)
+    return np.concatenate(rows_a), np.concatenate(blocks_b), np.array(row_off, np.int32)
 
 
 @pytest.mark.parametrize("case", ["1", "2", "ragged", "ragged-pad", "3-pad"])
@@ -45,51 +49,55 @@ def test_pack_roundtrip(case):
     note(f"pack {case} pad_to={pad_to}")
     store = pack(wl, dev, pad_to)
     torch.cuda.synchronize()
-    A_exp, Bt_exp, row_off = _expected_store(wl, pad_to)
+    A_exp, B_exp, row_off = _expected_store(wl, pad_to)
     dt = TORCH_DTYPE[wl.dtype]
     R = A_exp.shape[0]
     assert store.c.R == R and store.r_max == (pad_to or int(wl.module.ranks.max()))
     A_got = store.A_pack[: R * wl.module.d_in * dt.itemsize].view(dt).float().cpu().numpy()
-    Bt_got = store.Bt_pack[: R * wl.module.d_out * dt.itemsize].view(dt).float().cpu().numpy()
+    B_got = store.B_pack[: R * wl.module.d_out * dt.itemsize].view(dt).float().cpu().numpy()
     assert np.array_equal(A_got.reshape(A_exp.shape), A_exp)
-    assert np.array_equal(Bt_got.reshape(Bt_exp.shape), Bt_exp)
+    assert np.array_equal(B_got, B_exp)
     ro, rk, sc = store.device_meta()
     assert np.array_equal(ro.cpu().numpy(), row_off)
     assert np.array_equal(rk.cpu().numpy(), np.diff(row_off))
     assert np.array_equal(sc.cpu().numpy(), wl.module.scales)
 
 
-def _plan_offsets(T, n):
-    max_tiles = (T + 63 * min(n, T)) // 64 if T > 0 else 0
-    return 64, 64 + 16 * max_tiles
+def _read_plan(ws):
+    """(count, entries) of the work plan at the start of a workspace: a
+    256-byte header (int32 count), then 128-byte entries {adapter, first
+    grouped position, tokens, stored rank, row offset, scale, -, -,
+    token indices[16], -}."""
+    raw = ws.cpu().numpy()
+    count = int(raw[:4].view(np.int32)[0])
+    ent = raw[256: 256 + 128 * count].view(np.int32).reshape(count, 32)
+    return count, ent
 
 
-def _check_plan(seg, n):
-    """Expand tiles (<= 64 tokens; tiles of more than 4 tokens first) and
-    shrink sub-tiles (<= 16 tokens) each cover every grouped token of a real
-    adapter exactly once; each list is in (adapter, position) order."""
-    ws = seg.ws.cpu().numpy()
-    hdr = ws[:64].view(np.int32)
-    count, n_large, n_small, n_sub = int(hdr[0]), int(hdr[1]), int(hdr[2]), int(hdr[3])
-    assert count == n_large + n_small
-    t_off, s_off = _plan_offsets(seg.T, n)
-    tiles = ws[t_off: t_off + 16 * count].view(np.int32).reshape(count, 4)
-    subs = ws[s_off: s_off + 16 * n_sub].view(np.int32).reshape(n_sub, 4)
-    so = seg.seg_off.cpu().numpy()
-    for lst, cap, large in ((tiles, rs._lib.LORA_TILE_TOKENS, n_large), (subs, 16, None)):
-        covered = []
-        for k, (a, p0, m, _) in enumerate(lst):
-            assert 0 <= a < n and 1 <= m <= cap
-            if large is not None:
-                assert (m > 4) == (k < large)
-            assert so[a] <= p0 and p0 + m <= so[a + 1]
-            assert (p0 - so[a]) % cap == 0
-            covered.extend(range(p0, p0 + m))
-        assert sorted(covered) == list(range(int(so[n])))
-    for part in (tiles[:n_large], tiles[n_large:], subs):
-        keys = [(int(a), int(p)) for a, p, _, _ in part]
-        assert keys == sorted(keys)
-    return np.concatenate([tiles.ravel(), subs.ravel()])
+def _expected_plan(seg_off, perm, ranks, row_off, scales):
+    """Every adapter with tokens and a non-zero stored rank, cut into runs of
+    16 grouped positions, in adapter order."""
+    out = []
+    for a in range(len(ranks)):
+        c = seg_off[a + 1] - seg_off[a]
+        if ranks[a] <= 0:
+            continue
+        for j in range(0, c, 16):
+            p0 = seg_off[a] + j
+            m = min(16, c - j)
+            tok = list(perm[p0: p0 + m]) + [-1] * (16 - m)
+            out.append([a, p0, m, int(ranks[a]), int(row_off[a]), scales[a], tok])
+    return out
+
+
+def _check_plan(ws, expect):
+    count, ent = _read_plan(ws)
+    assert count == len(expect)
+    for k, (a, p0, m, r, ro, sc, tok) in enumerate(expect):
+        e = ent[k]
+        assert [int(e[0]), int(e[1]), int(e[2]), int(e[3]), int(e[4])] == [a, p0, m, r, ro], k
+        assert np.float32(e[5:6].view(np.float32)[0]) == np.float32(sc)
+        assert e[8:24].tolist() == tok, k
 
 
 def _segment_case(name):
@@ -139,7 +147,6 @@ def test_segment_exact(name):
     assert seg.seg_off.cpu().tolist() == so_ref
     assert seg.perm.cpu().tolist() == perm_ref
     assert int(seg.n_invalid.cpu()[0]) == inv_ref
-    _check_plan(seg, n)
 
 
 def test_segment_empty():
@@ -148,18 +155,6 @@ def test_segment_empty():
     seg = rs.lora_segment(torch.empty(0, dtype=torch.int32, device=dev), 4)
     torch.cuda.synchronize()
     assert seg.seg_off.cpu().tolist() == [0] * 6
-    assert int(seg.ws.cpu().numpy()[:4].view(np.int32)[0]) == 0
-
-
-@pytest.mark.parametrize("name", ["3", "out_of_range", "all_same"])
-def test_plan_from_offsets_matches(name):
-    dev = device()
-    ids, n = _segment_case(name)
-    note(f"plan_from_offsets {name}")
-    seg = rs.lora_segment(torch.from_numpy(ids).to(dev), n)
-    seg2 = rs.lora_segment_from_offsets(seg.seg_off, seg.perm, n)
-    torch.cuda.synchronize()
-    assert np.array_equal(_check_plan(seg, n), _check_plan(seg2, n))
 
 
 def test_segment_repeatable():
@@ -171,4 +166,65 @@ def test_segment_repeatable():
     b = rs.lora_segment(t, n)
     torch.cuda.synchronize()
     assert torch.equal(a.perm, b.perm) and torch.equal(a.seg_off, b.seg_off)
-    assert np.array_equal(_check_plan(a, n), _check_plan(b, n))
+
+
+PLAN_CASES = ["1", "2", "3", "4", "5", "all_same", "all_invalid", "out_of_range", "distinct", "max_T",
+              "many_adapters", "one_token", "n1", "sorted_desc"]
+
+
+def _plan_store(n, dev, seed):
+    """A small bf16 store over n adapters with ranks 0..64 (some zero)."""
+    rng = np.random.default_rng(seed)
+    ranks = rng.integers(0, 65, size=n)
+    ranks[rng.random(n) < 0.1] = 0
+    A = [torch.zeros(int(r), 64, dtype=torch.bfloat16, device=dev) for r in ranks]
+    B = [torch.zeros(64, int(r), dtype=torch.bfloat16, device=dev) for r in ranks]
+    scales = rng.random(n).astype(np.float32)
+    store = rs.lora_pack_retained(A, B, scales)
+    return store, ranks, scales
+
+
+@pytest.mark.parametrize("name", PLAN_CASES)
+def test_plan_from_ids(name):
+    """The plan the shrink forms from ids inside its workgroups (or, beyond
+    4096 adapters, from the sort it runs first) equals the sub-tiles of the
+    oracle's grouping, token for token."""
+    dev = device()
+    ids, n = _segment_case(name)
+    T = len(ids)
+    store, ranks, scales = _plan_store(n, dev, zlib.crc32(name.encode()))
+    x = torch.zeros(T, 64, dtype=torch.bfloat16, device=dev)
+    y = torch.zeros(T, 64, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(rs.lora_workspace_bytes(store, T), dtype=torch.uint8, device=dev)
+    note(f"plan from ids {name} T={T} n={n}")
+    rs.lora_apply_batched(store, x, y, ids=torch.from_numpy(ids).to(dev), ws=ws)
+    torch.cuda.synchronize()
+    so_ref, perm_ref, _ = segment_ref(ids.tolist(), n)
+    row_off = np.concatenate([[0], np.cumsum(ranks)])
+    _check_plan(ws, _expected_plan(so_ref, perm_ref, ranks, row_off, scales))
+
+
+@pytest.mark.parametrize("name", ["3", "out_of_range", "all_same", "many_adapters"])
+def test_plan_from_grouping(name):
+    """The same plan from a caller-supplied grouping: the apply's shrink with
+    (seg_off, perm), and the plan kernel of the standalone expand."""
+    dev = device()
+    ids, n = _segment_case(name)
+    T = len(ids)
+    store, ranks, scales = _plan_store(n, dev, zlib.crc32(name.encode()) + 1)
+    seg = rs.lora_segment(torch.from_numpy(ids).to(dev), n)
+    x = torch.zeros(T, 64, dtype=torch.bfloat16, device=dev)
+    y = torch.zeros(T, 64, dtype=torch.bfloat16, device=dev)
+    h = torch.zeros(T, max(store.r_max, 1), dtype=torch.float32, device=dev)
+    so_ref, perm_ref, _ = segment_ref(ids.tolist(), n)
+    row_off = np.concatenate([[0], np.cumsum(ranks)])
+    want = _expected_plan(so_ref, perm_ref, ranks, row_off, scales)
+    ws = torch.empty(rs.lora_workspace_bytes(store, T), dtype=torch.uint8, device=dev)
+    note(f"plan from grouping {name}")
+    rs.lora_apply_batched(store, x, y, seg=seg, ws=ws)
+    torch.cuda.synchronize()
+    _check_plan(ws, want)
+    ws.fill_(0xAB)
+    rs.lora_expand(store, h, seg, y, ws=ws)
+    torch.cuda.synchronize()
+    _check_plan(ws, want)
