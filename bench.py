@@ -117,7 +117,7 @@ def make_copies(rs, torch, wl, dev, pad_to: int, cold: bool):
 
 
 def time_apply(rs, torch, copies, ids, ws, steps, warmup):
-    """Events bracket exactly `steps` calls; returns ms per call."""
+    """Events bracket exactly `steps` eager calls; returns ms per call."""
     for k in range(warmup):
         c = copies[k % len(copies)]
         rs.lora_apply_batched(c.store, c.x, c.y, ids=ids, ws=ws)
@@ -135,15 +135,63 @@ def time_apply(rs, torch, copies, ids, ws, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall
 
 
+def time_apply_graph(rs, torch, copies, ids, ws, steps, warmup):
+    """The same `steps` calls captured once in a HIP graph (a decode loop's
+    launches replayed without host work per kernel); events bracket one
+    replay of all of them.  Returns ms per call."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for k in range(max(1, warmup)):
+            c = copies[k % len(copies)]
+            rs.lora_apply_batched(c.store, c.x, c.y, ids=ids, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for k in range(steps):
+            c = copies[(warmup + k) % len(copies)]
+            rs.lora_apply_batched(c.store, c.x, c.y, ids=ids, ws=ws)
+    g.replay()  # untimed warm replay
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    del g
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def queue_ahead(torch, ms: float):
+    """Enqueue a spin kernel of about `ms` milliseconds, so that the launches
+    that follow queue up behind it and then run back to back: events around
+    them time the GPU, not the host's launch rate."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    probe = 1 << 20
+    e0.record()
+    torch.cuda._sleep(probe)
+    e1.record()
+    torch.cuda.synchronize()
+    per_ms = probe / max(e0.elapsed_time(e1), 1e-3)
+    torch.cuda._sleep(int(per_ms * ms))
+
+
 def time_kernels(rs, torch, copies, ids, ws, steps):
     """Per-kernel average duration of the apply's two kernels: HIP events
     recorded on the launch stream before the shrink, between the kernels and
-    after the expand, over the same rotation of copies as the timed steps."""
+    after the expand, over the same rotation of copies as the timed steps
+    (queued behind a spin kernel so that host launch time stays out)."""
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for k in range(min(steps, 10)):  # warm the launch path
         c = copies[k % len(copies)]
         rs.lora_apply_batched_timed(c.store, c.x, c.y, ev[k], ids=ids, ws=ws)
     torch.cuda.synchronize()
+    queue_ahead(torch, 0.08 * steps + 2.0)
     for k in range(steps):
         c = copies[k % len(copies)]
         rs.lora_apply_batched_timed(c.store, c.x, c.y, ev[k], ids=ids, ws=ws)
@@ -221,7 +269,8 @@ def main():
 
     copies, per_copy = make_copies(rs, torch, wl, dev, 0, not args.warm)
     ws = torch.empty(rs.lora_workspace_bytes(copies[0].store, wl.T), dtype=torch.uint8, device=dev)
-    ms, wall = time_apply(rs, torch, copies, ids, ws, args.steps, args.warmup)
+    eager_ms, eager_wall = time_apply(rs, torch, copies, ids, ws, args.steps, args.warmup)
+    ms, wall = time_apply_graph(rs, torch, copies, ids, ws, args.steps, args.warmup)
     kern = time_kernels(rs, torch, copies, ids, ws, args.steps)
     gbps = nbytes["total"] / (ms * 1e-3) / 1e9
 
@@ -252,7 +301,7 @@ def main():
         for name, pad in variants.items():
             pc, _ = make_copies(rs, torch, wl, dev, pad, not args.warm)
             pws = torch.empty(rs.lora_workspace_bytes(pc[0].store, wl.T), dtype=torch.uint8, device=dev)
-            pms, _ = time_apply(rs, torch, pc, ids, pws, max(20, args.steps // 2), args.warmup)
+            pms, _ = time_apply_graph(rs, torch, pc, ids, pws, max(20, args.steps // 2), args.warmup)
             own = algorithmic_bytes(wl.ids, np.full(m.n, pad), m.n, m.d_in, m.d_out, e)["total"]
             padded[name] = {"pad_to": pad, "ms_per_step": round(pms, 5),
                             "tokens_per_s": round(wl.T / (pms * 1e-3), 1),
@@ -287,7 +336,9 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kern,
         "padded": padded,
-        "wall_s_timed": round(wall, 3),
+        "wall_s_timed": round(wall, 6),
+        "timed_as": "one HIP-graph replay of the K captured steps (eager launches: see eager_ms_per_step)",
+        "eager_ms_per_step": round(eager_ms, 5),
         "kernel_sources_sha": kernel_source_digest(),
     }
     print(json.dumps(out), flush=True)

@@ -33,7 +33,7 @@ namespace lora {
 
 struct ExpandArgs {
   const char* b_pack;
-  int d_out, T, S, max_sub, fbn;
+  int d_out, T, max_sub, fbn;
   const float* hsrc;      // partial sums (kPart) or h
   int64_t ldh, hstride;   // floats
   const char* plan;
@@ -43,7 +43,7 @@ struct ExpandArgs {
 
 template <typename E, bool kPart, int NQ>
 __device__ __forceinline__ void expand_item(const ExpandArgs& p, const TileEntry* ent, int m, int r, int pos0,
-                                            int ro, float sc, int o) {
+                                            int ro, float sc, int S, int o) {
   constexpr int V = E::kVec;
   constexpr int KSTEP = 4 * V;  // ranks per K chunk
   constexpr int YV = 8 / V;     // 16-byte vectors per 8 features: bf16 1, f32 2
@@ -108,7 +108,7 @@ __device__ __forceinline__ void expand_item(const ExpandArgs& p, const TileEntry
           const f32x4_t x = *reinterpret_cast<const f32x4_t*>(src + 4 * v);
           f[4 * v] = x[0]; f[4 * v + 1] = x[1]; f[4 * v + 2] = x[2]; f[4 * v + 3] = x[3];
         }
-        for (int k = 1; k < p.S; ++k) {
+        for (int k = 1; k < S; ++k) {
 #pragma unroll
           for (int v = 0; v < V / 4; ++v) {
             const f32x4_t x = *reinterpret_cast<const f32x4_t*>(src + (int64_t)k * p.hstride + 4 * v);
@@ -161,17 +161,18 @@ __global__ void __launch_bounds__(kExpandWaves * 64) expand_kernel(ExpandArgs p)
   const TileEntry* ent = reinterpret_cast<const TileEntry*>(p.plan + kPlanHeaderBytes) + st;
   const int m = ent->m, r = ent->r, pos0 = ent->pos0, ro = ent->row_off;
   const float sc = ent->scale;
+  const int S = kPart ? ent->S : 1;
   if (m <= 0 || r <= 0) return;
   const int o = fb * kExpandCols + 8 * (threadIdx.x & 15);
   const int nq = (r + KSTEP - 1) / KSTEP;
   if (nq <= 1) {
-    expand_item<E, kPart, 1>(p, ent, m, r, pos0, ro, sc, o);
+    expand_item<E, kPart, 1>(p, ent, m, r, pos0, ro, sc, S, o);
   } else if constexpr (KSTEP == 32) {  // bf16: ranks <= 64 take at most 2 chunks
-    expand_item<E, kPart, 2>(p, ent, m, r, pos0, ro, sc, o);
+    expand_item<E, kPart, 2>(p, ent, m, r, pos0, ro, sc, S, o);
   } else {
-    if (nq == 2) expand_item<E, kPart, 2>(p, ent, m, r, pos0, ro, sc, o);
-    else if (nq == 3) expand_item<E, kPart, 3>(p, ent, m, r, pos0, ro, sc, o);
-    else expand_item<E, kPart, 4>(p, ent, m, r, pos0, ro, sc, o);
+    if (nq == 2) expand_item<E, kPart, 2>(p, ent, m, r, pos0, ro, sc, S, o);
+    else if (nq == 3) expand_item<E, kPart, 3>(p, ent, m, r, pos0, ro, sc, S, o);
+    else expand_item<E, kPart, 4>(p, ent, m, r, pos0, ro, sc, S, o);
   }
 }
 
@@ -192,12 +193,10 @@ hipError_t launch_expand(const lora_store& s, int T, const void* ws, const float
   a.ldy_bytes = ldy * elem_bytes(s.dtype);
   const bool part = h == nullptr;
   if (part) {
-    a.S = shrink_split(s.d_in, s.r_max, s.dtype).S;
     a.hsrc = reinterpret_cast<const float*>(base + L.part);
     a.ldh = partial_ld(s.r_max);
     a.hstride = (int64_t)T * a.ldh;
   } else {
-    a.S = 1;
     a.hsrc = h;
     a.ldh = ldh;
     a.hstride = 0;

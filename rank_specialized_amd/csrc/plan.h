@@ -13,8 +13,10 @@ namespace lora {
 // order: one 16-wide block of a matrix-core tile.
 constexpr int kSubTile = 16;
 
-// The shrink's workgroup: 16 waves share one (sub-tile, K chunk) item.
-constexpr int kShrinkWaves = 16;
+// The shrink's workgroup: 8 waves share one (sub-tile, K chunk) item; two
+// workgroups fit on a CU, so one's grouping and reduction overlap the
+// other's loads.
+constexpr int kShrinkWaves = 8;
 constexpr int kShrinkThreads = kShrinkWaves * 64;
 
 // The shrink groups tokens itself (histogram of the ids in LDS) when
@@ -45,7 +47,8 @@ struct TileEntry {
   int32_t r;        // stored rank
   int32_t row_off;  // first row of the adapter in the store
   float scale;      // s_a
-  int32_t pad0[2];
+  int32_t S;        // K chunks of the shrink (partial sums to add)
+  int32_t pad0;
   int32_t tok[kSubTile];  // token indices, ascending
   int32_t pad1[8];
 };
@@ -59,27 +62,39 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline int elem_bytes(int dtype) { return dtype == LORA_DTYPE_BF16 ? 2 : 4; }
 inline int vec_elems(int dtype) { return dtype == LORA_DTYPE_BF16 ? 8 : 4; }  // 16-byte vectors
 
-// The shrink splits d_in into S chunks; each of the 16 waves of an item
+// The shrink splits d_in into S chunks; each of the 8 waves of an item
 // takes `spw` consecutive K steps (a step is 4 x 16 bytes of K: 32 bf16 or
-// 16 f32 values).  spw is the per-batch step count the register budget
-// allows (4 for up to 32 retained ranks, 2 above), S at most 8 (more steps
-// per wave, in batches, for very wide inputs).
+// 16 f32 values), issued as one batch of loads.  The batch depends on the
+// adapter's number of 16-rank row groups (ng): 8, 5, 4, 3 steps for ng =
+// 1..4, about 60 registers of loads either way.  S is at most 8; very wide
+// inputs give more steps per wave (several batches).  Indexed by ng (1..4).
 struct ShrinkSplit {
-  int spw;     // K steps per wave
-  int S;       // K chunks (partial sums per output)
-  int kchunk;  // K elements per chunk = 16 * spw * step
+  int spw[5];     // K steps per wave
+  int S[5];       // K chunks (partial sums per output)
+  int kchunk[5];  // K elements per chunk = 8 * spw * step
+  int S_max;      // largest S over the row groups the store needs
 };
+inline int shrink_batch_steps(int ng) { return ng <= 1 ? 8 : ng == 2 ? 5 : ng == 3 ? 4 : 3; }
+inline int rank_groups(int r) { return r <= 16 ? 1 : (r + 15) / 16; }
 inline ShrinkSplit shrink_split(int d_in, int r_max, int dtype) {
   const int step = 4 * vec_elems(dtype);
   const int steps = (d_in + step - 1) / step;
-  const int ng = r_max <= 16 ? 1 : (r_max + 15) / 16;
-  int spw = ng <= 2 ? 4 : 2;
-  int S = (steps + kShrinkWaves * spw - 1) / (kShrinkWaves * spw);
-  if (S > 8) {
-    spw = (steps + kShrinkWaves * 8 - 1) / (kShrinkWaves * 8);
-    S = (steps + kShrinkWaves * spw - 1) / (kShrinkWaves * spw);
+  ShrinkSplit sp;
+  sp.spw[0] = sp.S[0] = sp.kchunk[0] = 0;
+  sp.S_max = 1;
+  for (int ng = 1; ng <= 4; ++ng) {
+    int spw = shrink_batch_steps(ng);
+    int S = (steps + kShrinkWaves * spw - 1) / (kShrinkWaves * spw);
+    if (S > 8) {
+      spw = (steps + kShrinkWaves * 8 - 1) / (kShrinkWaves * 8);
+      S = (steps + kShrinkWaves * spw - 1) / (kShrinkWaves * spw);
+    }
+    sp.spw[ng] = spw;
+    sp.S[ng] = S;
+    sp.kchunk[ng] = kShrinkWaves * spw * step;
+    if (ng <= rank_groups(r_max) && S > sp.S_max) sp.S_max = S;
   }
-  return ShrinkSplit{spw, S, kShrinkWaves * spw * step};
+  return sp;
 }
 
 // Row stride (floats) of the float32 partial sums: r_max rounded up to 8 so
@@ -97,7 +112,7 @@ inline WsLayout ws_layout(int T, int n, int d_in, int r_max, int dtype) {
   const ShrinkSplit sp = shrink_split(d_in, r_max, dtype);
   L.plan = 0;
   L.part = align_up(plan_bytes(T, n), 256);
-  L.seg_off = L.part + align_up((size_t)sp.S * (size_t)T * (size_t)partial_ld(r_max) * 4, 256);
+  L.seg_off = L.part + align_up((size_t)sp.S_max * (size_t)T * (size_t)partial_ld(r_max) * 4, 256);
   L.perm = L.seg_off + (n > kGroupMaxN ? align_up((size_t)(n + 2) * 4, 256) : 0);
   L.total = L.perm + (n > kGroupMaxN ? align_up((size_t)T * 4, 256) : 0);
   return L;

@@ -6,13 +6,13 @@
 // of one adapter (the segmented gather of its section 2), so each adapter's
 // retained rows are read once per sub-tile of at most 16 of its tokens.
 //
-// Work item = (sub-tile, K chunk); one workgroup of 16 waves per item, a
-// grid-stride loop over the items.  A sub-tile is the skinny GEMM
+// Work item = (sub-tile, K chunk); one workgroup of 8 waves per item, a
+// grid-stride loop over the items (two workgroups per CU).  A sub-tile is the skinny GEMM
 //   H^T[r_a x m] = A_a[r_a x d_in] . X^T[d_in x m]      (m <= 16)
 // on 16x16 MFMA tiles whatever m is.  d_in is cut into S chunks (S <= 8) so
 // that a popular or high-rank adapter's rows spread over several CUs; inside
 // an item each wave takes `spw` consecutive K steps and issues all of their
-// loads before the first MFMA.  The 16 waves' float32 tiles are summed in
+// loads before the first MFMA.  The 8 waves' float32 tiles are summed in
 // LDS in wave order, and chunk kc's sum is written as partial kc; the
 // consumer adds the S partials in chunk order.  No atomics: results are
 // deterministic.
@@ -20,8 +20,9 @@
 // Token grouping happens inside every workgroup, so no separate launch and
 // no round trip through memory precede the factor loads:
 //  * from ids (n <= 4096): a histogram of the ids in LDS, one block scan of
-//    (tokens, sub-tiles) per adapter, and for each item the sub-tile's
-//    tokens by a ballot rank over the ids (tokens keep ascending index);
+//    (tokens, sub-tiles, items) per adapter, and for each item the
+//    sub-tile's tokens by a ballot rank over the ids (tokens keep ascending
+//    index);
 //  * from a grouping (seg_off, perm): the same scan over seg_off.
 // Every adapter's rank, row offset and scale are loaded while the histogram
 // forms (one load each per thread), so the item loop finds its adapter's
@@ -50,105 +51,137 @@ struct ShrinkArgs {
   const int32_t* row_off;
   const int32_t* rank;
   const float* scale;
-  int d_in, ng_max, spw, S, kchunk;
+  int d_in, ng_max;
+  int spw[5], S[5], kchunk[5];  // by row groups ng = 1..4
   float* part;
   int64_t ldp, pstride;  // floats: row stride, distance between partials
   char* plan;
   int warm_key;
 };
 
+// v[ng] for ng = 1..4 without indexing the argument array at run time
+// (which would copy it to private memory).
+__device__ __forceinline__ int by_ng(const int (&v)[5], int ng) {
+  return ng <= 1 ? v[1] : ng == 2 ? v[2] : ng == 3 ? v[3] : v[4];
+}
+
+// Grouping state in LDS (no per-thread state lives across the item loop):
+//   info[a]  = tokens of adapter a | row groups of its rank << 20 (0: rank 0)
+//   pref[t]  = exclusive prefix, over the adapters of threads < t, of
+//              tokens << 44 | sub-tiles << 24 | items; pref[threads] = total
+// Thread t owns adapters [t * APT, (t + 1) * APT).
 template <typename E, bool kIds, int APT>
-__global__ void __launch_bounds__(kShrinkThreads) shrink_kernel(ShrinkArgs p) {
+__global__ void __launch_bounds__(kShrinkThreads, 4) shrink_kernel(ShrinkArgs p) {
   constexpr int KSTEP = 4 * E::kVec;
   extern __shared__ __align__(16) char dyn[];
-  f32x4_t* red = reinterpret_cast<f32x4_t*>(dyn);  // [16 waves][ng_max][64 lanes]
-  int* cnt = reinterpret_cast<int*>(dyn + (size_t)p.ng_max * kShrinkWaves * 64 * 16);  // [n]
-  uint16_t* id16 = reinterpret_cast<uint16_t*>(cnt + ((p.n + 3) & ~3));                // [T]
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(dyn);  // [8 waves][ng_max][64 lanes]
+  int* info = reinterpret_cast<int*>(dyn + (size_t)p.ng_max * kShrinkWaves * 64 * 16);  // [n]
+  uint16_t* id16 = reinterpret_cast<uint16_t*>(info + ((p.n + 3) & ~3));               // [T] (ids)
   __shared__ uint64_t s_wsum[kShrinkWaves];
-  __shared__ int s_tile[8];
+  __shared__ uint64_t s_pref[kShrinkThreads + 1];
+  __shared__ int s_tile[10];
   __shared__ int s_tok[kSubTile];
   __shared__ int s_bc[kMaxBlocks64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = p.n, T = p.T;
 
-  // 1. Tokens per adapter, and this thread's adapters [a0, a0 + APT).
-  if (kIds) {
-    for (int i = tid; i < n; i += kShrinkThreads) cnt[i] = 0;
-    __syncthreads();
-  }
+  // 1. Tokens per adapter into info[].  The metadata of this thread's
+  //    adapters is loaded meanwhile (ranks are needed below; row offsets and
+  //    scales are only folded into a value that is never stored in
+  //    practice: the loads bring them into the cache for the item loop).
   const int a0 = tid * APT;
-  int cnt_[APT], rk_[APT];
-  // The row offsets and scales of this thread's adapters are loaded now and
-  // only folded into a value that is never stored in practice: the loads
-  // bring them into the cache while the histogram forms, so the item loop
-  // below finds its adapter's metadata there.
+  int rk_[APT];
   int warm = 0;
 #pragma unroll
   for (int i = 0; i < APT; ++i) {
     const int a = a0 + i;
-    const bool v = a < n;
-    rk_[i] = v ? p.rank[a] : 0;
-    if (v) warm ^= p.row_off[a] ^ __float_as_int(p.scale[a]);
-    cnt_[i] = (!kIds && v) ? p.seg_off[a + 1] - p.seg_off[a] : 0;
+    rk_[i] = a < n ? p.rank[a] : 0;
+    if (a < n) warm ^= p.row_off[a] ^ __float_as_int(p.scale[a]);
   }
   if (kIds) {
+    for (int i = tid; i < n; i += kShrinkThreads) info[i] = 0;
+    __syncthreads();
     for (int t = tid; t < T; t += kShrinkThreads) {
       const int v = p.ids[t];
       const bool ok = (unsigned)v < (unsigned)n;
       id16[t] = ok ? (uint16_t)v : (uint16_t)0xFFFFu;
-      if (ok) atomicAdd(&cnt[v], 1);
+      if (ok) atomicAdd(&info[v], 1);
     }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < APT; ++i) cnt_[i] = a0 + i < n ? cnt[a0 + i] : 0;
+  } else {
+    for (int i = tid; i < n; i += kShrinkThreads) info[i] = p.seg_off[i + 1] - p.seg_off[i];
   }
-  if (warm == p.warm_key) s_tile[7] = warm;  // warm_key is never produced by valid metadata
-  // 2. Exclusive scan of (tokens << 32 | sub-tiles) in adapter order; each
-  //    adapter's (tokens << 16 | sub-tiles) is kept for the item loop.
+  __syncthreads();
+  if (warm == p.warm_key) s_tile[9] = warm;  // warm_key is never produced by valid metadata
+  // 2. Pack (tokens, row groups) per adapter; scan (tokens, sub-tiles, items).
   uint64_t mine = 0;
-  uint32_t cs_[APT];
 #pragma unroll
   for (int i = 0; i < APT; ++i) {
-    const int c = cnt_[i] < 0 ? 0 : (cnt_[i] > T ? T : cnt_[i]);  // T < 2^16
-    const int sub = rk_[i] > 0 ? (c + kSubTile - 1) / kSubTile : 0;
-    cs_[i] = ((uint32_t)c << 16) | (uint32_t)sub;
-    mine += ((uint64_t)c << 32) | (uint64_t)sub;
+    const int a = a0 + i;
+    if (a < n) {
+      int c = info[a];
+      c = c < 0 ? 0 : (c > T ? T : c);
+      const int ng = rk_[i] > 0 ? (rk_[i] + 15) / 16 : 0;
+      const int sub = ng ? (c + kSubTile - 1) / kSubTile : 0;
+      const int its = ng ? sub * by_ng(p.S, ng) : 0;
+      info[a] = c | (ng << 20);
+      mine += ((uint64_t)c << 44) | ((uint64_t)sub << 24) | (uint64_t)its;
+    }
   }
   uint64_t tot;
   const uint64_t pre = block_exclusive_scan<kShrinkWaves>(mine, s_wsum, &tot);
-  const int total_sub = min((int)(tot & 0xffffffffu), p.max_sub);
+  s_pref[tid] = pre;
+  if (tid == 0) s_pref[kShrinkThreads] = tot;
+  const int total_sub = min((int)((tot >> 24) & 0xfffffu), p.max_sub);
   if (blockIdx.x == 0 && tid == 0) *reinterpret_cast<int32_t*>(p.plan) = total_sub;
   const int base_pos = kIds ? 0 : p.seg_off[0];
-  const int items = total_sub * p.S;
+  const int items = (int)(tot & 0xffffffu);
   TileEntry* entries = reinterpret_cast<TileEntry*>(p.plan + kPlanHeaderBytes);
+  __syncthreads();
 
   for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    const int st = item / p.S, kc = item - st * p.S;
-    // 3. The adapter that owns sub-tile st.
-    {
-      int s = (int)(pre & 0xffffffffu), pos = base_pos + (int)(pre >> 32);
-#pragma unroll
-      for (int i = 0; i < APT; ++i) {
-        const int c = (int)(cs_[i] >> 16), sub = (int)(cs_[i] & 0xffffu);
-        if (st >= s && st < s + sub) {
-          const int j = st - s;
-          const int a = a0 + i;
-          s_tile[0] = a;
-          s_tile[1] = pos + j * kSubTile;
-          s_tile[2] = min(kSubTile, c - j * kSubTile);
-          s_tile[3] = p.rank[a];
-          s_tile[4] = p.row_off[a];
-          s_tile[5] = __float_as_int(p.scale[a]);
-          s_tile[6] = j;
+    // 3. The adapter, sub-tile and K chunk of this item (wave 0): the thread
+    //    range whose item prefix brackets it, then a walk over its adapters.
+    if (w == 0) {
+      constexpr int PER = kShrinkThreads / 64;
+      for (int q = 0; q < PER; ++q) {
+        const int t = lane * PER + q;
+        const int lo = (int)(s_pref[t] & 0xffffffu), hi = (int)(s_pref[t + 1] & 0xffffffu);
+        if (item >= lo && item < hi) {
+          const uint64_t b = s_pref[t];
+          int s_it = lo, s_sub = (int)((b >> 24) & 0xfffffu), pos = base_pos + (int)(b >> 44);
+          for (int i = 0; i < APT; ++i) {
+            const int a = t * APT + i;
+            const int v = info[a];
+            const int c = v & 0xfffff, ng = v >> 20;
+            const int sub = ng ? (c + kSubTile - 1) / kSubTile : 0;
+            const int S = by_ng(p.S, ng);
+            const int its = ng ? sub * S : 0;
+            if (item < s_it + its) {
+              const int j = (item - s_it) / S;
+              s_tile[0] = a;
+              s_tile[1] = pos + j * kSubTile;
+              s_tile[2] = min(kSubTile, c - j * kSubTile);
+              s_tile[6] = j;
+              s_tile[7] = s_sub + j;
+              s_tile[8] = item - s_it - j * S;
+              break;
+            }
+            s_it += its;
+            s_sub += sub;
+            pos += c;
+          }
         }
-        s += sub;
-        pos += c;
       }
     }
     __syncthreads();
-    const int a = s_tile[0], pos0 = s_tile[1], m = s_tile[2], r = s_tile[3], jt = s_tile[6];
-    const int ro = s_tile[4];
-    const float sc = __int_as_float(s_tile[5]);
+    // The adapter index is the same in every lane: scalar loads of its
+    // metadata (in the cache since the prologue).
+    const int a = __builtin_amdgcn_readfirstlane(s_tile[0]);
+    const int pos0 = s_tile[1], m = s_tile[2], jt = s_tile[6];
+    const int st = s_tile[7], kc = s_tile[8];
+    const int r = p.rank[a], ro = p.row_off[a];
+    const float sc = p.scale[a];
+    const int ng = (r + 15) >> 4;
     // 4. The sub-tile's tokens: ranks [16 jt, 16 jt + 16) among the tokens of
     //    adapter a, in token order.
     if (kIds) {
@@ -196,25 +229,25 @@ __global__ void __launch_bounds__(kShrinkThreads) shrink_kernel(ShrinkArgs p) {
     }
     __syncthreads();
     // 5. This wave's K steps of chunk kc.
-    const int ng = (r + 15) >> 4;
     {
       const int tl = lane & 15;
       const int tk = tl < m ? s_tok[tl] : -1;
       const bool tval = tk >= 0;
       const char* xrow = p.x + (int64_t)(tval ? tk : 0) * p.ldx_bytes;
       const char* a_rows = p.a_pack + (size_t)ro * p.d_in * E::kBytes;
-      const int k0 = kc * p.kchunk + w * p.spw * KSTEP;
-      const int kw = p.spw * KSTEP;
+      const int spw = by_ng(p.spw, ng);
+      const int k0 = kc * by_ng(p.kchunk, ng) + w * spw * KSTEP;
+      const int kw = spw * KSTEP;
       f32x4_t* slot = red + w * p.ng_max * 64;
       switch (ng) {
-        case 1: shrink_wave<E, 1, 4>(xrow, tval, a_rows, p.d_in, r, k0, kw, slot); break;
-        case 2: shrink_wave<E, 2, 4>(xrow, tval, a_rows, p.d_in, r, k0, kw, slot); break;
-        case 3: shrink_wave<E, 3, 2>(xrow, tval, a_rows, p.d_in, r, k0, kw, slot); break;
-        default: shrink_wave<E, 4, 2>(xrow, tval, a_rows, p.d_in, r, k0, kw, slot); break;
+        case 1: shrink_wave<E, 1, 8>(xrow, tval, a_rows, p.d_in, r, k0, kw, slot); break;
+        case 2: shrink_wave<E, 2, 5>(xrow, tval, a_rows, p.d_in, r, k0, kw, slot); break;
+        case 3: shrink_wave<E, 3, 4>(xrow, tval, a_rows, p.d_in, r, k0, kw, slot); break;
+        default: shrink_wave<E, 4, 3>(xrow, tval, a_rows, p.d_in, r, k0, kw, slot); break;
       }
     }
     __syncthreads();
-    // 6. Sum the 16 waves' tiles in wave order; write partial kc.  Lane l of
+    // 6. Sum the waves' tiles in wave order; write partial kc.  Lane l of
     //    row group q holds token l % 16, ranks 16 q + 4 (l / 16) + 0..3.
     if (tid < ng * 64) {
       const int q = tid >> 6, l = tid & 63;
@@ -243,6 +276,7 @@ __global__ void __launch_bounds__(kShrinkThreads) shrink_kernel(ShrinkArgs p) {
       else if (tid == 3) v = r;
       else if (tid == 4) v = ro;
       else if (tid == 5) v = __float_as_int(sc);
+      else if (tid == 6) v = by_ng(p.S, ng);
       else if (tid >= 8 && tid < 8 + kSubTile) v = tid - 8 < m ? s_tok[tid - 8] : -1;
       reinterpret_cast<int32_t*>(entries + st)[tid] = v;
     }
@@ -255,12 +289,12 @@ __global__ void __launch_bounds__(kShrinkThreads) shrink_kernel(ShrinkArgs p) {
 // them), for every sub-tile of the plan.
 __global__ void __launch_bounds__(256)
 reduce_partials_kernel(const char* __restrict__ plan, int max_sub, const float* __restrict__ part,
-                       int64_t ldp, int64_t pstride, int S, int T, float* __restrict__ h, int64_t ldh) {
+                       int64_t ldp, int64_t pstride, int T, float* __restrict__ h, int64_t ldh) {
   const int st = blockIdx.x;
   const int count = min(*reinterpret_cast<const int32_t*>(plan), max_sub);
   if (st >= count) return;
   const TileEntry* e = reinterpret_cast<const TileEntry*>(plan + kPlanHeaderBytes) + st;
-  const int m = e->m, r = e->r, pos0 = e->pos0;
+  const int m = e->m, r = e->r, pos0 = e->pos0, S = e->S;
   for (int idx = threadIdx.x; idx < m * r; idx += 256) {
     const int i = idx / r, j = idx - i * r;
     const int row = pos0 + i;
@@ -324,7 +358,8 @@ plan_kernel(const int32_t* __restrict__ seg_off, const int32_t* __restrict__ per
     e.r = rank[a];
     e.row_off = row_off[a];
     e.scale = scale[a];
-    e.pad0[0] = e.pad0[1] = 0;
+    e.S = 1;
+    e.pad0 = 0;
 #pragma unroll
     for (int i = 0; i < kSubTile; ++i) {
       const int q = pos0 + i;
@@ -353,8 +388,8 @@ static int cu_count() {
 static int ng_of(int r_max) { return r_max <= 16 ? 1 : (r_max + 15) / 16; }
 
 size_t shrink_lds_bytes(int T, int n, int r_max, bool with_ids) {
-  size_t b = (size_t)ng_of(r_max) * kShrinkWaves * 64 * 16;
-  if (with_ids) b += (size_t)((n + 3) & ~3) * 4 + align_up((size_t)T * 2, 16);
+  size_t b = (size_t)ng_of(r_max) * kShrinkWaves * 64 * 16 + (size_t)((n + 3) & ~3) * 4;
+  if (with_ids) b += align_up((size_t)T * 2, 16);
   return b;
 }
 
@@ -394,9 +429,11 @@ hipError_t launch_shrink(const lora_store& s, const int32_t* ids, const int32_t*
   a.scale = s.scale;
   a.d_in = s.d_in;
   a.ng_max = ng_of(s.r_max);
-  a.spw = sp.spw;
-  a.S = sp.S;
-  a.kchunk = sp.kchunk;
+  for (int g = 0; g < 5; ++g) {
+    a.spw[g] = sp.spw[g];
+    a.S[g] = sp.S[g];
+    a.kchunk[g] = sp.kchunk[g];
+  }
   a.part = reinterpret_cast<float*>(base + L.part);
   a.ldp = partial_ld(s.r_max);
   a.pstride = (int64_t)T * a.ldp;
@@ -404,30 +441,29 @@ hipError_t launch_shrink(const lora_store& s, const int32_t* ids, const int32_t*
   a.warm_key = 0x7fc00001;  // a NaN pattern folded with row offsets: never equal in practice
   const bool with_ids = ids != nullptr;
   const size_t lds = shrink_lds_bytes(T, s.n, s.r_max, with_ids);
-  const int64_t items = max_sub * sp.S;
+  const int64_t items = max_sub * sp.S_max;
   const int grid = (int)(items < 2LL * cu_count() ? items : 2LL * cu_count());
   const bool bf = s.dtype == LORA_DTYPE_BF16;
   if (with_ids)
-    return bf ? launch_shrink_t<BF16, true, 4>(a, grid, lds, stream)
-              : launch_shrink_t<F32, true, 4>(a, grid, lds, stream);
+    return bf ? launch_shrink_t<BF16, true, 8>(a, grid, lds, stream)
+              : launch_shrink_t<F32, true, 8>(a, grid, lds, stream);
   if (s.n <= kGroupMaxN)
-    return bf ? launch_shrink_t<BF16, false, 4>(a, grid, lds, stream)
-              : launch_shrink_t<F32, false, 4>(a, grid, lds, stream);
-  return bf ? launch_shrink_t<BF16, false, 16>(a, grid, lds, stream)
-            : launch_shrink_t<F32, false, 16>(a, grid, lds, stream);
+    return bf ? launch_shrink_t<BF16, false, 8>(a, grid, lds, stream)
+              : launch_shrink_t<F32, false, 8>(a, grid, lds, stream);
+  return bf ? launch_shrink_t<BF16, false, 32>(a, grid, lds, stream)
+            : launch_shrink_t<F32, false, 32>(a, grid, lds, stream);
 }
 
 hipError_t launch_reduce_partials(const lora_store& s, int T, const void* ws, float* h, int64_t ldh,
                                   hipStream_t stream) {
   const int64_t max_sub = plan_max_subtiles(T, s.n);
   if (max_sub == 0) return hipSuccess;
-  const ShrinkSplit sp = shrink_split(s.d_in, s.r_max, s.dtype);
   const WsLayout L = ws_layout(T, s.n, s.d_in, s.r_max, s.dtype);
   const char* base = reinterpret_cast<const char*>(ws);
   const int64_t ldp = partial_ld(s.r_max);
   hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)max_sub), dim3(256), 0, stream, base + L.plan,
-                     (int)max_sub, reinterpret_cast<const float*>(base + L.part), ldp, (int64_t)T * ldp, sp.S,
-                     T, h, ldh);
+                     (int)max_sub, reinterpret_cast<const float*>(base + L.part), ldp, (int64_t)T * ldp, T, h,
+                     ldh);
   return hipGetLastError();
 }
 

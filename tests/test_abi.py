@@ -187,20 +187,24 @@ def test_apply_rejects_before_launch(lib):
 def _layout_bytes(T, n, d_in, r_max, e):
     """The workspace layout restated: plan (256-byte header + one 128-byte
     entry per possible sub-tile of <= 16 tokens), float32 partial sums for
-    S chunks of d_in at row stride r_max rounded up to 8, and seg_off + perm
-    when n exceeds the in-kernel histogram's 4096 adapters; 256-byte aligned."""
+    the largest number S of d_in chunks any stored rank uses (8 waves times
+    8/5/4/3 steps of 64 bytes for 1..4 groups of 16 ranks, at most 8 chunks)
+    at row stride r_max rounded up to 8, and seg_off + perm when n exceeds
+    the in-kernel histogram's 4096 adapters; each part 256-byte aligned."""
     up = lambda v: -(-v // 256) * 256
     max_sub = (T + 15 * min(n, T)) // 16 if T > 0 else 0
-    step = 64 // e  # K values per 64 bytes
-    steps = -(-d_in // step)
-    ng = 1 if r_max <= 16 else -(-r_max // 16)
-    spw = 4 if ng <= 2 else 2
-    S = -(-steps // (16 * spw))
-    if S > 8:
-        spw = -(-steps // 128)
-        S = -(-steps // (16 * spw))
+    steps = -(-d_in // (64 // e))
+    ng_max = 1 if r_max <= 16 else -(-r_max // 16)
+    S_max = 1
+    for ng in range(1, ng_max + 1):
+        spw = {1: 8, 2: 5, 3: 4, 4: 3}[ng]
+        S = -(-steps // (8 * spw))
+        if S > 8:
+            spw = -(-steps // 64)
+            S = -(-steps // (8 * spw))
+        S_max = max(S_max, S)
     ldp = -(-max(r_max, 1) // 8) * 8
-    total = up(256 + 128 * max_sub) + up(S * T * ldp * 4)
+    total = up(256 + 128 * max_sub) + up(S_max * T * ldp * 4)
     if n > 4096:
         total += up((n + 2) * 4) + up(T * 4)
     return total

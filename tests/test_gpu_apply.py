@@ -127,13 +127,24 @@ def test_separate_kernels_integer_exact_decode():
 
 @pytest.mark.parametrize("key", ["1", "3", "4"])
 def test_padded_equals_specialized(key):
-    """The rank-padded store (zero rows up to r_max) gives bit-identical y."""
+    """The rank-padded store (zero rows and columns up to r_max) gives the
+    same y: bit for bit on exact integer data; on float data to float32
+    rounding (the shrink cuts d_in into chunks per rank bucket, so a padded
+    adapter's sum over d_in is formed in another order): within one output
+    ulp plus 1e-5 of the largest output for sums that cancel."""
     dev = device()
     for integer in (True, False):
         wl = make_config(key, integer=integer)
         _, _, _, y1 = _run_apply(wl, dev)
         _, _, _, y2 = _run_apply(wl, dev, pad_to=int(wl.module.ranks.max()))
-        assert np.array_equal(hbits(y1), hbits(y2)), (key, integer)
+        if integer:
+            assert np.array_equal(hbits(y1), hbits(y2)), key
+        else:
+            a, b = y_host(y1), y_host(y2)
+            ulp = 2.0 ** -7 if wl.dtype == "bf16" else 2.0 ** -22
+            floor = 1e-5 * np.abs(a).max()  # float32 rounding of sums that cancel
+            assert np.all(np.abs(a - b) <= ulp * np.maximum(np.abs(a), np.abs(b)) + floor), key
+            assert rel_err(a, _ref(wl)) <= TOL[wl.dtype] and rel_err(b, _ref(wl)) <= TOL[wl.dtype]
 
 
 def test_deterministic():
@@ -284,3 +295,38 @@ def test_fp32_output_width_not_multiple_of_8():
     assert torch.equal(wide[:, 44:], before[:, 44:])
     ref = _ref(wl)
     assert np.abs(y_host(wide[:, :44]) - ref).max() <= 1e-5 * np.abs(ref).max()
+
+
+def test_graph_replay_matches_eager():
+    """The apply captured in a HIP graph (as the benchmark times it) and
+    replayed several times, with eager work and synchronizations between the
+    replays: every replay equals the eager result bit for bit."""
+    dev = device()
+    wl = make_config("3", with_y0=True)
+    store = pack(wl, dev)
+    x, ids, y0 = inputs(wl, dev)
+    ws = torch.empty(rs.lora_workspace_bytes(store, wl.T), dtype=torch.uint8, device=dev)
+    note("graph: eager reference")
+    y_eager = y0.clone()
+    rs.lora_apply_batched(store, x, y_eager, ids=ids, ws=ws)
+    y = y0.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm up on the capture stream
+        y.copy_(y0)
+        rs.lora_apply_batched(store, x, y, ids=ids, ws=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    note("graph: capture")
+    with torch.cuda.graph(g):
+        y.copy_(y0)
+        rs.lora_apply_batched(store, x, y, ids=ids, ws=ws)
+    other = y0.clone()
+    for k in range(4):
+        note(f"graph: replay {k}")
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_eager.view(torch.int16)), k
+        rs.lora_apply_batched(store, x, other, ids=ids, ws=ws)  # eager work between replays
+        torch.cuda.synchronize()
