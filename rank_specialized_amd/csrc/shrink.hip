@@ -38,7 +38,6 @@
 
 namespace lora {
 
-constexpr int kMaxBlocks64 = LORA_SEGMENT_MAX_T / 64;  // 64-token blocks of the ids
 
 struct ShrinkArgs {
   const int32_t* ids;      // ids mode
@@ -69,7 +68,11 @@ __device__ __forceinline__ int by_ng(const int (&v)[5], int ng) {
 //   info[a]  = tokens of adapter a | row groups of its rank << 20 (0: rank 0)
 //   pref[t]  = exclusive prefix, over the adapters of threads < t, of
 //              tokens << 44 | sub-tiles << 24 | items; pref[threads] = total
-// Thread t owns adapters [t * APT, (t + 1) * APT).
+// Thread t owns adapters [t * APT, (t + 1) * APT).  A workgroup takes items
+// blockIdx.x + k * gridDim.x, k < kMaxItems, and prepares all of them (owner,
+// sub-tile, K chunk, tokens, metadata) before the first one's loads.
+constexpr int kMaxItems = 8;
+
 template <typename E, bool kIds, int APT>
 __global__ void __launch_bounds__(kShrinkThreads, 4) shrink_kernel(ShrinkArgs p) {
   constexpr int KSTEP = 4 * E::kVec;
@@ -79,16 +82,19 @@ __global__ void __launch_bounds__(kShrinkThreads, 4) shrink_kernel(ShrinkArgs p)
   uint16_t* id16 = reinterpret_cast<uint16_t*>(info + ((p.n + 3) & ~3));               // [T] (ids)
   __shared__ uint64_t s_wsum[kShrinkWaves];
   __shared__ uint64_t s_pref[kShrinkThreads + 1];
-  __shared__ int s_tile[10];
-  __shared__ int s_tok[kSubTile];
-  __shared__ int s_bc[kMaxBlocks64];
+  // Per item k: adapter, first grouped position, tokens, stored rank, row
+  // offset, scale bits, sub-tile index within the adapter, plan sub-tile, K chunk.
+  __shared__ int s_it[kMaxItems][9];
+  __shared__ int s_tok[kMaxItems][kSubTile];
+  __shared__ int s_bc[kMaxItems][kShrinkWaves];
+  __shared__ int s_sink;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = p.n, T = p.T;
 
   // 1. Tokens per adapter into info[].  The metadata of this thread's
   //    adapters is loaded meanwhile (ranks are needed below; row offsets and
   //    scales are only folded into a value that is never stored in
-  //    practice: the loads bring them into the cache for the item loop).
+  //    practice: the loads bring them into the cache for step 3).
   const int a0 = tid * APT;
   int rk_[APT];
   int warm = 0;
@@ -99,19 +105,52 @@ __global__ void __launch_bounds__(kShrinkThreads, 4) shrink_kernel(ShrinkArgs p)
     if (a < n) warm ^= p.row_off[a] ^ __float_as_int(p.scale[a]);
   }
   if (kIds) {
+    // ids: 4 per thread per 16-byte load, all loads issued before the
+    // histogram consumes them (T <= 16384: at most 8 loads per thread).
+    constexpr int kIdLoads = LORA_SEGMENT_MAX_T / (4 * kShrinkThreads);
+    int4 iv[kIdLoads];
+    const bool vec = ((uintptr_t)p.ids & 15u) == 0;  // same for every thread
+#pragma unroll
+    for (int q = 0; q < kIdLoads; ++q) {
+      const int t = 4 * (q * kShrinkThreads + tid);
+      if (vec && t + 3 < T) {
+        iv[q] = *reinterpret_cast<const int4*>(p.ids + t);
+      } else {
+        iv[q].x = t < T ? p.ids[t] : -1;
+        iv[q].y = t + 1 < T ? p.ids[t + 1] : -1;
+        iv[q].z = t + 2 < T ? p.ids[t + 2] : -1;
+        iv[q].w = t + 3 < T ? p.ids[t + 3] : -1;
+      }
+    }
     for (int i = tid; i < n; i += kShrinkThreads) info[i] = 0;
     __syncthreads();
-    for (int t = tid; t < T; t += kShrinkThreads) {
-      const int v = p.ids[t];
-      const bool ok = (unsigned)v < (unsigned)n;
-      id16[t] = ok ? (uint16_t)v : (uint16_t)0xFFFFu;
-      if (ok) atomicAdd(&info[v], 1);
+    // Histogram: a wave instruction whose ids are all equal (a run of one
+    // adapter's tokens, as in prefill segments) adds its count with one LDS
+    // atomic instead of 64 conflicting ones; otherwise one atomic per lane.
+#pragma unroll
+    for (int q = 0; q < kIdLoads; ++q) {
+      const int t = 4 * (q * kShrinkThreads + tid);
+      if (4 * q * kShrinkThreads < T) {  // uniform over the workgroup
+        const int v4[4] = {iv[q].x, iv[q].y, iv[q].z, iv[q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = t + e < T && (unsigned)v4[e] < (unsigned)n;
+          if (t + e < T) id16[t + e] = ok ? (uint16_t)v4[e] : (uint16_t)0xFFFFu;
+          const uint64_t valid = __ballot(ok);
+          const int leader = valid ? __ffsll((long long)valid) - 1 : 0;
+          const int lv = __shfl(v4[e], leader);
+          if (valid && __ballot(ok && v4[e] == lv) == valid) {
+            if (lane == leader) atomicAdd(&info[lv], __popcll(valid));
+          } else if (ok) {
+            atomicAdd(&info[v4[e]], 1);
+          }
+        }
+      }
     }
   } else {
     for (int i = tid; i < n; i += kShrinkThreads) info[i] = p.seg_off[i + 1] - p.seg_off[i];
   }
   __syncthreads();
-  if (warm == p.warm_key) s_tile[9] = warm;  // warm_key is never produced by valid metadata
   // 2. Pack (tokens, row groups) per adapter; scan (tokens, sub-tiles, items).
   uint64_t mine = 0;
 #pragma unroll
@@ -135,103 +174,137 @@ __global__ void __launch_bounds__(kShrinkThreads, 4) shrink_kernel(ShrinkArgs p)
   if (blockIdx.x == 0 && tid == 0) *reinterpret_cast<int32_t*>(p.plan) = total_sub;
   const int base_pos = kIds ? 0 : p.seg_off[0];
   const int items = (int)(tot & 0xffffffu);
-  TileEntry* entries = reinterpret_cast<TileEntry*>(p.plan + kPlanHeaderBytes);
+  const int first = blockIdx.x;
+  const int nk = first < items ? min(kMaxItems, (items - first + (int)gridDim.x - 1) / (int)gridDim.x) : 0;
+  __syncthreads();
+  if (nk == 0) {  // uniform: no barrier follows for this workgroup
+    if (warm == p.warm_key) s_sink = warm;
+    return;
+  }
+
+  // 3. Owner, sub-tile and K chunk of each item: lane k of wave 0 takes item
+  //    k (binary search for the thread range whose item prefix brackets it,
+  //    then a walk over that thread's adapters).  Its metadata loads are
+  //    issued here and written to LDS only after step 4.
+  int m_rank = 0, m_ro = 0;
+  float m_sc = 0.f;
+  if (w == 0 && lane < nk) {
+    const int it = first + lane * (int)gridDim.x;
+    int lo = 0, hi = kShrinkThreads;  // items(pref[lo]) <= it < items(pref[hi])
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if ((int)(s_pref[mid] & 0xffffffu) <= it) lo = mid; else hi = mid;
+    }
+    const uint64_t b = s_pref[lo];
+    int s_items = (int)(b & 0xffffffu), s_sub = (int)((b >> 24) & 0xfffffu);
+    int pos = base_pos + (int)(b >> 44);
+    for (int i = 0; i < APT; ++i) {
+      const int a = lo * APT + i;
+      const int v = info[a];
+      const int c = v & 0xfffff, ng = v >> 20;
+      const int sub = ng ? (c + kSubTile - 1) / kSubTile : 0;
+      const int S = by_ng(p.S, ng);
+      const int its = ng ? sub * S : 0;
+      if (it < s_items + its) {
+        const int j = (it - s_items) / S;
+        int* q = s_it[lane];
+        q[0] = a;
+        q[1] = pos + j * kSubTile;
+        q[2] = min(kSubTile, c - j * kSubTile);
+        q[6] = j;
+        q[7] = s_sub + j;
+        q[8] = it - s_items - j * S;
+        m_rank = p.rank[a];
+        m_ro = p.row_off[a];
+        m_sc = p.scale[a];
+        break;
+      }
+      s_items += its;
+      s_sub += sub;
+      pos += c;
+    }
+  }
+  __syncthreads();
+  // 4. Each item's tokens: ranks [16 j, 16 j + 16) among the tokens of its
+  //    adapter, in token order.  ids: wave w scans a contiguous range of
+  //    64-token blocks twice - once to count each item's matches, then, after
+  //    a scan of the (item, wave) counts, to place them with ballot ranks.
+  if (kIds) {
+    const int nb = (T + 63) >> 6;
+    const int per = (nb + kShrinkWaves - 1) / kShrinkWaves;
+    const int b0 = w * per, b1 = min(nb, b0 + per);
+    int ad[kMaxItems], cnt[kMaxItems];
+#pragma unroll
+    for (int k = 0; k < kMaxItems; ++k) {
+      ad[k] = k < nk ? s_it[k][0] : -2;
+      cnt[k] = 0;
+    }
+    for (int b = b0; b < b1; ++b) {
+      const int t = b * 64 + lane;
+      const int id = t < T ? (int)id16[t] : -1;
+#pragma unroll
+      for (int k = 0; k < kMaxItems; ++k)
+        if (k < nk) cnt[k] += __popcll(__ballot(id == ad[k]));
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int k = 0; k < kMaxItems; ++k)
+        if (k < nk) s_bc[k][w] = cnt[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kMaxItems; ++k) {  // tokens of item k before wave w's range
+      int before = 0;
+      if (k < nk)
+        for (int ww = 0; ww < w; ++ww) before += s_bc[k][ww];
+      cnt[k] = before - (k < nk ? s_it[k][6] : 0) * kSubTile;
+    }
+    for (int b = b0; b < b1; ++b) {
+      const int t = b * 64 + lane;
+      const int id = t < T ? (int)id16[t] : -1;
+#pragma unroll
+      for (int k = 0; k < kMaxItems; ++k) {
+        if (k < nk) {
+          const bool hit = id == ad[k];
+          const uint64_t bal = __ballot(hit);
+          const int rk = cnt[k] + __popcll(bal & lanemask_lt());
+          if (hit && rk >= 0 && rk < kSubTile) s_tok[k][rk] = t;
+          cnt[k] += __popcll(bal);
+        }
+      }
+    }
+  } else {
+    for (int idx = tid; idx < nk * kSubTile; idx += kShrinkThreads) {
+      const int k = idx / kSubTile, i = idx - k * kSubTile;
+      if (i < s_it[k][2]) {
+        const int q = s_it[k][1] + i;
+        const int tk = (q >= 0 && q < T) ? p.perm[q] : -1;
+        s_tok[k][i] = (unsigned)tk < (unsigned)T ? tk : -1;
+      }
+    }
+  }
+  if (w == 0 && lane < nk) {
+    s_it[lane][3] = m_rank;
+    s_it[lane][4] = m_ro;
+    s_it[lane][5] = __float_as_int(m_sc);
+  }
   __syncthreads();
 
-  for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    // 3. The adapter, sub-tile and K chunk of this item (wave 0): the thread
-    //    range whose item prefix brackets it, then a walk over its adapters.
-    if (w == 0) {
-      constexpr int PER = kShrinkThreads / 64;
-      for (int q = 0; q < PER; ++q) {
-        const int t = lane * PER + q;
-        const int lo = (int)(s_pref[t] & 0xffffffu), hi = (int)(s_pref[t + 1] & 0xffffffu);
-        if (item >= lo && item < hi) {
-          const uint64_t b = s_pref[t];
-          int s_it = lo, s_sub = (int)((b >> 24) & 0xfffffu), pos = base_pos + (int)(b >> 44);
-          for (int i = 0; i < APT; ++i) {
-            const int a = t * APT + i;
-            const int v = info[a];
-            const int c = v & 0xfffff, ng = v >> 20;
-            const int sub = ng ? (c + kSubTile - 1) / kSubTile : 0;
-            const int S = by_ng(p.S, ng);
-            const int its = ng ? sub * S : 0;
-            if (item < s_it + its) {
-              const int j = (item - s_it) / S;
-              s_tile[0] = a;
-              s_tile[1] = pos + j * kSubTile;
-              s_tile[2] = min(kSubTile, c - j * kSubTile);
-              s_tile[6] = j;
-              s_tile[7] = s_sub + j;
-              s_tile[8] = item - s_it - j * S;
-              break;
-            }
-            s_it += its;
-            s_sub += sub;
-            pos += c;
-          }
-        }
-      }
-    }
-    __syncthreads();
-    // The adapter index is the same in every lane: scalar loads of its
-    // metadata (in the cache since the prologue).
-    const int a = __builtin_amdgcn_readfirstlane(s_tile[0]);
-    const int pos0 = s_tile[1], m = s_tile[2], jt = s_tile[6];
-    const int st = s_tile[7], kc = s_tile[8];
-    const int r = p.rank[a], ro = p.row_off[a];
-    const float sc = p.scale[a];
+  TileEntry* entries = reinterpret_cast<TileEntry*>(p.plan + kPlanHeaderBytes);
+  for (int k = 0; k < nk; ++k) {
+    const int a = __builtin_amdgcn_readfirstlane(s_it[k][0]);
+    const int pos0 = __builtin_amdgcn_readfirstlane(s_it[k][1]);
+    const int m = __builtin_amdgcn_readfirstlane(s_it[k][2]);
+    const int r = __builtin_amdgcn_readfirstlane(s_it[k][3]);
+    const int ro = __builtin_amdgcn_readfirstlane(s_it[k][4]);
+    const float sc = __int_as_float(__builtin_amdgcn_readfirstlane(s_it[k][5]));
+    const int st = __builtin_amdgcn_readfirstlane(s_it[k][7]);
+    const int kc = __builtin_amdgcn_readfirstlane(s_it[k][8]);
     const int ng = (r + 15) >> 4;
-    // 4. The sub-tile's tokens: ranks [16 jt, 16 jt + 16) among the tokens of
-    //    adapter a, in token order.
-    if (kIds) {
-      const int nb = (T + 63) >> 6;
-      for (int b = w; b < nb; b += kShrinkWaves) {
-        const int t = b * 64 + lane;
-        const uint64_t bal = __ballot(t < T && id16[t] == (uint16_t)a);
-        if (lane == 0) s_bc[b] = __popcll(bal);
-      }
-      __syncthreads();
-      if (w == 0) {  // exclusive scan of the block counts (4 per lane)
-        int v[4], sum = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int idx = lane * 4 + q;
-          v[q] = idx < nb ? s_bc[idx] : 0;
-          sum += v[q];
-        }
-        int x = sum;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const int y = __shfl_up(x, d);
-          if (lane >= d) x += y;
-        }
-        int run = x - sum;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int idx = lane * 4 + q;
-          if (idx < nb) s_bc[idx] = run;
-          run += v[q];
-        }
-      }
-      __syncthreads();
-      for (int b = w; b < nb; b += kShrinkWaves) {
-        const int t = b * 64 + lane;
-        const bool hit = t < T && id16[t] == (uint16_t)a;
-        const uint64_t bal = __ballot(hit);
-        const int rk = s_bc[b] + __popcll(bal & lanemask_lt()) - jt * kSubTile;
-        if (hit && rk >= 0 && rk < kSubTile) s_tok[rk] = t;
-      }
-    } else if (tid < m) {
-      const int q = pos0 + tid;
-      const int tk = (q >= 0 && q < T) ? p.perm[q] : -1;
-      s_tok[tid] = (unsigned)tk < (unsigned)T ? tk : -1;
-    }
-    __syncthreads();
     // 5. This wave's K steps of chunk kc.
     {
       const int tl = lane & 15;
-      const int tk = tl < m ? s_tok[tl] : -1;
+      const int tk = tl < m ? s_tok[k][tl] : -1;
       const bool tval = tk >= 0;
       const char* xrow = p.x + (int64_t)(tval ? tk : 0) * p.ldx_bytes;
       const char* a_rows = p.a_pack + (size_t)ro * p.d_in * E::kBytes;
@@ -253,7 +326,7 @@ __global__ void __launch_bounds__(kShrinkThreads, 4) shrink_kernel(ShrinkArgs p)
       const int q = tid >> 6, l = tid & 63;
       f32x4_t s = red[q * 64 + l];
 #pragma unroll
-      for (int k = 1; k < kShrinkWaves; ++k) s += red[(k * p.ng_max + q) * 64 + l];
+      for (int kk = 1; kk < kShrinkWaves; ++kk) s += red[(kk * p.ng_max + q) * 64 + l];
       const int tk = l & 15;
       const int j0 = q * 16 + 4 * (l >> 4);
       const int row = pos0 + tk;
@@ -277,11 +350,12 @@ __global__ void __launch_bounds__(kShrinkThreads, 4) shrink_kernel(ShrinkArgs p)
       else if (tid == 4) v = ro;
       else if (tid == 5) v = __float_as_int(sc);
       else if (tid == 6) v = by_ng(p.S, ng);
-      else if (tid >= 8 && tid < 8 + kSubTile) v = tid - 8 < m ? s_tok[tid - 8] : -1;
+      else if (tid >= 8 && tid < 8 + kSubTile) v = tid - 8 < m ? s_tok[k][tid - 8] : -1;
       reinterpret_cast<int32_t*>(entries + st)[tid] = v;
     }
-    __syncthreads();  // s_tile, s_tok and red are rewritten by the next item
+    __syncthreads();  // red is rewritten by the next item
   }
+  if (warm == p.warm_key) s_sink = warm;  // warm_key is never produced by valid metadata
 }
 
 // ------------------------------------------------------------- reduce
@@ -442,7 +516,9 @@ hipError_t launch_shrink(const lora_store& s, const int32_t* ids, const int32_t*
   const bool with_ids = ids != nullptr;
   const size_t lds = shrink_lds_bytes(T, s.n, s.r_max, with_ids);
   const int64_t items = max_sub * sp.S_max;
-  const int grid = (int)(items < 2LL * cu_count() ? items : 2LL * cu_count());
+  int64_t g = (items + kMaxItems - 1) / kMaxItems;  // every item within kMaxItems of a workgroup
+  if (g < 2LL * cu_count()) g = 2LL * cu_count();    // two workgroups per CU
+  const int grid = (int)(g < items ? g : items);
   const bool bf = s.dtype == LORA_DTYPE_BF16;
   if (with_ids)
     return bf ? launch_shrink_t<BF16, true, 8>(a, grid, lds, stream)

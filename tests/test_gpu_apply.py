@@ -330,3 +330,21 @@ def test_graph_replay_matches_eager():
         assert torch.equal(y.view(torch.int16), y_eager.view(torch.int16)), k
         rs.lora_apply_batched(store, x, other, ids=ids, ws=ws)  # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_ids_not_16_byte_aligned():
+    """ids as a slice starting one element into a buffer (4-byte aligned
+    only): the grouping reads them element by element and gives the same y."""
+    dev = device()
+    wl = make_config("3", integer=True)
+    store = pack(wl, dev)
+    x, ids, y1 = inputs(wl, dev)
+    y2 = y1.clone()
+    big = torch.empty(wl.T + 1, dtype=torch.int32, device=dev)
+    big[1:] = ids
+    note("ids offset by one element")
+    rs.lora_apply_batched(store, x, y1, ids=ids)
+    rs.lora_apply_batched(store, x, y2, ids=big[1:])
+    torch.cuda.synchronize()
+    assert np.array_equal(hbits(y1), hbits(y2))
+    assert np.array_equal(y_host(y2), bf16_round_ref(_ref(wl)))
