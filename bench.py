@@ -55,6 +55,14 @@ def parse_args():
     p.add_argument("--no-padded", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--warm", action="store_true", help="no rotation (cache-resident timing)")
+    p.add_argument("--no-graph", action="store_true", help="time eager launches only (counter runs)")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="first run one elementwise copy of 256 MiB (reads and writes 256 MiB), the "
+                        "reference that scales the HBM byte counters")
+    p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="no GPU work: read two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of "
+                        "this script with --calibrate-copy and record HBM bytes per launch of each "
+                        "kernel in profiles/traffic.json")
     return p.parse_args()
 
 
@@ -166,41 +174,46 @@ def time_apply_graph(rs, torch, copies, ids, ws, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall
 
 
-def queue_ahead(torch, ms: float):
-    """Enqueue a spin kernel of about `ms` milliseconds, so that the launches
-    that follow queue up behind it and then run back to back: events around
-    them time the GPU, not the host's launch rate."""
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    probe = 1 << 20
-    e0.record()
-    torch.cuda._sleep(probe)
-    e1.record()
-    torch.cuda.synchronize()
-    per_ms = probe / max(e0.elapsed_time(e1), 1e-3)
-    torch.cuda._sleep(int(per_ms * ms))
-
-
-def time_kernels(rs, torch, copies, ids, ws, steps):
-    """Per-kernel average duration of the apply's two kernels: HIP events
-    recorded on the launch stream before the shrink, between the kernels and
-    after the expand, over the same rotation of copies as the timed steps
-    (queued behind a spin kernel so that host launch time stays out)."""
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    for k in range(min(steps, 10)):  # warm the launch path
-        c = copies[k % len(copies)]
-        rs.lora_apply_batched_timed(c.store, c.x, c.y, ev[k], ids=ids, ws=ws)
-    torch.cuda.synchronize()
-    queue_ahead(torch, 0.08 * steps + 2.0)
-    for k in range(steps):
-        c = copies[k % len(copies)]
-        rs.lora_apply_batched_timed(c.store, c.x, c.y, ev[k], ids=ids, ws=ws)
-    torch.cuda.synchronize()
+def time_kernels(rs, torch, copies, ids, ws, steps, warmup, graph=True):
+    """Average duration of each of the apply's two kernels, measured alone:
+    the same rotation of calls with only that kernel (lora_apply_batched_phases),
+    captured in a HIP graph; HIP events on the launch stream bracket one
+    replay of `steps` launches.  The expand replays read the plan and partial
+    sums the last shrink left in the workspace."""
     out = {}
-    for i, name in enumerate(["shrink", "expand"]):
-        ms = [ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(steps)]
-        out[name] = {"avg_us": 1e3 * float(np.mean(ms)), "p10_us": 1e3 * float(np.percentile(ms, 10)),
-                     "p90_us": 1e3 * float(np.percentile(ms, 90))}
+    for name, phase in (("shrink", 1), ("expand", 2)):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for k in range(max(1, warmup)):
+                c = copies[k % len(copies)]
+                rs.lora_apply_batched(c.store, c.x, c.y, ids=ids, ws=ws)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        def run():
+            for k in range(steps):
+                c = copies[k % len(copies)]
+                rs.lora_apply_batched_phases(c.store, c.x, c.y, phase, ids=ids, ws=ws)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        if graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run()
+            g.replay()
+            torch.cuda.synchronize()
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            del g
+        else:
+            e0.record()
+            run()
+            e1.record()
+            torch.cuda.synchronize()
+        out[name] = {"avg_us": 1e3 * e0.elapsed_time(e1) / steps, "launches": steps,
+                     "timed_as": "one HIP-graph replay" if graph else "eager launches"}
     return out
 
 
@@ -216,6 +229,59 @@ def traffic_for(workload: str, kernel: str):
     if not ent or ent.get("kernel_sources_sha") != kernel_source_digest():
         return None
     return ent.get("hbm_bytes_per_launch")
+
+
+CALIBRATE_BYTES = 256 << 20
+
+
+def read_pmc(run_dir: str, counter: str):
+    """{kernel name: [values per dispatch]} from a rocprofv3 counter run."""
+    import csv
+    import glob
+    out = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return out
+
+
+def summarize_pmc(key: str, fetch_dir: str, write_dir: str):
+    """HBM bytes per launch of the shrink and expand kernels: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) averaged over the dispatches, each scaled by
+    what the same counter reads for an elementwise copy of 256 MiB."""
+    fetch, write = read_pmc(fetch_dir, "FETCH_SIZE"), read_pmc(write_dir, "WRITE_SIZE")
+
+    def calib(d):
+        vals = [v for k, vs in d.items() if "neg" in k for v in vs]
+        if not vals:
+            raise SystemExit("no calibration copy kernel in the counter run (use --calibrate-copy)")
+        return max(vals) * 1024.0 / CALIBRATE_BYTES
+
+    cf, cw = calib(fetch), calib(write)
+    wl = build_workload(key)
+    m = wl.module
+    nb = algorithmic_bytes(wl.ids, m.ranks, m.n, m.d_in, m.d_out, 2 if wl.dtype == "bf16" else 4)
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    rec = json.load(open(path)) if os.path.exists(path) else {}
+    ent = {}
+    for kern in ("shrink", "expand"):
+        fk = [v for k, vs in fetch.items() if f"{kern}_kernel" in k for v in vs]
+        wk = [v for k, vs in write.items() if f"{kern}_kernel" in k for v in vs]
+        if not fk or not wk:
+            raise SystemExit(f"no {kern} dispatches in the counter runs")
+        fb = float(np.mean(fk)) * 1024.0 / cf
+        wb = float(np.mean(wk)) * 1024.0 / cw
+        ent[kern] = {"hbm_bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
+                     "algorithmic_bytes": nb[kern], "traffic_over_algorithmic": round((fb + wb) / nb[kern], 3),
+                     "dispatches": len(fk), "kernel_sources_sha": kernel_source_digest()}
+    ent["calibration"] = {"copy_bytes": CALIBRATE_BYTES, "fetch_factor": round(cf, 4), "write_factor": round(cw, 4)}
+    rec[f"config{key}"] = ent
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    print(json.dumps({f"config{key}": ent}))
 
 
 def cpu_baseline(wl, seconds: float):
@@ -248,6 +314,9 @@ def cpu_baseline(wl, seconds: float):
 
 def main():
     args = parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.config, *args.summarize_pmc)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; the apply's sharding across GPUs "
                                    "is described in DESIGN.md but not built", "n_gpus": args.gpus}))
@@ -260,6 +329,12 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     dev = torch.device("cuda", 0)
+    if args.calibrate_copy:
+        src = torch.ones(CALIBRATE_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     key = args.config
     wl = build_workload(key)
     m = wl.module
@@ -270,8 +345,11 @@ def main():
     copies, per_copy = make_copies(rs, torch, wl, dev, 0, not args.warm)
     ws = torch.empty(rs.lora_workspace_bytes(copies[0].store, wl.T), dtype=torch.uint8, device=dev)
     eager_ms, eager_wall = time_apply(rs, torch, copies, ids, ws, args.steps, args.warmup)
-    ms, wall = time_apply_graph(rs, torch, copies, ids, ws, args.steps, args.warmup)
-    kern = time_kernels(rs, torch, copies, ids, ws, args.steps)
+    if args.no_graph:
+        ms, wall = eager_ms, eager_wall
+    else:
+        ms, wall = time_apply_graph(rs, torch, copies, ids, ws, args.steps, args.warmup)
+    kern = time_kernels(rs, torch, copies, ids, ws, args.steps, args.warmup, graph=not args.no_graph)
     gbps = nbytes["total"] / (ms * 1e-3) / 1e9
 
     dom = max(("shrink", "expand"), key=lambda k: kern[k]["avg_us"])
@@ -301,7 +379,8 @@ def main():
         for name, pad in variants.items():
             pc, _ = make_copies(rs, torch, wl, dev, pad, not args.warm)
             pws = torch.empty(rs.lora_workspace_bytes(pc[0].store, wl.T), dtype=torch.uint8, device=dev)
-            pms, _ = time_apply_graph(rs, torch, pc, ids, pws, max(20, args.steps // 2), args.warmup)
+            pms, _ = (time_apply if args.no_graph else time_apply_graph)(rs, torch, pc, ids, pws,
+                                                                       max(20, args.steps // 2), args.warmup)
             own = algorithmic_bytes(wl.ids, np.full(m.n, pad), m.n, m.d_in, m.d_out, e)["total"]
             padded[name] = {"pad_to": pad, "ms_per_step": round(pms, 5),
                             "tokens_per_s": round(wl.T / (pms * 1e-3), 1),
@@ -337,7 +416,8 @@ def main():
         "kernels": kern,
         "padded": padded,
         "wall_s_timed": round(wall, 6),
-        "timed_as": "one HIP-graph replay of the K captured steps (eager launches: see eager_ms_per_step)",
+        "timed_as": "eager launches" if args.no_graph else
+                    "one HIP-graph replay of the K captured steps (eager launches: see eager_ms_per_step)",
         "eager_ms_per_step": round(eager_ms, 5),
         "kernel_sources_sha": kernel_source_digest(),
     }

@@ -225,17 +225,16 @@ int lora_apply_batched(const lora_store* store_host, const void* x, int64_t ldx,
                        size_t ws_bytes, void* stream);
 
 /*
- * lora_apply_batched with timing marks, for measurement: events_host[0..2]
- * are hipEvent_t handles (created by the caller) that are recorded on
- * `stream` before the shrink kernel, between the shrink and the expand, and
- * after the expand (when n > 4096 with ids, the sort runs after mark 0).
- * Errors: as lora_apply_batched; INVALID_ARG for a null events_host or
- * event.
+ * One kernel of lora_apply_batched at a time, for measuring each alone:
+ * phases = 1 runs the shrink only (grouping, partial sums and plan into ws;
+ * with ids and n > 4096 also the sort), 2 the expand only (from the plan and
+ * partial sums a previous phase-1 call left in ws, for the same store, T and
+ * grouping), 3 both (= lora_apply_batched).  Errors: as lora_apply_batched;
+ * INVALID_ARG for phases outside 1..3.
  */
-int lora_apply_batched_timed(const lora_store* store_host, const void* x, int64_t ldx, void* y,
-                             int64_t ldy, int T, const int32_t* ids, const int32_t* seg_off,
-                             const int32_t* perm, void* ws, size_t ws_bytes, void* stream,
-                             void* const* events_host);
+int lora_apply_batched_phases(const lora_store* store_host, const void* x, int64_t ldx, void* y,
+                              int64_t ldy, int T, const int32_t* ids, const int32_t* seg_off,
+                              const int32_t* perm, void* ws, size_t ws_bytes, void* stream, int phases);
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,7 @@ from ._lib import LoraError, lora_store  # noqa: F401
 __all__ = [
     "Store", "Segmentation", "LoraError", "lora_store_bytes", "lora_pack_retained",
     "lora_segment", "lora_workspace_bytes", "lora_shrink", "lora_expand", "lora_apply_batched",
-    "lora_apply_batched_timed", "load_library",
+    "lora_apply_batched_phases", "load_library",
 ]
 
 _DTYPES = {torch.bfloat16: L.LORA_DTYPE_BF16, torch.float32: L.LORA_DTYPE_F32}
@@ -227,26 +227,20 @@ def lora_apply_batched(store: Store, x: torch.Tensor, y: torch.Tensor, *,
     return y
 
 
-def lora_apply_batched_timed(store: Store, x: torch.Tensor, y: torch.Tensor, events, *,
-                             ids: Optional[torch.Tensor] = None, seg: Optional[Segmentation] = None,
-                             ws: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """lora_apply_batched that also records three torch.cuda.Event objects on
-    the launch stream: before the shrink, between shrink and expand, after."""
+def lora_apply_batched_phases(store: Store, x: torch.Tensor, y: torch.Tensor, phases: int, *,
+                              ids: Optional[torch.Tensor] = None, seg: Optional[Segmentation] = None,
+                              ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One kernel of lora_apply_batched at a time (phases 1 = shrink, 2 =
+    expand from the plan a phase-1 call left in ``ws``, 3 = both)."""
     T = x.shape[0]
     if (ids is None) == (seg is None):
         raise ValueError("pass exactly one of ids or seg")
-    if len(events) != 3:
-        raise ValueError("need three events")
-    for ev in events:  # make sure the HIP events exist
-        if ev.cuda_event == 0:
-            ev.record(torch.cuda.current_stream(x.device))
-    handles = (C.c_void_p * 3)(*[ev.cuda_event for ev in events])
     ws = _ws(store, T, ws, x.device)
     so = seg.seg_off.data_ptr() if seg is not None else None
     pm = _p(seg.perm) if seg is not None else None
     if ids is not None and (ids.dtype != torch.int32 or not ids.is_contiguous()):
         raise ValueError("ids must be a contiguous int32 vector")
-    L.check("lora_apply_batched_timed", L.lib().lora_apply_batched_timed(
+    L.check("lora_apply_batched_phases", L.lib().lora_apply_batched_phases(
         store.ref(), _p(x), _rows(x, "x"), _p(y), _rows(y, "y"), T, _p(ids) if ids is not None else None,
-        so, pm, ws.data_ptr(), ws.numel(), _stream(x), handles))
+        so, pm, ws.data_ptr(), ws.numel(), _stream(x), phases))
     return y

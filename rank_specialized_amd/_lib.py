@@ -47,8 +47,7 @@ SIGNATURES = {
     "lora_shrink": (I, [C.POINTER(lora_store), P, I64, I, P, P, P, I64, P, SZ, P]),
     "lora_expand": (I, [C.POINTER(lora_store), P, I64, I, P, P, P, I64, P, SZ, P]),
     "lora_apply_batched": (I, [C.POINTER(lora_store), P, I64, P, I64, I, P, P, P, P, SZ, P]),
-    "lora_apply_batched_timed": (I, [C.POINTER(lora_store), P, I64, P, I64, I, P, P, P, P, SZ, P,
-                                     C.POINTER(C.c_void_p)]),
+    "lora_apply_batched_phases": (I, [C.POINTER(lora_store), P, I64, P, I64, I, P, P, P, P, SZ, P, I]),
 }
 
 _lib = None

@@ -158,54 +158,49 @@ int lora_expand(const lora_store* store_host, const float* h, int64_t ldh, int T
 
 static int apply_impl(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy, int T,
                       const int32_t* ids, const int32_t* seg_off, const int32_t* perm, void* ws, size_t ws_bytes,
-                      void* stream, void* const* events) {
+                      void* stream, int phases) {
   int st = check_store(store_host);
   if (st != LORA_OK) return st;
   const lora_store& s = *store_host;
   if (T < 0) return LORA_ERR_INVALID_ARG;
+  if (phases < 1 || phases > 3) return LORA_ERR_INVALID_ARG;
   if ((st = check_rows(x, ldx, s.d_in, s.dtype, T)) != LORA_OK) return st;
   if ((st = check_rows(y, ldy, s.d_out, s.dtype, T)) != LORA_OK) return st;
   if ((st = check_ws(store_host, T, ws, ws_bytes)) != LORA_OK) return st;
   if (ids != nullptr && (T > LORA_SEGMENT_MAX_T || s.n > LORA_SEGMENT_MAX_N)) return LORA_ERR_UNSUPPORTED;
-  if (events != nullptr && (!events[0] || !events[1] || !events[2])) return LORA_ERR_INVALID_ARG;
   if (T == 0) return LORA_OK;  // nothing to group or apply
   if (ids == nullptr && (st = check_grouping(store_host, T, seg_off, perm)) != LORA_OK) return st;
   hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
-  auto mark = [&](int k) -> hipError_t {
-    return events ? hipEventRecord(reinterpret_cast<hipEvent_t>(events[k]), strm) : hipSuccess;
-  };
-  hipError_t e = mark(0);
-  if (e != hipSuccess) return hip_fail(e);
-  if (ids != nullptr && s.n > kGroupMaxN) {
-    // Too many adapters for the in-shrink histogram: sort first, into ws.
-    const WsLayout L = ws_layout(T, s.n, s.d_in, s.r_max, s.dtype);
-    int32_t* so = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + L.seg_off);
-    int32_t* pm = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + L.perm);
-    st = lora_segment(ids, T, s.n, so, pm, nullptr, stream);
-    if (st != LORA_OK) return st;
-    e = launch_shrink(s, nullptr, so, pm, T, x, ldx, ws, strm);
-  } else if (ids != nullptr) {
-    e = launch_shrink(s, ids, nullptr, nullptr, T, x, ldx, ws, strm);
-  } else {
-    e = launch_shrink(s, nullptr, seg_off, perm, T, x, ldx, ws, strm);
+  hipError_t e = hipSuccess;
+  if (phases & 1) {
+    if (ids != nullptr && s.n > kGroupMaxN) {
+      // Too many adapters for the in-shrink histogram: sort first, into ws.
+      const WsLayout L = ws_layout(T, s.n, s.d_in, s.r_max, s.dtype);
+      int32_t* so = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + L.seg_off);
+      int32_t* pm = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + L.perm);
+      st = lora_segment(ids, T, s.n, so, pm, nullptr, stream);
+      if (st != LORA_OK) return st;
+      e = launch_shrink(s, nullptr, so, pm, T, x, ldx, ws, strm);
+    } else if (ids != nullptr) {
+      e = launch_shrink(s, ids, nullptr, nullptr, T, x, ldx, ws, strm);
+    } else {
+      e = launch_shrink(s, nullptr, seg_off, perm, T, x, ldx, ws, strm);
+    }
   }
-  if (e == hipSuccess) e = mark(1);
-  if (e == hipSuccess) e = launch_expand(s, T, ws, nullptr, 0, y, ldy, strm);
-  if (e == hipSuccess) e = mark(2);
+  if (e == hipSuccess && (phases & 2)) e = launch_expand(s, T, ws, nullptr, 0, y, ldy, strm);
   return e == hipSuccess ? LORA_OK : hip_fail(e);
 }
 
 int lora_apply_batched(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy,
                        int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm, void* ws,
                        size_t ws_bytes, void* stream) {
-  return apply_impl(store_host, x, ldx, y, ldy, T, ids, seg_off, perm, ws, ws_bytes, stream, nullptr);
+  return apply_impl(store_host, x, ldx, y, ldy, T, ids, seg_off, perm, ws, ws_bytes, stream, 3);
 }
 
-int lora_apply_batched_timed(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy,
-                             int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm, void* ws,
-                             size_t ws_bytes, void* stream, void* const* events_host) {
-  if (events_host == nullptr) return LORA_ERR_INVALID_ARG;
-  return apply_impl(store_host, x, ldx, y, ldy, T, ids, seg_off, perm, ws, ws_bytes, stream, events_host);
+int lora_apply_batched_phases(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy,
+                              int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm, void* ws,
+                              size_t ws_bytes, void* stream, int phases) {
+  return apply_impl(store_host, x, ldx, y, ldy, T, ids, seg_off, perm, ws, ws_bytes, stream, phases);
 }
 
 }  // extern "C"

@@ -220,12 +220,11 @@ def test_workspace_bytes(lib, T, n, d_in, r_max, dtype):
     assert lib.lora_workspace_bytes(C.byref(st), -1) == 0
 
 
-def test_apply_timed_rejects_before_launch(lib):
+def test_apply_phases_rejects_before_launch(lib):
     st = _store()
-    f = lib.lora_apply_batched_timed
-    evs = (C.c_void_p * 3)(FAKE, FAKE, None)
-    good = (C.c_void_p * 3)(FAKE, FAKE, FAKE)
-    assert f(C.byref(st), FAKE, 64, FAKE, 32, 16, FAKE, None, None, FAKE, 1 << 30, None, None) == 1
-    assert f(C.byref(st), FAKE, 64, FAKE, 32, 16, FAKE, None, None, FAKE, 1 << 30, None, evs) == 1
-    assert f(None, FAKE, 64, FAKE, 32, 16, FAKE, None, None, FAKE, 1 << 30, None, good) == 1
-    assert f(C.byref(st), FAKE, 64, FAKE, 32, 0, FAKE, None, None, FAKE, 1 << 30, None, good) == 0
+    f = lib.lora_apply_batched_phases
+    args = (FAKE, 64, FAKE, 32, 16, FAKE, None, None, FAKE, 1 << 30, None)
+    for bad in (0, 4, -1):
+        assert f(C.byref(st), *args, bad) == 1
+    assert f(None, *args, 3) == 1
+    assert f(C.byref(st), FAKE, 64, FAKE, 32, 0, FAKE, None, None, FAKE, 1 << 30, None, 1) == 0

@@ -348,3 +348,20 @@ def test_ids_not_16_byte_aligned():
     torch.cuda.synchronize()
     assert np.array_equal(hbits(y1), hbits(y2))
     assert np.array_equal(y_host(y2), bf16_round_ref(_ref(wl)))
+
+
+def test_phases_compose_to_apply():
+    """The shrink-only and expand-only calls (the benchmark's per-kernel
+    timing) give the apply's y when run in order on one workspace."""
+    dev = device()
+    wl = make_config("3")
+    store = pack(wl, dev)
+    x, ids, y1 = inputs(wl, dev)
+    y2 = y1.clone()
+    ws = torch.empty(rs.lora_workspace_bytes(store, wl.T), dtype=torch.uint8, device=dev)
+    note("phases 1 then 2")
+    rs.lora_apply_batched(store, x, y1, ids=ids, ws=ws)
+    rs.lora_apply_batched_phases(store, x, y2, 1, ids=ids, ws=ws)
+    rs.lora_apply_batched_phases(store, x, y2, 2, ids=ids, ws=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(hbits(y1), hbits(y2))
