@@ -229,8 +229,10 @@ int lora_apply_batched(const lora_store* store_host, const void* x, int64_t ldx,
  * phases = 1 runs the shrink only (grouping, partial sums and plan into ws;
  * with ids and n > 4096 also the sort), 2 the expand only (from the plan and
  * partial sums a previous phase-1 call left in ws, for the same store, T and
- * grouping), 3 both (= lora_apply_batched).  Errors: as lora_apply_batched;
- * INVALID_ARG for phases outside 1..3.
+ * grouping; plan entries that do not fit this store are skipped, so a
+ * mismatched workspace gives wrong values, never an access outside the
+ * store's buffers), 3 both (= lora_apply_batched).  Errors: as
+ * lora_apply_batched; INVALID_ARG for phases outside 1..3.
  */
 int lora_apply_batched_phases(const lora_store* store_host, const void* x, int64_t ldx, void* y,
                               int64_t ldy, int T, const int32_t* ids, const int32_t* seg_off,

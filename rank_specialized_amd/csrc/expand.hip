@@ -34,6 +34,7 @@ namespace lora {
 struct ExpandArgs {
   const char* b_pack;
   int d_out, T, max_sub, fbn;
+  int n, r_max, R, S_max;  // the store's bounds: plan entries outside them are skipped
   const float* hsrc;      // partial sums (kPart) or h
   int64_t ldh, hstride;   // floats
   const char* plan;
@@ -159,10 +160,15 @@ __global__ void __launch_bounds__(kExpandWaves * 64) expand_kernel(ExpandArgs p)
   const int count = *reinterpret_cast<const int32_t*>(p.plan);
   if (st >= count) return;
   const TileEntry* ent = reinterpret_cast<const TileEntry*>(p.plan + kPlanHeaderBytes) + st;
-  const int m = ent->m, r = ent->r, pos0 = ent->pos0, ro = ent->row_off;
+  const int a = ent->a, m = ent->m, r = ent->r, pos0 = ent->pos0, ro = ent->row_off;
   const float sc = ent->scale;
   const int S = kPart ? ent->S : 1;
-  if (m <= 0 || r <= 0) return;
+  // An entry must describe this store (a plan left in the workspace by a
+  // call on another store is skipped): every B row and partial sum it names
+  // then lies inside the store's and the workspace's buffers.
+  if ((unsigned)a >= (unsigned)p.n || m <= 0 || m > kSubTile || r <= 0 || r > p.r_max || ro < 0 ||
+      ro > p.R - r || S <= 0 || S > p.S_max)
+    return;
   const int o = fb * kExpandCols + 8 * (threadIdx.x & 15);
   const int nq = (r + KSTEP - 1) / KSTEP;
   if (nq <= 1) {
@@ -189,6 +195,10 @@ hipError_t launch_expand(const lora_store& s, int T, const void* ws, const float
   a.max_sub = (int)max_sub;
   a.fbn = (s.d_out + kExpandCols - 1) / kExpandCols;
   a.plan = base + L.plan;
+  a.n = s.n;
+  a.r_max = s.r_max;
+  a.R = s.R;
+  a.S_max = shrink_split(s.d_in, s.r_max, s.dtype).S_max;
   a.y = reinterpret_cast<char*>(y);
   a.ldy_bytes = ldy * elem_bytes(s.dtype);
   const bool part = h == nullptr;

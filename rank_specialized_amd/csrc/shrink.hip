@@ -363,12 +363,14 @@ __global__ void __launch_bounds__(kShrinkThreads, 4) shrink_kernel(ShrinkArgs p)
 // them), for every sub-tile of the plan.
 __global__ void __launch_bounds__(256)
 reduce_partials_kernel(const char* __restrict__ plan, int max_sub, const float* __restrict__ part,
-                       int64_t ldp, int64_t pstride, int T, float* __restrict__ h, int64_t ldh) {
+                       int64_t ldp, int64_t pstride, int T, int r_max, int S_max, float* __restrict__ h,
+                       int64_t ldh) {
   const int st = blockIdx.x;
   const int count = min(*reinterpret_cast<const int32_t*>(plan), max_sub);
   if (st >= count) return;
   const TileEntry* e = reinterpret_cast<const TileEntry*>(plan + kPlanHeaderBytes) + st;
   const int m = e->m, r = e->r, pos0 = e->pos0, S = e->S;
+  if (m <= 0 || m > kSubTile || r <= 0 || r > r_max || S <= 0 || S > S_max) return;
   for (int idx = threadIdx.x; idx < m * r; idx += 256) {
     const int i = idx / r, j = idx - i * r;
     const int row = pos0 + i;
@@ -538,8 +540,8 @@ hipError_t launch_reduce_partials(const lora_store& s, int T, const void* ws, fl
   const char* base = reinterpret_cast<const char*>(ws);
   const int64_t ldp = partial_ld(s.r_max);
   hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)max_sub), dim3(256), 0, stream, base + L.plan,
-                     (int)max_sub, reinterpret_cast<const float*>(base + L.part), ldp, (int64_t)T * ldp, T, h,
-                     ldh);
+                     (int)max_sub, reinterpret_cast<const float*>(base + L.part), ldp, (int64_t)T * ldp, T,
+                     s.r_max, shrink_split(s.d_in, s.r_max, s.dtype).S_max, h, ldh);
   return hipGetLastError();
 }
 

@@ -365,3 +365,46 @@ def test_phases_compose_to_apply():
     rs.lora_apply_batched_phases(store, x, y2, 2, ids=ids, ws=ws)
     torch.cuda.synchronize()
     assert np.array_equal(hbits(y1), hbits(y2))
+
+
+def _two_stores(dev):
+    """Two stores with the same shapes and ids but different rank totals."""
+    big = make_random_workload(80, 300, 8, 256, 192, [64, 60, 33, 17, 64, 5, 48, 41], dtype="bf16")
+    small = make_random_workload(80, 300, 8, 256, 192, [3, 1, 5, 2, 7, 4, 1, 6], dtype="bf16")
+    return big, pack(big, dev), small, pack(small, dev)
+
+
+def test_expand_skips_plan_of_another_store():
+    """The expand-only call on a workspace whose plan was made for another
+    store (larger row offsets and ranks): entries that do not fit the store
+    are skipped, nothing outside its buffers is read, and the call succeeds."""
+    dev = device()
+    big, sb, small, ss = _two_stores(dev)
+    x, ids, y = inputs(big, dev)
+    ws = torch.empty(max(rs.lora_workspace_bytes(sb, big.T), rs.lora_workspace_bytes(ss, big.T)),
+                     dtype=torch.uint8, device=dev)
+    note("plan of the large store, expand on the small one")
+    rs.lora_apply_batched_phases(sb, x, y, 1, ids=ids, ws=ws)
+    rs.lora_apply_batched_phases(ss, x, y, 2, ids=ids, ws=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y.float()).all()
+
+
+@pytest.mark.parametrize("fill", ["ones", "random"])
+def test_expand_on_garbage_workspace(fill):
+    """An expand-only call on a workspace of arbitrary bytes never reads
+    outside the store's buffers (every plan entry is checked against the
+    store before use) and leaves y finite."""
+    dev = device()
+    big, sb, _, _ = _two_stores(dev)
+    x, ids, y = inputs(big, dev)
+    ws = torch.empty(rs.lora_workspace_bytes(sb, big.T), dtype=torch.uint8, device=dev)
+    if fill == "ones":
+        ws.fill_(0xFF)
+    else:
+        ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, generator=torch.Generator().manual_seed(5)))
+        ws[:4].copy_(torch.tensor([200, 0, 0, 0], dtype=torch.uint8))  # a plausible sub-tile count
+    note(f"expand on a workspace of {fill}")
+    rs.lora_apply_batched_phases(sb, x, y, 2, ids=ids, ws=ws)
+    torch.cuda.synchronize()
+    assert y.shape == (big.T, 192)
