@@ -25,6 +25,18 @@
 // Rank specialization: the number of 32-deep (bf16) or 16-deep (f32) K
 // chunks is a template parameter; a tile of rank r_a issues exactly the loads
 // and MFMAs of ceil(r_a / 32) chunks.
+//
+// Decode sub-tiles (at most 8 tokens, rank at most 16 in bf16 or 8 in
+// float32) take the vector path
+// instead: one wave per (sub-tile, 512 output features, 4 tokens).  Lane l
+// owns features o .. o + 7 (o = 512 fb + 8 l); in the [d_out, r] layout their
+// B values are 16 r contiguous bytes, read as r fully used 16-byte loads.
+// h[t, j] is held by lane t r + j and broadcast with a lane read; each output
+// is y + s * sum_j h[t, j] B[o + f, j] in float32 (h exact, no bf16 split).
+// The path is instantiated per exact rank 1..16, so the unpacking of the B
+// block is static.  Both paths live in one kernel: a sub-tile owns `slots`
+// consecutive waves and its entry decides which path they take (waves a path
+// does not need return at once), so the plan is read in one launch.
 #include "device_common.h"
 #include "kernels.h"
 #include "tile_ops.h"
@@ -33,7 +45,10 @@ namespace lora {
 
 struct ExpandArgs {
   const char* b_pack;
-  int d_out, T, max_sub, fbn;
+  int d_out, T, max_sub;
+  int slots;  // waves per sub-tile: max(fbn, (kVecMaxTokens / kVecTokens) fbv)
+  int fbn;    // kExpandCols-feature blocks (matrix path)
+  int fbv;    // kVecCols-feature blocks (vector path)
   int n, r_max, R, S_max;  // the store's bounds: plan entries outside them are skipped
   const float* hsrc;      // partial sums (kPart) or h
   int64_t ldh, hstride;   // floats
@@ -151,25 +166,142 @@ __device__ __forceinline__ void expand_item(const ExpandArgs& p, const TileEntry
   }
 }
 
+// Plan entry st checked against the store (an entry left in the workspace by
+// a call on another store is skipped): every B row and partial sum it names
+// then lies inside the store's and the workspace's buffers.
+__device__ __forceinline__ bool entry_fits(const ExpandArgs& p, const TileEntry* ent, int S) {
+  const int a = ent->a, m = ent->m, r = ent->r, ro = ent->row_off;
+  return (unsigned)a < (unsigned)p.n && m > 0 && m <= kSubTile && r > 0 && r <= p.r_max && ro >= 0 &&
+         ro <= p.R - r && S > 0 && S <= p.S_max;
+}
+
+// ------------------------------------------------------------ vector path
+// float32 B blocks are twice as large: that path stops at rank kVecMaxRank / 2.
+template <typename E>
+__device__ __forceinline__ bool vector_expand(int r, int m) {
+  return r <= kVecMaxRank * 2 / E::kBytes && m <= kVecMaxTokens;
+}
+
+template <typename E, bool kPart, int R>
+__device__ __forceinline__ void expand_vec_item(const ExpandArgs& p, const TileEntry* ent, int m, int t0,
+                                                int pos0, int ro, float sc, int S, int o) {
+  constexpr int V = E::kVec;
+  constexpr int YV = 8 / V;                   // 16-byte vectors per 8 features
+  constexpr int BV = 8 * R * E::kBytes / 16;  // 16-byte vectors of the lane's 8 x R block of B
+  const int lane = threadIdx.x & 63;
+  const int mt = min(kVecTokens, m - t0);
+  const int nf = min(8, p.d_out - o);  // 8; 4 for a float32 row of 4 (mod 8) features; <= 0 past the row
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+  // y rows of tokens t0 .. t0 + 3 and the B block, issued first.
+  char* yp[kVecTokens];
+  uint4 yv[kVecTokens][YV];
+#pragma unroll
+  for (int t = 0; t < kVecTokens; ++t) {
+    const int tok = t < mt ? ent->tok[t0 + t] : -1;
+    yp[t] = ((unsigned)tok < (unsigned)p.T && nf > 0) ? p.y + (int64_t)tok * p.ldy_bytes + (size_t)o * E::kBytes
+                                                      : nullptr;
+#pragma unroll
+    for (int v = 0; v < YV; ++v) yv[t][v] = (yp[t] && v * V < nf) ? ld16(yp[t] + 16 * v) : zero;
+  }
+  const char* bb = p.b_pack + ((size_t)ro * p.d_out + (size_t)o * R) * E::kBytes;
+  uint4 bv[BV];
+#pragma unroll
+  for (int i = 0; i < BV; ++i) bv[i] = (16 * i < nf * R * E::kBytes) ? ld16(bb + 16 * i) : zero;
+  // h[t, j] in lane t R + j (t < 4): the S partial sums in chunk order, or h.
+  float hv = 0.f;
+  {
+    const int t = lane / R, j = lane - t * R;
+    if (t < mt) {
+      const int row = pos0 + t0 + t;
+      if (row >= 0 && row < p.T) {
+        const float* src = p.hsrc + (int64_t)row * p.ldh + j;
+        hv = src[0];
+        if (kPart)
+          for (int k = 1; k < S; ++k) hv += src[(int64_t)k * p.hstride];
+      }
+    }
+  }
+  float acc[kVecTokens][8];
+#pragma unroll
+  for (int t = 0; t < kVecTokens; ++t)
+#pragma unroll
+    for (int f = 0; f < 8; ++f) acc[t][f] = 0.f;
+  const uint32_t* bw = reinterpret_cast<const uint32_t*>(bv);
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    float bj[8];  // B[o + f, j]: element f R + j of the lane's block
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      const int e = f * R + j;
+      if constexpr (E::kBytes == 2)
+        bj[f] = (e & 1) ? bf16_hi(bw[e >> 1]) : bf16_lo(bw[e >> 1]);
+      else
+        bj[f] = __uint_as_float(bw[e]);
+    }
+#pragma unroll
+    for (int t = 0; t < kVecTokens; ++t) {
+      const float h = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hv), t * R + j));
+#pragma unroll
+      for (int f = 0; f < 8; ++f) acc[t][f] += h * bj[f];
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kVecTokens; ++t) {
+    if (yp[t] == nullptr) continue;
+#pragma unroll
+    for (int v = 0; v < YV; ++v) {
+      if (v * V >= nf) continue;
+      float f[V];
+      E::widen(yv[t][v], f);
+#pragma unroll
+      for (int k = 0; k < V; ++k) f[k] = f[k] + sc * acc[t][v * V + k];
+      st16(yp[t] + 16 * v, E::narrow(f));
+    }
+  }
+}
+
+// ------------------------------------------------------------ the kernel
 template <typename E, bool kPart>
-__global__ void __launch_bounds__(kExpandWaves * 64) expand_kernel(ExpandArgs p) {
+__global__ void __launch_bounds__(kExpandWaves * 64) __attribute__((amdgpu_waves_per_eu(E::kBytes == 2 ? 3 : 1)))
+expand_kernel(ExpandArgs p) {
   constexpr int KSTEP = 4 * E::kVec;
+  constexpr int kGroups = kVecMaxTokens / kVecTokens;
   const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * kExpandWaves + (threadIdx.x >> 6));
-  const int st = item / p.fbn, fb = item - st * p.fbn;
+  const int st = item / p.slots, slot = item - st * p.slots;
   if (st >= p.max_sub) return;
   const int count = *reinterpret_cast<const int32_t*>(p.plan);
   if (st >= count) return;
   const TileEntry* ent = reinterpret_cast<const TileEntry*>(p.plan + kPlanHeaderBytes) + st;
-  const int a = ent->a, m = ent->m, r = ent->r, pos0 = ent->pos0, ro = ent->row_off;
-  const float sc = ent->scale;
   const int S = kPart ? ent->S : 1;
-  // An entry must describe this store (a plan left in the workspace by a
-  // call on another store is skipped): every B row and partial sum it names
-  // then lies inside the store's and the workspace's buffers.
-  if ((unsigned)a >= (unsigned)p.n || m <= 0 || m > kSubTile || r <= 0 || r > p.r_max || ro < 0 ||
-      ro > p.R - r || S <= 0 || S > p.S_max)
+  if (!entry_fits(p, ent, S)) return;
+  const int m = ent->m, r = ent->r, pos0 = ent->pos0, ro = ent->row_off;
+  const float sc = ent->scale;
+  if (vector_expand<E>(r, m)) {
+    const int fb = slot / kGroups, tg = slot - fb * kGroups;
+    if (fb >= p.fbv || tg * kVecTokens >= m) return;
+    // Every lane stays: lanes past d_out load and store nothing but may hold h.
+    const int o = fb * kVecCols + 8 * (threadIdx.x & 63);
+    const int t0 = tg * kVecTokens;
+    switch (r) {
+#define LORA_VEC_CASE(RR) \
+  case RR: expand_vec_item<E, kPart, RR>(p, ent, m, t0, pos0, ro, sc, S, o); break;
+      LORA_VEC_CASE(1) LORA_VEC_CASE(2) LORA_VEC_CASE(3) LORA_VEC_CASE(4)
+      LORA_VEC_CASE(5) LORA_VEC_CASE(6) LORA_VEC_CASE(7) LORA_VEC_CASE(8)
+      default:
+        if constexpr (E::kBytes == 2) {
+          switch (r) {
+            LORA_VEC_CASE(9) LORA_VEC_CASE(10) LORA_VEC_CASE(11) LORA_VEC_CASE(12)
+            LORA_VEC_CASE(13) LORA_VEC_CASE(14) LORA_VEC_CASE(15) LORA_VEC_CASE(16)
+            default: break;
+          }
+        }
+        break;
+#undef LORA_VEC_CASE
+    }
     return;
-  const int o = fb * kExpandCols + 8 * (threadIdx.x & 15);
+  }
+  if (slot >= p.fbn) return;
+  const int o = slot * kExpandCols + 8 * (threadIdx.x & 15);
   const int nq = (r + KSTEP - 1) / KSTEP;
   if (nq <= 1) {
     expand_item<E, kPart, 1>(p, ent, m, r, pos0, ro, sc, S, o);
@@ -211,9 +343,12 @@ hipError_t launch_expand(const lora_store& s, int T, const void* ws, const float
     a.ldh = ldh;
     a.hstride = 0;
   }
-  const int64_t items = max_sub * a.fbn;
-  const dim3 grid((unsigned)((items + kExpandWaves - 1) / kExpandWaves));
+  a.fbv = (s.d_out + kVecCols - 1) / kVecCols;
+  const int vec_waves = (kVecMaxTokens / kVecTokens) * a.fbv;
+  a.slots = a.fbn > vec_waves ? a.fbn : vec_waves;
+  const int64_t items = max_sub * a.slots;
   const dim3 block(kExpandWaves * 64);
+  const dim3 grid((unsigned)((items + kExpandWaves - 1) / kExpandWaves));
   if (s.dtype == LORA_DTYPE_BF16) {
     if (part) hipLaunchKernelGGL((expand_kernel<BF16, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((expand_kernel<BF16, false>), grid, block, 0, stream, a);

@@ -26,6 +26,14 @@ constexpr int kGroupMaxN = 4096;
 // The expand's wave covers kExpandCols output features of one sub-tile.
 constexpr int kExpandCols = 128;
 constexpr int kExpandWaves = 4;  // waves per expand workgroup
+// Sub-tiles of at most kVecMaxTokens tokens and rank at most kVecMaxRank
+// (bf16; half that for float32) take the vector path of the expand: one wave
+// per (sub-tile, kVecCols output features, group of kVecTokens tokens); the
+// others its matrix-core path.
+constexpr int kVecMaxRank = 16;
+constexpr int kVecMaxTokens = 8;
+constexpr int kVecTokens = 4;
+constexpr int kVecCols = 512;
 
 // Upper bound on the number of runs of at most `len` tokens that T tokens
 // over n adapters cut into: each non-empty group of c tokens gives
