@@ -59,6 +59,18 @@ struct F32 {
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+// Streaming (nontemporal) forms, for data touched exactly once (the y rows of
+// the expand, the x rows of the shrink): they do not displace the factor rows
+// and partial sums that other waves read again from L2.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld16_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st16_stream(void* p, const uint4& v) {
+  u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+}
 
 // ----------------------------------------------------------- buffer loads
 // A buffer resource (base address and size in bytes) lets a load carry a

@@ -26,15 +26,15 @@
 // chunks is a template parameter; a tile of rank r_a issues exactly the loads
 // and MFMAs of ceil(r_a / 32) chunks.
 //
-// Decode sub-tiles (at most 8 tokens, rank at most 16 in bf16 or 8 in
+// Decode sub-tiles (at most 8 tokens, rank at most 8 in bf16 or 4 in
 // float32) take the vector path
 // instead: one wave per (sub-tile, 512 output features, 4 tokens).  Lane l
 // owns features o .. o + 7 (o = 512 fb + 8 l); in the [d_out, r] layout their
 // B values are 16 r contiguous bytes, read as r fully used 16-byte loads.
 // h[t, j] is held by lane t r + j and broadcast with a lane read; each output
 // is y + s * sum_j h[t, j] B[o + f, j] in float32 (h exact, no bf16 split).
-// The path is instantiated per exact rank 1..16, so the unpacking of the B
-// block is static.  Both paths live in one kernel: a sub-tile owns `slots`
+// The path is instantiated per exact rank, so the unpacking of the B block
+// is static.  Both paths live in one kernel: a sub-tile owns `slots`
 // consecutive waves and its entry decides which path they take (waves a path
 // does not need return at once), so the plan is read in one launch.
 #include "device_common.h"
@@ -77,7 +77,7 @@ __device__ __forceinline__ void expand_item(const ExpandArgs& p, const TileEntry
                 ? p.y + (int64_t)tok * p.ldy_bytes + (size_t)o * E::kBytes
                 : nullptr;
 #pragma unroll
-    for (int v = 0; v < YV; ++v) yv[e][v] = (yp[e] && o + v * V < p.d_out) ? ld16(yp[e] + 16 * v) : zero;
+    for (int v = 0; v < YV; ++v) yv[e][v] = (yp[e] && o + v * V < p.d_out) ? ld16_stream(yp[e] + 16 * v) : zero;
   }
   // B rows o .. o + 7 (one per N block), ranks of this lane's K chunks.
   // bf16 rows of an odd rank start on 2-byte boundaries, and a 16-byte
@@ -161,7 +161,7 @@ __device__ __forceinline__ void expand_item(const ExpandArgs& p, const TileEntry
       E::widen(yv[e][v], f);
 #pragma unroll
       for (int k = 0; k < V; ++k) f[k] = f[k] + sc * acc[v * V + k][e];
-      st16(yp[e] + 16 * v, E::narrow(f));
+      st16_stream(yp[e] + 16 * v, E::narrow(f));
     }
   }
 }
@@ -201,7 +201,7 @@ __device__ __forceinline__ void expand_vec_item(const ExpandArgs& p, const TileE
     yp[t] = ((unsigned)tok < (unsigned)p.T && nf > 0) ? p.y + (int64_t)tok * p.ldy_bytes + (size_t)o * E::kBytes
                                                       : nullptr;
 #pragma unroll
-    for (int v = 0; v < YV; ++v) yv[t][v] = (yp[t] && v * V < nf) ? ld16(yp[t] + 16 * v) : zero;
+    for (int v = 0; v < YV; ++v) yv[t][v] = (yp[t] && v * V < nf) ? ld16_stream(yp[t] + 16 * v) : zero;
   }
   const char* bb = p.b_pack + ((size_t)ro * p.d_out + (size_t)o * R) * E::kBytes;
   uint4 bv[BV];
@@ -255,15 +255,14 @@ __device__ __forceinline__ void expand_vec_item(const ExpandArgs& p, const TileE
       E::widen(yv[t][v], f);
 #pragma unroll
       for (int k = 0; k < V; ++k) f[k] = f[k] + sc * acc[t][v * V + k];
-      st16(yp[t] + 16 * v, E::narrow(f));
+      st16_stream(yp[t] + 16 * v, E::narrow(f));
     }
   }
 }
 
 // ------------------------------------------------------------ the kernel
 template <typename E, bool kPart>
-__global__ void __launch_bounds__(kExpandWaves * 64) __attribute__((amdgpu_waves_per_eu(E::kBytes == 2 ? 3 : 1)))
-expand_kernel(ExpandArgs p) {
+__device__ __forceinline__ void expand_wave(const ExpandArgs& p) {
   constexpr int KSTEP = 4 * E::kVec;
   constexpr int kGroups = kVecMaxTokens / kVecTokens;
   const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * kExpandWaves + (threadIdx.x >> 6));
@@ -288,7 +287,7 @@ expand_kernel(ExpandArgs p) {
       LORA_VEC_CASE(1) LORA_VEC_CASE(2) LORA_VEC_CASE(3) LORA_VEC_CASE(4)
       LORA_VEC_CASE(5) LORA_VEC_CASE(6) LORA_VEC_CASE(7) LORA_VEC_CASE(8)
       default:
-        if constexpr (E::kBytes == 2) {
+        if constexpr (kVecMaxRank * 2 / E::kBytes > 8) {
           switch (r) {
             LORA_VEC_CASE(9) LORA_VEC_CASE(10) LORA_VEC_CASE(11) LORA_VEC_CASE(12)
             LORA_VEC_CASE(13) LORA_VEC_CASE(14) LORA_VEC_CASE(15) LORA_VEC_CASE(16)
@@ -312,6 +311,15 @@ expand_kernel(ExpandArgs p) {
     else if (nq == 3) expand_item<E, kPart, 3>(p, ent, m, r, pos0, ro, sc, S, o);
     else expand_item<E, kPart, 4>(p, ent, m, r, pos0, ro, sc, S, o);
   }
+}
+
+// bf16 runs 4 waves per SIMD (more y rows in flight; the matrix path of
+// ranks above 32 then keeps a few values in scratch); float32, a small-shape
+// type here, is left to the compiler.
+template <typename E, bool kPart>
+__global__ void __launch_bounds__(kExpandWaves * 64) __attribute__((amdgpu_waves_per_eu(E::kBytes == 2 ? 4 : 1)))
+expand_kernel(ExpandArgs p) {
+  expand_wave<E, kPart>(p);
 }
 
 hipError_t launch_expand(const lora_store& s, int T, const void* ws, const float* h, int64_t ldh, void* y,

@@ -30,7 +30,7 @@ constexpr int kExpandWaves = 4;  // waves per expand workgroup
 // (bf16; half that for float32) take the vector path of the expand: one wave
 // per (sub-tile, kVecCols output features, group of kVecTokens tokens); the
 // others its matrix-core path.
-constexpr int kVecMaxRank = 16;
+constexpr int kVecMaxRank = 8;
 constexpr int kVecMaxTokens = 8;
 constexpr int kVecTokens = 4;
 constexpr int kVecCols = 512;
