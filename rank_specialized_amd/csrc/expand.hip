@@ -7,7 +7,8 @@
 //
 // Work item = one wave: (sub-tile, 128 output features).  Waves are
 // independent (no barriers); every wave issues its y rows and its B rows
-// before any arithmetic, so an item costs one memory round trip.
+// before any arithmetic, so an item costs one memory round trip (two for
+// bf16 ranks above 32, whose second K chunk of B is read after the first).
 //   D[token, feature] = H[token, j] . B_a^T[j, feature]
 // on 16x16 MFMA tiles (bf16: 16x16x32, f32: 16x16x4), eight N blocks per
 // wave.  Column c of N block b is feature o0 + 8 c + b, so lane (c, g) ends
@@ -87,9 +88,7 @@ __device__ __forceinline__ void expand_item(const ExpandArgs& p, const TileEntry
   const uint32_t row_bytes = (uint32_t)r * E::kBytes;
   const rsrc_t br = make_rsrc(p.b_pack + (size_t)ro * p.d_out * E::kBytes, (uint32_t)p.d_out * row_bytes);
   const bool odd_rows = E::kBytes == 2 && (r & 1);
-  uint4 bq[NQ][8];
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
+  auto load_b = [&](int q, uint4(&bb)[8]) {
     const int j0 = q * KSTEP + g * V;
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
@@ -99,13 +98,21 @@ __device__ __forceinline__ void expand_item(const ExpandArgs& p, const TileEntry
         const uint32_t lo = ok ? off - 2 : kOutOfRange;
         const uint4 d = buf_ld16(br, lo, 0);
         const uint32_t t = buf_ld4(br, ok ? lo + 16 : kOutOfRange);
-        bq[q][b] = make_uint4(__builtin_amdgcn_alignbit(d.y, d.x, 16), __builtin_amdgcn_alignbit(d.z, d.y, 16),
-                              __builtin_amdgcn_alignbit(d.w, d.z, 16), __builtin_amdgcn_alignbit(t, d.w, 16));
+        bb[b] = make_uint4(__builtin_amdgcn_alignbit(d.y, d.x, 16), __builtin_amdgcn_alignbit(d.z, d.y, 16),
+                           __builtin_amdgcn_alignbit(d.w, d.z, 16), __builtin_amdgcn_alignbit(t, d.w, 16));
       } else {
-        bq[q][b] = buf_ld16(br, ok ? off : kOutOfRange, 0);
+        bb[b] = buf_ld16(br, ok ? off : kOutOfRange, 0);
       }
     }
-  }
+  };
+  // bf16 ranks above 32 take two K chunks.  The second chunk's B rows are
+  // loaded after the first chunk's products, into the same registers: the
+  // kernel then fits the registers of 4 waves per SIMD, for one more (mostly
+  // L2) round trip on those sub-tiles only.
+  constexpr int NB = (E::kBytes == 2 && NQ > 1) ? 1 : NQ;  // chunks loaded up front
+  uint4 bq[NB][8];
+#pragma unroll
+  for (int q = 0; q < NB; ++q) load_b(q, bq[q]);
   // H chunks: token c of the sub-tile, ranks j0 .. j0 + V.
   HChunk<E> hc[NQ];
   const int hrow = pos0 + c;
@@ -124,6 +131,7 @@ __device__ __forceinline__ void expand_item(const ExpandArgs& p, const TileEntry
           const f32x4_t x = *reinterpret_cast<const f32x4_t*>(src + 4 * v);
           f[4 * v] = x[0]; f[4 * v + 1] = x[1]; f[4 * v + 2] = x[2]; f[4 * v + 3] = x[3];
         }
+#pragma unroll 4
         for (int k = 1; k < S; ++k) {
 #pragma unroll
           for (int v = 0; v < V / 4; ++v) {
@@ -146,9 +154,13 @@ __device__ __forceinline__ void expand_item(const ExpandArgs& p, const TileEntry
   for (int b = 0; b < 8; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
+    if (q >= NB) {
+      __builtin_amdgcn_sched_barrier(0);  // not above the previous chunk's products
+      load_b(q, bq[NB - 1]);
+    }
     const int nvalid = r - (q * KSTEP + g * V);
 #pragma unroll
-    for (int b = 0; b < 8; ++b) acc[b] = hc[q].mma(keep_first<E>(bq[q][b], nvalid), acc[b]);
+    for (int b = 0; b < 8; ++b) acc[b] = hc[q].mma(keep_first<E>(bq[q < NB ? q : NB - 1][b], nvalid), acc[b]);
   }
   // acc[b][e] = feature o + b of token 4g + e.
 #pragma unroll
@@ -216,8 +228,15 @@ __device__ __forceinline__ void expand_vec_item(const ExpandArgs& p, const TileE
       if (row >= 0 && row < p.T) {
         const float* src = p.hsrc + (int64_t)row * p.ldh + j;
         hv = src[0];
-        if (kPart)
-          for (int k = 1; k < S; ++k) hv += src[(int64_t)k * p.hstride];
+        if (kPart) {
+          // All S loads issued together (S <= kMaxChunks), summed in chunk order.
+          float pk[kMaxChunks - 1];
+#pragma unroll
+          for (int k = 1; k < kMaxChunks; ++k) pk[k - 1] = k < S ? src[(int64_t)k * p.hstride] : 0.f;
+#pragma unroll
+          for (int k = 1; k < kMaxChunks; ++k)
+            if (k < S) hv += pk[k - 1];
+        }
       }
     }
   }
@@ -313,9 +332,8 @@ __device__ __forceinline__ void expand_wave(const ExpandArgs& p) {
   }
 }
 
-// bf16 runs 4 waves per SIMD (more y rows in flight; the matrix path of
-// ranks above 32 then keeps a few values in scratch); float32, a small-shape
-// type here, is left to the compiler.
+// bf16 runs 4 waves per SIMD (more y rows in flight); float32, a
+// small-shape type here, is left to the compiler.
 template <typename E, bool kPart>
 __global__ void __launch_bounds__(kExpandWaves * 64) __attribute__((amdgpu_waves_per_eu(E::kBytes == 2 ? 4 : 1)))
 expand_kernel(ExpandArgs p) {

@@ -70,12 +70,13 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline int elem_bytes(int dtype) { return dtype == LORA_DTYPE_BF16 ? 2 : 4; }
 inline int vec_elems(int dtype) { return dtype == LORA_DTYPE_BF16 ? 8 : 4; }  // 16-byte vectors
 
-// The shrink splits d_in into S chunks; each of the 8 waves of an item
+// The shrink splits d_in into S <= kMaxChunks chunks; each of the 8 waves of an item
 // takes `spw` consecutive K steps (a step is 4 x 16 bytes of K: 32 bf16 or
 // 16 f32 values), issued as one batch of loads.  The batch depends on the
 // adapter's number of 16-rank row groups (ng): 8, 5, 4, 3 steps for ng =
 // 1..4, about 60 registers of loads either way.  S is at most 8; very wide
 // inputs give more steps per wave (several batches).  Indexed by ng (1..4).
+constexpr int kMaxChunks = 8;
 struct ShrinkSplit {
   int spw[5];     // K steps per wave
   int S[5];       // K chunks (partial sums per output)
@@ -93,8 +94,8 @@ inline ShrinkSplit shrink_split(int d_in, int r_max, int dtype) {
   for (int ng = 1; ng <= 4; ++ng) {
     int spw = shrink_batch_steps(ng);
     int S = (steps + kShrinkWaves * spw - 1) / (kShrinkWaves * spw);
-    if (S > 8) {
-      spw = (steps + kShrinkWaves * 8 - 1) / (kShrinkWaves * 8);
+    if (S > kMaxChunks) {
+      spw = (steps + kShrinkWaves * kMaxChunks - 1) / (kShrinkWaves * kMaxChunks);
       S = (steps + kShrinkWaves * spw - 1) / (kShrinkWaves * spw);
     }
     sp.spw[ng] = spw;

@@ -376,8 +376,13 @@ reduce_partials_kernel(const char* __restrict__ plan, int max_sub, const float* 
     const int row = pos0 + i;
     if (row < 0 || row >= T) continue;
     const float* src = part + (int64_t)row * ldp + j;
-    float s = src[0];
-    for (int k = 1; k < S; ++k) s += src[(int64_t)k * pstride];
+    float pk[kMaxChunks];  // S <= kMaxChunks: all loads issued together, summed in chunk order
+#pragma unroll
+    for (int k = 0; k < kMaxChunks; ++k) pk[k] = k < S ? src[(int64_t)k * pstride] : 0.f;
+    float s = pk[0];
+#pragma unroll
+    for (int k = 1; k < kMaxChunks; ++k)
+      if (k < S) s += pk[k];
     h[(int64_t)row * ldh + j] = s;
   }
 }

@@ -245,6 +245,10 @@ EDGE = {
                         invalid_frac=1.0),
     "distinct": dict(seed=66, T=100, n=200, d_in=256, d_out=128, ranks=list(range(1, 65)) * 3 + [8] * 8,
                      id_mode="distinct"),
+    # d_in = 18944 splits K into the most chunks (8 partial sums per h value).
+    "wide_in_decode": dict(seed=67, T=48, n=12, d_in=18944, d_out=520, ranks=[6, 3, 8, 1, 5, 2, 7, 4, 16, 40, 6, 3],
+                           id_mode="uniform"),
+    "wide_in_tiles": dict(seed=68, T=70, n=3, d_in=18944, d_out=136, ranks=[6, 24, 64], id_mode="sorted"),
 }
 
 
