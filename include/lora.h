@@ -212,12 +212,19 @@ int lora_expand(const lora_store* store_host, const float* h, int64_t ldh, int T
 
 /*
  * The batched apply:  y[t] += s_a * B_a (A_a x[t])  for every token.
- * Either ids (the grouping is then formed inside the shrink), or ids = NULL
+ * Either ids (the grouping is then formed inside the kernel), or ids = NULL
  * and seg_off / perm from lora_segment (one grouping reused across many
- * stores, e.g. every projection of a decode step).  Two kernels: the shrink
- * (grouping + float32 partial sums over chunks of d_in, in the workspace)
- * and the expand (partials summed in chunk order, then y updated).  The
- * result equals lora_segment + lora_shrink + lora_expand bit for bit.
+ * stores, e.g. every projection of a decode step).
+ * Decode-sized calls with ids (lora_apply_launches returns 1) run as one
+ * kernel, a workgroup per (token, slice of the output features): it reads
+ * the token's adapter from ids, reduces h over all of d_in (float32, a fixed
+ * order) and adds the delta into that slice of the token's y row (the
+ * per-token indexed form of the same two steps: section 13.4 of the Compress
+ * then Serve page).  Other calls run as two kernels: the shrink (grouping +
+ * float32 partial sums over chunks of d_in, in the workspace) and the expand
+ * (partials summed in chunk order, then y updated); their result equals
+ * lora_segment + lora_shrink + lora_expand bit for bit.  The two forms sum h
+ * in different orders, so on float data they agree to float32 rounding.
  * Errors: union of those calls'.
  */
 int lora_apply_batched(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy,
@@ -231,12 +238,26 @@ int lora_apply_batched(const lora_store* store_host, const void* x, int64_t ldx,
  * partial sums a previous phase-1 call left in ws, for the same store, T and
  * grouping; plan entries that do not fit this store are skipped, so a
  * mismatched workspace gives wrong values, never an access outside the
- * store's buffers), 3 both (= lora_apply_batched).  Errors: as
- * lora_apply_batched; INVALID_ARG for phases outside 1..3.
+ * store's buffers), 3 = lora_apply_batched (the one-kernel form for
+ * decode-sized calls with ids).  Phases 1 and 2 always run the two-kernel
+ * form.
+ * Errors: as lora_apply_batched; INVALID_ARG for phases outside 1..3.
  */
 int lora_apply_batched_phases(const lora_store* store_host, const void* x, int64_t ldx, void* y,
                               int64_t ldy, int T, const int32_t* ids, const int32_t* seg_off,
                               const int32_t* perm, void* ws, size_t ws_bytes, void* stream, int phases);
+
+/*
+ * Kernel launches lora_apply_batched enqueues for this store, T and kind of
+ * grouping (host only, nothing enqueued): 1 for the one-kernel decode form
+ * (ids given, T <= 512, r_max <= 8 for bf16 or <= 4 for f32, d_in <= 4096
+ * for bf16 or <= 2048 for f32), 2 for the shrink and the expand, 3 when the
+ * sort precedes them (ids given and n > 4096), 0 for T = 0.  with_ids:
+ * nonzero if ids are passed, 0 for a prior grouping.  A negative value is
+ * -(the status the apply would return): an invalid store or T, or
+ * UNSUPPORTED sizes.
+ */
+int lora_apply_launches(const lora_store* store_host, int T, int with_ids);
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,7 @@ from ._lib import LoraError, lora_store  # noqa: F401
 __all__ = [
     "Store", "Segmentation", "LoraError", "lora_store_bytes", "lora_pack_retained",
     "lora_segment", "lora_workspace_bytes", "lora_shrink", "lora_expand", "lora_apply_batched",
-    "lora_apply_batched_phases", "load_library",
+    "lora_apply_batched_phases", "lora_apply_launches", "load_library",
 ]
 
 _DTYPES = {torch.bfloat16: L.LORA_DTYPE_BF16, torch.float32: L.LORA_DTYPE_F32}
@@ -231,7 +231,8 @@ def lora_apply_batched_phases(store: Store, x: torch.Tensor, y: torch.Tensor, ph
                               ids: Optional[torch.Tensor] = None, seg: Optional[Segmentation] = None,
                               ws: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One kernel of lora_apply_batched at a time (phases 1 = shrink, 2 =
-    expand from the plan a phase-1 call left in ``ws``, 3 = both)."""
+    expand from the plan a phase-1 call left in ``ws``, 3 = the apply, a
+    single fused kernel for decode-sized calls)."""
     T = x.shape[0]
     if (ids is None) == (seg is None):
         raise ValueError("pass exactly one of ids or seg")
@@ -244,3 +245,12 @@ def lora_apply_batched_phases(store: Store, x: torch.Tensor, y: torch.Tensor, ph
         store.ref(), _p(x), _rows(x, "x"), _p(y), _rows(y, "y"), T, _p(ids) if ids is not None else None,
         so, pm, ws.data_ptr(), ws.numel(), _stream(x), phases))
     return y
+
+
+def lora_apply_launches(store: Store, T: int, with_ids: bool = True) -> int:
+    """Kernel launches lora_apply_batched makes for this store and T: 1 (the
+    fused decode kernel), 2 (shrink, expand) or 3 (sort, shrink, expand)."""
+    v = L.lib().lora_apply_launches(store.ref(), int(T), 1 if with_ids else 0)
+    if v < 0:
+        L.check("lora_apply_launches", -v)
+    return v

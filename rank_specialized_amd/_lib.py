@@ -48,6 +48,7 @@ SIGNATURES = {
     "lora_expand": (I, [C.POINTER(lora_store), P, I64, I, P, P, P, I64, P, SZ, P]),
     "lora_apply_batched": (I, [C.POINTER(lora_store), P, I64, P, I64, I, P, P, P, P, SZ, P]),
     "lora_apply_batched_phases": (I, [C.POINTER(lora_store), P, I64, P, I64, I, P, P, P, P, SZ, P, I]),
+    "lora_apply_launches": (I, [C.POINTER(lora_store), I, I]),
 }
 
 _lib = None

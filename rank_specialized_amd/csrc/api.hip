@@ -33,7 +33,7 @@ const char* lora_status_string(int status) {
 
 int lora_last_hip_error(void) { return g_last_hip; }
 
-int lora_abi_version(void) { return 2; }
+int lora_abi_version(void) { return 3; }
 
 int lora_store_bytes(int n, int d_in, int d_out, int dtype, const int32_t* ranks_host, int pad_to,
                      size_t* a_bytes_host, size_t* b_bytes_host, size_t* meta_bytes_host) {
@@ -172,6 +172,10 @@ static int apply_impl(const lora_store* store_host, const void* x, int64_t ldx, 
   if (ids == nullptr && (st = check_grouping(store_host, T, seg_off, perm)) != LORA_OK) return st;
   hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
+  if (phases == 3 && decode_apply_fits(s, T, ids != nullptr)) {
+    e = launch_decode_apply(s, ids, T, x, ldx, y, ldy, strm);
+    return e == hipSuccess ? LORA_OK : hip_fail(e);
+  }
   if (phases & 1) {
     if (ids != nullptr && s.n > kGroupMaxN) {
       // Too many adapters for the in-shrink histogram: sort first, into ws.
@@ -195,6 +199,17 @@ int lora_apply_batched(const lora_store* store_host, const void* x, int64_t ldx,
                        int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm, void* ws,
                        size_t ws_bytes, void* stream) {
   return apply_impl(store_host, x, ldx, y, ldy, T, ids, seg_off, perm, ws, ws_bytes, stream, 3);
+}
+
+int lora_apply_launches(const lora_store* store_host, int T, int with_ids) {
+  const int st = check_store(store_host);
+  if (st != LORA_OK) return -st;
+  if (T < 0) return -LORA_ERR_INVALID_ARG;
+  const lora_store& s = *store_host;
+  if (with_ids && (T > LORA_SEGMENT_MAX_T || s.n > LORA_SEGMENT_MAX_N)) return -LORA_ERR_UNSUPPORTED;
+  if (T == 0) return 0;
+  if (decode_apply_fits(s, T, with_ids != 0)) return 1;
+  return (with_ids && s.n > kGroupMaxN) ? 3 : 2;
 }
 
 int lora_apply_batched_phases(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy,

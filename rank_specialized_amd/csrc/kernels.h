@@ -22,6 +22,11 @@ hipError_t launch_segment(const int32_t* ids, int T, int n, int32_t* seg_off, in
 size_t shrink_lds_bytes(int T, int n, int r_max, bool with_ids);
 hipError_t launch_shrink(const lora_store& s, const int32_t* ids, const int32_t* seg_off, const int32_t* perm,
                          int T, const void* x, int64_t ldx, void* ws, hipStream_t stream);
+// The whole apply in one launch for decode-sized calls with ids
+// (decode_apply_fits): one workgroup per (token, slice of output features).
+bool decode_apply_fits(const lora_store& s, int T, bool with_ids);
+hipError_t launch_decode_apply(const lora_store& s, const int32_t* ids, int T, const void* x, int64_t ldx, void* y,
+                               int64_t ldy, hipStream_t stream);
 // h (grouped rows) = sum of the partials, in chunk order.
 hipError_t launch_reduce_partials(const lora_store& s, int T, const void* ws, float* h, int64_t ldh,
                                   hipStream_t stream);

@@ -35,6 +35,13 @@ constexpr int kVecMaxTokens = 8;
 constexpr int kVecTokens = 4;
 constexpr int kVecCols = 512;
 
+// A batched apply with ids of at most kDecodeMaxT tokens over a store of
+// rank <= kVecMaxRank whose d_in is one 16-byte chunk per thread of a
+// 512-thread workgroup runs as one launch, a workgroup per token (the
+// adapter's A and B are then read once per token, from cache after the
+// first: worth it while tokens per adapter stay few).
+constexpr int kDecodeMaxT = 512;
+
 // Upper bound on the number of runs of at most `len` tokens that T tokens
 // over n adapters cut into: each non-empty group of c tokens gives
 // ceil(c / len) runs and at most min(n, T) groups are non-empty.

@@ -50,7 +50,7 @@ def test_status_strings(lib):
     assert b"invalid" in lib.lora_status_string(1)
     assert b"unsupported" in lib.lora_status_string(2)
     assert b"HIP" in lib.lora_status_string(3)
-    assert lib.lora_abi_version() == 2
+    assert lib.lora_abi_version() == 3
     assert lib.lora_last_hip_error() == 0
 
 
@@ -228,3 +228,31 @@ def test_apply_phases_rejects_before_launch(lib):
         assert f(C.byref(st), *args, bad) == 1
     assert f(None, *args, 3) == 1
     assert f(C.byref(st), FAKE, 64, FAKE, 32, 0, FAKE, None, None, FAKE, 1 << 30, None, 1) == 0
+
+
+@pytest.mark.parametrize("T,n,d_in,r_max,dtype,with_ids,want", [
+    (256, 64, 4096, 4, 1, 1, 1),      # decode-uniform: one launch, a workgroup per token
+    (512, 64, 4096, 8, 1, 1, 1),      # the largest T and rank of that path
+    (512, 64, 4096, 8, 1, 0, 2),      # a grouping given: shrink + expand
+    (513, 64, 4096, 8, 1, 1, 2),      # one token more: shrink + expand
+    (256, 64, 4104, 4, 1, 1, 2),      # d_in beyond one 16-byte step per thread
+    (256, 64, 4096, 9, 1, 1, 2),      # rank above the fused path's
+    (16, 4, 256, 4, 0, 1, 1),         # float32 up to rank 4 ...
+    (16, 4, 256, 5, 0, 1, 2),         # ... not beyond
+    (16, 4, 2052, 4, 0, 1, 2),        # float32 d_in above 2048
+    (2048, 512, 3584, 64, 1, 1, 2),   # decode-spectral
+    (300, 5000, 64, 4, 1, 1, 1),      # per-token path: any number of adapters
+    (600, 5000, 64, 4, 1, 1, 3),      # beyond it, more adapters than the in-kernel histogram: sort first
+    (300, 5000, 64, 9, 1, 0, 2),      # ... unless the grouping is given
+    (0, 4, 64, 4, 1, 1, 0),
+])
+def test_apply_launches(lib, T, n, d_in, r_max, dtype, with_ids, want):
+    st = _store(n=n, d_in=d_in, d_out=32, r_max=r_max, dtype=dtype)
+    assert lib.lora_apply_launches(C.byref(st), T, with_ids) == want
+
+
+def test_apply_launches_errors(lib):
+    assert lib.lora_apply_launches(None, 16, 1) == -1
+    assert lib.lora_apply_launches(C.byref(_store()), -1, 1) == -1
+    assert lib.lora_apply_launches(C.byref(_store(r_max=65)), 16, 1) == -2
+    assert lib.lora_apply_launches(C.byref(_store()), L.LORA_SEGMENT_MAX_T + 1, 1) == -2

@@ -94,21 +94,73 @@ def test_shrink_h_within_fp32_bound(key):
 
 @pytest.mark.parametrize("key", ["1", "2", "3", "4"])
 def test_shrink_then_expand_equals_apply(key):
-    """lora_segment + lora_shrink + lora_expand and the batched apply compute
-    the same y bit for bit (same sub-tiles, same partial sums, same order)."""
+    """lora_segment + lora_shrink + lora_expand and the two-launch apply
+    (shrink, then expand: phases 1 and 2) compute the same y bit for bit
+    (same sub-tiles, same partial sums, same order)."""
     dev = device()
     for integer in (False, True):
         wl = make_config(key, integer=integer)
         store = pack(wl, dev)
         x, ids, y1 = inputs(wl, dev)
         y2 = y1.clone()
+        ws = torch.empty(rs.lora_workspace_bytes(store, wl.T), dtype=torch.uint8, device=dev)
         note(f"compose {key} integer={integer}")
-        rs.lora_apply_batched(store, x, y1, ids=ids)
+        rs.lora_apply_batched_phases(store, x, y1, 1, ids=ids, ws=ws)
+        rs.lora_apply_batched_phases(store, x, y1, 2, ids=ids, ws=ws)
         seg = rs.lora_segment(ids, store.n)
         h = rs.lora_shrink(store, x, seg)
         rs.lora_expand(store, h, seg, y2)
         torch.cuda.synchronize()
         assert np.array_equal(hbits(y1), hbits(y2)), (key, integer)
+
+
+# Decode-sized calls with ids (T <= 512, ranks <= 8 in bf16 or 4 in float32,
+# d_in at most one 16-byte chunk per thread of a 512-thread workgroup) run as
+# one launch, a workgroup per (token, 4096 output features).
+FUSED = {
+    "r4": dict(seed=90, T=256, n=64, d_in=4096, d_out=4096, ranks=[4] * 64),
+    "r6_ragged_out": dict(seed=91, T=200, n=30, d_in=1024, d_out=2056, ranks=[6, 5, 1, 0, 3, 6] * 5),
+    "r8_short_in": dict(seed=92, T=150, n=12, d_in=64, d_out=520, ranks=[8, 7, 2, 8, 1, 3, 5, 8, 6, 4, 2, 7]),
+    "many_tiles": dict(seed=93, T=512, n=3, d_in=2048, d_out=1024, ranks=[3, 4, 2], id_mode="zipf"),
+    "invalid_ids": dict(seed=94, T=300, n=9, d_in=512, d_out=768, ranks=[2, 4, 1, 3, 4, 2, 1, 3, 4],
+                        invalid_frac=0.3),
+    "wide_out_many_adapters": dict(seed=95, T=96, n=5000, d_in=256, d_out=9000,
+                                   ranks=[(a * 7) % 5 for a in range(5000)]),
+}
+
+
+@pytest.mark.parametrize("name", list(FUSED))
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("grouped", [False, True])
+def test_decode_fused_matches_split(name, dtype, grouped):
+    """The one-launch decode form (phases 3 with ids) against the oracle and
+    against the same call as two launches (phases 1 and 2): bit for bit on
+    exact integer data, within the tolerance on float data.  With a grouping
+    given, or a float32 store of rank above 4, both are the two launches."""
+    dev = device()
+    for integer in (True, False):
+        kw = dict(FUSED[name])
+        wl = make_random_workload(kw.pop("seed"), kw.pop("T"), kw.pop("n"), kw.pop("d_in"), kw.pop("d_out"),
+                                  kw.pop("ranks"), dtype=dtype, integer=integer, **kw)
+        store = pack(wl, dev)
+        x, ids, y1 = inputs(wl, dev)
+        y2 = y1.clone()
+        ws = torch.empty(rs.lora_workspace_bytes(store, wl.T), dtype=torch.uint8, device=dev)
+        grp = dict(seg=rs.lora_segment(ids, store.n)) if grouped else dict(ids=ids)
+        note(f"fused vs split {name} {dtype} grouped={grouped} integer={integer}")
+        rs.lora_apply_batched(store, x, y1, ws=ws, **grp)
+        rs.lora_apply_batched_phases(store, x, y2, 1, ws=ws, **grp)
+        rs.lora_apply_batched_phases(store, x, y2, 2, ws=ws, **grp)
+        torch.cuda.synchronize()
+        ref = _ref(wl)
+        if integer:
+            want = bf16_round_ref(ref) if dtype == "bf16" else ref.astype(np.float32)
+            assert np.array_equal(y_host(y1), want), "fused"
+            assert np.array_equal(y_host(y2), want), "split"
+        else:
+            tol = TOL[dtype] * max(np.abs(ref).max(), 1e-30)
+            assert np.abs(y_host(y1) - ref).max() <= tol, "fused"
+            assert np.abs(y_host(y2) - ref).max() <= tol, "split"
 
 
 def test_separate_kernels_integer_exact_decode():
@@ -301,12 +353,14 @@ def test_fp32_output_width_not_multiple_of_8():
     assert np.abs(y_host(wide[:, :44]) - ref).max() <= 1e-5 * np.abs(ref).max()
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("key", ["2", "3"])
+def test_graph_replay_matches_eager(key):
     """The apply captured in a HIP graph (as the benchmark times it) and
     replayed several times, with eager work and synchronizations between the
-    replays: every replay equals the eager result bit for bit."""
+    replays: every replay equals the eager result bit for bit (decode-uniform
+    runs the fused launch, decode-spectral the two launches)."""
     dev = device()
-    wl = make_config("3", with_y0=True)
+    wl = make_config(key, with_y0=True)
     store = pack(wl, dev)
     x, ids, y0 = inputs(wl, dev)
     ws = torch.empty(rs.lora_workspace_bytes(store, wl.T), dtype=torch.uint8, device=dev)

@@ -186,9 +186,9 @@ def _plan_store(n, dev, seed):
 
 @pytest.mark.parametrize("name", PLAN_CASES)
 def test_plan_from_ids(name):
-    """The plan the shrink forms from ids inside its workgroups (or, beyond
-    4096 adapters, from the sort it runs first) equals the sub-tiles of the
-    oracle's grouping, token for token."""
+    """The plan the shrink (phase 1 of the two-launch apply) forms from ids
+    inside its workgroups (or, beyond 4096 adapters, from the sort it runs
+    first) equals the sub-tiles of the oracle's grouping, token for token."""
     dev = device()
     ids, n = _segment_case(name)
     T = len(ids)
@@ -197,7 +197,7 @@ def test_plan_from_ids(name):
     y = torch.zeros(T, 64, dtype=torch.bfloat16, device=dev)
     ws = torch.empty(rs.lora_workspace_bytes(store, T), dtype=torch.uint8, device=dev)
     note(f"plan from ids {name} T={T} n={n}")
-    rs.lora_apply_batched(store, x, y, ids=torch.from_numpy(ids).to(dev), ws=ws)
+    rs.lora_apply_batched_phases(store, x, y, 1, ids=torch.from_numpy(ids).to(dev), ws=ws)
     torch.cuda.synchronize()
     so_ref, perm_ref, _ = segment_ref(ids.tolist(), n)
     row_off = np.concatenate([[0], np.cumsum(ranks)])
@@ -221,7 +221,7 @@ def test_plan_from_grouping(name):
     want = _expected_plan(so_ref, perm_ref, ranks, row_off, scales)
     ws = torch.empty(rs.lora_workspace_bytes(store, T), dtype=torch.uint8, device=dev)
     note(f"plan from grouping {name}")
-    rs.lora_apply_batched(store, x, y, seg=seg, ws=ws)
+    rs.lora_apply_batched_phases(store, x, y, 1, seg=seg, ws=ws)
     torch.cuda.synchronize()
     _check_plan(ws, want)
     ws.fill_(0xAB)
