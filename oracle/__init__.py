@@ -14,6 +14,8 @@ sources define (float64 unless stated, Python loops over tokens):
                      orders, for tiny inputs
 * ``bf16_round_ref`` - round-to-nearest-even onto bfloat16, used where a
                      floating-point result is compared bit for bit
+* ``jd_apply_ref`` - the shared-basis apply y = y0 + s_a U_c Sigma_a V_c^T x
+* ``jd_brute_force`` - the same in exact rational arithmetic, two orders
 
 Parity status: every function here is pinned by tests in
 ``tests/test_oracle.py`` (closed forms, invariants, brute force, library
@@ -27,3 +29,4 @@ from .lora_ref import (  # noqa: F401
     shrink_ref,
     shrink_error_bound,
 )
+from .jd_ref import jd_apply_ref, jd_brute_force  # noqa: F401,E402

@@ -209,3 +209,131 @@ def pin_segment_invariants(segment_fn):
 
 
 SEGMENT_PINS = (pin_segment_worked_example, pin_segment_vs_stable_argsort, pin_segment_invariants)
+
+
+# ------------------------------------------------------- shared-basis pins
+# The shared-basis (joint-diagonalization) apply of "Compress then Serve"
+# sections 3.1-3.2 and 11: y += s_i U_j Sigma_i V_j^T x for adapter i in
+# cluster j.  Each pin takes the function under test (the signature of
+# oracle.jd_apply_ref).
+
+def _jd_small(mode, seed=0, **kw):
+    from workloads import make_jd_workload
+    args = dict(T=30, n=7, k=3, d_in=24, d_out=20, r=5)
+    args.update(kw)
+    return make_jd_workload(seed, args["T"], args["n"], args["k"], args["d_in"], args["d_out"], args["r"],
+                            mode=mode, dtype="fp32", id_mode="uniform", invalid_frac=0.1)
+
+
+def _jd_call(fn, w, **over):
+    args = dict(x=w.x, ids=w.ids, cluster_of=w.cluster_of, U_list=w.U, V_list=w.V, sigma=w.sigma,
+                scales=w.scales)
+    args.update(over)
+    return np.asarray(fn(args["x"], args["ids"], args["cluster_of"], args["U_list"], args["V_list"],
+                         args["sigma"], args["scales"], over.get("y0")), np.float64)
+
+
+def pin_jd_merged_weight(fn):
+    """With y0 = 0 the delta equals x (W + s U Sigma V^T)^T - x W^T for any W
+    (the merged form of section 11 with B_i A_i = U Sigma_i V^T), for full
+    and diagonal Sigma; the merged matrix is built with dense products."""
+    for mode in ("full", "diag"):
+        w = _jd_small(mode, seed=1)
+        rng = np.random.default_rng(2)
+        W = rng.normal(size=(w.d_out, w.d_in))
+        ref = np.zeros((w.T, w.d_out))
+        for t in range(w.T):
+            a = int(w.ids[t])
+            if not 0 <= a < w.n:
+                continue
+            c = int(w.cluster_of[a])
+            S = w.sigma[a].astype(np.float64)
+            S = S if S.ndim == 2 else np.diag(S)
+            M = W + float(w.scales[a]) * (w.U[c].astype(np.float64) @ S @ w.V[c].astype(np.float64).T)
+            ref[t] = M @ w.x[t].astype(np.float64) - W @ w.x[t].astype(np.float64)
+        y = _jd_call(fn, w)
+        assert np.abs(y - ref).max() <= 1e-10 * max(np.abs(ref).max(), 1e-300), mode
+
+
+def pin_jd_diag_is_lora(fn):
+    """A diagonal Sigma_i is a LoRA adapter with B_i = U_j diag(Sigma_i) and
+    A_i = V_j^T (section 3.1): the result equals the LoRA oracle's on those
+    factors."""
+    from oracle import apply_ref
+    w = _jd_small("diag", seed=3)
+    A = [w.V[int(w.cluster_of[a])].astype(np.float64).T for a in range(w.n)]
+    B = [w.U[int(w.cluster_of[a])].astype(np.float64) * w.sigma[a].astype(np.float64)[None, :] for a in range(w.n)]
+    ref = apply_ref(w.x, w.ids, A, B, w.scales)
+    y = _jd_call(fn, w)
+    assert np.abs(y - ref).max() <= 1e-12 * max(np.abs(ref).max(), 1e-300)
+
+
+def pin_jd_exact_reconstruction(fn):
+    """JD-Full with orthonormal U, V: for adapters whose B_i A_i lies in
+    span(U) x span(V), the optimal Sigma_i = U^T B_i A_i V (section 8.1,
+    equation 6) reproduces B_i A_i exactly, so the apply equals the LoRA
+    oracle on the original B_i, A_i."""
+    from oracle import apply_ref
+    rng = np.random.default_rng(4)
+    T, n, k, d_in, d_out, r = 25, 5, 2, 18, 14, 4
+    U = [np.linalg.qr(rng.normal(size=(d_out, r)))[0] for _ in range(k)]
+    V = [np.linalg.qr(rng.normal(size=(d_in, r)))[0] for _ in range(k)]
+    cluster_of = rng.integers(0, k, size=n)
+    A_l, B_l, sig = [], [], []
+    for a in range(n):
+        c = cluster_of[a]
+        ra = 1 + a % 3
+        Ba = U[c] @ rng.normal(size=(r, ra))
+        Aa = rng.normal(size=(ra, r)) @ V[c].T
+        A_l.append(Aa)
+        B_l.append(Ba)
+        sig.append(U[c].T @ (Ba @ Aa) @ V[c])
+    x = rng.normal(size=(T, d_in))
+    ids = rng.integers(-1, n, size=T)
+    scales = rng.random(n) + 0.5
+    ref = apply_ref(x, ids, A_l, B_l, scales)
+    y = np.asarray(fn(x, ids, cluster_of, U, V, np.array(sig), scales, None), np.float64)
+    assert np.abs(y - ref).max() <= 1e-10 * max(np.abs(ref).max(), 1e-300)
+
+
+def pin_jd_brute_force(fn):
+    """Tiny integer inputs: equal to exact rational loops in both association
+    orders, U (Sigma (V^T x)) and (U Sigma V^T) x, for full and diagonal Sigma."""
+    from oracle import jd_brute_force
+    from workloads import make_jd_workload
+    for mode in ("full", "diag"):
+        w = make_jd_workload(5, 6, 4, 2, 5, 4, 3, mode=mode, dtype="fp32", id_mode="uniform",
+                             invalid_frac=0.2, integer=True)
+        y = _jd_call(fn, w)
+        for form in ("U(S(Vx))", "(USV)x"):
+            ex = jd_brute_force(w.x, w.ids, w.cluster_of, w.U, w.V, w.sigma, w.scales, form=form)
+            assert np.array_equal(y, np.array([[float(v) for v in row] for row in ex])), (mode, form)
+
+
+def pin_jd_zero_scale_invalid(fn):
+    """Sigma = 0 gives an exactly zero delta; doubling every scale doubles the
+    delta bit for bit; a token without adapter (-1) keeps y0."""
+    w = _jd_small("full", seed=6)
+    y0 = np.random.default_rng(7).normal(size=(w.T, w.d_out))
+    y = _jd_call(fn, w, sigma=np.zeros_like(w.sigma), y0=y0)
+    assert np.array_equal(y, y0)
+    d1 = _jd_call(fn, w)
+    d2 = _jd_call(fn, w, scales=w.scales * 2)
+    assert np.array_equal(d2, 2 * d1)
+    none = np.full(w.T, -1, np.int32)
+    assert np.array_equal(_jd_call(fn, w, ids=none, y0=y0), y0)
+
+
+def pin_jd_cluster_relabel(fn):
+    """Renaming the clusters (and permuting U, V alike) changes nothing."""
+    w = _jd_small("full", seed=8)
+    perm = np.array([2, 0, 1])  # new label of old cluster c
+    inv = np.argsort(perm)
+    y1 = _jd_call(fn, w)
+    y2 = _jd_call(fn, w, cluster_of=perm[w.cluster_of], U_list=[w.U[inv[c]] for c in range(w.k)],
+                  V_list=[w.V[inv[c]] for c in range(w.k)])
+    assert np.array_equal(y1, y2)
+
+
+JD_PINS = [pin_jd_merged_weight, pin_jd_diag_is_lora, pin_jd_exact_reconstruction, pin_jd_brute_force,
+           pin_jd_zero_scale_invalid, pin_jd_cluster_relabel]

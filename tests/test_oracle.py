@@ -86,3 +86,9 @@ def test_bf16_round_matches_torch_cpu():
 
 def test_oracle_header_marks_test_infrastructure():
     assert "TEST INFRASTRUCTURE" in oracle.__doc__
+
+
+@pytest.mark.parametrize("pin", P.JD_PINS, ids=lambda f: f.__name__)
+def test_jd_pin(pin):
+    from oracle import jd_apply_ref
+    pin(jd_apply_ref)

@@ -101,3 +101,66 @@ def test_segment_mutant_is_caught(kind):
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f"segment mutant {kind} passed every pin"
+
+
+def _jd_mutant(kind):
+    def fn(x, ids, cluster_of, U_list, V_list, sigma, scales, y0=None):
+        x64 = np.asarray(x, np.float64)
+        T = x64.shape[0]
+        n = len(cluster_of)
+        d_out = np.asarray(U_list[0]).shape[0]
+        y = np.zeros((T, d_out)) if y0 is None else np.asarray(y0, np.float64).copy()
+        for t in range(T):
+            a = int(ids[t])
+            if not 0 <= a < n:
+                continue
+            c = int(cluster_of[a])
+            if kind == "cluster_zero":
+                c = 0
+            if kind == "cluster_by_adapter":
+                c = a % len(U_list)
+            U = np.asarray(U_list[c], np.float64)
+            V = np.asarray(V_list[c], np.float64)
+            S = np.asarray(sigma[a], np.float64)
+            if kind == "sigma_of_next_adapter":
+                S = np.asarray(sigma[(a + 1) % n], np.float64)
+            if S.ndim == 1:
+                S = np.diag(S)
+            if kind == "sigma_transposed":
+                S = S.T
+            if kind == "sigma_dropped":
+                S = np.eye(S.shape[0])
+            s = float(scales[a])
+            if kind == "drop_scale":
+                s = 1.0
+            h = V.T @ x64[t]
+            if kind == "h_abs":
+                h = np.abs(h)
+            g = S @ h
+            if kind == "sigma_twice":
+                g = S @ g
+            y[t] += s * (U @ g)
+        return y
+    return fn
+
+
+JD_MUTANTS = ["cluster_zero", "cluster_by_adapter", "sigma_of_next_adapter", "sigma_transposed", "sigma_dropped",
+              "drop_scale", "h_abs", "sigma_twice"]
+
+
+@pytest.mark.parametrize("kind", JD_MUTANTS)
+def test_jd_mutant_is_caught(kind):
+    fn = _jd_mutant(kind)
+    caught = []
+    for pin in P.JD_PINS:
+        try:
+            pin(fn)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"shared-basis mutant {kind} passed every pin"
+
+
+def test_jd_unmutated_copy_passes():
+    fn = _jd_mutant("none")
+    for pin in P.JD_PINS:
+        pin(fn)

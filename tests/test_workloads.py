@@ -80,3 +80,19 @@ def test_integer_variant_is_exact_and_bounded():
     assert np.all(wl.module.A[0] == np.round(wl.module.A[0]))
     s = make_config("4", integer=True).module.scales
     assert np.all(np.log2(s) == np.round(np.log2(s)))
+
+
+def test_jd_workloads_seeded_and_shaped():
+    from workloads import JD_CONFIGS, make_jd_config, make_jd_workload
+    a = make_jd_workload(4, 40, 9, 3, 32, 16, 4, mode="full")
+    b = make_jd_workload(4, 40, 9, 3, 32, 16, 4, mode="full")
+    assert np.array_equal(a.ids, b.ids) and np.array_equal(a.sigma, b.sigma)
+    assert all(np.array_equal(u, v) for u, v in zip(a.U, b.U))
+    assert a.sigma.shape == (9, 4, 4) and a.U[0].shape == (16, 4) and a.V[0].shape == (32, 4)
+    d = make_jd_workload(4, 40, 9, 3, 32, 16, 4, mode="diag")
+    assert d.sigma.shape == (9, 4)
+    assert set(JD_CONFIGS) == {"jd-full", "jd-diag"}
+    for name in JD_CONFIGS:
+        w = make_jd_config(name)
+        assert (w.T, w.n, w.k, w.r, w.d_in, w.d_out) == (2048, 1024, 32, 16, 4096, 4096)
+        assert w.cluster_of.min() >= 0 and w.cluster_of.max() < 32

@@ -25,3 +25,4 @@ from .configs import (  # noqa: F401
     timing_y0,
     zipf_ids,
 )
+from .jd import JD_CONFIGS, JDWorkload, make_jd_config, make_jd_workload  # noqa: F401,E402
