@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "LoRA-delta tokens/s and achieved HBM GB/s (% of ~8 TB/s peak), 1 MI355X"
 PEAK_GBPS = 8000.0
 COLD_BYTES = 2.0e9  # rotation set size: well past the 256 MB Infinity Cache
-KERNEL_SOURCES = ["shrink.hip", "expand.hip", "decode.hip", "tile_ops.h", "device_common.h", "plan.h"]
+KERNEL_SOURCES = ["shrink.hip", "expand.hip", "decode.hip", "jd.hip", "tile_ops.h", "device_common.h", "plan.h"]
 
 WORKLOAD_NAMES = {
     "1": "tiny-fp32: d_in=d_out=256 f32, 4 adapters ranks {1,2,3,4}, T=16",
@@ -42,6 +42,10 @@ WORKLOAD_NAMES = {
     "3": "decode-spectral: d_in=d_out=3584 bf16, 512 adapters ranks max(6,ceil(64e)) e~Beta(2,5), "
          "T=2048 Zipf(1.1) ids",
     "4": "prefill: 4096->14336 bf16, 32 adapters ranks in {8,12,16,24,32}, T=8192 in 32x256 segments",
+    "jd-full": "shared-basis decode (JD-Full): d_in=d_out=4096 bf16, 1024 adapters in 32 clusters of rank 16, "
+               "full 16x16 Sigma per adapter, T=2048 Zipf(1.1) ids",
+    "jd-diag": "shared-basis decode (JD-Diag): d_in=d_out=4096 bf16, 1024 adapters in 32 clusters of rank 16, "
+               "diagonal Sigma per adapter, T=2048 Zipf(1.1) ids",
     "5U": "fleet decode step: 28 layers x 7 projections (3584/512/18944 dims) bf16, 1024 adapters rank 6 "
           "(orig 64), T=4096 Zipf(1.1) ids, one grouping reused by 196 applies",
     "5S": "fleet decode step: 28 layers x 7 projections (3584/512/18944 dims) bf16, 1024 adapters ranks "
@@ -128,42 +132,44 @@ def make_copies(rs, torch, wl, dev, pad_to: int, cold: bool):
     return copies, per_copy
 
 
-def time_apply(rs, torch, copies, ids, ws, steps, warmup):
+def _lora_step(rs, ids, ws):
+    return lambda c: rs.lora_apply_batched(c.store, c.x, c.y, ids=ids, ws=ws)
+
+
+def time_apply(rs, torch, copies, ids, ws, steps, warmup, step=None):
     """Events bracket exactly `steps` eager calls; returns ms per call."""
+    step = step or _lora_step(rs, ids, ws)
     for k in range(warmup):
-        c = copies[k % len(copies)]
-        rs.lora_apply_batched(c.store, c.x, c.y, ids=ids, ws=ws)
+        step(copies[k % len(copies)])
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
     for k in range(steps):
-        c = copies[(warmup + k) % len(copies)]
-        rs.lora_apply_batched(c.store, c.x, c.y, ids=ids, ws=ws)
+        step(copies[(warmup + k) % len(copies)])
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return e0.elapsed_time(e1) / steps, wall
 
 
-def time_apply_graph(rs, torch, copies, ids, ws, steps, warmup):
+def time_apply_graph(rs, torch, copies, ids, ws, steps, warmup, step=None):
     """The same `steps` calls captured once in a HIP graph (a decode loop's
     launches replayed without host work per kernel); events bracket one
     replay of all of them.  Returns ms per call."""
+    step = step or _lora_step(rs, ids, ws)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         for k in range(max(1, warmup)):
-            c = copies[k % len(copies)]
-            rs.lora_apply_batched(c.store, c.x, c.y, ids=ids, ws=ws)
+            step(copies[k % len(copies)])
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for k in range(steps):
-            c = copies[(warmup + k) % len(copies)]
-            rs.lora_apply_batched(c.store, c.x, c.y, ids=ids, ws=ws)
+            step(copies[(warmup + k) % len(copies)])
     g.replay()  # untimed warm replay
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
@@ -288,6 +294,116 @@ def summarize_pmc(key: str, fetch_dir: str, write_dir: str):
     with open(path, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
     print(json.dumps({f"config{key}": ent}))
+
+
+def jd_algorithmic_bytes(w, e: int):
+    """What the shared-basis apply must move: ids and the tokens' cluster ids,
+    x rows and y read + write of the tokens with an adapter in a cluster,
+    U_j and V_j of every touched cluster once, Sigma_i, scale and cluster of
+    every touched adapter once, and the two float32 buffers of [tokens, r]
+    (V^T x, then Sigma applied) written and read once."""
+    ids = w.ids.astype(np.int64)
+    ok = (ids >= 0) & (ids < w.n)
+    c = np.where(ok, w.cluster_of[np.clip(ids, 0, w.n - 1)], -1)
+    ok &= (c >= 0) & (c < w.k)
+    tv = int(ok.sum())
+    adapters = np.unique(ids[ok])
+    clusters = np.unique(c[ok])
+    sig = w.r * w.r if w.mode == "full" else w.r
+    parts = {"ids": 4 * w.T + 8 * w.T, "x": tv * w.d_in * e, "y": 2 * tv * w.d_out * e,
+             "basis": len(clusters) * w.r * (w.d_in + w.d_out) * e, "sigma": len(adapters) * (4 * sig + 8),
+             "h": 16 * tv * w.r}
+    parts["total"] = sum(parts.values())
+    return parts
+
+
+def run_jd(args, rs, torch, dev, key):
+    from workloads import make_jd_config
+    w = make_jd_config(key)
+    e = 2
+    dt = torch.bfloat16
+    gen = torch.Generator(device=dev).manual_seed(7)
+    st = rs.lora_jd_pack([torch.from_numpy(u).to(dev).to(dt) for u in w.U],
+                         [torch.from_numpy(v).to(dev).to(dt) for v in w.V], w.cluster_of, w.sigma, w.scales)
+    x = torch.from_numpy(w.x).to(dev).to(dt)
+    y = torch.randn(w.T, w.d_out, generator=gen, device=dev).to(dt)
+    ids = torch.from_numpy(w.ids).to(dev)
+    per_copy = (st.basis.A_pack.numel() + st.basis.B_pack.numel() + st.sigma.numel() * 4
+                + x.numel() * 2 + y.numel() * 2)
+    n_copies = 1 if args.warm else int(min(512, max(1, math.ceil(COLD_BYTES / per_copy))))
+    copies = [Copy(st, x, y)] + [Copy(st.clone(), x.clone(), y.clone()) for _ in range(n_copies - 1)]
+    ws = torch.empty(rs.lora_jd_workspace_bytes(st, w.T), dtype=torch.uint8, device=dev)
+    step = lambda c: rs.lora_jd_apply(c.store, c.x, c.y, ids, ws=ws)
+    eager_ms, _ = time_apply(rs, torch, copies, ids, ws, args.steps, args.warmup, step=step)
+    ms, wall = (eager_ms, 0.0) if args.no_graph else \
+        time_apply_graph(rs, torch, copies, ids, ws, args.steps, args.warmup, step=step)
+    nb = jd_algorithmic_bytes(w, e)
+    gbps = nb["total"] / (ms * 1e-3) / 1e9
+    del copies
+    torch.cuda.empty_cache()
+    # The same adapters served as ordinary rank-r LoRA: B_i = U_j Sigma_i, A_i = V_j^T.
+    as_lora = None
+    if not args.no_padded:
+        A_l, B_l = [], []
+        for a in range(w.n):
+            cj = int(w.cluster_of[a])
+            S = torch.from_numpy(w.sigma[a]).to(dev)
+            S = S if S.dim() == 2 else torch.diag(S)
+            U = torch.from_numpy(w.U[cj]).to(dev)
+            B_l.append((U @ S).to(dt).contiguous())
+            A_l.append(torch.from_numpy(w.V[cj]).to(dev).t().contiguous().to(dt))
+        ls = rs.lora_pack_retained(A_l, B_l, w.scales)
+        del A_l, B_l
+        lper = ls.A_pack.numel() + ls.B_pack.numel() + x.numel() * 2 + y.numel() * 2
+        lcopies = [Copy(ls, x, y)] + [Copy(ls.clone(), x.clone(), y.clone())
+                                      for _ in range((1 if args.warm else max(1, math.ceil(COLD_BYTES / lper))) - 1)]
+        lws = torch.empty(rs.lora_workspace_bytes(ls, w.T), dtype=torch.uint8, device=dev)
+        lms, _ = (time_apply if args.no_graph else time_apply_graph)(rs, torch, lcopies, ids, lws,
+                                                                   max(20, args.steps // 2), args.warmup)
+        as_lora = {"ms_per_step": round(lms, 5), "tokens_per_s": round(w.T / (lms * 1e-3), 1),
+                   "store_bytes": ls.A_pack.numel() + ls.B_pack.numel(),
+                   "jd_store_bytes": st.basis.A_pack.numel() + st.basis.B_pack.numel() + st.sigma.numel() * 4,
+                   "jd_speedup": round(lms / ms, 3)}
+        del lcopies, lws, ls
+        torch.cuda.empty_cache()
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import jd_apply_ref
+        try:
+            from threadpoolctl import threadpool_limits
+            limiter = threadpool_limits(1)
+        except Exception:  # pragma: no cover
+            limiter = None
+        Ts = min(w.T, 256)
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            jd_apply_ref(w.x[:Ts], w.ids[:Ts], w.cluster_of, w.U, w.V, w.sigma, w.scales)
+            reps += 1
+        el = time.perf_counter() - t0
+        if limiter is not None:
+            limiter.unregister()
+        cpu = {"value": round(reps * Ts / el, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {Ts} tokens, float64 per-token loop, {reps} repetitions over {el:.1f} s, "
+                         "BLAS pinned to 1 thread"}
+    roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gbps / PEAK_GBPS, 4), "traffic": None,
+                "kernel": "the step's four launches together (cluster ids, shrink, Sigma, expand)",
+                "algorithmic_bytes_per_launch": nb["total"], "avg_launch_us": round(ms * 1e3, 2)}
+    out = {
+        "metric": METRIC, "value": round(w.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded orthonormal (full) or N(0,1/sqrt(d)) (diag) bases, N(0,.) Sigma, N(0,1) x, bf16",
+        "config": {"workload": WORKLOAD_NAMES[key], "T": w.T, "n_adapters": w.n, "clusters": w.k, "r": w.r,
+                   "d_in": w.d_in, "d_out": w.d_out, "timing": "warm" if args.warm else
+                   f"cold-HBM rotation over {n_copies} copies"},
+        "gbps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_GBPS, 4), "bytes_per_step": nb["total"],
+        "bytes_breakdown": nb, "roofline": roofline, "cpu_baseline": cpu, "launches_per_step": 4,
+        "as_lora": as_lora, "eager_ms_per_step": round(eager_ms, 5),
+        "timed_as": "eager launches" if args.no_graph else "one HIP-graph replay of the K captured steps",
+        "kernel_sources_sha": kernel_source_digest(),
+    }
+    print(json.dumps(out), flush=True)
 
 
 def cpu_baseline(wl, seconds: float):
@@ -506,6 +622,9 @@ def main():
     key = args.config
     if key in ("5U", "5S"):
         run_fleet(args, rs, torch, dev)
+        return
+    if key.startswith("jd-"):
+        run_jd(args, rs, torch, dev, key)
         return
     wl = build_workload(key)
     m = wl.module

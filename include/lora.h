@@ -259,6 +259,62 @@ int lora_apply_batched_phases(const lora_store* store_host, const void* x, int64
  */
 int lora_apply_launches(const lora_store* store_host, int T, int with_ids);
 
+/*
+ * Shared-basis (joint-diagonalization) adapters.  "Compress then Serve"
+ * section 3.1 holds adapter i's product B_i A_i as U Sigma_i V^T, with U
+ * (d_out x r) and V (d_in x r) shared and Sigma_i a full r x r matrix
+ * (JD-Full) or diagonal (JD-Diag); section 3.2 splits the adapters into
+ * clusters, cluster j with its own U_j, V_j; section 11 serves the branch as
+ * U (Sigma (V^T x)).  The apply is
+ *
+ *     y[t] += s_a * U_c (Sigma_a (V_c^T x[t]))     a = ids[t], c = cluster_of[a]
+ *
+ * The store:
+ *   basis      : an ordinary store (lora_pack_retained) whose n = k entries
+ *                are the clusters, every one at rank r: A_j = V_j^T (r x
+ *                d_in), B_j = U_j (d_out x r), scale 1.
+ *   n_adapters : adapters.
+ *   r          : the shared rank (= basis.r_max; basis.R must be k * r).
+ *   diag       : 1: Sigma_a is a vector of r values (JD-Diag); 0: r x r
+ *                row-major (JD-Full).
+ *   cluster_of : device int32 [n_adapters]; a value outside [0, k) means the
+ *                adapter adds nothing.
+ *   sigma      : device float32, [n_adapters][r] or [n_adapters][r][r].
+ *   scale      : device float32 [n_adapters] (s_a).
+ * The caller owns every buffer; the struct only points at them.
+ */
+typedef struct lora_jd_store {
+  lora_store basis;
+  int32_t n_adapters;
+  int32_t r;
+  int32_t diag;
+  int32_t reserved;
+  const int32_t* cluster_of;
+  const float* sigma;
+  const float* scale;
+} lora_jd_store;
+
+/* Workspace of lora_jd_apply for T tokens (host only; 0 on invalid
+ * arguments): the tokens' cluster ids, the float32 h buffer (Sigma applied),
+ * and the basis store's lora_workspace_bytes. */
+size_t lora_jd_workspace_bytes(const lora_jd_store* store_host, int T);
+
+/*
+ * The shared-basis apply (section 13.4's three steps with a per-token index:
+ * V^T, then Sigma with the scale, then U, added into y).  Four kernels: the
+ * cluster of each token's adapter; the shrink of the basis store grouped by
+ * cluster (h = V_c^T x, float32); per token g = s_a Sigma_a h (float32, a
+ * fixed order); the expand of the basis store from g (y updated, one
+ * rounding).  x [T, ldx], y [T, ldy] in token order as for
+ * lora_apply_batched; ids as for lora_apply_batched (ids outside [0,
+ * n_adapters) add nothing).  Errors: INVALID_ARG (null pointers, T < 0,
+ * r != basis.r_max, basis.R != basis.n * r, diag not 0 or 1, workspace too
+ * small); UNSUPPORTED (those of lora_apply_batched for the basis store, more
+ * than 4096 clusters, T > LORA_SEGMENT_MAX_T).
+ */
+int lora_jd_apply(const lora_jd_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy, int T,
+                  const int32_t* ids, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,9 +37,11 @@ def _sigma_times(sig, h):
 def jd_apply_ref(x, ids, cluster_of, U_list, V_list, sigma, scales, y0=None) -> np.ndarray:
     """y[t] = y0[t] + s_a U_c (Sigma_a (V_c^T x[t])), a = ids[t], c = cluster_of[a].
 
-    Tokens whose id is outside [0, n) (-1 = no adapter) keep y0.  float64
-    throughout, on the exact values of the inputs, in the served order of
-    [CtS] section 11 (V^T x, then Sigma, then U).
+    Tokens whose id is outside [0, n) (-1 = no adapter) keep y0, and so do
+    tokens whose adapter's cluster is outside [0, k) (a reading: the pages
+    assign every adapter a cluster; an unassigned one adds nothing).
+    float64 throughout, on the exact values of the inputs, in the served
+    order of [CtS] section 11 (V^T x, then Sigma, then U).
     """
     x64 = _as64(x)
     T = x64.shape[0]
@@ -51,6 +53,8 @@ def jd_apply_ref(x, ids, cluster_of, U_list, V_list, sigma, scales, y0=None) -> 
         if not 0 <= a < n:
             continue
         c = int(cluster_of[a])
+        if not 0 <= c < len(U_list):
+            continue
         U = _as64(U_list[c])
         V = _as64(V_list[c])
         h = V.T @ x64[t]
@@ -78,6 +82,8 @@ def jd_brute_force(x, ids, cluster_of, U_list, V_list, sigma, scales, y0=None,
         if not 0 <= a < n:
             continue
         c = int(cluster_of[a])
+        if not 0 <= c < len(U_list):
+            continue
         U = [[Fraction(float(v)) for v in row] for row in np.asarray(U_list[c])]
         V = [[Fraction(float(v)) for v in row] for row in np.asarray(V_list[c])]
         r = len(U[0])

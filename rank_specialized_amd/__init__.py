@@ -27,7 +27,8 @@ from ._lib import LoraError, lora_store  # noqa: F401
 __all__ = [
     "Store", "Segmentation", "LoraError", "lora_store_bytes", "lora_pack_retained",
     "lora_segment", "lora_workspace_bytes", "lora_shrink", "lora_expand", "lora_apply_batched",
-    "lora_apply_batched_phases", "lora_apply_launches", "load_library",
+    "lora_apply_batched_phases", "lora_apply_launches", "JDStore", "lora_jd_pack", "lora_jd_workspace_bytes",
+    "lora_jd_apply", "load_library",
 ]
 
 _DTYPES = {torch.bfloat16: L.LORA_DTYPE_BF16, torch.float32: L.LORA_DTYPE_F32}
@@ -254,3 +255,82 @@ def lora_apply_launches(store: Store, T: int, with_ids: bool = True) -> int:
     if v < 0:
         L.check("lora_apply_launches", -v)
     return v
+
+
+@dataclass
+class JDStore:
+    """A shared-basis store: the basis store over clusters (A = V_j^T, B = U_j,
+    rank r, scale 1) plus per-adapter cluster, Sigma and scale buffers."""
+
+    c: L.lora_jd_store
+    basis: Store
+    cluster_of: torch.Tensor
+    sigma: torch.Tensor
+    scale: torch.Tensor
+
+    @property
+    def n(self) -> int:
+        return self.c.n_adapters
+
+    @property
+    def k(self) -> int:
+        return self.basis.n
+
+    @property
+    def r(self) -> int:
+        return self.c.r
+
+    def ref(self):
+        return C.byref(self.c)
+
+    def clone(self) -> "JDStore":
+        return _jd_store(self.basis.clone(), self.cluster_of.clone(), self.sigma.clone(), self.scale.clone(),
+                         self.c.diag)
+
+
+def _jd_store(basis: Store, cluster_of, sigma, scale, diag: int) -> JDStore:
+    c = L.lora_jd_store()
+    c.basis = basis.c
+    c.n_adapters = int(cluster_of.numel())
+    c.r = basis.r_max
+    c.diag = int(diag)
+    c.cluster_of, c.sigma, c.scale = cluster_of.data_ptr(), sigma.data_ptr(), scale.data_ptr()
+    return JDStore(c, basis, cluster_of, sigma, scale)
+
+
+def lora_jd_pack(U_list: Sequence[torch.Tensor], V_list: Sequence[torch.Tensor], cluster_of, sigma, scales) -> JDStore:
+    """Shared-basis store from per-cluster U_j [d_out, r] and V_j [d_in, r]
+    (device tensors of one dtype), cluster_of [n], Sigma [n, r, r] (full) or
+    [n, r] (diagonal) and scales [n]."""
+    k = len(U_list)
+    if k == 0 or len(V_list) != k:
+        raise ValueError("need one U and one V per cluster")
+    device = U_list[0].device
+    basis = lora_pack_retained([V.t().contiguous() for V in V_list], [U.contiguous() for U in U_list], [1.0] * k)
+    r = basis.r_max
+    sig = torch.as_tensor(sigma, dtype=torch.float32).to(device).contiguous()
+    n = sig.shape[0]
+    if sig.shape not in ((n, r, r), (n, r)):
+        raise ValueError("sigma must be [n, r, r] or [n, r]")
+    cl = torch.as_tensor(cluster_of, dtype=torch.int32).to(device).contiguous()
+    sc = torch.as_tensor(scales, dtype=torch.float32).to(device).contiguous()
+    if cl.shape != (n,) or sc.shape != (n,):
+        raise ValueError("cluster_of and scales need one entry per adapter")
+    return _jd_store(basis, cl, sig, sc, 1 if sig.dim() == 2 else 0)
+
+
+def lora_jd_workspace_bytes(store: JDStore, T: int) -> int:
+    return int(L.lib().lora_jd_workspace_bytes(store.ref(), int(T)))
+
+
+def lora_jd_apply(store: JDStore, x: torch.Tensor, y: torch.Tensor, ids: torch.Tensor,
+                  ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[t] += s_a U_c Sigma_a V_c^T x[t] in place (a = ids[t], c = its cluster)."""
+    T = x.shape[0]
+    if ids.dtype != torch.int32 or not ids.is_contiguous():
+        raise ValueError("ids must be a contiguous int32 vector")
+    if ws is None:
+        ws = torch.empty(max(lora_jd_workspace_bytes(store, T), 16), dtype=torch.uint8, device=x.device)
+    L.check("lora_jd_apply", L.lib().lora_jd_apply(store.ref(), _p(x), _rows(x, "x"), _p(y), _rows(y, "y"), T,
+                                                   _p(ids), ws.data_ptr(), ws.numel(), _stream(x)))
+    return y

@@ -31,6 +31,13 @@ class lora_store(C.Structure):
     ]
 
 
+class lora_jd_store(C.Structure):
+    _fields_ = [
+        ("basis", lora_store), ("n_adapters", C.c_int32), ("r", C.c_int32), ("diag", C.c_int32),
+        ("reserved", C.c_int32), ("cluster_of", C.c_void_p), ("sigma", C.c_void_p), ("scale", C.c_void_p),
+    ]
+
+
 # name -> (restype, argtypes); mirrors include/lora.h
 P = C.c_void_p
 I = C.c_int
@@ -49,6 +56,8 @@ SIGNATURES = {
     "lora_apply_batched": (I, [C.POINTER(lora_store), P, I64, P, I64, I, P, P, P, P, SZ, P]),
     "lora_apply_batched_phases": (I, [C.POINTER(lora_store), P, I64, P, I64, I, P, P, P, P, SZ, P, I]),
     "lora_apply_launches": (I, [C.POINTER(lora_store), I, I]),
+    "lora_jd_workspace_bytes": (SZ, [C.POINTER(lora_jd_store), I]),
+    "lora_jd_apply": (I, [C.POINTER(lora_jd_store), P, I64, P, I64, I, P, P, SZ, P]),
 }
 
 _lib = None

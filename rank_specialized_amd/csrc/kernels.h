@@ -27,6 +27,13 @@ hipError_t launch_shrink(const lora_store& s, const int32_t* ids, const int32_t*
 bool decode_apply_fits(const lora_store& s, int T, bool with_ids);
 hipError_t launch_decode_apply(const lora_store& s, const int32_t* ids, int T, const void* x, int64_t ldx, void* y,
                                int64_t ldy, hipStream_t stream);
+// Shared-basis apply: cluster id of each token's adapter (-1: none); and per
+// token of each planned sub-tile g = s_a Sigma_a (sum of the partials) into h.
+hipError_t launch_jd_cluster_ids(const int32_t* ids, int T, int n, const int32_t* cluster_of, int k, int32_t* cid,
+                                 hipStream_t stream);
+hipError_t launch_jd_sigma(const lora_store& basis, int T, const void* ws, const int32_t* ids, int n,
+                           const int32_t* cluster_of, const float* sigma, int diag, const float* scale, float* h,
+                           int64_t ldh, hipStream_t stream);
 // h (grouped rows) = sum of the partials, in chunk order.
 hipError_t launch_reduce_partials(const lora_store& s, int T, const void* ws, float* h, int64_t ldh,
                                   hipStream_t stream);

@@ -322,6 +322,13 @@ def pin_jd_zero_scale_invalid(fn):
     assert np.array_equal(d2, 2 * d1)
     none = np.full(w.T, -1, np.int32)
     assert np.array_equal(_jd_call(fn, w, ids=none, y0=y0), y0)
+    # an adapter outside every cluster (cluster -1 or k) adds nothing; the others are unchanged
+    cl = w.cluster_of.copy()
+    cl[0], cl[1] = -1, w.k
+    y_cut = _jd_call(fn, w, cluster_of=cl, y0=y0)
+    y_all = _jd_call(fn, w, y0=y0)
+    cut = np.isin(w.ids, [0, 1])
+    assert np.array_equal(y_cut[cut], y0[cut]) and np.array_equal(y_cut[~cut], y_all[~cut])
 
 
 def pin_jd_cluster_relabel(fn):

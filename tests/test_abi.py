@@ -256,3 +256,49 @@ def test_apply_launches_errors(lib):
     assert lib.lora_apply_launches(C.byref(_store()), -1, 1) == -1
     assert lib.lora_apply_launches(C.byref(_store(r_max=65)), 16, 1) == -2
     assert lib.lora_apply_launches(C.byref(_store()), L.LORA_SEGMENT_MAX_T + 1, 1) == -2
+
+
+def _jd(k=4, r=8, n=10, diag=0, d_in=64, d_out=32):
+    j = L.lora_jd_store()
+    j.basis = _store(n=k, d_in=d_in, d_out=d_out, r_max=r, R=k * r)
+    j.n_adapters, j.r, j.diag = n, r, diag
+    j.cluster_of = j.sigma = j.scale = FAKE
+    return j
+
+
+def test_jd_workspace_bytes(lib):
+    j = _jd()
+    T = 100
+    up = lambda v: -(-v // 256) * 256
+    want = up(T * 4) + up(T * 8 * 4) + lib.lora_workspace_bytes(C.byref(j.basis), T)
+    assert lib.lora_jd_workspace_bytes(C.byref(j), T) == want
+    assert lib.lora_jd_workspace_bytes(None, T) == 0
+    bad = _jd()
+    bad.r = 7  # must equal the basis r_max (8)
+    assert lib.lora_jd_workspace_bytes(C.byref(bad), T) == 0
+
+
+def test_jd_apply_rejects_before_launch(lib):
+    big = 1 << 30
+    f = lib.lora_jd_apply
+
+    def call(j=None, T=16, ids=FAKE, ws=FAKE, wsb=big, x=FAKE, y=FAKE, ldx=64, ldy=32):
+        j = j if j is not None else _jd()
+        return f(C.byref(j), x, ldx, y, ldy, T, ids, ws, wsb, None)
+
+    assert f(None, FAKE, 64, FAKE, 32, 16, FAKE, FAKE, big, None) == 1
+    assert call(T=-1) == 1
+    assert call(T=0) == 0
+    assert call(ids=None) == 1
+    assert call(ws=None) == 1
+    assert call(wsb=64) == 1
+    assert call(ws=FAKE + 8) == 2
+    assert call(x=None) == 1
+    assert call(ldy=16) == 1
+    j = _jd()
+    j.basis.R = 31  # not k * r
+    assert call(j=j) == 1
+    assert call(j=_jd(diag=2)) == 1
+    assert call(j=_jd(r=65)) == 2
+    assert call(j=_jd(k=5000, n=6000)) == 2  # more clusters than the in-kernel grouping takes
+    assert call(T=L.LORA_SEGMENT_MAX_T + 1) == 2

@@ -119,6 +119,8 @@ def _jd_mutant(kind):
                 c = 0
             if kind == "cluster_by_adapter":
                 c = a % len(U_list)
+            if not 0 <= c < len(U_list):
+                continue
             U = np.asarray(U_list[c], np.float64)
             V = np.asarray(V_list[c], np.float64)
             S = np.asarray(sigma[a], np.float64)
