@@ -297,8 +297,7 @@ def summarize_pmc(key: str, fetch_dir: str, write_dir: str):
 
 
 def jd_algorithmic_bytes(w, e: int):
-    """What the shared-basis apply must move: ids and the tokens' cluster ids,
-    x rows and y read + write of the tokens with an adapter in a cluster,
+    """What the shared-basis apply must move: ids, x rows and y read + write of the tokens with an adapter in a cluster,
     U_j and V_j of every touched cluster once, Sigma_i, scale and cluster of
     every touched adapter once, and the two float32 buffers of [tokens, r]
     (V^T x, then Sigma applied) written and read once."""
@@ -310,7 +309,7 @@ def jd_algorithmic_bytes(w, e: int):
     adapters = np.unique(ids[ok])
     clusters = np.unique(c[ok])
     sig = w.r * w.r if w.mode == "full" else w.r
-    parts = {"ids": 4 * w.T + 8 * w.T, "x": tv * w.d_in * e, "y": 2 * tv * w.d_out * e,
+    parts = {"ids": 4 * w.T, "x": tv * w.d_in * e, "y": 2 * tv * w.d_out * e,
              "basis": len(clusters) * w.r * (w.d_in + w.d_out) * e, "sigma": len(adapters) * (4 * sig + 8),
              "h": 16 * tv * w.r}
     parts["total"] = sum(parts.values())
@@ -387,7 +386,7 @@ def run_jd(args, rs, torch, dev, key):
                          "BLAS pinned to 1 thread"}
     roofline = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                 "frac": round(gbps / PEAK_GBPS, 4), "traffic": None,
-                "kernel": "the step's four launches together (cluster ids, shrink, Sigma, expand)",
+                "kernel": "the step's three launches together (shrink grouped by cluster, Sigma, expand)",
                 "algorithmic_bytes_per_launch": nb["total"], "avg_launch_us": round(ms * 1e3, 2)}
     out = {
         "metric": METRIC, "value": round(w.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
@@ -398,7 +397,7 @@ def run_jd(args, rs, torch, dev, key):
                    "d_in": w.d_in, "d_out": w.d_out, "timing": "warm" if args.warm else
                    f"cold-HBM rotation over {n_copies} copies"},
         "gbps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_GBPS, 4), "bytes_per_step": nb["total"],
-        "bytes_breakdown": nb, "roofline": roofline, "cpu_baseline": cpu, "launches_per_step": 4,
+        "bytes_breakdown": nb, "roofline": roofline, "cpu_baseline": cpu, "launches_per_step": 3,
         "as_lora": as_lora, "eager_ms_per_step": round(eager_ms, 5),
         "timed_as": "eager launches" if args.no_graph else "one HIP-graph replay of the K captured steps",
         "kernel_sources_sha": kernel_source_digest(),

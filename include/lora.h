@@ -295,15 +295,15 @@ typedef struct lora_jd_store {
 } lora_jd_store;
 
 /* Workspace of lora_jd_apply for T tokens (host only; 0 on invalid
- * arguments): the tokens' cluster ids, the float32 h buffer (Sigma applied),
- * and the basis store's lora_workspace_bytes. */
+ * arguments): the float32 h buffer (Sigma applied) and the basis store's
+ * lora_workspace_bytes. */
 size_t lora_jd_workspace_bytes(const lora_jd_store* store_host, int T);
 
 /*
  * The shared-basis apply (section 13.4's three steps with a per-token index:
- * V^T, then Sigma with the scale, then U, added into y).  Four kernels: the
- * cluster of each token's adapter; the shrink of the basis store grouped by
- * cluster (h = V_c^T x, float32); per token g = s_a Sigma_a h (float32, a
+ * V^T, then Sigma with the scale, then U, added into y).  Three kernels: the
+ * shrink of the basis store with the tokens grouped by the cluster of their
+ * adapter (h = V_c^T x, float32); per token g = s_a Sigma_a h (float32, a
  * fixed order); the expand of the basis store from g (y updated, one
  * rounding).  x [T, ldx], y [T, ldy] in token order as for
  * lora_apply_batched; ids as for lora_apply_batched (ids outside [0,

@@ -201,8 +201,7 @@ int lora_apply_batched(const lora_store* store_host, const void* x, int64_t ldx,
   return apply_impl(store_host, x, ldx, y, ldy, T, ids, seg_off, perm, ws, ws_bytes, stream, 3);
 }
 
-// Shared-basis workspace: cluster ids [T] | h [T][ldp] | the basis store's workspace.
-static size_t jd_cid_bytes(int T) { return align_up((size_t)(T > 0 ? T : 0) * 4, 256); }
+// Shared-basis workspace: h [T][ldp] | the basis store's workspace.
 static size_t jd_h_bytes(const lora_store& b, int T) {
   return align_up((size_t)(T > 0 ? T : 0) * (size_t)partial_ld(b.r_max) * 4, 256);
 }
@@ -220,7 +219,7 @@ static int check_jd_store(const lora_jd_store* s) {
 
 size_t lora_jd_workspace_bytes(const lora_jd_store* store_host, int T) {
   if (check_jd_store(store_host) != LORA_OK || T < 0) return 0;
-  return jd_cid_bytes(T) + jd_h_bytes(store_host->basis, T) + workspace_bytes(&store_host->basis, T);
+  return jd_h_bytes(store_host->basis, T) + workspace_bytes(&store_host->basis, T);
 }
 
 int lora_jd_apply(const lora_jd_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy, int T,
@@ -238,13 +237,11 @@ int lora_jd_apply(const lora_jd_store* store_host, const void* x, int64_t ldx, v
   if (T > LORA_SEGMENT_MAX_T) return LORA_ERR_UNSUPPORTED;
   if (ws_bytes < lora_jd_workspace_bytes(store_host, T)) return LORA_ERR_INVALID_ARG;
   char* base = reinterpret_cast<char*>(ws);
-  int32_t* cid = reinterpret_cast<int32_t*>(base);
-  float* h = reinterpret_cast<float*>(base + jd_cid_bytes(T));
-  void* bws = base + jd_cid_bytes(T) + jd_h_bytes(b, T);
+  float* h = reinterpret_cast<float*>(base);
+  void* bws = base + jd_h_bytes(b, T);
   const int64_t ldh = partial_ld(b.r_max);
   hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = launch_jd_cluster_ids(ids, T, j.n_adapters, j.cluster_of, b.n, cid, strm);
-  if (e == hipSuccess) e = launch_shrink(b, cid, nullptr, nullptr, T, x, ldx, bws, strm);
+  hipError_t e = launch_shrink(b, ids, nullptr, nullptr, T, x, ldx, bws, strm, j.cluster_of, j.n_adapters);
   if (e == hipSuccess)
     e = launch_jd_sigma(b, T, bws, ids, j.n_adapters, j.cluster_of, j.sigma, j.diag, j.scale, h, ldh, strm);
   if (e == hipSuccess) e = launch_expand(b, T, bws, h, ldh, y, ldy, strm);

@@ -9,31 +9,15 @@
 // section 13.4: the three steps (A, Sigma, B) take a per-token index.
 //
 // Here the clusters are the "adapters" of an ordinary store (A rows = V_j^T,
-// B block = U_j, every rank r, scale 1), so the tokens are grouped by
-// cluster and the shrink and the expand run unchanged; between them:
-//   jd_cluster_ids_kernel  cluster of each token's adapter (-1: none), the
-//                          ids the shrink groups by;
-//   jd_sigma_kernel        per token of each planned sub-tile: h = the
-//                          shrink's partial sums (chunk order), then
-//                          g = s_a Sigma_a h, written as the expand's h.
+// B block = U_j, every rank r, scale 1): the shrink groups the tokens by the
+// cluster of their adapter (its ids mapped through cluster_of) and the
+// expand runs unchanged; between them, jd_sigma_kernel takes each token of
+// each planned sub-tile: h = the shrink's partial sums (chunk order), then
+// g = s_a Sigma_a h, written as the expand's h.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace lora {
-
-__global__ void __launch_bounds__(256) jd_cluster_ids_kernel(const int32_t* __restrict__ ids, int T, int n,
-                                                             const int32_t* __restrict__ cluster_of, int k,
-                                                             int32_t* __restrict__ cid) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= T) return;
-  const int a = ids[t];
-  int c = -1;
-  if ((unsigned)a < (unsigned)n) {
-    const int v = cluster_of[a];
-    c = (unsigned)v < (unsigned)k ? v : -1;  // an adapter outside every cluster adds nothing
-  }
-  cid[t] = c;
-}
 
 struct SigmaArgs {
   const char* plan;
@@ -106,14 +90,6 @@ __global__ void __launch_bounds__(256) jd_sigma_kernel(SigmaArgs p) {
                   : sigma_full<LORA_MAX_RANK>(srow, h, r, s);
   }
   if (lane < r) p.h[(int64_t)row * p.ldh + lane] = g;
-}
-
-hipError_t launch_jd_cluster_ids(const int32_t* ids, int T, int n, const int32_t* cluster_of, int k, int32_t* cid,
-                                 hipStream_t stream) {
-  if (T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(jd_cluster_ids_kernel, dim3((unsigned)((T + 255) / 256)), dim3(256), 0, stream, ids, T, n,
-                     cluster_of, k, cid);
-  return hipGetLastError();
 }
 
 hipError_t launch_jd_sigma(const lora_store& basis, int T, const void* ws, const int32_t* ids, int n,

@@ -21,16 +21,15 @@ hipError_t launch_segment(const int32_t* ids, int T, int n, int32_t* seg_off, in
 // tokens from ids (n <= kGroupMaxN) or from (seg_off, perm); writes the plan.
 size_t shrink_lds_bytes(int T, int n, int r_max, bool with_ids);
 hipError_t launch_shrink(const lora_store& s, const int32_t* ids, const int32_t* seg_off, const int32_t* perm,
-                         int T, const void* x, int64_t ldx, void* ws, hipStream_t stream);
+                         int T, const void* x, int64_t ldx, void* ws, hipStream_t stream,
+                         const int32_t* id_map = nullptr, int id_map_n = 0);
 // The whole apply in one launch for decode-sized calls with ids
 // (decode_apply_fits): one workgroup per (token, slice of output features).
 bool decode_apply_fits(const lora_store& s, int T, bool with_ids);
 hipError_t launch_decode_apply(const lora_store& s, const int32_t* ids, int T, const void* x, int64_t ldx, void* y,
                                int64_t ldy, hipStream_t stream);
-// Shared-basis apply: cluster id of each token's adapter (-1: none); and per
-// token of each planned sub-tile g = s_a Sigma_a (sum of the partials) into h.
-hipError_t launch_jd_cluster_ids(const int32_t* ids, int T, int n, const int32_t* cluster_of, int k, int32_t* cid,
-                                 hipStream_t stream);
+// Shared-basis apply: per token of each planned sub-tile (grouped by the
+// cluster of its adapter), g = s_a Sigma_a (sum of the partials) into h.
 hipError_t launch_jd_sigma(const lora_store& basis, int T, const void* ws, const int32_t* ids, int n,
                            const int32_t* cluster_of, const float* sigma, int diag, const float* scale, float* h,
                            int64_t ldh, hipStream_t stream);

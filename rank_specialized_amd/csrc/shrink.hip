@@ -56,6 +56,10 @@ struct ShrinkArgs {
   int64_t ldp, pstride;  // floats: row stride, distance between partials
   char* plan;
   int warm_key;
+  // ids mode: when set, token t is grouped by id_map[ids[t]] (ids outside
+  // [0, id_map_n) by -1), e.g. the cluster of its adapter.
+  const int32_t* id_map;
+  int id_map_n;
 };
 
 // v[ng] for ng = 1..4 without indexing the argument array at run time
@@ -120,6 +124,18 @@ __global__ void __launch_bounds__(kShrinkThreads, 4) shrink_kernel(ShrinkArgs p)
         iv[q].y = t + 1 < T ? p.ids[t + 1] : -1;
         iv[q].z = t + 2 < T ? p.ids[t + 2] : -1;
         iv[q].w = t + 3 < T ? p.ids[t + 3] : -1;
+      }
+    }
+    if (p.id_map) {  // uniform
+      auto mapped = [&](int v) { return (unsigned)v < (unsigned)p.id_map_n ? p.id_map[v] : -1; };
+#pragma unroll
+      for (int q = 0; q < kIdLoads; ++q) {
+        if (4 * q * kShrinkThreads < T) {
+          iv[q].x = mapped(iv[q].x);
+          iv[q].y = mapped(iv[q].y);
+          iv[q].z = mapped(iv[q].z);
+          iv[q].w = mapped(iv[q].w);
+        }
       }
     }
     for (int i = tid; i < n; i += kShrinkThreads) info[i] = 0;
@@ -489,7 +505,8 @@ static hipError_t launch_shrink_t(const ShrinkArgs& a, int grid, size_t lds, hip
 }
 
 hipError_t launch_shrink(const lora_store& s, const int32_t* ids, const int32_t* seg_off, const int32_t* perm,
-                         int T, const void* x, int64_t ldx, void* ws, hipStream_t stream) {
+                         int T, const void* x, int64_t ldx, void* ws, hipStream_t stream, const int32_t* id_map,
+                         int id_map_n) {
   const ShrinkSplit sp = shrink_split(s.d_in, s.r_max, s.dtype);
   const WsLayout L = ws_layout(T, s.n, s.d_in, s.r_max, s.dtype);
   const int64_t max_sub = plan_max_subtiles(T, s.n);
@@ -520,6 +537,8 @@ hipError_t launch_shrink(const lora_store& s, const int32_t* ids, const int32_t*
   a.pstride = (int64_t)T * a.ldp;
   a.plan = base + L.plan;
   a.warm_key = 0x7fc00001;  // a NaN pattern folded with row offsets: never equal in practice
+  a.id_map = ids ? id_map : nullptr;
+  a.id_map_n = id_map_n;
   const bool with_ids = ids != nullptr;
   const size_t lds = shrink_lds_bytes(T, s.n, s.r_max, with_ids);
   const int64_t items = max_sub * sp.S_max;

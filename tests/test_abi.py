@@ -270,7 +270,7 @@ def test_jd_workspace_bytes(lib):
     j = _jd()
     T = 100
     up = lambda v: -(-v // 256) * 256
-    want = up(T * 4) + up(T * 8 * 4) + lib.lora_workspace_bytes(C.byref(j.basis), T)
+    want = up(T * 8 * 4) + lib.lora_workspace_bytes(C.byref(j.basis), T)
     assert lib.lora_jd_workspace_bytes(C.byref(j), T) == want
     assert lib.lora_jd_workspace_bytes(None, T) == 0
     bad = _jd()
