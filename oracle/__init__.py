@@ -16,6 +16,8 @@ sources define (float64 unless stated, Python loops over tokens):
                      floating-point result is compared bit for bit
 * ``jd_apply_ref`` - the shared-basis apply y = y0 + s_a U_c Sigma_a V_c^T x
 * ``jd_brute_force`` - the same in exact rational arithmetic, two orders
+* ``uniform_ranks_ref``, ``spectral_ranks_ref`` - retained-rank allocation
+                     (uniform ratio with a floor; spectral budget)
 
 Parity status: every function here is pinned by tests in
 ``tests/test_oracle.py`` (closed forms, invariants, brute force, library
@@ -30,3 +32,4 @@ from .lora_ref import (  # noqa: F401
     shrink_error_bound,
 )
 from .jd_ref import jd_apply_ref, jd_brute_force  # noqa: F401,E402
+from .rank_ref import captured_energy_ref, spectral_ranks_ref, uniform_ranks_ref  # noqa: F401,E402

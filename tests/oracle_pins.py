@@ -344,3 +344,88 @@ def pin_jd_cluster_relabel(fn):
 
 JD_PINS = [pin_jd_merged_weight, pin_jd_diag_is_lora, pin_jd_exact_reconstruction, pin_jd_brute_force,
            pin_jd_zero_scale_invalid, pin_jd_cluster_relabel]
+
+
+# ------------------------------------------------------------ rank policies
+# Retained-rank allocation (LoRAForge core design section: uniform ratio with
+# a floor, spectral budget).  Pins take (uniform_fn, spectral_fn).
+
+def _rank_units(seed, n=12, r_hi=16):
+    rng = np.random.default_rng(seed)
+    r_orig = [int(v) for v in rng.integers(1, r_hi + 1, size=n)]
+    sig = [sorted(rng.gamma(2.0, 1.0, size=r).tolist(), reverse=True) for r in r_orig]
+    return r_orig, sig
+
+
+def _energy(r, sig):
+    return sum(sum(s * s for s in sig[u][: r[u]]) for u in range(len(r)))
+
+
+def pin_uniform_closed_form(uniform_fn, spectral_fn):
+    """ratio 1 keeps every rank, ratio 0 keeps the floor (or all if fewer),
+    and the fleet reading: 64 ranks at 1/12 with floor 4 keep 6."""
+    assert list(uniform_fn([64, 16, 3], 1.0, 4)) == [64, 16, 3]
+    assert list(uniform_fn([64, 16, 3], 0.0, 4)) == [4, 4, 3]
+    assert list(uniform_fn([64], 1 / 12, 4)) == [6]
+    assert list(uniform_fn([16, 10], 0.25, 1)) == [4, 3]
+
+
+def pin_spectral_budget_and_floors(uniform_fn, spectral_fn):
+    """The budget is met exactly (or every unit is at its original rank),
+    floors are kept, no unit exceeds its original rank."""
+    for seed in range(4):
+        r_orig, sig = _rank_units(seed)
+        for floor in (0, 2, 5):
+            lo = sum(min(floor, r) for r in r_orig)
+            for budget in (lo, lo + 7, lo + 30, sum(r_orig), sum(r_orig) + 9):
+                r = list(spectral_fn(r_orig, sig, floor, budget))
+                assert sum(r) == min(budget, sum(r_orig)), (seed, floor, budget)
+                assert all(min(floor, ro) <= v <= ro for v, ro in zip(r, r_orig))
+
+
+def pin_spectral_monotone(uniform_fn, spectral_fn):
+    """One more rank of budget adds exactly one rank to one unit."""
+    r_orig, sig = _rank_units(7)
+    prev = list(spectral_fn(r_orig, sig, 2, sum(min(2, r) for r in r_orig)))
+    for budget in range(sum(prev) + 1, sum(r_orig) + 1):
+        cur = list(spectral_fn(r_orig, sig, 2, budget))
+        diff = [c - p for c, p in zip(cur, prev)]
+        assert sorted(diff)[-1] == 1 and sum(diff) == 1 and min(diff) == 0, budget
+        prev = cur
+
+
+def pin_spectral_beats_uniform(uniform_fn, spectral_fn):
+    """At the uniform policy's total budget, the spectral allocation keeps at
+    least as much energy (the uniform allocation is one of its candidates)."""
+    for seed in range(5):
+        r_orig, sig = _rank_units(10 + seed, n=20, r_hi=32)
+        u = list(uniform_fn(r_orig, 0.3, 2))
+        s = list(spectral_fn(r_orig, sig, 2, sum(u)))
+        assert sum(s) == sum(u)
+        assert _energy(s, sig) >= _energy(u, sig) - 1e-12
+
+
+def pin_spectral_optimal_brute_force(uniform_fn, spectral_fn):
+    """On tiny fleets, the spectral allocation keeps the most energy of every
+    allocation with the same floors and total (exhaustive enumeration)."""
+    import itertools
+    for seed in range(3):
+        r_orig, sig = _rank_units(20 + seed, n=4, r_hi=5)
+        floor = 1
+        for budget in range(sum(min(floor, r) for r in r_orig), sum(r_orig) + 1):
+            best = max(_energy(list(c), sig) for c in itertools.product(*[range(min(floor, r), r + 1) for r in r_orig])
+                       if sum(c) == budget)
+            s = list(spectral_fn(r_orig, sig, floor, budget))
+            assert abs(_energy(s, sig) - best) <= 1e-12 * max(best, 1.0), (seed, budget)
+
+
+def pin_spectral_ties(uniform_fn, spectral_fn):
+    """Equal singular values everywhere: ranks go to the lower unit first."""
+    r_orig = [3, 3, 3]
+    sig = [[1.0, 1.0, 1.0]] * 3
+    assert list(spectral_fn(r_orig, sig, 0, 4)) == [3, 1, 0]
+    assert list(spectral_fn(r_orig, sig, 1, 4)) == [2, 1, 1]
+
+
+RANK_PINS = [pin_uniform_closed_form, pin_spectral_budget_and_floors, pin_spectral_monotone,
+             pin_spectral_beats_uniform, pin_spectral_optimal_brute_force, pin_spectral_ties]

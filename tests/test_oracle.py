@@ -92,3 +92,9 @@ def test_oracle_header_marks_test_infrastructure():
 def test_jd_pin(pin):
     from oracle import jd_apply_ref
     pin(jd_apply_ref)
+
+
+@pytest.mark.parametrize("pin", P.RANK_PINS, ids=lambda f: f.__name__)
+def test_rank_pin(pin):
+    from oracle import spectral_ranks_ref, uniform_ranks_ref
+    pin(uniform_ranks_ref, lambda r, s, f, b: spectral_ranks_ref(r, s, f, budget=b))

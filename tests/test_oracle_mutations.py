@@ -166,3 +166,47 @@ def test_jd_unmutated_copy_passes():
     fn = _jd_mutant("none")
     for pin in P.JD_PINS:
         pin(fn)
+
+
+def _rank_mutants(kind):
+    import math
+    from oracle import spectral_ranks_ref, uniform_ranks_ref
+
+    def uni(r_orig, ratio, floor):
+        if kind == "uniform_round":
+            return [min(r, max(floor, round(ratio * r))) for r in r_orig]
+        if kind == "uniform_no_floor":
+            return [min(r, math.ceil(ratio * r)) for r in r_orig]
+        if kind == "uniform_floor_beyond_rank":
+            return [max(floor, math.ceil(ratio * r)) for r in r_orig]
+        return uniform_ranks_ref(r_orig, ratio, floor)
+
+    def spec(r_orig, sig, floor, budget):
+        if kind == "spectral_smallest_first":
+            # 1/sigma is largest where sigma is smallest
+            return spectral_ranks_ref(r_orig, [[1.0 / (1e-9 + abs(v)) for v in s] for s in sig], floor, budget=budget)
+        if kind == "spectral_no_floor":
+            return spectral_ranks_ref(r_orig, sig, 0, budget=budget)
+        if kind == "spectral_budget_minus_one":
+            return spectral_ranks_ref(r_orig, sig, floor, budget=budget - 1)
+        if kind == "spectral_ties_high_first":
+            rev = spectral_ranks_ref(r_orig[::-1], sig[::-1], floor, budget=budget)
+            return rev[::-1]
+        return spectral_ranks_ref(r_orig, sig, floor, budget=budget)
+    return uni, spec
+
+
+RANK_MUTANTS = ["uniform_round", "uniform_no_floor", "uniform_floor_beyond_rank", "spectral_smallest_first",
+                "spectral_no_floor", "spectral_budget_minus_one", "spectral_ties_high_first"]
+
+
+@pytest.mark.parametrize("kind", RANK_MUTANTS)
+def test_rank_mutant_is_caught(kind):
+    uni, spec = _rank_mutants(kind)
+    caught = []
+    for pin in P.RANK_PINS:
+        try:
+            pin(uni, spec)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"rank-policy mutant {kind} passed every pin"
