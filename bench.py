@@ -46,6 +46,8 @@ WORKLOAD_NAMES = {
                "full 16x16 Sigma per adapter, T=2048 Zipf(1.1) ids",
     "jd-diag": "shared-basis decode (JD-Diag): d_in=d_out=4096 bf16, 1024 adapters in 32 clusters of rank 16, "
                "diagonal Sigma per adapter, T=2048 Zipf(1.1) ids",
+    "ranks-fleet": "retained-rank allocation on the host: 1024 adapters x 196 modules (200704 units) of "
+                   "original rank 64, uniform (ratio 1/12, floor 4) and spectral at the same budget",
     "5U": "fleet decode step: 28 layers x 7 projections (3584/512/18944 dims) bf16, 1024 adapters rank 6 "
           "(orig 64), T=4096 Zipf(1.1) ids, one grouping reused by 196 applies",
     "5S": "fleet decode step: 28 layers x 7 projections (3584/512/18944 dims) bf16, 1024 adapters ranks "
@@ -405,6 +407,47 @@ def run_jd(args, rs, torch, dev, key):
     print(json.dumps(out), flush=True)
 
 
+def run_ranks(args):
+    """Host timing of the rank policies at fleet scale (no GPU work)."""
+    import rank_specialized_amd as rs
+    from oracle import spectral_ranks_ref
+    rng = np.random.default_rng(5)
+    m, r = 1024 * 196, 64
+    r_orig = [r] * m
+    # singular values of a rank-64 adapter product: a decaying spectrum, per unit
+    sig = np.sort(rng.gamma(2.0, 1.0, size=(m, r)).astype(np.float32) *
+                  np.exp(-np.arange(r) / 16.0).astype(np.float32), axis=1)[:, ::-1].copy()
+    sig_list = list(sig)
+    t0 = time.perf_counter()
+    u = rs.lora_ranks_uniform(r_orig, 1 / 12, 4)
+    t_u = time.perf_counter() - t0
+    budget = sum(u)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        s = rs.lora_ranks_spectral(r_orig, sig_list, 4, budget)
+        reps += 1
+        if time.perf_counter() - t0 > 2.0:
+            break
+    t_s = (time.perf_counter() - t0) / reps
+    e_u = float(sum((sig[i, : u[i]].astype(np.float64) ** 2).sum() for i in range(0, m, 97)))
+    e_s = float(sum((sig[i, : s[i]].astype(np.float64) ** 2).sum() for i in range(0, m, 97)))
+    ms_o = 64
+    t0 = time.perf_counter()
+    spectral_ranks_ref(r_orig[:ms_o], [x.astype(np.float64) for x in sig_list[:ms_o]], 4,
+                       budget=sum(u[:ms_o]))
+    t_o = time.perf_counter() - t0
+    print(json.dumps({
+        "metric": "retained-rank allocation units per second (host, one thread)", "value": round(m / t_s, 1),
+        "unit": "units/s", "n_gpus": 0, "ms_per_step": round(t_s * 1e3, 3), "higher_is_better": True,
+        "config": {"workload": WORKLOAD_NAMES["ranks-fleet"], "units": m, "r_orig": r, "budget": budget},
+        "uniform_ms": round(t_u * 1e3, 3), "spectral_ms": round(t_s * 1e3, 3),
+        "spectral_rank_range": [int(min(s)), int(max(s))],
+        "energy_kept_sampled": {"uniform": round(e_u, 1), "spectral": round(e_s, 1)},
+        "cpu_baseline": {"value": round(ms_o / t_o, 1), "unit": "units/s", "cores": 1, "kind": "oracle",
+                         "sample": f"first {ms_o} units, the oracle's repeated greedy selection"},
+    }), flush=True)
+
+
 def cpu_baseline(wl, seconds: float):
     """The CPU oracle as it stands, on a bounded sample of the same workload,
     with BLAS pinned to one thread."""
@@ -599,6 +642,9 @@ def main():
     args = parse_args()
     if args.summarize_pmc:
         summarize_pmc(args.config, *args.summarize_pmc)
+        return
+    if args.config == "ranks-fleet":
+        run_ranks(args)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; the apply's sharding across GPUs "

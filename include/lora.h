@@ -315,6 +315,29 @@ size_t lora_jd_workspace_bytes(const lora_jd_store* store_host, int T);
 int lora_jd_apply(const lora_jd_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy, int T,
                   const int32_t* ids, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Retained-rank allocation (host only, nothing enqueued): how many ranks each
+ * of m units (one adapter of one module: a factor pair of original rank
+ * r_orig[u]) keeps after compression.  "LoRAForge" core design section: a
+ * uniform ratio with a floor, or a spectral budget that keeps the
+ * components carrying the most energy (sigma^2).
+ *
+ * lora_ranks_uniform:  r[u] = min(r_orig[u], max(floor, ceil(ratio r_orig[u]))),
+ *   0 <= ratio <= 1.
+ * lora_ranks_spectral: every unit first keeps min(floor, r_orig[u]); the rest
+ *   of `budget` (total ranks over all units) goes one rank at a time to the
+ *   unit whose next singular value is largest (ties: the lower unit), never
+ *   beyond r_orig[u].  sigma: the units' singular values end to end, unit u
+ *   at sigma[sigma_off[u] .. sigma_off[u+1]) with sigma_off[u+1] -
+ *   sigma_off[u] = r_orig[u], each unit's values finite, >= 0 and
+ *   non-increasing (as an SVD gives them).
+ * Errors: INVALID_ARG (null pointers with m > 0, negative sizes, ratio
+ * outside [0, 1], sigma inconsistent with r_orig or not non-increasing).
+ */
+int lora_ranks_uniform(int m, const int32_t* r_orig_host, double ratio, int floor_rank, int32_t* r_out_host);
+int lora_ranks_spectral(int m, const int32_t* r_orig_host, const float* sigma_host, const int64_t* sigma_off_host,
+                        int floor_rank, int64_t budget, int32_t* r_out_host);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ __all__ = [
     "Store", "Segmentation", "LoraError", "lora_store_bytes", "lora_pack_retained",
     "lora_segment", "lora_workspace_bytes", "lora_shrink", "lora_expand", "lora_apply_batched",
     "lora_apply_batched_phases", "lora_apply_launches", "JDStore", "lora_jd_pack", "lora_jd_workspace_bytes",
-    "lora_jd_apply", "load_library",
+    "lora_jd_apply", "lora_ranks_uniform", "lora_ranks_spectral", "load_library",
 ]
 
 _DTYPES = {torch.bfloat16: L.LORA_DTYPE_BF16, torch.float32: L.LORA_DTYPE_F32}
@@ -334,3 +334,28 @@ def lora_jd_apply(store: JDStore, x: torch.Tensor, y: torch.Tensor, ids: torch.T
     L.check("lora_jd_apply", L.lib().lora_jd_apply(store.ref(), _p(x), _rows(x, "x"), _p(y), _rows(y, "y"), T,
                                                    _p(ids), ws.data_ptr(), ws.numel(), _stream(x)))
     return y
+
+
+def lora_ranks_uniform(r_orig: Sequence[int], ratio: float, floor: int) -> List[int]:
+    """Retained ranks by a uniform ratio of the original rank, with a floor."""
+    m = len(r_orig)
+    ro = (C.c_int32 * max(m, 1))(*[int(v) for v in r_orig])
+    out = (C.c_int32 * max(m, 1))()
+    L.check("lora_ranks_uniform", L.lib().lora_ranks_uniform(m, ro, float(ratio), int(floor), out))
+    return list(out)[:m]
+
+
+def lora_ranks_spectral(r_orig: Sequence[int], sigmas, floor: int, budget: int) -> List[int]:
+    """Retained ranks by a spectral budget: floors first, then the largest
+    remaining singular values over all units, `budget` ranks in total."""
+    import numpy as np
+    m = len(r_orig)
+    ro = np.ascontiguousarray(np.asarray(r_orig, np.int32))
+    flat = np.ascontiguousarray(np.concatenate([np.asarray(s, np.float32) for s in sigmas]) if m else
+                                np.zeros(1, np.float32))
+    off = np.zeros(m + 1, np.int64)
+    off[1:] = np.cumsum(ro)
+    out = np.zeros(max(m, 1), np.int32)
+    L.check("lora_ranks_spectral", L.lib().lora_ranks_spectral(
+        m, ro.ctypes.data, flat.ctypes.data, off.ctypes.data, int(floor), int(budget), out.ctypes.data))
+    return [int(v) for v in out[:m]]

@@ -58,6 +58,8 @@ SIGNATURES = {
     "lora_apply_launches": (I, [C.POINTER(lora_store), I, I]),
     "lora_jd_workspace_bytes": (SZ, [C.POINTER(lora_jd_store), I]),
     "lora_jd_apply": (I, [C.POINTER(lora_jd_store), P, I64, P, I64, I, P, P, SZ, P]),
+    "lora_ranks_uniform": (I, [I, P, C.c_double, I, P]),
+    "lora_ranks_spectral": (I, [I, P, P, P, I, I64, P]),
 }
 
 _lib = None
