@@ -18,6 +18,8 @@ sources define (float64 unless stated, Python loops over tokens):
 * ``jd_brute_force`` - the same in exact rational arithmetic, two orders
 * ``uniform_ranks_ref``, ``spectral_ranks_ref`` - retained-rank allocation
                      (uniform ratio with a floor; spectral budget)
+* ``retained_factors_ref``, ``tall_skinny_r_ref`` - retained factors by the
+                     SVD of B A through thin QRs of B and A^T
 
 Parity status: every function here is pinned by tests in
 ``tests/test_oracle.py`` (closed forms, invariants, brute force, library
@@ -33,3 +35,4 @@ from .lora_ref import (  # noqa: F401
 )
 from .jd_ref import jd_apply_ref, jd_brute_force  # noqa: F401,E402
 from .rank_ref import captured_energy_ref, spectral_ranks_ref, uniform_ranks_ref  # noqa: F401,E402
+from .rsvd_ref import retained_factors_ref, rsvd_ref, tall_skinny_r_ref  # noqa: F401,E402

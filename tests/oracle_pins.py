@@ -429,3 +429,72 @@ def pin_spectral_ties(uniform_fn, spectral_fn):
 
 RANK_PINS = [pin_uniform_closed_form, pin_spectral_budget_and_floors, pin_spectral_monotone,
              pin_spectral_beats_uniform, pin_spectral_optimal_brute_force, pin_spectral_ties]
+
+
+# ------------------------------------------------- retained-factor (r-SVD) pins
+# Retained factors of one adapter by the SVD of B A through the thin QRs of B
+# and A^T (LoRAForge FlashTSQR section; Compress then Serve section 4).  Pins
+# take fn(A, B, k) -> (A', B', sigma) and, for R, r_fn(M) -> R.
+
+def _rsvd_factors(seed, r=8, d_in=40, d_out=30):
+    rng = np.random.default_rng(seed)
+    return rng.normal(size=(r, d_in)), rng.normal(size=(d_out, r))
+
+
+def pin_rsvd_eckart_young(fn):
+    """sigma equals the dense SVD of B A (numpy, on the d_out x d_in product),
+    and the rank-k residual's squared Frobenius norm is the sum of the
+    discarded sigma^2, for every k."""
+    for seed in range(3):
+        A, B = _rsvd_factors(seed)
+        dense = B @ A
+        sv = np.linalg.svd(dense, compute_uv=False)[: A.shape[0]]
+        for k in range(1, A.shape[0] + 1):
+            A2, B2, s = fn(A, B, k)
+            assert np.allclose(np.asarray(s), sv, rtol=1e-10, atol=1e-12 * sv[0]), seed
+            res = np.linalg.norm(dense - np.asarray(B2) @ np.asarray(A2)) ** 2
+            assert abs(res - float(np.sum(sv[k:] ** 2))) <= 1e-9 * float(np.sum(sv ** 2)), (seed, k)
+
+
+def pin_rsvd_orthonormal(fn):
+    """B' has orthonormal columns and A' A'^T = diag(sigma_k^2)."""
+    A, B = _rsvd_factors(5)
+    for k in (1, 4, 8):
+        A2, B2, s = fn(A, B, k)
+        B2, A2 = np.asarray(B2), np.asarray(A2)
+        assert np.allclose(B2.T @ B2, np.eye(k), atol=1e-10)
+        assert np.allclose(A2 @ A2.T, np.diag(np.asarray(s)[:k] ** 2), rtol=1e-10, atol=1e-9)
+
+
+def pin_rsvd_full_rank_exact(fn):
+    """Keeping every component reproduces B A."""
+    A, B = _rsvd_factors(6, r=6, d_in=20, d_out=25)
+    A2, B2, _ = fn(A, B, 6)
+    assert np.allclose(np.asarray(B2) @ np.asarray(A2), B @ A, rtol=1e-11, atol=1e-11)
+
+
+def pin_rsvd_worked_example(fn):
+    """By hand: B = [[3, 0], [0, 1], [0, 0]], A = [[1, 0, 0], [0, 2, 0]]
+    give B A = diag(3, 2, 0) (3 x 3 with a zero row and column): singular
+    values 3 and 2; keeping one, B' A' = diag(3, 0, 0)."""
+    B = np.array([[3.0, 0.0], [0.0, 1.0], [0.0, 0.0]])
+    A = np.array([[1.0, 0.0, 0.0], [0.0, 2.0, 0.0]])
+    A2, B2, s = fn(A, B, 1)
+    assert np.allclose(np.asarray(s), [3.0, 2.0], atol=1e-14)
+    assert np.allclose(np.asarray(B2) @ np.asarray(A2), np.diag([3.0, 0.0, 0.0]), atol=1e-14)
+
+
+def pin_tall_skinny_r(r_fn):
+    """R is upper triangular with a positive diagonal, R^T R = M^T M, and it
+    equals the transposed Cholesky factor of M^T M (numpy)."""
+    rng = np.random.default_rng(9)
+    for shape in ((50, 8), (200, 16), (16, 16)):
+        M = rng.normal(size=shape)
+        R = np.asarray(r_fn(M))
+        assert np.allclose(np.tril(R, -1), 0.0) and np.all(np.diag(R) > 0)
+        G = M.T @ M
+        assert np.allclose(R.T @ R, G, rtol=1e-12, atol=1e-10)
+        assert np.allclose(R, np.linalg.cholesky(G).T, rtol=1e-9, atol=1e-10)
+
+
+RSVD_PINS = [pin_rsvd_eckart_young, pin_rsvd_orthonormal, pin_rsvd_full_rank_exact, pin_rsvd_worked_example]

@@ -98,3 +98,14 @@ def test_jd_pin(pin):
 def test_rank_pin(pin):
     from oracle import spectral_ranks_ref, uniform_ranks_ref
     pin(uniform_ranks_ref, lambda r, s, f, b: spectral_ranks_ref(r, s, f, budget=b))
+
+
+@pytest.mark.parametrize("pin", P.RSVD_PINS, ids=lambda f: f.__name__)
+def test_rsvd_pin(pin):
+    from oracle import retained_factors_ref
+    pin(retained_factors_ref)
+
+
+def test_tall_skinny_r_pin():
+    from oracle import tall_skinny_r_ref
+    P.pin_tall_skinny_r(tall_skinny_r_ref)

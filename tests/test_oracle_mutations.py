@@ -210,3 +210,39 @@ def test_rank_mutant_is_caught(kind):
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f"rank-policy mutant {kind} passed every pin"
+
+
+def _rsvd_mutant(kind):
+    def fn(A, B, k):
+        A64, B64 = np.asarray(A, np.float64), np.asarray(B, np.float64)
+        Q_B, R_B = np.linalg.qr(B64)
+        Q_A, R_A = np.linalg.qr(A64.T)
+        core = R_B @ R_A if kind == "core_untransposed" else R_B @ R_A.T
+        U, s, Vt = np.linalg.svd(core)
+        if kind == "smallest_components":
+            U, s, Vt = U[:, ::-1], s[::-1], Vt[::-1, :]
+        B2 = Q_B @ U[:, :k]
+        A2 = (s[:k, None] * Vt[:k, :]) @ Q_A.T
+        if kind == "drop_sigma":
+            A2 = Vt[:k, :] @ Q_A.T
+        if kind == "sigma_on_both":
+            B2 = B2 * s[None, :k]
+        if kind == "no_q_a":
+            A2 = np.pad(s[:k, None] * Vt[:k, :], ((0, 0), (0, A64.shape[1] - Vt.shape[1])))
+        return A2, B2, s
+    return fn
+
+
+RSVD_MUTANTS = ["core_untransposed", "smallest_components", "drop_sigma", "sigma_on_both", "no_q_a"]
+
+
+@pytest.mark.parametrize("kind", RSVD_MUTANTS)
+def test_rsvd_mutant_is_caught(kind):
+    fn = _rsvd_mutant(kind)
+    caught = []
+    for pin in P.RSVD_PINS:
+        try:
+            pin(fn)
+        except (AssertionError, ValueError):
+            caught.append(pin.__name__)
+    assert caught, f"r-SVD mutant {kind} passed every pin"
