@@ -140,9 +140,12 @@ int lora_store_bytes(int n, int d_in, int d_out, int dtype, const int32_t* ranks
  *                     lora_store_bytes returns, 16-byte aligned.
  *   out_host        : filled on success (references A_pack, B_pack, meta).
  * Copies the factors (bit-exact), writes zeros where pad_to pads, and
- * writes row_off / rank / scale into meta.  Synchronizes `stream` before
- * returning.  Errors: as lora_store_bytes, plus INVALID_ARG for null buffers
- * or a null factor pointer with r_a > 0.
+ * writes row_off / rank / scale into meta.  With A_ptrs_host and B_ptrs_host
+ * both NULL, only meta and *out_host are written and A_pack / B_pack are left
+ * as they are (for lora_rsvd_write to fill).  Synchronizes `stream` before
+ * returning.  Errors: as lora_store_bytes, plus INVALID_ARG for null buffers,
+ * one pointer array NULL and not the other, or a null factor pointer with
+ * r_a > 0.
  */
 int lora_pack_retained(lora_store* out_host, int n, int d_in, int d_out, int dtype,
                        const int32_t* ranks_host, const float* scales_host,
@@ -337,6 +340,51 @@ int lora_jd_apply(const lora_jd_store* store_host, const void* x, int64_t ldx, v
 int lora_ranks_uniform(int m, const int32_t* r_orig_host, double ratio, int floor_rank, int32_t* r_out_host);
 int lora_ranks_spectral(int m, const int32_t* r_orig_host, const float* sigma_host, const int64_t* sigma_off_host,
                         int floor_rank, int64_t budget, int32_t* r_out_host);
+
+/*
+ * Retained-factor construction (r-SVD), batched over the n adapters of one
+ * module that share an original rank r.  "LoRAForge" post-hoc compression
+ * decomposes each adapter's original factors into retained ones, with a
+ * tall-and-skinny QR of row blocks merged afterwards, parallel over adapters
+ * and row blocks (section "FlashTSQR: An Accelerator for Batched Factor
+ * Construction"); "Compress then Serve" section 4: alone, an adapter's best
+ * rank-k replacement is the rank-k SVD of B A.  With B = Q_B R_B, A^T = Q_A
+ * R_A and the core R_B R_A^T = U S V^T, the retained factors are
+ * B' = Q_B U_k = B (R_B^-1 U_k) and A' = S_k V_k^T Q_A^T = (R_A^-1 V_k S_k)^T A:
+ * B' has orthonormal columns and B' A' is the best rank-k approximation of
+ * B A.  R comes from the Gram matrix M^T M in float64 (the Cholesky form of
+ * the QR: one pass over the rows; accurate while cond(B), cond(A) stay well
+ * below 1e7).
+ *
+ * lora_rsvd_workspace_bytes: bytes of ws for n adapters (host only; 0 on
+ *   invalid arguments).  Holds W_B, W_A between the two calls below.
+ * lora_rsvd_factor: stage 1, enqueued on `stream`.
+ *   A_all  : device [n][r][d_in] (each A_a row-major), dtype elements.
+ *   B_all  : device [n][d_out][r] (each B_a row-major).
+ *   sigma  : out, device float32 [n][r]: the singular values of each B_a A_a,
+ *            descending.
+ *   status : out, device int32 [n]: 0, or 1 when a pivot of the Cholesky of
+ *            B_a^T B_a or A_a A_a^T fell to 1e-14 of its largest diagonal
+ *            entry or below (a numerically rank-deficient factor; zero
+ *            factors give sigma = 0 and zero retained factors).
+ *   ws     : device, 16-byte aligned, at least lora_rsvd_workspace_bytes.
+ * lora_rsvd_write: stage 2.  Writes the retained factors of the same adapters
+ *   (A_all, B_all and ws as given to lora_rsvd_factor) into `store`, a store
+ *   of n = the same adapters, built by lora_pack_retained with both factor
+ *   pointer arrays NULL and each adapter's retained rank k_a (chosen, e.g.,
+ *   by lora_ranks_uniform or lora_ranks_spectral from sigma).  Adapter a gets
+ *   A' (k_a x d_in) and B' (d_out x k_a) at its row offset, rounded from
+ *   float64 through float32 to the store's dtype; components past r (k_a > r)
+ *   and padding up to the stored rank are zero.
+ * Errors: INVALID_ARG (null pointers, n < 0, d < 1, r < 1, workspace too
+ * small, an invalid store); UNSUPPORTED (r above LORA_MAX_RANK, d_in < r or
+ * d_out < r, unknown dtype, unaligned ws, n too large for one grid).
+ */
+size_t lora_rsvd_workspace_bytes(int n, int d_in, int d_out);
+int lora_rsvd_factor(int n, int d_in, int d_out, int dtype, int r, const void* A_all, const void* B_all,
+                     float* sigma, int32_t* status, void* ws, size_t ws_bytes, void* stream);
+int lora_rsvd_write(const lora_store* store_host, int r, const void* A_all, const void* B_all, const void* ws,
+                    size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -28,7 +28,8 @@ __all__ = [
     "Store", "Segmentation", "LoraError", "lora_store_bytes", "lora_pack_retained",
     "lora_segment", "lora_workspace_bytes", "lora_shrink", "lora_expand", "lora_apply_batched",
     "lora_apply_batched_phases", "lora_apply_launches", "JDStore", "lora_jd_pack", "lora_jd_workspace_bytes",
-    "lora_jd_apply", "lora_ranks_uniform", "lora_ranks_spectral", "load_library",
+    "lora_jd_apply", "lora_ranks_uniform", "lora_ranks_spectral", "RsvdFactors", "lora_rsvd_workspace_bytes",
+    "lora_rsvd_factor", "lora_rsvd_write", "load_library",
 ]
 
 _DTYPES = {torch.bfloat16: L.LORA_DTYPE_BF16, torch.float32: L.LORA_DTYPE_F32}
@@ -132,19 +133,24 @@ def lora_pack_retained(A_list: Sequence[torch.Tensor], B_list: Sequence[torch.Te
             raise ValueError("factor shapes/dtypes are inconsistent")
         if not (a.is_contiguous() and b.is_contiguous()):
             raise ValueError("factors must be contiguous")
+    return _pack(n, d_in, d_out, dtype, ranks, scales, pad_to, device,
+                 (C.c_void_p * n)(*[_p(a) for a in A_list]), (C.c_void_p * n)(*[_p(b) for b in B_list]))
+
+
+def _pack(n, d_in, d_out, dtype, ranks, scales, pad_to, device, a_ptrs, b_ptrs) -> Store:
+    """Allocate a store's buffers and call lora_pack_retained (a_ptrs and
+    b_ptrs None: metadata only)."""
     a_bytes, b_bytes, m_bytes = lora_store_bytes(n, d_in, d_out, dtype, ranks, pad_to)
     A_pack = torch.empty(max(a_bytes, 16), dtype=torch.uint8, device=device)
     B_pack = torch.empty(max(b_bytes, 16), dtype=torch.uint8, device=device)
     meta = torch.empty(m_bytes, dtype=torch.uint8, device=device)
     r_arr = (C.c_int32 * n)(*ranks)
     s_arr = (C.c_float * n)(*[float(v) for v in scales])
-    a_ptrs = (C.c_void_p * n)(*[_p(a) for a in A_list])
-    b_ptrs = (C.c_void_p * n)(*[_p(b) for b in B_list])
     st = lora_store()
     L.check("lora_pack_retained", L.lib().lora_pack_retained(
         C.byref(st), n, d_in, d_out, _DTYPES[dtype], r_arr, s_arr, a_ptrs, b_ptrs,
         A_pack.data_ptr(), B_pack.data_ptr(), meta.data_ptr(), pad_to, _stream(meta)))
-    return Store(st, A_pack, B_pack, meta, ranks, dtype)
+    return Store(st, A_pack, B_pack, meta, list(ranks), dtype)
 
 
 @dataclass
@@ -359,3 +365,63 @@ def lora_ranks_spectral(r_orig: Sequence[int], sigmas, floor: int, budget: int) 
     L.check("lora_ranks_spectral", L.lib().lora_ranks_spectral(
         m, ro.ctypes.data, flat.ctypes.data, off.ctypes.data, int(floor), int(budget), out.ctypes.data))
     return [int(v) for v in out[:m]]
+
+
+@dataclass
+class RsvdFactors:
+    """What lora_rsvd_factor leaves for lora_rsvd_write: the original factors
+    (kept referenced), the singular values, the status flags and the
+    workspace holding W_B, W_A."""
+
+    A_all: torch.Tensor  # [n, r, d_in]
+    B_all: torch.Tensor  # [n, d_out, r]
+    sigma: torch.Tensor  # float32 [n, r], descending
+    status: torch.Tensor  # int32 [n]
+    ws: torch.Tensor
+
+    @property
+    def n(self) -> int:
+        return self.A_all.shape[0]
+
+    @property
+    def r(self) -> int:
+        return self.A_all.shape[1]
+
+
+def lora_rsvd_workspace_bytes(n: int, d_in: int, d_out: int) -> int:
+    return int(L.lib().lora_rsvd_workspace_bytes(n, d_in, d_out))
+
+
+def lora_rsvd_factor(A_all: torch.Tensor, B_all: torch.Tensor, ws: Optional[torch.Tensor] = None) -> RsvdFactors:
+    """Stage 1 of retained-factor construction for n adapters of one rank r:
+    A_all [n, r, d_in], B_all [n, d_out, r] (contiguous, bf16 or float32)."""
+    if A_all.dim() != 3 or B_all.dim() != 3:
+        raise ValueError("A_all is [n, r, d_in] and B_all [n, d_out, r]")
+    n, r, d_in = A_all.shape
+    d_out = B_all.shape[1]
+    if B_all.shape != (n, d_out, r) or A_all.dtype != B_all.dtype:
+        raise ValueError("A_all and B_all are inconsistent")
+    if not (A_all.is_contiguous() and B_all.is_contiguous()):
+        raise ValueError("factors must be contiguous")
+    sigma = torch.empty(n, r, dtype=torch.float32, device=A_all.device)
+    status = torch.empty(n, dtype=torch.int32, device=A_all.device)
+    if ws is None:
+        ws = torch.empty(max(lora_rsvd_workspace_bytes(n, d_in, d_out), 16), dtype=torch.uint8, device=A_all.device)
+    L.check("lora_rsvd_factor", L.lib().lora_rsvd_factor(
+        n, d_in, d_out, _DTYPES[A_all.dtype], r, _p(A_all), _p(B_all), _p(sigma), _p(status), ws.data_ptr(),
+        ws.numel(), _stream(A_all)))
+    return RsvdFactors(A_all, B_all, sigma, status, ws)
+
+
+def lora_rsvd_write(f: RsvdFactors, ranks: Sequence[int], scales, pad_to: int = 0) -> Store:
+    """Stage 2: a store of the retained factors at `ranks` (one per adapter,
+    e.g. from lora_ranks_uniform / lora_ranks_spectral over f.sigma)."""
+    n, r, d_in = f.A_all.shape
+    d_out = f.B_all.shape[1]
+    ranks = [int(v) for v in ranks]
+    if len(ranks) != n:
+        raise ValueError("one retained rank per adapter")
+    store = _pack(n, d_in, d_out, f.A_all.dtype, ranks, scales, pad_to, f.A_all.device, None, None)
+    L.check("lora_rsvd_write", L.lib().lora_rsvd_write(store.ref(), r, _p(f.A_all), _p(f.B_all), f.ws.data_ptr(),
+                                                       f.ws.numel(), _stream(f.A_all)))
+    return store

@@ -60,6 +60,9 @@ SIGNATURES = {
     "lora_jd_apply": (I, [C.POINTER(lora_jd_store), P, I64, P, I64, I, P, P, SZ, P]),
     "lora_ranks_uniform": (I, [I, P, C.c_double, I, P]),
     "lora_ranks_spectral": (I, [I, P, P, P, I, I64, P]),
+    "lora_rsvd_workspace_bytes": (SZ, [I, I, I]),
+    "lora_rsvd_factor": (I, [I, I, I, I, I, P, P, P, P, P, SZ, P]),
+    "lora_rsvd_write": (I, [C.POINTER(lora_store), I, P, P, P, SZ, P]),
 }
 
 _lib = None

@@ -59,12 +59,16 @@ int lora_pack_retained(lora_store* out_host, int n, int d_in, int d_out, int dty
   int64_t rows = 0;
   int st = check_store_shape(n, d_in, d_out, dtype, ranks_host, pad_to, &r_max, &rows);
   if (st != LORA_OK) return st;
-  if (!A_ptrs_host || !B_ptrs_host) return LORA_ERR_INVALID_ARG;
+  // Both pointer arrays NULL: metadata only, the factors are written later
+  // (lora_rsvd_write).
+  const bool meta_only = !A_ptrs_host && !B_ptrs_host;
+  if (!meta_only && (!A_ptrs_host || !B_ptrs_host)) return LORA_ERR_INVALID_ARG;
   if (rows > 0 && (!A_pack || !B_pack)) return LORA_ERR_INVALID_ARG;
   if (!aligned16(meta) || (A_pack && !aligned16(A_pack)) || (B_pack && !aligned16(B_pack)))
     return LORA_ERR_UNSUPPORTED;
-  for (int a = 0; a < n; ++a)
-    if (ranks_host[a] > 0 && (!A_ptrs_host[a] || !B_ptrs_host[a])) return LORA_ERR_INVALID_ARG;
+  if (!meta_only)
+    for (int a = 0; a < n; ++a)
+      if (ranks_host[a] > 0 && (!A_ptrs_host[a] || !B_ptrs_host[a])) return LORA_ERR_INVALID_ARG;
 
   // Host image of the meta buffer.
   std::vector<char> img(meta_bytes(n), 0);
@@ -80,14 +84,16 @@ int lora_pack_retained(lora_store* out_host, int n, int d_in, int d_out, int dty
     true_rank[a] = ranks_host[a];
     scale[a] = scales_host[a];
     row_off[a + 1] = row_off[a] + stored;
-    ptrs[a] = A_ptrs_host[a];
-    ptrs[n + a] = B_ptrs_host[a];
+    ptrs[a] = meta_only ? nullptr : A_ptrs_host[a];
+    ptrs[n + a] = meta_only ? nullptr : B_ptrs_host[a];
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipMemcpyAsync(meta, img.data(), img.size(), hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return hip_fail(e);
-  e = launch_pack(dtype, meta, n, d_in, d_out, (int)rows, A_pack, B_pack, s);
-  if (e != hipSuccess) return hip_fail(e);
+  if (!meta_only) {
+    e = launch_pack(dtype, meta, n, d_in, d_out, (int)rows, A_pack, B_pack, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
   e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e);
 
@@ -263,6 +269,49 @@ int lora_apply_batched_phases(const lora_store* store_host, const void* x, int64
                               int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm, void* ws,
                               size_t ws_bytes, void* stream, int phases) {
   return apply_impl(store_host, x, ldx, y, ldy, T, ids, seg_off, perm, ws, ws_bytes, stream, phases);
+}
+
+size_t lora_rsvd_workspace_bytes(int n, int d_in, int d_out) {
+  if (n < 0 || d_in < 1 || d_out < 1) return 0;
+  return rsvd_workspace_bytes(n, d_in, d_out);
+}
+
+static int check_rsvd(int n, int d_in, int d_out, int dtype, int r) {
+  if (n < 0 || d_in < 1 || d_out < 1 || r < 1) return LORA_ERR_INVALID_ARG;
+  if (dtype != LORA_DTYPE_BF16 && dtype != LORA_DTYPE_F32) return LORA_ERR_UNSUPPORTED;
+  if (r > LORA_MAX_RANK || d_in < r || d_out < r) return LORA_ERR_UNSUPPORTED;
+  // Grids (workgroups of 256 threads) stay below 2^32 threads.
+  const int64_t wgs = (int64_t)n * (2 * 4 + (d_in + 255) / 256 + (d_out + 255) / 256);
+  if (wgs * 256 >= ((int64_t)1 << 32)) return LORA_ERR_UNSUPPORTED;
+  return LORA_OK;
+}
+
+int lora_rsvd_factor(int n, int d_in, int d_out, int dtype, int r, const void* A_all, const void* B_all,
+                     float* sigma, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_rsvd(n, d_in, d_out, dtype, r);
+  if (st != LORA_OK) return st;
+  if (n == 0) return LORA_OK;
+  if (!A_all || !B_all || !sigma || !status || !ws) return LORA_ERR_INVALID_ARG;
+  if (ws_bytes < rsvd_workspace_bytes(n, d_in, d_out)) return LORA_ERR_INVALID_ARG;
+  if (!aligned16(ws)) return LORA_ERR_UNSUPPORTED;
+  hipError_t e = launch_rsvd_factor(n, d_in, d_out, dtype, r, A_all, B_all, sigma, status, ws,
+                                    reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LORA_OK : hip_fail(e);
+}
+
+int lora_rsvd_write(const lora_store* store_host, int r, const void* A_all, const void* B_all, const void* ws,
+                    size_t ws_bytes, void* stream) {
+  int st = check_store(store_host);
+  if (st != LORA_OK) return st;
+  const lora_store& s = *store_host;
+  st = check_rsvd(s.n, s.d_in, s.d_out, s.dtype, r);
+  if (st != LORA_OK) return st;
+  if (s.n == 0 || s.R == 0) return LORA_OK;
+  if (!A_all || !B_all || !ws) return LORA_ERR_INVALID_ARG;
+  if (ws_bytes < rsvd_workspace_bytes(s.n, s.d_in, s.d_out)) return LORA_ERR_INVALID_ARG;
+  if (!aligned16(ws)) return LORA_ERR_UNSUPPORTED;
+  hipError_t e = launch_rsvd_write(s, r, A_all, B_all, ws, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? LORA_OK : hip_fail(e);
 }
 
 }  // extern "C"

@@ -107,6 +107,11 @@ def test_pack_rejects_before_launch(lib):
     assert f(C.byref(st), 2, 64, 64, 1, r, s, ptrs, ptrs, FAKE, FAKE, None, 0, None) == 1
     assert f(C.byref(st), 2, 64, 64, 1, r, s, ptrs, ptrs, FAKE + 4, FAKE, FAKE, 0, None) == 2
     assert f(C.byref(st), 2, 64, 64, 1, r, s, ptrs, ptrs, FAKE, FAKE, FAKE, 2, None) == 1
+    # metadata only takes both pointer arrays NULL, not one of them
+    assert f(C.byref(st), 2, 64, 64, 1, r, s, None, ptrs, FAKE, FAKE, FAKE, 0, None) == 1
+    assert f(C.byref(st), 2, 64, 64, 1, r, s, ptrs, None, FAKE, FAKE, FAKE, 0, None) == 1
+    assert f(C.byref(st), 2, 64, 64, 1, r, s, None, None, None, FAKE, FAKE, 0, None) == 1
+    assert f(C.byref(st), 2, 64, 64, 1, r, s, None, None, FAKE, FAKE, None, 0, None) == 1
 
 
 def test_segment_rejects_before_launch(lib):
@@ -302,3 +307,58 @@ def test_jd_apply_rejects_before_launch(lib):
     assert call(j=_jd(r=65)) == 2
     assert call(j=_jd(k=5000, n=6000)) == 2  # more clusters than the in-kernel grouping takes
     assert call(T=L.LORA_SEGMENT_MAX_T + 1) == 2
+
+
+def _rsvd_ws(n, d_in, d_out):
+    blocks = min(4, -(-max(d_in, d_out) // 64))
+    return n * (2 * blocks + 2) * 64 * 64 * 8
+
+
+@pytest.mark.parametrize("n,d_in,d_out", [(1, 16, 16), (1024, 3584, 3584), (7, 520, 264), (3, 64, 200),
+                                          (0, 64, 64)])
+def test_rsvd_workspace_bytes(lib, n, d_in, d_out):
+    assert lib.lora_rsvd_workspace_bytes(n, d_in, d_out) == _rsvd_ws(n, d_in, d_out)
+
+
+def test_rsvd_workspace_bytes_invalid(lib):
+    assert lib.lora_rsvd_workspace_bytes(-1, 64, 64) == 0
+    assert lib.lora_rsvd_workspace_bytes(4, 0, 64) == 0
+    assert lib.lora_rsvd_workspace_bytes(4, 64, 0) == 0
+
+
+def test_rsvd_factor_rejects_before_launch(lib):
+    f = lib.lora_rsvd_factor
+    big = 1 << 40
+
+    def call(n=4, d_in=256, d_out=128, dtype=1, r=16, A=FAKE, B=FAKE, sig=FAKE, st=FAKE, ws=FAKE, wsb=big):
+        return f(n, d_in, d_out, dtype, r, A, B, sig, st, ws, wsb, None)
+
+    assert call(n=0) == 0
+    assert call(n=-1) == 1
+    assert call(r=0) == 1
+    assert call(d_in=0) == 1
+    assert call(r=65) == 2
+    assert call(d_in=15) == 2  # fewer rows than the rank
+    assert call(d_out=8) == 2
+    assert call(dtype=7) == 2
+    for k in ("A", "B", "sig", "st", "ws"):
+        assert call(**{k: None}) == 1
+    assert call(wsb=_rsvd_ws(4, 256, 128) - 1) == 1
+    assert call(ws=FAKE + 8) == 2
+    assert call(n=1 << 22) == 2  # grid too large
+
+
+def test_rsvd_write_rejects_before_launch(lib):
+    f = lib.lora_rsvd_write
+    big = 1 << 40
+    st = _store(n=4, d_in=64, d_out=32, r_max=8)
+    assert f(None, 8, FAKE, FAKE, FAKE, big, None) == 1
+    assert f(C.byref(st), 0, FAKE, FAKE, FAKE, big, None) == 1
+    assert f(C.byref(st), 33, FAKE, FAKE, FAKE, big, None) == 2  # d_out below r
+    assert f(C.byref(st), 8, None, FAKE, FAKE, big, None) == 1
+    assert f(C.byref(st), 8, FAKE, None, FAKE, big, None) == 1
+    assert f(C.byref(st), 8, FAKE, FAKE, None, big, None) == 1
+    assert f(C.byref(st), 8, FAKE, FAKE, FAKE, _rsvd_ws(4, 64, 32) - 1, None) == 1
+    assert f(C.byref(st), 8, FAKE, FAKE, FAKE + 8, big, None) == 2
+    empty = _store(n=4, d_in=64, d_out=32, r_max=0, R=0)
+    assert f(C.byref(empty), 8, None, None, None, 0, None) == 0

@@ -26,3 +26,4 @@ from .configs import (  # noqa: F401
     zipf_ids,
 )
 from .jd import JD_CONFIGS, JDWorkload, make_jd_config, make_jd_workload  # noqa: F401,E402
+from .rsvd import RSVD_CONFIGS, RsvdWorkload, make_rsvd_config, make_rsvd_workload  # noqa: F401,E402
