@@ -34,7 +34,9 @@ sys.path.insert(0, ROOT)
 METRIC = "LoRA-delta tokens/s and achieved HBM GB/s (% of ~8 TB/s peak), 1 MI355X"
 PEAK_GBPS = 8000.0
 COLD_BYTES = 2.0e9  # rotation set size: well past the 256 MB Infinity Cache
-KERNEL_SOURCES = ["shrink.hip", "expand.hip", "decode.hip", "jd.hip", "tile_ops.h", "device_common.h", "plan.h"]
+KERNEL_SOURCES = ["shrink.hip", "expand.hip", "decode.hip", "jd.hip", "rsvd.hip", "tile_ops.h", "device_common.h",
+                  "plan.h"]
+PEAK_FP64_TFLOPS = 78.6  # 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2.4 GHz
 
 WORKLOAD_NAMES = {
     "1": "tiny-fp32: d_in=d_out=256 f32, 4 adapters ranks {1,2,3,4}, T=16",
@@ -46,6 +48,8 @@ WORKLOAD_NAMES = {
                "full 16x16 Sigma per adapter, T=2048 Zipf(1.1) ids",
     "jd-diag": "shared-basis decode (JD-Diag): d_in=d_out=4096 bf16, 1024 adapters in 32 clusters of rank 16, "
                "diagonal Sigma per adapter, T=2048 Zipf(1.1) ids",
+    "rsvd-q": "retained-factor construction (r-SVD through tall-skinny QR): 1024 adapters of rank 64 of one "
+              "3584->3584 projection, bf16, spectral-budget ranks (floor 4, budget 6 per adapter)",
     "ranks-fleet": "retained-rank allocation on the host: 1024 adapters x 196 modules (200704 units) of "
                    "original rank 64, uniform (ratio 1/12, floor 4) and spectral at the same budget",
     "5U": "fleet decode step: 28 layers x 7 projections (3584/512/18944 dims) bf16, 1024 adapters rank 6 "
@@ -407,6 +411,103 @@ def run_jd(args, rs, torch, dev, key):
     print(json.dumps(out), flush=True)
 
 
+def rsvd_algorithmic(n: int, r: int, d_in: int, d_out: int, keep_total: int, e: int):
+    """Algorithmic work of retained-factor construction: the Grams B^T B and
+    A A^T (symmetric: r (r + 1) / 2 entries of d multiply-adds, r (r + 1) d
+    flops each), reading every factor once; the write reads them once more
+    (the retained factors depend on all rows) and forms k_a columns of B' and
+    rows of A' (2 r k_a d flops)."""
+    d = d_in + d_out
+    return {"gram_flops": n * r * (r + 1) * d, "gram_bytes": n * r * d * e,
+            "write_flops": 2 * r * keep_total * d, "write_bytes": n * r * d * e + keep_total * d * e}
+
+
+def run_rsvd(args, rs, torch, dev, key):
+    from workloads import make_rsvd_config
+    t0 = time.perf_counter()
+    w = make_rsvd_config(key)
+    print(f"[rsvd] inputs drawn in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    dt = torch.bfloat16
+    A = torch.from_numpy(w.A).to(dev).to(dt)
+    B = torch.from_numpy(w.B).to(dev).to(dt)
+    f = rs.lora_rsvd_factor(A, B)
+    torch.cuda.synchronize()
+    sig = f.sigma.cpu().numpy()
+    bad = int(f.status.cpu().numpy().sum())
+    r_orig = [w.r] * w.n
+    budget = sum(rs.lora_ranks_uniform(r_orig, 1.0 / 12.0, 4))
+    t0 = time.perf_counter()
+    ranks = rs.lora_ranks_spectral(r_orig, list(sig), 4, budget)
+    policy_ms = 1e3 * (time.perf_counter() - t0)
+    store = rs.lora_rsvd_write(f, ranks, w.scales)
+    torch.cuda.synchronize()
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def step():
+        rs.lora_rsvd_factor(A, B, out=f)
+        rs.lora_rsvd_write(f, None, None, store=store)
+
+    steps, warmup = args.steps, args.warmup
+    ms = timed(step, steps, warmup)
+    kern = {name: timed(lambda ph=ph: rs.lora_rsvd_factor(A, B, phases=ph, out=f), steps, warmup)
+            for name, ph in (("rsvd_gram", 1), ("rsvd_prep", 2), ("rsvd_jacobi", 4), ("rsvd_post", 8))}
+    kern["rsvd_write"] = timed(lambda: rs.lora_rsvd_write(f, None, None, store=store), steps, warmup)
+    keep = int(sum(ranks))
+    alg = rsvd_algorithmic(w.n, w.r, w.d_in, w.d_out, keep, 2)
+    g_tf = alg["gram_flops"] / (kern["rsvd_gram"] * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import retained_factors_ref
+        try:
+            from threadpoolctl import threadpool_limits
+            limiter = threadpool_limits(1)
+        except Exception:  # pragma: no cover
+            limiter = None
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            a = reps % w.n
+            retained_factors_ref(w.A[a].astype(np.float64), w.B[a].astype(np.float64), ranks[a])
+            reps += 1
+        el = time.perf_counter() - t0
+        if limiter is not None:
+            limiter.unregister()
+        cpu = {"value": round(reps / el, 2), "unit": "adapters/s", "cores": 1, "kind": "oracle",
+               "sample": f"{reps} adapters in {el:.1f} s (numpy QR + SVD in float64 per adapter), BLAS pinned "
+                         "to 1 thread"}
+    roofline = {"bound": "alu", "achieved": round(g_tf, 2), "peak": PEAK_FP64_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(g_tf / PEAK_FP64_TFLOPS, 4), "traffic": None, "kernel": "rsvd_gram",
+                "algorithmic_flops_per_launch": alg["gram_flops"],
+                "avg_launch_us": round(kern["rsvd_gram"] * 1e3, 2)}
+    out = {
+        "metric": "retained-factor construction adapters/s (r-SVD through tall-skinny QR), 1 MI355X",
+        "value": round(w.n / (ms * 1e-3), 1), "unit": "adapters/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64",
+        "data": "synthetic: seeded N(0,1/sqrt(d)) factors, B columns scaled by (j+1)^-alpha, alpha~U(0,1.5), bf16",
+        "config": {"workload": WORKLOAD_NAMES[key], "n_adapters": w.n, "r": w.r, "d_in": w.d_in,
+                   "d_out": w.d_out, "retained_total": keep, "rank_range": [int(min(ranks)), int(max(ranks))]},
+        "kernels_avg_ms": {k: round(v, 4) for k, v in kern.items()},
+        "gram_tflops": round(g_tf, 2),
+        "algorithmic": alg, "roofline": roofline, "cpu_baseline": cpu, "status_flagged": bad,
+        "host_policy_ms": round(policy_ms, 3),
+        "write_gbps": round(alg["write_bytes"] / (kern["rsvd_write"] * 1e-3) / 1e9, 1),
+        "timed_as": "eager launches (a step: factor, i.e. Gram + core, then write), HIP events on the stream",
+        "kernel_sources_sha": kernel_source_digest(),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def run_ranks(args):
     """Host timing of the rank policies at fleet scale (no GPU work)."""
     import rank_specialized_amd as rs
@@ -670,6 +771,9 @@ def main():
         return
     if key.startswith("jd-"):
         run_jd(args, rs, torch, dev, key)
+        return
+    if key.startswith("rsvd-"):
+        run_rsvd(args, rs, torch, dev, key)
         return
     wl = build_workload(key)
     m = wl.module

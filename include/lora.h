@@ -349,16 +349,17 @@ int lora_ranks_spectral(int m, const int32_t* r_orig_host, const float* sigma_ho
  * and row blocks (section "FlashTSQR: An Accelerator for Batched Factor
  * Construction"); "Compress then Serve" section 4: alone, an adapter's best
  * rank-k replacement is the rank-k SVD of B A.  With B = Q_B R_B, A^T = Q_A
- * R_A and the core R_B R_A^T = U S V^T, the retained factors are
- * B' = Q_B U_k = B (R_B^-1 U_k) and A' = S_k V_k^T Q_A^T = (R_A^-1 V_k S_k)^T A:
+ * R_A and the core C = R_B R_A^T = U S V^T, the retained factors are
+ * B' = Q_B U_k = B (R_B^-1 U_k) and A' = S_k V_k^T Q_A^T = U_k^T R_B A:
  * B' has orthonormal columns and B' A' is the best rank-k approximation of
  * B A.  R comes from the Gram matrix M^T M in float64 (the Cholesky form of
  * the QR: one pass over the rows; accurate while cond(B), cond(A) stay well
- * below 1e7).
+ * below 1e7); the core's SVD is a one-sided Jacobi iteration in float64.
  *
  * lora_rsvd_workspace_bytes: bytes of ws for n adapters (host only; 0 on
- *   invalid arguments).  Holds W_B, W_A between the two calls below.
- * lora_rsvd_factor: stage 1, enqueued on `stream`.
+ *   invalid arguments): 6 float64 64 x 64 matrices per adapter, holding W_B
+ *   and W_A between the two calls below.
+ * lora_rsvd_factor: stage 1, enqueued on `stream` (four kernels).
  *   A_all  : device [n][r][d_in] (each A_a row-major), dtype elements.
  *   B_all  : device [n][d_out][r] (each B_a row-major).
  *   sigma  : out, device float32 [n][r]: the singular values of each B_a A_a,
@@ -367,7 +368,9 @@ int lora_ranks_spectral(int m, const int32_t* r_orig_host, const float* sigma_ho
  *            B_a^T B_a or A_a A_a^T fell to 1e-14 of its largest diagonal
  *            entry or below (a numerically rank-deficient factor; zero
  *            factors give sigma = 0 and zero retained factors).
- *   ws     : device, 16-byte aligned, at least lora_rsvd_workspace_bytes.
+ *   ws     : device, at least lora_rsvd_workspace_bytes.
+ *   A_all, B_all and ws 16-byte aligned; d_in and d_out multiples of 8
+ *   (bf16) / 4 (f32), as for a store.
  * lora_rsvd_write: stage 2.  Writes the retained factors of the same adapters
  *   (A_all, B_all and ws as given to lora_rsvd_factor) into `store`, a store
  *   of n = the same adapters, built by lora_pack_retained with both factor
@@ -378,13 +381,25 @@ int lora_ranks_spectral(int m, const int32_t* r_orig_host, const float* sigma_ho
  *   and padding up to the stored rank are zero.
  * Errors: INVALID_ARG (null pointers, n < 0, d < 1, r < 1, workspace too
  * small, an invalid store); UNSUPPORTED (r above LORA_MAX_RANK, d_in < r or
- * d_out < r, unknown dtype, unaligned ws, n too large for one grid).
+ * d_out < r, d not a multiple of 8 / 4, unknown dtype, unaligned pointers, n
+ * too large for one grid).
  */
 size_t lora_rsvd_workspace_bytes(int n, int d_in, int d_out);
 int lora_rsvd_factor(int n, int d_in, int d_out, int dtype, int r, const void* A_all, const void* B_all,
                      float* sigma, int32_t* status, void* ws, size_t ws_bytes, void* stream);
 int lora_rsvd_write(const lora_store* store_host, int r, const void* A_all, const void* B_all, const void* ws,
                     size_t ws_bytes, void* stream);
+
+/*
+ * Some kernels of lora_rsvd_factor, for measuring each alone: phases is a
+ * bit mask, 1 the Grams, 2 the Cholesky factors and the core C, 4 the
+ * core's SVD (sigma, U), 8 W_B and W_A; each reads what the earlier ones
+ * left in ws (from a call for the same A_all, B_all, n, d_in, d_out, r).
+ * 15 = lora_rsvd_factor.
+ * Errors: as lora_rsvd_factor; INVALID_ARG for phases outside 1..15.
+ */
+int lora_rsvd_factor_phases(int n, int d_in, int d_out, int dtype, int r, const void* A_all, const void* B_all,
+                            float* sigma, int32_t* status, void* ws, size_t ws_bytes, void* stream, int phases);
 
 #ifdef __cplusplus
 }

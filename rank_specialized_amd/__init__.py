@@ -392,9 +392,12 @@ def lora_rsvd_workspace_bytes(n: int, d_in: int, d_out: int) -> int:
     return int(L.lib().lora_rsvd_workspace_bytes(n, d_in, d_out))
 
 
-def lora_rsvd_factor(A_all: torch.Tensor, B_all: torch.Tensor, ws: Optional[torch.Tensor] = None) -> RsvdFactors:
+def lora_rsvd_factor(A_all: torch.Tensor, B_all: torch.Tensor, ws: Optional[torch.Tensor] = None,
+                     phases: int = 15, out: Optional[RsvdFactors] = None) -> RsvdFactors:
     """Stage 1 of retained-factor construction for n adapters of one rank r:
-    A_all [n, r, d_in], B_all [n, d_out, r] (contiguous, bf16 or float32)."""
+    A_all [n, r, d_in], B_all [n, d_out, r] (contiguous, bf16 or float32).
+    phases: a bit mask of its kernels (lora_rsvd_factor_phases; 15 = all);
+    ``out`` reuses the sigma, status and workspace buffers of a previous call."""
     if A_all.dim() != 3 or B_all.dim() != 3:
         raise ValueError("A_all is [n, r, d_in] and B_all [n, d_out, r]")
     n, r, d_in = A_all.shape
@@ -403,25 +406,32 @@ def lora_rsvd_factor(A_all: torch.Tensor, B_all: torch.Tensor, ws: Optional[torc
         raise ValueError("A_all and B_all are inconsistent")
     if not (A_all.is_contiguous() and B_all.is_contiguous()):
         raise ValueError("factors must be contiguous")
-    sigma = torch.empty(n, r, dtype=torch.float32, device=A_all.device)
-    status = torch.empty(n, dtype=torch.int32, device=A_all.device)
+    if out is not None:
+        sigma, status, ws = out.sigma, out.status, out.ws
+    else:
+        sigma = torch.empty(n, r, dtype=torch.float32, device=A_all.device)
+        status = torch.empty(n, dtype=torch.int32, device=A_all.device)
     if ws is None:
         ws = torch.empty(max(lora_rsvd_workspace_bytes(n, d_in, d_out), 16), dtype=torch.uint8, device=A_all.device)
-    L.check("lora_rsvd_factor", L.lib().lora_rsvd_factor(
+    L.check("lora_rsvd_factor", L.lib().lora_rsvd_factor_phases(
         n, d_in, d_out, _DTYPES[A_all.dtype], r, _p(A_all), _p(B_all), _p(sigma), _p(status), ws.data_ptr(),
-        ws.numel(), _stream(A_all)))
+        ws.numel(), _stream(A_all), int(phases)))
     return RsvdFactors(A_all, B_all, sigma, status, ws)
 
 
-def lora_rsvd_write(f: RsvdFactors, ranks: Sequence[int], scales, pad_to: int = 0) -> Store:
+def lora_rsvd_write(f: RsvdFactors, ranks: Sequence[int], scales, pad_to: int = 0,
+                    store: Optional[Store] = None) -> Store:
     """Stage 2: a store of the retained factors at `ranks` (one per adapter,
-    e.g. from lora_ranks_uniform / lora_ranks_spectral over f.sigma)."""
+    e.g. from lora_ranks_uniform / lora_ranks_spectral over f.sigma).  With
+    ``store`` (built by an earlier call for the same adapters), its buffers are
+    rewritten in place and ranks / scales / pad_to are taken from it."""
     n, r, d_in = f.A_all.shape
     d_out = f.B_all.shape[1]
-    ranks = [int(v) for v in ranks]
-    if len(ranks) != n:
-        raise ValueError("one retained rank per adapter")
-    store = _pack(n, d_in, d_out, f.A_all.dtype, ranks, scales, pad_to, f.A_all.device, None, None)
+    if store is None:
+        ranks = [int(v) for v in ranks]
+        if len(ranks) != n:
+            raise ValueError("one retained rank per adapter")
+        store = _pack(n, d_in, d_out, f.A_all.dtype, ranks, scales, pad_to, f.A_all.device, None, None)
     L.check("lora_rsvd_write", L.lib().lora_rsvd_write(store.ref(), r, _p(f.A_all), _p(f.B_all), f.ws.data_ptr(),
                                                        f.ws.numel(), _stream(f.A_all)))
     return store

@@ -63,6 +63,7 @@ SIGNATURES = {
     "lora_rsvd_workspace_bytes": (SZ, [I, I, I]),
     "lora_rsvd_factor": (I, [I, I, I, I, I, P, P, P, P, P, SZ, P]),
     "lora_rsvd_write": (I, [C.POINTER(lora_store), I, P, P, P, SZ, P]),
+    "lora_rsvd_factor_phases": (I, [I, I, I, I, I, P, P, P, P, P, SZ, P, I]),
 }
 
 _lib = None

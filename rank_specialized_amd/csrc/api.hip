@@ -273,30 +273,38 @@ int lora_apply_batched_phases(const lora_store* store_host, const void* x, int64
 
 size_t lora_rsvd_workspace_bytes(int n, int d_in, int d_out) {
   if (n < 0 || d_in < 1 || d_out < 1) return 0;
-  return rsvd_workspace_bytes(n, d_in, d_out);
+  return rsvd_workspace_bytes(n);
 }
 
 static int check_rsvd(int n, int d_in, int d_out, int dtype, int r) {
   if (n < 0 || d_in < 1 || d_out < 1 || r < 1) return LORA_ERR_INVALID_ARG;
   if (dtype != LORA_DTYPE_BF16 && dtype != LORA_DTYPE_F32) return LORA_ERR_UNSUPPORTED;
   if (r > LORA_MAX_RANK || d_in < r || d_out < r) return LORA_ERR_UNSUPPORTED;
+  const int v = dtype == LORA_DTYPE_BF16 ? 8 : 4;  // rows are read as 16-byte vectors
+  if (d_in % v != 0 || d_out % v != 0) return LORA_ERR_UNSUPPORTED;
   // Grids (workgroups of 256 threads) stay below 2^32 threads.
-  const int64_t wgs = (int64_t)n * (2 * 4 + (d_in + 255) / 256 + (d_out + 255) / 256);
+  const int64_t wgs = (int64_t)n * (2 + (d_in + 255) / 256 + (d_out + 255) / 256);
   if (wgs * 256 >= ((int64_t)1 << 32)) return LORA_ERR_UNSUPPORTED;
   return LORA_OK;
 }
 
-int lora_rsvd_factor(int n, int d_in, int d_out, int dtype, int r, const void* A_all, const void* B_all,
-                     float* sigma, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+int lora_rsvd_factor_phases(int n, int d_in, int d_out, int dtype, int r, const void* A_all, const void* B_all,
+                            float* sigma, int32_t* status, void* ws, size_t ws_bytes, void* stream, int phases) {
+  if (phases < 1 || phases > 15) return LORA_ERR_INVALID_ARG;
   int st = check_rsvd(n, d_in, d_out, dtype, r);
   if (st != LORA_OK) return st;
   if (n == 0) return LORA_OK;
   if (!A_all || !B_all || !sigma || !status || !ws) return LORA_ERR_INVALID_ARG;
-  if (ws_bytes < rsvd_workspace_bytes(n, d_in, d_out)) return LORA_ERR_INVALID_ARG;
-  if (!aligned16(ws)) return LORA_ERR_UNSUPPORTED;
+  if (ws_bytes < rsvd_workspace_bytes(n)) return LORA_ERR_INVALID_ARG;
+  if (!aligned16(ws) || !aligned16(A_all) || !aligned16(B_all)) return LORA_ERR_UNSUPPORTED;
   hipError_t e = launch_rsvd_factor(n, d_in, d_out, dtype, r, A_all, B_all, sigma, status, ws,
-                                    reinterpret_cast<hipStream_t>(stream));
+                                    reinterpret_cast<hipStream_t>(stream), phases);
   return e == hipSuccess ? LORA_OK : hip_fail(e);
+}
+
+int lora_rsvd_factor(int n, int d_in, int d_out, int dtype, int r, const void* A_all, const void* B_all,
+                     float* sigma, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+  return lora_rsvd_factor_phases(n, d_in, d_out, dtype, r, A_all, B_all, sigma, status, ws, ws_bytes, stream, 15);
 }
 
 int lora_rsvd_write(const lora_store* store_host, int r, const void* A_all, const void* B_all, const void* ws,
@@ -308,8 +316,8 @@ int lora_rsvd_write(const lora_store* store_host, int r, const void* A_all, cons
   if (st != LORA_OK) return st;
   if (s.n == 0 || s.R == 0) return LORA_OK;
   if (!A_all || !B_all || !ws) return LORA_ERR_INVALID_ARG;
-  if (ws_bytes < rsvd_workspace_bytes(s.n, s.d_in, s.d_out)) return LORA_ERR_INVALID_ARG;
-  if (!aligned16(ws)) return LORA_ERR_UNSUPPORTED;
+  if (ws_bytes < rsvd_workspace_bytes(s.n)) return LORA_ERR_INVALID_ARG;
+  if (!aligned16(ws) || !aligned16(A_all) || !aligned16(B_all)) return LORA_ERR_UNSUPPORTED;
   hipError_t e = launch_rsvd_write(s, r, A_all, B_all, ws, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? LORA_OK : hip_fail(e);
 }

@@ -45,11 +45,13 @@ hipError_t launch_expand(const lora_store& s, int T, const void* ws, const float
                          int64_t ldy, hipStream_t stream);
 
 // Retained-factor construction (r-SVD): per adapter, the Grams of B and A^T
-// (row blocks, float64), then Cholesky, the core SVD and W_B, W_A into ws;
-// the write forms B W_B and W_A^T A into a store's buffers.
-size_t rsvd_workspace_bytes(int n, int d_in, int d_out);
+// (float64 MFMA), Cholesky and the core C, its Jacobi SVD, W_B and W_A, in
+// ws; the write forms B W_B and W_A^T A into a store's buffers.
+size_t rsvd_workspace_bytes(int n);
+// phases: bit 0 the Gram kernel, bit 1 Cholesky + core, bit 2 Jacobi, bit 3
+// W_B / W_A.
 hipError_t launch_rsvd_factor(int n, int d_in, int d_out, int dtype, int r, const void* A, const void* B,
-                              float* sigma, int32_t* status, void* ws, hipStream_t stream);
+                              float* sigma, int32_t* status, void* ws, hipStream_t stream, int phases);
 hipError_t launch_rsvd_write(const lora_store& s, int r, const void* A, const void* B, const void* ws,
                              hipStream_t stream);
 

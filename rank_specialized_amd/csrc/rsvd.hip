@@ -10,37 +10,60 @@
 // rank-k SVD of B A (Eckart-Young).
 //
 // For B (d_out x r) and A (r x d_in), with B = Q_B R_B and A^T = Q_A R_A:
-// B A = Q_B (R_B R_A^T) Q_A^T, and the SVD of the r x r core C = U S V^T
-// gives B' = Q_B U_k = B (R_B^-1 U_k) and A' = S_k V_k^T Q_A^T =
-// (R_A^-1 V_k S_k)^T A.  Q is never formed.
+// B A = Q_B C Q_A^T with the r x r core C = R_B R_A^T.  With C = U S V^T,
+// B' = Q_B U_k = B (R_B^-1 U_k) and A' = S_k V_k^T Q_A^T = U_k^T C Q_A^T =
+// U_k^T R_B A, so W_B = R_B^-1 U and W_A = R_B^T U (V is never needed, nor Q).
 //
-//   rsvd_gram_kernel   R's Gram matrix M^T M of a factor (M = B, or A^T),
-//                      one row block per workgroup, float64 (bf16 and f32
-//                      products are exact in float64): the blocks' parts
-//                      are merged by the core kernel, summed in block order.
-//                      R^T R = M^T M, so R is the Cholesky factor: this is
-//                      the Cholesky form of the tall-skinny QR (one pass over
-//                      the rows; its R loses accuracy as cond(M)^2, which the
-//                      core kernel reports when a pivot collapses).
-//   rsvd_core_kernel   per adapter, in LDS: Cholesky of both Grams, the core
-//                      C = R_B R_A^T, its SVD by one-sided Jacobi (column
-//                      pairs in a round-robin order, rotations until every
-//                      pair is orthogonal to 1e-15), the singular values in
-//                      descending order, and W_B = R_B^-1 U, W_A = R_A^-1 V S
-//                      by back substitution.
-//   rsvd_write_kernel  B'[o, c] = sum_i B[o, i] W_B[i, c] and
-//                      A'[c, k] = sum_i W_A[i, c] A[i, k] for c < k_a, written
-//                      straight into a store's A and B buffers at the store's
-//                      row offsets and ranks (k_a), rounded once.
+//   rsvd_gram_kernel    the Gram matrix M^T M of one factor (M = B, or A^T):
+//                       four waves each take every fourth block of rows,
+//                       float64 MFMA (16x16x4) on the ten upper 16 x 16 tiles,
+//                       the waves' parts summed in wave order.  R^T R = M^T M:
+//                       this is the Cholesky form of the tall-skinny QR (one
+//                       pass over the rows, the row blocks merged by a sum).
+//                       bf16 and f32 inputs are exact in float64.
+//   rsvd_prep_kernel    per adapter, two waves: the Cholesky factors R_B and
+//                       R_A (a pivot at 1e-14 of the largest diagonal entry or
+//                       below flags the adapter), then C = R_B R_A^T.
+//   rsvd_jacobi_kernel  per adapter, one wave, lane j holding column j of C
+//                       in registers: one-sided Jacobi, column pairs (j, j^m)
+//                       for m = 1 .. 2^ceil(log2 r) - 1 (every pair once per
+//                       sweep), partner columns fetched across lanes, until a
+//                       sweep rotates nothing (each pair orthogonal to 1e-15);
+//                       then sigma_j = |C_j|, their descending order, U.
+//   rsvd_post_kernel    per adapter, one wave: W_A = R_B^T U and
+//                       W_B = R_B^-1 U (back substitution), columns in sigma
+//                       order.
+//   rsvd_write_kernel   B'[o, c] = sum_i B[o, i] W_B[i, c] and
+//                       A'[c, k] = sum_i W_A[i, c] A[i, k] (float64) for
+//                       c < k_a, into a store's A and B buffers at the store's
+//                       row offsets and ranks.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace lora {
 
-constexpr int kRsvdThreads = 256;
 constexpr int kRsvdR = LORA_MAX_RANK;  // largest original rank
-constexpr int kRsvdTile = 64;          // rows of a Gram tile
-constexpr int kRsvdMaxBlocks = 4;      // row blocks per factor
+constexpr int kRsvdMat = kRsvdR * kRsvdR;
+constexpr int kGramWaves = 4;
+constexpr int kGramTiles = 10;  // upper 16 x 16 tiles of a 64 x 64 Gram
+// Workspace, float64 matrices per adapter (64 x 64 each): the Grams of B and
+// of A^T, the core C (then U), R_B, W_B, W_A.
+constexpr int kWsGramB = 0, kWsGramA = 1, kWsC = 2, kWsRB = 3, kWsWB = 4, kWsWA = 5, kWsMats = 6;
+
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
+struct RsvdArgs {
+  int n, d_in, d_out, r;
+  const char* A;  // [n][r][d_in]
+  const char* B;  // [n][d_out][r]
+  double* ws;     // [n][kWsMats][64][64]
+  float* sigma;   // [n][r]
+  int32_t* status;
+};
+
+__device__ __forceinline__ double* ws_mat(const RsvdArgs& p, int a, int m) {
+  return p.ws + ((size_t)a * kWsMats + m) * kRsvdMat;
+}
 
 template <typename E>
 __device__ __forceinline__ double load_elem(const char* base, int64_t i) {
@@ -48,252 +71,265 @@ __device__ __forceinline__ double load_elem(const char* base, int64_t i) {
   else return (double)reinterpret_cast<const float*>(base)[i];
 }
 
-struct RsvdArgs {
-  int n, d_in, d_out, r, nblk;
-  const char* A;  // [n][r][d_in]
-  const char* B;  // [n][d_out][r]
-  double* part;   // [n][2][nblk][kRsvdR][kRsvdR]
-  double* WB;     // [n][kRsvdR][kRsvdR]
-  double* WA;     // [n][kRsvdR][kRsvdR]
-  float* sigma;   // [n][r]
-  int32_t* status;
-};
-
-// Workgroup (adapter, side, row block): side 0 = B (rows of length r, d_out
-// of them), side 1 = A^T (the columns of A).
-template <typename E>
-__global__ void __launch_bounds__(kRsvdThreads) rsvd_gram_kernel(RsvdArgs p) {
-  __shared__ double t[kRsvdTile][kRsvdR + 1];
-  const int b = blockIdx.x;
-  const int blk = b % p.nblk, side = (b / p.nblk) & 1, a = b / (2 * p.nblk);
-  const int tid = threadIdx.x, r = p.r;
+// ------------------------------------------------------------------ Gram
+// Workgroup (adapter, side): side 0 = B (rows of r elements), side 1 = A^T
+// (the columns of A).  A chunk is E::kVec rows of M: side 0 reads it as r
+// contiguous 16-byte vectors of B (lane l < r the l-th), side 1 as one
+// 16-byte vector per row of A (lane l < r: A[l][k0 .. k0 + kVec)).  Each wave
+// stages its chunk in float64 in its own LDS tile (zero outside the r
+// columns) and feeds 16 x 16 x 4 MFMAs: lane l holds M[k0 + l/16][16 b + l%16]
+// as the A operand of tile row b and the B operand of tile column b.
+template <typename E, int NB>
+__global__ void __launch_bounds__(kGramWaves * 64) rsvd_gram_kernel(RsvdArgs p) {
+  constexpr int KV = E::kVec;  // rows per chunk
+  constexpr int kStage = kGramWaves * 2 * 8 * kRsvdR;             // doubles
+  constexpr int kRed = (kGramWaves - 1) * kGramTiles * 256;         // doubles
+  __shared__ double lds[kStage > kRed ? kStage : kRed];
+  const int a = blockIdx.x >> 1, side = blockIdx.x & 1;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = p.r;
   const int D = side == 0 ? p.d_out : p.d_in;
-  const int per = ((D + p.nblk - 1) / p.nblk + kRsvdTile - 1) / kRsvdTile * kRsvdTile;
-  const int k0 = blk * per, k1 = min(D, k0 + per);
-  const int i0 = 4 * (tid / 16), j0 = 4 * (tid % 16);
-  double acc[4][4];
+  const int nchunks = D / KV;
+  const int iters = (nchunks + kGramWaves - 1) / kGramWaves;
+  double* st = lds + (size_t)w * 2 * 8 * kRsvdR;
+  for (int e = l; e < 2 * 8 * kRsvdR; e += 64) st[e] = 0.0;
+  const char* base = side == 0 ? p.B + (size_t)a * p.d_out * r * E::kBytes
+                               : p.A + (size_t)a * r * p.d_in * E::kBytes;
+  // Side 0: the kVec elements of lane l's vector sit at flat offsets
+  // l * KV + t of the chunk, i.e. (row, col) = divmod(l * KV + t, r).
+  const int e0 = l * KV, row0 = e0 / r, col0 = e0 - row0 * r;
+  f64x4_t acc[kGramTiles];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) acc[u][v] = 0.0;
-  const char* base = side == 0 ? p.B + (size_t)a * p.d_out * r * E::kBytes : p.A + (size_t)a * r * p.d_in * E::kBytes;
-  for (int kt = k0; kt < k1; kt += kRsvdTile) {
-    const int rows = min(kRsvdTile, k1 - kt);
-    // Stage rows kt .. kt + rows of M (row kk holds M[kt + kk][0 .. r)).
-    for (int e = tid; e < kRsvdTile * kRsvdR; e += kRsvdThreads) {
-      int kk, i;
+  for (int t = 0; t < kGramTiles; ++t) acc[t] = (f64x4_t){0.0, 0.0, 0.0, 0.0};
+  auto load = [&](int c) -> uint4 {
+    if (c >= nchunks || l >= r) return make_uint4(0u, 0u, 0u, 0u);
+    const size_t off = side == 0 ? ((size_t)c * KV * r + (size_t)l * KV) : ((size_t)l * p.d_in + (size_t)c * KV);
+    return ld16(base + off * E::kBytes);
+  };
+  uint4 q = load(w);
+  for (int it = 0; it < iters; ++it) {
+    double* tile = st + (it & 1) * 8 * kRsvdR;
+    if (l < r) {
+      float f[KV];
+      E::widen(q, f);
       if (side == 0) {
-        kk = e / kRsvdR;
-        i = e - kk * kRsvdR;
+        int row = row0, col = col0;
+#pragma unroll
+        for (int t = 0; t < KV; ++t) {
+          tile[row * kRsvdR + col] = (double)f[t];
+          if (++col == r) {
+            col = 0;
+            ++row;
+          }
+        }
       } else {
-        i = e / kRsvdTile;
-        kk = e - i * kRsvdTile;
-      }
-      double v = 0.0;
-      if (kk < rows && i < r)
-        v = side == 0 ? load_elem<E>(base, (int64_t)(kt + kk) * r + i) : load_elem<E>(base, (int64_t)i * p.d_in + kt + kk);
-      t[kk][i] = v;
-    }
-    __syncthreads();
-    if (i0 < r && j0 < r) {
-      for (int kk = 0; kk < rows; ++kk) {
-        double x[4], y[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          x[u] = t[kk][i0 + u];
-          y[u] = t[kk][j0 + u];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int v = 0; v < 4; ++v) acc[u][v] += x[u] * y[v];
+        for (int t = 0; t < KV; ++t) tile[t * kRsvdR + l] = (double)f[t];
       }
     }
+    q = load((it + 1) * kGramWaves + w);  // next chunk in flight during the MFMAs
     __syncthreads();
+#pragma unroll
+    for (int s = 0; s < KV / 4; ++s) {
+      double x[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) x[b] = b < NB ? tile[(4 * s + (l >> 4)) * kRsvdR + 16 * b + (l & 15)] : 0.0;
+      int t = 0;
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+        for (int jb = ib; jb < 4; ++jb, ++t)
+          if (jb < NB) acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(x[ib], x[jb], acc[t], 0, 0, 0);
+    }
   }
-  double* out = p.part + ((((size_t)a * 2 + side) * p.nblk + blk) * kRsvdR) * kRsvdR;
+  __syncthreads();  // every wave is done with its staging tiles
+  if (w > 0) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+    for (int t = 0; t < kGramTiles; ++t)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) out[(size_t)(i0 + u) * kRsvdR + j0 + v] = acc[u][v];
+      for (int v = 0; v < 4; ++v) lds[((w - 1) * kGramTiles + t) * 256 + v * 64 + l] = acc[t][v];
+  }
+  __syncthreads();
+  if (w == 0) {
+    double* G = ws_mat(p, a, side == 0 ? kWsGramB : kWsGramA);
+    int t = 0;
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+      for (int jb = ib; jb < 4; ++jb, ++t) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          double s = acc[t][v];
+#pragma unroll
+          for (int ww = 0; ww < kGramWaves - 1; ++ww) s += lds[(ww * kGramTiles + t) * 256 + v * 64 + l];
+          // MFMA result layout: lane l, element v holds row 4 v + l / 16,
+          // column l % 16 of the tile.
+          const int i = 16 * ib + 4 * v + (l >> 4), j = 16 * jb + (l & 15);
+          G[i * kRsvdR + j] = s;
+          if (ib != jb) G[j * kRsvdR + i] = s;
+        }
+      }
+  }
 }
 
-// Upper Cholesky factor of the r x r matrix g in place (R in the upper
-// triangle, R^T R = g; the lower triangle is left as it was).  A pivot at or
-// below 1e-14 of the largest diagonal entry (cond(M) above about 1e7, where
-// the Cholesky form of the QR stops being accurate) sets *bad; a pivot at or
-// below 1e-30 of it, or not positive, is raised to that floor so that the
-// factorization finishes (a zero column gives a zero row of R but for a tiny
-// diagonal).
-__device__ void cholesky_upper(double (*g)[kRsvdR + 1], int r, double* s_d, int* bad) {
-  const int tid = threadIdx.x;
+// ------------------------------------------------------------------ prep
+// Upper Cholesky factor of m (lane c owns column c; R in the upper triangle,
+// the lower triangle zeroed).  Pivot rules as in the file comment; a pivot at
+// or below 1e-30 of the largest diagonal entry, or not positive, is raised to
+// that floor so the factorization finishes (a zero column gives a zero row of
+// R but for a tiny diagonal).
+__device__ void cholesky_lanes(double (*m)[kRsvdR + 1], int r, int c, int* bad) {
   double dmax = 0.0;
-  for (int j = 0; j < r; ++j) dmax = fmax(dmax, g[j][j]);
-  __syncthreads();  // every thread has read the diagonal before it changes
+  for (int j = 0; j < r; ++j) dmax = fmax(dmax, m[j][j]);
   const double warn = 1e-14 * dmax, floor_v = fmax(1e-30 * dmax, 1e-300);
+  __syncthreads();
   for (int j = 0; j < r; ++j) {
-    if (tid == 0) {
-      double d = g[j][j];
-      if (!(d > warn)) *bad = 1;
-      if (!(d > floor_v)) d = floor_v;
-      *s_d = sqrt(d);
-      g[j][j] = *s_d;
-    }
+    double d2 = m[j][j];
+    if (!(d2 > warn) && c == 0) *bad = 1;
+    if (!(d2 > floor_v)) d2 = floor_v;
+    const double d = sqrt(d2);
+    __syncthreads();  // every lane has read the pivot
+    if (c == j) m[j][j] = d;
+    if (c > j && c < r) m[j][c] /= d;
     __syncthreads();
-    const double d = *s_d;
-    for (int c = j + 1 + tid; c < r; c += kRsvdThreads) g[j][c] /= d;
-    __syncthreads();
-    const int m = r - j - 1;
-    for (int e = tid; e < m * m; e += kRsvdThreads) {
-      const int c1 = j + 1 + e / m, c2 = j + 1 + e % m;
-      if (c2 >= c1) g[c1][c2] -= g[j][c1] * g[j][c2];
+    if (c > j && c < r) {
+      const double rc = m[j][c];
+      for (int i = j + 1; i <= c; ++i) m[i][c] -= m[j][i] * rc;
     }
     __syncthreads();
   }
+  for (int i = c + 1; i < kRsvdR; ++i) m[i][c] = 0.0;
+  __syncthreads();
 }
 
-__global__ void __launch_bounds__(kRsvdThreads) rsvd_core_kernel(RsvdArgs p) {
-  extern __shared__ double lds[];
-  double (*gb)[kRsvdR + 1] = reinterpret_cast<double (*)[kRsvdR + 1]>(lds);
-  double (*ga)[kRsvdR + 1] = gb + kRsvdR;
-  double (*c)[kRsvdR + 1] = ga + kRsvdR;
-  double (*v)[kRsvdR + 1] = c + kRsvdR;
-  __shared__ double s_d;
-  __shared__ double s_sig[kRsvdR];
-  __shared__ int s_pos[kRsvdR];
-  __shared__ int s_rot, s_bad;
-  const int a = blockIdx.x, tid = threadIdx.x, r = p.r;
+// Workgroup per adapter: wave 0 factors B's Gram, wave 1 A^T's; then wave w
+// forms rows 32 w .. 32 w + 31 of C = R_B R_A^T (lane j: column j).
+__global__ void __launch_bounds__(128) rsvd_prep_kernel(RsvdArgs p) {
+  __shared__ double m[2][kRsvdR][kRsvdR + 1];
+  __shared__ int s_bad;
+  const int a = blockIdx.x, tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = p.r;
   if (tid == 0) s_bad = 0;
-  // 1. The Grams: the row blocks' parts summed in block order.
-  for (int e = tid; e < kRsvdR * kRsvdR; e += kRsvdThreads) {
-    const int i = e / kRsvdR, j = e % kRsvdR;
-    double sb = 0.0, sa = 0.0;
-    for (int blk = 0; blk < p.nblk; ++blk) {
-      sb += p.part[((((size_t)a * 2 + 0) * p.nblk + blk) * kRsvdR + i) * kRsvdR + j];
-      sa += p.part[((((size_t)a * 2 + 1) * p.nblk + blk) * kRsvdR + i) * kRsvdR + j];
-    }
-    gb[i][j] = sb;
-    ga[i][j] = sa;
-  }
+  const double* G = ws_mat(p, a, w == 0 ? kWsGramB : kWsGramA);
+  for (int i = 0; i < kRsvdR; ++i) m[w][i][l] = G[i * kRsvdR + l];
   __syncthreads();
-  // 2. R_B, R_A (upper triangles of gb, ga).
-  cholesky_upper(gb, r, &s_d, &s_bad);
-  cholesky_upper(ga, r, &s_d, &s_bad);
-  // 3. C = R_B R_A^T, V = I.
-  for (int e = tid; e < kRsvdR * kRsvdR; e += kRsvdThreads) {
-    const int i = e / kRsvdR, j = e % kRsvdR;
-    double s = 0.0;
-    if (i < r && j < r)
-      for (int k = max(i, j); k < r; ++k) s += gb[i][k] * ga[j][k];
-    c[i][j] = s;
-    v[i][j] = (i == j) ? 1.0 : 0.0;
-  }
-  __syncthreads();
-  // 4. One-sided Jacobi: rotate column pairs of C (and V) until orthogonal.
-  //    Round-robin pairing of m = r rounded up to even players: each round,
-  //    m / 2 disjoint pairs, 8 threads per pair; m - 1 rounds per sweep.
-  const int m = (r + 1) & ~1;
-  const int grp = tid >> 3, l = tid & 7;
-  for (int sweep = 0; sweep < 40; ++sweep) {
-    if (tid == 0) s_rot = 0;
-    __syncthreads();
-    for (int rnd = 0; rnd < m - 1; ++rnd) {
-      for (int pr = grp; pr < m / 2; pr += kRsvdThreads / 8) {
-        int pp, qq;
-        if (pr == 0) {
-          pp = m - 1;
-          qq = rnd;
-        } else {
-          pp = (rnd + pr) % (m - 1);
-          qq = (rnd - pr + m - 1) % (m - 1);
-        }
-        const int P = min(pp, qq), Q = max(pp, qq);
-        double al = 0.0, be = 0.0, ga_ = 0.0;
-        if (Q < r) {
-          for (int i = l; i < r; i += 8) {
-            const double x = c[i][P], y = c[i][Q];
-            al += x * x;
-            be += y * y;
-            ga_ += x * y;
-          }
-        }
+  cholesky_lanes(m[w], r, l, &s_bad);
+  double c[32];
 #pragma unroll
-        for (int sh = 1; sh < 8; sh <<= 1) {
-          al += __shfl_xor(al, sh, 8);
-          be += __shfl_xor(be, sh, 8);
-          ga_ += __shfl_xor(ga_, sh, 8);
-        }
-        if (Q < r && fabs(ga_) > 1e-15 * sqrt(al * be) && ga_ != 0.0) {
-          const double zeta = (be - al) / (2.0 * ga_);
-          const double tt = (zeta >= 0 ? 1.0 : -1.0) / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
-          const double cs = 1.0 / sqrt(1.0 + tt * tt), sn = cs * tt;
-          for (int i = l; i < r; i += 8) {
-            const double x = c[i][P], y = c[i][Q];
-            c[i][P] = cs * x - sn * y;
-            c[i][Q] = sn * x + cs * y;
-            const double vx = v[i][P], vy = v[i][Q];
-            v[i][P] = cs * vx - sn * vy;
-            v[i][Q] = sn * vx + cs * vy;
-          }
-          if (l == 0) s_rot = 1;
-        }
-      }
-      __syncthreads();
-    }
-    const bool more = s_rot != 0;
-    __syncthreads();
-    if (!more) break;
+  for (int ii = 0; ii < 32; ++ii) c[ii] = 0.0;
+  for (int k = 0; k < r; ++k) {
+    const double raj = m[1][l][k];  // R_A[j][k], j = l
+#pragma unroll
+    for (int ii = 0; ii < 32; ++ii) c[ii] = fma(m[0][32 * w + ii][k], raj, c[ii]);
   }
-  // 5. Singular values (column norms) and their descending order.
-  if (tid < r) {
-    double s = 0.0;
-    for (int i = 0; i < r; ++i) s += c[i][tid] * c[i][tid];
-    s_sig[tid] = sqrt(s);
+  double* C = ws_mat(p, a, kWsC);
+#pragma unroll
+  for (int ii = 0; ii < 32; ++ii) C[(32 * w + ii) * kRsvdR + l] = c[ii];
+  if (w == 0) {
+    double* RB = ws_mat(p, a, kWsRB);
+    for (int i = 0; i < kRsvdR; ++i) RB[i * kRsvdR + l] = m[0][i][l];
   }
   __syncthreads();
-  if (tid < r) {
-    int pos = 0;
-    const double me = s_sig[tid];
-    for (int k = 0; k < r; ++k) pos += (s_sig[k] > me || (s_sig[k] == me && k < tid)) ? 1 : 0;
-    s_pos[tid] = pos;
-  }
-  __syncthreads();
-  // 6. Thread j: u_j = C[:, j] / sigma_j, then W_B[:, pos_j] = R_B^-1 u_j and
-  //    W_A[:, pos_j] = R_A^-1 (sigma_j v_j), by back substitution in place.
-  if (tid < r) {
-    const int j = tid, pos = s_pos[j];
-    const double sg = s_sig[j];
-    const double inv = sg > 0.0 ? 1.0 / sg : 0.0;
-    for (int i = 0; i < r; ++i) {
-      c[i][j] *= inv;
-      v[i][j] *= sg;
-    }
-    for (int i = r - 1; i >= 0; --i) {
-      double sb = c[i][j], sa = v[i][j];
-      for (int k = i + 1; k < r; ++k) {
-        sb -= gb[i][k] * c[k][j];
-        sa -= ga[i][k] * v[k][j];
-      }
-      c[i][j] = sb / gb[i][i];
-      v[i][j] = sa / ga[i][i];
-    }
-    double* wb = p.WB + (size_t)a * kRsvdR * kRsvdR;
-    double* wa = p.WA + (size_t)a * kRsvdR * kRsvdR;
-    for (int i = 0; i < r; ++i) {
-      wb[(size_t)i * kRsvdR + pos] = c[i][j];
-      wa[(size_t)i * kRsvdR + pos] = v[i][j];
-    }
-    p.sigma[(size_t)a * r + pos] = (float)sg;
-  }
   if (tid == 0) p.status[a] = s_bad;
 }
 
+// ---------------------------------------------------------------- Jacobi
+// One wave per adapter; RB = the rank rounded up to a power of two (>= 8):
+// rows and pairings beyond it are all zero.
+template <int RB>
+__global__ void __launch_bounds__(64) rsvd_jacobi_kernel(RsvdArgs p) {
+  const int a = blockIdx.x, j = threadIdx.x, r = p.r;
+  double* C = ws_mat(p, a, kWsC);
+  double c[RB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i) c[i] = C[i * kRsvdR + j];
+  for (int sweep = 0; sweep < 40; ++sweep) {
+    bool rot = false;
+    for (int mm = 1; mm < RB; ++mm) {
+      const bool lower = j < (j ^ mm);
+      double y[RB];
+      double own = 0.0, oth = 0.0, g = 0.0;
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        y[i] = __shfl_xor(c[i], mm);
+        own = fma(c[i], c[i], own);
+        oth = fma(y[i], y[i], oth);
+        g = fma(c[i], y[i], g);
+      }
+      // Both lanes of a pair see the same alpha (lower column), beta, gamma.
+      const double al = lower ? own : oth, be = lower ? oth : own;
+      if (g != 0.0 && fabs(g) > 1e-15 * sqrt(al * be)) {
+        const double zeta = (be - al) / (2.0 * g);
+        const double t = (zeta >= 0.0 ? 1.0 : -1.0) / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
+        const double cs = 1.0 / sqrt(1.0 + t * t), sn = cs * t;
+        if (lower) {
+#pragma unroll
+          for (int i = 0; i < RB; ++i) c[i] = cs * c[i] - sn * y[i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < RB; ++i) c[i] = sn * y[i] + cs * c[i];
+        }
+        rot = true;
+      }
+    }
+    if (!__any(rot)) break;
+  }
+  double s2 = 0.0;
+#pragma unroll
+  for (int i = 0; i < RB; ++i) s2 = fma(c[i], c[i], s2);
+  const double sg = sqrt(s2);
+  // Descending order, ties (and a NaN, ranked last) by lane: a permutation.
+  const double key = sg == sg ? sg : -1.0;
+  int pos = 0;
+  for (int k = 0; k < 64; ++k) {
+    const double o = __shfl(key, k);
+    pos += (o > key || (o == key && k < j)) ? 1 : 0;
+  }
+  const double inv = sg > 0.0 ? 1.0 / sg : 0.0;
+  // U in sigma order, in place of C (every lane has read its column).
+#pragma unroll
+  for (int i = 0; i < RB; ++i) C[i * kRsvdR + pos] = c[i] * inv;
+  if (j < r) p.sigma[(size_t)a * r + pos] = (float)sg;
+}
+
+// ------------------------------------------------------------------ post
+// One wave per adapter, lane c: column c of W_A = R_B^T U and of
+// W_B = R_B^-1 U (row-oriented back substitution in LDS).
+__global__ void __launch_bounds__(64) rsvd_post_kernel(RsvdArgs p) {
+  __shared__ double rb[kRsvdR][kRsvdR + 1];
+  __shared__ double x[kRsvdR][kRsvdR + 1];
+  const int a = blockIdx.x, c = threadIdx.x, r = p.r;
+  const double* RB = ws_mat(p, a, kWsRB);
+  const double* U = ws_mat(p, a, kWsC);
+  double* WB = ws_mat(p, a, kWsWB);
+  double* WA = ws_mat(p, a, kWsWA);
+  double u[kRsvdR];
+#pragma unroll
+  for (int k = 0; k < kRsvdR; ++k) {
+    rb[k][c] = RB[k * kRsvdR + c];
+    u[k] = U[k * kRsvdR + c];
+    x[k][c] = u[k];
+  }
+  __syncthreads();
+  for (int i = 0; i < r; ++i) {
+    double s = 0.0;
+#pragma unroll
+    for (int k = 0; k < kRsvdR; ++k) s = fma(rb[k][i], u[k], s);  // rb is zero below the diagonal
+    WA[i * kRsvdR + c] = s;
+  }
+  for (int i = r - 1; i >= 0; --i) {
+    double s = x[i][c];
+    for (int k = i + 1; k < r; ++k) s -= rb[i][k] * x[k][c];
+    s /= rb[i][i];
+    x[i][c] = s;
+    WB[i * kRsvdR + c] = s;
+  }
+}
+
+// ----------------------------------------------------------------- write
 struct RsvdWriteArgs {
-  int n, d_in, d_out, r, R, nbo;  // nbo: row blocks of B' (kRsvdThreads rows each)
+  int n, d_in, d_out, r, R, nbo;  // nbo: row blocks of B' (256 rows each)
   const char* A;
   const char* B;
-  const double* WB;
-  const double* WA;
+  const double* ws;
   const int32_t* row_off;
   const int32_t* rank;       // stored rank
   const int32_t* true_rank;  // retained rank k_a
@@ -307,69 +343,75 @@ __device__ __forceinline__ void store_elem(typename E::storage* out, size_t i, d
   else out[i] = (float)v;
 }
 
-// Workgroup (adapter, block): blocks [0, nbo) write kRsvdThreads rows of B'
-// each (a thread per row), the rest kRsvdThreads columns of A' each (a
-// thread per column).  Components c < min(k_a, r) come from W; the others
-// (a retained rank above r, or padding up to the stored rank) are zero.
+// Workgroup (adapter, block): blocks [0, nbo) write 256 rows of B' each (a
+// thread per row), the rest 256 columns of A' each (a thread per column).
+// Components c < min(k_a, r) come from W; the others (a retained rank above
+// r, or padding up to the stored rank) are zero.
 template <typename E>
-__global__ void __launch_bounds__(kRsvdThreads) rsvd_write_kernel(RsvdWriteArgs p) {
+__global__ void __launch_bounds__(256) rsvd_write_kernel(RsvdWriteArgs p) {
   __shared__ double w[kRsvdR][kRsvdR];
-  const int nb = p.nbo + (p.d_in + kRsvdThreads - 1) / kRsvdThreads;
+  const int nb = p.nbo + (p.d_in + 255) / 256;
   const int a = blockIdx.x / nb, blk = blockIdx.x - a * nb;
   const int tid = threadIdx.x, r = p.r;
   const int ro = p.row_off[a], stored = p.rank[a];
   const int k = min(p.true_rank[a], r);
   if (stored <= 0 || ro < 0 || ro > p.R - stored) return;  // uniform per workgroup
   const bool bside = blk < p.nbo;
-  const double* W = (bside ? p.WB : p.WA) + (size_t)a * kRsvdR * kRsvdR;
-  for (int e = tid; e < kRsvdR * kRsvdR; e += kRsvdThreads) w[e / kRsvdR][e % kRsvdR] = e / kRsvdR < r ? W[e] : 0.0;
+  const double* W = p.ws + ((size_t)a * kWsMats + (bside ? kWsWB : kWsWA)) * kRsvdMat;
+  for (int e = tid; e < kRsvdMat; e += 256) w[e / kRsvdR][e % kRsvdR] = e / kRsvdR < r ? W[e] : 0.0;
   __syncthreads();
   typename E::storage* outA = reinterpret_cast<typename E::storage*>(p.A_pack);
   typename E::storage* outB = reinterpret_cast<typename E::storage*>(p.B_pack);
+  double x[kRsvdR];
   if (bside) {
-    const int o = blk * kRsvdThreads + tid;
+    const int o = blk * 256 + tid;
     if (o >= p.d_out) return;
     const char* brow = p.B + ((size_t)a * p.d_out + o) * r * E::kBytes;
-    double x[kRsvdR];
+    if (r % E::kVec == 0) {  // rows are 16-byte aligned: vector loads
 #pragma unroll
-    for (int i = 0; i < kRsvdR; ++i) x[i] = i < r ? load_elem<E>(brow, i) : 0.0;
+      for (int v = 0; v < kRsvdR / E::kVec; ++v) {
+        float f[E::kVec];
+        if (v * E::kVec < r) {
+          E::widen(ld16(brow + (size_t)v * 16), f);
+        } else {
+#pragma unroll
+          for (int t = 0; t < E::kVec; ++t) f[t] = 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < E::kVec; ++t) x[v * E::kVec + t] = (double)f[t];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kRsvdR; ++i) x[i] = i < r ? load_elem<E>(brow, i) : 0.0;
+    }
     const size_t base = (size_t)ro * p.d_out + (size_t)o * stored;
     for (int cc = 0; cc < stored; ++cc) {
       double s = 0.0;
       if (cc < k) {
 #pragma unroll
-        for (int i = 0; i < kRsvdR; ++i) s += x[i] * w[i][cc];
+        for (int i = 0; i < kRsvdR; ++i) s = fma(x[i], w[i][cc], s);
       }
       store_elem<E>(outB, base + cc, s);
     }
   } else {
-    const int col = (blk - p.nbo) * kRsvdThreads + tid;
+    const int col = (blk - p.nbo) * 256 + tid;
     if (col >= p.d_in) return;
     const char* abase = p.A + (size_t)a * r * p.d_in * E::kBytes;
-    double x[kRsvdR];
 #pragma unroll
     for (int i = 0; i < kRsvdR; ++i) x[i] = i < r ? load_elem<E>(abase, (int64_t)i * p.d_in + col) : 0.0;
     for (int cc = 0; cc < stored; ++cc) {
       double s = 0.0;
       if (cc < k) {
 #pragma unroll
-        for (int i = 0; i < kRsvdR; ++i) s += w[i][cc] * x[i];
+        for (int i = 0; i < kRsvdR; ++i) s = fma(w[i][cc], x[i], s);
       }
       store_elem<E>(outA, (size_t)(ro + cc) * p.d_in + col, s);
     }
   }
 }
 
-int rsvd_blocks(int d_in, int d_out) {
-  const int d = d_in > d_out ? d_in : d_out;
-  const int b = (d + kRsvdTile - 1) / kRsvdTile;
-  return b < kRsvdMaxBlocks ? b : kRsvdMaxBlocks;
-}
-
-size_t rsvd_workspace_bytes(int n, int d_in, int d_out) {
-  const size_t m = (size_t)kRsvdR * kRsvdR * sizeof(double);
-  return (size_t)n * (2 * (size_t)rsvd_blocks(d_in, d_out) + 2) * m;
-}
+// ------------------------------------------------------------------ host
+size_t rsvd_workspace_bytes(int n) { return (size_t)n * kWsMats * kRsvdMat * sizeof(double); }
 
 static RsvdArgs rsvd_args(int n, int d_in, int d_out, int r, const void* A, const void* B, float* sigma,
                           int32_t* status, void* ws) {
@@ -378,61 +420,69 @@ static RsvdArgs rsvd_args(int n, int d_in, int d_out, int r, const void* A, cons
   a.d_in = d_in;
   a.d_out = d_out;
   a.r = r;
-  a.nblk = rsvd_blocks(d_in, d_out);
   a.A = reinterpret_cast<const char*>(A);
   a.B = reinterpret_cast<const char*>(B);
-  const size_t m = (size_t)kRsvdR * kRsvdR;
-  a.part = reinterpret_cast<double*>(ws);
-  a.WB = a.part + (size_t)n * 2 * a.nblk * m;
-  a.WA = a.WB + (size_t)n * m;
+  a.ws = reinterpret_cast<double*>(ws);
   a.sigma = sigma;
   a.status = status;
   return a;
 }
 
+template <typename E>
+static void launch_gram(const RsvdArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)(2 * a.n)), blk(kGramWaves * 64);
+  if (a.r <= 16) hipLaunchKernelGGL((rsvd_gram_kernel<E, 1>), grid, blk, 0, stream, a);
+  else if (a.r <= 32) hipLaunchKernelGGL((rsvd_gram_kernel<E, 2>), grid, blk, 0, stream, a);
+  else hipLaunchKernelGGL((rsvd_gram_kernel<E, 4>), grid, blk, 0, stream, a);
+}
+
 hipError_t launch_rsvd_factor(int n, int d_in, int d_out, int dtype, int r, const void* A, const void* B,
-                              float* sigma, int32_t* status, void* ws, hipStream_t stream) {
+                              float* sigma, int32_t* status, void* ws, hipStream_t stream, int phases) {
   const RsvdArgs a = rsvd_args(n, d_in, d_out, r, A, B, sigma, status, ws);
-  const dim3 blk(kRsvdThreads);
-  if (dtype == LORA_DTYPE_BF16)
-    hipLaunchKernelGGL(rsvd_gram_kernel<BF16>, dim3((unsigned)(n * 2 * a.nblk)), blk, 0, stream, a);
-  else
-    hipLaunchKernelGGL(rsvd_gram_kernel<F32>, dim3((unsigned)(n * 2 * a.nblk)), blk, 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const size_t lds = (size_t)4 * kRsvdR * (kRsvdR + 1) * sizeof(double);
-  static bool raised = false;
-  if (!raised) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(rsvd_core_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    raised = true;
+  hipError_t e;
+  if (phases & 1) {
+    if (dtype == LORA_DTYPE_BF16) launch_gram<BF16>(a, stream);
+    else launch_gram<F32>(a, stream);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(rsvd_core_kernel, dim3((unsigned)n), blk, lds, stream, a);
-  return hipGetLastError();
+  if (phases & 2) {
+    hipLaunchKernelGGL(rsvd_prep_kernel, dim3((unsigned)n), dim3(128), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (phases & 4) {
+    const dim3 grid((unsigned)n), blk(64);
+    if (r <= 8) hipLaunchKernelGGL(rsvd_jacobi_kernel<8>, grid, blk, 0, stream, a);
+    else if (r <= 16) hipLaunchKernelGGL(rsvd_jacobi_kernel<16>, grid, blk, 0, stream, a);
+    else if (r <= 32) hipLaunchKernelGGL(rsvd_jacobi_kernel<32>, grid, blk, 0, stream, a);
+    else hipLaunchKernelGGL(rsvd_jacobi_kernel<64>, grid, blk, 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (phases & 8) {
+    hipLaunchKernelGGL(rsvd_post_kernel, dim3((unsigned)n), dim3(64), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_rsvd_write(const lora_store& s, int r, const void* A, const void* B, const void* ws,
                              hipStream_t stream) {
-  const RsvdArgs f = rsvd_args(s.n, s.d_in, s.d_out, r, A, B, nullptr, nullptr, const_cast<void*>(ws));
   RsvdWriteArgs a;
   a.n = s.n;
   a.d_in = s.d_in;
   a.d_out = s.d_out;
   a.r = r;
   a.R = s.R;
-  a.nbo = (s.d_out + kRsvdThreads - 1) / kRsvdThreads;
+  a.nbo = (s.d_out + 255) / 256;
   a.A = reinterpret_cast<const char*>(A);
   a.B = reinterpret_cast<const char*>(B);
-  a.WB = f.WB;
-  a.WA = f.WA;
+  a.ws = reinterpret_cast<const double*>(ws);
   a.row_off = s.row_off;
   a.rank = s.rank;
   a.true_rank = s.rank + 2 * s.n;  // meta: row_off | rank | scale | true_rank
   a.A_pack = reinterpret_cast<char*>(const_cast<void*>(s.A_pack));
   a.B_pack = reinterpret_cast<char*>(const_cast<void*>(s.B_pack));
-  const int nb = a.nbo + (s.d_in + kRsvdThreads - 1) / kRsvdThreads;
-  const dim3 grid((unsigned)((int64_t)s.n * nb)), blk(kRsvdThreads);
+  const int nb = a.nbo + (s.d_in + 255) / 256;
+  const dim3 grid((unsigned)((int64_t)s.n * nb)), blk(256);
   if (s.dtype == LORA_DTYPE_BF16) hipLaunchKernelGGL(rsvd_write_kernel<BF16>, grid, blk, 0, stream, a);
   else hipLaunchKernelGGL(rsvd_write_kernel<F32>, grid, blk, 0, stream, a);
   return hipGetLastError();

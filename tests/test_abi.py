@@ -310,8 +310,7 @@ def test_jd_apply_rejects_before_launch(lib):
 
 
 def _rsvd_ws(n, d_in, d_out):
-    blocks = min(4, -(-max(d_in, d_out) // 64))
-    return n * (2 * blocks + 2) * 64 * 64 * 8
+    return n * 6 * 64 * 64 * 8
 
 
 @pytest.mark.parametrize("n,d_in,d_out", [(1, 16, 16), (1024, 3584, 3584), (7, 520, 264), (3, 64, 200),
@@ -345,7 +344,18 @@ def test_rsvd_factor_rejects_before_launch(lib):
         assert call(**{k: None}) == 1
     assert call(wsb=_rsvd_ws(4, 256, 128) - 1) == 1
     assert call(ws=FAKE + 8) == 2
-    assert call(n=1 << 22) == 2  # grid too large
+    assert call(A=FAKE + 2) == 2
+    assert call(B=FAKE + 4) == 2
+    assert call(d_in=260) == 2  # rows read as 16-byte vectors: bf16 d a multiple of 8
+    assert call(d_out=132, dtype=1) == 2
+    assert call(n=1 << 24) == 2  # grid too large
+    g = lib.lora_rsvd_factor_phases
+    for bad in (0, 16, -1):
+        assert g(4, 256, 128, 1, 16, FAKE, FAKE, FAKE, FAKE, FAKE, big, None, bad) == 1
+    for good in (1, 2, 4, 8, 6, 15):
+        assert g(0, 256, 128, 1, 16, FAKE, FAKE, FAKE, FAKE, FAKE, big, None, good) == 0
+    assert g(0, 256, 128, 1, 16, FAKE, FAKE, FAKE, FAKE, FAKE, big, None, 1) == 0
+    assert g(4, 256, 128, 1, 65, FAKE, FAKE, FAKE, FAKE, FAKE, big, None, 2) == 2
 
 
 def test_rsvd_write_rejects_before_launch(lib):
@@ -360,5 +370,6 @@ def test_rsvd_write_rejects_before_launch(lib):
     assert f(C.byref(st), 8, FAKE, FAKE, None, big, None) == 1
     assert f(C.byref(st), 8, FAKE, FAKE, FAKE, _rsvd_ws(4, 64, 32) - 1, None) == 1
     assert f(C.byref(st), 8, FAKE, FAKE, FAKE + 8, big, None) == 2
+    assert f(C.byref(st), 8, FAKE + 2, FAKE, FAKE, big, None) == 2
     empty = _store(n=4, d_in=64, d_out=32, r_max=0, R=0)
     assert f(C.byref(empty), 8, None, None, None, 0, None) == 0

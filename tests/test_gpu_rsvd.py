@@ -47,6 +47,7 @@ CASES = {
     "rank1": dict(seed=2, n=3, r=1, d_in=16, d_out=16),
     "rank33": dict(seed=3, n=4, r=33, d_in=200, d_out=136),
     "rank64_ragged": dict(seed=4, n=6, r=64, d_in=520, d_out=264),
+    "rank5_tall": dict(seed=12, n=7, r=5, d_in=1032, d_out=8),
     "square": dict(seed=5, n=3, r=16, d_in=16, d_out=16),
     "k_proj": dict(seed=6, n=4, r=64, d_in=3584, d_out=512),
     "flat": dict(seed=7, n=4, r=32, d_in=256, d_out=128, spectrum="flat"),
@@ -107,6 +108,21 @@ def test_rsvd_parity(name, dtype):
         torch.cuda.synchronize()
         for a in range(w.n):
             _check_adapter(w, store, a, keep[a], TOL[dtype], dtype == "fp32" and w.r > 1)
+
+
+def test_rsvd_phases_match_whole():
+    """The four kernels run one call at a time give the same bits."""
+    dev = device()
+    w = _make("rank64_ragged", "bf16")
+    A, B = _upload(w, dev)
+    note("rsvd phases")
+    f = rs.lora_rsvd_factor(A, B)
+    g = rs.lora_rsvd_factor(A, B, phases=1)
+    for ph in (2, 4, 8):
+        rs.lora_rsvd_factor(A, B, phases=ph, out=g)
+    torch.cuda.synchronize()
+    assert torch.equal(f.sigma, g.sigma) and torch.equal(f.status, g.status)
+    assert torch.equal(f.ws, g.ws)
 
 
 def test_rsvd_ranks_above_r():
