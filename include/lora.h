@@ -357,7 +357,7 @@ int lora_ranks_spectral(int m, const int32_t* r_orig_host, const float* sigma_ho
  * below 1e7); the core's SVD is a one-sided Jacobi iteration in float64.
  *
  * lora_rsvd_workspace_bytes: bytes of ws for n adapters (host only; 0 on
- *   invalid arguments): 6 float64 64 x 64 matrices per adapter, holding W_B
+ *   invalid arguments): 7 float64 64 x 64 matrices per adapter, holding W_B
  *   and W_A between the two calls below.
  * lora_rsvd_factor: stage 1, enqueued on `stream` (four kernels).
  *   A_all  : device [n][r][d_in] (each A_a row-major), dtype elements.

@@ -24,12 +24,15 @@
 //   rsvd_prep_kernel    per adapter, two waves: the Cholesky factors R_B and
 //                       R_A (a pivot at 1e-14 of the largest diagonal entry or
 //                       below flags the adapter), then C = R_B R_A^T.
-//   rsvd_jacobi_kernel  per adapter, one wave, lane j holding column j of C
-//                       in registers: one-sided Jacobi, column pairs (j, j^m)
-//                       for m = 1 .. 2^ceil(log2 r) - 1 (every pair once per
-//                       sweep), partner columns fetched across lanes, until a
-//                       sweep rotates nothing (each pair orthogonal to 1e-15);
-//                       then sigma_j = |C_j|, their descending order, U.
+//   rsvd_jacobi_kernel  per adapter, four waves, lane j holding column j of C
+//                       (a quarter of its rows per wave) in registers:
+//                       one-sided Jacobi, column pairs (j, j^m) for
+//                       m = 1 .. 2^ceil(log2 r) - 1 (every pair once per
+//                       sweep), partner rows fetched across lanes, column
+//                       norms carried through each sweep's rotations, until
+//                       every pair is orthogonal to 1e-15 or a sweep's
+//                       rotations all had |tan| < 1e-8; then sigma_j = |C_j|,
+//                       their descending order, U.
 //   rsvd_post_kernel    per adapter, one wave: W_A = R_B^T U and
 //                       W_B = R_B^-1 U (back substitution), columns in sigma
 //                       order.
@@ -47,8 +50,9 @@ constexpr int kRsvdMat = kRsvdR * kRsvdR;
 constexpr int kGramWaves = 4;
 constexpr int kGramTiles = 10;  // upper 16 x 16 tiles of a 64 x 64 Gram
 // Workspace, float64 matrices per adapter (64 x 64 each): the Grams of B and
-// of A^T, the core C (then U), R_B, W_B, W_A.
-constexpr int kWsGramB = 0, kWsGramA = 1, kWsC = 2, kWsRB = 3, kWsWB = 4, kWsWA = 5, kWsMats = 6;
+// of A^T, the core C, R_B, U, W_B, W_A (W_B and W_A transposed).
+constexpr int kWsGramB = 0, kWsGramA = 1, kWsC = 2, kWsRB = 3, kWsU = 4, kWsWB = 5, kWsWA = 6, kWsMats = 7;
+constexpr int kJacobiWaves = 4;
 
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
@@ -105,7 +109,8 @@ __global__ void __launch_bounds__(kGramWaves * 64) rsvd_gram_kernel(RsvdArgs p) 
     const size_t off = side == 0 ? ((size_t)c * KV * r + (size_t)l * KV) : ((size_t)l * p.d_in + (size_t)c * KV);
     return ld16(base + off * E::kBytes);
   };
-  uint4 q = load(w);
+  // Chunks in flight: three ahead of the one being staged.
+  uint4 q = load(w), q1 = load(kGramWaves + w), q2 = load(2 * kGramWaves + w);
   for (int it = 0; it < iters; ++it) {
     double* tile = st + (it & 1) * 8 * kRsvdR;
     if (l < r) {
@@ -126,7 +131,9 @@ __global__ void __launch_bounds__(kGramWaves * 64) rsvd_gram_kernel(RsvdArgs p) 
         for (int t = 0; t < KV; ++t) tile[t * kRsvdR + l] = (double)f[t];
       }
     }
-    q = load((it + 1) * kGramWaves + w);  // next chunk in flight during the MFMAs
+    q = q1;
+    q1 = q2;
+    q2 = load((it + 3) * kGramWaves + w);
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < KV / 4; ++s) {
@@ -232,49 +239,101 @@ __global__ void __launch_bounds__(128) rsvd_prep_kernel(RsvdArgs p) {
 }
 
 // ---------------------------------------------------------------- Jacobi
-// One wave per adapter; RB = the rank rounded up to a power of two (>= 8):
-// rows and pairings beyond it are all zero.
+// 1 / x and 1 / sqrt(x) for the rotation: the hardware estimates refined by
+// two Newton steps each (to within an ulp or so; the rotation only needs
+// cos^2 + sin^2 = 1 to working precision, not correct rounding).
+__device__ __forceinline__ double rcp_nr(double x) {
+  double y = __builtin_amdgcn_rcp(x);
+  y = fma(y, fma(-x, y, 1.0), y);
+  return fma(y, fma(-x, y, 1.0), y);
+}
+__device__ __forceinline__ double rsq_nr(double x) {
+  double y = __builtin_amdgcn_rsq(x);
+  const double hx = 0.5 * x;
+  y = y * fma(-hx * y, y, 1.5);
+  return y * fma(-hx * y, y, 1.5);
+}
+
+// Workgroup of four waves per adapter; RB = the rank rounded up to a power of
+// two (>= 8), rows and pairings beyond it all zero.  Lane j of wave h holds
+// rows h RB/4 .. (h + 1) RB/4 - 1 of column j in registers.  In the round of
+// m, column j meets column j ^ m: the partner's rows come from lane j ^ m of
+// the same wave; each wave's partial sums (|C_j|^2, |C_p|^2, C_j . C_p) go
+// through LDS and every wave adds the four in wave order, so both lanes of a
+// pair, in all four waves, take the same rotation.
 template <int RB>
-__global__ void __launch_bounds__(64) rsvd_jacobi_kernel(RsvdArgs p) {
-  const int a = blockIdx.x, j = threadIdx.x, r = p.r;
-  double* C = ws_mat(p, a, kWsC);
-  double c[RB];
+__global__ void __launch_bounds__(kJacobiWaves * 64) rsvd_jacobi_kernel(RsvdArgs p) {
+  constexpr int RPW = RB / kJacobiWaves;  // rows per wave
+  __shared__ double part[2][kJacobiWaves][64];
+  const int a = blockIdx.x, tid = threadIdx.x, h = tid >> 6, j = tid & 63, r = p.r;
+  const double* C = ws_mat(p, a, kWsC);
+  double* U = ws_mat(p, a, kWsU);
+  double c[RPW];
 #pragma unroll
-  for (int i = 0; i < RB; ++i) c[i] = C[i * kRsvdR + j];
+  for (int i = 0; i < RPW; ++i) c[i] = C[(h * RPW + i) * kRsvdR + j];
+  int buf = 0;
+  // |C_j|^2 over the four waves' rows, summed in wave order (the same bits in
+  // every wave).
+  auto column_norm = [&](double* nrm) {
+    double s = 0.0;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) s = fma(c[i], c[i], s);
+    part[buf][h][j] = s;
+    __syncthreads();
+    s = 0.0;
+#pragma unroll
+    for (int hh = 0; hh < kJacobiWaves; ++hh) s += part[buf][hh][j];
+    buf ^= 1;
+    *nrm = s;
+  };
   for (int sweep = 0; sweep < 40; ++sweep) {
-    bool rot = false;
-    for (int mm = 1; mm < RB; ++mm) {
+    // Squared norms are computed exactly once a sweep and carried through
+    // its rotations (a rotation by tan = t moves t * gamma from the lower
+    // column's norm to the upper's).
+    double nrm;
+    column_norm(&nrm);
+    bool rot = false;  // a rotation with |tan| >= 1e-8 this sweep
+    for (int mm = 1; mm < RB; ++mm, buf ^= 1) {
       const bool lower = j < (j ^ mm);
-      double y[RB];
-      double own = 0.0, oth = 0.0, g = 0.0;
+      double y[RPW];
+      double g = 0.0;
 #pragma unroll
-      for (int i = 0; i < RB; ++i) {
+      for (int i = 0; i < RPW; ++i) {
         y[i] = __shfl_xor(c[i], mm);
-        own = fma(c[i], c[i], own);
-        oth = fma(y[i], y[i], oth);
         g = fma(c[i], y[i], g);
       }
+      const double pn = __shfl_xor(nrm, mm);
+      part[buf][h][j] = g;
+      __syncthreads();
+      g = 0.0;
+#pragma unroll
+      for (int hh = 0; hh < kJacobiWaves; ++hh) g += part[buf][hh][j];
       // Both lanes of a pair see the same alpha (lower column), beta, gamma.
-      const double al = lower ? own : oth, be = lower ? oth : own;
-      if (g != 0.0 && fabs(g) > 1e-15 * sqrt(al * be)) {
-        const double zeta = (be - al) / (2.0 * g);
-        const double t = (zeta >= 0.0 ? 1.0 : -1.0) / (fabs(zeta) + sqrt(1.0 + zeta * zeta));
-        const double cs = 1.0 / sqrt(1.0 + t * t), sn = cs * t;
+      const double al = lower ? nrm : pn, be = lower ? pn : nrm;
+      if (g != 0.0 && g * g > 1e-30 * (al * be)) {
+        const double zeta = (be - al) * rcp_nr(2.0 * g);
+        const double z2 = fma(zeta, zeta, 1.0);
+        const double t = copysign(rcp_nr(fabs(zeta) + z2 * rsq_nr(z2)), zeta);
+        const double cs = rsq_nr(fma(t, t, 1.0)), sn = cs * t;
         if (lower) {
 #pragma unroll
-          for (int i = 0; i < RB; ++i) c[i] = cs * c[i] - sn * y[i];
+          for (int i = 0; i < RPW; ++i) c[i] = cs * c[i] - sn * y[i];
+          nrm = fma(-t, g, nrm);
         } else {
 #pragma unroll
-          for (int i = 0; i < RB; ++i) c[i] = sn * y[i] + cs * c[i];
+          for (int i = 0; i < RPW; ++i) c[i] = sn * y[i] + cs * c[i];
+          nrm = fma(t, g, nrm);
         }
-        rot = true;
+        rot = rot || fabs(t) >= 1e-8;
       }
     }
+    // Every wave took the same decisions, so every wave leaves together.  A
+    // sweep whose rotations all had |tan| < 1e-8 leaves off-diagonal terms
+    // of that order squared (quadratic convergence): no further sweep.
     if (!__any(rot)) break;
   }
-  double s2 = 0.0;
-#pragma unroll
-  for (int i = 0; i < RB; ++i) s2 = fma(c[i], c[i], s2);
+  double s2;
+  column_norm(&s2);
   const double sg = sqrt(s2);
   // Descending order, ties (and a NaN, ranked last) by lane: a permutation.
   const double key = sg == sg ? sg : -1.0;
@@ -284,21 +343,22 @@ __global__ void __launch_bounds__(64) rsvd_jacobi_kernel(RsvdArgs p) {
     pos += (o > key || (o == key && k < j)) ? 1 : 0;
   }
   const double inv = sg > 0.0 ? 1.0 / sg : 0.0;
-  // U in sigma order, in place of C (every lane has read its column).
 #pragma unroll
-  for (int i = 0; i < RB; ++i) C[i * kRsvdR + pos] = c[i] * inv;
-  if (j < r) p.sigma[(size_t)a * r + pos] = (float)sg;
+  for (int i = 0; i < RPW; ++i) U[(h * RPW + i) * kRsvdR + pos] = c[i] * inv;
+  for (int i = RB + h; i < kRsvdR; i += kJacobiWaves) U[i * kRsvdR + pos] = 0.0;
+  if (h == 0 && j < r) p.sigma[(size_t)a * r + pos] = (float)sg;
 }
 
 // ------------------------------------------------------------------ post
 // One wave per adapter, lane c: column c of W_A = R_B^T U and of
-// W_B = R_B^-1 U (row-oriented back substitution in LDS).
+// W_B = R_B^-1 U (row-oriented back substitution in LDS), each written as
+// row c of the transposed matrix.
 __global__ void __launch_bounds__(64) rsvd_post_kernel(RsvdArgs p) {
   __shared__ double rb[kRsvdR][kRsvdR + 1];
   __shared__ double x[kRsvdR][kRsvdR + 1];
   const int a = blockIdx.x, c = threadIdx.x, r = p.r;
   const double* RB = ws_mat(p, a, kWsRB);
-  const double* U = ws_mat(p, a, kWsC);
+  const double* U = ws_mat(p, a, kWsU);
   double* WB = ws_mat(p, a, kWsWB);
   double* WA = ws_mat(p, a, kWsWA);
   double u[kRsvdR];
@@ -309,32 +369,29 @@ __global__ void __launch_bounds__(64) rsvd_post_kernel(RsvdArgs p) {
     x[k][c] = u[k];
   }
   __syncthreads();
-  for (int i = 0; i < r; ++i) {
+  // Stored transposed (column c of W at W[c][0 .. 64)), rows past r zero.
+  for (int i = 0; i < kRsvdR; ++i) {  // rb and u are zero past r
     double s = 0.0;
 #pragma unroll
     for (int k = 0; k < kRsvdR; ++k) s = fma(rb[k][i], u[k], s);  // rb is zero below the diagonal
-    WA[i * kRsvdR + c] = s;
+    WA[c * kRsvdR + i] = s;
   }
+  for (int i = r; i < kRsvdR; ++i) WB[c * kRsvdR + i] = 0.0;
   for (int i = r - 1; i >= 0; --i) {
     double s = x[i][c];
     for (int k = i + 1; k < r; ++k) s -= rb[i][k] * x[k][c];
     s /= rb[i][i];
     x[i][c] = s;
-    WB[i * kRsvdR + c] = s;
+    WB[c * kRsvdR + i] = s;
   }
 }
 
 // ----------------------------------------------------------------- write
 struct RsvdWriteArgs {
   int n, d_in, d_out, r, R, nbo;  // nbo: row blocks of B' (256 rows each)
-  const char* A;
-  const char* B;
-  const double* ws;
   const int32_t* row_off;
   const int32_t* rank;       // stored rank
   const int32_t* true_rank;  // retained rank k_a
-  char* A_pack;
-  char* B_pack;
 };
 
 template <typename E>
@@ -344,12 +401,17 @@ __device__ __forceinline__ void store_elem(typename E::storage* out, size_t i, d
 }
 
 // Workgroup (adapter, block): blocks [0, nbo) write 256 rows of B' each (a
-// thread per row), the rest 256 columns of A' each (a thread per column).
+// thread per row), the rest 256 columns of A' each (a thread per column);
+// the thread holds its row of B (column of A) in float64 registers.
 // Components c < min(k_a, r) come from W; the others (a retained rank above
-// r, or padding up to the stored rank) are zero.
-template <typename E>
-__global__ void __launch_bounds__(256) rsvd_write_kernel(RsvdWriteArgs p) {
-  __shared__ double w[kRsvdR][kRsvdR];
+// r, or padding up to the stored rank) are zero.  W is read with addresses
+// uniform over the workgroup (the separate restrict-qualified arguments let
+// those loads go through the scalar unit, one operand per FMA from SGPRs).
+template <typename E, int RB>
+__global__ void __launch_bounds__(256) rsvd_write_kernel(RsvdWriteArgs p, const char* __restrict__ A,
+                                                         const char* __restrict__ B, const double* __restrict__ ws,
+                                                         typename E::storage* __restrict__ outA,
+                                                         typename E::storage* __restrict__ outB) {
   const int nb = p.nbo + (p.d_in + 255) / 256;
   const int a = blockIdx.x / nb, blk = blockIdx.x - a * nb;
   const int tid = threadIdx.x, r = p.r;
@@ -357,19 +419,15 @@ __global__ void __launch_bounds__(256) rsvd_write_kernel(RsvdWriteArgs p) {
   const int k = min(p.true_rank[a], r);
   if (stored <= 0 || ro < 0 || ro > p.R - stored) return;  // uniform per workgroup
   const bool bside = blk < p.nbo;
-  const double* W = p.ws + ((size_t)a * kWsMats + (bside ? kWsWB : kWsWA)) * kRsvdMat;
-  for (int e = tid; e < kRsvdMat; e += 256) w[e / kRsvdR][e % kRsvdR] = e / kRsvdR < r ? W[e] : 0.0;
-  __syncthreads();
-  typename E::storage* outA = reinterpret_cast<typename E::storage*>(p.A_pack);
-  typename E::storage* outB = reinterpret_cast<typename E::storage*>(p.B_pack);
-  double x[kRsvdR];
+  const double* __restrict__ W = ws + ((size_t)a * kWsMats + (bside ? kWsWB : kWsWA)) * kRsvdMat;
+  double x[RB];
   if (bside) {
     const int o = blk * 256 + tid;
     if (o >= p.d_out) return;
-    const char* brow = p.B + ((size_t)a * p.d_out + o) * r * E::kBytes;
+    const char* brow = B + ((size_t)a * p.d_out + o) * r * E::kBytes;
     if (r % E::kVec == 0) {  // rows are 16-byte aligned: vector loads
 #pragma unroll
-      for (int v = 0; v < kRsvdR / E::kVec; ++v) {
+      for (int v = 0; v < RB / E::kVec; ++v) {
         float f[E::kVec];
         if (v * E::kVec < r) {
           E::widen(ld16(brow + (size_t)v * 16), f);
@@ -382,28 +440,28 @@ __global__ void __launch_bounds__(256) rsvd_write_kernel(RsvdWriteArgs p) {
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < kRsvdR; ++i) x[i] = i < r ? load_elem<E>(brow, i) : 0.0;
+      for (int i = 0; i < RB; ++i) x[i] = i < r ? load_elem<E>(brow, i) : 0.0;
     }
     const size_t base = (size_t)ro * p.d_out + (size_t)o * stored;
     for (int cc = 0; cc < stored; ++cc) {
       double s = 0.0;
       if (cc < k) {
 #pragma unroll
-        for (int i = 0; i < kRsvdR; ++i) s = fma(x[i], w[i][cc], s);
+        for (int i = 0; i < RB; ++i) s = fma(x[i], W[cc * kRsvdR + i], s);
       }
       store_elem<E>(outB, base + cc, s);
     }
   } else {
     const int col = (blk - p.nbo) * 256 + tid;
     if (col >= p.d_in) return;
-    const char* abase = p.A + (size_t)a * r * p.d_in * E::kBytes;
+    const char* abase = A + (size_t)a * r * p.d_in * E::kBytes;
 #pragma unroll
-    for (int i = 0; i < kRsvdR; ++i) x[i] = i < r ? load_elem<E>(abase, (int64_t)i * p.d_in + col) : 0.0;
+    for (int i = 0; i < RB; ++i) x[i] = i < r ? load_elem<E>(abase, (int64_t)i * p.d_in + col) : 0.0;
     for (int cc = 0; cc < stored; ++cc) {
       double s = 0.0;
       if (cc < k) {
 #pragma unroll
-        for (int i = 0; i < kRsvdR; ++i) s = fma(w[i][cc], x[i], s);
+        for (int i = 0; i < RB; ++i) s = fma(W[cc * kRsvdR + i], x[i], s);
       }
       store_elem<E>(outA, (size_t)(ro + cc) * p.d_in + col, s);
     }
@@ -450,7 +508,7 @@ hipError_t launch_rsvd_factor(int n, int d_in, int d_out, int dtype, int r, cons
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (phases & 4) {
-    const dim3 grid((unsigned)n), blk(64);
+    const dim3 grid((unsigned)n), blk(kJacobiWaves * 64);
     if (r <= 8) hipLaunchKernelGGL(rsvd_jacobi_kernel<8>, grid, blk, 0, stream, a);
     else if (r <= 16) hipLaunchKernelGGL(rsvd_jacobi_kernel<16>, grid, blk, 0, stream, a);
     else if (r <= 32) hipLaunchKernelGGL(rsvd_jacobi_kernel<32>, grid, blk, 0, stream, a);
@@ -464,6 +522,21 @@ hipError_t launch_rsvd_factor(int n, int d_in, int d_out, int dtype, int r, cons
   return hipSuccess;
 }
 
+template <typename E>
+static void launch_write(const RsvdWriteArgs& a, dim3 grid, const void* A, const void* B, const void* ws,
+                         const lora_store& s, hipStream_t stream) {
+  const char* pa = reinterpret_cast<const char*>(A);
+  const char* pb = reinterpret_cast<const char*>(B);
+  const double* w = reinterpret_cast<const double*>(ws);
+  auto* oa = reinterpret_cast<typename E::storage*>(const_cast<void*>(s.A_pack));
+  auto* ob = reinterpret_cast<typename E::storage*>(const_cast<void*>(s.B_pack));
+  const dim3 blk(256);
+  if (a.r <= 8) hipLaunchKernelGGL((rsvd_write_kernel<E, 8>), grid, blk, 0, stream, a, pa, pb, w, oa, ob);
+  else if (a.r <= 16) hipLaunchKernelGGL((rsvd_write_kernel<E, 16>), grid, blk, 0, stream, a, pa, pb, w, oa, ob);
+  else if (a.r <= 32) hipLaunchKernelGGL((rsvd_write_kernel<E, 32>), grid, blk, 0, stream, a, pa, pb, w, oa, ob);
+  else hipLaunchKernelGGL((rsvd_write_kernel<E, 64>), grid, blk, 0, stream, a, pa, pb, w, oa, ob);
+}
+
 hipError_t launch_rsvd_write(const lora_store& s, int r, const void* A, const void* B, const void* ws,
                              hipStream_t stream) {
   RsvdWriteArgs a;
@@ -473,18 +546,13 @@ hipError_t launch_rsvd_write(const lora_store& s, int r, const void* A, const vo
   a.r = r;
   a.R = s.R;
   a.nbo = (s.d_out + 255) / 256;
-  a.A = reinterpret_cast<const char*>(A);
-  a.B = reinterpret_cast<const char*>(B);
-  a.ws = reinterpret_cast<const double*>(ws);
   a.row_off = s.row_off;
   a.rank = s.rank;
   a.true_rank = s.rank + 2 * s.n;  // meta: row_off | rank | scale | true_rank
-  a.A_pack = reinterpret_cast<char*>(const_cast<void*>(s.A_pack));
-  a.B_pack = reinterpret_cast<char*>(const_cast<void*>(s.B_pack));
   const int nb = a.nbo + (s.d_in + 255) / 256;
-  const dim3 grid((unsigned)((int64_t)s.n * nb)), blk(256);
-  if (s.dtype == LORA_DTYPE_BF16) hipLaunchKernelGGL(rsvd_write_kernel<BF16>, grid, blk, 0, stream, a);
-  else hipLaunchKernelGGL(rsvd_write_kernel<F32>, grid, blk, 0, stream, a);
+  const dim3 grid((unsigned)((int64_t)s.n * nb));
+  if (s.dtype == LORA_DTYPE_BF16) launch_write<BF16>(a, grid, A, B, ws, s, stream);
+  else launch_write<F32>(a, grid, A, B, ws, s, stream);
   return hipGetLastError();
 }
 

@@ -310,7 +310,7 @@ def test_jd_apply_rejects_before_launch(lib):
 
 
 def _rsvd_ws(n, d_in, d_out):
-    return n * 6 * 64 * 64 * 8
+    return n * 7 * 64 * 64 * 8
 
 
 @pytest.mark.parametrize("n,d_in,d_out", [(1, 16, 16), (1024, 3584, 3584), (7, 520, 264), (3, 64, 200),
