@@ -76,67 +76,95 @@ __device__ __forceinline__ double load_elem(const char* base, int64_t i) {
 }
 
 // ------------------------------------------------------------------ Gram
+// Wait for this wave's LDS writes before its lanes read each other's: LDS
+// operations of one wave complete in order, so only the wave itself waits.
+__device__ __forceinline__ void wave_lds_sync() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Workgroup (adapter, side): side 0 = B (rows of r elements), side 1 = A^T
-// (the columns of A).  A chunk is E::kVec rows of M: side 0 reads it as r
+// (the columns of A).  A sub-chunk is E::kVec rows of M: side 0 reads it as r
 // contiguous 16-byte vectors of B (lane l < r the l-th), side 1 as one
-// 16-byte vector per row of A (lane l < r: A[l][k0 .. k0 + kVec)).  Each wave
-// stages its chunk in float64 in its own LDS tile (zero outside the r
-// columns) and feeds 16 x 16 x 4 MFMAs: lane l holds M[k0 + l/16][16 b + l%16]
-// as the A operand of tile row b and the B operand of tile column b.
+// 16-byte vector per row of A (lane l < r: A[l][k0 .. k0 + kVec)).  Wave w
+// takes every fourth group of kGramSub sub-chunks, stages it in float64 in
+// its own LDS tile (zero outside the r columns) and feeds 16 x 16 x 4 MFMAs:
+// lane l holds M[k0 + l/16][16 b + l%16] as the A operand of tile row b and
+// the B operand of tile column b.
+constexpr int kGramSub = 2;
 template <typename E, int NB>
 __global__ void __launch_bounds__(kGramWaves * 64) rsvd_gram_kernel(RsvdArgs p) {
-  constexpr int KV = E::kVec;  // rows per chunk
-  constexpr int kStage = kGramWaves * 2 * 8 * kRsvdR;             // doubles
-  constexpr int kRed = (kGramWaves - 1) * kGramTiles * 256;         // doubles
-  __shared__ double lds[kStage > kRed ? kStage : kRed];
+  constexpr int KV = E::kVec;                // rows per sub-chunk
+  constexpr int kRows = kGramSub * KV;       // rows per group
+  constexpr int kStage = kGramWaves * kRows * kRsvdR;         // doubles
+  constexpr int kRed = (kGramWaves - 1) * kGramTiles * 256;   // doubles
+  __shared__ __align__(16) double lds[kStage > kRed ? kStage : kRed];
   const int a = blockIdx.x >> 1, side = blockIdx.x & 1;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = p.r;
   const int D = side == 0 ? p.d_out : p.d_in;
-  const int nchunks = D / KV;
-  const int iters = (nchunks + kGramWaves - 1) / kGramWaves;
-  double* st = lds + (size_t)w * 2 * 8 * kRsvdR;
-  for (int e = l; e < 2 * 8 * kRsvdR; e += 64) st[e] = 0.0;
+  const int nsub = D / KV;
+  const int ngroups = (nsub + kGramSub - 1) / kGramSub;
+  double* tile = lds + (size_t)w * kRows * kRsvdR;
+  for (int e = l; e < kRows * kRsvdR; e += 64) tile[e] = 0.0;
   const char* base = side == 0 ? p.B + (size_t)a * p.d_out * r * E::kBytes
                                : p.A + (size_t)a * r * p.d_in * E::kBytes;
   // Side 0: the kVec elements of lane l's vector sit at flat offsets
-  // l * KV + t of the chunk, i.e. (row, col) = divmod(l * KV + t, r).
+  // l * KV + t of the sub-chunk, i.e. (row, col) = divmod(l * KV + t, r).
   const int e0 = l * KV, row0 = e0 / r, col0 = e0 - row0 * r;
+  const bool whole = r % KV == 0;  // side 0: a vector never crosses a row
   f64x4_t acc[kGramTiles];
 #pragma unroll
   for (int t = 0; t < kGramTiles; ++t) acc[t] = (f64x4_t){0.0, 0.0, 0.0, 0.0};
   auto load = [&](int c) -> uint4 {
-    if (c >= nchunks || l >= r) return make_uint4(0u, 0u, 0u, 0u);
+    if (c >= nsub || l >= r) return make_uint4(0u, 0u, 0u, 0u);
     const size_t off = side == 0 ? ((size_t)c * KV * r + (size_t)l * KV) : ((size_t)l * p.d_in + (size_t)c * KV);
     return ld16(base + off * E::kBytes);
   };
-  // Chunks in flight: three ahead of the one being staged.
-  uint4 q = load(w), q1 = load(kGramWaves + w), q2 = load(2 * kGramWaves + w);
-  for (int it = 0; it < iters; ++it) {
-    double* tile = st + (it & 1) * 8 * kRsvdR;
-    if (l < r) {
-      float f[KV];
-      E::widen(q, f);
-      if (side == 0) {
-        int row = row0, col = col0;
+  // Groups in flight: the one being staged and the next.
+  uint4 q[2][kGramSub];
 #pragma unroll
-        for (int t = 0; t < KV; ++t) {
-          tile[row * kRsvdR + col] = (double)f[t];
-          if (++col == r) {
-            col = 0;
-            ++row;
+  for (int u = 0; u < kGramSub; ++u) {
+    q[0][u] = load(w * kGramSub + u);
+    q[1][u] = load((w + kGramWaves) * kGramSub + u);
+  }
+  for (int g = w; g < ngroups; g += kGramWaves) {
+#pragma unroll
+    for (int u = 0; u < kGramSub; ++u) {
+      if (l < r) {
+        float f[KV];
+        E::widen(q[0][u], f);
+        double* sub = tile + u * KV * kRsvdR;
+        if (side == 1) {
+#pragma unroll
+          for (int t = 0; t < KV; ++t) sub[t * kRsvdR + l] = (double)f[t];
+        } else if (whole) {
+#pragma unroll
+          for (int t = 0; t < KV; t += 2) {
+            double2 v2;
+            v2.x = (double)f[t];
+            v2.y = (double)f[t + 1];
+            *reinterpret_cast<double2*>(&sub[row0 * kRsvdR + col0 + t]) = v2;
+          }
+        } else {
+          int row = row0, col = col0;
+#pragma unroll
+          for (int t = 0; t < KV; ++t) {
+            sub[row * kRsvdR + col] = (double)f[t];
+            if (++col == r) {
+              col = 0;
+              ++row;
+            }
           }
         }
-      } else {
-#pragma unroll
-        for (int t = 0; t < KV; ++t) tile[t * kRsvdR + l] = (double)f[t];
       }
+      q[0][u] = q[1][u];
+      q[1][u] = load((g + 2 * kGramWaves) * kGramSub + u);
     }
-    q = q1;
-    q1 = q2;
-    q2 = load((it + 3) * kGramWaves + w);
-    __syncthreads();
+    wave_lds_sync();
 #pragma unroll
-    for (int s = 0; s < KV / 4; ++s) {
+    for (int s = 0; s < kRows / 4; ++s) {
       double x[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) x[b] = b < NB ? tile[(4 * s + (l >> 4)) * kRsvdR + 16 * b + (l & 15)] : 0.0;
@@ -147,8 +175,12 @@ __global__ void __launch_bounds__(kGramWaves * 64) rsvd_gram_kernel(RsvdArgs p) 
         for (int jb = ib; jb < 4; ++jb, ++t)
           if (jb < NB) acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(x[ib], x[jb], acc[t], 0, 0, 0);
     }
+    // The MFMAs consumed this wave's reads before the next group's writes
+    // (which cover every (row, column < r) of the tile, with zeros past the
+    // end of M).
+    wave_lds_sync();
   }
-  __syncthreads();  // every wave is done with its staging tiles
+  __syncthreads();  // every wave is done with its staging tile
   if (w > 0) {
 #pragma unroll
     for (int t = 0; t < kGramTiles; ++t)
@@ -400,18 +432,44 @@ __device__ __forceinline__ void store_elem(typename E::storage* out, size_t i, d
   else out[i] = (float)v;
 }
 
+// out[c * step] = sum_i x[i] W[c][i] (W transposed) for c < k, 0 for
+// k <= c < stored.  Four interleaved partial sums per component keep the
+// float64 FMA chain short; W[c][0 .. RB) is read with uniform addresses.
+template <typename E, int RB>
+__device__ __forceinline__ void write_components(const double* x, const double* __restrict__ W, int k, int stored,
+                                                 typename E::storage* out, size_t step) {
+  for (int c = 0; c < stored; ++c) {
+    double s = 0.0;
+    if (c < k) {
+      double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int i = 0; i < RB; ++i) acc[i & 3] = fma(x[i], W[c * kRsvdR + i], acc[i & 3]);
+      s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    }
+    store_elem<E>(out, (size_t)c * step, s);
+  }
+}
+
 // Workgroup (adapter, block): blocks [0, nbo) write 256 rows of B' each (a
-// thread per row), the rest 256 columns of A' each (a thread per column);
-// the thread holds its row of B (column of A) in float64 registers.
-// Components c < min(k_a, r) come from W; the others (a retained rank above
-// r, or padding up to the stored rank) are zero.  W is read with addresses
-// uniform over the workgroup (the separate restrict-qualified arguments let
-// those loads go through the scalar unit, one operand per FMA from SGPRs).
+// thread per row), the rest 256 columns of A' each (a thread per column).
+// The workgroup first copies its tile of B (256 whole rows, when rows are
+// 16-byte multiples) or of A (all r rows, 256 columns) into LDS with
+// coalesced 16-byte loads; each thread then takes its row or column from
+// LDS into float64 registers.  Components c < min(k_a, r) come from W; the
+// others (a retained rank above r, or padding up to the stored rank) are
+// zero.  W is read with addresses uniform over the workgroup (the separate
+// restrict-qualified arguments let those loads go through the scalar unit,
+// one operand per FMA from SGPRs).
 template <typename E, int RB>
 __global__ void __launch_bounds__(256) rsvd_write_kernel(RsvdWriteArgs p, const char* __restrict__ A,
                                                          const char* __restrict__ B, const double* __restrict__ ws,
                                                          typename E::storage* __restrict__ outA,
                                                          typename E::storage* __restrict__ outB) {
+  typedef typename E::storage S;
+  constexpr int KV = E::kVec;
+  constexpr int kRowB = RB + KV;  // padded B row in LDS (elements), 16-byte multiple
+  constexpr int kTileB = 256 * kRowB, kTileA = RB * 256;
+  __shared__ __align__(16) S tile[kTileB > kTileA ? kTileB : kTileA];
   const int nb = p.nbo + (p.d_in + 255) / 256;
   const int a = blockIdx.x / nb, blk = blockIdx.x - a * nb;
   const int tid = threadIdx.x, r = p.r;
@@ -422,49 +480,55 @@ __global__ void __launch_bounds__(256) rsvd_write_kernel(RsvdWriteArgs p, const 
   const double* __restrict__ W = ws + ((size_t)a * kWsMats + (bside ? kWsWB : kWsWA)) * kRsvdMat;
   double x[RB];
   if (bside) {
-    const int o = blk * 256 + tid;
-    if (o >= p.d_out) return;
-    const char* brow = B + ((size_t)a * p.d_out + o) * r * E::kBytes;
-    if (r % E::kVec == 0) {  // rows are 16-byte aligned: vector loads
+    const int o0 = blk * 256, rows = min(256, p.d_out - o0);
+    const int o = o0 + tid;
+    const char* bblk = B + ((size_t)a * p.d_out + o0) * r * E::kBytes;
+    if (r % KV == 0) {
+      const int vpr = r / KV;  // 16-byte vectors per row
+      for (int v = tid; v < rows * vpr; v += 256) {
+        const int row = v / vpr, c0 = (v - row * vpr) * KV;
+        *reinterpret_cast<uint4*>(&tile[row * kRowB + c0]) = ld16(bblk + (size_t)v * 16);
+      }
+      __syncthreads();
+      if (tid >= rows) return;
 #pragma unroll
-      for (int v = 0; v < RB / E::kVec; ++v) {
-        float f[E::kVec];
-        if (v * E::kVec < r) {
-          E::widen(ld16(brow + (size_t)v * 16), f);
+      for (int vv = 0; vv < RB / KV; ++vv) {
+        float f[KV];
+        if (vv * KV < r) {
+          E::widen(*reinterpret_cast<const uint4*>(&tile[tid * kRowB + vv * KV]), f);
         } else {
 #pragma unroll
-          for (int t = 0; t < E::kVec; ++t) f[t] = 0.f;
+          for (int t = 0; t < KV; ++t) f[t] = 0.f;
         }
 #pragma unroll
-        for (int t = 0; t < E::kVec; ++t) x[v * E::kVec + t] = (double)f[t];
+        for (int t = 0; t < KV; ++t) x[vv * KV + t] = (double)f[t];
       }
     } else {
+      if (tid >= rows) return;
+      const char* brow = bblk + (size_t)tid * r * E::kBytes;
 #pragma unroll
       for (int i = 0; i < RB; ++i) x[i] = i < r ? load_elem<E>(brow, i) : 0.0;
     }
-    const size_t base = (size_t)ro * p.d_out + (size_t)o * stored;
-    for (int cc = 0; cc < stored; ++cc) {
-      double s = 0.0;
-      if (cc < k) {
-#pragma unroll
-        for (int i = 0; i < RB; ++i) s = fma(x[i], W[cc * kRsvdR + i], s);
-      }
-      store_elem<E>(outB, base + cc, s);
-    }
+    S* out = outB + (size_t)ro * p.d_out + (size_t)o * stored;
+    write_components<E, RB>(x, W, k, stored, out, 1);
   } else {
-    const int col = (blk - p.nbo) * 256 + tid;
-    if (col >= p.d_in) return;
-    const char* abase = A + (size_t)a * r * p.d_in * E::kBytes;
-#pragma unroll
-    for (int i = 0; i < RB; ++i) x[i] = i < r ? load_elem<E>(abase, (int64_t)i * p.d_in + col) : 0.0;
-    for (int cc = 0; cc < stored; ++cc) {
-      double s = 0.0;
-      if (cc < k) {
-#pragma unroll
-        for (int i = 0; i < RB; ++i) s = fma(W[cc * kRsvdR + i], x[i], s);
-      }
-      store_elem<E>(outA, (size_t)(ro + cc) * p.d_in + col, s);
+    const int col0 = (blk - p.nbo) * 256, cols = min(256, p.d_in - col0);
+    const char* ablk = A + ((size_t)a * r * p.d_in + col0) * E::kBytes;
+    const int vpr = 256 / KV;  // 16-byte vectors per tile row
+    for (int v = tid; v < r * vpr; v += 256) {
+      const int i = v / vpr, c0 = (v - i * vpr) * KV;
+      if (c0 < cols)  // d_in is a multiple of KV: a vector is wholly in or out
+        *reinterpret_cast<uint4*>(&tile[i * 256 + c0]) = ld16(ablk + ((size_t)i * p.d_in + c0) * E::kBytes);
     }
+    __syncthreads();
+    if (tid >= cols) return;
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      if constexpr (E::kBytes == 2) x[i] = i < r ? (double)__uint_as_float((uint32_t)tile[i * 256 + tid] << 16) : 0.0;
+      else x[i] = i < r ? (double)tile[i * 256 + tid] : 0.0;
+    }
+    S* out = outA + (size_t)ro * p.d_in + col0 + tid;
+    write_components<E, RB>(x, W, k, stored, out, p.d_in);
   }
 }
 
