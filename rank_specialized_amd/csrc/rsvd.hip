@@ -24,8 +24,8 @@
 //   rsvd_prep_kernel    per adapter, two waves: the Cholesky factors R_B and
 //                       R_A (a pivot at 1e-14 of the largest diagonal entry or
 //                       below flags the adapter), then C = R_B R_A^T.
-//   rsvd_jacobi_kernel  per adapter, four waves, lane j holding column j of C
-//                       (a quarter of its rows per wave) in registers:
+//   rsvd_jacobi_kernel  per adapter, two waves, lane j holding column j of C
+//                       (half of its rows per wave) in registers:
 //                       one-sided Jacobi, column pairs (j, j^m) for
 //                       m = 1 .. 2^ceil(log2 r) - 1 (every pair once per
 //                       sweep), partner rows fetched across lanes, column
@@ -52,7 +52,7 @@ constexpr int kGramTiles = 10;  // upper 16 x 16 tiles of a 64 x 64 Gram
 // Workspace, float64 matrices per adapter (64 x 64 each): the Grams of B and
 // of A^T, the core C, R_B, U, W_B, W_A (W_B and W_A transposed).
 constexpr int kWsGramB = 0, kWsGramA = 1, kWsC = 2, kWsRB = 3, kWsU = 4, kWsWB = 5, kWsWA = 6, kWsMats = 7;
-constexpr int kJacobiWaves = 4;
+constexpr int kJacobiWaves = 2;
 
 typedef double f64x4_t __attribute__((ext_vector_type(4)));
 
@@ -286,13 +286,13 @@ __device__ __forceinline__ double rsq_nr(double x) {
   return y * fma(-hx * y, y, 1.5);
 }
 
-// Workgroup of four waves per adapter; RB = the rank rounded up to a power of
+// Workgroup of two waves per adapter; RB = the rank rounded up to a power of
 // two (>= 8), rows and pairings beyond it all zero.  Lane j of wave h holds
-// rows h RB/4 .. (h + 1) RB/4 - 1 of column j in registers.  In the round of
+// rows h RB/2 .. (h + 1) RB/2 - 1 of column j in registers.  In the round of
 // m, column j meets column j ^ m: the partner's rows come from lane j ^ m of
-// the same wave; each wave's partial sums (|C_j|^2, |C_p|^2, C_j . C_p) go
-// through LDS and every wave adds the four in wave order, so both lanes of a
-// pair, in all four waves, take the same rotation.
+// the same wave; each wave's partial dot product C_j . C_p goes through LDS
+// and every wave adds the parts in wave order, so both lanes of a
+// pair, in both waves, take the same rotation.
 template <int RB>
 __global__ void __launch_bounds__(kJacobiWaves * 64) rsvd_jacobi_kernel(RsvdArgs p) {
   constexpr int RPW = RB / kJacobiWaves;  // rows per wave
@@ -328,18 +328,21 @@ __global__ void __launch_bounds__(kJacobiWaves * 64) rsvd_jacobi_kernel(RsvdArgs
     for (int mm = 1; mm < RB; ++mm, buf ^= 1) {
       const bool lower = j < (j ^ mm);
       double y[RPW];
-      double g = 0.0;
+      double g4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
       for (int i = 0; i < RPW; ++i) {
         y[i] = __shfl_xor(c[i], mm);
-        g = fma(c[i], y[i], g);
+        g4[i & 3] = fma(c[i], y[i], g4[i & 3]);
       }
+      double g = (g4[0] + g4[1]) + (g4[2] + g4[3]);
       const double pn = __shfl_xor(nrm, mm);
-      part[buf][h][j] = g;
-      __syncthreads();
-      g = 0.0;
+      if constexpr (kJacobiWaves > 1) {
+        part[buf][h][j] = g;
+        __syncthreads();
+        g = 0.0;
 #pragma unroll
-      for (int hh = 0; hh < kJacobiWaves; ++hh) g += part[buf][hh][j];
+        for (int hh = 0; hh < kJacobiWaves; ++hh) g += part[buf][hh][j];
+      }
       // Both lanes of a pair see the same alpha (lower column), beta, gamma.
       const double al = lower ? nrm : pn, be = lower ? pn : nrm;
       if (g != 0.0 && g * g > 1e-30 * (al * be)) {
@@ -347,15 +350,11 @@ __global__ void __launch_bounds__(kJacobiWaves * 64) rsvd_jacobi_kernel(RsvdArgs
         const double z2 = fma(zeta, zeta, 1.0);
         const double t = copysign(rcp_nr(fabs(zeta) + z2 * rsq_nr(z2)), zeta);
         const double cs = rsq_nr(fma(t, t, 1.0)), sn = cs * t;
-        if (lower) {
+        // Lower column: cs c - sn c_partner; upper: cs c + sn c_partner.
+        const double ssn = lower ? -sn : sn;
 #pragma unroll
-          for (int i = 0; i < RPW; ++i) c[i] = cs * c[i] - sn * y[i];
-          nrm = fma(-t, g, nrm);
-        } else {
-#pragma unroll
-          for (int i = 0; i < RPW; ++i) c[i] = sn * y[i] + cs * c[i];
-          nrm = fma(t, g, nrm);
-        }
+        for (int i = 0; i < RPW; ++i) c[i] = fma(ssn, y[i], cs * c[i]);
+        nrm = fma(lower ? -t : t, g, nrm);
         rot = rot || fabs(t) >= 1e-8;
       }
     }
