@@ -34,8 +34,11 @@ sys.path.insert(0, ROOT)
 METRIC = "LoRA-delta tokens/s and achieved HBM GB/s (% of ~8 TB/s peak), 1 MI355X"
 PEAK_GBPS = 8000.0
 COLD_BYTES = 2.0e9  # rotation set size: well past the 256 MB Infinity Cache
-KERNEL_SOURCES = ["shrink.hip", "expand.hip", "decode.hip", "jd.hip", "rsvd.hip", "tile_ops.h", "device_common.h",
-                  "plan.h"]
+# Sources each measured kernel family is built from: a counter record is used
+# only while the sources of its family are unchanged.
+KERNEL_SOURCES = ["shrink.hip", "expand.hip", "decode.hip", "tile_ops.h", "device_common.h", "plan.h"]
+JD_SOURCES = KERNEL_SOURCES + ["jd.hip"]
+RSVD_SOURCES = ["rsvd.hip", "device_common.h", "plan.h"]
 PEAK_FP64_TFLOPS = 78.6  # 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2.4 GHz
 
 WORKLOAD_NAMES = {
@@ -80,9 +83,9 @@ def parse_args():
     return p.parse_args()
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(sources=None) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
+    for name in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, "rank_specialized_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -233,16 +236,16 @@ def time_kernels(rs, torch, copies, ids, ws, steps, warmup, graph=True):
     return out
 
 
-def traffic_for(workload: str, kernel: str):
+def traffic_for(workload: str, kernel: str, sources=None):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel sources."""
+    were taken on the current sources of that kernel family."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     ent = rec.get(workload, {}).get(kernel)
-    if not ent or ent.get("kernel_sources_sha") != kernel_source_digest():
+    if not ent or ent.get("kernel_sources_sha") != kernel_source_digest(sources):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -277,13 +280,23 @@ def summarize_pmc(key: str, fetch_dir: str, write_dir: str):
         return max(vals) * 1024.0 / CALIBRATE_BYTES
 
     cf, cw = calib(fetch), calib(write)
-    wl = build_workload(key)
-    m = wl.module
-    nb = algorithmic_bytes(wl.ids, m.ranks, m.n, m.d_in, m.d_out, 2 if wl.dtype == "bf16" else 4)
+    if key.startswith("rsvd-"):
+        import rank_specialized_amd as rs
+        from workloads import RSVD_CONFIGS
+        c = RSVD_CONFIGS[key]
+        keep = sum(rs.lora_ranks_uniform([c["r"]] * c["n"], 1.0 / 12.0, 4))  # the spectral budget, met exactly
+        alg = rsvd_algorithmic(c["n"], c["r"], c["d_in"], c["d_out"], keep, 2)
+        kernels, sources = (("rsvd_gram", alg["gram_bytes"]), ("rsvd_write", alg["write_bytes"])), RSVD_SOURCES
+    else:
+        wl = build_workload(key)
+        m = wl.module
+        nb = algorithmic_bytes(wl.ids, m.ranks, m.n, m.d_in, m.d_out, 2 if wl.dtype == "bf16" else 4)
+        kernels = (("shrink", nb["shrink"]), ("expand", nb["expand"]), ("decode_apply", nb["total"]))
+        sources = KERNEL_SOURCES
     path = os.path.join(ROOT, "profiles", "traffic.json")
     rec = json.load(open(path)) if os.path.exists(path) else {}
     ent = {}
-    for kern, alg in (("shrink", nb["shrink"]), ("expand", nb["expand"]), ("decode_apply", nb["total"])):
+    for kern, alg in kernels:
         fk = [v for k, vs in fetch.items() if f"{kern}_kernel" in k for v in vs]
         wk = [v for k, vs in write.items() if f"{kern}_kernel" in k for v in vs]
         if not fk or not wk:
@@ -292,7 +305,7 @@ def summarize_pmc(key: str, fetch_dir: str, write_dir: str):
         wb = float(np.mean(wk)) * 1024.0 / cw
         ent[kern] = {"hbm_bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
                      "algorithmic_bytes": alg, "traffic_over_algorithmic": round((fb + wb) / alg, 3),
-                     "dispatches": len(fk), "kernel_sources_sha": kernel_source_digest()}
+                     "dispatches": len(fk), "kernel_sources_sha": kernel_source_digest(sources)}
     if not ent:
         raise SystemExit("no library kernel dispatches in the counter runs")
     ent["calibration"] = {"copy_bytes": CALIBRATE_BYTES, "fetch_factor": round(cf, 4), "write_factor": round(cw, 4)}
@@ -406,7 +419,7 @@ def run_jd(args, rs, torch, dev, key):
         "bytes_breakdown": nb, "roofline": roofline, "cpu_baseline": cpu, "launches_per_step": 3,
         "as_lora": as_lora, "eager_ms_per_step": round(eager_ms, 5),
         "timed_as": "eager launches" if args.no_graph else "one HIP-graph replay of the K captured steps",
-        "kernel_sources_sha": kernel_source_digest(),
+        "kernel_sources_sha": kernel_source_digest(JD_SOURCES),
     }
     print(json.dumps(out), flush=True)
 
@@ -486,7 +499,8 @@ def run_rsvd(args, rs, torch, dev, key):
                "sample": f"{reps} adapters in {el:.1f} s (numpy QR + SVD in float64 per adapter), BLAS pinned "
                          "to 1 thread"}
     roofline = {"bound": "alu", "achieved": round(g_tf, 2), "peak": PEAK_FP64_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(g_tf / PEAK_FP64_TFLOPS, 4), "traffic": None, "kernel": "rsvd_gram",
+                "frac": round(g_tf / PEAK_FP64_TFLOPS, 4),
+                "traffic": traffic_for(f"config{key}", "rsvd_gram", RSVD_SOURCES), "kernel": "rsvd_gram",
                 "algorithmic_flops_per_launch": alg["gram_flops"],
                 "avg_launch_us": round(kern["rsvd_gram"] * 1e3, 2)}
     out = {
@@ -503,7 +517,7 @@ def run_rsvd(args, rs, torch, dev, key):
         "host_policy_ms": round(policy_ms, 3),
         "write_gbps": round(alg["write_bytes"] / (kern["rsvd_write"] * 1e-3) / 1e9, 1),
         "timed_as": "eager launches (a step: factor, i.e. Gram + core, then write), HIP events on the stream",
-        "kernel_sources_sha": kernel_source_digest(),
+        "kernel_sources_sha": kernel_source_digest(RSVD_SOURCES),
     }
     print(json.dumps(out), flush=True)
 
