@@ -66,6 +66,7 @@ enum lora_dtype { LORA_DTYPE_F32 = 0, LORA_DTYPE_BF16 = 1 };
 
 /* Largest retained (or padded) rank the kernels accept. */
 #define LORA_MAX_RANK 64
+#define LORA_MAX_SLICES 4
 /* Largest T and n that lora_segment accepts (single-workgroup sort); the
  * batched apply with ids accepts the same T. */
 #define LORA_SEGMENT_MAX_T 16384
@@ -317,6 +318,75 @@ size_t lora_jd_workspace_bytes(const lora_jd_store* store_host, int T);
  */
 int lora_jd_apply(const lora_jd_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy, int T,
                   const int32_t* ids, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Multi-slice apply: several projections that read the same input (q, k and
+ * v; gate and up) applied with one read of x.  "Compress then Serve"
+ * section 13.4 adds the B step into a slice of y given by an offset and a
+ * width; here each slice is an ordinary store of the same adapters (same n,
+ * d_in and dtype; each slice with its own d_out, ranks, row offsets and
+ * scales), and its y may be a column slice of one fused output (a pointer
+ * into the row plus the fused row stride).
+ *
+ *     y_s[t] += s_{s,a} * B_{s,a} (A_{s,a} x[t])     for every slice s,  a = ids[t]
+ *
+ * The multi store:
+ *   slice[s]  : the slices' stores (their B, ranks, row offsets and scales are
+ *               used; their A rows are copied into `stacked`).
+ *   stacked   : per adapter, the A rows of slice 0, then slice 1, ... (stored
+ *               ranks); rank = the sum of the slices' stored ranks, at most
+ *               LORA_MAX_RANK.  Not an ordinary store: its B_pack aliases its
+ *               A_pack and its d_out is d_in, so that no call reads outside
+ *               its buffers, but only lora_apply_multi gives it a meaning.
+ *   hoff      : device int32 [n_slices][n]: the first stacked row (and h
+ *               column) of slice s of adapter a.
+ * The caller owns every buffer; the struct only points at them.
+ */
+typedef struct lora_multi_store {
+  int32_t n_slices;
+  int32_t reserved;
+  lora_store stacked;
+  lora_store slice[LORA_MAX_SLICES];
+  const int32_t* hoff;
+} lora_multi_store;
+
+/*
+ * Size query (host only): bytes of the stacked A buffer, of its metadata and
+ * of hoff for these slices.  Errors: INVALID_ARG (null pointers, n_slices
+ * outside 1..LORA_MAX_SLICES, an invalid slice store, slices whose n, d_in or
+ * dtype differ).
+ */
+int lora_multi_bytes(int n_slices, const lora_store* slices_host, size_t* a_bytes_host, size_t* meta_bytes_host,
+                     size_t* hoff_bytes_host);
+
+/*
+ * Build a multi store from the slices' stores: reads their ranks back (the
+ * stream is synchronized), writes the stacked metadata and hoff, and copies
+ * every slice's A rows into A_stacked (bit-exact).  A_stacked, meta and hoff:
+ * caller buffers of lora_multi_bytes' sizes, 16-byte aligned.  The slices'
+ * stores must stay alive (their B and metadata are used by the apply).
+ * Errors: as lora_multi_bytes; INVALID_ARG for null buffers; UNSUPPORTED
+ * when an adapter's stacked rank exceeds LORA_MAX_RANK.
+ */
+int lora_pack_multi(lora_multi_store* out_host, int n_slices, const lora_store* slices_host, void* A_stacked,
+                    void* meta, int32_t* hoff, void* stream);
+
+/* Workspace of lora_apply_multi for T tokens (host only; 0 on invalid
+ * arguments): that of the stacked store. */
+size_t lora_multi_workspace_bytes(const lora_multi_store* store_host, int T);
+
+/*
+ * The multi-slice apply: one shrink of the stacked store (x read once for
+ * every slice; tokens grouped from ids, or from a grouping as for
+ * lora_apply_batched), then one expand per slice into y_host[s] (device
+ * pointers, row stride ldy_host[s] elements, [T, d_out of slice s]).  Each
+ * y_s is updated once, rounded once.  Errors: those of lora_apply_batched
+ * for the stacked store and each slice's y; INVALID_ARG for an inconsistent
+ * multi store.
+ */
+int lora_apply_multi(const lora_multi_store* store_host, const void* x, int64_t ldx, void* const* y_host,
+                     const int64_t* ldy_host, int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm,
+                     void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Retained-rank allocation (host only, nothing enqueued): how many ranks each

@@ -29,7 +29,8 @@ __all__ = [
     "lora_segment", "lora_workspace_bytes", "lora_shrink", "lora_expand", "lora_apply_batched",
     "lora_apply_batched_phases", "lora_apply_launches", "JDStore", "lora_jd_pack", "lora_jd_workspace_bytes",
     "lora_jd_apply", "lora_ranks_uniform", "lora_ranks_spectral", "RsvdFactors", "lora_rsvd_workspace_bytes",
-    "lora_rsvd_factor", "lora_rsvd_write", "load_library",
+    "lora_rsvd_factor", "lora_rsvd_write", "MultiStore", "lora_pack_multi", "lora_multi_workspace_bytes",
+    "lora_apply_multi", "load_library",
 ]
 
 _DTYPES = {torch.bfloat16: L.LORA_DTYPE_BF16, torch.float32: L.LORA_DTYPE_F32}
@@ -435,3 +436,71 @@ def lora_rsvd_write(f: RsvdFactors, ranks: Sequence[int], scales, pad_to: int = 
     L.check("lora_rsvd_write", L.lib().lora_rsvd_write(store.ref(), r, _p(f.A_all), _p(f.B_all), f.ws.data_ptr(),
                                                        f.ws.numel(), _stream(f.A_all)))
     return store
+
+
+@dataclass
+class MultiStore:
+    """Slices of one input (q/k/v, gate/up) for the multi-slice apply: the
+    slices' stores (kept referenced), the stacked A buffer, its metadata and
+    hoff."""
+
+    c: L.lora_multi_store
+    slices: List[Store]
+    A: torch.Tensor
+    meta: torch.Tensor
+    hoff: torch.Tensor
+
+    @property
+    def n(self) -> int:
+        return self.c.stacked.n
+
+    @property
+    def n_slices(self) -> int:
+        return self.c.n_slices
+
+    def ref(self):
+        return C.byref(self.c)
+
+
+def lora_pack_multi(slices: Sequence[Store]) -> MultiStore:
+    """Stack the A rows of stores of the same adapters (same n, d_in, dtype)."""
+    k = len(slices)
+    arr = (L.lora_store * max(k, 1))(*[st.c for st in slices])
+    a, m, h = C.c_size_t(), C.c_size_t(), C.c_size_t()
+    L.check("lora_multi_bytes", L.lib().lora_multi_bytes(k, arr, C.byref(a), C.byref(m), C.byref(h)))
+    dev = slices[0].meta.device
+    A = torch.empty(max(a.value, 16), dtype=torch.uint8, device=dev)
+    meta = torch.empty(m.value, dtype=torch.uint8, device=dev)
+    hoff = torch.empty(max(h.value // 4, 4), dtype=torch.int32, device=dev)
+    c = L.lora_multi_store()
+    L.check("lora_pack_multi", L.lib().lora_pack_multi(C.byref(c), k, arr, A.data_ptr(), meta.data_ptr(),
+                                                       hoff.data_ptr(), _stream(meta)))
+    return MultiStore(c, list(slices), A, meta, hoff)
+
+
+def lora_multi_workspace_bytes(store: MultiStore, T: int) -> int:
+    return int(L.lib().lora_multi_workspace_bytes(store.ref(), T))
+
+
+def lora_apply_multi(store: MultiStore, x: torch.Tensor, ys: Sequence[torch.Tensor], ids=None,
+                     seg: Optional[Segmentation] = None, ws: Optional[torch.Tensor] = None):
+    """y_s += s B_s A_s x for every slice, x read once; ys may be column
+    slices of one fused buffer (row stride taken from each view)."""
+    T = x.shape[0]
+    k = store.n_slices
+    if len(ys) != k:
+        raise ValueError("one y per slice")
+    if (ids is None) == (seg is None):
+        raise ValueError("pass exactly one of ids or seg")
+    yp = (C.c_void_p * k)(*[_p(y) for y in ys])
+    ld = (C.c_int64 * k)(*[_rows(y, "y") for y in ys])
+    if ids is not None and (ids.dtype != torch.int32 or not ids.is_contiguous()):
+        raise ValueError("ids must be a contiguous int32 vector")
+    if ws is None:
+        ws = torch.empty(max(lora_multi_workspace_bytes(store, T), 16), dtype=torch.uint8, device=x.device)
+    so = seg.seg_off if seg is not None else None
+    pm = seg.perm if seg is not None else None
+    L.check("lora_apply_multi", L.lib().lora_apply_multi(
+        store.ref(), _p(x), _rows(x, "x"), yp, ld, T, _p(ids), _p(so), _p(pm), ws.data_ptr(), ws.numel(),
+        _stream(x)))
+    return ys

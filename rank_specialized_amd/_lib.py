@@ -38,6 +38,16 @@ class lora_jd_store(C.Structure):
     ]
 
 
+LORA_MAX_SLICES = 4
+
+
+class lora_multi_store(C.Structure):
+    _fields_ = [
+        ("n_slices", C.c_int32), ("reserved", C.c_int32), ("stacked", lora_store),
+        ("slice", lora_store * LORA_MAX_SLICES), ("hoff", C.c_void_p),
+    ]
+
+
 # name -> (restype, argtypes); mirrors include/lora.h
 P = C.c_void_p
 I = C.c_int
@@ -64,6 +74,10 @@ SIGNATURES = {
     "lora_rsvd_factor": (I, [I, I, I, I, I, P, P, P, P, P, SZ, P]),
     "lora_rsvd_write": (I, [C.POINTER(lora_store), I, P, P, P, SZ, P]),
     "lora_rsvd_factor_phases": (I, [I, I, I, I, I, P, P, P, P, P, SZ, P, I]),
+    "lora_multi_bytes": (I, [I, P, C.POINTER(SZ), C.POINTER(SZ), C.POINTER(SZ)]),
+    "lora_pack_multi": (I, [C.POINTER(lora_multi_store), I, P, P, P, P, P]),
+    "lora_multi_workspace_bytes": (SZ, [C.POINTER(lora_multi_store), I]),
+    "lora_apply_multi": (I, [C.POINTER(lora_multi_store), P, I64, P, P, I, P, P, P, P, SZ, P]),
 }
 
 _lib = None

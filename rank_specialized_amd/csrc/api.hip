@@ -322,4 +322,150 @@ int lora_rsvd_write(const lora_store* store_host, int r, const void* A_all, cons
   return e == hipSuccess ? LORA_OK : hip_fail(e);
 }
 
+static int check_slices(int n_slices, const lora_store* sl) {
+  if (!sl || n_slices < 1 || n_slices > LORA_MAX_SLICES) return LORA_ERR_INVALID_ARG;
+  for (int k = 0; k < n_slices; ++k) {
+    const int st = check_store(&sl[k]);
+    if (st != LORA_OK) return st;
+    if (sl[k].n != sl[0].n || sl[k].d_in != sl[0].d_in || sl[k].dtype != sl[0].dtype) return LORA_ERR_INVALID_ARG;
+  }
+  return LORA_OK;
+}
+
+int lora_multi_bytes(int n_slices, const lora_store* slices_host, size_t* a_bytes_host, size_t* meta_bytes_host,
+                     size_t* hoff_bytes_host) {
+  if (!a_bytes_host || !meta_bytes_host || !hoff_bytes_host) return LORA_ERR_INVALID_ARG;
+  const int st = check_slices(n_slices, slices_host);
+  if (st != LORA_OK) return st;
+  int64_t R = 0;  // the stacked total rank is the sum of the slices' totals
+  for (int k = 0; k < n_slices; ++k) R += slices_host[k].R;
+  if (R > INT32_MAX) return LORA_ERR_INVALID_ARG;
+  const lora_store& s0 = slices_host[0];
+  *a_bytes_host = (size_t)R * s0.d_in * elem_bytes(s0.dtype);
+  *meta_bytes_host = meta_bytes(s0.n);
+  *hoff_bytes_host = (size_t)n_slices * s0.n * sizeof(int32_t);
+  return LORA_OK;
+}
+
+int lora_pack_multi(lora_multi_store* out_host, int n_slices, const lora_store* slices_host, void* A_stacked,
+                    void* meta, int32_t* hoff, void* stream) {
+  size_t ab = 0, mb = 0, hb = 0;
+  int st = lora_multi_bytes(n_slices, slices_host, &ab, &mb, &hb);
+  if (st != LORA_OK) return st;
+  if (!out_host || !meta || !hoff || (ab > 0 && !A_stacked)) return LORA_ERR_INVALID_ARG;
+  if (!aligned16(meta) || !aligned16(hoff) || (A_stacked && !aligned16(A_stacked))) return LORA_ERR_UNSUPPORTED;
+  const lora_store& s0 = slices_host[0];
+  const int n = s0.n;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // The slices' stored ranks, read back.
+  std::vector<int32_t> rk((size_t)n_slices * n);
+  for (int k = 0; k < n_slices; ++k) {
+    hipError_t e = hipMemcpyAsync(rk.data() + (size_t)k * n, slices_host[k].rank, (size_t)n * sizeof(int32_t),
+                                  hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e);
+  std::vector<char> img(mb, 0);
+  int32_t* row_off = reinterpret_cast<int32_t*>(img.data());
+  int32_t* rank = row_off + (n + 1);
+  float* scale = reinterpret_cast<float*>(rank + n);
+  int32_t* true_rank = reinterpret_cast<int32_t*>(scale + n);
+  std::vector<int32_t> ho((size_t)n_slices * n);
+  int r_max = 0;
+  row_off[0] = 0;
+  for (int a = 0; a < n; ++a) {
+    int r = 0;
+    for (int k = 0; k < n_slices; ++k) {
+      const int v = rk[(size_t)k * n + a];
+      if (v < 0 || v > LORA_MAX_RANK) return LORA_ERR_INVALID_ARG;  // not a store's metadata
+      ho[(size_t)k * n + a] = r;
+      r += v;
+    }
+    if (r > LORA_MAX_RANK) return LORA_ERR_UNSUPPORTED;
+    rank[a] = true_rank[a] = r;
+    scale[a] = 1.f;
+    row_off[a + 1] = row_off[a] + r;
+    r_max = r > r_max ? r : r_max;
+  }
+  const int R = row_off[n];
+  if ((size_t)R * s0.d_in * elem_bytes(s0.dtype) != ab) return LORA_ERR_INVALID_ARG;  // ranks disagree with R
+  e = hipMemcpyAsync(meta, img.data(), img.size(), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(hoff, ho.data(), hb, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = launch_stack_rows(n, s0.d_in, s0.dtype, n_slices, R, reinterpret_cast<const int32_t*>(meta), hoff,
+                          slices_host, A_stacked, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e);
+  lora_multi_store m;
+  std::memset(&m, 0, sizeof(m));
+  m.n_slices = n_slices;
+  for (int k = 0; k < n_slices; ++k) m.slice[k] = slices_host[k];
+  lora_store& t = m.stacked;
+  t.n = n;
+  t.d_in = s0.d_in;
+  t.d_out = s0.d_in;  // B_pack aliases A_pack: bounded by A's size
+  t.dtype = s0.dtype;
+  t.r_max = r_max;
+  t.R = R;
+  t.pad_to = 0;
+  t.A_pack = A_stacked;
+  t.B_pack = A_stacked;
+  t.row_off = reinterpret_cast<const int32_t*>(meta);
+  t.rank = t.row_off + (n + 1);
+  t.scale = reinterpret_cast<const float*>(t.rank + n);
+  m.hoff = hoff;
+  *out_host = m;
+  return LORA_OK;
+}
+
+static int check_multi(const lora_multi_store* m) {
+  if (!m || !m->hoff) return LORA_ERR_INVALID_ARG;
+  int st = check_slices(m->n_slices, m->slice);
+  if (st != LORA_OK) return st;
+  if ((st = check_store(&m->stacked)) != LORA_OK) return st;
+  const lora_store& t = m->stacked;
+  if (t.n != m->slice[0].n || t.d_in != m->slice[0].d_in || t.dtype != m->slice[0].dtype) return LORA_ERR_INVALID_ARG;
+  return LORA_OK;
+}
+
+size_t lora_multi_workspace_bytes(const lora_multi_store* store_host, int T) {
+  if (check_multi(store_host) != LORA_OK) return 0;
+  return workspace_bytes(&store_host->stacked, T);
+}
+
+int lora_apply_multi(const lora_multi_store* store_host, const void* x, int64_t ldx, void* const* y_host,
+                     const int64_t* ldy_host, int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm,
+                     void* ws, size_t ws_bytes, void* stream) {
+  int st = check_multi(store_host);
+  if (st != LORA_OK) return st;
+  const lora_multi_store& m = *store_host;
+  const lora_store& s = m.stacked;
+  if (T < 0 || !y_host || !ldy_host) return LORA_ERR_INVALID_ARG;
+  if ((st = check_rows(x, ldx, s.d_in, s.dtype, T)) != LORA_OK) return st;
+  for (int k = 0; k < m.n_slices; ++k)
+    if ((st = check_rows(y_host[k], ldy_host[k], m.slice[k].d_out, s.dtype, T)) != LORA_OK) return st;
+  if ((st = check_ws(&s, T, ws, ws_bytes)) != LORA_OK) return st;
+  if (ids != nullptr && (T > LORA_SEGMENT_MAX_T || s.n > LORA_SEGMENT_MAX_N)) return LORA_ERR_UNSUPPORTED;
+  if (T == 0) return LORA_OK;
+  if (ids == nullptr && (st = check_grouping(&s, T, seg_off, perm)) != LORA_OK) return st;
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (ids != nullptr && s.n > kGroupMaxN) {
+    const WsLayout L = ws_layout(T, s.n, s.d_in, s.r_max, s.dtype);
+    int32_t* so = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + L.seg_off);
+    int32_t* pm = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + L.perm);
+    st = lora_segment(ids, T, s.n, so, pm, nullptr, stream);
+    if (st != LORA_OK) return st;
+    e = launch_shrink(s, nullptr, so, pm, T, x, ldx, ws, strm);
+  } else if (ids != nullptr) {
+    e = launch_shrink(s, ids, nullptr, nullptr, T, x, ldx, ws, strm);
+  } else {
+    e = launch_shrink(s, nullptr, seg_off, perm, T, x, ldx, ws, strm);
+  }
+  for (int k = 0; e == hipSuccess && k < m.n_slices; ++k)
+    e = launch_expand_slice(s, m.slice[k], m.hoff + (size_t)k * s.n, T, ws, y_host[k], ldy_host[k], strm);
+  return e == hipSuccess ? LORA_OK : hip_fail(e);
+}
+
 }  // extern "C"

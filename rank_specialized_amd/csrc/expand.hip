@@ -56,11 +56,20 @@ struct ExpandArgs {
   const char* plan;
   char* y;
   int64_t ldy_bytes;
+  // Slice mode (multi-slice apply): the plan and partial sums come from the
+  // shrink of a stacked store (the bounds above are that store's); B, rank,
+  // row offset and scale come from the slice's store, and h from column
+  // sl_hoff[a] of the stacked h.  sl_rank == nullptr: ordinary mode.
+  const int32_t* sl_rank;
+  const int32_t* sl_row_off;
+  const float* sl_scale;
+  const int32_t* sl_hoff;
+  int sl_r_max, sl_R;
 };
 
 template <typename E, bool kPart, int NQ>
 __device__ __forceinline__ void expand_item(const ExpandArgs& p, const TileEntry* ent, int m, int r, int pos0,
-                                            int ro, float sc, int S, int o) {
+                                            int ro, float sc, int S, int o, int hoff) {
   constexpr int V = E::kVec;
   constexpr int KSTEP = 4 * V;  // ranks per K chunk
   constexpr int YV = 8 / V;     // 16-byte vectors per 8 features: bf16 1, f32 2
@@ -124,8 +133,18 @@ __device__ __forceinline__ void expand_item(const ExpandArgs& p, const TileEntry
 #pragma unroll
     for (int e = 0; e < V; ++e) f[e] = 0.f;
     if (hv && j0 < r) {
-      const float* src = p.hsrc + (int64_t)hrow * p.ldh + j0;
-      if (kPart) {
+      const float* src = p.hsrc + (int64_t)hrow * p.ldh + hoff + j0;
+      if (kPart && (hoff & 3)) {  // a slice's columns off 16-byte boundaries (multi-slice apply)
+#pragma unroll
+        for (int e = 0; e < V; ++e) f[e] = src[e];
+#pragma unroll 4
+        for (int k = 1; k < S; ++k)
+#pragma unroll
+          for (int e = 0; e < V; ++e) f[e] += src[(int64_t)k * p.hstride + e];
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+          if (j0 + e >= r) f[e] = 0.f;
+      } else if (kPart) {
 #pragma unroll
         for (int v = 0; v < V / 4; ++v) {
           const f32x4_t x = *reinterpret_cast<const f32x4_t*>(src + 4 * v);
@@ -196,7 +215,7 @@ __device__ __forceinline__ bool vector_expand(int r, int m) {
 
 template <typename E, bool kPart, int R>
 __device__ __forceinline__ void expand_vec_item(const ExpandArgs& p, const TileEntry* ent, int m, int t0,
-                                                int pos0, int ro, float sc, int S, int o) {
+                                                int pos0, int ro, float sc, int S, int o, int hoff) {
   constexpr int V = E::kVec;
   constexpr int YV = 8 / V;                   // 16-byte vectors per 8 features
   constexpr int BV = 8 * R * E::kBytes / 16;  // 16-byte vectors of the lane's 8 x R block of B
@@ -226,7 +245,7 @@ __device__ __forceinline__ void expand_vec_item(const ExpandArgs& p, const TileE
     if (t < mt) {
       const int row = pos0 + t0 + t;
       if (row >= 0 && row < p.T) {
-        const float* src = p.hsrc + (int64_t)row * p.ldh + j;
+        const float* src = p.hsrc + (int64_t)row * p.ldh + hoff + j;
         hv = src[0];
         if (kPart) {
           // All S loads issued together (S <= kMaxChunks), summed in chunk order.
@@ -280,7 +299,7 @@ __device__ __forceinline__ void expand_vec_item(const ExpandArgs& p, const TileE
 }
 
 // ------------------------------------------------------------ the kernel
-template <typename E, bool kPart>
+template <typename E, bool kPart, bool kSlice>
 __device__ __forceinline__ void expand_wave(const ExpandArgs& p) {
   constexpr int KSTEP = 4 * E::kVec;
   constexpr int kGroups = kVecMaxTokens / kVecTokens;
@@ -292,8 +311,18 @@ __device__ __forceinline__ void expand_wave(const ExpandArgs& p) {
   const TileEntry* ent = reinterpret_cast<const TileEntry*>(p.plan + kPlanHeaderBytes) + st;
   const int S = kPart ? ent->S : 1;
   if (!entry_fits(p, ent, S)) return;
-  const int m = ent->m, r = ent->r, pos0 = ent->pos0, ro = ent->row_off;
-  const float sc = ent->scale;
+  const int m = ent->m, pos0 = ent->pos0;
+  int r = ent->r, ro = ent->row_off, hoff = 0;
+  float sc = ent->scale;
+  if constexpr (kSlice) {  // slice mode: this slice's rank, B rows, scale and h columns
+    const int a = ent->a;
+    const int r2 = p.sl_rank[a], ro2 = p.sl_row_off[a], h2 = p.sl_hoff[a];
+    if (r2 <= 0 || r2 > p.sl_r_max || ro2 < 0 || ro2 > p.sl_R - r2 || h2 < 0 || h2 > r - r2) return;
+    r = r2;
+    ro = ro2;
+    hoff = h2;
+    sc = p.sl_scale[a];
+  }
   if (vector_expand<E>(r, m)) {
     const int fb = slot / kGroups, tg = slot - fb * kGroups;
     if (fb >= p.fbv || tg * kVecTokens >= m) return;
@@ -302,7 +331,7 @@ __device__ __forceinline__ void expand_wave(const ExpandArgs& p) {
     const int t0 = tg * kVecTokens;
     switch (r) {
 #define LORA_VEC_CASE(RR) \
-  case RR: expand_vec_item<E, kPart, RR>(p, ent, m, t0, pos0, ro, sc, S, o); break;
+  case RR: expand_vec_item<E, kPart, RR>(p, ent, m, t0, pos0, ro, sc, S, o, hoff); break;
       LORA_VEC_CASE(1) LORA_VEC_CASE(2) LORA_VEC_CASE(3) LORA_VEC_CASE(4)
       LORA_VEC_CASE(5) LORA_VEC_CASE(6) LORA_VEC_CASE(7) LORA_VEC_CASE(8)
       default:
@@ -322,36 +351,38 @@ __device__ __forceinline__ void expand_wave(const ExpandArgs& p) {
   const int o = slot * kExpandCols + 8 * (threadIdx.x & 15);
   const int nq = (r + KSTEP - 1) / KSTEP;
   if (nq <= 1) {
-    expand_item<E, kPart, 1>(p, ent, m, r, pos0, ro, sc, S, o);
+    expand_item<E, kPart, 1>(p, ent, m, r, pos0, ro, sc, S, o, hoff);
   } else if constexpr (KSTEP == 32) {  // bf16: ranks <= 64 take at most 2 chunks
-    expand_item<E, kPart, 2>(p, ent, m, r, pos0, ro, sc, S, o);
+    expand_item<E, kPart, 2>(p, ent, m, r, pos0, ro, sc, S, o, hoff);
   } else {
-    if (nq == 2) expand_item<E, kPart, 2>(p, ent, m, r, pos0, ro, sc, S, o);
-    else if (nq == 3) expand_item<E, kPart, 3>(p, ent, m, r, pos0, ro, sc, S, o);
-    else expand_item<E, kPart, 4>(p, ent, m, r, pos0, ro, sc, S, o);
+    if (nq == 2) expand_item<E, kPart, 2>(p, ent, m, r, pos0, ro, sc, S, o, hoff);
+    else if (nq == 3) expand_item<E, kPart, 3>(p, ent, m, r, pos0, ro, sc, S, o, hoff);
+    else expand_item<E, kPart, 4>(p, ent, m, r, pos0, ro, sc, S, o, hoff);
   }
 }
 
 // bf16 runs 4 waves per SIMD (more y rows in flight); float32, a
 // small-shape type here, is left to the compiler.
-template <typename E, bool kPart>
-__global__ void __launch_bounds__(kExpandWaves * 64) __attribute__((amdgpu_waves_per_eu(E::kBytes == 2 ? 4 : 1)))
+template <typename E, bool kPart, bool kSlice = false>
+__global__ void __launch_bounds__(kExpandWaves * 64) __attribute__((amdgpu_waves_per_eu(E::kBytes == 2 ? (kSlice ? 3 : 4) : 1)))
 expand_kernel(ExpandArgs p) {
-  expand_wave<E, kPart>(p);
+  expand_wave<E, kPart, kSlice>(p);
 }
 
-hipError_t launch_expand(const lora_store& s, int T, const void* ws, const float* h, int64_t ldh, void* y,
-                         int64_t ldy, hipStream_t stream) {
+static hipError_t launch_expand_impl(const lora_store& s, const lora_store* slice, const int32_t* hoff, int T,
+                                     const void* ws, const float* h, int64_t ldh, void* y, int64_t ldy,
+                                     hipStream_t stream) {
   const int64_t max_sub = plan_max_subtiles(T, s.n);
   if (max_sub == 0) return hipSuccess;
   const WsLayout L = ws_layout(T, s.n, s.d_in, s.r_max, s.dtype);
   const char* base = reinterpret_cast<const char*>(ws);
+  const lora_store& out = slice ? *slice : s;  // the store whose B is applied
   ExpandArgs a;
-  a.b_pack = reinterpret_cast<const char*>(s.B_pack);
-  a.d_out = s.d_out;
+  a.b_pack = reinterpret_cast<const char*>(out.B_pack);
+  a.d_out = out.d_out;
   a.T = T;
   a.max_sub = (int)max_sub;
-  a.fbn = (s.d_out + kExpandCols - 1) / kExpandCols;
+  a.fbn = (out.d_out + kExpandCols - 1) / kExpandCols;
   a.plan = base + L.plan;
   a.n = s.n;
   a.r_max = s.r_max;
@@ -359,6 +390,12 @@ hipError_t launch_expand(const lora_store& s, int T, const void* ws, const float
   a.S_max = shrink_split(s.d_in, s.r_max, s.dtype).S_max;
   a.y = reinterpret_cast<char*>(y);
   a.ldy_bytes = ldy * elem_bytes(s.dtype);
+  a.sl_rank = slice ? slice->rank : nullptr;
+  a.sl_row_off = slice ? slice->row_off : nullptr;
+  a.sl_scale = slice ? slice->scale : nullptr;
+  a.sl_hoff = hoff;
+  a.sl_r_max = slice ? slice->r_max : 0;
+  a.sl_R = slice ? slice->R : 0;
   const bool part = h == nullptr;
   if (part) {
     a.hsrc = reinterpret_cast<const float*>(base + L.part);
@@ -369,13 +406,16 @@ hipError_t launch_expand(const lora_store& s, int T, const void* ws, const float
     a.ldh = ldh;
     a.hstride = 0;
   }
-  a.fbv = (s.d_out + kVecCols - 1) / kVecCols;
+  a.fbv = (out.d_out + kVecCols - 1) / kVecCols;
   const int vec_waves = (kVecMaxTokens / kVecTokens) * a.fbv;
   a.slots = a.fbn > vec_waves ? a.fbn : vec_waves;
   const int64_t items = max_sub * a.slots;
   const dim3 block(kExpandWaves * 64);
   const dim3 grid((unsigned)((items + kExpandWaves - 1) / kExpandWaves));
-  if (s.dtype == LORA_DTYPE_BF16) {
+  if (slice) {  // slice mode reads the shrink's partial sums
+    if (s.dtype == LORA_DTYPE_BF16) hipLaunchKernelGGL((expand_kernel<BF16, true, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((expand_kernel<F32, true, true>), grid, block, 0, stream, a);
+  } else if (s.dtype == LORA_DTYPE_BF16) {
     if (part) hipLaunchKernelGGL((expand_kernel<BF16, true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((expand_kernel<BF16, false>), grid, block, 0, stream, a);
   } else {
@@ -383,6 +423,16 @@ hipError_t launch_expand(const lora_store& s, int T, const void* ws, const float
     else hipLaunchKernelGGL((expand_kernel<F32, false>), grid, block, 0, stream, a);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_expand(const lora_store& s, int T, const void* ws, const float* h, int64_t ldh, void* y,
+                         int64_t ldy, hipStream_t stream) {
+  return launch_expand_impl(s, nullptr, nullptr, T, ws, h, ldh, y, ldy, stream);
+}
+
+hipError_t launch_expand_slice(const lora_store& stacked, const lora_store& slice, const int32_t* hoff, int T,
+                               const void* ws, void* y, int64_t ldy, hipStream_t stream) {
+  return launch_expand_impl(stacked, &slice, hoff, T, ws, nullptr, 0, y, ldy, stream);
 }
 
 }  // namespace lora

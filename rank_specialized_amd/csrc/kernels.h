@@ -55,4 +55,12 @@ hipError_t launch_rsvd_factor(int n, int d_in, int d_out, int dtype, int r, cons
 hipError_t launch_rsvd_write(const lora_store& s, int r, const void* A, const void* B, const void* ws,
                              hipStream_t stream);
 
+// Multi-slice apply: the stacked A rows (one workgroup per stacked row),
+// and the expand of one slice over the stacked shrink's plan and partials.
+constexpr int kMaxSlices = LORA_MAX_SLICES;
+hipError_t launch_stack_rows(int n, int d_in, int dtype, int n_slices, int R, const int32_t* stk_row_off,
+                             const int32_t* hoff, const lora_store* slices, void* dst, hipStream_t stream);
+hipError_t launch_expand_slice(const lora_store& stacked, const lora_store& slice, const int32_t* hoff, int T,
+                               const void* ws, void* y, int64_t ldy, hipStream_t stream);
+
 }  // namespace lora

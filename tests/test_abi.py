@@ -373,3 +373,69 @@ def test_rsvd_write_rejects_before_launch(lib):
     assert f(C.byref(st), 8, FAKE + 2, FAKE, FAKE, big, None) == 2
     empty = _store(n=4, d_in=64, d_out=32, r_max=0, R=0)
     assert f(C.byref(empty), 8, None, None, None, 0, None) == 0
+
+
+def _multi(k=2, n=4, d_in=64, d_outs=(32, 16), r_max=8):
+    m = L.lora_multi_store()
+    m.n_slices = k
+    m.stacked = _store(n=n, d_in=d_in, d_out=d_in, r_max=2 * r_max, R=40)
+    for s in range(k):
+        m.slice[s] = _store(n=n, d_in=d_in, d_out=d_outs[s % len(d_outs)], r_max=r_max, R=20)
+    m.hoff = FAKE
+    return m
+
+
+def test_multi_bytes_and_rejects(lib):
+    arr = (L.lora_store * 2)(_store(n=4, d_in=64, d_out=32, R=20), _store(n=4, d_in=64, d_out=16, R=12))
+    a, mb, hb = C.c_size_t(), C.c_size_t(), C.c_size_t()
+    assert lib.lora_multi_bytes(2, arr, C.byref(a), C.byref(mb), C.byref(hb)) == 0
+    assert a.value == (20 + 12) * 64 * 2 and hb.value == 2 * 4 * 4
+    assert lib.lora_multi_bytes(0, arr, C.byref(a), C.byref(mb), C.byref(hb)) == 1
+    assert lib.lora_multi_bytes(5, arr, C.byref(a), C.byref(mb), C.byref(hb)) == 1
+    assert lib.lora_multi_bytes(2, None, C.byref(a), C.byref(mb), C.byref(hb)) == 1
+    bad = (L.lora_store * 2)(_store(n=4, d_in=64), _store(n=5, d_in=64))  # different adapters
+    assert lib.lora_multi_bytes(2, bad, C.byref(a), C.byref(mb), C.byref(hb)) == 1
+    bad = (L.lora_store * 2)(_store(n=4, d_in=64), _store(n=4, d_in=128))
+    assert lib.lora_multi_bytes(2, bad, C.byref(a), C.byref(mb), C.byref(hb)) == 1
+    bad = (L.lora_store * 2)(_store(n=4, d_in=64, dtype=1), _store(n=4, d_in=64, dtype=0))
+    assert lib.lora_multi_bytes(2, bad, C.byref(a), C.byref(mb), C.byref(hb)) == 1
+    st = L.lora_multi_store()
+    assert lib.lora_pack_multi(C.byref(st), 2, arr, FAKE, None, FAKE, None) == 1
+    assert lib.lora_pack_multi(C.byref(st), 2, arr, FAKE, FAKE, None, None) == 1
+    assert lib.lora_pack_multi(C.byref(st), 2, arr, FAKE, FAKE + 4, FAKE, None) == 2
+    assert lib.lora_pack_multi(None, 2, arr, FAKE, FAKE, FAKE, None) == 1
+
+
+def test_multi_workspace_and_apply_rejects(lib):
+    m = _multi()
+    assert lib.lora_multi_workspace_bytes(C.byref(m), 16) == lib.lora_workspace_bytes(C.byref(m.stacked), 16)
+    assert lib.lora_multi_workspace_bytes(None, 16) == 0
+    big = 1 << 30
+    ys = (C.c_void_p * 2)(FAKE, FAKE)
+    lds = (C.c_int64 * 2)(32, 16)
+    f = lib.lora_apply_multi
+
+    def call(mm=None, T=16, ids=FAKE, x=FAKE, ldx=64, y=ys, ld=lds, ws=FAKE, wsb=big):
+        mm = mm if mm is not None else _multi()
+        return f(C.byref(mm), x, ldx, y, ld, T, ids, None, None, ws, wsb, None)
+
+    assert call(T=0) == 0
+    assert call(T=-1) == 1
+    assert call(x=None) == 1
+    assert call(ldx=32) == 1
+    assert call(y=None) == 1
+    assert call(ld=(C.c_int64 * 2)(32, 8)) == 1  # slice 1's row shorter than its d_out
+    assert call(y=(C.c_void_p * 2)(FAKE, FAKE + 2)) == 2
+    assert call(ws=None) == 1
+    assert call(wsb=64) == 1
+    assert call(T=L.LORA_SEGMENT_MAX_T + 1) == 2
+    mm = _multi()
+    mm.hoff = None
+    assert call(mm=mm) == 1
+    mm = _multi()
+    mm.n_slices = 0
+    assert call(mm=mm) == 1
+    mm = _multi()
+    mm.slice[1].d_in = 128  # slices disagree
+    assert call(mm=mm) == 1
+    assert f(None, FAKE, 64, ys, lds, 16, FAKE, None, None, FAKE, big, None) == 1
