@@ -70,6 +70,7 @@ def parse_args():
     p.add_argument("--config", default="2", choices=sorted(WORKLOAD_NAMES))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-padded", action="store_true")
+    p.add_argument("--no-multi", action="store_true", help="fleet: skip the multi-slice (q/k/v, gate/up) step")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--warm", action="store_true", help="no rotation (cache-resident timing)")
     p.add_argument("--no-graph", action="store_true", help="time eager launches only (counter runs)")
@@ -708,6 +709,37 @@ def run_fleet(args, rs, torch, dev):
                 "kernel": f"{dom}_kernel<BF16> over the 196 modules of a step",
                 "algorithmic_bytes_per_launch": round(kern[dom]["algorithmic_bytes_per_step"] / len(stores)),
                 "avg_launch_us": kern[dom]["avg_us"]}
+    multi = {}
+    if not args.no_multi:
+        # The same step with the projections that share an input applied
+        # together (q/k/v, gate/up): one x read per group.
+        groups = {}
+        for i, m in enumerate(meta):
+            groups.setdefault((m[0], m[5]), []).append(i)
+        mstores = {g: rs.lora_pack_multi([stores[i] for i in idx]) for g, idx in groups.items() if len(idx) > 1}
+        mws = torch.empty(max([rs.lora_multi_workspace_bytes(mst, T) for mst in mstores.values()] +
+                              [ws.numel()]), dtype=torch.uint8, device=dev)
+
+        def step_multi(phases=3):
+            rs.lora_segment(ids, n, seg=seg)
+            for g, idx in groups.items():
+                x = xs[g]
+                if len(idx) > 1:
+                    rs.lora_apply_multi(mstores[g], x, [ys[i] for i in idx], seg=seg, ws=mws)
+                else:
+                    rs.lora_apply_batched(stores[idx[0]], x, ys[idx[0]], seg=seg, ws=mws)
+
+        saved = sum(T * meta[idx[0]][3] * 2 * (len(idx) - 1) for idx in groups.values())
+        step_fn = step
+        step = step_multi
+        mms = timed(3, steps)
+        step = step_fn
+        multi = {"groups": "per layer: q+k+v, o, gate+up, down", "calls_per_step": len(groups),
+                 "ms_per_step": round(mms, 4), "tokens_per_s": round(T / (mms * 1e-3), 1),
+                 "x_bytes_saved_per_step": saved, "algorithmic_bytes_per_step": step_bytes - saved,
+                 "gbps": round((step_bytes - saved) / (mms * 1e-3) / 1e9, 1), "speedup": round(ms / mms, 3)}
+        del mstores, mws
+        torch.cuda.empty_cache()
     padded = {}
     if not args.no_padded and key == "5S":
         del stores
@@ -754,7 +786,7 @@ def run_fleet(args, rs, torch, dev):
         "gbps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / PEAK_GBPS, 4),
         "bytes_per_step": step_bytes, "roofline": roofline, "cpu_baseline": cpu, "kernels": kern,
-        "padded": padded, "wall_s_timed": round(wall, 6),
+        "padded": padded, "multi_slice": multi, "wall_s_timed": round(wall, 6),
         "timed_as": "eager launches" if args.no_graph else "HIP-graph replays of one captured step",
         "kernel_sources_sha": kernel_source_digest(),
     }
