@@ -33,7 +33,7 @@
 //                       every pair is orthogonal to 1e-15 or a sweep's
 //                       rotations all had |tan| < 1e-8; then sigma_j = |C_j|,
 //                       their descending order, U.
-//   rsvd_post_kernel    per adapter, one wave: W_A = R_B^T U and
+//   rsvd_post_kernel    per adapter, two waves: W_A = R_B^T U and
 //                       W_B = R_B^-1 U (back substitution), columns in sigma
 //                       order.
 //   rsvd_write_kernel   B'[o, c] = sum_i B[o, i] W_B[i, c] and
@@ -212,28 +212,42 @@ __global__ void __launch_bounds__(kGramWaves * 64) rsvd_gram_kernel(RsvdArgs p) 
 
 // ------------------------------------------------------------------ prep
 // Upper Cholesky factor of m (lane c owns column c; R in the upper triangle,
-// the lower triangle zeroed).  Pivot rules as in the file comment; a pivot at
-// or below 1e-30 of the largest diagonal entry, or not positive, is raised to
-// that floor so the factorization finishes (a zero column gives a zero row of
-// R but for a tiny diagonal).
+// the lower triangle zeroed), left-looking: step j forms row j of R from the
+// rows above it, R[j][c] = (G[j][c] - sum_{k<j} R[k][j] R[k][c]) / R[j][j],
+// with only reads in its sums (every lane also forms the pivot, in the same
+// order, so all agree on it), then one write per lane and one barrier.
+// Pivot rules as in the file comment; a pivot at or below 1e-30 of the
+// largest diagonal entry, or not positive, is raised to that floor so the
+// factorization finishes (a zero column gives a zero row of R but for a tiny
+// diagonal).
 __device__ void cholesky_lanes(double (*m)[kRsvdR + 1], int r, int c, int* bad) {
   double dmax = 0.0;
   for (int j = 0; j < r; ++j) dmax = fmax(dmax, m[j][j]);
   const double warn = 1e-14 * dmax, floor_v = fmax(1e-30 * dmax, 1e-300);
-  __syncthreads();
+  __syncthreads();  // every lane has read the diagonal before it changes
   for (int j = 0; j < r; ++j) {
-    double d2 = m[j][j];
+    double dg[4] = {0.0, 0.0, 0.0, 0.0}, ac[4] = {0.0, 0.0, 0.0, 0.0};
+    int k = 0;
+    for (; k + 3 < j; k += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const double rkj = m[k + u][j];
+        dg[u] = fma(rkj, rkj, dg[u]);
+        ac[u] = fma(rkj, m[k + u][c], ac[u]);
+      }
+    }
+    for (; k < j; ++k) {
+      const double rkj = m[k][j];
+      dg[0] = fma(rkj, rkj, dg[0]);
+      ac[0] = fma(rkj, m[k][c], ac[0]);
+    }
+    double d2 = m[j][j] - ((dg[0] + dg[1]) + (dg[2] + dg[3]));
+    const double g = m[j][c] - ((ac[0] + ac[1]) + (ac[2] + ac[3]));
     if (!(d2 > warn) && c == 0) *bad = 1;
     if (!(d2 > floor_v)) d2 = floor_v;
     const double d = sqrt(d2);
-    __syncthreads();  // every lane has read the pivot
     if (c == j) m[j][j] = d;
-    if (c > j && c < r) m[j][c] /= d;
-    __syncthreads();
-    if (c > j && c < r) {
-      const double rc = m[j][c];
-      for (int i = j + 1; i <= c; ++i) m[i][c] -= m[j][i] * rc;
-    }
+    else if (c > j && c < r) m[j][c] = g / d;
     __syncthreads();
   }
   for (int i = c + 1; i < kRsvdR; ++i) m[i][c] = 0.0;
@@ -381,39 +395,45 @@ __global__ void __launch_bounds__(kJacobiWaves * 64) rsvd_jacobi_kernel(RsvdArgs
 }
 
 // ------------------------------------------------------------------ post
-// One wave per adapter, lane c: column c of W_A = R_B^T U and of
-// W_B = R_B^-1 U (row-oriented back substitution in LDS), each written as
-// row c of the transposed matrix.
-__global__ void __launch_bounds__(64) rsvd_post_kernel(RsvdArgs p) {
+// Two waves per adapter, lane c of each holding column c of U: wave 0 forms
+// column c of W_A = R_B^T U, wave 1 column c of W_B = R_B^-1 U (row-oriented
+// back substitution in LDS); each is written as row c of the transposed
+// matrix, with rows past r zero.
+__global__ void __launch_bounds__(128) rsvd_post_kernel(RsvdArgs p) {
   __shared__ double rb[kRsvdR][kRsvdR + 1];
   __shared__ double x[kRsvdR][kRsvdR + 1];
-  const int a = blockIdx.x, c = threadIdx.x, r = p.r;
+  const int a = blockIdx.x, tid = threadIdx.x, w = tid >> 6, c = tid & 63, r = p.r;
   const double* RB = ws_mat(p, a, kWsRB);
   const double* U = ws_mat(p, a, kWsU);
-  double* WB = ws_mat(p, a, kWsWB);
-  double* WA = ws_mat(p, a, kWsWA);
-  double u[kRsvdR];
-#pragma unroll
-  for (int k = 0; k < kRsvdR; ++k) {
-    rb[k][c] = RB[k * kRsvdR + c];
-    u[k] = U[k * kRsvdR + c];
-    x[k][c] = u[k];
-  }
+  for (int k = w; k < kRsvdR; k += 2) rb[k][c] = RB[k * kRsvdR + c];
+  if (w == 1)
+    for (int k = 0; k < kRsvdR; ++k) x[k][c] = U[k * kRsvdR + c];
   __syncthreads();
-  // Stored transposed (column c of W at W[c][0 .. 64)), rows past r zero.
-  for (int i = 0; i < kRsvdR; ++i) {  // rb and u are zero past r
-    double s = 0.0;
+  if (w == 0) {
+    double* WA = ws_mat(p, a, kWsWA);
+    double u[kRsvdR];
 #pragma unroll
-    for (int k = 0; k < kRsvdR; ++k) s = fma(rb[k][i], u[k], s);  // rb is zero below the diagonal
-    WA[c * kRsvdR + i] = s;
-  }
-  for (int i = r; i < kRsvdR; ++i) WB[c * kRsvdR + i] = 0.0;
-  for (int i = r - 1; i >= 0; --i) {
-    double s = x[i][c];
-    for (int k = i + 1; k < r; ++k) s -= rb[i][k] * x[k][c];
-    s /= rb[i][i];
-    x[i][c] = s;
-    WB[c * kRsvdR + i] = s;
+    for (int k = 0; k < kRsvdR; ++k) u[k] = U[k * kRsvdR + c];
+    for (int i = 0; i < kRsvdR; ++i) {  // rb and u are zero past r
+      double s4[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int k = 0; k < kRsvdR; ++k) s4[k & 3] = fma(rb[k][i], u[k], s4[k & 3]);  // rb is zero below the diagonal
+      WA[c * kRsvdR + i] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    }
+  } else {
+    double* WB = ws_mat(p, a, kWsWB);
+    for (int i = r; i < kRsvdR; ++i) WB[c * kRsvdR + i] = 0.0;
+    for (int i = r - 1; i >= 0; --i) {
+      double s4[4] = {0.0, 0.0, 0.0, 0.0};
+      int k = i + 1;
+      for (; k + 3 < r; k += 4)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s4[q] = fma(rb[i][k + q], x[k + q][c], s4[q]);
+      for (; k < r; ++k) s4[0] = fma(rb[i][k], x[k][c], s4[0]);
+      const double s = (x[i][c] - ((s4[0] + s4[1]) + (s4[2] + s4[3]))) / rb[i][i];
+      x[i][c] = s;
+      WB[c * kRsvdR + i] = s;
+    }
   }
 }
 
@@ -579,7 +599,7 @@ hipError_t launch_rsvd_factor(int n, int d_in, int d_out, int dtype, int r, cons
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (phases & 8) {
-    hipLaunchKernelGGL(rsvd_post_kernel, dim3((unsigned)n), dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(rsvd_post_kernel, dim3((unsigned)n), dim3(128), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
