@@ -31,7 +31,7 @@
 //                       sweep), partner rows fetched across lanes, column
 //                       norms carried through each sweep's rotations, until
 //                       every pair is orthogonal to 1e-15 or a sweep's
-//                       rotations all had |tan| < 1e-8; then sigma_j = |C_j|,
+//                       rotations all had |tan| < 1e-4; then sigma_j = |C_j|,
 //                       their descending order, U.
 //   rsvd_post_kernel    per adapter, two waves: W_A = R_B^T U and
 //                       W_B = R_B^-1 U (back substitution), columns in sigma
@@ -338,7 +338,7 @@ __global__ void __launch_bounds__(kJacobiWaves * 64) rsvd_jacobi_kernel(RsvdArgs
     // column's norm to the upper's).
     double nrm;
     column_norm(&nrm);
-    bool rot = false;  // a rotation with |tan| >= 1e-8 this sweep
+    bool rot = false;  // a rotation with |tan| >= 1e-4 this sweep
     for (int mm = 1; mm < RB; ++mm, buf ^= 1) {
       const bool lower = j < (j ^ mm);
       double y[RPW];
@@ -369,12 +369,14 @@ __global__ void __launch_bounds__(kJacobiWaves * 64) rsvd_jacobi_kernel(RsvdArgs
 #pragma unroll
         for (int i = 0; i < RPW; ++i) c[i] = fma(ssn, y[i], cs * c[i]);
         nrm = fma(lower ? -t : t, g, nrm);
-        rot = rot || fabs(t) >= 1e-8;
+        rot = rot || fabs(t) >= 1e-4;
       }
     }
     // Every wave took the same decisions, so every wave leaves together.  A
-    // sweep whose rotations all had |tan| < 1e-8 leaves off-diagonal terms
-    // of that order squared (quadratic convergence): no further sweep.
+    // sweep whose rotations all had |tan| < 1e-4 leaves off-diagonal terms of
+    // about that order squared (quadratic convergence; about 1e-12 relative
+    // on rank-64 cores): no further sweep.  Large rotations (close singular
+    // values) never stop it early.
     if (!__any(rot)) break;
   }
   double s2;
