@@ -56,9 +56,9 @@ WORKLOAD_NAMES = {
     "ranks-fleet": "retained-rank allocation on the host: 1024 adapters x 196 modules (200704 units) of "
                    "original rank 64, uniform (ratio 1/12, floor 4) and spectral at the same budget",
     "5U": "fleet decode step: 28 layers x 7 projections (3584/512/18944 dims) bf16, 1024 adapters rank 6 "
-          "(orig 64), T=4096 Zipf(1.1) ids, one grouping reused by 196 applies",
+          "(orig 64), T=4096 Zipf(1.1) ids, one grouping reused by 196 applies (spread over streams)",
     "5S": "fleet decode step: 28 layers x 7 projections (3584/512/18944 dims) bf16, 1024 adapters ranks "
-          "4..16 per module, T=4096 Zipf(1.1) ids, one grouping reused by 196 applies",
+          "4..16 per module, T=4096 Zipf(1.1) ids, one grouping reused by 196 applies (spread over streams)",
 }
 
 
@@ -71,6 +71,8 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-padded", action="store_true")
     p.add_argument("--no-multi", action="store_true", help="fleet: skip the multi-slice (q/k/v, gate/up) step")
+    p.add_argument("--streams", type=int, default=3,
+                   help="fleet: spread the step's modules over this many streams (one workspace each)")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--warm", action="store_true", help="no rotation (cache-resident timing)")
     p.add_argument("--no-graph", action="store_true", help="time eager launches only (counter runs)")
@@ -649,9 +651,26 @@ def run_fleet(args, rs, torch, dev):
     # a module's expand reads the plan and partial sums of its own shrink.
     mod_ws = [torch.empty(rs.lora_workspace_bytes(st, T), dtype=torch.uint8, device=dev) for st in stores]
 
+    nstr = max(1, args.streams)
+    side_streams = [torch.cuda.Stream() for _ in range(nstr - 1)]  # default priority
+    str_ws = [ws] + [torch.empty_like(ws) for _ in range(nstr - 1)]
+
     def step(phases=3):
         if phases == 3:
             rs.lora_segment(ids, n, seg=seg)
+        if phases == 3 and nstr > 1:
+            # Module i on stream i % nstr with that stream's workspace; the
+            # streams fork after the grouping and join at the end.
+            main = torch.cuda.current_stream()
+            for sst in side_streams:
+                sst.wait_stream(main)
+            for i, (st, m, y) in enumerate(zip(stores, meta, ys)):
+                k = i % nstr
+                with torch.cuda.stream(main if k == 0 else side_streams[k - 1]):
+                    rs.lora_apply_batched(st, xs[(m[0], m[5])], y, seg=seg, ws=str_ws[k])
+            for sst in side_streams:
+                main.wait_stream(sst)
+            return
         for st, m, y, w in zip(stores, meta, ys, mod_ws):
             x = xs[(m[0], m[5])]
             if phases == 3:
@@ -717,17 +736,23 @@ def run_fleet(args, rs, torch, dev):
         for i, m in enumerate(meta):
             groups.setdefault((m[0], m[5]), []).append(i)
         mstores = {g: rs.lora_pack_multi([stores[i] for i in idx]) for g, idx in groups.items() if len(idx) > 1}
-        mws = torch.empty(max([rs.lora_multi_workspace_bytes(mst, T) for mst in mstores.values()] +
-                              [ws.numel()]), dtype=torch.uint8, device=dev)
+        mbytes = max([rs.lora_multi_workspace_bytes(mst, T) for mst in mstores.values()] + [ws.numel()])
+        mws = [torch.empty(mbytes, dtype=torch.uint8, device=dev) for _ in range(nstr)]
 
         def step_multi(phases=3):
             rs.lora_segment(ids, n, seg=seg)
-            for g, idx in groups.items():
-                x = xs[g]
-                if len(idx) > 1:
-                    rs.lora_apply_multi(mstores[g], x, [ys[i] for i in idx], seg=seg, ws=mws)
-                else:
-                    rs.lora_apply_batched(stores[idx[0]], x, ys[idx[0]], seg=seg, ws=mws)
+            main = torch.cuda.current_stream()
+            for sst in side_streams:
+                sst.wait_stream(main)
+            for i, (g, idx) in enumerate(groups.items()):
+                k = i % nstr
+                with torch.cuda.stream(main if k == 0 else side_streams[k - 1]):
+                    if len(idx) > 1:
+                        rs.lora_apply_multi(mstores[g], xs[g], [ys[j] for j in idx], seg=seg, ws=mws[k])
+                    else:
+                        rs.lora_apply_batched(stores[idx[0]], xs[g], ys[idx[0]], seg=seg, ws=mws[k])
+            for sst in side_streams:
+                main.wait_stream(sst)
 
         saved = sum(T * meta[idx[0]][3] * 2 * (len(idx) - 1) for idx in groups.values())
         step_fn = step
@@ -786,7 +811,7 @@ def run_fleet(args, rs, torch, dev):
         "gbps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
         "hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / PEAK_GBPS, 4),
         "bytes_per_step": step_bytes, "roofline": roofline, "cpu_baseline": cpu, "kernels": kern,
-        "padded": padded, "multi_slice": multi, "wall_s_timed": round(wall, 6),
+        "padded": padded, "multi_slice": multi, "streams": nstr, "wall_s_timed": round(wall, 6),
         "timed_as": "eager launches" if args.no_graph else "HIP-graph replays of one captured step",
         "kernel_sources_sha": kernel_source_digest(),
     }
