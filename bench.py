@@ -56,9 +56,9 @@ WORKLOAD_NAMES = {
     "ranks-fleet": "retained-rank allocation on the host: 1024 adapters x 196 modules (200704 units) of "
                    "original rank 64, uniform (ratio 1/12, floor 4) and spectral at the same budget",
     "5U": "fleet decode step: 28 layers x 7 projections (3584/512/18944 dims) bf16, 1024 adapters rank 6 "
-          "(orig 64), T=4096 Zipf(1.1) ids, one grouping reused by 196 applies (spread over streams)",
+          "(orig 64), T=4096 Zipf(1.1) ids, one grouping reused by 196 applies (q/k/v and gate/up concurrent)",
     "5S": "fleet decode step: 28 layers x 7 projections (3584/512/18944 dims) bf16, 1024 adapters ranks "
-          "4..16 per module, T=4096 Zipf(1.1) ids, one grouping reused by 196 applies (spread over streams)",
+          "4..16 per module, T=4096 Zipf(1.1) ids, one grouping reused by 196 applies (q/k/v and gate/up concurrent)",
 }
 
 
@@ -72,7 +72,7 @@ def parse_args():
     p.add_argument("--no-padded", action="store_true")
     p.add_argument("--no-multi", action="store_true", help="fleet: skip the multi-slice (q/k/v, gate/up) step")
     p.add_argument("--streams", type=int, default=3,
-                   help="fleet: spread the step's modules over this many streams (one workspace each)")
+                   help="fleet: run the modules of one stage (q/k/v; gate/up) on up to this many streams")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--warm", action="store_true", help="no rotation (cache-resident timing)")
     p.add_argument("--no-graph", action="store_true", help="time eager launches only (counter runs)")
@@ -652,6 +652,12 @@ def run_fleet(args, rs, torch, dev):
     mod_ws = [torch.empty(rs.lora_workspace_bytes(st, T), dtype=torch.uint8, device=dev) for st in stores]
 
     nstr = max(1, args.streams)
+    stages = []  # module indices per (layer, input kind), in forward order
+    for i, m in enumerate(meta):
+        if stages and meta[stages[-1][0]][0] == m[0] and meta[stages[-1][0]][5] == m[5]:
+            stages[-1].append(i)
+        else:
+            stages.append([i])
     side_streams = [torch.cuda.Stream() for _ in range(nstr - 1)]  # default priority
     str_ws = [ws] + [torch.empty_like(ws) for _ in range(nstr - 1)]
 
@@ -659,17 +665,21 @@ def run_fleet(args, rs, torch, dev):
         if phases == 3:
             rs.lora_segment(ids, n, seg=seg)
         if phases == 3 and nstr > 1:
-            # Module i on stream i % nstr with that stream's workspace; the
-            # streams fork after the grouping and join at the end.
+            # The modules of one stage (those reading the same input: q/k/v,
+            # then o, then gate/up, then down, layer after layer) go to
+            # different streams, each with its own workspace; a stage starts
+            # when the previous one has finished, as in a forward pass, where
+            # each stage's input comes from the one before.
             main = torch.cuda.current_stream()
-            for sst in side_streams:
-                sst.wait_stream(main)
-            for i, (st, m, y) in enumerate(zip(stores, meta, ys)):
-                k = i % nstr
-                with torch.cuda.stream(main if k == 0 else side_streams[k - 1]):
-                    rs.lora_apply_batched(st, xs[(m[0], m[5])], y, seg=seg, ws=str_ws[k])
-            for sst in side_streams:
-                main.wait_stream(sst)
+            for stage in stages:
+                for sst in side_streams:
+                    sst.wait_stream(main)
+                for k, i in enumerate(stage):
+                    m = meta[i]
+                    with torch.cuda.stream(main if k % nstr == 0 else side_streams[k % nstr - 1]):
+                        rs.lora_apply_batched(stores[i], xs[(m[0], m[5])], ys[i], seg=seg, ws=str_ws[k % nstr])
+                for sst in side_streams:
+                    main.wait_stream(sst)
             return
         for st, m, y, w in zip(stores, meta, ys, mod_ws):
             x = xs[(m[0], m[5])]
@@ -737,22 +747,16 @@ def run_fleet(args, rs, torch, dev):
             groups.setdefault((m[0], m[5]), []).append(i)
         mstores = {g: rs.lora_pack_multi([stores[i] for i in idx]) for g, idx in groups.items() if len(idx) > 1}
         mbytes = max([rs.lora_multi_workspace_bytes(mst, T) for mst in mstores.values()] + [ws.numel()])
-        mws = [torch.empty(mbytes, dtype=torch.uint8, device=dev) for _ in range(nstr)]
+        mws = [torch.empty(mbytes, dtype=torch.uint8, device=dev)]
 
         def step_multi(phases=3):
+            # One call per stage: nothing is left to overlap in a forward pass.
             rs.lora_segment(ids, n, seg=seg)
-            main = torch.cuda.current_stream()
-            for sst in side_streams:
-                sst.wait_stream(main)
-            for i, (g, idx) in enumerate(groups.items()):
-                k = i % nstr
-                with torch.cuda.stream(main if k == 0 else side_streams[k - 1]):
-                    if len(idx) > 1:
-                        rs.lora_apply_multi(mstores[g], xs[g], [ys[j] for j in idx], seg=seg, ws=mws[k])
-                    else:
-                        rs.lora_apply_batched(stores[idx[0]], xs[g], ys[idx[0]], seg=seg, ws=mws[k])
-            for sst in side_streams:
-                main.wait_stream(sst)
+            for g, idx in groups.items():
+                if len(idx) > 1:
+                    rs.lora_apply_multi(mstores[g], xs[g], [ys[j] for j in idx], seg=seg, ws=mws[0])
+                else:
+                    rs.lora_apply_batched(stores[idx[0]], xs[g], ys[idx[0]], seg=seg, ws=mws[0])
 
         saved = sum(T * meta[idx[0]][3] * 2 * (len(idx) - 1) for idx in groups.values())
         step_fn = step
