@@ -453,34 +453,19 @@ __device__ __forceinline__ void store_elem(typename E::storage* out, size_t i, d
   else out[i] = (float)v;
 }
 
-// out[c * step] = sum_i x[i] W[c][i] (W transposed) for c < k, 0 for
-// k <= c < stored.  Four interleaved partial sums per component keep the
-// float64 FMA chain short; W[c][0 .. RB) is read with uniform addresses.
-template <typename E, int RB>
-__device__ __forceinline__ void write_components(const double* x, const double* __restrict__ W, int k, int stored,
-                                                 typename E::storage* out, size_t step) {
-  for (int c = 0; c < stored; ++c) {
-    double s = 0.0;
-    if (c < k) {
-      double acc[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-      for (int i = 0; i < RB; ++i) acc[i & 3] = fma(x[i], W[c * kRsvdR + i], acc[i & 3]);
-      s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    }
-    store_elem<E>(out, (size_t)c * step, s);
-  }
-}
-
-// Workgroup (adapter, block): blocks [0, nbo) write 256 rows of B' each (a
-// thread per row), the rest 256 columns of A' each (a thread per column).
-// The workgroup first copies its tile of B (256 whole rows, when rows are
-// 16-byte multiples) or of A (all r rows, 256 columns) into LDS with
-// coalesced 16-byte loads; each thread then takes its row or column from
-// LDS into float64 registers.  Components c < min(k_a, r) come from W; the
-// others (a retained rank above r, or padding up to the stored rank) are
-// zero.  W is read with addresses uniform over the workgroup (the separate
-// restrict-qualified arguments let those loads go through the scalar unit,
-// one operand per FMA from SGPRs).
+// Workgroup (adapter, block): blocks [0, nbo) write 256 rows of B' each, the
+// rest 256 columns of A' each.  The workgroup first copies its tile of B
+// (256 whole rows) or of A (all r rows, 256 columns) into LDS with coalesced
+// 16-byte loads (element by element when B's rows are not 16-byte
+// multiples).  Then float64 MFMA (16 x 16 x 4), K = the original rank:
+//   B side: D[row][c] = sum_i B[row][i] W_B[i][c]   (M = 16 rows, N = 16 components)
+//   A side: D[c][col] = sum_i W_A[i][c] A[i][col]   (M = 16 components, N = 16 columns)
+// W operand: lane l holds W[4 s + l/16][c0 + l%16] (zero for components at or
+// past min(k_a, r), so that padding up to the stored rank comes out zero);
+// tile operand: lane l holds the tile value at (row or column l%16, rank
+// 4 s + l/16), zero past r.  Wave w takes the tile's 16-row (16-column) blocks
+// w, w + 4, w + 8, w + 12.  Result layout: lane l, element v holds row 4 v +
+// l/16, column l%16 of the 16 x 16 block.
 template <typename E, int RB>
 __global__ void __launch_bounds__(256) rsvd_write_kernel(RsvdWriteArgs p, const char* __restrict__ A,
                                                          const char* __restrict__ B, const double* __restrict__ ws,
@@ -488,68 +473,82 @@ __global__ void __launch_bounds__(256) rsvd_write_kernel(RsvdWriteArgs p, const 
                                                          typename E::storage* __restrict__ outB) {
   typedef typename E::storage S;
   constexpr int KV = E::kVec;
+  constexpr int KS = RB / 4;       // K steps
   constexpr int kRowB = RB + KV;  // padded B row in LDS (elements), 16-byte multiple
   constexpr int kTileB = 256 * kRowB, kTileA = RB * 256;
   __shared__ __align__(16) S tile[kTileB > kTileA ? kTileB : kTileA];
   const int nb = p.nbo + (p.d_in + 255) / 256;
   const int a = blockIdx.x / nb, blk = blockIdx.x - a * nb;
-  const int tid = threadIdx.x, r = p.r;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = p.r;
   const int ro = p.row_off[a], stored = p.rank[a];
   const int k = min(p.true_rank[a], r);
   if (stored <= 0 || ro < 0 || ro > p.R - stored) return;  // uniform per workgroup
   const bool bside = blk < p.nbo;
-  const double* __restrict__ W = ws + ((size_t)a * kWsMats + (bside ? kWsWB : kWsWA)) * kRsvdMat;
-  double x[RB];
+  const double* __restrict__ Wt = ws + ((size_t)a * kWsMats + (bside ? kWsWB : kWsWA)) * kRsvdMat;
+  auto widen1 = [](S v) -> double {
+    if constexpr (E::kBytes == 2) return (double)__uint_as_float((uint32_t)v << 16);
+    else return (double)v;
+  };
+  const int li = l >> 4, lj = l & 15;
+  int n0 = 0, nrows = 0;  // the tile's first row (B) or column (A), and how many
   if (bside) {
-    const int o0 = blk * 256, rows = min(256, p.d_out - o0);
-    const int o = o0 + tid;
-    const char* bblk = B + ((size_t)a * p.d_out + o0) * r * E::kBytes;
+    n0 = blk * 256;
+    nrows = min(256, p.d_out - n0);
+    const char* bblk = B + ((size_t)a * p.d_out + n0) * r * E::kBytes;
     if (r % KV == 0) {
       const int vpr = r / KV;  // 16-byte vectors per row
-      for (int v = tid; v < rows * vpr; v += 256) {
+      for (int v = tid; v < nrows * vpr; v += 256) {
         const int row = v / vpr, c0 = (v - row * vpr) * KV;
         *reinterpret_cast<uint4*>(&tile[row * kRowB + c0]) = ld16(bblk + (size_t)v * 16);
       }
-      __syncthreads();
-      if (tid >= rows) return;
-#pragma unroll
-      for (int vv = 0; vv < RB / KV; ++vv) {
-        float f[KV];
-        if (vv * KV < r) {
-          E::widen(*reinterpret_cast<const uint4*>(&tile[tid * kRowB + vv * KV]), f);
-        } else {
-#pragma unroll
-          for (int t = 0; t < KV; ++t) f[t] = 0.f;
-        }
-#pragma unroll
-        for (int t = 0; t < KV; ++t) x[vv * KV + t] = (double)f[t];
-      }
     } else {
-      if (tid >= rows) return;
-      const char* brow = bblk + (size_t)tid * r * E::kBytes;
-#pragma unroll
-      for (int i = 0; i < RB; ++i) x[i] = i < r ? load_elem<E>(brow, i) : 0.0;
+      const S* src = reinterpret_cast<const S*>(bblk);
+      for (int e = tid; e < nrows * r; e += 256) tile[(e / r) * kRowB + e % r] = src[e];
     }
-    S* out = outB + (size_t)ro * p.d_out + (size_t)o * stored;
-    write_components<E, RB>(x, W, k, stored, out, 1);
   } else {
-    const int col0 = (blk - p.nbo) * 256, cols = min(256, p.d_in - col0);
-    const char* ablk = A + ((size_t)a * r * p.d_in + col0) * E::kBytes;
+    n0 = (blk - p.nbo) * 256;
+    nrows = min(256, p.d_in - n0);
+    const char* ablk = A + ((size_t)a * r * p.d_in + n0) * E::kBytes;
     const int vpr = 256 / KV;  // 16-byte vectors per tile row
     for (int v = tid; v < r * vpr; v += 256) {
       const int i = v / vpr, c0 = (v - i * vpr) * KV;
-      if (c0 < cols)  // d_in is a multiple of KV: a vector is wholly in or out
+      if (c0 < nrows)  // d_in is a multiple of KV: a vector is wholly in or out
         *reinterpret_cast<uint4*>(&tile[i * 256 + c0]) = ld16(ablk + ((size_t)i * p.d_in + c0) * E::kBytes);
     }
-    __syncthreads();
-    if (tid >= cols) return;
+  }
+  __syncthreads();
+  const int nblocks = (nrows + 15) / 16;
+  for (int c0 = 0; c0 < stored; c0 += 16) {  // 16 components at a time
+    const int cw = c0 + lj;                  // this lane's component in the W operand
+    double wv[KS];
 #pragma unroll
-    for (int i = 0; i < RB; ++i) {
-      if constexpr (E::kBytes == 2) x[i] = i < r ? (double)__uint_as_float((uint32_t)tile[i * 256 + tid] << 16) : 0.0;
-      else x[i] = i < r ? (double)tile[i * 256 + tid] : 0.0;
+    for (int s = 0; s < KS; ++s) {
+      const int i = 4 * s + li;
+      wv[s] = (cw < k && i < r) ? Wt[cw * kRsvdR + i] : 0.0;
     }
-    S* out = outA + (size_t)ro * p.d_in + col0 + tid;
-    write_components<E, RB>(x, W, k, stored, out, p.d_in);
+    for (int b = w; b < nblocks; b += 4) {
+      const int m0 = b * 16;  // first row (B) or column (A) of the block in the tile
+      f64x4_t acc = (f64x4_t){0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int i = 4 * s + li;
+        const double tv = i < r ? widen1(bside ? tile[(m0 + lj) * kRowB + i] : tile[i * 256 + m0 + lj]) : 0.0;
+        acc = bside ? __builtin_amdgcn_mfma_f64_16x16x4f64(tv, wv[s], acc, 0, 0, 0)
+                    : __builtin_amdgcn_mfma_f64_16x16x4f64(wv[s], tv, acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int rr = 4 * v + li;  // row of the 16 x 16 result
+        if (bside) {
+          const int row = m0 + rr, c = c0 + lj;
+          if (row < nrows && c < stored)
+            store_elem<E>(outB, (size_t)ro * p.d_out + (size_t)(n0 + row) * stored + c, acc[v]);
+        } else {
+          const int c = c0 + rr, col = m0 + lj;
+          if (c < stored && col < nrows) store_elem<E>(outA, (size_t)(ro + c) * p.d_in + n0 + col, acc[v]);
+        }
+      }
+    }
   }
 }
 
