@@ -36,9 +36,23 @@ PEAK_GBPS = 8000.0
 COLD_BYTES = 2.0e9  # rotation set size: well past the 256 MB Infinity Cache
 # Sources each measured kernel family is built from: a counter record is used
 # only while the sources of its family are unchanged.
-KERNEL_SOURCES = ["shrink.hip", "expand.hip", "decode.hip", "tile_ops.h", "device_common.h", "plan.h"]
-JD_SOURCES = KERNEL_SOURCES + ["jd.hip"]
+# Sources of each kernel family: a traffic record holds only while its own
+# family's sources are unchanged.
+APPLY_SOURCES = ["shrink.hip", "expand.hip", "tile_ops.h", "device_common.h", "plan.h"]
+DECODE_SOURCES = ["decode.hip", "device_common.h", "plan.h"]
+KERNEL_SOURCES = APPLY_SOURCES + ["decode.hip"]
+JD_SOURCES = APPLY_SOURCES + ["jd.hip"]
 RSVD_SOURCES = ["rsvd.hip", "device_common.h", "plan.h"]
+
+
+def sources_of(kernel: str):
+    if kernel == "decode_apply":
+        return DECODE_SOURCES
+    if kernel.startswith("rsvd_"):
+        return RSVD_SOURCES
+    if kernel.startswith("jd_"):
+        return JD_SOURCES
+    return APPLY_SOURCES
 PEAK_FP64_TFLOPS = 78.6  # 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2.4 GHz
 
 WORKLOAD_NAMES = {
@@ -248,7 +262,7 @@ def traffic_for(workload: str, kernel: str, sources=None):
     with open(path) as f:
         rec = json.load(f)
     ent = rec.get(workload, {}).get(kernel)
-    if not ent or ent.get("kernel_sources_sha") != kernel_source_digest(sources):
+    if not ent or ent.get("kernel_sources_sha") != kernel_source_digest(sources or sources_of(kernel)):
         return None
     return ent.get("hbm_bytes_per_launch")
 
@@ -289,13 +303,12 @@ def summarize_pmc(key: str, fetch_dir: str, write_dir: str):
         c = RSVD_CONFIGS[key]
         keep = sum(rs.lora_ranks_uniform([c["r"]] * c["n"], 1.0 / 12.0, 4))  # the spectral budget, met exactly
         alg = rsvd_algorithmic(c["n"], c["r"], c["d_in"], c["d_out"], keep, 2)
-        kernels, sources = (("rsvd_gram", alg["gram_bytes"]), ("rsvd_write", alg["write_bytes"])), RSVD_SOURCES
+        kernels = (("rsvd_gram", alg["gram_bytes"]), ("rsvd_write", alg["write_bytes"]))
     else:
         wl = build_workload(key)
         m = wl.module
         nb = algorithmic_bytes(wl.ids, m.ranks, m.n, m.d_in, m.d_out, 2 if wl.dtype == "bf16" else 4)
         kernels = (("shrink", nb["shrink"]), ("expand", nb["expand"]), ("decode_apply", nb["total"]))
-        sources = KERNEL_SOURCES
     path = os.path.join(ROOT, "profiles", "traffic.json")
     rec = json.load(open(path)) if os.path.exists(path) else {}
     ent = {}
@@ -308,7 +321,7 @@ def summarize_pmc(key: str, fetch_dir: str, write_dir: str):
         wb = float(np.mean(wk)) * 1024.0 / cw
         ent[kern] = {"hbm_bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
                      "algorithmic_bytes": alg, "traffic_over_algorithmic": round((fb + wb) / alg, 3),
-                     "dispatches": len(fk), "kernel_sources_sha": kernel_source_digest(sources)}
+                     "dispatches": len(fk), "kernel_sources_sha": kernel_source_digest(sources_of(kern))}
     if not ent:
         raise SystemExit("no library kernel dispatches in the counter runs")
     ent["calibration"] = {"copy_bytes": CALIBRATE_BYTES, "fetch_factor": round(cf, 4), "write_factor": round(cw, 4)}

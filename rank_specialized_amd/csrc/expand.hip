@@ -223,16 +223,18 @@ __device__ __forceinline__ void expand_vec_item(const ExpandArgs& p, const TileE
   const int mt = min(kVecTokens, m - t0);
   const int nf = min(8, p.d_out - o);  // 8; 4 for a float32 row of 4 (mod 8) features; <= 0 past the row
   const uint4 zero = make_uint4(0, 0, 0, 0);
-  // y rows of tokens t0 .. t0 + 3 and the B block, issued first.
-  char* yp[kVecTokens];
+  // y rows of tokens t0 .. t0 + 3 and the B block, issued first, after the
+  // four token indices in one load (t0 is a multiple of 4).
+  static_assert(kVecTokens == 4, "one 16-byte load of token indices");
+  const int4 tk4 = *reinterpret_cast<const int4*>(ent->tok + t0);
+  int tk[kVecTokens] = {tk4.x, tk4.y, tk4.z, tk4.w};  // -1: no row
   uint4 yv[kVecTokens][YV];
 #pragma unroll
   for (int t = 0; t < kVecTokens; ++t) {
-    const int tok = t < mt ? ent->tok[t0 + t] : -1;
-    yp[t] = ((unsigned)tok < (unsigned)p.T && nf > 0) ? p.y + (int64_t)tok * p.ldy_bytes + (size_t)o * E::kBytes
-                                                      : nullptr;
+    tk[t] = (t < mt && (unsigned)tk[t] < (unsigned)p.T && nf > 0) ? tk[t] : -1;
+    const char* yr = p.y + (int64_t)tk[t] * p.ldy_bytes + (size_t)o * E::kBytes;
 #pragma unroll
-    for (int v = 0; v < YV; ++v) yv[t][v] = (yp[t] && v * V < nf) ? ld16_stream(yp[t] + 16 * v) : zero;
+    for (int v = 0; v < YV; ++v) yv[t][v] = (tk[t] >= 0 && v * V < nf) ? ld16_stream(yr + 16 * v) : zero;
   }
   const char* bb = p.b_pack + ((size_t)ro * p.d_out + (size_t)o * R) * E::kBytes;
   uint4 bv[BV];
@@ -285,7 +287,8 @@ __device__ __forceinline__ void expand_vec_item(const ExpandArgs& p, const TileE
   }
 #pragma unroll
   for (int t = 0; t < kVecTokens; ++t) {
-    if (yp[t] == nullptr) continue;
+    if (tk[t] < 0) continue;
+    char* yr = p.y + (int64_t)tk[t] * p.ldy_bytes + (size_t)o * E::kBytes;
 #pragma unroll
     for (int v = 0; v < YV; ++v) {
       if (v * V >= nf) continue;
@@ -293,7 +296,7 @@ __device__ __forceinline__ void expand_vec_item(const ExpandArgs& p, const TileE
       E::widen(yv[t][v], f);
 #pragma unroll
       for (int k = 0; k < V; ++k) f[k] = f[k] + sc * acc[t][v * V + k];
-      st16_stream(yp[t] + 16 * v, E::narrow(f));
+      st16_stream(yr + 16 * v, E::narrow(f));
     }
   }
 }

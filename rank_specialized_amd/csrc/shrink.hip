@@ -63,9 +63,14 @@ struct ShrinkArgs {
 };
 
 // v[ng] for ng = 1..4 without indexing the argument array at run time
-// (which would copy it to private memory).
+// (which would copy it to private memory).  The four values are taken as
+// wave-uniform scalars first: a select between argument fields is otherwise
+// turned into one vector load of the selected field, a memory round trip
+// (waited for at once) wherever ng differs across lanes.
 __device__ __forceinline__ int by_ng(const int (&v)[5], int ng) {
-  return ng <= 1 ? v[1] : ng == 2 ? v[2] : ng == 3 ? v[3] : v[4];
+  const int v1 = __builtin_amdgcn_readfirstlane(v[1]), v2 = __builtin_amdgcn_readfirstlane(v[2]);
+  const int v3 = __builtin_amdgcn_readfirstlane(v[3]), v4 = __builtin_amdgcn_readfirstlane(v[4]);
+  return ng <= 1 ? v1 : ng == 2 ? v2 : ng == 3 ? v3 : v4;
 }
 
 // Grouping state in LDS (no per-thread state lives across the item loop):
