@@ -55,7 +55,6 @@ struct ShrinkArgs {
   float* part;
   int64_t ldp, pstride;  // floats: row stride, distance between partials
   char* plan;
-  int warm_key;
   // ids mode: when set, token t is grouped by id_map[ids[t]] (ids outside
   // [0, id_map_n) by -1), e.g. the cluster of its adapter.
   const int32_t* id_map;
@@ -96,23 +95,20 @@ __global__ void __launch_bounds__(kShrinkThreads, 4) shrink_kernel(ShrinkArgs p)
   __shared__ int s_it[kMaxItems][9];
   __shared__ int s_tok[kMaxItems][kSubTile];
   __shared__ int s_bc[kMaxItems][kShrinkWaves];
-  __shared__ int s_sink;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = p.n, T = p.T;
 
-  // 1. Tokens per adapter into info[].  The metadata of this thread's
-  //    adapters is loaded meanwhile (ranks are needed below; row offsets and
-  //    scales are only folded into a value that is never stored in
-  //    practice: the loads bring them into the cache for step 3).
+  // 1. Tokens per adapter into info[], and the ranks of this thread's
+  //    adapters (needed in step 2).
+  //    The APT loads are issued before any is used, from indices clamped
+  //    into [0, n): a load under a branch, used at once, is waited for before
+  //    the next one is issued (APT serial round trips).
   const int a0 = tid * APT;
   int rk_[APT];
-  int warm = 0;
 #pragma unroll
-  for (int i = 0; i < APT; ++i) {
-    const int a = a0 + i;
-    rk_[i] = a < n ? p.rank[a] : 0;
-    if (a < n) warm ^= p.row_off[a] ^ __float_as_int(p.scale[a]);
-  }
+  for (int i = 0; i < APT; ++i) rk_[i] = p.rank[min(a0 + i, n - 1)];  // n >= 1
+#pragma unroll
+  for (int i = 0; i < APT; ++i) rk_[i] = a0 + i < n ? rk_[i] : 0;
   if (kIds) {
     // ids: 4 per thread per 16-byte load, all loads issued before the
     // histogram consumes them (T <= 16384: at most 8 loads per thread).
@@ -198,10 +194,7 @@ __global__ void __launch_bounds__(kShrinkThreads, 4) shrink_kernel(ShrinkArgs p)
   const int first = blockIdx.x;
   const int nk = first < items ? min(kMaxItems, (items - first + (int)gridDim.x - 1) / (int)gridDim.x) : 0;
   __syncthreads();
-  if (nk == 0) {  // uniform: no barrier follows for this workgroup
-    if (warm == p.warm_key) s_sink = warm;
-    return;
-  }
+  if (nk == 0) return;  // uniform: no barrier follows for this workgroup
 
   // 3. Owner, sub-tile and K chunk of each item: lane k of wave 0 takes item
   //    k (binary search for the thread range whose item prefix brackets it,
@@ -376,7 +369,6 @@ __global__ void __launch_bounds__(kShrinkThreads, 4) shrink_kernel(ShrinkArgs p)
     }
     __syncthreads();  // red is rewritten by the next item
   }
-  if (warm == p.warm_key) s_sink = warm;  // warm_key is never produced by valid metadata
 }
 
 // ------------------------------------------------------------- reduce
@@ -541,7 +533,6 @@ hipError_t launch_shrink(const lora_store& s, const int32_t* ids, const int32_t*
   a.ldp = partial_ld(s.r_max);
   a.pstride = (int64_t)T * a.ldp;
   a.plan = base + L.plan;
-  a.warm_key = 0x7fc00001;  // a NaN pattern folded with row offsets: never equal in practice
   a.id_map = ids ? id_map : nullptr;
   a.id_map_n = id_map_n;
   const bool with_ids = ids != nullptr;
