@@ -95,6 +95,7 @@ __global__ void __launch_bounds__(kShrinkThreads, 4) shrink_kernel(ShrinkArgs p)
   __shared__ int s_it[kMaxItems][9];
   __shared__ int s_tok[kMaxItems][kSubTile];
   __shared__ int s_bc[kMaxItems][kShrinkWaves];
+  __shared__ int s_owner[kMaxItems];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n = p.n, T = p.T;
 
@@ -193,28 +194,36 @@ __global__ void __launch_bounds__(kShrinkThreads, 4) shrink_kernel(ShrinkArgs p)
   const int items = (int)(tot & 0xffffffu);
   const int first = blockIdx.x;
   const int nk = first < items ? min(kMaxItems, (items - first + (int)gridDim.x - 1) / (int)gridDim.x) : 0;
+  {  // the thread whose item range holds item k records itself as its owner
+    const int i0 = (int)(pre & 0xffffffu), ni = (int)(mine & 0xffffffu);
+#pragma unroll
+    for (int k = 0; k < kMaxItems; ++k) {
+      const int it = first + k * (int)gridDim.x;
+      if (k < nk && it >= i0 && it < i0 + ni) s_owner[k] = tid;
+    }
+  }
   __syncthreads();
   if (nk == 0) return;  // uniform: no barrier follows for this workgroup
 
   // 3. Owner, sub-tile and K chunk of each item: lane k of wave 0 takes item
-  //    k (binary search for the thread range whose item prefix brackets it,
-  //    then a walk over that thread's adapters).  Its metadata loads are
-  //    issued here and written to LDS only after step 4.
+  //    k (the thread that owns it, recorded above, then a walk over that
+  //    thread's adapters, whose info entries are read together first).  Its
+  //    metadata loads are issued here and written to LDS only after step 4.
   int m_rank = 0, m_ro = 0;
   float m_sc = 0.f;
   if (w == 0 && lane < nk) {
     const int it = first + lane * (int)gridDim.x;
-    int lo = 0, hi = kShrinkThreads;  // items(pref[lo]) <= it < items(pref[hi])
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if ((int)(s_pref[mid] & 0xffffffu) <= it) lo = mid; else hi = mid;
-    }
+    const int lo = s_owner[lane];
     const uint64_t b = s_pref[lo];
+    int iv_[APT];
+#pragma unroll
+    for (int i = 0; i < APT; ++i) iv_[i] = lo * APT + i < n ? info[lo * APT + i] : 0;
     int s_items = (int)(b & 0xffffffu), s_sub = (int)((b >> 24) & 0xfffffu);
     int pos = base_pos + (int)(b >> 44);
+#pragma unroll
     for (int i = 0; i < APT; ++i) {
       const int a = lo * APT + i;
-      const int v = info[a];
+      const int v = iv_[i];
       const int c = v & 0xfffff, ng = v >> 20;
       const int sub = ng ? (c + kSubTile - 1) / kSubTile : 0;
       const int S = by_ng(p.S, ng);
