@@ -366,8 +366,9 @@ __device__ __forceinline__ void expand_wave(const ExpandArgs& p) {
 
 // bf16 runs 4 waves per SIMD (more y rows in flight); float32, a
 // small-shape type here, is left to the compiler.  The slice mode of bf16
-// spills 12 bytes per lane at 4 waves per SIMD and is still faster there
-// than at 3 (the y rows in flight matter more).
+// fits 4 waves per SIMD without spilling since the vector path keeps its
+// rows as token indices; at 3 waves per SIMD it was slower (the y rows in
+// flight matter more).
 template <typename E, bool kPart, bool kSlice = false>
 __global__ void __launch_bounds__(kExpandWaves * 64) __attribute__((amdgpu_waves_per_eu(E::kBytes == 2 ? 4 : 1)))
 expand_kernel(ExpandArgs p) {

@@ -163,6 +163,24 @@ def test_decode_fused_matches_split(name, dtype, grouped):
             assert np.abs(y_host(y2) - ref).max() <= tol, "split"
 
 
+def test_decode_float32_half_feature_group():
+    """float32 rows of 4 (mod 8) output features, where the row's last
+    thread holds 4 features (half its B block and y chunks in range), with
+    one adapter and with 64 (the largest fleet whose metadata comes from lane
+    copies), d_in down to one 4-element chunk: the one-launch form, bit for
+    bit on exact integer data."""
+    dev = device()
+    for n, d_in, d_out, ranks in ((1, 4, 4100, [3]), (64, 2044, 12, [1, 2, 3, 4] * 16)):
+        wl = make_random_workload(97 + n, 70, n, d_in, d_out, ranks, dtype="fp32", integer=True)
+        store = pack(wl, dev)
+        assert rs.lora_apply_launches(store, wl.T, True) == 1
+        x, ids, y = inputs(wl, dev)
+        note(f"decode f32 half group n={n} d={d_in}->{d_out}")
+        rs.lora_apply_batched(store, x, y, ids=ids)
+        torch.cuda.synchronize()
+        assert np.array_equal(y_host(y), _ref(wl).astype(np.float32)), (n, d_in, d_out)
+
+
 def test_separate_kernels_integer_exact_decode():
     """The standalone shrink + expand (not the fused path) on a decode shape."""
     dev = device()
