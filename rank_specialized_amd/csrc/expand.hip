@@ -67,28 +67,32 @@ struct ExpandArgs {
   int sl_r_max, sl_R;
 };
 
-template <typename E, bool kPart, int NQ>
-__device__ __forceinline__ void expand_item(const ExpandArgs& p, const TileEntry* ent, int m, int r, int pos0,
-                                            int ro, float sc, int S, int o, int hoff) {
+template <typename E, bool kPart, int NQ, int RUN>
+__device__ __forceinline__ void expand_run(const ExpandArgs& p, const TileEntry* ent, int m, int r, int pos0,
+                                           int ro, float sc, int S, int fb0, int nb, int hoff) {
   constexpr int V = E::kVec;
   constexpr int KSTEP = 4 * V;  // ranks per K chunk
   constexpr int YV = 8 / V;     // 16-byte vectors per 8 features: bf16 1, f32 2
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, g = lane >> 4;
   const uint4 zero = make_uint4(0, 0, 0, 0);
-  // y rows of tokens 4g .. 4g + 3 (issued first: the longest wait).
-  char* yp[4];
-  uint4 yv[4][YV];
+  // Rows of tokens 4g .. 4g + 3 (nullptr: no token), the same for every
+  // feature block of the run.
+  const char* yrow[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int t = 4 * g + e;
     const int tok = t < m ? ent->tok[t] : -1;
-    yp[e] = ((unsigned)tok < (unsigned)p.T && o < p.d_out)
-                ? p.y + (int64_t)tok * p.ldy_bytes + (size_t)o * E::kBytes
-                : nullptr;
-#pragma unroll
-    for (int v = 0; v < YV; ++v) yv[e][v] = (yp[e] && o + v * V < p.d_out) ? ld16_stream(yp[e] + 16 * v) : zero;
+    yrow[e] = (unsigned)tok < (unsigned)p.T ? p.y + (int64_t)tok * p.ldy_bytes : nullptr;
   }
+  auto feat = [&](int k) { return (fb0 + k) * kExpandCols + 8 * c; };  // first feature of the lane in block k
+  auto load_y = [&](int o, uint4(&yv)[4][YV]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int v = 0; v < YV; ++v)
+        yv[e][v] = (yrow[e] && o + v * V < p.d_out) ? ld16_stream(yrow[e] + (size_t)(o + v * V) * E::kBytes) : zero;
+  };
   // B rows o .. o + 7 (one per N block), ranks of this lane's K chunks.
   // bf16 rows of an odd rank start on 2-byte boundaries, and a 16-byte
   // buffer load must start on a 4-byte one: such a chunk (row o + b odd,
@@ -97,7 +101,7 @@ __device__ __forceinline__ void expand_item(const ExpandArgs& p, const TileEntry
   const uint32_t row_bytes = (uint32_t)r * E::kBytes;
   const rsrc_t br = make_rsrc(p.b_pack + (size_t)ro * p.d_out * E::kBytes, (uint32_t)p.d_out * row_bytes);
   const bool odd_rows = E::kBytes == 2 && (r & 1);
-  auto load_b = [&](int q, uint4(&bb)[8]) {
+  auto load_b = [&](int q, int o, uint4(&bb)[8]) {
     const int j0 = q * KSTEP + g * V;
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
@@ -114,6 +118,10 @@ __device__ __forceinline__ void expand_item(const ExpandArgs& p, const TileEntry
       }
     }
   };
+  // First block's y rows and B rows, then the H chunks (read once for the
+  // whole run).
+  uint4 ya[4][YV], yb[4][YV];
+  load_y(feat(0), ya);
   // bf16 ranks above 32 take two K chunks.  The second chunk's B rows are
   // loaded after the first chunk's products, into the same registers: the
   // kernel then fits the registers of 4 waves per SIMD, for one more (mostly
@@ -121,7 +129,7 @@ __device__ __forceinline__ void expand_item(const ExpandArgs& p, const TileEntry
   constexpr int NB = (E::kBytes == 2 && NQ > 1) ? 1 : NQ;  // chunks loaded up front
   uint4 bq[NB][8];
 #pragma unroll
-  for (int q = 0; q < NB; ++q) load_b(q, bq[q]);
+  for (int q = 0; q < NB; ++q) load_b(q, feat(0), bq[q]);
   // H chunks: token c of the sub-tile, ranks j0 .. j0 + V.
   HChunk<E> hc[NQ];
   const int hrow = pos0 + c;
@@ -168,31 +176,48 @@ __device__ __forceinline__ void expand_item(const ExpandArgs& p, const TileEntry
     }
     hc[q].set(f);
   }
-  f32x4_t acc[8];
+  // The run: block k's products and stores, with block k + 1's y rows
+  // issued before block k is waited for (its B rows first: waits are in
+  // issue order, so the next block's y loads must come after what block k
+  // needs).
 #pragma unroll
-  for (int b = 0; b < 8; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < RUN; ++k) {
+    if (k >= nb) break;
+    const int o = feat(k);
+    uint4(&ycur)[4][YV] = (k & 1) ? yb : ya;
+    uint4(&ynxt)[4][YV] = (k & 1) ? ya : yb;
+    if (k > 0) {
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    if (q >= NB) {
-      __builtin_amdgcn_sched_barrier(0);  // not above the previous chunk's products
-      load_b(q, bq[NB - 1]);
+      for (int q = 0; q < NB; ++q) load_b(q, o, bq[q]);
     }
-    const int nvalid = r - (q * KSTEP + g * V);
+    if (k + 1 < nb) load_y(feat(k + 1), ynxt);
+    f32x4_t acc[8];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) acc[b] = hc[q].mma(keep_first<E>(bq[q < NB ? q : NB - 1][b], nvalid), acc[b]);
-  }
-  // acc[b][e] = feature o + b of token 4g + e.
+    for (int b = 0; b < 8; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    if (yp[e] == nullptr) continue;
+    for (int q = 0; q < NQ; ++q) {
+      if (q >= NB) {
+        __builtin_amdgcn_sched_barrier(0);  // not above the previous chunk's products
+        load_b(q, o, bq[NB - 1]);
+      }
+      const int nvalid = r - (q * KSTEP + g * V);
 #pragma unroll
-    for (int v = 0; v < YV; ++v) {
-      if (o + v * V >= p.d_out) continue;
-      float f[V];
-      E::widen(yv[e][v], f);
+      for (int b = 0; b < 8; ++b) acc[b] = hc[q].mma(keep_first<E>(bq[q < NB ? q : NB - 1][b], nvalid), acc[b]);
+    }
+    // acc[b][e] = feature o + b of token 4g + e.
 #pragma unroll
-      for (int k = 0; k < V; ++k) f[k] = f[k] + sc * acc[v * V + k][e];
-      st16_stream(yp[e] + 16 * v, E::narrow(f));
+    for (int e = 0; e < 4; ++e) {
+      if (yrow[e] == nullptr) continue;
+      char* yp = const_cast<char*>(yrow[e]) + (size_t)o * E::kBytes;
+#pragma unroll
+      for (int v = 0; v < YV; ++v) {
+        if (o + v * V >= p.d_out) continue;
+        float f[V];
+        E::widen(ycur[e][v], f);
+#pragma unroll
+        for (int kk = 0; kk < V; ++kk) f[kk] = f[kk] + sc * acc[v * V + kk][e];
+        st16_stream(yp + 16 * v, E::narrow(f));
+      }
     }
   }
 }
@@ -302,7 +327,7 @@ __device__ __forceinline__ void expand_vec_item(const ExpandArgs& p, const TileE
 }
 
 // ------------------------------------------------------------ the kernel
-template <typename E, bool kPart, bool kSlice>
+template <typename E, bool kPart, bool kSlice, int RUN>
 __device__ __forceinline__ void expand_wave(const ExpandArgs& p) {
   constexpr int KSTEP = 4 * E::kVec;
   constexpr int kGroups = kVecMaxTokens / kVecTokens;
@@ -350,29 +375,45 @@ __device__ __forceinline__ void expand_wave(const ExpandArgs& p) {
     }
     return;
   }
-  if (slot >= p.fbn) return;
-  const int o = slot * kExpandCols + 8 * (threadIdx.x & 15);
+  const int runs = (p.fbn + RUN - 1) / RUN;
+  if (slot >= runs) return;
+  const int fb0 = slot * RUN, nb = min(RUN, p.fbn - fb0);
   const int nq = (r + KSTEP - 1) / KSTEP;
   if (nq <= 1) {
-    expand_item<E, kPart, 1>(p, ent, m, r, pos0, ro, sc, S, o, hoff);
+    expand_run<E, kPart, 1, RUN>(p, ent, m, r, pos0, ro, sc, S, fb0, nb, hoff);
   } else if constexpr (KSTEP == 32) {  // bf16: ranks <= 64 take at most 2 chunks
-    expand_item<E, kPart, 2>(p, ent, m, r, pos0, ro, sc, S, o, hoff);
+    expand_run<E, kPart, 2, RUN>(p, ent, m, r, pos0, ro, sc, S, fb0, nb, hoff);
   } else {
-    if (nq == 2) expand_item<E, kPart, 2>(p, ent, m, r, pos0, ro, sc, S, o, hoff);
-    else if (nq == 3) expand_item<E, kPart, 3>(p, ent, m, r, pos0, ro, sc, S, o, hoff);
-    else expand_item<E, kPart, 4>(p, ent, m, r, pos0, ro, sc, S, o, hoff);
+    if (nq == 2) expand_run<E, kPart, 2, RUN>(p, ent, m, r, pos0, ro, sc, S, fb0, nb, hoff);
+    else if (nq == 3) expand_run<E, kPart, 3, RUN>(p, ent, m, r, pos0, ro, sc, S, fb0, nb, hoff);
+    else expand_run<E, kPart, 4, RUN>(p, ent, m, r, pos0, ro, sc, S, fb0, nb, hoff);
   }
 }
 
-// bf16 runs 4 waves per SIMD (more y rows in flight); float32, a
-// small-shape type here, is left to the compiler.  The slice mode of bf16
-// fits 4 waves per SIMD without spilling since the vector path keeps its
-// rows as token indices; at 3 waves per SIMD it was slower (the y rows in
-// flight matter more).
-template <typename E, bool kPart, bool kSlice = false>
-__global__ void __launch_bounds__(kExpandWaves * 64) __attribute__((amdgpu_waves_per_eu(E::kBytes == 2 ? 4 : 1)))
-expand_kernel(ExpandArgs p) {
-  expand_wave<E, kPart, kSlice>(p);
+// bf16 runs 4 waves per SIMD with one feature block per wave, 3 with runs
+// (the second y buffer; spilling at 4 was slower); float32, a small-shape
+// type here, is left to the compiler.  At 3 waves per SIMD the one-block
+// form was slower (the y rows in flight matter more).
+template <typename E, bool kPart, bool kSlice, int RUN>
+__global__ void __launch_bounds__(kExpandWaves * 64)
+__attribute__((amdgpu_waves_per_eu(E::kBytes == 2 ? (RUN > 1 ? 3 : 4) : 1))) expand_kernel(ExpandArgs p) {
+  expand_wave<E, kPart, kSlice, RUN>(p);
+}
+
+template <int RUN>
+static hipError_t launch_expand_kernel(int dtype, bool part, bool slice, dim3 grid, dim3 block, hipStream_t stream,
+                                       const ExpandArgs& a) {
+  if (slice) {  // slice mode reads the shrink's partial sums
+    if (dtype == LORA_DTYPE_BF16) hipLaunchKernelGGL((expand_kernel<BF16, true, true, RUN>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((expand_kernel<F32, true, true, RUN>), grid, block, 0, stream, a);
+  } else if (dtype == LORA_DTYPE_BF16) {
+    if (part) hipLaunchKernelGGL((expand_kernel<BF16, true, false, RUN>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((expand_kernel<BF16, false, false, RUN>), grid, block, 0, stream, a);
+  } else {
+    if (part) hipLaunchKernelGGL((expand_kernel<F32, true, false, RUN>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((expand_kernel<F32, false, false, RUN>), grid, block, 0, stream, a);
+  }
+  return hipGetLastError();
 }
 
 static hipError_t launch_expand_impl(const lora_store& s, const lora_store* slice, const int32_t* hoff, int T,
@@ -414,21 +455,18 @@ static hipError_t launch_expand_impl(const lora_store& s, const lora_store* slic
   }
   a.fbv = (out.d_out + kVecCols - 1) / kVecCols;
   const int vec_waves = (kVecMaxTokens / kVecTokens) * a.fbv;
-  a.slots = a.fbn > vec_waves ? a.fbn : vec_waves;
+  // Runs of kExpandRun feature blocks per wave when the one-block form would
+  // launch many times the waves the GPU holds; otherwise one block per wave
+  // (more waves in flight).
+  const bool run = max_sub * (int64_t)a.fbn >= kExpandRunMinItems;
+  const int run_len = run ? kExpandRun : 1;
+  const int runs = (a.fbn + run_len - 1) / run_len;
+  a.slots = runs > vec_waves ? runs : vec_waves;
   const int64_t items = max_sub * a.slots;
   const dim3 block(kExpandWaves * 64);
   const dim3 grid((unsigned)((items + kExpandWaves - 1) / kExpandWaves));
-  if (slice) {  // slice mode reads the shrink's partial sums
-    if (s.dtype == LORA_DTYPE_BF16) hipLaunchKernelGGL((expand_kernel<BF16, true, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((expand_kernel<F32, true, true>), grid, block, 0, stream, a);
-  } else if (s.dtype == LORA_DTYPE_BF16) {
-    if (part) hipLaunchKernelGGL((expand_kernel<BF16, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((expand_kernel<BF16, false>), grid, block, 0, stream, a);
-  } else {
-    if (part) hipLaunchKernelGGL((expand_kernel<F32, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((expand_kernel<F32, false>), grid, block, 0, stream, a);
-  }
-  return hipGetLastError();
+  return run ? launch_expand_kernel<kExpandRun>(s.dtype, part, slice != nullptr, grid, block, stream, a)
+             : launch_expand_kernel<1>(s.dtype, part, slice != nullptr, grid, block, stream, a);
 }
 
 hipError_t launch_expand(const lora_store& s, int T, const void* ws, const float* h, int64_t ldh, void* y,

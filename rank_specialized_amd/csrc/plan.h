@@ -26,6 +26,13 @@ constexpr int kGroupMaxN = 4096;
 // The expand's wave covers kExpandCols output features of one sub-tile.
 constexpr int kExpandCols = 128;
 constexpr int kExpandWaves = 4;  // waves per expand workgroup
+// Feature blocks one matrix-path expand wave takes in turn (a run): its
+// sub-tile's tokens and h are read once, and each block's y rows are
+// issued before the previous block is computed.
+constexpr int kExpandRun = 4;
+// One-block items (sub-tiles x feature blocks) from which a call uses runs:
+// about 16 times the waves the GPU holds at 3 per SIMD.
+constexpr int64_t kExpandRunMinItems = 48 * 1024;
 // Sub-tiles of at most kVecMaxTokens tokens and rank at most kVecMaxRank
 // (bf16; half that for float32) take the vector path of the expand: one wave
 // per (sub-tile, kVecCols output features, group of kVecTokens tokens); the

@@ -181,6 +181,37 @@ def test_decode_float32_half_feature_group():
         assert np.array_equal(y_host(y), _ref(wl).astype(np.float32)), (n, d_in, d_out)
 
 
+# The matrix-path expand takes runs of feature blocks per wave when a call has
+# at least 48 Ki one-block items (plan sub-tile bound x 128-feature blocks);
+# prefill and the fleet's wide projections do.
+RUN_MIN_ITEMS = 48 * 1024
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_expand_runs_integer_exact(dtype):
+    """A call past the run threshold (T=4096, 128 adapters, d_out=17408): the
+    two-launch apply from ids, and the standalone shrink + expand from a
+    grouping, both bit for bit on exact integer data."""
+    dev = device()
+    T, n, d_in, d_out = 4096, 128, 32, 17408
+    assert (T + 15 * n) // 16 * ((d_out + 127) // 128) >= RUN_MIN_ITEMS
+    ranks = [1 + (a * 5) % 16 for a in range(n)] if dtype == "bf16" else [1 + (a * 3) % 4 for a in range(n)]
+    wl = make_random_workload(99, T, n, d_in, d_out, ranks, dtype=dtype, integer=True)
+    store = pack(wl, dev)
+    x, ids, y1 = inputs(wl, dev)
+    y2 = y1.clone()
+    note(f"expand runs {dtype} T={T} n={n} d_out={d_out}")
+    rs.lora_apply_batched(store, x, y1, ids=ids)
+    seg = rs.lora_segment(ids, store.n)
+    h = rs.lora_shrink(store, x, seg)
+    rs.lora_expand(store, h, seg, y2)
+    torch.cuda.synchronize()
+    ref = _ref(wl)
+    want = bf16_round_ref(ref) if dtype == "bf16" else ref.astype(np.float32)
+    assert np.array_equal(y_host(y1), want)
+    assert np.array_equal(y_host(y2), want)
+
+
 def test_separate_kernels_integer_exact_decode():
     """The standalone shrink + expand (not the fused path) on a decode shape."""
     dev = device()

@@ -130,3 +130,24 @@ def test_multi_stacked_rank_limit():
     with pytest.raises(rs.LoraError) as e:
         rs.lora_pack_multi(stores)
     assert e.value.status == 2
+
+
+def test_multi_runs_integer_exact():
+    """Slices wide enough that each slice's expand takes runs of feature
+    blocks (T=4096, 128 adapters, d_out 17408 and 2048): bit for bit on exact
+    integer data."""
+    dev = device()
+    T, n, d_in = 4096, 128, 32
+    ranks = ([1 + (a * 5) % 16 for a in range(n)], [1 + (a * 7) % 12 for a in range(n)])
+    ws = _slices(11, T, n, d_in, (17408, 2048), ranks, "bf16", integer=True)
+    stores = [pack(w, dev) for w in ws]
+    ms = rs.lora_pack_multi(stores)
+    x = to_dev(ws[0].x, torch.bfloat16, dev)
+    ids = torch.from_numpy(ws[0].ids.astype(np.int32)).to(dev)
+    ys = [torch.zeros(T, d, dtype=torch.bfloat16, device=dev) for d in (17408, 2048)]
+    note("multi runs")
+    rs.lora_apply_multi(ms, x, ys, ids=ids)
+    torch.cuda.synchronize()
+    for k, w in enumerate(ws):
+        ref = apply_ref(ws[0].x, ws[0].ids, w.module.A, w.module.B, w.module.scales)
+        assert np.array_equal(y_host(ys[k]), bf16_round_ref(ref)), k
