@@ -9,6 +9,10 @@
 // independent (no barriers); every wave issues its y rows and its B rows
 // before any arithmetic, so an item costs one memory round trip (two for
 // bf16 ranks above 32, whose second K chunk of B is read after the first).
+// In calls of at least kExpandRunMinItems such items a wave takes a run of
+// kExpandRun consecutive feature blocks of its sub-tile instead: tokens and
+// h are read once, and each block's y rows are issued before the previous
+// block's products, so the next block's loads overlap this block's work.
 //   D[token, feature] = H[token, j] . B_a^T[j, feature]
 // on 16x16 MFMA tiles (bf16: 16x16x32, f32: 16x16x4), eight N blocks per
 // wave.  Column c of N block b is feature o0 + 8 c + b, so lane (c, g) ends

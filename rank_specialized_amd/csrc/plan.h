@@ -28,8 +28,9 @@ constexpr int kExpandCols = 128;
 constexpr int kExpandWaves = 4;  // waves per expand workgroup
 // Feature blocks one matrix-path expand wave takes in turn (a run): its
 // sub-tile's tokens and h are read once, and each block's y rows are
-// issued before the previous block is computed.
-constexpr int kExpandRun = 4;
+// issued before the previous block is computed.  Measured against 4 and 8
+// (prefill, fleet): 2 is as fast or faster.
+constexpr int kExpandRun = 2;
 // One-block items (sub-tiles x feature blocks) from which a call uses runs:
 // about 16 times the waves the GPU holds at 3 per SIMD.
 constexpr int64_t kExpandRunMinItems = 48 * 1024;
