@@ -77,8 +77,9 @@ __device__ __forceinline__ int by_ng(const int (&v)[5], int ng) {
 //   pref[t]  = exclusive prefix, over the adapters of threads < t, of
 //              tokens << 44 | sub-tiles << 24 | items; pref[threads] = total
 // Thread t owns adapters [t * APT, (t + 1) * APT).  A workgroup takes items
-// blockIdx.x + k * gridDim.x, k < kMaxItems, and prepares all of them (owner,
-// sub-tile, K chunk, tokens, metadata) before the first one's loads.
+// blockIdx.x + k * gridDim.x in batches of kMaxItems, and prepares all of a
+// batch (owner, sub-tile, K chunk, tokens, metadata) before the first one's
+// loads.
 constexpr int kMaxItems = 8;
 
 template <typename E, bool kIds, int APT>
@@ -192,192 +193,197 @@ __global__ void __launch_bounds__(kShrinkThreads, 4) shrink_kernel(ShrinkArgs p)
   if (blockIdx.x == 0 && tid == 0) *reinterpret_cast<int32_t*>(p.plan) = total_sub;
   const int base_pos = kIds ? 0 : p.seg_off[0];
   const int items = (int)(tot & 0xffffffu);
-  const int first = blockIdx.x;
-  const int nk = first < items ? min(kMaxItems, (items - first + (int)gridDim.x - 1) / (int)gridDim.x) : 0;
-  {  // the thread whose item range holds item k records itself as its owner
-    const int i0 = (int)(pre & 0xffffffu), ni = (int)(mine & 0xffffffu);
+  // This workgroup's items: first + k G, k < n_mine (G workgroups, at most
+  // two per CU, so all are resident); taken in batches of kMaxItems, steps
+  // 3 to 5 once per batch on the grouping state of steps 1 and 2.
+  const int first = blockIdx.x, G = (int)gridDim.x;
+  const int n_mine = first < items ? (items - first + G - 1) / G : 0;
+  const int i0 = (int)(pre & 0xffffffu), ni = (int)(mine & 0xffffffu);
+  for (int b0 = 0; b0 < n_mine; b0 += kMaxItems) {  // uniform over the workgroup
+    const int nk = min(kMaxItems, n_mine - b0);
+    // The thread whose item range holds item k of the batch records itself
+    // as its owner.
 #pragma unroll
     for (int k = 0; k < kMaxItems; ++k) {
-      const int it = first + k * (int)gridDim.x;
+      const int it = first + (b0 + k) * G;
       if (k < nk && it >= i0 && it < i0 + ni) s_owner[k] = tid;
     }
-  }
-  __syncthreads();
-  if (nk == 0) return;  // uniform: no barrier follows for this workgroup
+    __syncthreads();
 
-  // 3. Owner, sub-tile and K chunk of each item: lane k of wave 0 takes item
-  //    k (the thread that owns it, recorded above, then a walk over that
-  //    thread's adapters, whose info entries are read together first).  Its
-  //    metadata loads are issued here and written to LDS only after step 4.
-  int m_rank = 0, m_ro = 0;
-  float m_sc = 0.f;
-  if (w == 0 && lane < nk) {
-    const int it = first + lane * (int)gridDim.x;
-    const int lo = s_owner[lane];
-    const uint64_t b = s_pref[lo];
-    int iv_[APT];
+    // 3. Owner, sub-tile and K chunk of each item: lane k of wave 0 takes item
+    //    k (the thread that owns it, recorded above, then a walk over that
+    //    thread's adapters, whose info entries are read together first).  Its
+    //    metadata loads are issued here and written to LDS only after step 4.
+    int m_rank = 0, m_ro = 0;
+    float m_sc = 0.f;
+    if (w == 0 && lane < nk) {
+      const int it = first + (b0 + lane) * G;
+      const int lo = s_owner[lane];
+      const uint64_t b = s_pref[lo];
+      int iv_[APT];
 #pragma unroll
-    for (int i = 0; i < APT; ++i) iv_[i] = lo * APT + i < n ? info[lo * APT + i] : 0;
-    int s_items = (int)(b & 0xffffffu), s_sub = (int)((b >> 24) & 0xfffffu);
-    int pos = base_pos + (int)(b >> 44);
+      for (int i = 0; i < APT; ++i) iv_[i] = lo * APT + i < n ? info[lo * APT + i] : 0;
+      int s_items = (int)(b & 0xffffffu), s_sub = (int)((b >> 24) & 0xfffffu);
+      int pos = base_pos + (int)(b >> 44);
 #pragma unroll
-    for (int i = 0; i < APT; ++i) {
-      const int a = lo * APT + i;
-      const int v = iv_[i];
-      const int c = v & 0xfffff, ng = v >> 20;
-      const int sub = ng ? (c + kSubTile - 1) / kSubTile : 0;
-      const int S = by_ng(p.S, ng);
-      const int its = ng ? sub * S : 0;
-      if (it < s_items + its) {
-        const int j = (it - s_items) / S;
-        int* q = s_it[lane];
-        q[0] = a;
-        q[1] = pos + j * kSubTile;
-        q[2] = min(kSubTile, c - j * kSubTile);
-        q[6] = j;
-        q[7] = s_sub + j;
-        q[8] = it - s_items - j * S;
-        m_rank = p.rank[a];
-        m_ro = p.row_off[a];
-        m_sc = p.scale[a];
-        break;
+      for (int i = 0; i < APT; ++i) {
+        const int a = lo * APT + i;
+        const int v = iv_[i];
+        const int c = v & 0xfffff, ng = v >> 20;
+        const int sub = ng ? (c + kSubTile - 1) / kSubTile : 0;
+        const int S = by_ng(p.S, ng);
+        const int its = ng ? sub * S : 0;
+        if (it < s_items + its) {
+          const int j = (it - s_items) / S;
+          int* q = s_it[lane];
+          q[0] = a;
+          q[1] = pos + j * kSubTile;
+          q[2] = min(kSubTile, c - j * kSubTile);
+          q[6] = j;
+          q[7] = s_sub + j;
+          q[8] = it - s_items - j * S;
+          m_rank = p.rank[a];
+          m_ro = p.row_off[a];
+          m_sc = p.scale[a];
+          break;
+        }
+        s_items += its;
+        s_sub += sub;
+        pos += c;
       }
-      s_items += its;
-      s_sub += sub;
-      pos += c;
-    }
-  }
-  __syncthreads();
-  // 4. Each item's tokens: ranks [16 j, 16 j + 16) among the tokens of its
-  //    adapter, in token order.  ids: wave w scans a contiguous range of
-  //    64-token blocks twice - once to count each item's matches, then, after
-  //    a scan of the (item, wave) counts, to place them with ballot ranks.
-  if (kIds) {
-    const int nb = (T + 63) >> 6;
-    const int per = (nb + kShrinkWaves - 1) / kShrinkWaves;
-    const int b0 = w * per, b1 = min(nb, b0 + per);
-    int ad[kMaxItems], cnt[kMaxItems];
-#pragma unroll
-    for (int k = 0; k < kMaxItems; ++k) {
-      ad[k] = k < nk ? s_it[k][0] : -2;
-      cnt[k] = 0;
-    }
-    for (int b = b0; b < b1; ++b) {
-      const int t = b * 64 + lane;
-      const int id = t < T ? (int)id16[t] : -1;
-#pragma unroll
-      for (int k = 0; k < kMaxItems; ++k)
-        if (k < nk) cnt[k] += __popcll(__ballot(id == ad[k]));
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int k = 0; k < kMaxItems; ++k)
-        if (k < nk) s_bc[k][w] = cnt[k];
     }
     __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kMaxItems; ++k) {  // tokens of item k before wave w's range
-      int before = 0;
-      if (k < nk)
-        for (int ww = 0; ww < w; ++ww) before += s_bc[k][ww];
-      cnt[k] = before - (k < nk ? s_it[k][6] : 0) * kSubTile;
-    }
-    for (int b = b0; b < b1; ++b) {
-      const int t = b * 64 + lane;
-      const int id = t < T ? (int)id16[t] : -1;
+    // 4. Each item's tokens: ranks [16 j, 16 j + 16) among the tokens of its
+    //    adapter, in token order.  ids: wave w scans a contiguous range of
+    //    64-token blocks twice - once to count each item's matches, then, after
+    //    a scan of the (item, wave) counts, to place them with ballot ranks.
+    if (kIds) {
+      const int nb = (T + 63) >> 6;
+      const int per = (nb + kShrinkWaves - 1) / kShrinkWaves;
+      const int b0 = w * per, b1 = min(nb, b0 + per);
+      int ad[kMaxItems], cnt[kMaxItems];
 #pragma unroll
       for (int k = 0; k < kMaxItems; ++k) {
-        if (k < nk) {
-          const bool hit = id == ad[k];
-          const uint64_t bal = __ballot(hit);
-          const int rk = cnt[k] + __popcll(bal & lanemask_lt());
-          if (hit && rk >= 0 && rk < kSubTile) s_tok[k][rk] = t;
-          cnt[k] += __popcll(bal);
+        ad[k] = k < nk ? s_it[k][0] : -2;
+        cnt[k] = 0;
+      }
+      for (int b = b0; b < b1; ++b) {
+        const int t = b * 64 + lane;
+        const int id = t < T ? (int)id16[t] : -1;
+#pragma unroll
+        for (int k = 0; k < kMaxItems; ++k)
+          if (k < nk) cnt[k] += __popcll(__ballot(id == ad[k]));
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int k = 0; k < kMaxItems; ++k)
+          if (k < nk) s_bc[k][w] = cnt[k];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kMaxItems; ++k) {  // tokens of item k before wave w's range
+        int before = 0;
+        if (k < nk)
+          for (int ww = 0; ww < w; ++ww) before += s_bc[k][ww];
+        cnt[k] = before - (k < nk ? s_it[k][6] : 0) * kSubTile;
+      }
+      for (int b = b0; b < b1; ++b) {
+        const int t = b * 64 + lane;
+        const int id = t < T ? (int)id16[t] : -1;
+#pragma unroll
+        for (int k = 0; k < kMaxItems; ++k) {
+          if (k < nk) {
+            const bool hit = id == ad[k];
+            const uint64_t bal = __ballot(hit);
+            const int rk = cnt[k] + __popcll(bal & lanemask_lt());
+            if (hit && rk >= 0 && rk < kSubTile) s_tok[k][rk] = t;
+            cnt[k] += __popcll(bal);
+          }
+        }
+      }
+    } else {
+      for (int idx = tid; idx < nk * kSubTile; idx += kShrinkThreads) {
+        const int k = idx / kSubTile, i = idx - k * kSubTile;
+        if (i < s_it[k][2]) {
+          const int q = s_it[k][1] + i;
+          const int tk = (q >= 0 && q < T) ? p.perm[q] : -1;
+          s_tok[k][i] = (unsigned)tk < (unsigned)T ? tk : -1;
         }
       }
     }
-  } else {
-    for (int idx = tid; idx < nk * kSubTile; idx += kShrinkThreads) {
-      const int k = idx / kSubTile, i = idx - k * kSubTile;
-      if (i < s_it[k][2]) {
-        const int q = s_it[k][1] + i;
-        const int tk = (q >= 0 && q < T) ? p.perm[q] : -1;
-        s_tok[k][i] = (unsigned)tk < (unsigned)T ? tk : -1;
-      }
-    }
-  }
-  if (w == 0 && lane < nk) {
-    s_it[lane][3] = m_rank;
-    s_it[lane][4] = m_ro;
-    s_it[lane][5] = __float_as_int(m_sc);
-  }
-  __syncthreads();
-
-  TileEntry* entries = reinterpret_cast<TileEntry*>(p.plan + kPlanHeaderBytes);
-  for (int k = 0; k < nk; ++k) {
-    const int a = __builtin_amdgcn_readfirstlane(s_it[k][0]);
-    const int pos0 = __builtin_amdgcn_readfirstlane(s_it[k][1]);
-    const int m = __builtin_amdgcn_readfirstlane(s_it[k][2]);
-    const int r = __builtin_amdgcn_readfirstlane(s_it[k][3]);
-    const int ro = __builtin_amdgcn_readfirstlane(s_it[k][4]);
-    const float sc = __int_as_float(__builtin_amdgcn_readfirstlane(s_it[k][5]));
-    const int st = __builtin_amdgcn_readfirstlane(s_it[k][7]);
-    const int kc = __builtin_amdgcn_readfirstlane(s_it[k][8]);
-    const int ng = (r + 15) >> 4;
-    // 5. This wave's K steps of chunk kc.
-    {
-      const int tl = lane & 15;
-      const int tk = tl < m ? s_tok[k][tl] : -1;
-      const bool tval = tk >= 0;
-      const char* xrow = p.x + (int64_t)(tval ? tk : 0) * p.ldx_bytes;
-      const char* a_rows = p.a_pack + (size_t)ro * p.d_in * E::kBytes;
-      const int spw = by_ng(p.spw, ng);
-      const int k0 = kc * by_ng(p.kchunk, ng) + w * spw * KSTEP;
-      const int kw = spw * KSTEP;
-      f32x4_t* slot = red + w * p.ng_max * 64;
-      switch (ng) {
-        case 1: shrink_wave<E, 1, 8>(xrow, tval, a_rows, p.d_in, r, k0, kw, slot); break;
-        case 2: shrink_wave<E, 2, 5>(xrow, tval, a_rows, p.d_in, r, k0, kw, slot); break;
-        case 3: shrink_wave<E, 3, 4>(xrow, tval, a_rows, p.d_in, r, k0, kw, slot); break;
-        default: shrink_wave<E, 4, 3>(xrow, tval, a_rows, p.d_in, r, k0, kw, slot); break;
-      }
+    if (w == 0 && lane < nk) {
+      s_it[lane][3] = m_rank;
+      s_it[lane][4] = m_ro;
+      s_it[lane][5] = __float_as_int(m_sc);
     }
     __syncthreads();
-    // 6. Sum the waves' tiles in wave order; write partial kc.  Lane l of
-    //    row group q holds token l % 16, ranks 16 q + 4 (l / 16) + 0..3.
-    if (tid < ng * 64) {
-      const int q = tid >> 6, l = tid & 63;
-      f32x4_t s = red[q * 64 + l];
-#pragma unroll
-      for (int kk = 1; kk < kShrinkWaves; ++kk) s += red[(kk * p.ng_max + q) * 64 + l];
-      const int tk = l & 15;
-      const int j0 = q * 16 + 4 * (l >> 4);
-      const int row = pos0 + tk;
-      if (tk < m && row >= 0 && row < T) {
-        float* dst = p.part + (int64_t)kc * p.pstride + (int64_t)row * p.ldp + j0;
-        if (j0 + 3 < r) {
-          *reinterpret_cast<f32x4_t*>(dst) = s;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (j0 + e < r) dst[e] = s[e];
+
+    TileEntry* entries = reinterpret_cast<TileEntry*>(p.plan + kPlanHeaderBytes);
+    for (int k = 0; k < nk; ++k) {
+      const int a = __builtin_amdgcn_readfirstlane(s_it[k][0]);
+      const int pos0 = __builtin_amdgcn_readfirstlane(s_it[k][1]);
+      const int m = __builtin_amdgcn_readfirstlane(s_it[k][2]);
+      const int r = __builtin_amdgcn_readfirstlane(s_it[k][3]);
+      const int ro = __builtin_amdgcn_readfirstlane(s_it[k][4]);
+      const float sc = __int_as_float(__builtin_amdgcn_readfirstlane(s_it[k][5]));
+      const int st = __builtin_amdgcn_readfirstlane(s_it[k][7]);
+      const int kc = __builtin_amdgcn_readfirstlane(s_it[k][8]);
+      const int ng = (r + 15) >> 4;
+      // 5. This wave's K steps of chunk kc.
+      {
+        const int tl = lane & 15;
+        const int tk = tl < m ? s_tok[k][tl] : -1;
+        const bool tval = tk >= 0;
+        const char* xrow = p.x + (int64_t)(tval ? tk : 0) * p.ldx_bytes;
+        const char* a_rows = p.a_pack + (size_t)ro * p.d_in * E::kBytes;
+        const int spw = by_ng(p.spw, ng);
+        const int k0 = kc * by_ng(p.kchunk, ng) + w * spw * KSTEP;
+        const int kw = spw * KSTEP;
+        f32x4_t* slot = red + w * p.ng_max * 64;
+        switch (ng) {
+          case 1: shrink_wave<E, 1, 8>(xrow, tval, a_rows, p.d_in, r, k0, kw, slot); break;
+          case 2: shrink_wave<E, 2, 5>(xrow, tval, a_rows, p.d_in, r, k0, kw, slot); break;
+          case 3: shrink_wave<E, 3, 4>(xrow, tval, a_rows, p.d_in, r, k0, kw, slot); break;
+          default: shrink_wave<E, 4, 3>(xrow, tval, a_rows, p.d_in, r, k0, kw, slot); break;
         }
       }
+      __syncthreads();
+      // 6. Sum the waves' tiles in wave order; write partial kc.  Lane l of
+      //    row group q holds token l % 16, ranks 16 q + 4 (l / 16) + 0..3.
+      if (tid < ng * 64) {
+        const int q = tid >> 6, l = tid & 63;
+        f32x4_t s = red[q * 64 + l];
+#pragma unroll
+        for (int kk = 1; kk < kShrinkWaves; ++kk) s += red[(kk * p.ng_max + q) * 64 + l];
+        const int tk = l & 15;
+        const int j0 = q * 16 + 4 * (l >> 4);
+        const int row = pos0 + tk;
+        if (tk < m && row >= 0 && row < T) {
+          float* dst = p.part + (int64_t)kc * p.pstride + (int64_t)row * p.ldp + j0;
+          if (j0 + 3 < r) {
+            *reinterpret_cast<f32x4_t*>(dst) = s;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (j0 + e < r) dst[e] = s[e];
+          }
+        }
+      }
+      if (kc == 0 && tid < 32) {
+        int v = 0;
+        if (tid == 0) v = a;
+        else if (tid == 1) v = pos0;
+        else if (tid == 2) v = m;
+        else if (tid == 3) v = r;
+        else if (tid == 4) v = ro;
+        else if (tid == 5) v = __float_as_int(sc);
+        else if (tid == 6) v = by_ng(p.S, ng);
+        else if (tid >= 8 && tid < 8 + kSubTile) v = tid - 8 < m ? s_tok[k][tid - 8] : -1;
+        reinterpret_cast<int32_t*>(entries + st)[tid] = v;
+      }
+      __syncthreads();  // red is rewritten by the next item (and s_it, s_tok by the next batch)
     }
-    if (kc == 0 && tid < 32) {
-      int v = 0;
-      if (tid == 0) v = a;
-      else if (tid == 1) v = pos0;
-      else if (tid == 2) v = m;
-      else if (tid == 3) v = r;
-      else if (tid == 4) v = ro;
-      else if (tid == 5) v = __float_as_int(sc);
-      else if (tid == 6) v = by_ng(p.S, ng);
-      else if (tid >= 8 && tid < 8 + kSubTile) v = tid - 8 < m ? s_tok[k][tid - 8] : -1;
-      reinterpret_cast<int32_t*>(entries + st)[tid] = v;
-    }
-    __syncthreads();  // red is rewritten by the next item
-  }
+  }  // batches
 }
 
 // ------------------------------------------------------------- reduce
@@ -546,9 +552,10 @@ hipError_t launch_shrink(const lora_store& s, const int32_t* ids, const int32_t*
   a.id_map_n = id_map_n;
   const bool with_ids = ids != nullptr;
   const size_t lds = shrink_lds_bytes(T, s.n, s.r_max, with_ids);
+  // Two workgroups per CU, all resident (no second round of workgroups),
+  // each taking its items in batches of kMaxItems; fewer for fewer items.
   const int64_t items = max_sub * sp.S_max;
-  int64_t g = (items + kMaxItems - 1) / kMaxItems;  // every item within kMaxItems of a workgroup
-  if (g < 2LL * cu_count()) g = 2LL * cu_count();    // two workgroups per CU
+  const int64_t g = 2LL * cu_count();
   const int grid = (int)(g < items ? g : items);
   const bool bf = s.dtype == LORA_DTYPE_BF16;
   if (with_ids)
