@@ -212,6 +212,25 @@ def test_expand_runs_integer_exact(dtype):
     assert np.array_equal(y_host(y2), want)
 
 
+def test_shrink_batches_integer_exact():
+    """The fleet's down projection (d_in 18944: eight K chunks per sub-tile)
+    gives each resident shrink workgroup more than one batch of items: from
+    ids and from a supplied grouping, bit for bit on exact integer data."""
+    dev = device()
+    wl = make_config("5U", integer=True, layer=27, proj=6)
+    assert wl.module.d_in == 18944
+    store = pack(wl, dev)
+    x, ids, y1 = inputs(wl, dev)
+    y2 = y1.clone()
+    note("shrink batches: 5U down, ids and grouping")
+    rs.lora_apply_batched(store, x, y1, ids=ids)
+    rs.lora_apply_batched(store, x, y2, seg=rs.lora_segment(ids, store.n))
+    torch.cuda.synchronize()
+    want = bf16_round_ref(_ref(wl))
+    assert np.array_equal(y_host(y1), want)
+    assert np.array_equal(y_host(y2), want)
+
+
 def test_separate_kernels_integer_exact_decode():
     """The standalone shrink + expand (not the fused path) on a decode shape."""
     dev = device()
