@@ -261,7 +261,7 @@ __device__ __forceinline__ void expand_vec_item(const ExpandArgs& p, const TileE
 #pragma unroll
   for (int t = 0; t < kVecTokens; ++t) {
     tk[t] = (t < mt && (unsigned)tk[t] < (unsigned)p.T && nf > 0) ? tk[t] : -1;
-    const char* yr = p.y + (int64_t)tk[t] * p.ldy_bytes + (size_t)o * E::kBytes;
+    const char* yr = p.y + (int64_t)max(tk[t], 0) * p.ldy_bytes + (size_t)max(o, 0) * E::kBytes;
 #pragma unroll
     for (int v = 0; v < YV; ++v) yv[t][v] = (tk[t] >= 0 && v * V < nf) ? ld16_stream(yr + 16 * v) : zero;
   }

@@ -199,13 +199,13 @@ __global__ void __launch_bounds__(kShrinkThreads, 4) shrink_kernel(ShrinkArgs p)
   const int first = blockIdx.x, G = (int)gridDim.x;
   const int n_mine = first < items ? (items - first + G - 1) / G : 0;
   const int i0 = (int)(pre & 0xffffffu), ni = (int)(mine & 0xffffffu);
-  for (int b0 = 0; b0 < n_mine; b0 += kMaxItems) {  // uniform over the workgroup
-    const int nk = min(kMaxItems, n_mine - b0);
+  for (int kb = 0; kb < n_mine; kb += kMaxItems) {  // uniform over the workgroup
+    const int nk = min(kMaxItems, n_mine - kb);
     // The thread whose item range holds item k of the batch records itself
     // as its owner.
 #pragma unroll
     for (int k = 0; k < kMaxItems; ++k) {
-      const int it = first + (b0 + k) * G;
+      const int it = first + (kb + k) * G;
       if (k < nk && it >= i0 && it < i0 + ni) s_owner[k] = tid;
     }
     __syncthreads();
@@ -217,7 +217,7 @@ __global__ void __launch_bounds__(kShrinkThreads, 4) shrink_kernel(ShrinkArgs p)
     int m_rank = 0, m_ro = 0;
     float m_sc = 0.f;
     if (w == 0 && lane < nk) {
-      const int it = first + (b0 + lane) * G;
+      const int it = first + (kb + lane) * G;
       const int lo = s_owner[lane];
       const uint64_t b = s_pref[lo];
       int iv_[APT];
