@@ -166,6 +166,20 @@ __global__ void __launch_bounds__(kShrinkThreads, 4) shrink_kernel(ShrinkArgs p)
         }
       }
     }
+  } else if constexpr (APT <= 8) {
+    // Tokens per adapter from the grouping: all the thread's seg_off loads
+    // issued first, from indices clamped into the array's n + 2 entries (a
+    // loop of dependent load/store pairs waits for each pair in turn).
+    int s0[APT], s1[APT];
+#pragma unroll
+    for (int k = 0; k < APT; ++k) {
+      const int i = min(tid + k * kShrinkThreads, n);
+      s0[k] = p.seg_off[i];
+      s1[k] = p.seg_off[i + 1];
+    }
+#pragma unroll
+    for (int k = 0; k < APT; ++k)
+      if (tid + k * kShrinkThreads < n) info[tid + k * kShrinkThreads] = s1[k] - s0[k];
   } else {
     for (int i = tid; i < n; i += kShrinkThreads) info[i] = p.seg_off[i + 1] - p.seg_off[i];
   }
