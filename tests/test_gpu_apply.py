@@ -187,13 +187,15 @@ def test_decode_float32_half_feature_group():
 RUN_MIN_ITEMS = 48 * 1024
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_expand_runs_integer_exact(dtype):
-    """A call past the run threshold (T=4096, 128 adapters, d_out=17408): the
-    two-launch apply from ids, and the standalone shrink + expand from a
-    grouping, both bit for bit on exact integer data."""
+@pytest.mark.parametrize("dtype,d_out", [("bf16", 17408), ("fp32", 17408), ("bf16", 17416), ("fp32", 17412)])
+def test_expand_runs_integer_exact(dtype, d_out):
+    """A call past the run threshold (T=4096, 128 adapters, d_out about 17 K):
+    the two-launch apply from ids, and the standalone shrink + expand from a
+    grouping, both bit for bit on exact integer data.  d_out = 17408 fills 136
+    feature blocks, 68 full runs; 17416 and 17412 add a 137th block of 8 or 4
+    features, alone in the last run."""
     dev = device()
-    T, n, d_in, d_out = 4096, 128, 32, 17408
+    T, n, d_in = 4096, 128, 32
     assert (T + 15 * n) // 16 * ((d_out + 127) // 128) >= RUN_MIN_ITEMS
     ranks = [1 + (a * 5) % 16 for a in range(n)] if dtype == "bf16" else [1 + (a * 3) % 4 for a in range(n)]
     wl = make_random_workload(99, T, n, d_in, d_out, ranks, dtype=dtype, integer=True)
