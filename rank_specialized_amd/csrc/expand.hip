@@ -122,10 +122,13 @@ __device__ __forceinline__ void expand_run(const ExpandArgs& p, const TileEntry*
       }
     }
   };
-  // First block's y rows and B rows, then the H chunks (read once for the
-  // whole run).
+  // First block's y rows, B rows, then the H chunks (read once for the
+  // whole run).  One block per wave issues its y rows first (the longest
+  // wait); a run issues them after B and h instead, so that its first
+  // products need not wait for them (prefill's expand 122.4 -> 119.0 us; one
+  // block per wave was slower that way).
   uint4 ya[4][YV], yb[4][YV];
-  load_y(feat(0), ya);
+  if constexpr (RUN == 1) load_y(feat(0), ya);
   // bf16 ranks above 32 take two K chunks.  The second chunk's B rows are
   // loaded after the first chunk's products, into the same registers: the
   // kernel then fits the registers of 4 waves per SIMD, for one more (mostly
@@ -180,6 +183,7 @@ __device__ __forceinline__ void expand_run(const ExpandArgs& p, const TileEntry*
     }
     hc[q].set(f);
   }
+  if constexpr (RUN > 1) load_y(feat(0), ya);
   // The run: block k's products and stores, with block k + 1's y rows
   // issued before block k is waited for (its B rows first: waits are in
   // issue order, so the next block's y loads must come after what block k
