@@ -9,6 +9,7 @@ sources define (float64 unless stated, Python loops over tokens):
 
 * ``segment_ref``  - stable grouping of tokens by adapter id
 * ``shrink_ref``   - h = A_a x per token
+* ``shrink_error_bound`` - the float32 accumulation bound of h (gamma_n form)
 * ``apply_ref``    - y = y0 + s_a B_a (A_a x) per token
 * ``brute_force``  - the same in exact rational arithmetic, two association
                      orders, for tiny inputs
@@ -34,5 +35,5 @@ from .lora_ref import (  # noqa: F401
     shrink_error_bound,
 )
 from .jd_ref import jd_apply_ref, jd_brute_force  # noqa: F401,E402
-from .rank_ref import captured_energy_ref, spectral_ranks_ref, uniform_ranks_ref  # noqa: F401,E402
+from .rank_ref import spectral_ranks_ref, uniform_ranks_ref  # noqa: F401,E402
 from .rsvd_ref import retained_factors_ref, rsvd_ref, tall_skinny_r_ref  # noqa: F401,E402

@@ -90,7 +90,21 @@ def shrink_ref(x, ids, A_list) -> List[np.ndarray]:
 
 
 def shrink_error_bound(x, ids, A_list, unit_roundoff: float = 2.0 ** -24) -> List[np.ndarray]:
-    """Standard float32 dot-product bound per entry: d_in * u * sum_k |A_jk x_k|."""
+    """Largest error of h = A_a x when it is accumulated in float32.
+
+    [CtS] section 13.4 keeps h in a float32 buffer.  Each of the d_in
+    products and d_in - 1 additions rounds at most once, with relative error
+    at most the unit roundoff u = 2^-24 (round to nearest; products of bf16
+    values are exact, so there only the additions round).  For any order of
+    the additions the textbook dot-product bound (Higham, "Accuracy and
+    Stability of Numerical Algorithms", 2nd ed., section 3.1) gives
+
+        |h_float32[j] - h[j]|  <=  gamma_n * sum_k |A_a[j, k] x[k]|,
+        gamma_n = n u / (1 - n u),   n = d_in,
+
+    whose first-order term is d_in * u * sum_k |A_a[j, k] x[k]|.  Returns one
+    array of r_a bounds per token (empty for tokens without an adapter).
+    """
     x64 = np.abs(_as64(x))
     n = len(A_list)
     out = []
@@ -100,7 +114,8 @@ def shrink_error_bound(x, ids, A_list, unit_roundoff: float = 2.0 ** -24) -> Lis
             out.append(np.zeros(0))
             continue
         Aa = np.abs(_as64(A_list[a]))
-        out.append(Aa.shape[1] * unit_roundoff * (Aa @ x64[t]))
+        nu = Aa.shape[1] * unit_roundoff
+        out.append(nu / (1.0 - nu) * (Aa @ x64[t]))
     return out
 
 

@@ -54,8 +54,3 @@ def spectral_ranks_ref(r_orig: Sequence[int], sigmas: Sequence[Sequence[float]],
         r[best] += 1
         left -= 1
     return r
-
-
-def captured_energy_ref(ranks: Sequence[int], sigmas: Sequence[Sequence[float]]) -> float:
-    """sum over units of sigma_1^2 + ... + sigma_r^2: the energy kept."""
-    return float(sum(sum(float(s) ** 2 for s in sigmas[u][: int(ranks[u])]) for u in range(len(ranks))))

@@ -211,6 +211,131 @@ def pin_segment_invariants(segment_fn):
 SEGMENT_PINS = (pin_segment_worked_example, pin_segment_vs_stable_argsort, pin_segment_invariants)
 
 
+# ------------------------------------------------- float32 bound of the shrink
+# The intermediate h = A_a x is accumulated in float32 (Compress then Serve
+# section 13.4: a float32 buffer).  shrink_error_bound(x, ids, A_list) gives,
+# per token and retained rank, the largest |h_float32 - h_exact| that any
+# summation order may produce.  The pins below simulate float32 summation in
+# several orders (numpy float32 arithmetic, one rounding per addition) on
+# inputs chosen to make rounding errors large, and compare with the exact
+# sum (bf16 x bf16 products are exact in float64; math.fsum rounds their sum
+# once).  They are checked against what rounding actually does, not against
+# the bound's formula.
+
+_U32 = 2.0 ** -24  # float32 unit roundoff (round to nearest)
+
+
+def _bf16_exact(v):
+    """Round float64 values to the nearest bfloat16 (ties to even) by bit
+    manipulation of their float32 image; the inputs below are chosen exact."""
+    f = np.asarray(v, np.float32)
+    b = f.view(np.uint32).astype(np.uint64)
+    b = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16) << 16
+    return b.astype(np.uint32).view(np.float32)
+
+
+def _sum32(p, order):
+    """float32 sum of the last axis of p (products, exact in float32) in a
+    given order: 'fwd', 'rev', 'pairwise' (recursive halving) or 'blocked'
+    (64-term blocks summed in turn, then the block sums in turn)."""
+    p = np.asarray(p, np.float32)
+    if order == "rev":
+        p = p[..., ::-1]
+    if order in ("fwd", "rev"):
+        s = np.zeros(p.shape[:-1], np.float32)
+        for k in range(p.shape[-1]):
+            s = np.float32(s + p[..., k])
+        return s
+    if order == "pairwise":
+        while p.shape[-1] > 1:
+            if p.shape[-1] % 2:
+                p = np.concatenate([p, np.zeros(p.shape[:-1] + (1,), np.float32)], axis=-1)
+            p = (p[..., 0::2] + p[..., 1::2]).astype(np.float32)
+        return p[..., 0]
+    if order == "blocked":
+        n = p.shape[-1]
+        blocks = [_sum32(p[..., i:i + 64], "fwd") for i in range(0, n, 64)]
+        return _sum32(np.stack(blocks, axis=-1), "fwd")
+    raise ValueError(order)
+
+
+def _bound_cases(d=18944):
+    """Tokens paired with one-row adapters (token t uses adapter t), bf16-exact:
+      0 stagnation: 2^24 followed by d-1 ones; each float32 addition of 1 to
+        2^24 is a tie that rounds back to 2^24, so sequential summation loses
+        every one of them (the error reaches (d-1)/d of the first-order bound);
+      1 cancellation: 2^24 + 1 - 2^24 (the exact sum 1 is lost to rounding);
+      2 equal terms (1 + 2^-7)^2, whose rounding errors all have one sign;
+      3 mixed magnitudes: N(0,1) values scaled by 2^e, e uniform in [-20, 20];
+      4 N(0,1) bf16 values."""
+    rng = np.random.default_rng(23)
+    X = np.zeros((5, d), np.float64)
+    A = np.zeros((5, d), np.float64)
+    X[0, 0], A[0, 0] = 2.0 ** 12, 2.0 ** 12
+    X[0, 1:], A[0, 1:] = 1.0, 1.0
+    X[1, :3] = [2.0 ** 12, 1.0, 2.0 ** 12]
+    A[1, :3] = [2.0 ** 12, 1.0, -(2.0 ** 12)]
+    X[2, :], A[2, :] = 1.0 + 2.0 ** -7, 1.0 + 2.0 ** -7
+    X[3] = rng.normal(size=d) * 2.0 ** rng.integers(-20, 21, size=d)
+    A[3] = rng.normal(size=d) * 2.0 ** rng.integers(-20, 21, size=d)
+    X[4], A[4] = rng.normal(size=d), rng.normal(size=d)
+    X, A = _bf16_exact(X), _bf16_exact(A)
+    return X, [A[t:t + 1] for t in range(5)], np.arange(5, dtype=np.int32)
+
+
+def _exact_dots(X, A_list, ids):
+    import math
+    out = []
+    for t, a in enumerate(ids):
+        p = np.asarray(A_list[a], np.float64) * np.asarray(X[t], np.float64)  # exact products
+        out.append(np.array([math.fsum(row) for row in p]))
+    return out
+
+
+def pin_shrink_bound_sound(bound_fn):
+    """No float32 summation order exceeds the bound on the adversarial cases
+    (any order the GPU may take: sequential either way, pairwise, blocked)."""
+    X, A_list, ids = _bound_cases()
+    bound = bound_fn(X, ids, A_list)
+    exact = _exact_dots(X, A_list, ids)
+    for order in ("fwd", "rev", "pairwise", "blocked"):
+        for t, a in enumerate(ids):
+            p = (np.asarray(A_list[a], np.float32) * np.asarray(X[t], np.float32))
+            h32 = _sum32(p, order).astype(np.float64)
+            err = np.abs(h32 - exact[t])
+            assert np.all(err <= np.asarray(bound[t])), (order, t, err, bound[t])
+
+
+def pin_shrink_bound_attained(bound_fn):
+    """The bound is nearly reached: sequential summation of the stagnation
+    case loses d - 1 of a first-order bound of d u (2^24 + d - 1)."""
+    X, A_list, ids = _bound_cases()
+    bound = bound_fn(X, ids, A_list)
+    exact = _exact_dots(X, A_list, ids)
+    p = np.asarray(A_list[0], np.float32) * np.asarray(X[0], np.float32)
+    err = abs(float(_sum32(p, "fwd")[0]) - float(exact[0][0]))
+    assert err == X.shape[1] - 1, err
+    assert err >= 0.99 * float(np.asarray(bound[0])[0]), (err, bound[0])
+
+
+def pin_shrink_bound_shape(bound_fn):
+    """One non-negative value per retained rank for tokens with an adapter,
+    none for the others; zero for a zero input."""
+    wl = make_random_workload(6, 12, 3, 16, 4, [2, 0, 3], dtype="bf16", id_mode="uniform", invalid_frac=0.3)
+    m = wl.module
+    b = bound_fn(wl.x, wl.ids, m.A)
+    for t, a in enumerate(wl.ids):
+        if 0 <= a < m.n:
+            assert np.asarray(b[t]).shape == (m.ranks[a],) and np.all(np.asarray(b[t]) >= 0)
+        else:
+            assert np.asarray(b[t]).size == 0
+    z = bound_fn(np.zeros_like(wl.x), wl.ids, m.A)
+    assert all(np.all(np.asarray(v) == 0) for v in z)
+
+
+SHRINK_BOUND_PINS = (pin_shrink_bound_sound, pin_shrink_bound_attained, pin_shrink_bound_shape)
+
+
 # ------------------------------------------------------- shared-basis pins
 # The shared-basis (joint-diagonalization) apply of "Compress then Serve"
 # sections 3.1-3.2 and 11: y += s_i U_j Sigma_i V_j^T x for adapter i in

@@ -53,6 +53,11 @@ def test_shrink_matches_per_segment_product():
         assert h[t].size == 0
 
 
+@pytest.mark.parametrize("pin", P.SHRINK_BOUND_PINS, ids=lambda f: f.__name__)
+def test_shrink_bound_pin(pin):
+    pin(shrink_error_bound)
+
+
 def test_bf16_round_known_values():
     """Hand-checked roundings: ties go to the even neighbour."""
     one = 1.0

@@ -3,7 +3,7 @@ that the pins catch every one of them."""
 import numpy as np
 import pytest
 
-from oracle import apply_ref, segment_ref
+from oracle import apply_ref, segment_ref, shrink_error_bound
 
 import oracle_pins as P
 
@@ -246,3 +246,49 @@ def test_rsvd_mutant_is_caught(kind):
         except (AssertionError, ValueError):
             caught.append(pin.__name__)
     assert caught, f"r-SVD mutant {kind} passed every pin"
+
+
+def _bound_mutant(kind):
+    """Copies of the float32 bound of h with a plausible mistake planted."""
+    def fn(x, ids, A_list):
+        x64 = np.abs(np.asarray(x, np.float64))
+        out = []
+        for t in range(x64.shape[0]):
+            a = int(ids[t])
+            if not 0 <= a < len(A_list):
+                out.append(np.zeros(0))
+                continue
+            A = np.asarray(A_list[a], np.float64)
+            d = A.shape[1]
+            u = 2.0 ** -16 if kind == "unit_2^-16" else 2.0 ** -24
+            n = {"no_d_in": 1, "sqrt_d_in": np.sqrt(d), "d_in_squared": d * d}.get(kind, d)
+            if kind == "abs_of_sum":
+                s = np.abs(A @ np.asarray(x, np.float64)[t])  # |sum| instead of sum of |.|
+            else:
+                s = np.abs(A) @ x64[t]
+            out.append(n * u / (1 - min(n * u, 0.5)) * s)
+        return out
+    return fn
+
+
+BOUND_MUTANTS = ["unit_2^-16", "no_d_in", "sqrt_d_in", "d_in_squared", "abs_of_sum"]
+
+
+@pytest.mark.parametrize("kind", BOUND_MUTANTS)
+def test_bound_mutant_is_caught(kind):
+    fn = _bound_mutant(kind)
+    caught = []
+    for pin in P.SHRINK_BOUND_PINS:
+        try:
+            pin(fn)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"mutant {kind} passed every pin"
+
+
+def test_bound_unmutated_copy_passes():
+    fn = _bound_mutant("none")
+    for pin in P.SHRINK_BOUND_PINS:
+        pin(fn)
+    for pin in P.SHRINK_BOUND_PINS:
+        pin(shrink_error_bound)
