@@ -5,6 +5,7 @@
 #include <cstring>
 #include <vector>
 
+#include "host_util.h"
 #include "kernels.h"
 #include "validate.h"
 
@@ -119,8 +120,8 @@ int lora_segment(const int32_t* ids, int T, int n, int32_t* seg_off, int32_t* pe
                  void* stream) {
   int st = check_segment_args(ids, T, n, seg_off, perm);
   if (st != LORA_OK) return st;
-  int max_lds = 0;
-  hipError_t e = hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, 0);
+  int max_lds = 0;  // of the current device
+  hipError_t e = device_attribute<hipDeviceAttributeMaxSharedMemoryPerBlock>(&max_lds);
   if (e != hipSuccess) return hip_fail(e);
   if (segment_lds_bytes(T, n) + segment_static_lds_bytes() > (size_t)max_lds) return LORA_ERR_UNSUPPORTED;
   e = launch_segment(ids, T, n, seg_off, perm, n_invalid, reinterpret_cast<hipStream_t>(stream));

@@ -149,16 +149,18 @@ __device__ __forceinline__ void expand_run(const ExpandArgs& p, const TileEntry*
     for (int e = 0; e < V; ++e) f[e] = 0.f;
     if (hv && j0 < r) {
       const float* src = p.hsrc + (int64_t)hrow * p.ldh + hoff + j0;
-      if (kPart && (hoff & 3)) {  // a slice's columns off 16-byte boundaries (multi-slice apply)
+      // A slice's columns (multi-slice apply) may start off a 16-byte
+      // boundary, or end so that a whole vector would run past the row of
+      // partial sums: those are read column by column, only below the rank.
+      const bool whole = (hoff & 3) == 0 && hoff + j0 + V <= p.ldh;
+      if (kPart && !whole) {
 #pragma unroll
-        for (int e = 0; e < V; ++e) f[e] = src[e];
+        for (int e = 0; e < V; ++e) f[e] = j0 + e < r ? src[e] : 0.f;
 #pragma unroll 4
         for (int k = 1; k < S; ++k)
 #pragma unroll
-          for (int e = 0; e < V; ++e) f[e] += src[(int64_t)k * p.hstride + e];
-#pragma unroll
-        for (int e = 0; e < V; ++e)
-          if (j0 + e >= r) f[e] = 0.f;
+          for (int e = 0; e < V; ++e)
+            if (j0 + e < r) f[e] += src[(int64_t)k * p.hstride + e];
       } else if (kPart) {
 #pragma unroll
         for (int v = 0; v < V / 4; ++v) {

@@ -18,6 +18,7 @@
 //     earlier waves first.
 //  3. perm = low bits of the sorted keys; seg_off[b] = lower_bound(b).
 #include "device_common.h"
+#include "host_util.h"
 #include "kernels.h"
 
 namespace lora {
@@ -157,13 +158,9 @@ static hipError_t launch_segment_w(const int32_t* ids, int T, int n, int32_t* se
   const int passes = (gbits + kDigitBits - 1) / kDigitBits;
   const int cap = T > n + 2 ? T : n + 2;
   const size_t lds = segment_lds_bytes(T, n);
-  static size_t raised = 48 * 1024;
-  if (lds > raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(segment_kernel<W>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    raised = lds;
-  }
+  static DynLdsLimit lim;
+  hipError_t e = ensure_dynamic_lds(lim, reinterpret_cast<const void*>(segment_kernel<W>), lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(segment_kernel<W>, dim3(1), dim3(W * 64), lds, stream, ids, T, n, tbits, passes, cap,
                      seg_off, perm, n_invalid);
   return hipGetLastError();

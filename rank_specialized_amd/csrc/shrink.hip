@@ -33,6 +33,7 @@
 // Rank specialization: NG = ceil(r_a / 16) row groups is a template
 // parameter; rows j >= r_a and tokens >= m are never loaded.
 #include "device_common.h"
+#include "host_util.h"
 #include "kernels.h"
 #include "tile_ops.h"
 
@@ -496,18 +497,6 @@ plan_kernel(const int32_t* __restrict__ seg_off, const int32_t* __restrict__ per
 }
 
 // --------------------------------------------------------------- host
-static int cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cached[dev] = v;
-  }
-  return cached[dev];
-}
-
 static int ng_of(int r_max) { return r_max <= 16 ? 1 : (r_max + 15) / 16; }
 
 size_t shrink_lds_bytes(int T, int n, int r_max, bool with_ids) {
@@ -519,13 +508,9 @@ size_t shrink_lds_bytes(int T, int n, int r_max, bool with_ids) {
 template <typename E, bool kIds, int APT>
 static hipError_t launch_shrink_t(const ShrinkArgs& a, int grid, size_t lds, hipStream_t stream) {
   auto fn = shrink_kernel<E, kIds, APT>;
-  static size_t raised = 48 * 1024;  // dynamic LDS above this needs the attribute
-  if (lds > raised) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    raised = lds;
-  }
+  static DynLdsLimit lim;
+  hipError_t e = ensure_dynamic_lds(lim, reinterpret_cast<const void*>(fn), lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fn, dim3(grid), dim3(kShrinkThreads), lds, stream, a);
   return hipGetLastError();
 }
@@ -605,13 +590,9 @@ hipError_t launch_plan(const lora_store& s, const int32_t* seg_off, const int32_
     hipLaunchKernelGGL(plan_kernel<4>, dim3(1), dim3(1024), lds, stream, seg_off, perm, T, s.n, s.row_off,
                        s.rank, s.scale, (int)max_sub, plan);
   } else {
-    static size_t raised = 48 * 1024;
-    if (lds > raised) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(plan_kernel<16>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      raised = lds;
-    }
+    static DynLdsLimit lim;
+    hipError_t e = ensure_dynamic_lds(lim, reinterpret_cast<const void*>(plan_kernel<16>), lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(plan_kernel<16>, dim3(1), dim3(1024), lds, stream, seg_off, perm, T, s.n, s.row_off,
                        s.rank, s.scale, (int)max_sub, plan);
   }

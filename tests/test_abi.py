@@ -189,6 +189,57 @@ def test_apply_rejects_before_launch(lib):
     assert call(T=0, x=None, y=None, ws=None, wsb=0) == 0
 
 
+def test_concurrent_validation_from_threads(lib):
+    """Eight host threads run the apply's argument checks at once, each with
+    its own arguments and expected status (ctypes releases the GIL during the
+    call, so the calls overlap).  The checks keep no shared mutable state, so
+    every call returns its own status.  Without a GPU, a call that reaches
+    the HIP runtime fails there; its error code is kept per thread, so only
+    the failing thread sees it."""
+    import threading
+
+    st = _store()
+    f = lib.lora_apply_batched
+    big = 1 << 30
+    cases = [dict(s=None, want=1), dict(T=-3, want=1), dict(ws=FAKE + 8, want=2),
+             dict(T=L.LORA_SEGMENT_MAX_T + 1, want=2), dict(ids=None, want=1), dict(T=0, want=0),
+             dict(wsb=16, want=1), dict(ldy=16, want=1)]
+    errors = []
+
+    def worker(c):
+        kw = dict(T=16, ids=FAKE, ws=FAKE, wsb=big, x=FAKE, y=FAKE, ldx=64, ldy=32, s=st)
+        kw.update({k: v for k, v in c.items() if k != "want"})
+        s = kw["s"]
+        for _ in range(3000):
+            got = f(C.byref(s) if s is not None else None, kw["x"], kw["ldx"], kw["y"], kw["ldy"], kw["T"],
+                    kw["ids"], None, None, kw["ws"], kw["wsb"], None)
+            if got != c["want"]:
+                errors.append((c, got))
+                return
+        if lib.lora_last_hip_error() != 0:
+            errors.append((c, "hip error seen by a thread that made no HIP call"))
+
+    hip_seen = {}
+
+    def hip_worker():
+        # Reaches the HIP runtime (the current device's LDS limit); only where
+        # no GPU is present, so nothing is ever launched.
+        got = lib.lora_segment(FAKE, 16, 4, FAKE, FAKE, None, None)
+        hip_seen["status"], hip_seen["err"] = got, lib.lora_last_hip_error()
+
+    threads = [threading.Thread(target=worker, args=(c,)) for c in cases]
+    no_gpu = not os.path.exists("/dev/kfd")
+    if no_gpu:
+        threads.append(threading.Thread(target=hip_worker))
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    if no_gpu:
+        assert hip_seen["status"] == 3 and hip_seen["err"] != 0, hip_seen
+
+
 def _layout_bytes(T, n, d_in, r_max, e):
     """The workspace layout restated: plan (256-byte header + one 128-byte
     entry per possible sub-tile of <= 16 tokens), float32 partial sums for

@@ -37,6 +37,11 @@ CASES = {
     "high_rank": dict(seed=4, T=200, n=3, d_in=256, d_outs=(128, 64),
                       ranks=([33, 20, 1], [31, 44, 63])),
     "one_slice": dict(seed=5, T=90, n=6, d_in=64, d_outs=(48,), ranks=([1, 2, 3, 4, 5, 6],)),
+    # Every adapter at rank 4 in both slices: a stacked rank of 8, so the
+    # partial-sum rows are 8 floats wide and slice 1 starts at column 4; its
+    # sub-tiles (~67 tokens per adapter) take the matrix path, whose h chunk
+    # must not read past the row.
+    "rank4_pairs": dict(seed=6, T=200, n=3, d_in=64, d_outs=(64, 32), ranks=([4, 4, 4], [4, 4, 4])),
 }
 
 
@@ -86,7 +91,7 @@ def test_multi_parity(name, dtype):
     _run(name, dtype)
 
 
-@pytest.mark.parametrize("name", ["qkv_small", "odd_offsets_matrix", "high_rank"])
+@pytest.mark.parametrize("name", ["qkv_small", "odd_offsets_matrix", "high_rank", "rank4_pairs"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_multi_integer_exact(name, dtype):
     _run(name, dtype, integer=True)
