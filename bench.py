@@ -1,19 +1,33 @@
 #!/usr/bin/env python3
 """Benchmark of the batched, rank-specialized LoRA-delta apply on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5S]
 
-A step is one pass of the whole hot path over one batch: token grouping,
-shrink and expand, i.e. one lora_apply_batched call with adapter ids (one
-fused kernel for decode-sized calls, else two: the shrink, which also groups
-the tokens, and the expand), on inputs already resident in HBM.  Steps rotate through independent copies of
-(store, x, y) whose total size exceeds the 256 MB last-level cache, so every
-step reads its factors and activations from HBM (cold-HBM timing).
+Default workload: the fleet decode step (5S): 28 layers x 7 projections of a
+Qwen2-7B-like model (hidden 3584, k/v 512, MLP 18944), bf16, 1024 adapters
+whose retained ranks vary 4..16 per module, T = 4096 decode tokens with
+Zipf(1.1) adapter popularity.  A step is one pass of the whole hot path over
+that batch: one token grouping (lora_segment) and the 196 module applies
+(lora_apply_batched on that grouping: shrink, then expand), inputs resident
+in HBM.  A step streams ~50 GB, 200 times the 256 MB last-level cache, so it
+reads its factors and activations from HBM by construction.
+
+`--config 1|2|3|4` times one lora_apply_batched call with ids of the smaller
+workloads instead; there the timed steps rotate through distinct copies of
+(store, x, y) and every timed segment of steps starts after a 2 GiB cache
+flush (outside the timed events), so each step reads from HBM too.
+
+Timing: W untimed warm-up steps, then exactly K timed steps, bracketed by a
+device synchronization on both sides.  The K steps are replays of HIP
+graphs in at least 5 segments (one step per replay for the fleet), each
+bracketed by HIP events on the launch stream: ms_per_step is their total
+over K, and the line also carries the median, p10 and p90 per step.
 
 Prints ONE JSON line: tokens/s of the rank-specialized apply, achieved
 algorithmic HBM GB/s and fraction of the 8 TB/s peak, the roofline of the
-dominant kernel (HIP events on the launch stream), the same kernels on
-rank-padded stores, and the CPU oracle timed on a bounded sample.
+dominant kernel (HIP events on its launch stream), the same kernels on
+rank-padded stores, and the CPU oracle timed on a bounded sample (one core
+and all host cores), run before the GPU is touched.
 """
 from __future__ import annotations
 
@@ -21,6 +35,7 @@ import argparse
 import hashlib
 import json
 import math
+import multiprocessing
 import os
 import platform
 import sys
@@ -33,9 +48,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "LoRA-delta tokens/s and achieved HBM GB/s (% of ~8 TB/s peak), 1 MI355X"
 PEAK_GBPS = 8000.0
-COLD_BYTES = 2.0e9  # rotation set size: well past the 256 MB Infinity Cache
-# Sources each measured kernel family is built from: a counter record is used
-# only while the sources of its family are unchanged.
+FLUSH_BYTES = 2 << 30  # cache flush between timed segments: 8x the 256 MB Infinity Cache
+MIN_SEGMENTS = 5       # the K timed steps are split into at least this many timed replays
 # Sources of each kernel family: a traffic record holds only while its own
 # family's sources are unchanged.
 APPLY_SOURCES = ["shrink.hip", "expand.hip", "tile_ops.h", "device_common.h", "plan.h"]
@@ -53,6 +67,8 @@ def sources_of(kernel: str):
     if kernel.startswith("jd_"):
         return JD_SOURCES
     return APPLY_SOURCES
+
+
 PEAK_FP64_TFLOPS = 78.6  # 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2.4 GHz
 
 WORKLOAD_NAMES = {
@@ -79,16 +95,18 @@ WORKLOAD_NAMES = {
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="2", choices=sorted(WORKLOAD_NAMES))
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="5S", choices=sorted(WORKLOAD_NAMES))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-padded", action="store_true")
     p.add_argument("--no-multi", action="store_true", help="fleet: skip the multi-slice (q/k/v, gate/up) step")
+    p.add_argument("--no-5u", action="store_true", help="fleet 5S: skip the uniform-rank (5U) step")
+    p.add_argument("--no-kernels", action="store_true", help="skip the per-kernel timing passes")
     p.add_argument("--streams", type=int, default=3,
                    help="fleet: run the modules of one stage (q/k/v; gate/up) on up to this many streams")
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
-    p.add_argument("--warm", action="store_true", help="no rotation (cache-resident timing)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="seconds per CPU-oracle leg")
+    p.add_argument("--warm", action="store_true", help="no rotation and no flush (cache-resident timing)")
     p.add_argument("--no-graph", action="store_true", help="time eager launches only (counter runs)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run one elementwise copy of 256 MiB (reads and writes 256 MiB), the "
@@ -130,129 +148,222 @@ def algorithmic_bytes(ids: np.ndarray, ranks: np.ndarray, n: int, d_in: int, d_o
             "flops": 2 * sum_r * (d_in + d_out), "touched": int(len(touched)), "R_touched": R_touched}
 
 
-# ------------------------------------------------------------------ workload
-def build_workload(key: str):
-    from workloads import make_config
-    return make_config(key, with_y0=True)
+# ------------------------------------------------------------------ bytes
+def algorithmic_bytes(ids: np.ndarray, ranks: np.ndarray, n: int, d_in: int, d_out: int, e: int):
+    """Bytes the method itself must move per call (nothing for untouched
+    adapters or padding): the ids, each used adapter's factors once, each
+    token's x row once, each token's y row read and written once, and the
+    float32 intermediate h (sum of the tokens' ranks) written once and read
+    once.  The shrink kernel owns the ids, A, x and the h write; the expand
+    the h read, B and y."""
+    valid = (ids >= 0) & (ids < n)
+    tok_r = np.where(valid, ranks[np.clip(ids, 0, n - 1)], 0)
+    active = valid & (tok_r > 0)
+    touched = np.unique(ids[active])
+    R_touched = int(ranks[touched].sum())
+    Tv = int(active.sum())
+    sum_r = int(tok_r.sum())
+    T = len(ids)
+    shrink = 4 * T + R_touched * d_in * e + Tv * d_in * e + 4 * sum_r
+    expand = R_touched * d_out * e + 2 * Tv * d_out * e + 4 * sum_r
+    return {"shrink": shrink, "expand": expand, "total": shrink + expand,
+            "flops": 2 * sum_r * (d_in + d_out), "touched": int(len(touched)), "R_touched": R_touched}
 
 
-class Copy:
-    def __init__(self, store, x, y):
-        self.store, self.x, self.y = store, x, y
+def fleet_algorithmic(key: str, T: int = 4096, n: int = 1024):
+    """Per-module algorithmic bytes of the fleet step (module order), and the
+    segmentation's own bytes (ids read, perm written, seg_off written)."""
+    from workloads import fleet_ids, fleet_module_shapes, fleet_ranks
+    ids = fleet_ids(T, n)
+    ranks = fleet_ranks(key, n)
+    per_mod = [algorithmic_bytes(ids, ranks[l, p], n, d_in, d_out, 2)
+               for (l, p, _nm, d_in, d_out, _k) in fleet_module_shapes()]
+    return ids, per_mod, 4 * (2 * T + n + 2)
 
 
-def make_copies(rs, torch, wl, dev, pad_to: int, cold: bool):
-    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-    A = [torch.from_numpy(a).to(dev).to(dt) for a in wl.module.A]
-    B = [torch.from_numpy(b).to(dev).to(dt) for b in wl.module.B]
-    store = rs.lora_pack_retained(A, B, wl.module.scales, pad_to=pad_to)
-    del A, B
-    x = torch.from_numpy(wl.x).to(dev).to(dt)
-    y = torch.from_numpy(wl.y0).to(dev).to(dt)
-    per_copy = store.A_pack.numel() + store.B_pack.numel() + x.numel() * x.element_size() \
-        + y.numel() * y.element_size()
-    n_copies = 1 if not cold else int(min(512, max(1, math.ceil(COLD_BYTES / per_copy))))
-    copies = [Copy(store, x, y)]
-    for _ in range(n_copies - 1):
-        copies.append(Copy(store.clone(), x.clone(), y.clone()))
-    return copies, per_copy
+# ------------------------------------------------------------------ CPU oracle
+# The oracle as it stands, timed on the host on a bounded sample of the same
+# workload: one core (BLAS pinned to one thread), then every core the process
+# may use (capped at 16, the host share of one GPU), one forked worker per
+# core on its own slice of tokens.  It runs before anything touches the GPU,
+# so the forked workers inherit no GPU state.
+_CPU_JOB = {}
 
 
-def _lora_step(rs, ids, ws):
-    return lambda c: rs.lora_apply_batched(c.store, c.x, c.y, ids=ids, ws=ws)
+def _blas_one_thread():
+    try:
+        from threadpoolctl import threadpool_limits
+        return threadpool_limits(1)
+    except Exception:  # pragma: no cover
+        return None
 
 
-def time_apply(rs, torch, copies, ids, ws, steps, warmup, step=None):
-    """Events bracket exactly `steps` eager calls; returns ms per call."""
-    step = step or _lora_step(rs, ids, ws)
-    for k in range(warmup):
+def _cpu_leg(i: int):
+    """Worker i of a leg: apply_ref over its slice of the sample until the
+    leg's time is up; returns (tokens, seconds)."""
+    from oracle import apply_ref
+    job = _CPU_JOB
+    lim = _blas_one_thread()
+    lo = (i * job["per"]) % max(1, job["T"] - job["per"] + 1)
+    x, ids = job["x"][lo:lo + job["per"]], job["ids"][lo:lo + job["per"]]
+    done, t0 = 0, time.perf_counter()
+    while True:
+        apply_ref(x, ids, job["A"], job["B"], job["scales"])
+        done += len(ids)
+        el = time.perf_counter() - t0
+        if el >= job["seconds"]:
+            break
+    if lim is not None:
+        lim.unregister()
+    return done, el
+
+
+def host_cores() -> int:
+    try:
+        c = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        c = os.cpu_count() or 1
+    return max(1, min(16, c))
+
+
+def cpu_oracle(x, ids, A, B, scales, seconds: float, per: int, scale_to_step: int, what: str):
+    """tokens/s of the oracle on a bounded sample (per tokens per worker),
+    divided by scale_to_step (the modules of a fleet step; 1 otherwise)."""
+    _CPU_JOB.update(x=x, ids=ids, A=A, B=B, scales=scales, seconds=seconds, per=per, T=len(ids))
+    d1, e1 = _cpu_leg(0)
+    one = d1 / e1 / scale_to_step
+    cores = host_cores()
+    with multiprocessing.get_context("fork").Pool(cores) as pool:
+        res = pool.map(_cpu_leg, range(cores))
+    all_rate = sum(d for d, _ in res) / max(e for _, e in res) / scale_to_step
+    cpu = platform.processor() or platform.machine()
+    unit_note = (f"; token-module rate divided by the {scale_to_step} modules of a step"
+                 if scale_to_step > 1 else "")
+    return {"value": round(all_rate, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{what}: float64 per-token loop (oracle apply_ref), {cores} forked workers of "
+                      f"{per} tokens each (distinct slices), {seconds:.0f} s per leg, BLAS pinned to 1 thread "
+                      f"per worker, on {cpu} ({os.cpu_count()} logical CPUs visible){unit_note}",
+            "one_core": {"value": round(one, 3), "unit": "tokens/s", "cores": 1,
+                         "sample": f"worker 0 alone, {d1} tokens in {e1:.1f} s"}}
+
+
+# ------------------------------------------------------------------ timing
+def split_steps(K: int):
+    """K timed steps as R = min(K, MIN_SEGMENTS) segments of consecutive
+    steps (the last takes the remainder)."""
+    R = max(1, min(K, MIN_SEGMENTS))
+    g = K // R
+    return [g] * (R - 1) + [K - g * (R - 1)]
+
+
+def percentiles(per_step_ms):
+    v = np.asarray(per_step_ms, dtype=np.float64)
+    return {"median_ms": round(float(np.median(v)), 6), "p10_ms": round(float(np.percentile(v, 10)), 6),
+            "p90_ms": round(float(np.percentile(v, 90)), 6), "samples": int(len(v))}
+
+
+class Flush:
+    """A 2 GiB buffer read and written between timed segments (outside the
+    timed events): afterwards neither the L2s nor the 256 MB last-level cache
+    hold anything a step reads."""
+
+    def __init__(self, torch, dev, enabled: bool):
+        self.buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev) if enabled else None
+
+    def __call__(self):
+        if self.buf is not None:
+            self.buf.add_(1.0)
+
+
+def time_steps(torch, step, copies, K, W, flush, graph=True):
+    """Exactly K timed steps, as segments (split_steps) of consecutive steps
+    on distinct copies (step i of a segment uses copies[i]), each segment one
+    HIP-graph replay (or eager launches) bracketed by events on the launch
+    stream and preceded by a cache flush.  W untimed eager warm-up steps come
+    first.  Returns ms per step (total over K) and the per-segment
+    distribution of ms per step."""
+    lengths = split_steps(K)
+    assert len(copies) >= max(lengths)
+    for k in range(W):
         step(copies[k % len(copies)])
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    graphs = {}
+    if graph:
+        for L in sorted(set(lengths)):
+            side = torch.cuda.Stream()  # default priority
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for i in range(L):
+                    step(copies[i])
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(L):
+                    step(copies[i])
+            g.replay()  # untimed first replay
+            graphs[L] = g
+    torch.cuda.synchronize()
+    ev = []
     t0 = time.perf_counter()
-    e0.record()
-    for k in range(steps):
-        step(copies[(warmup + k) % len(copies)])
-    e1.record()
+    for L in lengths:
+        flush()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        if graph:
+            graphs[L].replay()
+        else:
+            for i in range(L):
+                step(copies[i])
+        e1.record()
+        ev.append((L, e0, e1))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return e0.elapsed_time(e1) / steps, wall
+    seg_ms = [e0.elapsed_time(e1) for _, e0, e1 in ev]
+    per_step = [t / L for (L, _, _), t in zip(ev, seg_ms)]
+    graphs.clear()
+    return {"ms_per_step": sum(seg_ms) / K, "dist": percentiles(per_step), "wall_s": wall,
+            "segments": lengths}
 
 
-def time_apply_graph(rs, torch, copies, ids, ws, steps, warmup, step=None):
-    """The same `steps` calls captured once in a HIP graph (a decode loop's
-    launches replayed without host work per kernel); events bracket one
-    replay of all of them.  Returns ms per call."""
-    step = step or _lora_step(rs, ids, ws)
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        for k in range(max(1, warmup)):
-            step(copies[k % len(copies)])
-    torch.cuda.current_stream().wait_stream(side)
+def time_replays(torch, step, K, W, graph=True):
+    """Exactly K timed steps of a self-contained step (the fleet: each step
+    streams ~50 GB, so no flush is needed): W eager warm-up steps, then one
+    step captured in a HIP graph and replayed K times, each replay bracketed
+    by events on the launch stream."""
+    for _ in range(max(1, W)):
+        step()
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for k in range(steps):
-            step(copies[(warmup + k) % len(copies)])
-    g.replay()  # untimed warm replay
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    del g
-    return e0.elapsed_time(e1) / steps, wall
-
-
-def time_kernels(rs, torch, copies, ids, ws, steps, warmup, graph=True):
-    """Average duration of each of the apply's two kernels, measured alone:
-    the same rotation of calls with only that kernel (lora_apply_batched_phases),
-    captured in a HIP graph; HIP events on the launch stream bracket one
-    replay of `steps` launches.  The expand replays read the plan and partial
-    sums the last shrink left in the workspace."""
-    out = {}
-    for name, phase in (("shrink", 1), ("expand", 2)):
+    g = None
+    if graph:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            for k in range(max(1, warmup)):
-                c = copies[k % len(copies)]
-                rs.lora_apply_batched(c.store, c.x, c.y, ids=ids, ws=ws)
+            step()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        def run():
-            for k in range(steps):
-                c = copies[k % len(copies)]
-                rs.lora_apply_batched_phases(c.store, c.x, c.y, phase, ids=ids, ws=ws)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        if graph:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                run()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    t0 = time.perf_counter()
+    evs[0].record()
+    for k in range(K):
+        if g is not None:
             g.replay()
-            torch.cuda.synchronize()
-            e0.record()
-            g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            del g
         else:
-            e0.record()
-            run()
-            e1.record()
-            torch.cuda.synchronize()
-        out[name] = {"avg_us": 1e3 * e0.elapsed_time(e1) / steps, "launches": steps,
-                     "timed_as": "one HIP-graph replay" if graph else "eager launches"}
-    return out
+            step()
+        evs[k + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [evs[k].elapsed_time(evs[k + 1]) for k in range(K)]
+    del g
+    return {"ms_per_step": evs[0].elapsed_time(evs[K]) / K, "dist": percentiles(per), "wall_s": wall}
 
 
+# ------------------------------------------------------------------ counters
 def traffic_for(workload: str, kernel: str, sources=None):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they
     were taken on the current sources of that kernel family."""
@@ -285,9 +396,11 @@ def read_pmc(run_dir: str, counter: str):
 
 
 def summarize_pmc(key: str, fetch_dir: str, write_dir: str):
-    """HBM bytes per launch of the shrink and expand kernels: FETCH_SIZE and
-    WRITE_SIZE (KiB per dispatch) averaged over the dispatches, each scaled by
-    what the same counter reads for an elementwise copy of 256 MiB."""
+    """HBM bytes per launch of the library's kernels: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) averaged over the dispatches, each scaled
+    by what the same counter reads for an elementwise copy of 256 MiB.  For
+    the fleet the algorithmic bytes are the mean over its 196 modules (every
+    pass of a run covers each module once)."""
     fetch, write = read_pmc(fetch_dir, "FETCH_SIZE"), read_pmc(write_dir, "WRITE_SIZE")
 
     def calib(d):
@@ -304,6 +417,9 @@ def summarize_pmc(key: str, fetch_dir: str, write_dir: str):
         keep = sum(rs.lora_ranks_uniform([c["r"]] * c["n"], 1.0 / 12.0, 4))  # the spectral budget, met exactly
         alg = rsvd_algorithmic(c["n"], c["r"], c["d_in"], c["d_out"], keep, 2)
         kernels = (("rsvd_gram", alg["gram_bytes"]), ("rsvd_write", alg["write_bytes"]))
+    elif key in ("5U", "5S"):
+        _, per_mod, _ = fleet_algorithmic(key)
+        kernels = tuple((k, float(np.mean([b[k] for b in per_mod]))) for k in ("shrink", "expand"))
     else:
         wl = build_workload(key)
         m = wl.module
@@ -320,7 +436,7 @@ def summarize_pmc(key: str, fetch_dir: str, write_dir: str):
         fb = float(np.mean(fk)) * 1024.0 / cf
         wb = float(np.mean(wk)) * 1024.0 / cw
         ent[kern] = {"hbm_bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb),
-                     "algorithmic_bytes": alg, "traffic_over_algorithmic": round((fb + wb) / alg, 3),
+                     "algorithmic_bytes": round(alg), "traffic_over_algorithmic": round((fb + wb) / alg, 3),
                      "dispatches": len(fk), "kernel_sources_sha": kernel_source_digest(sources_of(kern))}
     if not ent:
         raise SystemExit("no library kernel dispatches in the counter runs")
@@ -329,6 +445,130 @@ def summarize_pmc(key: str, fetch_dir: str, write_dir: str):
     with open(path, "w") as f:
         json.dump(rec, f, indent=1, sort_keys=True)
     print(json.dumps({f"config{key}": ent}))
+
+
+# ------------------------------------------------------------------ workloads 1-4
+def build_workload(key: str):
+    from workloads import make_config
+    return make_config(key, with_y0=True)
+
+
+class Copy:
+    def __init__(self, store, x, y):
+        self.store, self.x, self.y = store, x, y
+
+
+def make_copies(rs, torch, wl, dev, pad_to: int, n_copies: int):
+    """n_copies independent (store, x, y) triples of the workload."""
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    A = [torch.from_numpy(a).to(dev).to(dt) for a in wl.module.A]
+    B = [torch.from_numpy(b).to(dev).to(dt) for b in wl.module.B]
+    store = rs.lora_pack_retained(A, B, wl.module.scales, pad_to=pad_to)
+    del A, B
+    x = torch.from_numpy(wl.x).to(dev).to(dt)
+    y = torch.from_numpy(wl.y0).to(dev).to(dt)
+    copies = [Copy(store, x, y)]
+    for _ in range(n_copies - 1):
+        copies.append(Copy(store.clone(), x.clone(), y.clone()))
+    return copies
+
+
+def run_config(args, rs, torch, dev, key, cpu):
+    wl = build_workload(key)
+    m = wl.module
+    e = 2 if wl.dtype == "bf16" else 4
+    ids = torch.from_numpy(wl.ids).to(dev)
+    nbytes = algorithmic_bytes(wl.ids, m.ranks, m.n, m.d_in, m.d_out, e)
+    K, W = args.steps, args.warmup
+    n_copies = 1 if args.warm else max(split_steps(K))
+    flush = Flush(torch, dev, not args.warm)
+    copies = make_copies(rs, torch, wl, dev, 0, n_copies)
+    ws = torch.empty(rs.lora_workspace_bytes(copies[0].store, wl.T), dtype=torch.uint8, device=dev)
+    graph = not args.no_graph
+
+    def step(c):
+        rs.lora_apply_batched(c.store, c.x, c.y, ids=ids, ws=ws)
+
+    t = time_steps(torch, step, copies, K, W, flush, graph=graph)
+    eager = time_steps(torch, step, copies, K, 0, flush, graph=False) if graph else t
+    ms = t["ms_per_step"]
+    launches = rs.lora_apply_launches(copies[0].store, wl.T, True)
+    # The two-launch form's kernels, each alone (for a fused call: a comparison).
+    split = {}
+    if not args.no_kernels:
+        for name, phase in (("shrink", 1), ("expand", 2)):
+            kt = time_steps(torch, lambda c, ph=phase: rs.lora_apply_batched_phases(c.store, c.x, c.y, ph, ids=ids,
+                                                                                  ws=ws),
+                            copies, K, 1, flush, graph=graph)
+            us = kt["ms_per_step"] * 1e3
+            split[name] = {"avg_us": round(us, 2), "launches": K, "algorithmic_bytes": nbytes[name],
+                           "gbps": round(nbytes[name] / (us * 1e-6) / 1e9, 1),
+                           "timed_as": "graph replays of that kernel alone, each segment after a cache flush "
+                                       "(an expand alone then reads a cold plan and partial sums)"}
+    gbps = nbytes["total"] / (ms * 1e-3) / 1e9
+    if launches == 1:
+        kern = {"decode_apply": {"avg_us": round(ms * 1e3, 2), "launches": K,
+                                 "timed_as": "the step's timing (one launch per step)",
+                                 "algorithmic_bytes": nbytes["total"], "gbps": round(gbps, 1)}}
+        dom, dom_bytes = "decode_apply", nbytes["total"]
+    else:
+        kern = split
+        dom = max(("shrink", "expand"), key=lambda k: kern[k]["avg_us"]) if split else "shrink"
+        dom_bytes = nbytes[dom]
+    dom_us = kern[dom]["avg_us"] if dom in kern else ms * 1e3
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic_for(f"config{key}", dom),
+                "kernel": f"{dom}_kernel<{'BF16' if e == 2 else 'F32'}>",
+                "algorithmic_bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_us, 2)}
+    del copies
+    torch.cuda.empty_cache()
+
+    padded = {}
+    if not args.no_padded:
+        r_max = int(m.ranks.max())
+        variants = {"pad_r_max": r_max}
+        if m.orig_rank and m.orig_rank > r_max:
+            variants["pad_orig"] = int(m.orig_rank)
+        p8 = int(-(-r_max // 8) * 8)
+        if p8 != r_max:
+            variants["pad8"] = p8
+        for name, pad in variants.items():
+            pc = make_copies(rs, torch, wl, dev, pad, n_copies)
+            pws = torch.empty(rs.lora_workspace_bytes(pc[0].store, wl.T), dtype=torch.uint8, device=dev)
+            pt = time_steps(torch, lambda c: rs.lora_apply_batched(c.store, c.x, c.y, ids=ids, ws=pws),
+                            pc, K, W, flush, graph=graph)
+            pms = pt["ms_per_step"]
+            own = algorithmic_bytes(wl.ids, np.full(m.n, pad), m.n, m.d_in, m.d_out, e)["total"]
+            padded[name] = {"pad_to": pad, "ms_per_step": round(pms, 5), "median_ms": pt["dist"]["median_ms"],
+                            "tokens_per_s": round(wl.T / (pms * 1e-3), 1),
+                            "effective_gbps": round(nbytes["total"] / (pms * 1e-3) / 1e9, 1),
+                            "own_bytes": own, "own_gbps": round(own / (pms * 1e-3) / 1e9, 1),
+                            "specialized_speedup": round(pms / ms, 3)}
+            del pc, pws
+            torch.cuda.empty_cache()
+
+    out = {
+        "metric": METRIC, "value": round(wl.T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic: seeded N(0,1) activations and y0, N(0,1/sqrt(d)) factors, rounded to bf16",
+        "config": {"workload": WORKLOAD_NAMES[key], "T": wl.T, "n_adapters": m.n, "d_in": m.d_in,
+                   "d_out": m.d_out, "ranks_sum": int(m.ranks.sum()), "r_max": int(m.ranks.max()),
+                   "touched_adapters": nbytes["touched"],
+                   "timing": "warm (cache-resident)" if args.warm else
+                   f"cold: {len(split_steps(K))} timed segments, each after a 2 GiB cache flush, steps of a "
+                   f"segment on {n_copies} distinct copies of (store, x, y)"},
+        "timing": dict(t["dist"], segments=t["segments"]),
+        "gbps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_GBPS, 4), "bytes_per_step": nbytes["total"],
+        "roofline": roofline, "cpu_baseline": cpu, "launches_per_step": launches, "kernels": kern,
+        "two_launch_kernels": split if launches == 1 else None, "padded": padded,
+        "wall_s_timed": round(t["wall_s"], 6),
+        "timed_as": "eager launches" if args.no_graph else "HIP-graph replays (see timing.segments)",
+        "eager_ms_per_step": round(eager["ms_per_step"], 6),
+        "kernel_sources_sha": kernel_source_digest(),
+    }
+    print(json.dumps(out), flush=True)
 
 
 def jd_algorithmic_bytes(w, e: int):
@@ -362,15 +602,16 @@ def run_jd(args, rs, torch, dev, key):
     x = torch.from_numpy(w.x).to(dev).to(dt)
     y = torch.randn(w.T, w.d_out, generator=gen, device=dev).to(dt)
     ids = torch.from_numpy(w.ids).to(dev)
-    per_copy = (st.basis.A_pack.numel() + st.basis.B_pack.numel() + st.sigma.numel() * 4
-                + x.numel() * 2 + y.numel() * 2)
-    n_copies = 1 if args.warm else int(min(512, max(1, math.ceil(COLD_BYTES / per_copy))))
+    K, W = args.steps, args.warmup
+    n_copies = 1 if args.warm else max(split_steps(K))
+    flush = Flush(torch, dev, not args.warm)
     copies = [Copy(st, x, y)] + [Copy(st.clone(), x.clone(), y.clone()) for _ in range(n_copies - 1)]
     ws = torch.empty(rs.lora_jd_workspace_bytes(st, w.T), dtype=torch.uint8, device=dev)
     step = lambda c: rs.lora_jd_apply(c.store, c.x, c.y, ids, ws=ws)
-    eager_ms, _ = time_apply(rs, torch, copies, ids, ws, args.steps, args.warmup, step=step)
-    ms, wall = (eager_ms, 0.0) if args.no_graph else \
-        time_apply_graph(rs, torch, copies, ids, ws, args.steps, args.warmup, step=step)
+    graph = not args.no_graph
+    t = time_steps(torch, step, copies, K, W, flush, graph=graph)
+    eager_ms = time_steps(torch, step, copies, K, 0, flush, graph=False)["ms_per_step"] if graph else t["ms_per_step"]
+    ms, wall = t["ms_per_step"], t["wall_s"]
     nb = jd_algorithmic_bytes(w, e)
     gbps = nb["total"] / (ms * 1e-3) / 1e9
     del copies
@@ -388,12 +629,10 @@ def run_jd(args, rs, torch, dev, key):
             A_l.append(torch.from_numpy(w.V[cj]).to(dev).t().contiguous().to(dt))
         ls = rs.lora_pack_retained(A_l, B_l, w.scales)
         del A_l, B_l
-        lper = ls.A_pack.numel() + ls.B_pack.numel() + x.numel() * 2 + y.numel() * 2
-        lcopies = [Copy(ls, x, y)] + [Copy(ls.clone(), x.clone(), y.clone())
-                                      for _ in range((1 if args.warm else max(1, math.ceil(COLD_BYTES / lper))) - 1)]
+        lcopies = [Copy(ls, x, y)] + [Copy(ls.clone(), x.clone(), y.clone()) for _ in range(n_copies - 1)]
         lws = torch.empty(rs.lora_workspace_bytes(ls, w.T), dtype=torch.uint8, device=dev)
-        lms, _ = (time_apply if args.no_graph else time_apply_graph)(rs, torch, lcopies, ids, lws,
-                                                                   max(20, args.steps // 2), args.warmup)
+        lms = time_steps(torch, lambda c: rs.lora_apply_batched(c.store, c.x, c.y, ids=ids, ws=lws), lcopies, K, W,
+                         flush, graph=graph)["ms_per_step"]
         as_lora = {"ms_per_step": round(lms, 5), "tokens_per_s": round(w.T / (lms * 1e-3), 1),
                    "store_bytes": ls.A_pack.numel() + ls.B_pack.numel(),
                    "jd_store_bytes": st.basis.A_pack.numel() + st.basis.B_pack.numel() + st.sigma.numel() * 4,
@@ -403,11 +642,7 @@ def run_jd(args, rs, torch, dev, key):
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import jd_apply_ref
-        try:
-            from threadpoolctl import threadpool_limits
-            limiter = threadpool_limits(1)
-        except Exception:  # pragma: no cover
-            limiter = None
+        limiter = _blas_one_thread()
         Ts = min(w.T, 256)
         reps, t0 = 0, time.perf_counter()
         while time.perf_counter() - t0 < args.cpu_seconds:
@@ -430,11 +665,12 @@ def run_jd(args, rs, torch, dev, key):
         "data": "synthetic: seeded orthonormal (full) or N(0,1/sqrt(d)) (diag) bases, N(0,.) Sigma, N(0,1) x, bf16",
         "config": {"workload": WORKLOAD_NAMES[key], "T": w.T, "n_adapters": w.n, "clusters": w.k, "r": w.r,
                    "d_in": w.d_in, "d_out": w.d_out, "timing": "warm" if args.warm else
-                   f"cold-HBM rotation over {n_copies} copies"},
+                   f"cold: timed segments each after a 2 GiB cache flush, on {n_copies} distinct copies"},
+        "timing": t["dist"],
         "gbps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_GBPS, 4), "bytes_per_step": nb["total"],
         "bytes_breakdown": nb, "roofline": roofline, "cpu_baseline": cpu, "launches_per_step": 3,
         "as_lora": as_lora, "eager_ms_per_step": round(eager_ms, 5),
-        "timed_as": "eager launches" if args.no_graph else "one HIP-graph replay of the K captured steps",
+        "timed_as": "eager launches" if args.no_graph else "HIP-graph replays in timed segments",
         "kernel_sources_sha": kernel_source_digest(JD_SOURCES),
     }
     print(json.dumps(out), flush=True)
@@ -587,34 +823,6 @@ def run_ranks(args):
     }), flush=True)
 
 
-def cpu_baseline(wl, seconds: float):
-    """The CPU oracle as it stands, on a bounded sample of the same workload,
-    with BLAS pinned to one thread."""
-    from oracle import apply_ref
-    try:
-        from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(1)
-    except Exception:  # pragma: no cover
-        limiter = None
-    m = wl.module
-    T = wl.T
-    sample = min(T, 256)
-    x, ids, y0 = wl.x[:sample], wl.ids[:sample], wl.y0[:sample]
-    tokens, t0 = 0, time.perf_counter()
-    while True:
-        apply_ref(x, ids, m.A, m.B, m.scales, y0)
-        tokens += sample
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    if limiter is not None:
-        limiter.unregister()
-    return {"value": tokens / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {sample} tokens of the same workload, float64 per-token loop, repeated "
-                      f"{tokens // sample}x over {el:.1f} s on {platform.processor() or platform.machine()}"
-                      f" (host has {os.cpu_count()} logical CPUs; BLAS pinned to 1 thread)"}
-
-
 # ------------------------------------------------------------------ fleet
 def build_fleet(rs, torch, key: str, dev, pad_to_rmax: bool):
     """The 196 module stores of one decode step.  Factor values are drawn on
@@ -641,198 +849,213 @@ def build_fleet(rs, torch, key: str, dev, pad_to_rmax: bool):
     return stores, meta
 
 
-def run_fleet(args, rs, torch, dev):
-    from workloads import FLEET_INPUT_DIMS, fleet_ids
-    key = args.config
-    T, n = 4096, 1024
-    ids_np = fleet_ids(T, n)
-    ids = torch.from_numpy(ids_np).to(dev)
-    stores, meta = build_fleet(rs, torch, key, dev, False)
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(2612)
-    layers = max(m[0] for m in meta) + 1
-    xs = {(l, k): torch.randn(T, d, generator=gen, device=dev).to(torch.bfloat16)
-          for l in range(layers) for k, d in enumerate(FLEET_INPUT_DIMS)}
-    ys = [torch.randn(T, m[4], generator=gen, device=dev).to(torch.bfloat16) for m in meta]
-    ws = torch.empty(max(rs.lora_workspace_bytes(st, T) for st in stores), dtype=torch.uint8, device=dev)
-    seg = rs.lora_segment(ids, n)
-    per_mod = [algorithmic_bytes(ids_np, m[6], n, m[3], m[4], 2) for m in meta]
-    seg_bytes = 4 * (2 * T + n + 2)
-    step_bytes = seg_bytes + sum(b["total"] for b in per_mod)
-
-    # The shrink-only and expand-only passes need one workspace per module:
-    # a module's expand reads the plan and partial sums of its own shrink.
-    mod_ws = [torch.empty(rs.lora_workspace_bytes(st, T), dtype=torch.uint8, device=dev) for st in stores]
-
-    nstr = max(1, args.streams)
-    stages = []  # module indices per (layer, input kind), in forward order
+def fleet_stages(meta):
+    """Module indices per (layer, input kind), in forward order: the modules
+    of a stage read the same input (q/k/v; o; gate/up; down)."""
+    stages = []
     for i, m in enumerate(meta):
         if stages and meta[stages[-1][0]][0] == m[0] and meta[stages[-1][0]][5] == m[5]:
             stages[-1].append(i)
         else:
             stages.append([i])
-    side_streams = [torch.cuda.Stream() for _ in range(nstr - 1)]  # default priority
-    str_ws = [ws] + [torch.empty_like(ws) for _ in range(nstr - 1)]
+    return stages
 
-    def step(phases=3):
-        if phases == 3:
-            rs.lora_segment(ids, n, seg=seg)
-        if phases == 3 and nstr > 1:
-            # The modules of one stage (those reading the same input: q/k/v,
-            # then o, then gate/up, then down, layer after layer) go to
-            # different streams, each with its own workspace; a stage starts
-            # when the previous one has finished, as in a forward pass, where
-            # each stage's input comes from the one before.
-            main = torch.cuda.current_stream()
-            for stage in stages:
-                for sst in side_streams:
-                    sst.wait_stream(main)
-                for k, i in enumerate(stage):
-                    m = meta[i]
-                    with torch.cuda.stream(main if k % nstr == 0 else side_streams[k % nstr - 1]):
-                        rs.lora_apply_batched(stores[i], xs[(m[0], m[5])], ys[i], seg=seg, ws=str_ws[k % nstr])
-                for sst in side_streams:
-                    main.wait_stream(sst)
+
+def fleet_step(rs, torch, stores, meta, xs, ys, ids, seg, n, nstr, str_ws):
+    """One decode step: the grouping, then every module's apply on it.  The
+    modules of a stage go to up to nstr streams (default priority, one
+    workspace each); a stage starts when the previous one has finished, as in
+    a forward pass, where each stage's input comes from the one before."""
+    stages = fleet_stages(meta)
+    side = [torch.cuda.Stream() for _ in range(nstr - 1)]
+
+    def step():
+        rs.lora_segment(ids, n, seg=seg)
+        if nstr == 1:
+            for st, m, y in zip(stores, meta, ys):
+                rs.lora_apply_batched(st, xs[(m[0], m[5])], y, seg=seg, ws=str_ws[0])
             return
-        for st, m, y, w in zip(stores, meta, ys, mod_ws):
-            x = xs[(m[0], m[5])]
-            if phases == 3:
-                rs.lora_apply_batched(st, x, y, seg=seg, ws=ws)
-            else:
-                rs.lora_apply_batched_phases(st, x, y, phases, seg=seg, ws=w)
+        main = torch.cuda.current_stream()
+        for stage in stages:
+            for s in side:
+                s.wait_stream(main)
+            for k, i in enumerate(stage):
+                m = meta[i]
+                with torch.cuda.stream(main if k % nstr == 0 else side[k % nstr - 1]):
+                    rs.lora_apply_batched(stores[i], xs[(m[0], m[5])], ys[i], seg=seg, ws=str_ws[k % nstr])
+            for s in side:
+                main.wait_stream(s)
+    return step
 
-    def timed(phases, reps):
-        for _ in range(max(1, args.warmup)):
-            step(phases)
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        if args.no_graph:
-            e0.record()
-            for _ in range(reps):
-                step(phases)
-            e1.record()
-            torch.cuda.synchronize()
-        else:
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                step(phases)
-            torch.cuda.current_stream().wait_stream(side)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step(phases)
-            g.replay()
-            torch.cuda.synchronize()
-            e0.record()
-            for _ in range(reps):
-                g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            del g
-        return e0.elapsed_time(e1) / reps
 
-    steps = args.steps
-    t0 = time.perf_counter()
-    ms = timed(3, steps)
-    wall = time.perf_counter() - t0
-    k_ms = {"shrink": timed(1, steps), "expand": timed(2, steps)}  # expand after shrink: plans in place
-    mod_ws[:] = [None] * len(mod_ws)  # only the full step (one shared workspace) runs from here
+def run_fleet_key(args, rs, torch, dev, key, xs, ys, ids, full: bool):
+    """Time the fleet step of `key` (5U or 5S); with `full`, also each kernel
+    alone, the multi-slice step and the rank-padded stores."""
+    T, n = 4096, 1024
+    _, per_mod, seg_bytes = fleet_algorithmic(key, T, n)
+    step_bytes = seg_bytes + sum(b["total"] for b in per_mod)
+    stores, meta = build_fleet(rs, torch, key, dev, False)
+    seg = rs.lora_segment(ids, n)
+    nstr = max(1, args.streams)
+    wsb = max(rs.lora_workspace_bytes(st, T) for st in stores)
+    str_ws = [torch.empty(wsb, dtype=torch.uint8, device=dev) for _ in range(nstr)]
+    graph = not args.no_graph
+    K, W = args.steps, args.warmup
+    t = time_replays(torch, fleet_step(rs, torch, stores, meta, xs, ys, ids, seg, n, nstr, str_ws), K, W, graph)
+    ms = t["ms_per_step"]
+    res = {"ms_per_step": ms, "timing": t["dist"], "wall_s": t["wall_s"], "bytes_per_step": step_bytes,
+           "gbps": step_bytes / (ms * 1e-3) / 1e9, "tokens_per_s": T / (ms * 1e-3),
+           "ranks_sum_per_module_mean": float(np.mean([int(m[6].sum()) for m in meta]))}
+    if not full:
+        del stores, str_ws
+        torch.cuda.empty_cache()
+        return res
+
     kern = {}
-    for name, kms in k_ms.items():
-        nb = sum(b[name] for b in per_mod)
-        kern[name] = {"avg_us": round(1e3 * kms / len(stores), 2), "launches_per_step": len(stores),
-                      "algorithmic_bytes_per_step": nb, "gbps": round(nb / (kms * 1e-3) / 1e9, 1)}
-    dom = max(kern, key=lambda k: kern[k]["avg_us"])
-    achieved = kern[dom]["algorithmic_bytes_per_step"] / (k_ms[dom] * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic_for(f"config{key}", dom),
-                "kernel": f"{dom}_kernel<BF16> over the 196 modules of a step",
-                "algorithmic_bytes_per_launch": round(kern[dom]["algorithmic_bytes_per_step"] / len(stores)),
-                "avg_launch_us": kern[dom]["avg_us"]}
-    multi = {}
+    if not args.no_kernels:
+        # Each kernel alone over the 196 modules (one stream, a workspace per
+        # module: a module's expand reads the plan and partial sums its own
+        # shrink left).
+        mod_ws = [torch.empty(rs.lora_workspace_bytes(st, T), dtype=torch.uint8, device=dev) for st in stores]
+
+        def phase_step(ph):
+            def f():
+                for st, m, y, w in zip(stores, meta, ys, mod_ws):
+                    rs.lora_apply_batched_phases(st, xs[(m[0], m[5])], y, ph, seg=seg, ws=w)
+            return f
+
+        reps = max(MIN_SEGMENTS, min(K, 10))
+        for name, ph in (("shrink", 1), ("expand", 2)):  # expand after shrink: plans in place
+            kt = time_replays(torch, phase_step(ph), reps, 1, graph)
+            nb = sum(b[name] for b in per_mod)
+            us = kt["ms_per_step"] * 1e3 / len(stores)
+            kern[name] = {"avg_us": round(us, 2), "launches_per_step": len(stores), "replays": reps,
+                          "algorithmic_bytes_per_step": nb, "gbps": round(nb / (kt["ms_per_step"] * 1e-3) / 1e9, 1),
+                          "timed_as": "graph replays of the 196 launches of that kernel alone, one stream"}
+        del mod_ws
+        torch.cuda.empty_cache()
+    res["kernels"] = kern
+    if kern:
+        dom = max(kern, key=lambda k: kern[k]["avg_us"])
+        dom_bytes = kern[dom]["algorithmic_bytes_per_step"] / len(stores)
+        achieved = dom_bytes / (kern[dom]["avg_us"] * 1e-6) / 1e9
+        res["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                           "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic_for(f"config{key}", dom),
+                           "kernel": f"{dom}_kernel<BF16>, mean over the 196 modules of a step",
+                           "algorithmic_bytes_per_launch": round(dom_bytes), "avg_launch_us": kern[dom]["avg_us"]}
+
     if not args.no_multi:
-        # The same step with the projections that share an input applied
-        # together (q/k/v, gate/up): one x read per group.
+        # The projections that share an input applied together (q/k/v,
+        # gate/up): one x read per group, one call per stage.
         groups = {}
         for i, m in enumerate(meta):
             groups.setdefault((m[0], m[5]), []).append(i)
         mstores = {g: rs.lora_pack_multi([stores[i] for i in idx]) for g, idx in groups.items() if len(idx) > 1}
-        mbytes = max([rs.lora_multi_workspace_bytes(mst, T) for mst in mstores.values()] + [ws.numel()])
-        mws = [torch.empty(mbytes, dtype=torch.uint8, device=dev)]
+        mbytes = max([rs.lora_multi_workspace_bytes(mst, T) for mst in mstores.values()] + [wsb])
+        mws = torch.empty(mbytes, dtype=torch.uint8, device=dev)
 
-        def step_multi(phases=3):
-            # One call per stage: nothing is left to overlap in a forward pass.
+        def step_multi():
             rs.lora_segment(ids, n, seg=seg)
             for g, idx in groups.items():
                 if len(idx) > 1:
-                    rs.lora_apply_multi(mstores[g], xs[g], [ys[j] for j in idx], seg=seg, ws=mws[0])
+                    rs.lora_apply_multi(mstores[g], xs[g], [ys[j] for j in idx], seg=seg, ws=mws)
                 else:
-                    rs.lora_apply_batched(stores[idx[0]], xs[g], ys[idx[0]], seg=seg, ws=mws[0])
+                    rs.lora_apply_batched(stores[idx[0]], xs[g], ys[idx[0]], seg=seg, ws=mws)
 
         saved = sum(T * meta[idx[0]][3] * 2 * (len(idx) - 1) for idx in groups.values())
-        step_fn = step
-        step = step_multi
-        mms = timed(3, steps)
-        step = step_fn
-        multi = {"groups": "per layer: q+k+v, o, gate+up, down", "calls_per_step": len(groups),
-                 "ms_per_step": round(mms, 4), "tokens_per_s": round(T / (mms * 1e-3), 1),
-                 "x_bytes_saved_per_step": saved, "algorithmic_bytes_per_step": step_bytes - saved,
-                 "gbps": round((step_bytes - saved) / (mms * 1e-3) / 1e9, 1), "speedup": round(ms / mms, 3)}
+        mt = time_replays(torch, step_multi, K, 1, graph)
+        mms = mt["ms_per_step"]
+        res["multi_slice"] = {"groups": "per layer: q+k+v, o, gate+up, down", "calls_per_step": len(groups),
+                              "ms_per_step": round(mms, 5), "median_ms": mt["dist"]["median_ms"],
+                              "tokens_per_s": round(T / (mms * 1e-3), 1), "x_bytes_saved_per_step": saved,
+                              "algorithmic_bytes_per_step": step_bytes - saved,
+                              "gbps": round((step_bytes - saved) / (mms * 1e-3) / 1e9, 1),
+                              "speedup": round(ms / mms, 3)}
         del mstores, mws
-        torch.cuda.empty_cache()
-    padded = {}
+    del stores, str_ws
+    torch.cuda.empty_cache()
+
     if not args.no_padded and key == "5S":
-        del stores
+        pstores, pmeta = build_fleet(rs, torch, key, dev, True)
+        pwsb = max(rs.lora_workspace_bytes(st, T) for st in pstores)
+        pws = [torch.empty(pwsb, dtype=torch.uint8, device=dev) for _ in range(nstr)]
+        pt = time_replays(torch, fleet_step(rs, torch, pstores, pmeta, xs, ys, ids, seg, n, nstr, pws),
+                          max(MIN_SEGMENTS, K // 2), 1, graph)
+        pms = pt["ms_per_step"]
+        res["padded"] = {"pad_r_max": {"pad_to": "r_max of each module (16)", "ms_per_step": round(pms, 5),
+                                       "median_ms": pt["dist"]["median_ms"],
+                                       "tokens_per_s": round(T / (pms * 1e-3), 1),
+                                       "effective_gbps": round(step_bytes / (pms * 1e-3) / 1e9, 1),
+                                       "specialized_speedup": round(pms / ms, 3)}}
+        del pstores, pws
         torch.cuda.empty_cache()
-        stores, _ = build_fleet(rs, torch, key, dev, True)
-        ws = torch.empty(max(rs.lora_workspace_bytes(st, T) for st in stores), dtype=torch.uint8, device=dev)
-        pms = timed(3, max(2, steps // 2))
-        padded["pad_r_max"] = {"pad_to": "r_max of each module (16)", "ms_per_step": round(pms, 4),
-                               "tokens_per_s": round(T / (pms * 1e-3), 1),
-                               "effective_gbps": round(step_bytes / (pms * 1e-3) / 1e9, 1),
-                               "specialized_speedup": round(pms / ms, 3)}
-    cpu = None
-    if not args.no_cpu_baseline:
-        from oracle import apply_ref
-        from workloads import make_fleet_module
-        try:
-            from threadpoolctl import threadpool_limits
-            limiter = threadpool_limits(1)
-        except Exception:  # pragma: no cover
-            limiter = None
-        wl = make_fleet_module(key, 0, 0)
-        sample = 64
-        done, c0 = 0, time.perf_counter()
-        while True:
-            apply_ref(wl.x[:sample], wl.ids[:sample], wl.module.A, wl.module.B, wl.module.scales)
-            done += sample
-            el = time.perf_counter() - c0
-            if el >= args.cpu_seconds:
-                break
-        if limiter is not None:
-            limiter.unregister()
-        cpu = {"value": round(done / el / len(meta), 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": f"first {sample} tokens through module L0.q (3584->3584), float64 per-token loop, "
-                         f"{done // sample} repetitions over {el:.1f} s, BLAS pinned to 1 thread; token-module "
-                         f"rate divided by the {len(meta)} modules of a step"}
+    return res
+
+
+def fleet_inputs(torch, dev, meta_shapes, T=4096):
+    """The step's activations (drawn on the GPU, N(0, 1), bf16): per layer
+    one input per kind (q/k/v, o, gate/up, down), and one y per module."""
+    from workloads import FLEET_INPUT_DIMS
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2612)
+    layers = max(m[0] for m in meta_shapes) + 1
+    xs = {(l, k): torch.randn(T, d, generator=gen, device=dev).to(torch.bfloat16)
+          for l in range(layers) for k, d in enumerate(FLEET_INPUT_DIMS)}
+    ys = [torch.randn(T, m[4], generator=gen, device=dev).to(torch.bfloat16) for m in meta_shapes]
+    return xs, ys
+
+
+def run_fleet(args, rs, torch, dev, cpu):
+    from workloads import fleet_ids, fleet_module_shapes
+    key = args.config
+    T, n = 4096, 1024
+    ids_np = fleet_ids(T, n)
+    ids = torch.from_numpy(ids_np).to(dev)
+    shapes = fleet_module_shapes()
+    xs, ys = fleet_inputs(torch, dev, shapes, T)
+    res = run_fleet_key(args, rs, torch, dev, key, xs, ys, ids, full=True)
+    other = None
+    if key == "5S" and not args.no_5u:
+        u = run_fleet_key(args, rs, torch, dev, "5U", xs, ys, ids, full=False)
+        other = {"workload": WORKLOAD_NAMES["5U"], "ms_per_step": round(u["ms_per_step"], 5),
+                 "median_ms": u["timing"]["median_ms"], "p10_ms": u["timing"]["p10_ms"],
+                 "p90_ms": u["timing"]["p90_ms"], "tokens_per_s": round(u["tokens_per_s"], 1),
+                 "bytes_per_step": u["bytes_per_step"], "gbps": round(u["gbps"], 1),
+                 "hbm_frac": round(u["gbps"] / PEAK_GBPS, 4)}
+    ms = res["ms_per_step"]
     out = {
-        "metric": METRIC, "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "metric": METRIC, "value": round(res["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic: seeded Zipf(1.1) ids; factors, activations and y0 drawn on the GPU, bf16",
-        "config": {"workload": WORKLOAD_NAMES[key], "T": T, "n_adapters": n, "modules": len(meta),
-                   "ranks_sum_per_module_mean": float(np.mean([int(m[6].sum()) for m in meta])),
-                   "timing": "HBM-resident working set of ~50 GB (no rotation needed)"},
-        "gbps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
-        "hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / PEAK_GBPS, 4),
-        "bytes_per_step": step_bytes, "roofline": roofline, "cpu_baseline": cpu, "kernels": kern,
-        "padded": padded, "multi_slice": multi, "streams": nstr, "wall_s_timed": round(wall, 6),
+        "config": {"workload": WORKLOAD_NAMES[key], "T": T, "n_adapters": n, "modules": len(shapes),
+                   "ranks_sum_per_module_mean": res["ranks_sum_per_module_mean"],
+                   "timing": "each step streams ~50 GB from HBM (200x the last-level cache); one HIP-graph "
+                             "replay per step, events around each"},
+        "timing": res["timing"],
+        "gbps": round(res["gbps"], 1), "hbm_frac": round(res["gbps"] / PEAK_GBPS, 4),
+        "bytes_per_step": res["bytes_per_step"], "roofline": res.get("roofline"), "cpu_baseline": cpu,
+        "kernels": res.get("kernels"), "padded": res.get("padded", {}), "multi_slice": res.get("multi_slice", {}),
+        "fleet_5U": other, "streams": max(1, args.streams), "wall_s_timed": round(res["wall_s"], 6),
         "timed_as": "eager launches" if args.no_graph else "HIP-graph replays of one captured step",
         "kernel_sources_sha": kernel_source_digest(),
     }
     print(json.dumps(out), flush=True)
+
+
+def cpu_for(args, key):
+    """The CPU-oracle leg of the bench line (before the GPU is touched)."""
+    if args.no_cpu_baseline:
+        return None
+    if key in ("5U", "5S"):
+        from workloads import make_fleet_module
+        wl = make_fleet_module(key, 0, 0)
+        return cpu_oracle(wl.x, wl.ids, wl.module.A, wl.module.B, wl.module.scales, args.cpu_seconds, 32, 196,
+                          "tokens of the step's module L0.q (3584->3584)")
+    wl = build_workload(key)
+    per = min(wl.T, 64)
+    return cpu_oracle(wl.x, wl.ids, wl.module.A, wl.module.B, wl.module.scales, args.cpu_seconds, per, 1,
+                      "tokens of the same workload")
 
 
 def main():
@@ -847,6 +1070,8 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; the apply's sharding across GPUs "
                                    "is described in DESIGN.md but not built", "n_gpus": args.gpus}))
         sys.exit(2)
+    key = args.config
+    cpu = cpu_for(args, key) if key in ("1", "2", "3", "4", "5U", "5S") else None
     import torch
 
     import rank_specialized_amd as rs
@@ -861,114 +1086,14 @@ def main():
         torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    key = args.config
     if key in ("5U", "5S"):
-        run_fleet(args, rs, torch, dev)
-        return
-    if key.startswith("jd-"):
+        run_fleet(args, rs, torch, dev, cpu)
+    elif key.startswith("jd-"):
         run_jd(args, rs, torch, dev, key)
-        return
-    if key.startswith("rsvd-"):
+    elif key.startswith("rsvd-"):
         run_rsvd(args, rs, torch, dev, key)
-        return
-    wl = build_workload(key)
-    m = wl.module
-    e = 2 if wl.dtype == "bf16" else 4
-    ids = torch.from_numpy(wl.ids).to(dev)
-    nbytes = algorithmic_bytes(wl.ids, m.ranks, m.n, m.d_in, m.d_out, e)
-
-    copies, per_copy = make_copies(rs, torch, wl, dev, 0, not args.warm)
-    ws = torch.empty(rs.lora_workspace_bytes(copies[0].store, wl.T), dtype=torch.uint8, device=dev)
-    eager_ms, eager_wall = time_apply(rs, torch, copies, ids, ws, args.steps, args.warmup)
-    if args.no_graph:
-        ms, wall = eager_ms, eager_wall
     else:
-        ms, wall = time_apply_graph(rs, torch, copies, ids, ws, args.steps, args.warmup)
-    launches = rs.lora_apply_launches(copies[0].store, wl.T, True)
-    # The two-launch form's kernels, each alone (for a fused call: a comparison).
-    split = time_kernels(rs, torch, copies, ids, ws, args.steps, args.warmup, graph=not args.no_graph)
-    gbps = nbytes["total"] / (ms * 1e-3) / 1e9
-    for k in ("shrink", "expand"):
-        split[k]["algorithmic_bytes"] = nbytes[k]
-        split[k]["gbps"] = round(nbytes[k] / (split[k]["avg_us"] * 1e-6) / 1e9, 1)
-        split[k] = {a: (round(b, 2) if isinstance(b, float) else b) for a, b in split[k].items()}
-    if launches == 1:
-        # One fused kernel per step: the step's timed replay is K launches of it.
-        kern = {"decode_apply": {"avg_us": round(ms * 1e3, 2), "launches": args.steps,
-                                 "timed_as": "the step's timing (one launch per step)",
-                                 "algorithmic_bytes": nbytes["total"], "gbps": round(gbps, 1)}}
-        dom, dom_bytes = "decode_apply", nbytes["total"]
-    else:
-        kern = split
-        dom = max(("shrink", "expand"), key=lambda k: kern[k]["avg_us"])
-        dom_bytes = nbytes[dom]
-    achieved = dom_bytes / (kern[dom]["avg_us"] * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_GBPS, 4),
-                "traffic": traffic_for(f"config{key}", dom),
-                "kernel": f"{dom}_kernel<{'BF16' if e == 2 else 'F32'}>",
-                "algorithmic_bytes_per_launch": dom_bytes,
-                "avg_launch_us": round(kern[dom]["avg_us"], 2)}
-    del copies
-    torch.cuda.empty_cache()
-
-    padded = {}
-    if not args.no_padded:
-        r_max = int(m.ranks.max())
-        variants = {"pad_r_max": r_max}
-        if m.orig_rank and m.orig_rank > r_max:
-            variants["pad_orig"] = int(m.orig_rank)
-        p8 = int(-(-r_max // 8) * 8)
-        if p8 != r_max:
-            variants["pad8"] = p8
-        for name, pad in variants.items():
-            pc, _ = make_copies(rs, torch, wl, dev, pad, not args.warm)
-            pws = torch.empty(rs.lora_workspace_bytes(pc[0].store, wl.T), dtype=torch.uint8, device=dev)
-            pms, _ = (time_apply if args.no_graph else time_apply_graph)(rs, torch, pc, ids, pws,
-                                                                       max(20, args.steps // 2), args.warmup)
-            own = algorithmic_bytes(wl.ids, np.full(m.n, pad), m.n, m.d_in, m.d_out, e)["total"]
-            padded[name] = {"pad_to": pad, "ms_per_step": round(pms, 5),
-                            "tokens_per_s": round(wl.T / (pms * 1e-3), 1),
-                            "effective_gbps": round(nbytes["total"] / (pms * 1e-3) / 1e9, 1),
-                            "own_bytes": own, "own_gbps": round(own / (pms * 1e-3) / 1e9, 1),
-                            "specialized_speedup": round(pms / ms, 3)}
-            del pc, pws
-            torch.cuda.empty_cache()
-
-    cpu = None if args.no_cpu_baseline else cpu_baseline(wl, args.cpu_seconds)
-    out = {
-        "metric": METRIC,
-        "value": round(wl.T / (ms * 1e-3), 1),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": wl.dtype,
-        "data": "synthetic: seeded N(0,1) activations and y0, N(0,1/sqrt(d)) factors, rounded to bf16",
-        "config": {"workload": WORKLOAD_NAMES[key], "T": wl.T, "n_adapters": m.n, "d_in": m.d_in,
-                   "d_out": m.d_out, "ranks_sum": int(m.ranks.sum()), "r_max": int(m.ranks.max()),
-                   "touched_adapters": nbytes["touched"], "timing": "warm" if args.warm else
-                   f"cold-HBM rotation over {max(1, min(512, math.ceil(COLD_BYTES / per_copy)))} copies"},
-        "gbps": round(gbps, 1),
-        "hbm_frac": round(gbps / PEAK_GBPS, 4),
-        "bytes_per_step": nbytes["total"],
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        "launches_per_step": launches,
-        "kernels": kern,
-        "two_launch_kernels": split if launches == 1 else None,
-        "padded": padded,
-        "wall_s_timed": round(wall, 6),
-        "timed_as": "eager launches" if args.no_graph else
-                    "one HIP-graph replay of the K captured steps (eager launches: see eager_ms_per_step)",
-        "eager_ms_per_step": round(eager_ms, 5),
-        "kernel_sources_sha": kernel_source_digest(),
-    }
-    print(json.dumps(out), flush=True)
+        run_config(args, rs, torch, dev, key, cpu)
 
 
 if __name__ == "__main__":
