@@ -236,6 +236,30 @@ int lora_apply_batched(const lora_store* store_host, const void* x, int64_t ldx,
                        size_t ws_bytes, void* stream);
 
 /*
+ * The batched apply without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory or pass one: code under HIP
+ * graph capture that must not call hipMalloc, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, same kernels and the same result
+ * as lora_apply_batched (bit for bit); the workspace is the library's own
+ * array of LORA_NOALLOC_SCRATCH_BYTES bytes, one per device, held from the
+ * first call on that device until the process ends.
+ *  - No hipMalloc, hipFree or allocating library call is made.
+ *  - Every call on a device shares that device's array, and the array keeps
+ *    the last call's contents (nothing in it needs to start at zero): calls
+ *    that overlap on one device (several streams, several host threads) race
+ *    on it and give wrong results.  Serialize them, or use lora_apply_batched
+ *    with a workspace each.
+ * Errors: those of lora_apply_batched (the workspace's aside), checked before
+ * any HIP call; UNSUPPORTED when lora_workspace_bytes(store, T) exceeds
+ * LORA_NOALLOC_SCRATCH_BYTES; HIP_ERROR if the array's address cannot be
+ * looked up on the current device.
+ */
+#define LORA_NOALLOC_SCRATCH_BYTES (32 << 20)
+int lora_apply_batched_noalloc(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy,
+                               int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm,
+                               void* stream);
+
+/*
  * One kernel of lora_apply_batched at a time, for measuring each alone:
  * phases = 1 runs the shrink only (grouping, partial sums and plan into ws;
  * with ids and n > 4096 also the sort), 2 the expand only (from the plan and

@@ -27,7 +27,7 @@ from ._lib import LoraError, lora_store  # noqa: F401
 __all__ = [
     "Store", "Segmentation", "LoraError", "lora_store_bytes", "lora_pack_retained",
     "lora_segment", "lora_workspace_bytes", "lora_shrink", "lora_expand", "lora_apply_batched",
-    "lora_apply_batched_phases", "lora_apply_launches", "JDStore", "lora_jd_pack", "lora_jd_workspace_bytes",
+    "lora_apply_batched_phases", "lora_apply_batched_noalloc", "lora_apply_launches", "JDStore", "lora_jd_pack", "lora_jd_workspace_bytes",
     "lora_jd_apply", "lora_ranks_uniform", "lora_ranks_spectral", "RsvdFactors", "lora_rsvd_workspace_bytes",
     "lora_rsvd_factor", "lora_rsvd_write", "MultiStore", "lora_pack_multi", "lora_multi_workspace_bytes",
     "lora_apply_multi", "load_library",
@@ -252,6 +252,27 @@ def lora_apply_batched_phases(store: Store, x: torch.Tensor, y: torch.Tensor, ph
     L.check("lora_apply_batched_phases", L.lib().lora_apply_batched_phases(
         store.ref(), _p(x), _rows(x, "x"), _p(y), _rows(y, "y"), T, _p(ids) if ids is not None else None,
         so, pm, ws.data_ptr(), ws.numel(), _stream(x), phases))
+    return y
+
+
+def lora_apply_batched_noalloc(store: Store, x: torch.Tensor, y: torch.Tensor, *,
+                               ids: Optional[torch.Tensor] = None,
+                               seg: Optional[Segmentation] = None) -> torch.Tensor:
+    """lora_apply_batched without a workspace: the library's own per-device
+    scratch array serves as one (nothing is allocated, here or in the
+    library).  Calls that overlap on one device race on that array."""
+    T = x.shape[0]
+    if (ids is None) == (seg is None):
+        raise ValueError("pass exactly one of ids or seg")
+    if seg is not None:
+        so, pm = seg.seg_off.data_ptr(), _p(seg.perm)
+    else:
+        if ids.dtype != torch.int32 or not ids.is_contiguous():
+            raise ValueError("ids must be a contiguous int32 vector")
+        so = pm = None
+    L.check("lora_apply_batched_noalloc", L.lib().lora_apply_batched_noalloc(
+        store.ref(), _p(x), _rows(x, "x"), _p(y), _rows(y, "y"), T, _p(ids) if ids is not None else None,
+        so, pm, _stream(x)))
     return y
 
 

@@ -39,6 +39,7 @@ class lora_jd_store(C.Structure):
 
 
 LORA_MAX_SLICES = 4
+LORA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class lora_multi_store(C.Structure):
@@ -65,6 +66,7 @@ SIGNATURES = {
     "lora_expand": (I, [C.POINTER(lora_store), P, I64, I, P, P, P, I64, P, SZ, P]),
     "lora_apply_batched": (I, [C.POINTER(lora_store), P, I64, P, I64, I, P, P, P, P, SZ, P]),
     "lora_apply_batched_phases": (I, [C.POINTER(lora_store), P, I64, P, I64, I, P, P, P, P, SZ, P, I]),
+    "lora_apply_batched_noalloc": (I, [C.POINTER(lora_store), P, I64, P, I64, I, P, P, P, P]),
     "lora_apply_launches": (I, [C.POINTER(lora_store), I, I]),
     "lora_jd_workspace_bytes": (SZ, [C.POINTER(lora_jd_store), I]),
     "lora_jd_apply": (I, [C.POINTER(lora_jd_store), P, I64, P, I64, I, P, P, SZ, P]),

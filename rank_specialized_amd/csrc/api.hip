@@ -2,6 +2,7 @@
 // Host dispatch only: validate, size grids, launch on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstring>
 #include <vector>
 
@@ -163,6 +164,20 @@ int lora_expand(const lora_store* store_host, const float* h, int64_t ldh, int T
   return e == hipSuccess ? LORA_OK : hip_fail(e);
 }
 
+// The apply's argument checks other than the workspace's (host only).
+static int check_apply_args(const lora_store* store_host, const void* x, int64_t ldx, const void* y, int64_t ldy,
+                            int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm) {
+  int st = check_store(store_host);
+  if (st != LORA_OK) return st;
+  const lora_store& s = *store_host;
+  if (T < 0) return LORA_ERR_INVALID_ARG;
+  if ((st = check_rows(x, ldx, s.d_in, s.dtype, T)) != LORA_OK) return st;
+  if ((st = check_rows(y, ldy, s.d_out, s.dtype, T)) != LORA_OK) return st;
+  if (ids != nullptr && (T > LORA_SEGMENT_MAX_T || s.n > LORA_SEGMENT_MAX_N)) return LORA_ERR_UNSUPPORTED;
+  if (T > 0 && ids == nullptr && (st = check_grouping(store_host, T, seg_off, perm)) != LORA_OK) return st;
+  return LORA_OK;
+}
+
 static int apply_impl(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy, int T,
                       const int32_t* ids, const int32_t* seg_off, const int32_t* perm, void* ws, size_t ws_bytes,
                       void* stream, int phases) {
@@ -206,6 +221,47 @@ int lora_apply_batched(const lora_store* store_host, const void* x, int64_t ldx,
                        int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm, void* ws,
                        size_t ws_bytes, void* stream) {
   return apply_impl(store_host, x, ldx, y, ldy, T, ids, seg_off, perm, ws, ws_bytes, stream, 3);
+}
+
+// ------------------------------------------------------------ no allocation
+// The workspace of lora_apply_batched_noalloc: one array per device, resident
+// for the life of the process.  Host code never uses its name as an address
+// (in host code it is a stand-in, not device memory): the device address is
+// looked up once per device with hipGetSymbolAddress and kept below.
+static __device__ __align__(256) char scratch[LORA_NOALLOC_SCRATCH_BYTES];
+static std::atomic<void*> g_scratch[kMaxDevices];  // per device; null until looked up
+
+// The scratch array's address on the current device (looked up on first use
+// there; two threads racing both look it up and store the same address).
+static hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = current_device(&dev);
+  if (e != hipSuccess) return e;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+int lora_apply_batched_noalloc(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy,
+                               int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm,
+                               void* stream) {
+  // Every argument check before any HIP call; then the size the call needs
+  // against the scratch array's.
+  const int st = check_apply_args(store_host, x, ldx, y, ldy, T, ids, seg_off, perm);
+  if (st != LORA_OK) return st;
+  if (workspace_bytes(store_host, T) > (size_t)LORA_NOALLOC_SCRATCH_BYTES) return LORA_ERR_UNSUPPORTED;
+  if (T == 0) return LORA_OK;
+  void* ws = nullptr;
+  hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return hip_fail(e);
+  return apply_impl(store_host, x, ldx, y, ldy, T, ids, seg_off, perm, ws, (size_t)LORA_NOALLOC_SCRATCH_BYTES,
+                    stream, 3);
 }
 
 // Shared-basis workspace: h [T][ldp] | the basis store's workspace.

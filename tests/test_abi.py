@@ -189,6 +189,34 @@ def test_apply_rejects_before_launch(lib):
     assert call(T=0, x=None, y=None, ws=None, wsb=0) == 0
 
 
+def test_noalloc_rejects_before_any_hip_call(lib):
+    """lora_apply_batched_noalloc checks every argument, and the size its call
+    needs against the scratch array, before any HIP call (so here, without a
+    GPU, no HIP error is recorded)."""
+    st = _store()
+    f = lib.lora_apply_batched_noalloc
+
+    def call(T=16, ids=FAKE, so=None, pm=None, x=FAKE, y=FAKE, ldx=64, ldy=32, s=st):
+        return f(C.byref(s) if s is not None else None, x, ldx, y, ldy, T, ids, so, pm, None)
+
+    assert call(s=None) == 1
+    assert call(s=_store(n=0)) == 1
+    assert call(T=-3) == 1
+    assert call(x=None) == 1
+    assert call(ldy=16) == 1
+    assert call(ldx=68) == 2
+    assert call(T=L.LORA_SEGMENT_MAX_T + 1) == 2
+    assert call(ids=None) == 1
+    assert call(ids=None, so=FAKE) == 1
+    assert call(T=0) == 0
+    assert call(T=0, ids=None, x=None, y=None) == 0
+    big = _store(n=16000, d_in=18944, r_max=64, R=16000 * 64)
+    T = 16384
+    assert lib.lora_workspace_bytes(C.byref(big), T) > L.LORA_NOALLOC_SCRATCH_BYTES
+    assert call(s=big, T=T, ldx=18944) == 2
+    assert lib.lora_last_hip_error() == 0
+
+
 def test_concurrent_validation_from_threads(lib):
     """Eight host threads run the apply's argument checks at once, each with
     its own arguments and expected status (ctypes releases the GIL during the
