@@ -7,9 +7,9 @@ Default workload: the fleet decode step (5S): 28 layers x 7 projections of a
 Qwen2-7B-like model (hidden 3584, k/v 512, MLP 18944), bf16, 1024 adapters
 whose retained ranks vary 4..16 per module, T = 4096 decode tokens with
 Zipf(1.1) adapter popularity.  A step is one pass of the whole hot path over
-that batch: one token grouping (lora_segment) and the 196 module applies
-(lora_apply_batched on that grouping: shrink, then expand), inputs resident
-in HBM.  A step streams ~50 GB, 200 times the 256 MB last-level cache, so it
+that batch: one token grouping with its plan of sub-tiles (lora_group) and
+the 196 module applies on that plan (lora_apply_planned: shrink, then
+expand), inputs resident in HBM.  A step streams ~50 GB, 200 times the 256 MB last-level cache, so it
 reads its factors and activations from HBM by construction.
 
 `--config 1|2|3|4` times one lora_apply_batched call with ids of the smaller
@@ -86,9 +86,11 @@ WORKLOAD_NAMES = {
     "ranks-fleet": "retained-rank allocation on the host: 1024 adapters x 196 modules (200704 units) of "
                    "original rank 64, uniform (ratio 1/12, floor 4) and spectral at the same budget",
     "5U": "fleet decode step: 28 layers x 7 projections (3584/512/18944 dims) bf16, 1024 adapters rank 6 "
-          "(orig 64), T=4096 Zipf(1.1) ids, one grouping reused by 196 applies (q/k/v and gate/up concurrent)",
+          "(orig 64), T=4096 Zipf(1.1) ids, one grouping and plan reused by 196 applies (q/k/v and gate/up "
+          "concurrent)",
     "5S": "fleet decode step: 28 layers x 7 projections (3584/512/18944 dims) bf16, 1024 adapters ranks "
-          "4..16 per module, T=4096 Zipf(1.1) ids, one grouping reused by 196 applies (q/k/v and gate/up concurrent)",
+          "4..16 per module, T=4096 Zipf(1.1) ids, one grouping and plan reused by 196 applies (q/k/v and gate/up "
+          "concurrent)",
 }
 
 
@@ -862,7 +864,8 @@ def fleet_stages(meta):
 
 
 def fleet_step(rs, torch, stores, meta, xs, ys, ids, seg, n, nstr, str_ws):
-    """One decode step: the grouping, then every module's apply on it.  The
+    """One decode step: the grouping and its plan (lora_group), then every
+    module's apply on that plan (lora_apply_planned).  The
     modules of a stage go to up to nstr streams (default priority, one
     workspace each); a stage starts when the previous one has finished, as in
     a forward pass, where each stage's input comes from the one before."""
@@ -870,10 +873,10 @@ def fleet_step(rs, torch, stores, meta, xs, ys, ids, seg, n, nstr, str_ws):
     side = [torch.cuda.Stream() for _ in range(nstr - 1)]
 
     def step():
-        rs.lora_segment(ids, n, seg=seg)
+        rs.lora_group(ids, n, seg=seg)  # the grouping and its plan, once per step
         if nstr == 1:
             for st, m, y in zip(stores, meta, ys):
-                rs.lora_apply_batched(st, xs[(m[0], m[5])], y, seg=seg, ws=str_ws[0])
+                rs.lora_apply_planned(st, xs[(m[0], m[5])], y, seg, ws=str_ws[0])
             return
         main = torch.cuda.current_stream()
         for stage in stages:
@@ -882,7 +885,7 @@ def fleet_step(rs, torch, stores, meta, xs, ys, ids, seg, n, nstr, str_ws):
             for k, i in enumerate(stage):
                 m = meta[i]
                 with torch.cuda.stream(main if k % nstr == 0 else side[k % nstr - 1]):
-                    rs.lora_apply_batched(stores[i], xs[(m[0], m[5])], ys[i], seg=seg, ws=str_ws[k % nstr])
+                    rs.lora_apply_planned(stores[i], xs[(m[0], m[5])], ys[i], seg, ws=str_ws[k % nstr])
             for s in side:
                 main.wait_stream(s)
     return step
@@ -895,7 +898,7 @@ def run_fleet_key(args, rs, torch, dev, key, xs, ys, ids, full: bool):
     _, per_mod, seg_bytes = fleet_algorithmic(key, T, n)
     step_bytes = seg_bytes + sum(b["total"] for b in per_mod)
     stores, meta = build_fleet(rs, torch, key, dev, False)
-    seg = rs.lora_segment(ids, n)
+    seg = rs.lora_group(ids, n)
     nstr = max(1, args.streams)
     wsb = max(rs.lora_workspace_bytes(st, T) for st in stores)
     str_ws = [torch.empty(wsb, dtype=torch.uint8, device=dev) for _ in range(nstr)]
@@ -921,7 +924,7 @@ def run_fleet_key(args, rs, torch, dev, key, xs, ys, ids, full: bool):
         def phase_step(ph):
             def f():
                 for st, m, y, w in zip(stores, meta, ys, mod_ws):
-                    rs.lora_apply_batched_phases(st, xs[(m[0], m[5])], y, ph, seg=seg, ws=w)
+                    rs.lora_apply_planned(st, xs[(m[0], m[5])], y, seg, ws=w, phases=ph)
             return f
 
         reps = max(MIN_SEGMENTS, min(K, 10))
@@ -955,12 +958,12 @@ def run_fleet_key(args, rs, torch, dev, key, xs, ys, ids, full: bool):
         mws = torch.empty(mbytes, dtype=torch.uint8, device=dev)
 
         def step_multi():
-            rs.lora_segment(ids, n, seg=seg)
+            rs.lora_group(ids, n, seg=seg)
             for g, idx in groups.items():
                 if len(idx) > 1:
                     rs.lora_apply_multi(mstores[g], xs[g], [ys[j] for j in idx], seg=seg, ws=mws)
                 else:
-                    rs.lora_apply_batched(stores[idx[0]], xs[g], ys[idx[0]], seg=seg, ws=mws)
+                    rs.lora_apply_planned(stores[idx[0]], xs[g], ys[idx[0]], seg, ws=mws)
 
         saved = sum(T * meta[idx[0]][3] * 2 * (len(idx) - 1) for idx in groups.values())
         mt = time_replays(torch, step_multi, K, 1, graph)

@@ -173,11 +173,33 @@ int lora_segment(const int32_t* ids, int T, int n, int32_t* seg_off, int32_t* pe
                  void* stream);
 
 /*
- * Workspace of lora_shrink, lora_expand and lora_apply_batched for T tokens
- * on this store (host only; 0 on invalid arguments).  It holds the work plan
- * (sub-tiles of at most 16 tokens of one adapter) and the shrink's float32
- * partial sums; the contents need no initialization and are scratch after
- * the call.  One workspace must not be shared by calls in flight together.
+ * The plan of a grouping: its sub-tiles (runs of at most 16 tokens of one
+ * adapter, in grouped order), each with its adapter, first grouped
+ * position, token count and token indices.  It depends on the grouping only
+ * (not on a store), so one plan serves every store over the same adapters,
+ * e.g. all the projections of a decode step, which then skip forming it
+ * ("Compress then Serve" section 2: the requests of one adapter are grouped
+ * once).
+ * lora_plan_bytes: bytes of a plan for T tokens over n adapters (host only;
+ *   0 on invalid arguments).
+ * lora_group: lora_segment plus the plan, in one launch where T <= 8192 and
+ *   n <= 2048 (else the sort, then a plan launch).  plan: caller buffer of
+ *   at least lora_plan_bytes(T, n) bytes, 16-byte aligned.  Other arguments
+ *   and errors as lora_segment, plus INVALID_ARG for a null or small plan
+ *   buffer and UNSUPPORTED for a misaligned one.
+ */
+size_t lora_plan_bytes(int T, int n);
+int lora_group(const int32_t* ids, int T, int n, int32_t* seg_off, int32_t* perm, void* plan, size_t plan_bytes,
+               int32_t* n_invalid, void* stream);
+
+/*
+ * Workspace of lora_shrink, lora_expand and the applies for T tokens on this
+ * store (host only; 0 on invalid arguments).  It holds each sub-tile's
+ * metadata for this store, the shrink's float32 partial sums, and the plan
+ * (and, beyond the one-launch grouping's size, seg_off and perm) of a call
+ * that forms its own grouping; the contents need no initialization and are
+ * scratch after the call.  One workspace must not be shared by calls in
+ * flight together.
  */
 size_t lora_workspace_bytes(const lora_store* store_host, int T);
 
@@ -216,19 +238,20 @@ int lora_expand(const lora_store* store_host, const float* h, int64_t ldh, int T
 
 /*
  * The batched apply:  y[t] += s_a * B_a (A_a x[t])  for every token.
- * Either ids (the grouping is then formed inside the kernel), or ids = NULL
- * and seg_off / perm from lora_segment (one grouping reused across many
- * stores, e.g. every projection of a decode step).
+ * Either ids, or ids = NULL and seg_off / perm from lora_segment.  (To reuse
+ * one grouping across many stores, form its plan once with lora_group and
+ * call lora_apply_planned.)
  * Decode-sized calls with ids (lora_apply_launches returns 1) run as one
  * kernel, a workgroup per (token, slice of the output features): it reads
  * the token's adapter from ids, reduces h over all of d_in (float32, a fixed
  * order) and adds the delta into that slice of the token's y row (the
  * per-token indexed form of the same two steps: section 13.4 of the Compress
- * then Serve page).  Other calls run as two kernels: the shrink (grouping +
- * float32 partial sums over chunks of d_in, in the workspace) and the expand
- * (partials summed in chunk order, then y updated); their result equals
- * lora_segment + lora_shrink + lora_expand bit for bit.  The two forms sum h
- * in different orders, so on float data they agree to float32 rounding.
+ * then Serve page).  Other calls run as three kernels: the grouping (the plan
+ * of sub-tiles, into the workspace), the shrink (float32 partial sums over
+ * chunks of d_in) and the expand (partials summed in chunk order, then y
+ * updated); their result equals lora_segment + lora_shrink + lora_expand bit
+ * for bit.  The two forms sum h in different orders, so on float data they
+ * agree to float32 rounding.
  * Errors: union of those calls'.
  */
 int lora_apply_batched(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy,
@@ -261,10 +284,10 @@ int lora_apply_batched_noalloc(const lora_store* store_host, const void* x, int6
 
 /*
  * One kernel of lora_apply_batched at a time, for measuring each alone:
- * phases = 1 runs the shrink only (grouping, partial sums and plan into ws;
- * with ids and n > 4096 also the sort), 2 the expand only (from the plan and
- * partial sums a previous phase-1 call left in ws, for the same store, T and
- * grouping; plan entries that do not fit this store are skipped, so a
+ * phases = 1 forms the plan and runs the shrink (partial sums and each
+ * sub-tile's metadata into ws), 2 the expand only (from the plan, metadata
+ * and partial sums a previous phase-1 call left in ws, for the same store, T
+ * and grouping; metadata that does not fit this store is skipped, so a
  * mismatched workspace gives wrong values, never an access outside the
  * store's buffers), 3 = lora_apply_batched (the one-kernel form for
  * decode-sized calls with ids).  Phases 1 and 2 always run the two-kernel
@@ -276,14 +299,33 @@ int lora_apply_batched_phases(const lora_store* store_host, const void* x, int64
                               const int32_t* perm, void* ws, size_t ws_bytes, void* stream, int phases);
 
 /*
- * Kernel launches lora_apply_batched enqueues for this store, T and kind of
- * grouping (host only, nothing enqueued): 1 for the one-kernel decode form
- * (ids given, T <= 512, r_max <= 8 for bf16 or <= 4 for f32, d_in <= 4096
- * for bf16 or <= 2048 for f32), 2 for the shrink and the expand, 3 when the
- * sort precedes them (ids given and n > 4096), 0 for T = 0.  with_ids:
- * nonzero if ids are passed, 0 for a prior grouping.  A negative value is
- * -(the status the apply would return): an invalid store or T, or
- * UNSUPPORTED sizes.
+ * The batched apply on a plan from lora_group (same T, and n = store->n):
+ * the shrink and the expand only, so that a grouping formed once serves many
+ * stores (every projection of a decode step).  plan_bytes: the plan buffer's
+ * size.  lora_apply_planned_phases runs one of them at a time, as
+ * lora_apply_batched_phases (3 = both).  A plan of another grouping gives
+ * wrong values, never an access outside the call's buffers (its entries are
+ * checked against T and the store).  Errors: as lora_apply_batched, plus
+ * INVALID_ARG for a null or small plan buffer, UNSUPPORTED for a misaligned
+ * one.
+ */
+int lora_apply_planned(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy, int T,
+                       const void* plan, size_t plan_bytes, void* ws, size_t ws_bytes, void* stream);
+int lora_apply_planned_phases(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy, int T,
+                              const void* plan, size_t plan_bytes, void* ws, size_t ws_bytes, void* stream,
+                              int phases);
+
+/*
+ * Kernel launches an apply enqueues for this store, T and kind of grouping
+ * (host only, nothing enqueued).  with_ids: 1 ids (lora_apply_batched), 0 a
+ * caller's seg_off / perm (lora_apply_batched), 2 a plan
+ * (lora_apply_planned).  Returns 1 for the one-kernel decode form (ids
+ * given, T <= 512, r_max <= 8 for bf16 or <= 4 for f32, d_in <= 4096 for
+ * bf16 or <= 2048 for f32), 2 for the shrink and the expand on a plan, 3 for
+ * the grouping (or the plan of a given grouping), the shrink and the expand,
+ * 4 when the sort precedes them (ids given, T > 8192 or n > 2048), 0 for
+ * T = 0.  A negative value is -(the status the apply would return): an
+ * invalid store, T or with_ids, or UNSUPPORTED sizes.
  */
 int lora_apply_launches(const lora_store* store_host, int T, int with_ids);
 
@@ -338,7 +380,7 @@ size_t lora_jd_workspace_bytes(const lora_jd_store* store_host, int T);
  * n_adapters) add nothing).  Errors: INVALID_ARG (null pointers, T < 0,
  * r != basis.r_max, basis.R != basis.n * r, diag not 0 or 1, workspace too
  * small); UNSUPPORTED (those of lora_apply_batched for the basis store, more
- * than 4096 clusters, T > LORA_SEGMENT_MAX_T).
+ * than 2048 clusters, T > 8192: the grouping by cluster runs in one workgroup).
  */
 int lora_jd_apply(const lora_jd_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy, int T,
                   const int32_t* ids, void* ws, size_t ws_bytes, void* stream);
@@ -411,6 +453,11 @@ size_t lora_multi_workspace_bytes(const lora_multi_store* store_host, int T);
 int lora_apply_multi(const lora_multi_store* store_host, const void* x, int64_t ldx, void* const* y_host,
                      const int64_t* ldy_host, int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm,
                      void* ws, size_t ws_bytes, void* stream);
+/* The same on a plan from lora_group (n = the multi store's n), as
+ * lora_apply_planned. */
+int lora_apply_multi_planned(const lora_multi_store* store_host, const void* x, int64_t ldx, void* const* y_host,
+                             const int64_t* ldy_host, int T, const void* plan, size_t plan_bytes, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /*
  * Retained-rank allocation (host only, nothing enqueued): how many ranks each

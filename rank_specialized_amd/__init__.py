@@ -26,7 +26,7 @@ from ._lib import LoraError, lora_store  # noqa: F401
 
 __all__ = [
     "Store", "Segmentation", "LoraError", "lora_store_bytes", "lora_pack_retained",
-    "lora_segment", "lora_workspace_bytes", "lora_shrink", "lora_expand", "lora_apply_batched",
+    "lora_segment", "lora_plan_bytes", "lora_group", "lora_apply_planned", "lora_workspace_bytes", "lora_shrink", "lora_expand", "lora_apply_batched",
     "lora_apply_batched_phases", "lora_apply_batched_noalloc", "lora_apply_launches", "JDStore", "lora_jd_pack", "lora_jd_workspace_bytes",
     "lora_jd_apply", "lora_ranks_uniform", "lora_ranks_spectral", "RsvdFactors", "lora_rsvd_workspace_bytes",
     "lora_rsvd_factor", "lora_rsvd_write", "MultiStore", "lora_pack_multi", "lora_multi_workspace_bytes",
@@ -163,6 +163,7 @@ class Segmentation:
     seg_off: torch.Tensor  # int32 [n + 2]
     perm: torch.Tensor  # int32 [T]
     n_invalid: Optional[torch.Tensor] = None
+    plan: Optional[torch.Tensor] = None  # uint8 [lora_plan_bytes(T, n)] (lora_group)
 
 
 def lora_segment(ids: torch.Tensor, n: int, *, seg: Optional[Segmentation] = None) -> Segmentation:
@@ -177,6 +178,29 @@ def lora_segment(ids: torch.Tensor, n: int, *, seg: Optional[Segmentation] = Non
                            torch.empty(1, dtype=torch.int32, device=dev))
     L.check("lora_segment", L.lib().lora_segment(
         _p(ids), T, n, seg.seg_off.data_ptr(), _p(seg.perm), seg.n_invalid.data_ptr(), _stream(seg.seg_off)))
+    return seg
+
+
+def lora_plan_bytes(T: int, n: int) -> int:
+    return int(L.lib().lora_plan_bytes(T, n))
+
+
+def lora_group(ids: torch.Tensor, n: int, *, seg: Optional[Segmentation] = None) -> Segmentation:
+    """lora_segment plus the plan of the grouping (its sub-tiles), which
+    lora_apply_planned reuses across stores."""
+    if ids.dtype != torch.int32 or ids.dim() != 1 or not ids.is_contiguous():
+        raise ValueError("ids must be a contiguous int32 vector")
+    T = ids.shape[0]
+    dev = ids.device
+    nb = lora_plan_bytes(T, n)
+    if seg is None or seg.plan is None:
+        seg = Segmentation(T, n, torch.empty(n + 2, dtype=torch.int32, device=dev),
+                           torch.empty(max(T, 1), dtype=torch.int32, device=dev)[:T],
+                           torch.empty(1, dtype=torch.int32, device=dev),
+                           torch.empty(max(nb, 16), dtype=torch.uint8, device=dev))
+    L.check("lora_group", L.lib().lora_group(
+        _p(ids), T, n, seg.seg_off.data_ptr(), _p(seg.perm), seg.plan.data_ptr(), seg.plan.numel(),
+        seg.n_invalid.data_ptr(), _stream(seg.seg_off)))
     return seg
 
 
@@ -276,10 +300,26 @@ def lora_apply_batched_noalloc(store: Store, x: torch.Tensor, y: torch.Tensor, *
     return y
 
 
-def lora_apply_launches(store: Store, T: int, with_ids: bool = True) -> int:
-    """Kernel launches lora_apply_batched makes for this store and T: 1 (the
-    fused decode kernel), 2 (shrink, expand) or 3 (sort, shrink, expand)."""
-    v = L.lib().lora_apply_launches(store.ref(), int(T), 1 if with_ids else 0)
+def lora_apply_planned(store: Store, x: torch.Tensor, y: torch.Tensor, seg: Segmentation, *,
+                       ws: Optional[torch.Tensor] = None, phases: int = 3) -> torch.Tensor:
+    """y[t] += s_a B_a (A_a x[t]) in place on the plan of ``seg`` (from
+    lora_group): the shrink and the expand only (phases 1 / 2: one of them)."""
+    T = x.shape[0]
+    if seg.plan is None:
+        raise ValueError("seg has no plan (use lora_group)")
+    ws = _ws(store, T, ws, x.device)
+    L.check("lora_apply_planned_phases", L.lib().lora_apply_planned_phases(
+        store.ref(), _p(x), _rows(x, "x"), _p(y), _rows(y, "y"), T, seg.plan.data_ptr(), seg.plan.numel(),
+        ws.data_ptr(), ws.numel(), _stream(x), phases))
+    return y
+
+
+def lora_apply_launches(store: Store, T: int, with_ids=True) -> int:
+    """Kernel launches an apply makes for this store and T: with_ids True / 1
+    (ids), False / 0 (a caller's seg_off, perm), 2 (a plan).  1 = the fused
+    decode kernel, 2 = shrink + expand, 3 = grouping + shrink + expand,
+    4 = sort + plan + shrink + expand."""
+    v = L.lib().lora_apply_launches(store.ref(), int(T), int(with_ids))
     if v < 0:
         L.check("lora_apply_launches", -v)
     return v
@@ -506,7 +546,8 @@ def lora_multi_workspace_bytes(store: MultiStore, T: int) -> int:
 def lora_apply_multi(store: MultiStore, x: torch.Tensor, ys: Sequence[torch.Tensor], ids=None,
                      seg: Optional[Segmentation] = None, ws: Optional[torch.Tensor] = None):
     """y_s += s B_s A_s x for every slice, x read once; ys may be column
-    slices of one fused buffer (row stride taken from each view)."""
+    slices of one fused buffer (row stride taken from each view).  A ``seg``
+    from lora_group carries a plan, which is then used as it is."""
     T = x.shape[0]
     k = store.n_slices
     if len(ys) != k:
@@ -519,6 +560,11 @@ def lora_apply_multi(store: MultiStore, x: torch.Tensor, ys: Sequence[torch.Tens
         raise ValueError("ids must be a contiguous int32 vector")
     if ws is None:
         ws = torch.empty(max(lora_multi_workspace_bytes(store, T), 16), dtype=torch.uint8, device=x.device)
+    if seg is not None and seg.plan is not None:
+        L.check("lora_apply_multi_planned", L.lib().lora_apply_multi_planned(
+            store.ref(), _p(x), _rows(x, "x"), yp, ld, T, seg.plan.data_ptr(), seg.plan.numel(), ws.data_ptr(),
+            ws.numel(), _stream(x)))
+        return ys
     so = seg.seg_off if seg is not None else None
     pm = seg.perm if seg is not None else None
     L.check("lora_apply_multi", L.lib().lora_apply_multi(

@@ -61,12 +61,16 @@ SIGNATURES = {
     "lora_store_bytes": (I, [I, I, I, I, P, I, C.POINTER(SZ), C.POINTER(SZ), C.POINTER(SZ)]),
     "lora_pack_retained": (I, [C.POINTER(lora_store), I, I, I, I, P, P, P, P, P, P, P, I, P]),
     "lora_segment": (I, [P, I, I, P, P, P, P]),
+    "lora_plan_bytes": (SZ, [I, I]),
+    "lora_group": (I, [P, I, I, P, P, P, SZ, P, P]),
     "lora_workspace_bytes": (SZ, [C.POINTER(lora_store), I]),
     "lora_shrink": (I, [C.POINTER(lora_store), P, I64, I, P, P, P, I64, P, SZ, P]),
     "lora_expand": (I, [C.POINTER(lora_store), P, I64, I, P, P, P, I64, P, SZ, P]),
     "lora_apply_batched": (I, [C.POINTER(lora_store), P, I64, P, I64, I, P, P, P, P, SZ, P]),
     "lora_apply_batched_phases": (I, [C.POINTER(lora_store), P, I64, P, I64, I, P, P, P, P, SZ, P, I]),
     "lora_apply_batched_noalloc": (I, [C.POINTER(lora_store), P, I64, P, I64, I, P, P, P, P]),
+    "lora_apply_planned": (I, [C.POINTER(lora_store), P, I64, P, I64, I, P, SZ, P, SZ, P]),
+    "lora_apply_planned_phases": (I, [C.POINTER(lora_store), P, I64, P, I64, I, P, SZ, P, SZ, P, I]),
     "lora_apply_launches": (I, [C.POINTER(lora_store), I, I]),
     "lora_jd_workspace_bytes": (SZ, [C.POINTER(lora_jd_store), I]),
     "lora_jd_apply": (I, [C.POINTER(lora_jd_store), P, I64, P, I64, I, P, P, SZ, P]),
@@ -80,6 +84,7 @@ SIGNATURES = {
     "lora_pack_multi": (I, [C.POINTER(lora_multi_store), I, P, P, P, P, P]),
     "lora_multi_workspace_bytes": (SZ, [C.POINTER(lora_multi_store), I]),
     "lora_apply_multi": (I, [C.POINTER(lora_multi_store), P, I64, P, P, I, P, P, P, P, SZ, P]),
+    "lora_apply_multi_planned": (I, [C.POINTER(lora_multi_store), P, I64, P, P, I, P, SZ, P, SZ, P]),
 }
 
 _lib = None

@@ -35,7 +35,7 @@ const char* lora_status_string(int status) {
 
 int lora_last_hip_error(void) { return g_last_hip; }
 
-int lora_abi_version(void) { return 3; }
+int lora_abi_version(void) { return 4; }
 
 int lora_store_bytes(int n, int d_in, int d_out, int dtype, const int32_t* ranks_host, int pad_to,
                      size_t* a_bytes_host, size_t* b_bytes_host, size_t* meta_bytes_host) {
@@ -121,17 +121,74 @@ int lora_segment(const int32_t* ids, int T, int n, int32_t* seg_off, int32_t* pe
                  void* stream) {
   int st = check_segment_args(ids, T, n, seg_off, perm);
   if (st != LORA_OK) return st;
-  int max_lds = 0;  // of the current device
-  hipError_t e = device_attribute<hipDeviceAttributeMaxSharedMemoryPerBlock>(&max_lds);
-  if (e != hipSuccess) return hip_fail(e);
-  if (segment_lds_bytes(T, n) + segment_static_lds_bytes() > (size_t)max_lds) return LORA_ERR_UNSUPPORTED;
-  e = launch_segment(ids, T, n, seg_off, perm, n_invalid, reinterpret_cast<hipStream_t>(stream));
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (group_fits(T, n)) {
+    e = launch_group(ids, T, n, nullptr, 0, seg_off, perm, nullptr, n_invalid, strm);
+  } else {
+    int max_lds = 0;  // of the current device
+    e = device_attribute<hipDeviceAttributeMaxSharedMemoryPerBlock>(&max_lds);
+    if (e != hipSuccess) return hip_fail(e);
+    if (segment_lds_bytes(T, n) + segment_static_lds_bytes() > (size_t)max_lds) return LORA_ERR_UNSUPPORTED;
+    e = launch_segment(ids, T, n, seg_off, perm, n_invalid, strm);
+  }
+  return e == hipSuccess ? LORA_OK : hip_fail(e);
+}
+
+size_t lora_plan_bytes(int T, int n) {
+  if (T < 0 || n < 1) return 0;
+  return plan_bytes(T, n);
+}
+
+static int check_plan(const void* plan, size_t plan_bytes_, int T, int n) {
+  if (T == 0) return LORA_OK;
+  if (plan == nullptr || plan_bytes_ < plan_bytes(T, n)) return LORA_ERR_INVALID_ARG;
+  if (!aligned16(plan)) return LORA_ERR_UNSUPPORTED;
+  return LORA_OK;
+}
+
+int lora_group(const int32_t* ids, int T, int n, int32_t* seg_off, int32_t* perm, void* plan, size_t plan_bytes_,
+               int32_t* n_invalid, void* stream) {
+  int st = check_segment_args(ids, T, n, seg_off, perm);
+  if (st != LORA_OK) return st;
+  if ((st = check_plan(plan, plan_bytes_, T, n)) != LORA_OK) return st;
+  if (T == 0) return lora_segment(ids, T, n, seg_off, perm, n_invalid, stream);
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (group_fits(T, n)) {
+    e = launch_group(ids, T, n, nullptr, 0, seg_off, perm, reinterpret_cast<char*>(plan), n_invalid, strm);
+  } else {
+    st = lora_segment(ids, T, n, seg_off, perm, n_invalid, stream);
+    if (st != LORA_OK) return st;
+    e = launch_plan(seg_off, perm, T, n, reinterpret_cast<char*>(plan), nullptr, nullptr, strm);
+  }
   return e == hipSuccess ? LORA_OK : hip_fail(e);
 }
 
 size_t lora_workspace_bytes(const lora_store* store_host, int T) {
   if (check_store(store_host) != LORA_OK) return 0;
   return workspace_bytes(store_host, T);
+}
+
+// The plan of a call's grouping, formed in ws when the caller did not pass
+// one: from ids (the grouping kernel; beyond its size, the sort and the plan
+// kernel), or from a caller's (seg_off, perm).  groups_n is the number of
+// groups (adapters, or clusters with id_map).
+static hipError_t form_plan(const lora_store& s, int groups_n, int T, const int32_t* ids, const int32_t* id_map,
+                            int id_map_n, const int32_t* seg_off, const int32_t* perm, void* ws, const char** plan,
+                            hipStream_t strm) {
+  const WsLayout L = ws_layout(T, s.n, s.d_in, s.r_max, s.dtype);
+  char* base = reinterpret_cast<char*>(ws);
+  char* pl = base + L.plan;
+  *plan = pl;
+  if (ids == nullptr) return launch_plan(seg_off, perm, T, groups_n, pl, nullptr, nullptr, strm);
+  if (group_fits(T, groups_n))
+    return launch_group(ids, T, groups_n, id_map, id_map_n, nullptr, nullptr, pl, nullptr, strm);
+  int32_t* so = reinterpret_cast<int32_t*>(base + L.seg_off);
+  int32_t* pm = reinterpret_cast<int32_t*>(base + L.perm);
+  hipError_t e = launch_segment(ids, T, groups_n, so, pm, nullptr, strm);
+  if (e != hipSuccess) return e;
+  return launch_plan(so, pm, T, groups_n, pl, nullptr, nullptr, strm);
 }
 
 int lora_shrink(const lora_store* store_host, const void* x, int64_t ldx, int T, const int32_t* seg_off,
@@ -144,8 +201,10 @@ int lora_shrink(const lora_store* store_host, const void* x, int64_t ldx, int T,
   if ((st = check_ws(store_host, T, ws, ws_bytes)) != LORA_OK) return st;
   if (T == 0) return LORA_OK;
   hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = launch_shrink(*store_host, nullptr, seg_off, perm, T, x, ldx, ws, strm);
-  if (e == hipSuccess) e = launch_reduce_partials(*store_host, T, ws, h, ldh, strm);
+  const char* plan = nullptr;
+  hipError_t e = form_plan(*store_host, store_host->n, T, nullptr, nullptr, 0, seg_off, perm, ws, &plan, strm);
+  if (e == hipSuccess) e = launch_shrink(*store_host, plan, T, x, ldx, ws, strm);
+  if (e == hipSuccess) e = launch_reduce_partials(*store_host, plan, T, ws, h, ldh, strm);
   return e == hipSuccess ? LORA_OK : hip_fail(e);
 }
 
@@ -159,8 +218,14 @@ int lora_expand(const lora_store* store_host, const float* h, int64_t ldh, int T
   if ((st = check_ws(store_host, T, ws, ws_bytes)) != LORA_OK) return st;
   if (T == 0) return LORA_OK;
   hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = launch_plan(*store_host, seg_off, perm, T, ws, strm);
-  if (e == hipSuccess) e = launch_expand(*store_host, T, ws, h, ldh, y, ldy, strm);
+  const lora_store& s = *store_host;
+  const WsLayout L = ws_layout(T, s.n, s.d_in, s.r_max, s.dtype);
+  char* base = reinterpret_cast<char*>(ws);
+  char* plan = base + L.plan;
+  // The plan and each sub-tile's metadata from the store (h is given: one
+  // partial sum).
+  hipError_t e = launch_plan(seg_off, perm, T, s.n, plan, &s, reinterpret_cast<TileMeta*>(base + L.meta), strm);
+  if (e == hipSuccess) e = launch_expand(s, plan, T, ws, h, ldh, y, ldy, strm);
   return e == hipSuccess ? LORA_OK : hip_fail(e);
 }
 
@@ -178,9 +243,13 @@ static int check_apply_args(const lora_store* store_host, const void* x, int64_t
   return LORA_OK;
 }
 
+// phases: 1 = plan (unless given) + shrink, 2 = expand (from the plan and the
+// metadata and partial sums of a phase-1 call in ws), 3 = the apply (the
+// one-kernel decode form when it fits).  `given_plan`: a caller's plan
+// (lora_group); otherwise the grouping comes from ids or (seg_off, perm).
 static int apply_impl(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy, int T,
-                      const int32_t* ids, const int32_t* seg_off, const int32_t* perm, void* ws, size_t ws_bytes,
-                      void* stream, int phases) {
+                      const int32_t* ids, const int32_t* seg_off, const int32_t* perm, const void* given_plan,
+                      void* ws, size_t ws_bytes, void* stream, int phases) {
   int st = check_store(store_host);
   if (st != LORA_OK) return st;
   const lora_store& s = *store_host;
@@ -191,36 +260,46 @@ static int apply_impl(const lora_store* store_host, const void* x, int64_t ldx, 
   if ((st = check_ws(store_host, T, ws, ws_bytes)) != LORA_OK) return st;
   if (ids != nullptr && (T > LORA_SEGMENT_MAX_T || s.n > LORA_SEGMENT_MAX_N)) return LORA_ERR_UNSUPPORTED;
   if (T == 0) return LORA_OK;  // nothing to group or apply
-  if (ids == nullptr && (st = check_grouping(store_host, T, seg_off, perm)) != LORA_OK) return st;
+  if (given_plan == nullptr && ids == nullptr && (st = check_grouping(store_host, T, seg_off, perm)) != LORA_OK)
+    return st;
   hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  if (phases == 3 && decode_apply_fits(s, T, ids != nullptr)) {
+  if (phases == 3 && given_plan == nullptr && decode_apply_fits(s, T, ids != nullptr)) {
     e = launch_decode_apply(s, ids, T, x, ldx, y, ldy, strm);
     return e == hipSuccess ? LORA_OK : hip_fail(e);
   }
-  if (phases & 1) {
-    if (ids != nullptr && s.n > kGroupMaxN) {
-      // Too many adapters for the in-shrink histogram: sort first, into ws.
-      const WsLayout L = ws_layout(T, s.n, s.d_in, s.r_max, s.dtype);
-      int32_t* so = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + L.seg_off);
-      int32_t* pm = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + L.perm);
-      st = lora_segment(ids, T, s.n, so, pm, nullptr, stream);
-      if (st != LORA_OK) return st;
-      e = launch_shrink(s, nullptr, so, pm, T, x, ldx, ws, strm);
-    } else if (ids != nullptr) {
-      e = launch_shrink(s, ids, nullptr, nullptr, T, x, ldx, ws, strm);
-    } else {
-      e = launch_shrink(s, nullptr, seg_off, perm, T, x, ldx, ws, strm);
-    }
+  const char* plan = reinterpret_cast<const char*>(given_plan);
+  if (plan == nullptr) {
+    const WsLayout L = ws_layout(T, s.n, s.d_in, s.r_max, s.dtype);
+    plan = reinterpret_cast<const char*>(ws) + L.plan;
+    if (phases & 1) e = form_plan(s, s.n, T, ids, nullptr, 0, seg_off, perm, ws, &plan, strm);
   }
-  if (e == hipSuccess && (phases & 2)) e = launch_expand(s, T, ws, nullptr, 0, y, ldy, strm);
+  if (e == hipSuccess && (phases & 1)) e = launch_shrink(s, plan, T, x, ldx, ws, strm);
+  if (e == hipSuccess && (phases & 2)) e = launch_expand(s, plan, T, ws, nullptr, 0, y, ldy, strm);
   return e == hipSuccess ? LORA_OK : hip_fail(e);
 }
 
 int lora_apply_batched(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy,
                        int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm, void* ws,
                        size_t ws_bytes, void* stream) {
-  return apply_impl(store_host, x, ldx, y, ldy, T, ids, seg_off, perm, ws, ws_bytes, stream, 3);
+  return apply_impl(store_host, x, ldx, y, ldy, T, ids, seg_off, perm, nullptr, ws, ws_bytes, stream, 3);
+}
+
+int lora_apply_planned_phases(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy, int T,
+                              const void* plan, size_t plan_bytes_, void* ws, size_t ws_bytes, void* stream,
+                              int phases) {
+  const int st = check_store(store_host);
+  if (st != LORA_OK) return st;
+  if (T < 0) return LORA_ERR_INVALID_ARG;
+  const int sp = check_plan(plan, plan_bytes_, T, store_host->n);
+  if (sp != LORA_OK) return sp;
+  return apply_impl(store_host, x, ldx, y, ldy, T, nullptr, nullptr, nullptr, T > 0 ? plan : nullptr, ws, ws_bytes,
+                    stream, phases);
+}
+
+int lora_apply_planned(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy, int T,
+                       const void* plan, size_t plan_bytes_, void* ws, size_t ws_bytes, void* stream) {
+  return lora_apply_planned_phases(store_host, x, ldx, y, ldy, T, plan, plan_bytes_, ws, ws_bytes, stream, 3);
 }
 
 // ------------------------------------------------------------ no allocation
@@ -260,8 +339,8 @@ int lora_apply_batched_noalloc(const lora_store* store_host, const void* x, int6
   void* ws = nullptr;
   hipError_t e = scratch_address(&ws);
   if (e != hipSuccess) return hip_fail(e);
-  return apply_impl(store_host, x, ldx, y, ldy, T, ids, seg_off, perm, ws, (size_t)LORA_NOALLOC_SCRATCH_BYTES,
-                    stream, 3);
+  return apply_impl(store_host, x, ldx, y, ldy, T, ids, seg_off, perm, nullptr, ws,
+                    (size_t)LORA_NOALLOC_SCRATCH_BYTES, stream, 3);
 }
 
 // Shared-basis workspace: h [T][ldp] | the basis store's workspace.
@@ -297,17 +376,19 @@ int lora_jd_apply(const lora_jd_store* store_host, const void* x, int64_t ldx, v
   if (T == 0) return LORA_OK;
   if (!ids || !ws) return LORA_ERR_INVALID_ARG;
   if (!aligned16(ws)) return LORA_ERR_UNSUPPORTED;
-  if (T > LORA_SEGMENT_MAX_T) return LORA_ERR_UNSUPPORTED;
+  if (!group_fits(T, b.n)) return LORA_ERR_UNSUPPORTED;  // the grouping by cluster runs in one workgroup
   if (ws_bytes < lora_jd_workspace_bytes(store_host, T)) return LORA_ERR_INVALID_ARG;
   char* base = reinterpret_cast<char*>(ws);
   float* h = reinterpret_cast<float*>(base);
   void* bws = base + jd_h_bytes(b, T);
   const int64_t ldh = partial_ld(b.r_max);
   hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = launch_shrink(b, ids, nullptr, nullptr, T, x, ldx, bws, strm, j.cluster_of, j.n_adapters);
+  const char* plan = nullptr;
+  hipError_t e = form_plan(b, b.n, T, ids, j.cluster_of, j.n_adapters, nullptr, nullptr, bws, &plan, strm);
+  if (e == hipSuccess) e = launch_shrink(b, plan, T, x, ldx, bws, strm);
   if (e == hipSuccess)
-    e = launch_jd_sigma(b, T, bws, ids, j.n_adapters, j.cluster_of, j.sigma, j.diag, j.scale, h, ldh, strm);
-  if (e == hipSuccess) e = launch_expand(b, T, bws, h, ldh, y, ldy, strm);
+    e = launch_jd_sigma(b, plan, T, bws, ids, j.n_adapters, j.cluster_of, j.sigma, j.diag, j.scale, h, ldh, strm);
+  if (e == hipSuccess) e = launch_expand(b, plan, T, bws, h, ldh, y, ldy, strm);
   return e == hipSuccess ? LORA_OK : hip_fail(e);
 }
 
@@ -316,16 +397,18 @@ int lora_apply_launches(const lora_store* store_host, int T, int with_ids) {
   if (st != LORA_OK) return -st;
   if (T < 0) return -LORA_ERR_INVALID_ARG;
   const lora_store& s = *store_host;
-  if (with_ids && (T > LORA_SEGMENT_MAX_T || s.n > LORA_SEGMENT_MAX_N)) return -LORA_ERR_UNSUPPORTED;
+  if (with_ids == 1 && (T > LORA_SEGMENT_MAX_T || s.n > LORA_SEGMENT_MAX_N)) return -LORA_ERR_UNSUPPORTED;
+  if (with_ids < 0 || with_ids > 2) return -LORA_ERR_INVALID_ARG;
   if (T == 0) return 0;
+  if (with_ids == 2) return 2;  // a plan: shrink, expand
   if (decode_apply_fits(s, T, with_ids != 0)) return 1;
-  return (with_ids && s.n > kGroupMaxN) ? 3 : 2;
+  return (with_ids && !group_fits(T, s.n)) ? 4 : 3;
 }
 
 int lora_apply_batched_phases(const lora_store* store_host, const void* x, int64_t ldx, void* y, int64_t ldy,
                               int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm, void* ws,
                               size_t ws_bytes, void* stream, int phases) {
-  return apply_impl(store_host, x, ldx, y, ldy, T, ids, seg_off, perm, ws, ws_bytes, stream, phases);
+  return apply_impl(store_host, x, ldx, y, ldy, T, ids, seg_off, perm, nullptr, ws, ws_bytes, stream, phases);
 }
 
 size_t lora_rsvd_workspace_bytes(int n, int d_in, int d_out) {
@@ -491,9 +574,9 @@ size_t lora_multi_workspace_bytes(const lora_multi_store* store_host, int T) {
   return workspace_bytes(&store_host->stacked, T);
 }
 
-int lora_apply_multi(const lora_multi_store* store_host, const void* x, int64_t ldx, void* const* y_host,
-                     const int64_t* ldy_host, int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm,
-                     void* ws, size_t ws_bytes, void* stream) {
+static int multi_impl(const lora_multi_store* store_host, const void* x, int64_t ldx, void* const* y_host,
+                      const int64_t* ldy_host, int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm,
+                      const void* given_plan, void* ws, size_t ws_bytes, void* stream) {
   int st = check_multi(store_host);
   if (st != LORA_OK) return st;
   const lora_multi_store& m = *store_host;
@@ -505,24 +588,33 @@ int lora_apply_multi(const lora_multi_store* store_host, const void* x, int64_t 
   if ((st = check_ws(&s, T, ws, ws_bytes)) != LORA_OK) return st;
   if (ids != nullptr && (T > LORA_SEGMENT_MAX_T || s.n > LORA_SEGMENT_MAX_N)) return LORA_ERR_UNSUPPORTED;
   if (T == 0) return LORA_OK;
-  if (ids == nullptr && (st = check_grouping(&s, T, seg_off, perm)) != LORA_OK) return st;
+  if (given_plan == nullptr && ids == nullptr && (st = check_grouping(&s, T, seg_off, perm)) != LORA_OK) return st;
   hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e;
-  if (ids != nullptr && s.n > kGroupMaxN) {
-    const WsLayout L = ws_layout(T, s.n, s.d_in, s.r_max, s.dtype);
-    int32_t* so = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + L.seg_off);
-    int32_t* pm = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + L.perm);
-    st = lora_segment(ids, T, s.n, so, pm, nullptr, stream);
-    if (st != LORA_OK) return st;
-    e = launch_shrink(s, nullptr, so, pm, T, x, ldx, ws, strm);
-  } else if (ids != nullptr) {
-    e = launch_shrink(s, ids, nullptr, nullptr, T, x, ldx, ws, strm);
-  } else {
-    e = launch_shrink(s, nullptr, seg_off, perm, T, x, ldx, ws, strm);
-  }
+  hipError_t e = hipSuccess;
+  const char* plan = reinterpret_cast<const char*>(given_plan);
+  if (plan == nullptr) e = form_plan(s, s.n, T, ids, nullptr, 0, seg_off, perm, ws, &plan, strm);
+  if (e == hipSuccess) e = launch_shrink(s, plan, T, x, ldx, ws, strm);
   for (int k = 0; e == hipSuccess && k < m.n_slices; ++k)
-    e = launch_expand_slice(s, m.slice[k], m.hoff + (size_t)k * s.n, T, ws, y_host[k], ldy_host[k], strm);
+    e = launch_expand_slice(s, m.slice[k], m.hoff + (size_t)k * s.n, plan, T, ws, y_host[k], ldy_host[k], strm);
   return e == hipSuccess ? LORA_OK : hip_fail(e);
+}
+
+int lora_apply_multi(const lora_multi_store* store_host, const void* x, int64_t ldx, void* const* y_host,
+                     const int64_t* ldy_host, int T, const int32_t* ids, const int32_t* seg_off, const int32_t* perm,
+                     void* ws, size_t ws_bytes, void* stream) {
+  return multi_impl(store_host, x, ldx, y_host, ldy_host, T, ids, seg_off, perm, nullptr, ws, ws_bytes, stream);
+}
+
+int lora_apply_multi_planned(const lora_multi_store* store_host, const void* x, int64_t ldx, void* const* y_host,
+                             const int64_t* ldy_host, int T, const void* plan, size_t plan_bytes_, void* ws,
+                             size_t ws_bytes, void* stream) {
+  const int st = check_multi(store_host);
+  if (st != LORA_OK) return st;
+  if (T < 0) return LORA_ERR_INVALID_ARG;
+  const int sp = check_plan(plan, plan_bytes_, T, store_host->stacked.n);
+  if (sp != LORA_OK) return sp;
+  return multi_impl(store_host, x, ldx, y_host, ldy_host, T, nullptr, nullptr, nullptr, T > 0 ? plan : nullptr, ws,
+                    ws_bytes, stream);
 }
 
 }  // extern "C"

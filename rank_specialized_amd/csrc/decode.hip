@@ -66,21 +66,6 @@ __device__ __forceinline__ float chunk_elem(const uint4& v, int e) {
   else return __uint_as_float(w);
 }
 
-// Sum of v over the 64 lanes of the wave, the same in every lane: sums of 2,
-// 4, 8 and 16 lanes by DPP, then the four rows' sums read from lanes 0, 16,
-// 32 and 48 and added in row order.
-__device__ __forceinline__ float wave_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));  // row_mirror
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return ((r0 + r1) + r2) + r3;
-}
-
 template <typename E, int R>
 __device__ __forceinline__ void decode_token(const DecodeArgs& p, const bool (&kv)[kDecodeChunks],
                                              const int (&kc)[kDecodeChunks], const uint4 (&xv)[kDecodeChunks],

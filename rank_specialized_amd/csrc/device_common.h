@@ -123,6 +123,72 @@ __device__ __forceinline__ f32x4_t mfma_chunk<F32>(const uint4& a, const uint4& 
   return c;
 }
 
+// ------------------------------------------------------------ partial sums
+// src[0] + src[stride] + ... + src[(S - 1) stride], added in chunk order; the
+// loads are issued kMaxChunks at a time.
+__device__ __forceinline__ float sum_partials(const float* src, int64_t stride, int S) {
+  float s = 0.f;
+  for (int k0 = 0; k0 < S; k0 += kMaxChunks) {
+    float pk[kMaxChunks];
+#pragma unroll
+    for (int k = 0; k < kMaxChunks; ++k) pk[k] = k0 + k < S ? src[(int64_t)(k0 + k) * stride] : 0.f;
+#pragma unroll
+    for (int k = 0; k < kMaxChunks; ++k)
+      if (k0 + k < S) s = (k0 + k == 0) ? pk[k] : s + pk[k];
+  }
+  return s;
+}
+
+// ------------------------------------------------------------ wave sum
+// Sum of v over the 64 lanes of the wave, the same in every lane: sums of 2,
+// 4, 8 and 16 lanes by DPP, then the four rows' sums read from lanes 0, 16,
+// 32 and 48 and added in row order.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));  // row_mirror
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return ((r0 + r1) + r2) + r3;
+}
+
+// Sums over the 64 lanes of Q values per lane (Q a power of two, 1..64), by
+// a reduce-scatter butterfly: at the exchange across lane bit d (32, 16,
+// ...) each lane keeps one half of its values and adds the partner's copy of
+// that half, so the values a lane holds halve at every step; once one is
+// left, plain exchanges finish the sum.  On return v[0] of lane l is the sum
+// of value l >> (6 - log2 Q) over all lanes (a fixed order, the same in
+// every lane).  Q + 6 - log2 Q - 1 exchanges in all.
+template <int Q, int D, int CNT>
+__device__ __forceinline__ void reduce_scatter_step(float (&v)[Q], int lane) {
+  if constexpr (D >= 1) {
+    if constexpr (CNT > 1) {
+      constexpr int H = CNT / 2;
+      const bool upper = (lane & D) != 0;
+#pragma unroll
+      for (int i = 0; i < H; ++i) {
+        const float send = upper ? v[i] : v[i + H];
+        const float keep = upper ? v[i + H] : v[i];
+        v[i] = keep + __shfl_xor(send, D);
+      }
+      reduce_scatter_step<Q, D / 2, H>(v, lane);
+    } else {
+      v[0] += __shfl_xor(v[0], D);
+      reduce_scatter_step<Q, D / 2, 1>(v, lane);
+    }
+  }
+}
+
+template <int Q>
+__device__ __forceinline__ float wave_reduce_scatter(float (&v)[Q]) {
+  static_assert(Q >= 1 && Q <= 64 && (Q & (Q - 1)) == 0, "Q is a power of two up to 64");
+  reduce_scatter_step<Q, 32, Q>(v, threadIdx.x & 63);
+  return v[0];
+}
+
 // ------------------------------------------------------------ block scan
 __device__ __forceinline__ uint64_t lanemask_lt() { return (1ull << __lane_id()) - 1ull; }
 

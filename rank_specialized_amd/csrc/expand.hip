@@ -41,7 +41,9 @@
 // The path is instantiated per exact rank, so the unpacking of the B block
 // is static.  Both paths live in one kernel: a sub-tile owns `slots`
 // consecutive waves and its entry decides which path they take (waves a path
-// does not need return at once), so the plan is read in one launch.
+// does not need return at once), so the plan is read in one launch.  A
+// sub-tile's rank, row offset, scale and partial count come from the
+// metadata the shrink recorded beside the plan, read with the entry.
 #include "device_common.h"
 #include "kernels.h"
 #include "tile_ops.h"
@@ -55,6 +57,7 @@ struct ExpandArgs {
   int fbn;    // kExpandCols-feature blocks (matrix path)
   int fbv;    // kVecCols-feature blocks (vector path)
   int n, r_max, R, S_max;  // the store's bounds: plan entries outside them are skipped
+  const TileMeta* meta;    // per sub-tile: rank, row offset, scale, partial count (from the shrink)
   const float* hsrc;      // partial sums (kPart) or h
   int64_t ldh, hstride;   // floats
   const char* plan;
@@ -232,13 +235,12 @@ __device__ __forceinline__ void expand_run(const ExpandArgs& p, const TileEntry*
   }
 }
 
-// Plan entry st checked against the store (an entry left in the workspace by
-// a call on another store is skipped): every B row and partial sum it names
-// then lies inside the store's and the workspace's buffers.
-__device__ __forceinline__ bool entry_fits(const ExpandArgs& p, const TileEntry* ent, int S) {
-  const int a = ent->a, m = ent->m, r = ent->r, ro = ent->row_off;
-  return (unsigned)a < (unsigned)p.n && m > 0 && m <= kSubTile && r > 0 && r <= p.r_max && ro >= 0 &&
-         ro <= p.R - r && S > 0 && S <= p.S_max;
+// Sub-tile st checked against T and the store (metadata left in the
+// workspace by a call on another store is skipped): every token, B row and
+// partial sum it names then lies inside the call's buffers.
+__device__ __forceinline__ bool entry_fits(const ExpandArgs& p, int a, int m, int pos0, const TileMeta& tm) {
+  return (unsigned)a < (unsigned)p.n && m > 0 && m <= kSubTile && pos0 >= 0 && pos0 <= p.T - m && tm.r > 0 &&
+         tm.r <= p.r_max && tm.row_off >= 0 && tm.row_off <= p.R - tm.r && tm.S > 0 && tm.S <= p.S_max;
 }
 
 // ------------------------------------------------------------ vector path
@@ -283,16 +285,9 @@ __device__ __forceinline__ void expand_vec_item(const ExpandArgs& p, const TileE
       const int row = pos0 + t0 + t;
       if (row >= 0 && row < p.T) {
         const float* src = p.hsrc + (int64_t)row * p.ldh + hoff + j;
-        hv = src[0];
-        if (kPart) {
-          // All S loads issued together (S <= kMaxChunks), summed in chunk order.
-          float pk[kMaxChunks - 1];
-#pragma unroll
-          for (int k = 1; k < kMaxChunks; ++k) pk[k - 1] = k < S ? src[(int64_t)k * p.hstride] : 0.f;
-#pragma unroll
-          for (int k = 1; k < kMaxChunks; ++k)
-            if (k < S) hv += pk[k - 1];
-        }
+        // The S partial sums in chunk order (their loads issued together,
+        // eight at a time), or h.
+        hv = kPart ? sum_partials(src, p.hstride, S) : src[0];
       }
     }
   }
@@ -347,11 +342,12 @@ __device__ __forceinline__ void expand_wave(const ExpandArgs& p) {
   const int count = *reinterpret_cast<const int32_t*>(p.plan);
   if (st >= count) return;
   const TileEntry* ent = reinterpret_cast<const TileEntry*>(p.plan + kPlanHeaderBytes) + st;
-  const int S = kPart ? ent->S : 1;
-  if (!entry_fits(p, ent, S)) return;
+  const TileMeta tm = p.meta[st];
   const int m = ent->m, pos0 = ent->pos0;
-  int r = ent->r, ro = ent->row_off, hoff = 0;
-  float sc = ent->scale;
+  if (!entry_fits(p, ent->a, m, pos0, tm)) return;
+  const int S = kPart ? tm.S : 1;
+  int r = tm.r, ro = tm.row_off, hoff = 0;
+  float sc = tm.scale;
   if constexpr (kSlice) {  // slice mode: this slice's rank, B rows, scale and h columns
     const int a = ent->a;
     const int r2 = p.sl_rank[a], ro2 = p.sl_row_off[a], h2 = p.sl_hoff[a];
@@ -426,9 +422,9 @@ static hipError_t launch_expand_kernel(int dtype, bool part, bool slice, dim3 gr
   return hipGetLastError();
 }
 
-static hipError_t launch_expand_impl(const lora_store& s, const lora_store* slice, const int32_t* hoff, int T,
-                                     const void* ws, const float* h, int64_t ldh, void* y, int64_t ldy,
-                                     hipStream_t stream) {
+static hipError_t launch_expand_impl(const lora_store& s, const lora_store* slice, const int32_t* hoff,
+                                     const char* plan, int T, const void* ws, const float* h, int64_t ldh, void* y,
+                                     int64_t ldy, hipStream_t stream) {
   const int64_t max_sub = plan_max_subtiles(T, s.n);
   if (max_sub == 0) return hipSuccess;
   const WsLayout L = ws_layout(T, s.n, s.d_in, s.r_max, s.dtype);
@@ -440,11 +436,12 @@ static hipError_t launch_expand_impl(const lora_store& s, const lora_store* slic
   a.T = T;
   a.max_sub = (int)max_sub;
   a.fbn = (out.d_out + kExpandCols - 1) / kExpandCols;
-  a.plan = base + L.plan;
+  a.plan = plan;
+  a.meta = reinterpret_cast<const TileMeta*>(base + L.meta);
   a.n = s.n;
   a.r_max = s.r_max;
   a.R = s.R;
-  a.S_max = shrink_split(s.d_in, s.r_max, s.dtype).S_max;
+  a.S_max = shrink_split(s.d_in, s.dtype).S;
   a.y = reinterpret_cast<char*>(y);
   a.ldy_bytes = ldy * elem_bytes(s.dtype);
   a.sl_rank = slice ? slice->rank : nullptr;
@@ -479,14 +476,14 @@ static hipError_t launch_expand_impl(const lora_store& s, const lora_store* slic
              : launch_expand_kernel<1>(s.dtype, part, slice != nullptr, grid, block, stream, a);
 }
 
-hipError_t launch_expand(const lora_store& s, int T, const void* ws, const float* h, int64_t ldh, void* y,
-                         int64_t ldy, hipStream_t stream) {
-  return launch_expand_impl(s, nullptr, nullptr, T, ws, h, ldh, y, ldy, stream);
+hipError_t launch_expand(const lora_store& s, const char* plan, int T, const void* ws, const float* h, int64_t ldh,
+                         void* y, int64_t ldy, hipStream_t stream) {
+  return launch_expand_impl(s, nullptr, nullptr, plan, T, ws, h, ldh, y, ldy, stream);
 }
 
-hipError_t launch_expand_slice(const lora_store& stacked, const lora_store& slice, const int32_t* hoff, int T,
-                               const void* ws, void* y, int64_t ldy, hipStream_t stream) {
-  return launch_expand_impl(stacked, &slice, hoff, T, ws, nullptr, 0, y, ldy, stream);
+hipError_t launch_expand_slice(const lora_store& stacked, const lora_store& slice, const int32_t* hoff,
+                               const char* plan, int T, const void* ws, void* y, int64_t ldy, hipStream_t stream) {
+  return launch_expand_impl(stacked, &slice, hoff, plan, T, ws, nullptr, 0, y, ldy, stream);
 }
 
 }  // namespace lora

@@ -10,8 +10,8 @@
 //
 // Here the clusters are the "adapters" of an ordinary store (A rows = V_j^T,
 // B block = U_j, every rank r, scale 1): the shrink groups the tokens by the
-// cluster of their adapter (its ids mapped through cluster_of) and the
-// expand runs unchanged; between them, jd_sigma_kernel takes each token of
+// cluster of their adapter (the grouping kernel maps the ids through
+// cluster_of) and the expand runs unchanged; between them, jd_sigma_kernel takes each token of
 // each planned sub-tile: h = the shrink's partial sums (chunk order), then
 // g = s_a Sigma_a h, written as the expand's h.
 #include "device_common.h"
@@ -21,6 +21,7 @@ namespace lora {
 
 struct SigmaArgs {
   const char* plan;
+  const TileMeta* meta;  // per sub-tile, from the shrink
   int max_sub, k, r, S_max;  // the basis store's bounds: entries outside them are skipped
   const float* part;
   int64_t ldp, pstride;
@@ -59,7 +60,8 @@ __global__ void __launch_bounds__(256) jd_sigma_kernel(SigmaArgs p) {
   if (st >= p.max_sub) return;
   if (st >= *reinterpret_cast<const int32_t*>(p.plan)) return;
   const TileEntry* e = reinterpret_cast<const TileEntry*>(p.plan + kPlanHeaderBytes) + st;
-  const int c = e->a, m = e->m, r = e->r, S = e->S, pos0 = e->pos0;
+  const TileMeta tm = p.meta[st];
+  const int c = e->a, m = e->m, r = tm.r, S = tm.S, pos0 = e->pos0;
   if ((unsigned)c >= (unsigned)p.k || m <= 0 || m > kSubTile || r != p.r || S <= 0 || S > p.S_max || i >= m)
     return;
   const int row = pos0 + i, t = e->tok[i];
@@ -70,13 +72,7 @@ __global__ void __launch_bounds__(256) jd_sigma_kernel(SigmaArgs p) {
   float h = 0.f;
   if (lane < r) {
     const float* src = p.part + (int64_t)row * p.ldp + lane;
-    float pk[kMaxChunks];
-#pragma unroll
-    for (int q = 0; q < kMaxChunks; ++q) pk[q] = q < S ? src[(int64_t)q * p.pstride] : 0.f;
-    h = pk[0];
-#pragma unroll
-    for (int q = 1; q < kMaxChunks; ++q)
-      if (q < S) h += pk[q];
+    h = sum_partials(src, p.pstride, S);
   }
   const float s = p.scale[a];
   float g;
@@ -92,7 +88,8 @@ __global__ void __launch_bounds__(256) jd_sigma_kernel(SigmaArgs p) {
   if (lane < r) p.h[(int64_t)row * p.ldh + lane] = g;
 }
 
-hipError_t launch_jd_sigma(const lora_store& basis, int T, const void* ws, const int32_t* ids, int n,
+hipError_t launch_jd_sigma(const lora_store& basis, const char* plan, int T, const void* ws, const int32_t* ids,
+                           int n,
                            const int32_t* cluster_of, const float* sigma, int diag, const float* scale, float* h,
                            int64_t ldh, hipStream_t stream) {
   const int64_t max_sub = plan_max_subtiles(T, basis.n);
@@ -100,11 +97,12 @@ hipError_t launch_jd_sigma(const lora_store& basis, int T, const void* ws, const
   const WsLayout L = ws_layout(T, basis.n, basis.d_in, basis.r_max, basis.dtype);
   const char* base = reinterpret_cast<const char*>(ws);
   SigmaArgs a;
-  a.plan = base + L.plan;
+  a.plan = plan;
+  a.meta = reinterpret_cast<const TileMeta*>(base + L.meta);
   a.max_sub = (int)max_sub;
   a.k = basis.n;
   a.r = basis.r_max;
-  a.S_max = shrink_split(basis.d_in, basis.r_max, basis.dtype).S_max;
+  a.S_max = shrink_split(basis.d_in, basis.dtype).S;
   a.part = reinterpret_cast<const float*>(base + L.part);
   a.ldp = partial_ld(basis.r_max);
   a.pstride = (int64_t)T * a.ldp;

@@ -13,15 +13,19 @@ namespace lora {
 // order: one 16-wide block of a matrix-core tile.
 constexpr int kSubTile = 16;
 
-// The shrink's workgroup: 8 waves share one (sub-tile, K chunk) item; two
-// workgroups fit on a CU, so one's grouping and reduction overlap the
-// other's loads.
+// The shrink's workgroup: 8 waves share one work item (a sub-tile and a chunk
+// of d_in), each wave taking an equal span of the chunk, and their float32
+// sums meet in LDS.  Two workgroups fit on a CU, so one's reduction overlaps
+// the other's loads.
 constexpr int kShrinkWaves = 8;
 constexpr int kShrinkThreads = kShrinkWaves * 64;
 
-// The shrink groups tokens itself (histogram of the ids in LDS) when
-// n <= kGroupMaxN; beyond that the apply first runs the single-workgroup sort.
-constexpr int kGroupMaxN = 4096;
+// The grouping kernel (one workgroup: a stable counting sort of the ids and
+// the sub-tile plan, in LDS) handles T <= kGroupMaxT and n <= kGroupMaxN;
+// larger groupings use the radix sort and a plan kernel.
+constexpr int kGroupMaxN = 2048;
+constexpr int kGroupMaxT = 8192;
+constexpr int kGroupWaves = 8;
 
 // The expand's wave covers kExpandCols output features of one sub-tile.
 constexpr int kExpandCols = 128;
@@ -42,6 +46,12 @@ constexpr int kVecMaxRank = 8;
 constexpr int kVecMaxTokens = 8;
 constexpr int kVecTokens = 4;
 constexpr int kVecCols = 512;
+// Sub-tiles of at most kGemvMaxTokens tokens and rank at most kVecMaxRank
+// (bf16; half that for float32) take the shrink's wavefront-reduction path:
+// lanes split d_in, every load is a fully used 16-byte chunk of x or A, and
+// the r x m dot products are reduced across the wave at the end.  The
+// others take its matrix-core path (16x16 tiles of ranks x tokens).
+constexpr int kGemvMaxTokens = 4;
 
 // A batched apply with ids of at most kDecodeMaxT tokens over a store of
 // rank <= kVecMaxRank whose d_in is one 16-byte chunk per thread of a
@@ -60,19 +70,18 @@ inline int64_t plan_max_runs(int T, int n, int len) {
 }
 inline int64_t plan_max_subtiles(int T, int n) { return plan_max_runs(T, n, kSubTile); }
 
-// The work plan: a 256-byte header (int32 [0] = number of sub-tiles), then
-// one 128-byte entry per sub-tile, in adapter order.  Written by the shrink
-// (or by the plan kernel) and read by the expand and the partial-sum reduce.
+// The plan of a grouping: its sub-tiles in grouped order (adapters
+// ascending, tokens ascending inside an adapter).  It depends on the
+// grouping only, so one plan serves every store of the same adapters (all
+// the projections of a decode step).  A 256-byte header (int32 [0] = number
+// of sub-tiles, [1] = T, [2] = n), then one 128-byte entry per sub-tile.
 struct TileEntry {
-  int32_t a;        // adapter
-  int32_t pos0;     // grouped position of the first token
-  int32_t m;        // tokens (1..kSubTile)
-  int32_t r;        // stored rank
-  int32_t row_off;  // first row of the adapter in the store
-  float scale;      // s_a
-  int32_t S;        // K chunks of the shrink (partial sums to add)
-  int32_t pad0;
-  int32_t tok[kSubTile];  // token indices, ascending
+  int32_t a;     // adapter
+  int32_t pos0;  // grouped position of the first token
+  int32_t m;     // tokens (1..kSubTile)
+  int32_t j;     // index of the sub-tile among its adapter's
+  int32_t pad0[4];
+  int32_t tok[kSubTile];  // token indices, ascending; -1 past m
   int32_t pad1[8];
 };
 static_assert(sizeof(TileEntry) == 128, "entry is one 128-byte line");
@@ -81,43 +90,46 @@ inline size_t plan_bytes(int T, int n) {
   return kPlanHeaderBytes + sizeof(TileEntry) * (size_t)plan_max_subtiles(T, n);
 }
 
+// A call's own view of each sub-tile: the store's values for its adapter
+// (written by the shrink, read by the expand, so that the expand's loads of
+// B, h and y need no dependent metadata load).
+struct TileMeta {
+  int32_t r;        // stored rank (0: the adapter adds nothing)
+  int32_t row_off;  // first row of the adapter in the store
+  float scale;      // s_a
+  int32_t S;        // partial sums of h (K chunks of the shrink)
+};
+static_assert(sizeof(TileMeta) == 16, "one 16-byte load");
+
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline int elem_bytes(int dtype) { return dtype == LORA_DTYPE_BF16 ? 2 : 4; }
 inline int vec_elems(int dtype) { return dtype == LORA_DTYPE_BF16 ? 8 : 4; }  // 16-byte vectors
 
-// The shrink splits d_in into S <= kMaxChunks chunks; each of the 8 waves of an item
-// takes `spw` consecutive K steps (a step is 4 x 16 bytes of K: 32 bf16 or
-// 16 f32 values), issued as one batch of loads.  The batch depends on the
-// adapter's number of 16-rank row groups (ng): 8, 5, 4, 3 steps for ng =
-// 1..4, about 60 registers of loads either way.  S is at most 8; very wide
-// inputs give more steps per wave (several batches).  Indexed by ng (1..4).
+// The shrink cuts d_in into S <= kMaxChunks chunks, one workgroup item per
+// (sub-tile, chunk).  Each of its 8 waves takes an equal span of the chunk,
+// 8 matrix-core K steps of 64 bytes per row (256 bf16, 128 float32 values)
+// or a multiple for very wide inputs, so that one batch of loads covers it
+// at ranks up to 16 (two or three batches above).  Smaller chunks for
+// higher ranks, to even out the items' bytes, were measured slower (decode
+// spectral and prefill: more partial sums for the expand, no better
+// balance).  S depends on d_in only, so it is the same for every sub-tile of
+// a store.  The last chunk may be shorter.
 constexpr int kMaxChunks = 8;
 struct ShrinkSplit {
-  int spw[5];     // K steps per wave
-  int S[5];       // K chunks (partial sums per output)
-  int kchunk[5];  // K elements per chunk = 8 * spw * step
-  int S_max;      // largest S over the row groups the store needs
+  int kchunk;  // K elements per chunk
+  int span;    // K elements per wave (kchunk / kShrinkWaves)
+  int S;       // chunks (partial sums per h value)
 };
-inline int shrink_batch_steps(int ng) { return ng <= 1 ? 8 : ng == 2 ? 5 : ng == 3 ? 4 : 3; }
-inline int rank_groups(int r) { return r <= 16 ? 1 : (r + 15) / 16; }
-inline ShrinkSplit shrink_split(int d_in, int r_max, int dtype) {
-  const int step = 4 * vec_elems(dtype);
-  const int steps = (d_in + step - 1) / step;
+inline ShrinkSplit shrink_split(int d_in, int dtype) {
+  const int unit = kShrinkWaves * 8 * 4 * vec_elems(dtype);  // 2048 bf16, 1024 float32
+  const int units = (d_in + unit - 1) / unit;
+  int mult = (units + kMaxChunks - 1) / kMaxChunks;
+  if (mult < 1) mult = 1;
   ShrinkSplit sp;
-  sp.spw[0] = sp.S[0] = sp.kchunk[0] = 0;
-  sp.S_max = 1;
-  for (int ng = 1; ng <= 4; ++ng) {
-    int spw = shrink_batch_steps(ng);
-    int S = (steps + kShrinkWaves * spw - 1) / (kShrinkWaves * spw);
-    if (S > kMaxChunks) {
-      spw = (steps + kShrinkWaves * kMaxChunks - 1) / (kShrinkWaves * kMaxChunks);
-      S = (steps + kShrinkWaves * spw - 1) / (kShrinkWaves * spw);
-    }
-    sp.spw[ng] = spw;
-    sp.S[ng] = S;
-    sp.kchunk[ng] = kShrinkWaves * spw * step;
-    if (ng <= rank_groups(r_max) && S > sp.S_max) sp.S_max = S;
-  }
+  sp.kchunk = mult * unit;
+  sp.span = sp.kchunk / kShrinkWaves;
+  sp.S = (d_in + sp.kchunk - 1) / sp.kchunk;
+  if (sp.S < 1) sp.S = 1;
   return sp;
 }
 
@@ -126,19 +138,23 @@ inline ShrinkSplit shrink_split(int d_in, int r_max, int dtype) {
 inline int64_t partial_ld(int r_max) { return (int64_t)align_up((size_t)(r_max < 1 ? 1 : r_max), 8); }
 
 // Workspace of shrink / expand / apply, each part 256-byte aligned:
-//   plan | partial sums [S][T][ldp] float32 | seg_off [n+2] | perm [T]
-// (the last two only when the apply has to sort: n > kGroupMaxN).
+//   tile meta [max_sub] | partial sums [S][T][ldp] float32 | plan |
+//   seg_off [n+2] | perm [T]
+// The plan, seg_off and perm parts hold the grouping a call forms itself
+// (from ids, or a plan from a caller's seg_off / perm); a call given a plan
+// leaves them unused.
 struct WsLayout {
-  size_t plan, part, seg_off, perm, total;
+  size_t meta, part, plan, seg_off, perm, total;
 };
 inline WsLayout ws_layout(int T, int n, int d_in, int r_max, int dtype) {
   WsLayout L;
-  const ShrinkSplit sp = shrink_split(d_in, r_max, dtype);
-  L.plan = 0;
-  L.part = align_up(plan_bytes(T, n), 256);
-  L.seg_off = L.part + align_up((size_t)sp.S_max * (size_t)T * (size_t)partial_ld(r_max) * 4, 256);
-  L.perm = L.seg_off + (n > kGroupMaxN ? align_up((size_t)(n + 2) * 4, 256) : 0);
-  L.total = L.perm + (n > kGroupMaxN ? align_up((size_t)T * 4, 256) : 0);
+  const ShrinkSplit sp = shrink_split(d_in, dtype);
+  L.meta = 0;
+  L.part = align_up(sizeof(TileMeta) * (size_t)plan_max_subtiles(T, n), 256);
+  L.plan = L.part + align_up((size_t)sp.S * (size_t)T * (size_t)partial_ld(r_max) * 4, 256);
+  L.seg_off = L.plan + align_up(plan_bytes(T, n), 256);
+  L.perm = L.seg_off + align_up((size_t)(n + 2) * 4, 256);
+  L.total = L.perm + align_up((size_t)T * 4, 256);
   return L;
 }
 

@@ -6,27 +6,27 @@
 namespace lora {
 
 // ------------------------------------------------------------ shrink wave
-// One wave's share of a sub-tile's shrink: K range [k0, k0 + kc) of
+// One wave's work item of the shrink on the matrix cores: K range
+// [k0, k0 + kc) of
 //   H^T[r_a x m] = A_a[r_a x d_in] . X^T[d_in x m]     (m <= 16)
-// on 16x16 MFMA tiles.  The wave's float32 partial tile (NG row groups of 16
-// ranks) goes to red_slot[q * 64 + lane]: lane l holds token l % 16, ranks
-// 16 q + 4 (l / 16) + 0..3.  Step s covers K indices [k0 + s * KSTEP,
-// +KSTEP); lane group g (lanes 16g..16g+15) takes the g-th 16 bytes of it, so
-// the four lane groups of a row read 64 contiguous bytes per instruction.
-// Both operands of every MFMA carry the same K indices (any K order that is
-// identical for the two operands gives the same sum up to rounding order).
-// Rows j >= r_a read as zero from the adapter's buffer resource and tokens
-// >= m are not loaded.  U steps of loads are issued before the first MFMA
-// that consumes them.
+// on 16x16 MFMA tiles, NG row groups of 16 ranks.  On return lane l holds, in
+// acc[q], token l % 16 and ranks 16 q + 4 (l / 16) + 0..3.  Step s covers K
+// indices [k0 + s * KSTEP, +KSTEP); lane group g (lanes 16g..16g+15) takes
+// the g-th 16 bytes of it, so the four lane groups of a row read 64
+// contiguous bytes per instruction.  Both operands of every MFMA carry the
+// same K indices (any K order that is identical for the two operands gives
+// the same sum up to rounding order).  Rows j >= r_a read as zero from the
+// adapter's buffer resource and tokens >= m are not loaded.  U steps of
+// loads are issued before the first MFMA that consumes them.
 template <typename E, int NG, int U>
-__device__ __forceinline__ void shrink_wave(const char* __restrict__ xrow, bool tval,
-                                            const char* __restrict__ a_rows, int d_in, int r, int k0,
-                                            int kc, f32x4_t* red_slot) {
+__device__ __forceinline__ void shrink_mfma(const char* __restrict__ xrow, bool tval,
+                                            const char* __restrict__ a_rows, int d_in, int r, int k0, int kc,
+                                            f32x4_t (&acc)[NG]) {
   constexpr int V = E::kVec;
   constexpr int KSTEP = 4 * V;
   const int lane = threadIdx.x & 63;
   const int i = lane & 15, g = lane >> 4;
-  const int steps = kc / KSTEP;
+  const int steps = (kc + KSTEP - 1) / KSTEP;
   const int kl = k0 + g * V;
   const uint32_t a_row_bytes = (uint32_t)d_in * E::kBytes;
   // The adapter's retained rows as one buffer: rows j >= r read as zero.
@@ -34,17 +34,17 @@ __device__ __forceinline__ void shrink_wave(const char* __restrict__ xrow, bool 
   uint32_t aoff[NG];
 #pragma unroll
   for (int q = 0; q < NG; ++q) aoff[q] = (uint32_t)(q * 16 + i) * a_row_bytes + (uint32_t)kl * E::kBytes;
-  f32x4_t acc[NG];
 #pragma unroll
   for (int q = 0; q < NG; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const uint4 zero = make_uint4(0, 0, 0, 0);
+  const int kend = k0 + kc;
   for (int s0 = 0; s0 < steps; s0 += U) {
     uint4 bx[U], ba[U][NG];
 #pragma unroll
     for (int uu = 0; uu < U; ++uu) {
       const int s = s0 + uu;
       const int k = kl + s * KSTEP;
-      const bool kv = s < steps && k < d_in;
+      const bool kv = s < steps && k < kend;
       bx[uu] = (tval && kv) ? ld16(xrow + (size_t)k * E::kBytes) : zero;
       const uint32_t so = (uint32_t)(s * KSTEP * E::kBytes);
 #pragma unroll
@@ -55,8 +55,6 @@ __device__ __forceinline__ void shrink_wave(const char* __restrict__ xrow, bool 
 #pragma unroll
       for (int q = 0; q < NG; ++q) acc[q] = mfma_chunk<E>(ba[uu][q], bx[uu], acc[q]);
   }
-#pragma unroll
-  for (int q = 0; q < NG; ++q) red_slot[q * 64 + lane] = acc[q];
 }
 
 // ------------------------------------------------------------ expand helpers

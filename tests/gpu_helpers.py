@@ -70,3 +70,26 @@ def hbits(y: torch.Tensor) -> np.ndarray:
     if y.dtype == torch.bfloat16:
         return y.view(torch.int16).cpu().numpy()
     return y.view(torch.int32).cpu().numpy()
+
+
+def chunks_of(d_in, r, e):
+    """Partial sums of an h value (the shrink's chunks of d_in) - restated:
+    8 waves x 8 K steps of 64 bytes per chunk (2048 bf16, 1024 float32
+    values), times the smallest multiple that keeps them at most 8; the
+    same for every rank r."""
+    unit = 8 * 8 * 4 * (16 // e)
+    mult = max(1, -(-(-(-d_in // unit)) // 8))
+    return max(1, -(-d_in // (mult * unit)))
+
+
+def ws_offsets(T, n, d_in, r_max, e):
+    """(metadata offset, plan offset, S) in an apply's workspace - the layout
+    restated: 16 bytes of metadata per possible sub-tile of <= 16 tokens, the
+    float32 partial sums of S chunks at row stride r_max rounded up to 8,
+    then the plan; each part 256-byte aligned."""
+    up = lambda v: -(-v // 256) * 256
+    max_sub = (T + 15 * min(n, T)) // 16 if T > 0 else 0
+    S = chunks_of(d_in, r_max, e)
+    ldp = -(-max(r_max, 1) // 8) * 8
+    part = up(16 * max_sub)
+    return 0, part + up(S * T * ldp * 4), S

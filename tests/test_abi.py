@@ -50,7 +50,7 @@ def test_status_strings(lib):
     assert b"invalid" in lib.lora_status_string(1)
     assert b"unsupported" in lib.lora_status_string(2)
     assert b"HIP" in lib.lora_status_string(3)
-    assert lib.lora_abi_version() == 3
+    assert lib.lora_abi_version() == 4
     assert lib.lora_last_hip_error() == 0
 
 
@@ -210,10 +210,10 @@ def test_noalloc_rejects_before_any_hip_call(lib):
     assert call(ids=None, so=FAKE) == 1
     assert call(T=0) == 0
     assert call(T=0, ids=None, x=None, y=None) == 0
-    big = _store(n=16000, d_in=18944, r_max=64, R=16000 * 64)
+    big = _store(n=16000, d_in=16384, r_max=64, R=16000 * 64)
     T = 16384
     assert lib.lora_workspace_bytes(C.byref(big), T) > L.LORA_NOALLOC_SCRATCH_BYTES
-    assert call(s=big, T=T, ldx=18944) == 2
+    assert call(s=big, T=T, ldx=16384) == 2
     assert lib.lora_last_hip_error() == 0
 
 
@@ -269,29 +269,68 @@ def test_concurrent_validation_from_threads(lib):
 
 
 def _layout_bytes(T, n, d_in, r_max, e):
-    """The workspace layout restated: plan (256-byte header + one 128-byte
-    entry per possible sub-tile of <= 16 tokens), float32 partial sums for
-    the largest number S of d_in chunks any stored rank uses (8 waves times
-    8/5/4/3 steps of 64 bytes for 1..4 groups of 16 ranks, at most 8 chunks)
-    at row stride r_max rounded up to 8, and seg_off + perm when n exceeds
-    the in-kernel histogram's 4096 adapters; each part 256-byte aligned."""
+    """The workspace layout restated: 16 bytes of metadata per possible
+    sub-tile of <= 16 tokens; float32 partial sums for the S chunks of d_in
+    (a chunk is 8 waves x 8 K steps of 64 bytes, or the smallest multiple of
+    that keeping S at most 8) at row stride r_max rounded up to 8; the plan (256-byte
+    header + one 128-byte entry per possible sub-tile); seg_off [n + 2] and
+    perm [T]; each part 256-byte aligned."""
     up = lambda v: -(-v // 256) * 256
     max_sub = (T + 15 * min(n, T)) // 16 if T > 0 else 0
-    steps = -(-d_in // (64 // e))
-    ng_max = 1 if r_max <= 16 else -(-r_max // 16)
-    S_max = 1
-    for ng in range(1, ng_max + 1):
-        spw = {1: 8, 2: 5, 3: 4, 4: 3}[ng]
-        S = -(-steps // (8 * spw))
-        if S > 8:
-            spw = -(-steps // 64)
-            S = -(-steps // (8 * spw))
-        S_max = max(S_max, S)
+    unit = 8 * 8 * 4 * (16 // e)  # 8 waves x 8 K steps of 64 bytes
+    mult = max(1, -(-(-(-d_in // unit)) // 8))
+    S = max(1, -(-d_in // (mult * unit)))
     ldp = -(-max(r_max, 1) // 8) * 8
-    total = up(256 + 128 * max_sub) + up(S_max * T * ldp * 4)
-    if n > 4096:
-        total += up((n + 2) * 4) + up(T * 4)
-    return total
+    return up(16 * max_sub) + up(S * T * ldp * 4) + up(256 + 128 * max_sub) + up((n + 2) * 4) + up(T * 4)
+
+
+def test_plan_bytes(lib):
+    for T, n in ((100, 4), (4096, 1024), (16384, 16382), (1, 1)):
+        assert lib.lora_plan_bytes(T, n) == 256 + 128 * ((T + 15 * min(n, T)) // 16)
+    assert lib.lora_plan_bytes(0, 4) == 256
+    assert lib.lora_plan_bytes(-1, 4) == 0
+    assert lib.lora_plan_bytes(4, 0) == 0
+
+
+def test_group_rejects_before_launch(lib):
+    f = lib.lora_group
+    big = 1 << 30
+
+    def call(ids=FAKE, T=16, n=4, so=FAKE, pm=FAKE, plan=FAKE, pb=big):
+        return f(ids, T, n, so, pm, plan, pb, None, None)
+
+    assert call(T=-1) == 1
+    assert call(n=0) == 1
+    assert call(so=None) == 1
+    assert call(pm=None) == 1
+    assert call(ids=None) == 1
+    assert call(plan=None) == 1
+    assert call(pb=8) == 1
+    assert call(plan=FAKE + 4) == 2
+    assert call(T=L.LORA_SEGMENT_MAX_T + 1) == 2
+    assert call(n=L.LORA_SEGMENT_MAX_N + 1) == 2
+
+
+def test_apply_planned_rejects_before_launch(lib):
+    st = _store()
+    big = 1 << 30
+    for f in (lib.lora_apply_planned, lambda *a: lib.lora_apply_planned_phases(*a, 3)):
+        def call(s=st, x=FAKE, ldx=64, y=FAKE, ldy=32, T=16, plan=FAKE, pb=big, ws=FAKE, wsb=big):
+            return f(C.byref(s) if s is not None else None, x, ldx, y, ldy, T, plan, pb, ws, wsb, None)
+
+        assert call(s=None) == 1
+        assert call(T=-1) == 1
+        assert call(plan=None) == 1
+        assert call(pb=100) == 1
+        assert call(plan=FAKE + 8) == 2
+        assert call(x=None) == 1
+        assert call(ldy=16) == 1
+        assert call(ws=None) == 1
+        assert call(wsb=16) == 1
+        assert call(T=0, plan=None, x=None, y=None, ws=None, wsb=0) == 0
+    for bad in (0, 4):
+        assert lib.lora_apply_planned_phases(C.byref(st), FAKE, 64, FAKE, 32, 16, FAKE, big, FAKE, big, None,
+                                             bad) == 1
 
 
 @pytest.mark.parametrize("T,n,d_in,r_max,dtype", [(100, 4, 64, 6, 1), (2048, 512, 3584, 64, 1),
@@ -317,17 +356,19 @@ def test_apply_phases_rejects_before_launch(lib):
 @pytest.mark.parametrize("T,n,d_in,r_max,dtype,with_ids,want", [
     (256, 64, 4096, 4, 1, 1, 1),      # decode-uniform: one launch, a workgroup per token
     (512, 64, 4096, 8, 1, 1, 1),      # the largest T and rank of that path
-    (512, 64, 4096, 8, 1, 0, 2),      # a grouping given: shrink + expand
-    (513, 64, 4096, 8, 1, 1, 2),      # one token more: shrink + expand
-    (256, 64, 4104, 4, 1, 1, 2),      # d_in beyond one 16-byte step per thread
-    (256, 64, 4096, 9, 1, 1, 2),      # rank above the fused path's
+    (512, 64, 4096, 8, 1, 0, 3),      # a grouping given: its plan, shrink, expand
+    (512, 64, 4096, 8, 1, 2, 2),      # a plan given: shrink + expand
+    (513, 64, 4096, 8, 1, 1, 3),      # one token more: grouping, shrink, expand
+    (256, 64, 4104, 4, 1, 1, 3),      # d_in beyond one 16-byte step per thread
+    (256, 64, 4096, 9, 1, 1, 3),      # rank above the fused path's
     (16, 4, 256, 4, 0, 1, 1),         # float32 up to rank 4 ...
-    (16, 4, 256, 5, 0, 1, 2),         # ... not beyond
-    (16, 4, 2052, 4, 0, 1, 2),        # float32 d_in above 2048
-    (2048, 512, 3584, 64, 1, 1, 2),   # decode-spectral
+    (16, 4, 256, 5, 0, 1, 3),         # ... not beyond
+    (16, 4, 2052, 4, 0, 1, 3),        # float32 d_in above 2048
+    (2048, 512, 3584, 64, 1, 1, 3),   # decode-spectral
     (300, 5000, 64, 4, 1, 1, 1),      # per-token path: any number of adapters
-    (600, 5000, 64, 4, 1, 1, 3),      # beyond it, more adapters than the in-kernel histogram: sort first
-    (300, 5000, 64, 9, 1, 0, 2),      # ... unless the grouping is given
+    (600, 5000, 64, 4, 1, 1, 4),      # beyond it, more adapters than the one-workgroup grouping: sort first
+    (300, 5000, 64, 9, 1, 0, 3),      # ... unless the grouping is given
+    (8193, 64, 4096, 16, 1, 1, 4),    # more tokens than the one-workgroup grouping
     (0, 4, 64, 4, 1, 1, 0),
 ])
 def test_apply_launches(lib, T, n, d_in, r_max, dtype, with_ids, want):
@@ -340,6 +381,8 @@ def test_apply_launches_errors(lib):
     assert lib.lora_apply_launches(C.byref(_store()), -1, 1) == -1
     assert lib.lora_apply_launches(C.byref(_store(r_max=65)), 16, 1) == -2
     assert lib.lora_apply_launches(C.byref(_store()), L.LORA_SEGMENT_MAX_T + 1, 1) == -2
+    assert lib.lora_apply_launches(C.byref(_store()), 16, 3) == -1
+    assert lib.lora_apply_launches(C.byref(_store()), 16, -1) == -1
 
 
 def _jd(k=4, r=8, n=10, diag=0, d_in=64, d_out=32):
@@ -384,7 +427,9 @@ def test_jd_apply_rejects_before_launch(lib):
     assert call(j=j) == 1
     assert call(j=_jd(diag=2)) == 1
     assert call(j=_jd(r=65)) == 2
-    assert call(j=_jd(k=5000, n=6000)) == 2  # more clusters than the in-kernel grouping takes
+    assert call(j=_jd(k=5000, n=6000)) == 2  # more clusters than the one-workgroup grouping takes
+    assert call(j=_jd(k=2049, n=3000)) == 2
+    assert call(T=8193) == 2                   # more tokens than it takes
     assert call(T=L.LORA_SEGMENT_MAX_T + 1) == 2
 
 

@@ -14,7 +14,7 @@ import rank_specialized_amd as rs
 from oracle import apply_ref, bf16_round_ref, shrink_error_bound, shrink_ref
 from workloads import make_config, make_random_workload
 
-from gpu_helpers import (TOL, TORCH_DTYPE, device, hbits, inputs, note, pack, rel_err, to_dev,
+from gpu_helpers import (TOL, TORCH_DTYPE, device, hbits, inputs, note, pack, rel_err, to_dev, ws_offsets,
                          y_host)
 
 pytestmark = pytest.mark.gpu
@@ -503,9 +503,10 @@ def _two_stores(dev):
 
 
 def test_expand_skips_plan_of_another_store():
-    """The expand-only call on a workspace whose plan was made for another
-    store (larger row offsets and ranks): entries that do not fit the store
-    are skipped, nothing outside its buffers is read, and the call succeeds."""
+    """The expand-only call on a workspace whose sub-tile metadata was made
+    for another store (larger row offsets and ranks): sub-tiles that do not
+    fit the store are skipped, nothing outside its buffers is read, and the
+    call succeeds."""
     dev = device()
     big, sb, small, ss = _two_stores(dev)
     x, ids, y = inputs(big, dev)
@@ -521,8 +522,8 @@ def test_expand_skips_plan_of_another_store():
 @pytest.mark.parametrize("fill", ["ones", "random"])
 def test_expand_on_garbage_workspace(fill):
     """An expand-only call on a workspace of arbitrary bytes never reads
-    outside the store's buffers (every plan entry is checked against the
-    store before use) and leaves y finite."""
+    outside the store's buffers (every plan entry and sub-tile metadata is
+    checked against T and the store before use)."""
     dev = device()
     big, sb, _, _ = _two_stores(dev)
     x, ids, y = inputs(big, dev)
@@ -531,8 +532,102 @@ def test_expand_on_garbage_workspace(fill):
         ws.fill_(0xFF)
     else:
         ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, generator=torch.Generator().manual_seed(5)))
-        ws[:4].copy_(torch.tensor([200, 0, 0, 0], dtype=torch.uint8))  # a plausible sub-tile count
+        _, plan_off, _ = ws_offsets(big.T, 8, 256, sb.r_max, 2)
+        ws[plan_off:plan_off + 4].copy_(torch.tensor([20, 0, 0, 0], dtype=torch.uint8))  # a plausible sub-tile count
     note(f"expand on a workspace of {fill}")
     rs.lora_apply_batched_phases(sb, x, y, 2, ids=ids, ws=ws)
     torch.cuda.synchronize()
     assert y.shape == (big.T, 192)
+
+
+# One plan (lora_group) shared by several stores of the same adapters, as a
+# decode step's projections share it: each store's result must equal the
+# same store applied with ids (the grouping formed per call), bit for bit,
+# and the oracle within the bf16 bar.  The fleet modules span every input and
+# output width of the step and ranks 4..16 (5S) or 6 (5U).
+PLANNED_MODULES = [("5S", 0, 0), ("5S", 0, 1), ("5S", 5, 3), ("5S", 9, 4), ("5S", 27, 6), ("5U", 1, 5)]
+
+
+def test_planned_apply_shares_one_plan():
+    dev = device()
+    wls = [make_config(k, layer=l, proj=p) for k, l, p in PLANNED_MODULES]
+    ids = torch.from_numpy(wls[0].ids.astype(np.int32)).to(dev)
+    n = wls[0].n
+    note(f"lora_group T={wls[0].T} n={n}")
+    seg = rs.lora_group(ids, n)
+    for wl, (k, l, p) in zip(wls, PLANNED_MODULES):
+        assert np.array_equal(wl.ids, wls[0].ids)
+        store = pack(wl, dev)
+        x, _, y = inputs(wl, dev)
+        y_ids = y.clone()
+        note(f"planned apply {k} L{l} p{p} {wl.module.d_in}->{wl.module.d_out}")
+        rs.lora_apply_planned(store, x, y, seg)
+        rs.lora_apply_batched(store, x, y_ids, ids=ids)
+        torch.cuda.synchronize()
+        assert np.array_equal(hbits(y), hbits(y_ids)), (k, l, p)
+        err = rel_err(y_host(y), _ref(wl))
+        assert err <= TOL["bf16"], (k, l, p, err)
+
+
+@pytest.mark.parametrize("key", ["3", "4"])
+def test_planned_phases_compose(key):
+    """Shrink alone, then expand alone, on a plan: the same bits as the
+    planned apply."""
+    dev = device()
+    wl = make_config(key, integer=True)
+    store = pack(wl, dev)
+    x, ids, y = inputs(wl, dev)
+    y2 = y.clone()
+    seg = rs.lora_group(ids, wl.n)
+    ws = torch.empty(rs.lora_workspace_bytes(store, wl.T), dtype=torch.uint8, device=dev)
+    note(f"planned phases {key}")
+    rs.lora_apply_planned(store, x, y, seg, ws=ws, phases=1)
+    rs.lora_apply_planned(store, x, y, seg, ws=ws, phases=2)
+    rs.lora_apply_planned(store, x, y2, seg)
+    torch.cuda.synchronize()
+    assert np.array_equal(hbits(y), hbits(y2))
+    ref = _ref(wl)
+    want = bf16_round_ref(ref) if wl.dtype == "bf16" else ref
+    assert np.array_equal(y_host(y), want)
+
+
+def test_planned_apply_on_plan_of_other_grouping():
+    """A plan made for another grouping of the same T and n (other ids) gives
+    wrong values but reads nothing outside the call's buffers: every entry and
+    token is checked against T and the store."""
+    dev = device()
+    wl = make_config("3")
+    store = pack(wl, dev)
+    x, ids, y = inputs(wl, dev)
+    other = torch.from_numpy(np.roll(wl.ids, 7).astype(np.int32)).to(dev)
+    seg = rs.lora_group(other, wl.n)
+    note("planned apply on another grouping's plan")
+    rs.lora_apply_planned(store, x, y, seg)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y.float()).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_eight_partial_sums_integer_exact(dtype):
+    """Ranks up to 64 over a 16384-wide input: the shrink cuts d_in into 8
+    chunks (bf16; float32 chunks are half as wide, 16 K values twice over).
+    The apply, and shrink + expand through h, are bit for bit the exact
+    result."""
+    from gpu_helpers import chunks_of
+    dev = device()
+    ranks = [64, 40, 3, 17, 64, 0, 9]
+    e = 2 if dtype == "bf16" else 4
+    assert chunks_of(16384, 64, e) == 8
+    wl = make_random_workload(41, 200, len(ranks), 16384, 136, ranks, dtype=dtype, integer=True,
+                              scales=[0.5] * len(ranks), id_mode="zipf", invalid_frac=0.05)
+    store, x, ids, y = _run_apply(wl, dev)
+    ref = _ref(wl)
+    assert np.abs(ref).max() < 2 ** 24
+    want = bf16_round_ref(ref) if dtype == "bf16" else ref
+    assert np.array_equal(y_host(y), want)
+    seg = rs.lora_segment(ids, wl.n)
+    h = rs.lora_shrink(store, x, seg)
+    y2 = torch.zeros_like(y)
+    rs.lora_expand(store, h, seg, y2)
+    torch.cuda.synchronize()
+    assert np.array_equal(y_host(y2), want)

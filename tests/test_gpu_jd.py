@@ -46,6 +46,9 @@ CASES = {
     "rank64": dict(seed=14, T=90, n=8, k=2, d_in=96, d_out=64, r=64),
     "one_cluster_many_tiles": dict(seed=15, T=400, n=20, k=1, d_in=128, d_out=128, r=8),
     "wide_in": dict(seed=16, T=40, n=6, k=2, d_in=18944, d_out=64, r=12),
+    # rank 64 over a wide input: 16 partial sums per h value (the shrink's
+    # chunks shrink with the rank), more than one batch of their loads.
+    "rank64_wide_in": dict(seed=17, T=70, n=7, k=2, d_in=8192, d_out=72, r=64),
 }
 
 

@@ -42,6 +42,11 @@ CASES = {
     # sub-tiles (~67 tokens per adapter) take the matrix path, whose h chunk
     # must not read past the row.
     "rank4_pairs": dict(seed=6, T=200, n=3, d_in=64, d_outs=(64, 32), ranks=([4, 4, 4], [4, 4, 4])),
+    # Four rank-8 slices (stacked rank 32) over a 12288-wide input: 12
+    # partial sums per h value, read by the expand's vector path (few tokens
+    # per adapter, slice ranks <= 8).
+    "wide_stacked": dict(seed=7, T=60, n=12, d_in=12288, d_outs=(64, 32, 32, 96),
+                         ranks=([8] * 12, [7] * 12, [8] * 12, [5] * 12)),
 }
 
 
@@ -65,7 +70,10 @@ def _run(name, dtype, integer=False, fused=False, grouping=False):
     else:
         ys = [torch.zeros(T, d, dtype=dt, device=dev) for d in c["d_outs"]]
     note(f"multi {name} {dtype} integer={integer} fused={fused} grouping={grouping}")
-    if grouping:
+    if grouping == "plan":
+        seg = rs.lora_group(ids, c["n"])
+        rs.lora_apply_multi(ms, x, ys, seg=seg)
+    elif grouping:
         seg = rs.lora_segment(ids, c["n"])
         rs.lora_apply_multi(ms, x, ys, seg=seg)
     else:
@@ -91,7 +99,7 @@ def test_multi_parity(name, dtype):
     _run(name, dtype)
 
 
-@pytest.mark.parametrize("name", ["qkv_small", "odd_offsets_matrix", "high_rank", "rank4_pairs"])
+@pytest.mark.parametrize("name", ["qkv_small", "odd_offsets_matrix", "high_rank", "rank4_pairs", "wide_stacked"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_multi_integer_exact(name, dtype):
     _run(name, dtype, integer=True)
@@ -105,6 +113,11 @@ def test_multi_fused_output(name):
 @pytest.mark.parametrize("name", ["odd_offsets_matrix", "gate_up"])
 def test_multi_from_grouping(name):
     _run(name, "bf16", integer=True, grouping=True)
+
+
+@pytest.mark.parametrize("name", ["qkv_small", "odd_offsets_matrix", "rank4_pairs"])
+def test_multi_from_plan(name):
+    _run(name, "bf16", integer=True, grouping="plan")
 
 
 def test_multi_equals_separate_applies_integer():

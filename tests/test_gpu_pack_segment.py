@@ -10,7 +10,7 @@ import rank_specialized_amd as rs
 from oracle import segment_ref
 from workloads import make_config, make_random_workload
 
-from gpu_helpers import TORCH_DTYPE, device, note, pack
+from gpu_helpers import chunks_of, ws_offsets, TORCH_DTYPE, device, note, pack
 
 pytestmark = pytest.mark.gpu
 
@@ -63,41 +63,49 @@ def test_pack_roundtrip(case):
     assert np.array_equal(sc.cpu().numpy(), wl.module.scales)
 
 
-def _read_plan(ws):
-    """(count, entries) of the work plan at the start of a workspace: a
-    256-byte header (int32 count), then 128-byte entries {adapter, first
-    grouped position, tokens, stored rank, row offset, scale, -, -,
-    token indices[16], -}."""
-    raw = ws.cpu().numpy()
+def _read_plan(buf, off=0):
+    """(count, entries) of a plan: a 256-byte header (int32 count, T, n),
+    then 128-byte entries {adapter, first grouped position, tokens, index of
+    the sub-tile within its adapter, -, -, -, -, token indices[16], -}."""
+    raw = buf.cpu().numpy()[off:]
     count = int(raw[:4].view(np.int32)[0])
     ent = raw[256: 256 + 128 * count].view(np.int32).reshape(count, 32)
-    return count, ent
+    return count, ent, raw[:12].view(np.int32).tolist()
 
 
-def _expected_plan(seg_off, perm, ranks, row_off, scales):
-    """Every adapter with tokens and a non-zero stored rank, cut into runs of
-    16 grouped positions, in adapter order."""
+def _expected_plan(seg_off, perm, n):
+    """Every adapter with tokens cut into runs of 16 grouped positions, in
+    adapter order (the plan depends on the grouping only)."""
     out = []
-    for a in range(len(ranks)):
+    for a in range(n):
         c = seg_off[a + 1] - seg_off[a]
-        if ranks[a] <= 0:
-            continue
-        for j in range(0, c, 16):
-            p0 = seg_off[a] + j
-            m = min(16, c - j)
+        for j, q in enumerate(range(0, c, 16)):
+            p0 = seg_off[a] + q
+            m = min(16, c - q)
             tok = list(perm[p0: p0 + m]) + [-1] * (16 - m)
-            out.append([a, p0, m, int(ranks[a]), int(row_off[a]), scales[a], tok])
+            out.append([a, p0, m, j, tok])
     return out
 
 
-def _check_plan(ws, expect):
-    count, ent = _read_plan(ws)
+def _check_plan(buf, expect, T, n, off=0):
+    count, ent, hdr = _read_plan(buf, off)
     assert count == len(expect)
-    for k, (a, p0, m, r, ro, sc, tok) in enumerate(expect):
+    assert hdr[1:3] == [T, n]
+    for k, (a, p0, m, j, tok) in enumerate(expect):
         e = ent[k]
-        assert [int(e[0]), int(e[1]), int(e[2]), int(e[3]), int(e[4])] == [a, p0, m, r, ro], k
-        assert np.float32(e[5:6].view(np.float32)[0]) == np.float32(sc)
+        assert [int(e[0]), int(e[1]), int(e[2]), int(e[3])] == [a, p0, m, j], k
         assert e[8:24].tolist() == tok, k
+
+
+def _check_meta(ws, expect, ranks, row_off, scales, S_of):
+    """The per-sub-tile metadata of a call: the store's rank, row offset and
+    scale of the sub-tile's adapter, and the partial-sum count S_of(rank)."""
+    raw = ws.cpu().numpy()
+    meta = raw[: 16 * len(expect)].view(np.int32).reshape(-1, 4)
+    for k, (a, _p0, _m, _j, _tok) in enumerate(expect):
+        want = [int(ranks[a]), int(row_off[a]), S_of(int(ranks[a]))]
+        assert [int(meta[k, 0]), int(meta[k, 1]), int(meta[k, 3])] == want, k
+        assert np.float32(meta[k, 2:3].view(np.float32)[0]) == np.float32(scales[a]), k
 
 
 def _segment_case(name):
@@ -184,11 +192,29 @@ def _plan_store(n, dev, seed):
     return store, ranks, scales
 
 
+@pytest.mark.parametrize("name", SEGMENT_CASES)
+def test_group_exact(name):
+    """lora_group: seg_off and perm equal the oracle's grouping, and the plan
+    holds its sub-tiles, token for token (one launch up to 8192 tokens and
+    2048 adapters; beyond, the sort and the plan kernel)."""
+    dev = device()
+    ids, n = _segment_case(name)
+    T = len(ids)
+    note(f"group {name} T={T} n={n}")
+    seg = rs.lora_group(torch.from_numpy(ids).to(dev), n)
+    torch.cuda.synchronize()
+    so_ref, perm_ref, inv_ref = segment_ref(ids.tolist(), n)
+    assert seg.seg_off.cpu().tolist() == so_ref
+    assert seg.perm.cpu().tolist() == perm_ref
+    assert int(seg.n_invalid.cpu()[0]) == inv_ref
+    _check_plan(seg.plan, _expected_plan(so_ref, perm_ref, n), T, n)
+
+
 @pytest.mark.parametrize("name", PLAN_CASES)
 def test_plan_from_ids(name):
-    """The plan the shrink (phase 1 of the two-launch apply) forms from ids
-    inside its workgroups (or, beyond 4096 adapters, from the sort it runs
-    first) equals the sub-tiles of the oracle's grouping, token for token."""
+    """The plan the apply forms from ids (phase 1 of the two-kernel form:
+    grouping, then shrink) equals the sub-tiles of the oracle's grouping,
+    token for token, and the shrink records each sub-tile's store metadata."""
     dev = device()
     ids, n = _segment_case(name)
     T = len(ids)
@@ -201,13 +227,17 @@ def test_plan_from_ids(name):
     torch.cuda.synchronize()
     so_ref, perm_ref, _ = segment_ref(ids.tolist(), n)
     row_off = np.concatenate([[0], np.cumsum(ranks)])
-    _check_plan(ws, _expected_plan(so_ref, perm_ref, ranks, row_off, scales))
+    want = _expected_plan(so_ref, perm_ref, n)
+    _, plan_off, S = ws_offsets(T, n, 64, store.r_max, 2)
+    _check_plan(ws, want, T, n, plan_off)
+    _check_meta(ws, want, ranks, row_off, scales, lambda r: chunks_of(64, r, 2))
 
 
 @pytest.mark.parametrize("name", ["3", "out_of_range", "all_same", "many_adapters"])
 def test_plan_from_grouping(name):
-    """The same plan from a caller-supplied grouping: the apply's shrink with
-    (seg_off, perm), and the plan kernel of the standalone expand."""
+    """The same plan from a caller-supplied grouping: the apply's phase 1
+    with (seg_off, perm), and the plan kernel of the standalone expand (which
+    records the store metadata itself, with one partial sum: h is given)."""
     dev = device()
     ids, n = _segment_case(name)
     T = len(ids)
@@ -218,13 +248,16 @@ def test_plan_from_grouping(name):
     h = torch.zeros(T, max(store.r_max, 1), dtype=torch.float32, device=dev)
     so_ref, perm_ref, _ = segment_ref(ids.tolist(), n)
     row_off = np.concatenate([[0], np.cumsum(ranks)])
-    want = _expected_plan(so_ref, perm_ref, ranks, row_off, scales)
+    want = _expected_plan(so_ref, perm_ref, n)
+    _, plan_off, S = ws_offsets(T, n, 64, store.r_max, 2)
     ws = torch.empty(rs.lora_workspace_bytes(store, T), dtype=torch.uint8, device=dev)
     note(f"plan from grouping {name}")
     rs.lora_apply_batched_phases(store, x, y, 1, seg=seg, ws=ws)
     torch.cuda.synchronize()
-    _check_plan(ws, want)
+    _check_plan(ws, want, T, n, plan_off)
+    _check_meta(ws, want, ranks, row_off, scales, lambda r: chunks_of(64, r, 2))
     ws.fill_(0xAB)
     rs.lora_expand(store, h, seg, y, ws=ws)
     torch.cuda.synchronize()
-    _check_plan(ws, want)
+    _check_plan(ws, want, T, n, plan_off)
+    _check_meta(ws, want, ranks, row_off, scales, lambda r: 1)

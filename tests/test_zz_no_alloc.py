@@ -79,13 +79,13 @@ def test_noalloc_equals_workspace_form(name, grouping):
 def test_noalloc_rejects_oversize_before_launch():
     """A call whose workspace would exceed the scratch array is refused with
     UNSUPPORTED, nothing enqueued (T = 16384 tokens at rank 64, 8 chunks of a
-    wide input: 33.5 MB of partial sums)."""
+    16384-wide input: 33.5 MB of partial sums)."""
     dev = device()
-    wl = make_random_workload(5, 8, 2, 18944, 64, [64, 1], dtype="bf16")
+    wl = make_random_workload(5, 8, 2, 16384, 64, [64, 1], dtype="bf16")
     store = pack(wl, dev)
     T = 16384
     assert rs.lora_workspace_bytes(store, T) > rs._lib.LORA_NOALLOC_SCRATCH_BYTES
-    x = torch.zeros(T, 18944, dtype=torch.bfloat16, device=dev)
+    x = torch.zeros(T, 16384, dtype=torch.bfloat16, device=dev)
     y = torch.zeros(T, 64, dtype=torch.bfloat16, device=dev)
     ids = torch.zeros(T, dtype=torch.int32, device=dev)
     note("noalloc oversize")
