@@ -113,6 +113,10 @@ def parse_args():
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run one elementwise copy of 256 MiB (reads and writes 256 MiB), the "
                         "reference that scales the HBM byte counters")
+    p.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                   help="no GPU work: per-kernel durations of a rocprofv3 --kernel-trace run of this script, over "
+                        "all dispatches and over the isolated ones (no other library kernel running: the "
+                        "one-stream per-kernel passes), as a markdown table")
     p.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU work: read two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of "
                         "this script with --calibrate-copy and record HBM bytes per launch of each "
@@ -395,6 +399,35 @@ def read_pmc(run_dir: str, counter: str):
                     continue
                 out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
     return out
+
+
+def summarize_trace(trace_dir: str):
+    """Markdown table of the library's kernels in a rocprofv3 kernel trace:
+    calls and average duration over all dispatches, and over the isolated
+    ones (no other library kernel overlapping in time: the one-stream
+    per-kernel passes, which bench.py's per-kernel figures time)."""
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            rows += [r for r in csv.DictReader(f) if "lora::" in r["Kernel_Name"]]
+    ev = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+                 r["Kernel_Name"].split("(")[0].replace("void ", "")) for r in rows)
+    stats = {}
+    for i, (s0, e0, k) in enumerate(ev):
+        prev_end = ev[i - 1][1] if i else -1
+        next_start = ev[i + 1][0] if i + 1 < len(ev) else 1 << 62
+        d = (e0 - s0) / 1000.0
+        a = stats.setdefault(k, ([], []))
+        a[0].append(d)
+        if prev_end <= s0 and e0 <= next_start:
+            a[1].append(d)
+    print("| kernel | calls | average (us) | isolated calls | isolated average (us) | isolated median (us) |")
+    print("|---|---|---|---|---|---|")
+    for k, (al, iso) in sorted(stats.items(), key=lambda kv: -sum(kv[1][0])):
+        print(f"| `{k}` | {len(al)} | {np.mean(al):.2f} | {len(iso)} | "
+              f"{(np.mean(iso) if iso else float('nan')):.2f} | {(np.median(iso) if iso else float('nan')):.2f} |")
 
 
 def summarize_pmc(key: str, fetch_dir: str, write_dir: str):
@@ -1063,6 +1096,9 @@ def cpu_for(args, key):
 
 def main():
     args = parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.summarize_pmc:
         summarize_pmc(args.config, *args.summarize_pmc)
         return

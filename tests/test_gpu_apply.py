@@ -631,3 +631,70 @@ def test_eight_partial_sums_integer_exact(dtype):
     rs.lora_expand(store, h, seg, y2)
     torch.cuda.synchronize()
     assert np.array_equal(y_host(y2), want)
+
+
+def test_expand_h_split_per_element_bound():
+    """The bf16 expand feeds h to the matrix cores as the pair hi + lo of bf16
+    values (hi = nearest bf16 of h, lo = nearest bf16 of h - hi), so
+    |h - (hi + lo)| <= 2^-16 |h| (two roundings of relative size 2^-8).
+    The 2r products are exact in float32 and summed in float32, then scaled
+    once, so before the output rounding the error in y[t, o] is at most
+        E = s (2^-16 + (2r + 2) 2^-24 (1 + 2^-6)) sum_j |B[o, j] h[t, j]|,
+    and the bf16 output adds at most half an ulp of the result.  Checked
+    element by element against the exact s B h (float64) on h with 24
+    significant bits and on outputs that cancel: with B = [b, -b] pairs the
+    exact sums are small next to sum |B h|, where a single bf16 copy of h
+    (error 2^-8 |h|) breaks the bound."""
+    dev = device()
+    rng = np.random.default_rng(77)
+    n, T, d_out = 4, 64, 256
+    ranks = [2, 8, 17, 40]
+    wl = make_random_workload(78, T, n, 64, d_out, ranks, dtype="bf16", id_mode="uniform")
+    m = wl.module
+    # B columns in cancelling pairs (column 2i+1 = -column 2i + small bf16 noise).
+    for a in range(n):
+        B = m.B[a].astype(np.float64)
+        for j in range(0, ranks[a] - 1, 2):
+            B[:, j + 1] = -B[:, j] + 2.0 ** -10 * np.sign(rng.normal(size=d_out))
+        m.B[a] = B.astype(np.float32)
+        m.B[a] = torch.from_numpy(m.B[a]).to(torch.bfloat16).float().numpy()
+    store = pack(wl, dev)
+    ids = torch.from_numpy(wl.ids.astype(np.int32)).to(dev)
+    seg = rs.lora_segment(ids, n)
+    so = seg.seg_off.cpu().numpy()
+    perm = seg.perm.cpu().numpy()
+    # h: float32 values with full 24-bit significands, equal within each
+    # cancelling pair up to a relative 2^-12, in grouped rows.
+    r_max = max(ranks)
+    h = np.zeros((T, r_max), np.float32)
+    base = rng.uniform(0.5, 2.0, size=(T, r_max)) * (1 + rng.integers(0, 2 ** 23, size=(T, r_max)) * 2.0 ** -23)
+    h[:] = base.astype(np.float32)
+    h[:, 1::2] = (h[:, 0::2][:, : h[:, 1::2].shape[1]] * (1 + 2.0 ** -12)).astype(np.float32)
+    y = torch.zeros(T, d_out, dtype=torch.bfloat16, device=dev)
+    note("expand from a float32 h: per-element bound of the hi + lo split")
+    rs.lora_expand(store, torch.from_numpy(h).to(dev), seg, y)
+    torch.cuda.synchronize()
+    got = y_host(y)
+    worst, n_cancel = 0.0, 0
+    for a in range(n):
+        r = ranks[a]
+        s = float(m.scales[a])
+        Ba = m.B[a].astype(np.float64)
+        for i in range(so[a], so[a + 1]):
+            t = perm[i]
+            hv = h[i, :r].astype(np.float64)
+            exact = s * (Ba @ hv)
+            mag = s * (np.abs(Ba) @ np.abs(hv))
+            E = (2.0 ** -16 + (2 * r + 2) * 2.0 ** -24 * (1 + 2.0 ** -6)) * mag
+            half_ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(exact) + E, 1e-300))) - 8)
+            err = np.abs(got[t] - exact)
+            assert np.all(err <= E + half_ulp), (a, t, float((err - E - half_ulp).max()))
+            # Where the sum cancels to below 2^-6 of its magnitude, the output
+            # rounding is below 2^-15 of it, so the error seen is h's: a single
+            # bf16 copy of h (2^-8 |h| per term) would exceed 2^-12 there.
+            c = np.abs(exact) <= 2.0 ** -6 * mag
+            n_cancel += int(c.sum())
+            if c.any():
+                worst = max(worst, float((err[c] / mag[c]).max()))
+    assert n_cancel > 1000, n_cancel
+    assert worst < 2.0 ** -12, worst
