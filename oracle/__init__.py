@@ -11,6 +11,7 @@ sources define (float64 unless stated, Python loops over tokens):
 * ``shrink_ref``   - h = A_a x per token
 * ``shrink_error_bound`` - the float32 accumulation bound of h (gamma_n form)
 * ``apply_ref``    - y = y0 + s_a B_a (A_a x) per token
+* ``base_fused_ref`` - y = W0 x + s_a B_a (A_a x) per token (the base layer with the branch)
 * ``brute_force``  - the same in exact rational arithmetic, two association
                      orders, for tiny inputs
 * ``bf16_round_ref`` - round-to-nearest-even onto bfloat16, used where a
@@ -28,6 +29,7 @@ routines, a hand-worked example); none is "parity unpinned".
 """
 from .lora_ref import (  # noqa: F401
     apply_ref,
+    base_fused_ref,
     bf16_round_ref,
     brute_force,
     segment_ref,

@@ -151,6 +151,24 @@ def apply_ref(x, ids, A_list, B_list, scales, y0=None) -> np.ndarray:
     return y
 
 
+def base_fused_ref(x, ids, W0, A_list, B_list, scales) -> np.ndarray:
+    """y[t] = W0 x[t] + s_a B_a (A_a x[t]) for every token t, a = ids[t].
+
+    [CtS] section 3: the LoRA-updated layer computes (W0 + B A) x; section
+    11: the base product W0 x is computed once for all requests and each
+    request's branch B_i A_i x is added to it.  W0 has the layer's [d_out,
+    d_in] orientation (y = W0 x).  Tokens without an adapter (id outside
+    [0, n)) get W0 x alone.  float64, a per-token loop.
+    """
+    x64 = _as64(x)
+    W = _as64(W0)
+    T = x64.shape[0]
+    y = np.zeros((T, W.shape[0]), dtype=np.float64)
+    for t in range(T):
+        y[t] = W @ x64[t]
+    return apply_ref(x, ids, A_list, B_list, scales, y0=y)
+
+
 def brute_force(x, ids, A_list, B_list, scales, y0=None, form: str = "B(Ax)") -> List[List[Fraction]]:
     """Exact rational evaluation with explicit triple loops (tiny inputs only).
 

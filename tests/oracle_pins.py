@@ -14,7 +14,7 @@ from fractions import Fraction
 
 import numpy as np
 
-from workloads import make_config, make_random_workload
+from workloads import make_config, make_integer_workload, make_random_workload
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -165,6 +165,73 @@ def pin_no_adapter_tokens(apply_fn):
 
 APPLY_PINS = (pin_worked_example, pin_merged_weight, pin_rank_zero, pin_scale_linearity,
               pin_zero_padding, pin_token_permutation, pin_per_segment, pin_no_adapter_tokens)
+
+
+# ------------------------------------------------------- base-fused pins
+# y = W0 x + s_a B_a A_a x per token ("Compress then Serve" sections 3 and
+# 11).  Each pin takes fn(x, ids, W0, A_list, B_list, scales).
+
+def _fused_case(seed=0, d_in=24, d_out=40):
+    wl = make_random_workload(60 + seed, 37, 5, d_in, d_out, [3, 0, 6, 1, 8], dtype="bf16", id_mode="zipf",
+                              invalid_frac=0.15)
+    W0 = np.random.default_rng(seed).normal(size=(d_out, d_in)) / np.sqrt(d_in)
+    return wl, W0
+
+
+def pin_fused_merged_weight(fn):
+    """Equals x (W0 + s_a B_a A_a)^T per token: the merged weight of the
+    token's adapter (W0 alone without one), applied with one numpy product."""
+    for seed, (di, do) in enumerate(((24, 40), (32, 32), (48, 16))):
+        wl, W0 = _fused_case(seed, di, do)
+        m = wl.module
+        ref = np.zeros((wl.T, do))
+        for t in range(wl.T):
+            a = int(wl.ids[t])
+            Wm = W0.copy()
+            if 0 <= a < m.n:
+                Wm = Wm + float(m.scales[a]) * (m.B[a].astype(np.float64) @ m.A[a].astype(np.float64))
+            ref[t] = wl.x[t].astype(np.float64) @ Wm.T
+        y = np.asarray(fn(wl.x, wl.ids, W0, m.A, m.B, m.scales), np.float64)
+        assert y.shape == ref.shape
+        assert np.abs(y - ref).max() <= 1e-12 * max(np.abs(ref).max(), 1.0), np.abs(y - ref).max()
+
+
+def pin_fused_no_adapter_is_base(fn):
+    """With every id outside [0, n), the result is the base product x W0^T
+    (numpy), whatever the factors."""
+    wl, W0 = _fused_case(3)
+    m = wl.module
+    ids = np.full(wl.T, -1, np.int32)
+    ids[::5] = m.n + 2
+    y = np.asarray(fn(wl.x, ids, W0, m.A, m.B, m.scales), np.float64)
+    ref = wl.x.astype(np.float64) @ W0.T
+    assert np.abs(y - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
+def pin_fused_zero_base(fn):
+    """With W0 = 0 only the branch remains: for integer inputs, exactly the
+    rational B (A x) of every token (brute force)."""
+    wl = make_integer_workload("1")
+    m = wl.module
+    W0 = np.zeros((m.d_out, m.d_in))
+    y = np.asarray(fn(wl.x[:6], wl.ids[:6], W0, m.A, m.B, m.scales), np.float64)
+    from oracle import brute_force
+    exact = brute_force(wl.x[:6], wl.ids[:6], m.A, m.B, m.scales)
+    assert [[float(v) for v in row] for row in exact] == y.tolist()
+
+
+def pin_fused_linear_in_base(fn):
+    """The result is affine in W0: f(W1 + W2) = f(W1) + f(W2) - f(0)."""
+    wl, W1 = _fused_case(4)
+    m = wl.module
+    W2 = np.random.default_rng(9).normal(size=W1.shape)
+    f = lambda W: np.asarray(fn(wl.x, wl.ids, W, m.A, m.B, m.scales), np.float64)
+    lhs = f(W1 + W2)
+    rhs = f(W1) + f(W2) - f(np.zeros_like(W1))
+    assert np.abs(lhs - rhs).max() <= 1e-12 * max(np.abs(lhs).max(), 1.0)
+
+
+FUSED_PINS = (pin_fused_merged_weight, pin_fused_no_adapter_is_base, pin_fused_zero_base, pin_fused_linear_in_base)
 
 
 # -------------------------------------------------------------- segment pins

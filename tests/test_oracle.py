@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import apply_ref, bf16_round_ref, brute_force, segment_ref, shrink_error_bound, shrink_ref
+from oracle import apply_ref, base_fused_ref, bf16_round_ref, brute_force, segment_ref, shrink_error_bound, shrink_ref
 from workloads import make_random_workload
 
 import oracle_pins as P
@@ -56,6 +56,11 @@ def test_shrink_matches_per_segment_product():
 @pytest.mark.parametrize("pin", P.SHRINK_BOUND_PINS, ids=lambda f: f.__name__)
 def test_shrink_bound_pin(pin):
     pin(shrink_error_bound)
+
+
+@pytest.mark.parametrize("pin", P.FUSED_PINS, ids=lambda f: f.__name__)
+def test_base_fused_pin(pin):
+    pin(base_fused_ref)
 
 
 def test_bf16_round_known_values():

@@ -3,7 +3,7 @@ that the pins catch every one of them."""
 import numpy as np
 import pytest
 
-from oracle import apply_ref, segment_ref, shrink_error_bound
+from oracle import apply_ref, base_fused_ref, segment_ref, shrink_error_bound
 
 import oracle_pins as P
 
@@ -292,3 +292,47 @@ def test_bound_unmutated_copy_passes():
         pin(fn)
     for pin in P.SHRINK_BOUND_PINS:
         pin(shrink_error_bound)
+
+
+def _fused_mutant(kind):
+    """Copies of the base-fused oracle with a plausible mistake planted."""
+    def fn(x, ids, W0, A_list, B_list, scales):
+        W = np.asarray(W0, np.float64)
+        if kind == "base_transposed" and W.shape[0] == W.shape[1]:
+            W = W.T
+        if kind == "no_base":
+            W = np.zeros_like(W)
+        y = np.asarray(x, np.float64) @ W.T
+        if kind == "base_twice":
+            y = 2 * y
+        if kind == "base_only_with_adapter":
+            keep = np.array([0 <= int(a) < len(A_list) for a in ids])
+            y = y * keep[:, None]
+        delta = apply_ref(x, ids, A_list, B_list, scales, y0=np.zeros_like(y))
+        if kind == "no_branch":
+            delta = 0 * delta
+        if kind == "branch_twice":
+            delta = 2 * delta
+        return y + delta
+    return fn
+
+
+FUSED_MUTANTS = ["base_transposed", "no_base", "base_twice", "base_only_with_adapter", "no_branch", "branch_twice"]
+
+
+@pytest.mark.parametrize("kind", FUSED_MUTANTS)
+def test_fused_mutant_is_caught(kind):
+    fn = _fused_mutant(kind)
+    caught = []
+    for pin in P.FUSED_PINS:
+        try:
+            pin(fn)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"mutant {kind} passed every pin"
+
+
+def test_fused_unmutated_copy_passes():
+    for pin in P.FUSED_PINS:
+        pin(_fused_mutant("none"))
+        pin(base_fused_ref)
