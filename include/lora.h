@@ -283,6 +283,36 @@ int lora_apply_batched_noalloc(const lora_store* store_host, const void* x, int6
                                void* stream);
 
 /*
+ * The base layer with the adapter branch in its epilogue ("Compress then
+ * Serve" section 3: the adapted layer computes (W0 + B A) x; section 11: the
+ * base product is shared by the batch and each request adds its branch):
+ *   y[t] = W0 x[t] + s_a B_a (A_a x[t])   for a = ids[t] in [0, n), r_a > 0,
+ *   y[t] = W0 x[t]                        for every other token.
+ * y is overwritten, and written once: the branch is added to the base
+ * product's float32 accumulators before y is rounded to bf16.
+ *   W0 [d_out, ldw] : device, bf16, row-major, the layer's [out, in]
+ *                     orientation (y = x W0^T); ldw >= d_in, ldw % 8 == 0,
+ *                     16-byte aligned.
+ *   x [T, ldx], y [T, ldy] : device bf16 rows as in lora_apply_batched; y
+ *                     must not overlap x or W0.
+ *   ids [T]         : device int32 adapter ids (-1 or any id outside [0, n):
+ *                     base only), or NULL for the base product alone.
+ *   ws              : lora_workspace_bytes(store, T) bytes when ids is given
+ *                     (the grouping, plan and partial sums); may be NULL
+ *                     without ids.
+ * Enqueues the grouping and the shrink (with ids) and one GEMM kernel.
+ * Accuracy: float32 accumulation of the bf16 products; h enters the branch
+ * as the exact pair hi + lo of bf16 values (about 16 significant bits).
+ * Errors: INVALID_ARG (null pointers, ldw < d_in, T < 0, ws too small);
+ * UNSUPPORTED (a float32 store, rows not 16-byte aligned, T above
+ * LORA_SEGMENT_MAX_T or n above LORA_SEGMENT_MAX_N with ids; 256 * ldw * 2,
+ * T * ldx * 2 or R * d_out * 2 bytes at or above 2^31).
+ */
+int lora_apply_base_fused(const lora_store* store_host, const void* W0, int64_t ldw, const void* x, int64_t ldx,
+                          void* y, int64_t ldy, int T, const int32_t* ids, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/*
  * One kernel of lora_apply_batched at a time, for measuring each alone:
  * phases = 1 forms the plan and runs the shrink (partial sums and each
  * sub-tile's metadata into ws), 2 the expand only (from the plan, metadata

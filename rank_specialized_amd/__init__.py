@@ -27,7 +27,7 @@ from ._lib import LoraError, lora_store  # noqa: F401
 __all__ = [
     "Store", "Segmentation", "LoraError", "lora_store_bytes", "lora_pack_retained",
     "lora_segment", "lora_plan_bytes", "lora_group", "lora_apply_planned", "lora_workspace_bytes", "lora_shrink", "lora_expand", "lora_apply_batched",
-    "lora_apply_batched_phases", "lora_apply_batched_noalloc", "lora_apply_launches", "JDStore", "lora_jd_pack", "lora_jd_workspace_bytes",
+    "lora_apply_batched_phases", "lora_apply_batched_noalloc", "lora_apply_launches", "lora_apply_base_fused", "JDStore", "lora_jd_pack", "lora_jd_workspace_bytes",
     "lora_jd_apply", "lora_ranks_uniform", "lora_ranks_spectral", "RsvdFactors", "lora_rsvd_workspace_bytes",
     "lora_rsvd_factor", "lora_rsvd_write", "MultiStore", "lora_pack_multi", "lora_multi_workspace_bytes",
     "lora_apply_multi", "load_library",
@@ -297,6 +297,25 @@ def lora_apply_batched_noalloc(store: Store, x: torch.Tensor, y: torch.Tensor, *
     L.check("lora_apply_batched_noalloc", L.lib().lora_apply_batched_noalloc(
         store.ref(), _p(x), _rows(x, "x"), _p(y), _rows(y, "y"), T, _p(ids) if ids is not None else None,
         so, pm, _stream(x)))
+    return y
+
+
+def lora_apply_base_fused(store: Store, W0: torch.Tensor, x: torch.Tensor, y: torch.Tensor, *,
+                          ids: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = x W0^T + s_a B_a (A_a x) per token (overwrites y): the base layer
+    W0 [d_out, d_in] with the adapter branch added in its epilogue, y written
+    once.  Without ids: the base product alone.  bf16 stores only."""
+    T = x.shape[0]
+    if W0.dim() != 2 or W0.shape[0] != store.d_out or W0.shape[1] < store.d_in:
+        raise ValueError("W0 must be [d_out, >= d_in]")
+    if ids is not None:
+        if ids.dtype != torch.int32 or not ids.is_contiguous():
+            raise ValueError("ids must be a contiguous int32 vector")
+        ws = _ws(store, T, ws, x.device)
+    L.check("lora_apply_base_fused", L.lib().lora_apply_base_fused(
+        store.ref(), _p(W0), _rows(W0, "W0"), _p(x), _rows(x, "x"), _p(y), _rows(y, "y"), T,
+        _p(ids) if ids is not None else None, ws.data_ptr() if ws is not None else None,
+        ws.numel() if ws is not None else 0, _stream(x)))
     return y
 
 

@@ -72,6 +72,7 @@ SIGNATURES = {
     "lora_apply_planned": (I, [C.POINTER(lora_store), P, I64, P, I64, I, P, SZ, P, SZ, P]),
     "lora_apply_planned_phases": (I, [C.POINTER(lora_store), P, I64, P, I64, I, P, SZ, P, SZ, P, I]),
     "lora_apply_launches": (I, [C.POINTER(lora_store), I, I]),
+    "lora_apply_base_fused": (I, [C.POINTER(lora_store), P, I64, P, I64, P, I64, I, P, P, SZ, P]),
     "lora_jd_workspace_bytes": (SZ, [C.POINTER(lora_jd_store), I]),
     "lora_jd_apply": (I, [C.POINTER(lora_jd_store), P, I64, P, I64, I, P, P, SZ, P]),
     "lora_ranks_uniform": (I, [I, P, C.c_double, I, P]),

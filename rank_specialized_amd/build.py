@@ -20,7 +20,7 @@ OUT = os.path.join(HERE, "librank_specialized.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 ARCH = os.environ.get("LORA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.hip", "pack.hip", "segment.hip", "group.hip", "shrink.hip", "expand.hip", "decode.hip", "jd.hip", "rsvd.hip", "multi.hip", "validate.cpp", "ranks.cpp"]
+SOURCES = ["api.hip", "pack.hip", "segment.hip", "group.hip", "shrink.hip", "expand.hip", "decode.hip", "jd.hip", "rsvd.hip", "multi.hip", "fused.hip", "validate.cpp", "ranks.cpp"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}"]

@@ -343,6 +343,51 @@ int lora_apply_batched_noalloc(const lora_store* store_host, const void* x, int6
                     (size_t)LORA_NOALLOC_SCRATCH_BYTES, stream, 3);
 }
 
+// ------------------------------------------------------- base layer fused
+int lora_apply_base_fused(const lora_store* store_host, const void* W0, int64_t ldw, const void* x, int64_t ldx,
+                          void* y, int64_t ldy, int T, const int32_t* ids, void* ws, size_t ws_bytes,
+                          void* stream) {
+  int st = check_store(store_host);
+  if (st != LORA_OK) return st;
+  const lora_store& s = *store_host;
+  if (T < 0) return LORA_ERR_INVALID_ARG;
+  if (s.dtype != LORA_DTYPE_BF16) return LORA_ERR_UNSUPPORTED;
+  if ((st = check_rows(x, ldx, s.d_in, s.dtype, T)) != LORA_OK) return st;
+  if ((st = check_rows(y, ldy, s.d_out, s.dtype, T)) != LORA_OK) return st;
+  if (W0 == nullptr) return LORA_ERR_INVALID_ARG;
+  if ((st = check_rows(W0, ldw, s.d_in, s.dtype, s.d_out)) != LORA_OK) return st;
+  constexpr int64_t kLimit = (int64_t)1 << 31;  // 32-bit buffer offsets
+  if (256 * ldw * 2 >= kLimit || (int64_t)T * ldx * 2 >= kLimit) return LORA_ERR_UNSUPPORTED;
+  if (ids != nullptr) {
+    if (T > LORA_SEGMENT_MAX_T || s.n > LORA_SEGMENT_MAX_N) return LORA_ERR_UNSUPPORTED;
+    if ((int64_t)s.R * s.d_out * 2 >= kLimit) return LORA_ERR_UNSUPPORTED;
+    if ((st = check_ws(store_host, T, ws, ws_bytes)) != LORA_OK) return st;
+  }
+  if (T == 0) return LORA_OK;
+  hipStream_t strm = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  const int32_t* perm = nullptr;
+  if (ids != nullptr) {
+    // The grouping with its permutation kept in ws (the GEMM takes tokens in
+    // grouped order), the plan, then the shrink's partial sums.
+    const WsLayout L = ws_layout(T, s.n, s.d_in, s.r_max, s.dtype);
+    char* base = reinterpret_cast<char*>(ws);
+    int32_t* so = reinterpret_cast<int32_t*>(base + L.seg_off);
+    int32_t* pm = reinterpret_cast<int32_t*>(base + L.perm);
+    char* pl = base + L.plan;
+    if (group_fits(T, s.n)) {
+      e = launch_group(ids, T, s.n, nullptr, 0, so, pm, pl, nullptr, strm);
+    } else {
+      e = launch_segment(ids, T, s.n, so, pm, nullptr, strm);
+      if (e == hipSuccess) e = launch_plan(so, pm, T, s.n, pl, nullptr, nullptr, strm);
+    }
+    if (e == hipSuccess) e = launch_shrink(s, pl, T, x, ldx, ws, strm);
+    perm = pm;
+  }
+  if (e == hipSuccess) e = launch_base_fused(s, W0, ldw, x, ldx, y, ldy, T, perm, ids, ws, strm);
+  return e == hipSuccess ? LORA_OK : hip_fail(e);
+}
+
 // Shared-basis workspace: h [T][ldp] | the basis store's workspace.
 static size_t jd_h_bytes(const lora_store& b, int T) {
   return align_up((size_t)(T > 0 ? T : 0) * (size_t)partial_ld(b.r_max) * 4, 256);

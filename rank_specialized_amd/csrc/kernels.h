@@ -51,6 +51,15 @@ hipError_t launch_reduce_partials(const lora_store& s, const char* plan, int T, 
 hipError_t launch_expand(const lora_store& s, const char* plan, int T, const void* ws, const float* h, int64_t ldh,
                          void* y, int64_t ldy, hipStream_t stream);
 
+// The base layer with the branch in its epilogue (bf16 store):
+// y = x W0^T + s_a B_a h over tiles of 256 outputs x 256 tokens, tokens in
+// grouped order through perm (nullptr: identity); with ids == nullptr the
+// base product alone.  h comes from the shrink's partial sums in ws.
+size_t base_fused_lds_bytes();
+hipError_t launch_base_fused(const lora_store& s, const void* w, int64_t ldw, const void* x, int64_t ldx, void* y,
+                             int64_t ldy, int T, const int32_t* perm, const int32_t* ids, const void* ws,
+                             hipStream_t stream);
+
 // Retained-factor construction (r-SVD): per adapter, the Grams of B and A^T
 // (float64 MFMA), Cholesky and the core C, its Jacobi SVD, W_B and W_A, in
 // ws; the write forms B W_B and W_A^T A into a store's buffers.

@@ -144,7 +144,7 @@ inline int64_t partial_ld(int r_max) { return (int64_t)align_up((size_t)(r_max <
 // (from ids, or a plan from a caller's seg_off / perm); a call given a plan
 // leaves them unused.
 struct WsLayout {
-  size_t meta, part, plan, seg_off, perm, total;
+  size_t meta, part, plan, seg_off, perm, hs, total;
 };
 inline WsLayout ws_layout(int T, int n, int d_in, int r_max, int dtype) {
   WsLayout L;
@@ -154,7 +154,9 @@ inline WsLayout ws_layout(int T, int n, int d_in, int r_max, int dtype) {
   L.plan = L.part + align_up((size_t)sp.S * (size_t)T * (size_t)partial_ld(r_max) * 4, 256);
   L.seg_off = L.plan + align_up(plan_bytes(T, n), 256);
   L.perm = L.seg_off + align_up((size_t)(n + 2) * 4, 256);
-  L.total = L.perm + align_up((size_t)T * 4, 256);
+  L.hs = L.perm + align_up((size_t)T * 4, 256);
+  // The base-fused apply's s h as bf16 pairs hi, lo: [T][2][ldp].
+  L.total = L.hs + align_up((size_t)T * (size_t)partial_ld(r_max) * 4, 256);
   return L;
 }
 

@@ -274,14 +274,16 @@ def _layout_bytes(T, n, d_in, r_max, e):
     (a chunk is 8 waves x 8 K steps of 64 bytes, or the smallest multiple of
     that keeping S at most 8) at row stride r_max rounded up to 8; the plan (256-byte
     header + one 128-byte entry per possible sub-tile); seg_off [n + 2] and
-    perm [T]; each part 256-byte aligned."""
+    perm [T]; s h as two bf16 values per rank for the base-fused apply
+    ([T][2][ldp]); each part 256-byte aligned."""
     up = lambda v: -(-v // 256) * 256
     max_sub = (T + 15 * min(n, T)) // 16 if T > 0 else 0
     unit = 8 * 8 * 4 * (16 // e)  # 8 waves x 8 K steps of 64 bytes
     mult = max(1, -(-(-(-d_in // unit)) // 8))
     S = max(1, -(-d_in // (mult * unit)))
     ldp = -(-max(r_max, 1) // 8) * 8
-    return up(16 * max_sub) + up(S * T * ldp * 4) + up(256 + 128 * max_sub) + up((n + 2) * 4) + up(T * 4)
+    return (up(16 * max_sub) + up(S * T * ldp * 4) + up(256 + 128 * max_sub) + up((n + 2) * 4) + up(T * 4)
+            + up(T * ldp * 4))
 
 
 def test_plan_bytes(lib):
@@ -309,6 +311,35 @@ def test_group_rejects_before_launch(lib):
     assert call(plan=FAKE + 4) == 2
     assert call(T=L.LORA_SEGMENT_MAX_T + 1) == 2
     assert call(n=L.LORA_SEGMENT_MAX_N + 1) == 2
+
+
+def test_base_fused_rejects_before_any_hip_call(lib):
+    """lora_apply_base_fused checks every argument before any HIP call."""
+    st = _store()  # bf16, d_in 64, d_out 32
+    f = lib.lora_apply_base_fused
+    big = 1 << 30
+
+    def call(s=st, w=FAKE, ldw=64, x=FAKE, ldx=64, y=FAKE, ldy=32, T=16, ids=FAKE, ws=FAKE, wsb=big):
+        return f(C.byref(s) if s is not None else None, w, ldw, x, ldx, y, ldy, T, ids, ws, wsb, None)
+
+    assert call(s=None) == 1
+    assert call(s=_store(dtype=0)) == 2          # float32 store
+    assert call(T=-1) == 1
+    assert call(w=None) == 1
+    assert call(ldw=56) == 1                      # W0 rows shorter than d_in
+    assert call(ldw=68) == 2                      # W0 rows off 16 bytes
+    assert call(w=FAKE + 8) == 2
+    assert call(ldw=1 << 22) == 2                 # a 256-row tile of W0 spans 2^31 bytes
+    assert call(T=1 << 14, ldx=1 << 16) == 2      # x spans 2^31 bytes
+    assert call(s=_store(d_out=1 << 20, R=1 << 10), ldy=1 << 20) == 2   # B spans 2^31 bytes
+    assert call(x=None) == 1
+    assert call(ldy=16) == 1
+    assert call(ws=None) == 1
+    assert call(wsb=16) == 1
+    assert call(T=L.LORA_SEGMENT_MAX_T + 1) == 2
+    assert call(T=0) == 0
+    assert call(T=0, ids=None, ws=None, wsb=0, x=None, y=None) == 0
+    assert lib.lora_last_hip_error() == 0
 
 
 def test_apply_planned_rejects_before_launch(lib):

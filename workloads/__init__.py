@@ -12,7 +12,9 @@ from .configs import (  # noqa: F401
     FLEET_PROJECTIONS,
     Module,
     Workload,
+    base_weight,
     bf16_bits,
+    fleet_base_weight,
     fleet_ids,
     fleet_module_shapes,
     fleet_ranks,

@@ -330,3 +330,18 @@ def make_random_workload(seed: int, T: int, n: int, d_in: int, d_out: int, ranks
     y0a = _quant(rng.normal(0, 1, size=(T, d_out)), dtype) if y0 else None
     mod = Module(d_in, d_out, ranks, scales, As, Bs, name=f"random{seed}")
     return Workload(f"rand{seed}", dtype, ids, x, mod, y0=y0a, meta={"seed": seed})
+
+
+def base_weight(seed: int, d_out: int, d_in: int, *, integer: bool = False) -> np.ndarray:
+    """Frozen base weight W0 [d_out, d_in] of a layer (the layer computes
+    W0 x): N(0, 1/d_in) entries rounded to bf16, or integers in [-2, 2]."""
+    rng = _rng(7, seed, d_out, d_in)
+    if integer:
+        return rng.integers(-2, 3, size=(d_out, d_in)).astype(np.float32)
+    return _quant(rng.normal(0.0, 1.0 / math.sqrt(d_in), size=(d_out, d_in)), "bf16")
+
+
+def fleet_base_weight(layer: int, proj: int, *, integer: bool = False) -> np.ndarray:
+    """W0 of one fleet module (the Qwen2-7B-like shapes), seeded by its place."""
+    _, d_in, d_out, _ = FLEET_PROJECTIONS[proj]
+    return base_weight(1000 + layer * len(FLEET_PROJECTIONS) + proj, d_out, d_in, integer=integer)
