@@ -70,6 +70,7 @@ def sources_of(kernel: str):
 
 
 PEAK_FP64_TFLOPS = 78.6  # 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2.4 GHz
+PEAK_BF16_TFLOPS = 2500.0  # dense bf16 matrix-core peak of the MI355X
 
 WORKLOAD_NAMES = {
     "1": "tiny-fp32: d_in=d_out=256 f32, 4 adapters ranks {1,2,3,4}, T=16",
@@ -85,6 +86,9 @@ WORKLOAD_NAMES = {
               "3584->3584 projection, bf16, spectral-budget ranks (floor 4, budget 6 per adapter)",
     "ranks-fleet": "retained-rank allocation on the host: 1024 adapters x 196 modules (200704 units) of "
                    "original rank 64, uniform (ratio 1/12, floor 4) and spectral at the same budget",
+    "fused": "base layer with the branch fused: the fleet step's L0.q (3584->3584) and L0.gate (3584->18944) "
+             "modules with a bf16 W0, y = x W0^T + s B A x for T=4096 Zipf(1.1) ids, against hipBLASLt's GEMM "
+             "followed by the apply",
     "5U": "fleet decode step: 28 layers x 7 projections (3584/512/18944 dims) bf16, 1024 adapters rank 6 "
           "(orig 64), T=4096 Zipf(1.1) ids, one grouping and plan reused by 196 applies (q/k/v and gate/up "
           "concurrent)",
@@ -104,6 +108,9 @@ def parse_args():
     p.add_argument("--no-padded", action="store_true")
     p.add_argument("--no-multi", action="store_true", help="fleet: skip the multi-slice (q/k/v, gate/up) step")
     p.add_argument("--no-5u", action="store_true", help="fleet 5S: skip the uniform-rank (5U) step")
+    p.add_argument("--no-fused", action="store_true", help="fleet: skip the base-fused comparison")
+    p.add_argument("--legs", default="fused,unfused,gemm,gemm_hipblaslt",
+                   help="base-fused comparison: which legs to time (comma list; counter runs take fewer)")
     p.add_argument("--no-kernels", action="store_true", help="skip the per-kernel timing passes")
     p.add_argument("--streams", type=int, default=3,
                    help="fleet: run the modules of one stage (q/k/v; gate/up) on up to this many streams")
@@ -413,7 +420,8 @@ def summarize_trace(trace_dir: str):
         with open(path) as f:
             rows += [r for r in csv.DictReader(f) if "lora::" in r["Kernel_Name"]]
     ev = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
-                 r["Kernel_Name"].split("(")[0].replace("void ", "")) for r in rows)
+                 r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", ""))
+                for r in rows)
     stats = {}
     for i, (s0, e0, k) in enumerate(ev):
         prev_end = ev[i - 1][1] if i else -1
@@ -859,7 +867,7 @@ def run_ranks(args):
 
 
 # ------------------------------------------------------------------ fleet
-def build_fleet(rs, torch, key: str, dev, pad_to_rmax: bool):
+def build_fleet(rs, torch, key: str, dev, pad_to_rmax: bool, layers=None):
     """The 196 module stores of one decode step.  Factor values are drawn on
     the GPU (N(0, 1/sqrt(d)), bf16): the apply's time depends only on shapes,
     ranks and ids, and parity of fleet modules is tested on the oracle's
@@ -870,6 +878,8 @@ def build_fleet(rs, torch, key: str, dev, pad_to_rmax: bool):
     gen.manual_seed(2611)
     stores, meta = [], []
     for (layer, proj, name, d_in, d_out, kind) in fleet_module_shapes():
+        if layers is not None and layer >= layers:
+            break
         r = ranks[layer, proj]
         off = np.concatenate([[0], np.cumsum(r)])
         R = int(off[-1])
@@ -980,6 +990,9 @@ def run_fleet_key(args, rs, torch, dev, key, xs, ys, ids, full: bool):
                            "kernel": f"{dom}_kernel<BF16>, mean over the 196 modules of a step",
                            "algorithmic_bytes_per_launch": round(dom_bytes), "avg_launch_us": kern[dom]["avg_us"]}
 
+    if not args.no_fused:
+        res["base_fused"] = run_base_fused(args, rs, torch, dev, stores, meta, xs, ids, T)
+
     if not args.no_multi:
         # The projections that share an input applied together (q/k/v,
         # gate/up): one x read per group, one call per stage.
@@ -1028,7 +1041,69 @@ def run_fleet_key(args, rs, torch, dev, key, xs, ys, ids, full: bool):
     return res
 
 
-def fleet_inputs(torch, dev, meta_shapes, T=4096):
+def run_base_fused(args, rs, torch, dev, stores, meta, xs, ids, T=4096):
+    """The base layer with the branch in its epilogue (lora_apply_base_fused)
+    against the unfused pair (hipBLASLt's GEMM through torch.matmul, then
+    lora_apply_batched), and the two GEMMs alone, for the L0.q and L0.gate
+    modules of the fleet step.  W0 is drawn on the GPU (N(0, 1/d_in), bf16).
+    Each figure: consecutive eager calls, events around each (hipBLASLt is
+    kept out of graph capture; every call runs 100 us or more, so launches
+    stay ahead of the GPU), caches warm (the GEMMs are bound by the matrix
+    cores, not by HBM)."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2613)
+    out = {}
+    reps = max(MIN_SEGMENTS, min(args.steps, 20))
+    for name, idx in (("q", 0), ("gate", 4)):
+        st, m = stores[idx], meta[idx]
+        d_in, d_out = m[3], m[4]
+        x = xs[(m[0], m[5])]
+        W0 = (torch.randn(d_out, d_in, generator=gen, device=dev) * d_in ** -0.5).to(torch.bfloat16)
+        y = torch.empty(T, d_out, dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(rs.lora_workspace_bytes(st, T), dtype=torch.uint8, device=dev)
+        Wt = W0.t()
+        legs = {
+            "fused": lambda: rs.lora_apply_base_fused(st, W0, x, y, ids=ids, ws=ws),
+            "unfused": lambda: (torch.matmul(x, Wt, out=y), rs.lora_apply_batched(st, x, y, ids=ids, ws=ws)),
+            "gemm": lambda: rs.lora_apply_base_fused(st, W0, x, y),
+            "gemm_hipblaslt": lambda: torch.matmul(x, Wt, out=y),
+        }
+        flops = 2.0 * T * d_in * d_out
+        r = {"shape": f"{T} x {d_in} -> {d_out}", "gemm_flops": flops}
+        wanted = args.legs.split(",")
+        for leg, f in legs.items():
+            if leg not in wanted:
+                continue
+            t = time_replays(torch, f, reps, 2, False)
+            us = t["ms_per_step"] * 1e3
+            r[leg] = {"us": round(us, 2), "median_us": round(t["dist"]["median_ms"] * 1e3, 2),
+                      "tflops": round(flops / (us * 1e-6) / 1e12, 1)}
+        if "fused" in r and "unfused" in r:
+            r["fused_speedup"] = round(r["unfused"]["us"] / r["fused"]["us"], 3)
+        r["y_bytes_not_moved"] = 2 * T * d_out * 2  # the unfused expand reads y and writes it again
+        if "fused" in r:
+            r["roofline"] = {"bound": "mfma", "achieved": r["fused"]["tflops"], "peak": PEAK_BF16_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(r["fused"]["tflops"] / PEAK_BF16_TFLOPS, 4)}
+        out[name] = r
+        del W0, y, ws
+        torch.cuda.empty_cache()
+    return out
+
+
+def run_fused_only(args, rs, torch, dev):
+    """--config fused: the base-fused comparison alone (for counter runs)."""
+    from workloads import fleet_ids, fleet_module_shapes
+    T, n = 4096, 1024
+    ids = torch.from_numpy(fleet_ids(T, n)).to(dev)
+    shapes = fleet_module_shapes()[:7]
+    xs, _ = fleet_inputs(torch, dev, shapes, T, with_y=False)
+    stores, meta = build_fleet(rs, torch, "5S", dev, False, layers=1)
+    res = run_base_fused(args, rs, torch, dev, stores, meta, xs, ids, T)
+    print(json.dumps({"metric": "base-fused apply us per call", "config": {"workload": WORKLOAD_NAMES["fused"]},
+                      "base_fused": res}), flush=True)
+
+
+def fleet_inputs(torch, dev, meta_shapes, T=4096, with_y=True):
     """The step's activations (drawn on the GPU, N(0, 1), bf16): per layer
     one input per kind (q/k/v, o, gate/up, down), and one y per module."""
     from workloads import FLEET_INPUT_DIMS
@@ -1037,7 +1112,7 @@ def fleet_inputs(torch, dev, meta_shapes, T=4096):
     layers = max(m[0] for m in meta_shapes) + 1
     xs = {(l, k): torch.randn(T, d, generator=gen, device=dev).to(torch.bfloat16)
           for l in range(layers) for k, d in enumerate(FLEET_INPUT_DIMS)}
-    ys = [torch.randn(T, m[4], generator=gen, device=dev).to(torch.bfloat16) for m in meta_shapes]
+    ys = [torch.randn(T, m[4], generator=gen, device=dev).to(torch.bfloat16) for m in meta_shapes] if with_y else None
     return xs, ys
 
 
@@ -1072,7 +1147,8 @@ def run_fleet(args, rs, torch, dev, cpu):
         "gbps": round(res["gbps"], 1), "hbm_frac": round(res["gbps"] / PEAK_GBPS, 4),
         "bytes_per_step": res["bytes_per_step"], "roofline": res.get("roofline"), "cpu_baseline": cpu,
         "kernels": res.get("kernels"), "padded": res.get("padded", {}), "multi_slice": res.get("multi_slice", {}),
-        "fleet_5U": other, "streams": max(1, args.streams), "wall_s_timed": round(res["wall_s"], 6),
+        "fleet_5U": other, "base_fused": res.get("base_fused"), "streams": max(1, args.streams),
+        "wall_s_timed": round(res["wall_s"], 6),
         "timed_as": "eager launches" if args.no_graph else "HIP-graph replays of one captured step",
         "kernel_sources_sha": kernel_source_digest(),
     }
@@ -1127,6 +1203,8 @@ def main():
         del src, dst
     if key in ("5U", "5S"):
         run_fleet(args, rs, torch, dev, cpu)
+    elif key == "fused":
+        run_fused_only(args, rs, torch, dev)
     elif key.startswith("jd-"):
         run_jd(args, rs, torch, dev, key)
     elif key.startswith("rsvd-"):
