@@ -276,16 +276,21 @@ def percentiles(per_step_ms):
 
 
 class Flush:
-    """A 2 GiB buffer read and written between timed segments (outside the
-    timed events): afterwards neither the L2s nor the 256 MB last-level cache
-    hold anything a step reads."""
+    """A 2 GiB buffer read between timed segments (outside the timed
+    events): afterwards neither the L2s nor the 256 MB last-level cache hold
+    anything a step reads.  Read only, so that no dirty lines of the flush
+    itself are still being written back when the timed segment starts (with
+    a read-and-write flush, decode-spectral measured 73.5 against 65.0 us
+    per step, prefill 181.0 against 167.9)."""
 
     def __init__(self, torch, dev, enabled: bool):
-        self.buf = torch.zeros(FLUSH_BYTES // 4, dtype=torch.float32, device=dev) if enabled else None
+        self.torch = torch
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev) if enabled else None
+        self.out = torch.zeros((), dtype=torch.float32, device=dev) if enabled else None
 
     def __call__(self):
         if self.buf is not None:
-            self.buf.add_(1.0)
+            self.torch.sum(self.buf, dim=0, out=self.out)
 
 
 def time_steps(torch, step, copies, K, W, flush, graph=True):
