@@ -544,15 +544,21 @@ def run_config(args, rs, torch, dev, key, cpu):
     # The two-launch form's kernels, each alone (for a fused call: a comparison).
     split = {}
     if not args.no_kernels:
+        # Each kernel alone on a plan formed once (lora_group): the shrink,
+        # then the expand on what the shrink left in ws; the grouping alone.
+        seg = rs.lora_group(ids, m.n)
         for name, phase in (("shrink", 1), ("expand", 2)):
-            kt = time_steps(torch, lambda c, ph=phase: rs.lora_apply_batched_phases(c.store, c.x, c.y, ph, ids=ids,
-                                                                                  ws=ws),
+            kt = time_steps(torch, lambda c, ph=phase: rs.lora_apply_planned(c.store, c.x, c.y, seg, ws=ws, phases=ph),
                             copies, K, 1, flush, graph=graph)
             us = kt["ms_per_step"] * 1e3
             split[name] = {"avg_us": round(us, 2), "launches": K, "algorithmic_bytes": nbytes[name],
                            "gbps": round(nbytes[name] / (us * 1e-6) / 1e9, 1),
-                           "timed_as": "graph replays of that kernel alone, each segment after a cache flush "
-                                       "(an expand alone then reads a cold plan and partial sums)"}
+                           "timed_as": "graph replays of that kernel alone on a plan formed once, each segment "
+                                       "after a cache flush (an expand alone then reads a cold plan and partial "
+                                       "sums)"}
+        gt = time_steps(torch, lambda c: rs.lora_group(ids, m.n, seg=seg), copies, K, 1, flush, graph=graph)
+        split["grouping"] = {"avg_us": round(gt["ms_per_step"] * 1e3, 2), "launches": K,
+                             "timed_as": "lora_group alone (seg_off, perm and the plan in one kernel)"}
     gbps = nbytes["total"] / (ms * 1e-3) / 1e9
     if launches == 1:
         kern = {"decode_apply": {"avg_us": round(ms * 1e3, 2), "launches": K,
@@ -561,7 +567,7 @@ def run_config(args, rs, torch, dev, key, cpu):
         dom, dom_bytes = "decode_apply", nbytes["total"]
     else:
         kern = split
-        dom = max(("shrink", "expand"), key=lambda k: kern[k]["avg_us"]) if split else "shrink"
+        dom = max(("shrink", "expand"), key=lambda k: kern[k]["avg_us"]) if split else "shrink"  # not the grouping
         dom_bytes = nbytes[dom]
     dom_us = kern[dom]["avg_us"] if dom in kern else ms * 1e3
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
