@@ -441,7 +441,7 @@ static hipError_t launch_expand_impl(const lora_store& s, const lora_store* slic
   a.n = s.n;
   a.r_max = s.r_max;
   a.R = s.R;
-  a.S_max = shrink_split(s.d_in, s.dtype).S;
+  a.S_max = shrink_split(s.d_in, s.dtype, max_sub).S;
   a.y = reinterpret_cast<char*>(y);
   a.ldy_bytes = ldy * elem_bytes(s.dtype);
   a.sl_rank = slice ? slice->rank : nullptr;

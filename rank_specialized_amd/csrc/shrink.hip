@@ -318,7 +318,7 @@ hipError_t launch_shrink(const lora_store& s, const char* plan, int T, const voi
                          hipStream_t stream) {
   const int64_t max_sub = plan_max_subtiles(T, s.n);
   if (max_sub == 0) return hipSuccess;
-  const ShrinkSplit sp = shrink_split(s.d_in, s.dtype);
+  const ShrinkSplit sp = shrink_split(s.d_in, s.dtype, max_sub);
   const WsLayout L = ws_layout(T, s.n, s.d_in, s.r_max, s.dtype);
   char* base = reinterpret_cast<char*>(ws);
   ShrinkArgs a;
@@ -366,7 +366,7 @@ hipError_t launch_reduce_partials(const lora_store& s, const char* plan, int T, 
   const int64_t ldp = partial_ld(s.r_max);
   hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)max_sub), dim3(256), 0, stream, plan, (int)max_sub,
                      reinterpret_cast<const TileMeta*>(base + L.meta), reinterpret_cast<const float*>(base + L.part),
-                     ldp, (int64_t)T * ldp, T, s.n, s.r_max, shrink_split(s.d_in, s.dtype).S, h, ldh);
+                     ldp, (int64_t)T * ldp, T, s.n, s.r_max, shrink_split(s.d_in, s.dtype, max_sub).S, h, ldh);
   return hipGetLastError();
 }
 

@@ -72,13 +72,18 @@ def hbits(y: torch.Tensor) -> np.ndarray:
     return y.view(torch.int32).cpu().numpy()
 
 
-def chunks_of(d_in, r, e):
+def chunks_of(d_in, r, e, T=0, n=0):
     """Partial sums of an h value (the shrink's chunks of d_in) - restated:
     8 waves x 8 K steps of 64 bytes per chunk (2048 bf16, 1024 float32
-    values), times the smallest multiple that keeps them at most 8; the
-    same for every rank r."""
+    values), times the smallest multiple that keeps them at most 8; an input
+    of up to two such units goes in one chunk when the call can hold 1024
+    sub-tiles or more; the same for every rank r."""
     unit = 8 * 8 * 4 * (16 // e)
-    mult = max(1, -(-(-(-d_in // unit)) // 8))
+    units = -(-d_in // unit)
+    mult = max(1, -(-units // 8))
+    max_sub = (T + 15 * min(n, T)) // 16 if T > 0 else 0
+    if units <= 2 and max_sub >= 1024:
+        mult = units
     return max(1, -(-d_in // (mult * unit)))
 
 
@@ -89,7 +94,7 @@ def ws_offsets(T, n, d_in, r_max, e):
     then the plan; each part 256-byte aligned."""
     up = lambda v: -(-v // 256) * 256
     max_sub = (T + 15 * min(n, T)) // 16 if T > 0 else 0
-    S = chunks_of(d_in, r_max, e)
+    S = chunks_of(d_in, r_max, e, T, n)
     ldp = -(-max(r_max, 1) // 8) * 8
     part = up(16 * max_sub)
     return 0, part + up(S * T * ldp * 4), S
