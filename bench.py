@@ -1127,6 +1127,32 @@ def fleet_inputs(torch, dev, meta_shapes, T=4096, with_y=True):
     return xs, ys
 
 
+def copy_reference(torch, dev, nbytes=1 << 30, reps=5):
+    """What a plain device copy streams here: torch's copy of nbytes (read
+    nbytes, write nbytes) between two buffers that exceed the last-level
+    cache, events around each of `reps` copies (median).  The apply's expand
+    also reads and writes its y rows, so this is the practical ceiling of a
+    read-write stream on this GPU, beside the 8 TB/s peak."""
+    a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    del a, b
+    torch.cuda.empty_cache()
+    return {"bytes_moved": 2 * nbytes, "ms": round(ms, 4), "gbps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1),
+            "what": "torch copy of 1 GiB (read + write), median of 5"}
+
+
 def run_fleet(args, rs, torch, dev, cpu):
     from workloads import fleet_ids, fleet_module_shapes
     key = args.config
@@ -1158,7 +1184,8 @@ def run_fleet(args, rs, torch, dev, cpu):
         "gbps": round(res["gbps"], 1), "hbm_frac": round(res["gbps"] / PEAK_GBPS, 4),
         "bytes_per_step": res["bytes_per_step"], "roofline": res.get("roofline"), "cpu_baseline": cpu,
         "kernels": res.get("kernels"), "padded": res.get("padded", {}), "multi_slice": res.get("multi_slice", {}),
-        "fleet_5U": other, "base_fused": res.get("base_fused"), "streams": max(1, args.streams),
+        "fleet_5U": other, "base_fused": res.get("base_fused"), "copy_reference": copy_reference(torch, dev),
+        "streams": max(1, args.streams),
         "wall_s_timed": round(res["wall_s"], 6),
         "timed_as": "eager launches" if args.no_graph else "HIP-graph replays of one captured step",
         "kernel_sources_sha": kernel_source_digest(),

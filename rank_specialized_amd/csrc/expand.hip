@@ -245,9 +245,13 @@ __device__ __forceinline__ bool entry_fits(const ExpandArgs& p, int a, int m, in
 
 // ------------------------------------------------------------ vector path
 // float32 B blocks are twice as large: that path stops at rank kVecMaxRank / 2.
-template <typename E>
+template <typename E, int RUN>
+constexpr int vec_rank_cap() {
+  return (RUN > 1 && E::kBytes == 2) ? kVecMaxRankRun : kVecMaxRank * 2 / E::kBytes;
+}
+template <typename E, int RUN>
 __device__ __forceinline__ bool vector_expand(int r, int m) {
-  return r <= kVecMaxRank * 2 / E::kBytes && m <= kVecMaxTokens;
+  return r <= vec_rank_cap<E, RUN>() && m <= kVecMaxTokens;
 }
 
 template <typename E, bool kPart, int R>
@@ -357,7 +361,7 @@ __device__ __forceinline__ void expand_wave(const ExpandArgs& p) {
     hoff = h2;
     sc = p.sl_scale[a];
   }
-  if (vector_expand<E>(r, m)) {
+  if (vector_expand<E, RUN>(r, m)) {
     const int fb = slot / kGroups, tg = slot - fb * kGroups;
     if (fb >= p.fbv || tg * kVecTokens >= m) return;
     // Every lane stays: lanes past d_out load and store nothing but may hold h.
@@ -369,7 +373,7 @@ __device__ __forceinline__ void expand_wave(const ExpandArgs& p) {
       LORA_VEC_CASE(1) LORA_VEC_CASE(2) LORA_VEC_CASE(3) LORA_VEC_CASE(4)
       LORA_VEC_CASE(5) LORA_VEC_CASE(6) LORA_VEC_CASE(7) LORA_VEC_CASE(8)
       default:
-        if constexpr (kVecMaxRank * 2 / E::kBytes > 8) {
+        if constexpr (vec_rank_cap<E, RUN>() > 8) {
           switch (r) {
             LORA_VEC_CASE(9) LORA_VEC_CASE(10) LORA_VEC_CASE(11) LORA_VEC_CASE(12)
             LORA_VEC_CASE(13) LORA_VEC_CASE(14) LORA_VEC_CASE(15) LORA_VEC_CASE(16)

@@ -69,6 +69,21 @@ def test_apply_integer_exact(key):
     assert bad.size == 0, (len(bad), bad[:5], got[tuple(bad[0])], want[tuple(bad[0])])
 
 
+@pytest.mark.parametrize("key,layer,proj", [("5S", 5, 4), ("5S", 20, 5), ("5U", 9, 4)])
+def test_apply_integer_exact_run_form(key, layer, proj):
+    """gate/up modules (3584 -> 18944): calls large enough for the expand's
+    run form, where sub-tiles of up to 8 tokens and rank up to 16 take the
+    vector path; integer data, bit for bit."""
+    dev = device()
+    wl = make_config(key, integer=True, layer=layer, proj=proj)
+    _, _, _, y = _run_apply(wl, dev)
+    ref = _ref(wl)
+    assert np.abs(ref).max() < 2 ** 24
+    got, want = y_host(y), bf16_round_ref(ref)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, (len(bad), bad[:5])
+
+
 @pytest.mark.parametrize("key", ["1", "2", "3", "4"])
 def test_shrink_h_within_fp32_bound(key):
     dev = device()
