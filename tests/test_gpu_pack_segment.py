@@ -7,10 +7,10 @@ import pytest
 import torch
 
 import rank_specialized_amd as rs
-from oracle import segment_ref
+from oracle import apply_ref, bf16_round_ref, segment_ref
 from workloads import make_config, make_random_workload
 
-from gpu_helpers import chunks_of, ws_offsets, TORCH_DTYPE, device, note, pack
+from gpu_helpers import chunks_of, ws_offsets, y_host, TORCH_DTYPE, device, note, pack
 
 pytestmark = pytest.mark.gpu
 
@@ -231,6 +231,43 @@ def test_plan_from_ids(name):
     _, plan_off, S = ws_offsets(T, n, 64, store.r_max, 2)
     _check_plan(ws, want, T, n, plan_off)
     _check_meta(ws, want, ranks, row_off, scales, lambda r: chunks_of(64, r, 2))
+
+
+def test_plan_meta_one_chunk_large_call():
+    """A call with room for 1024 sub-tiles or more and d_in of two chunk
+    units (the fleet's 4096 tokens over 1024 adapters, d_in 3584): every
+    sub-tile records one partial sum (d_in in one chunk, where a smaller call
+    has two), and the apply is the exact result rounded once (integer data,
+    ranks 0..24 on both sides of 16)."""
+    from workloads import fleet_ids
+    dev = device()
+    ids = fleet_ids()
+    n, T, d_in, d_out = 1024, len(ids), 3584, 64
+    rng = np.random.default_rng(57)
+    ranks = rng.integers(0, 25, size=n)
+    Ah = [rng.integers(-2, 3, size=(int(r), d_in)).astype(np.float32) for r in ranks]
+    Bh = [rng.integers(-2, 3, size=(d_out, int(r))).astype(np.float32) for r in ranks]
+    scales = np.full(n, 0.25, np.float32)
+    store = rs.lora_pack_retained([torch.from_numpy(a).to(torch.bfloat16).to(dev) for a in Ah],
+                                  [torch.from_numpy(b).to(torch.bfloat16).to(dev) for b in Bh], scales)
+    xh = rng.integers(-2, 3, size=(T, d_in)).astype(np.float32)
+    x = torch.from_numpy(xh).to(torch.bfloat16).to(dev)
+    y = torch.zeros(T, d_out, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(rs.lora_workspace_bytes(store, T), dtype=torch.uint8, device=dev)
+    note(f"one chunk T={T} n={n} d_in={d_in}")
+    rs.lora_apply_batched(store, x, y, ids=torch.from_numpy(ids).to(dev), ws=ws)
+    torch.cuda.synchronize()
+    so_ref, perm_ref, _ = segment_ref(ids.tolist(), n)
+    row_off = np.concatenate([[0], np.cumsum(ranks)])
+    want = _expected_plan(so_ref, perm_ref, n)
+    assert chunks_of(d_in, 16, 2) == 2 and chunks_of(d_in, 16, 2, T, n) == 1
+    assert any(m == 16 and ranks[a] > 16 for a, _p, m, _j, _t in want)
+    _check_meta(ws, want, ranks, row_off, scales, lambda r: chunks_of(d_in, r, 2, T, n))
+    # Integers: h and every float32 sum are exact, so y is the exact result
+    # rounded once to bf16.
+    ref = apply_ref(xh, ids, Ah, Bh, scales)
+    assert np.abs(ref).max() < 2 ** 24
+    assert np.array_equal(y_host(y), bf16_round_ref(ref))
 
 
 @pytest.mark.parametrize("name", ["3", "out_of_range", "all_same", "many_adapters"])
