@@ -85,11 +85,14 @@ __device__ __forceinline__ void expand_run(const ExpandArgs& p, const TileEntry*
   const uint4 zero = make_uint4(0, 0, 0, 0);
   // Rows of tokens 4g .. 4g + 3 (nullptr: no token), the same for every
   // feature block of the run.
+  // The four indices in one load (an entry always holds 16), not one
+  // guarded load per token: guarded loads were issued one after another.
+  const int4 tk4 = *reinterpret_cast<const int4*>(ent->tok + 4 * g);
+  const int tkv[4] = {tk4.x, tk4.y, tk4.z, tk4.w};
   const char* yrow[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int t = 4 * g + e;
-    const int tok = t < m ? ent->tok[t] : -1;
+    const int tok = 4 * g + e < m ? tkv[e] : -1;
     yrow[e] = (unsigned)tok < (unsigned)p.T ? p.y + (int64_t)tok * p.ldy_bytes : nullptr;
   }
   auto feat = [&](int k) { return (fb0 + k) * kExpandCols + 8 * c; };  // first feature of the lane in block k
@@ -342,18 +345,21 @@ __device__ __forceinline__ void expand_wave(const ExpandArgs& p) {
   constexpr int kGroups = kVecMaxTokens / kVecTokens;
   const int item = __builtin_amdgcn_readfirstlane(blockIdx.x * kExpandWaves + (threadIdx.x >> 6));
   const int st = item / p.slots, slot = item - st * p.slots;
-  if (st >= p.max_sub) return;
+  // The plan's count, the entry's head and the metadata are all read before
+  // the first test, so that they take one round trip (the index clamped into
+  // the plan; the tests decide what is used).
+  const int sc0 = min(st, p.max_sub - 1);
+  const TileEntry* ent = reinterpret_cast<const TileEntry*>(p.plan + kPlanHeaderBytes) + sc0;
   const int count = *reinterpret_cast<const int32_t*>(p.plan);
-  if (st >= count) return;
-  const TileEntry* ent = reinterpret_cast<const TileEntry*>(p.plan + kPlanHeaderBytes) + st;
-  const TileMeta tm = p.meta[st];
-  const int m = ent->m, pos0 = ent->pos0;
-  if (!entry_fits(p, ent->a, m, pos0, tm)) return;
+  const int4 head = *reinterpret_cast<const int4*>(ent);  // a, pos0, m, j
+  const TileMeta tm = p.meta[sc0];
+  const int m = head.z, pos0 = head.y;
+  if ((st >= p.max_sub) | (st >= count) | !entry_fits(p, head.x, m, pos0, tm)) return;
   const int S = kPart ? tm.S : 1;
   int r = tm.r, ro = tm.row_off, hoff = 0;
   float sc = tm.scale;
   if constexpr (kSlice) {  // slice mode: this slice's rank, B rows, scale and h columns
-    const int a = ent->a;
+    const int a = head.x;
     const int r2 = p.sl_rank[a], ro2 = p.sl_row_off[a], h2 = p.sl_hoff[a];
     if (r2 <= 0 || r2 > p.sl_r_max || ro2 < 0 || ro2 > p.sl_R - r2 || h2 < 0 || h2 > r - r2) return;
     r = r2;
