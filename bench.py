@@ -1127,30 +1127,67 @@ def fleet_inputs(torch, dev, meta_shapes, T=4096, with_y=True):
     return xs, ys
 
 
+def _stream_ref_lib():
+    """The benchmark's bandwidth references (libstream_ref.so, built beside the
+    LoRA library): a plain copy and a plain read, 16 bytes per thread with
+    streaming loads and stores.  None when it has not been built."""
+    import ctypes
+    path = os.path.join(ROOT, "rank_specialized_amd", "libstream_ref.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    for name, args in (("stream_ref_copy", [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+                       ("stream_ref_read", [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p])):
+        getattr(lib, name).argtypes = args
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
 def copy_reference(torch, dev, nbytes=1 << 30, reps=5):
-    """What a plain device copy streams here: torch's copy of nbytes (read
-    nbytes, write nbytes) between two buffers that exceed the last-level
-    cache, events around each of `reps` copies (median).  The apply's expand
-    also reads and writes its y rows, so this is the practical ceiling of a
-    read-write stream on this GPU, beside the 8 TB/s peak."""
+    """What plain streams reach here, beside the 8 TB/s peak: torch's copy of
+    nbytes (read nbytes, write nbytes), the reference copy kernel on the same
+    buffers, and the reference read of nbytes (buffers well beyond the
+    last-level cache; events around each of `reps` runs, median).  The expand
+    reads and writes its y rows (a read-write stream); the shrink only reads."""
     a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev)
     b = torch.empty_like(a)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
     a.fill_(1.0)
     b.copy_(a)
     torch.cuda.synchronize()
-    ts = []
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        b.copy_(a)
-        e1.record()
+    lib = _stream_ref_lib()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def timed(fn):
+        fn()
         torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1))
-    ms = float(np.median(ts))
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(f"stream reference failed ({rc})")
+
+    ms = timed(lambda: b.copy_(a))
+    out = {"bytes_moved": 2 * nbytes, "ms": round(ms, 4), "gbps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1),
+           "what": "torch copy of 1 GiB (read + write), median of 5"}
+    if lib is not None:
+        ms_c = timed(lambda: check(lib.stream_ref_copy(a.data_ptr(), b.data_ptr(), nbytes, stream)))
+        ms_r = timed(lambda: check(lib.stream_ref_read(a.data_ptr(), nbytes, sink.data_ptr(), stream)))
+        out["stream_copy_gbps"] = round(2 * nbytes / (ms_c * 1e-3) / 1e9, 1)
+        out["stream_read_gbps"] = round(nbytes / (ms_r * 1e-3) / 1e9, 1)
+        out["stream_what"] = ("reference kernels (libstream_ref.so): copy of 1 GiB (read + write) and read of "
+                              "1 GiB, 16 bytes per thread, streaming loads and stores, median of 5")
     del a, b
     torch.cuda.empty_cache()
-    return {"bytes_moved": 2 * nbytes, "ms": round(ms, 4), "gbps": round(2 * nbytes / (ms * 1e-3) / 1e9, 1),
-            "what": "torch copy of 1 GiB (read + write), median of 5"}
+    return out
 
 
 def run_fleet(args, rs, torch, dev, cpu):

@@ -3,7 +3,9 @@
     python -m rank_specialized_amd.build          # gfx950, -O3
 
 Every source is compiled with hipcc for gfx950 only, with packed-FP32
-instructions disabled, then linked into one shared library.
+instructions disabled, then linked into one shared library.  The benchmark's
+bandwidth references (a plain copy and a plain read) go into a library of
+their own, libstream_ref.so, apart from the LoRA library.
 """
 from __future__ import annotations
 
@@ -17,6 +19,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "librank_specialized.so")
+REF_OUT = os.path.join(HERE, "libstream_ref.so")
+REF_SOURCES = ["stream_ref.hip"]
 BUILD_DIR = os.path.join(HERE, "_build")
 ARCH = os.environ.get("LORA_OFFLOAD_ARCH", "gfx950")
 
@@ -48,18 +52,25 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra)), SOURCES))
-    tmp = OUT + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + REF_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, list(extra)), srcs))
+    _link(objs[: len(SOURCES)], OUT)
+    _link(objs[len(SOURCES):], REF_OUT)
     if verbose:
         print(f"built {OUT}")
+        print(f"built {REF_OUT}")
     return OUT
 
 
