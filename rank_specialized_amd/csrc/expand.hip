@@ -51,16 +51,17 @@
 namespace lora {
 
 struct ExpandArgs {
+  // The plan and the metadata first: a wave's first loads need both.
+  const char* plan;
+  const TileMeta* meta;  // per sub-tile: rank, row offset, scale, partial count (from the shrink)
   const char* b_pack;
   int d_out, T, max_sub;
   int slots;  // waves per sub-tile: max(fbn, (kVecMaxTokens / kVecTokens) fbv)
   int fbn;    // kExpandCols-feature blocks (matrix path)
   int fbv;    // kVecCols-feature blocks (vector path)
   int n, r_max, R, S_max;  // the store's bounds: plan entries outside them are skipped
-  const TileMeta* meta;    // per sub-tile: rank, row offset, scale, partial count (from the shrink)
   const float* hsrc;      // partial sums (kPart) or h
   int64_t ldh, hstride;   // floats
-  const char* plan;
   char* y;
   int64_t ldy_bytes;
   // Slice mode (multi-slice apply): the plan and partial sums come from the
@@ -75,7 +76,7 @@ struct ExpandArgs {
 };
 
 template <typename E, bool kPart, int NQ, int RUN>
-__device__ __forceinline__ void expand_run(const ExpandArgs& p, const TileEntry* ent, int m, int r, int pos0,
+__device__ __forceinline__ void expand_run(const ExpandArgs& p, const int4& tk4, int m, int r, int pos0,
                                            int ro, float sc, int S, int fb0, int nb, int hoff) {
   constexpr int V = E::kVec;
   constexpr int KSTEP = 4 * V;  // ranks per K chunk
@@ -85,9 +86,7 @@ __device__ __forceinline__ void expand_run(const ExpandArgs& p, const TileEntry*
   const uint4 zero = make_uint4(0, 0, 0, 0);
   // Rows of tokens 4g .. 4g + 3 (nullptr: no token), the same for every
   // feature block of the run.
-  // The four indices in one load (an entry always holds 16), not one
-  // guarded load per token: guarded loads were issued one after another.
-  const int4 tk4 = *reinterpret_cast<const int4*>(ent->tok + 4 * g);
+  // tk4: tokens 4g .. 4g + 3 of the sub-tile, read with the entry.
   const int tkv[4] = {tk4.x, tk4.y, tk4.z, tk4.w};
   const char* yrow[4];
 #pragma unroll
@@ -258,7 +257,7 @@ __device__ __forceinline__ bool vector_expand(int r, int m) {
 }
 
 template <typename E, bool kPart, int R>
-__device__ __forceinline__ void expand_vec_item(const ExpandArgs& p, const TileEntry* ent, int m, int t0,
+__device__ __forceinline__ void expand_vec_item(const ExpandArgs& p, const int4& tk4, int m, int t0,
                                                 int pos0, int ro, float sc, int S, int o, int hoff) {
   constexpr int V = E::kVec;
   constexpr int YV = 8 / V;                   // 16-byte vectors per 8 features
@@ -267,11 +266,12 @@ __device__ __forceinline__ void expand_vec_item(const ExpandArgs& p, const TileE
   const int mt = min(kVecTokens, m - t0);
   const int nf = min(8, p.d_out - o);  // 8; 4 for a float32 row of 4 (mod 8) features; <= 0 past the row
   const uint4 zero = make_uint4(0, 0, 0, 0);
-  // y rows of tokens t0 .. t0 + 3 and the B block, issued first, after the
-  // four token indices in one load (t0 is a multiple of 4).
-  static_assert(kVecTokens == 4, "one 16-byte load of token indices");
-  const int4 tk4 = *reinterpret_cast<const int4*>(ent->tok + t0);
-  int tk[kVecTokens] = {tk4.x, tk4.y, tk4.z, tk4.w};  // -1: no row
+  // y rows of tokens t0 .. t0 + 3 and the B block, issued first.  The four
+  // token indices were read with the entry: lane group t0 / 4 holds them.
+  static_assert(kVecTokens == 4, "tokens t0 .. t0 + 3 are one lane group's");
+  const int src = 16 * (t0 / 4);
+  int tk[kVecTokens] = {__builtin_amdgcn_readlane(tk4.x, src), __builtin_amdgcn_readlane(tk4.y, src),
+                        __builtin_amdgcn_readlane(tk4.z, src), __builtin_amdgcn_readlane(tk4.w, src)};  // -1: no row
   uint4 yv[kVecTokens][YV];
 #pragma unroll
   for (int t = 0; t < kVecTokens; ++t) {
@@ -353,6 +353,8 @@ __device__ __forceinline__ void expand_wave(const ExpandArgs& p) {
   const int count = *reinterpret_cast<const int32_t*>(p.plan);
   const int4 head = *reinterpret_cast<const int4*>(ent);  // a, pos0, m, j
   const TileMeta tm = p.meta[sc0];
+  // Tokens 4g .. 4g + 3 in lane group g (an entry always holds 16).
+  const int4 tk4 = *reinterpret_cast<const int4*>(ent->tok + 4 * ((threadIdx.x & 63) >> 4));
   const int m = head.z, pos0 = head.y;
   if ((st >= p.max_sub) | (st >= count) | !entry_fits(p, head.x, m, pos0, tm)) return;
   const int S = kPart ? tm.S : 1;
@@ -375,7 +377,7 @@ __device__ __forceinline__ void expand_wave(const ExpandArgs& p) {
     const int t0 = tg * kVecTokens;
     switch (r) {
 #define LORA_VEC_CASE(RR) \
-  case RR: expand_vec_item<E, kPart, RR>(p, ent, m, t0, pos0, ro, sc, S, o, hoff); break;
+  case RR: expand_vec_item<E, kPart, RR>(p, tk4, m, t0, pos0, ro, sc, S, o, hoff); break;
       LORA_VEC_CASE(1) LORA_VEC_CASE(2) LORA_VEC_CASE(3) LORA_VEC_CASE(4)
       LORA_VEC_CASE(5) LORA_VEC_CASE(6) LORA_VEC_CASE(7) LORA_VEC_CASE(8)
       default:
@@ -396,13 +398,13 @@ __device__ __forceinline__ void expand_wave(const ExpandArgs& p) {
   const int fb0 = slot * RUN, nb = min(RUN, p.fbn - fb0);
   const int nq = (r + KSTEP - 1) / KSTEP;
   if (nq <= 1) {
-    expand_run<E, kPart, 1, RUN>(p, ent, m, r, pos0, ro, sc, S, fb0, nb, hoff);
+    expand_run<E, kPart, 1, RUN>(p, tk4, m, r, pos0, ro, sc, S, fb0, nb, hoff);
   } else if constexpr (KSTEP == 32) {  // bf16: ranks <= 64 take at most 2 chunks
-    expand_run<E, kPart, 2, RUN>(p, ent, m, r, pos0, ro, sc, S, fb0, nb, hoff);
+    expand_run<E, kPart, 2, RUN>(p, tk4, m, r, pos0, ro, sc, S, fb0, nb, hoff);
   } else {
-    if (nq == 2) expand_run<E, kPart, 2, RUN>(p, ent, m, r, pos0, ro, sc, S, fb0, nb, hoff);
-    else if (nq == 3) expand_run<E, kPart, 3, RUN>(p, ent, m, r, pos0, ro, sc, S, fb0, nb, hoff);
-    else expand_run<E, kPart, 4, RUN>(p, ent, m, r, pos0, ro, sc, S, fb0, nb, hoff);
+    if (nq == 2) expand_run<E, kPart, 2, RUN>(p, tk4, m, r, pos0, ro, sc, S, fb0, nb, hoff);
+    else if (nq == 3) expand_run<E, kPart, 3, RUN>(p, tk4, m, r, pos0, ro, sc, S, fb0, nb, hoff);
+    else expand_run<E, kPart, 4, RUN>(p, tk4, m, r, pos0, ro, sc, S, fb0, nb, hoff);
   }
 }
 
