@@ -468,7 +468,10 @@ int lora_pack_multi(lora_multi_store* out_host, int n_slices, const lora_store* 
                     void* meta, int32_t* hoff, void* stream);
 
 /* Workspace of lora_apply_multi for T tokens (host only; 0 on invalid
- * arguments): that of the stacked store. */
+ * arguments): that of the stacked store, then 16 bytes per slice and
+ * possible sub-tile (each slice's rank, row offset, scale and h column for
+ * the sub-tile's adapter, written by the stacked shrink for the slices'
+ * expands), 256-byte aligned. */
 size_t lora_multi_workspace_bytes(const lora_multi_store* store_host, int T);
 
 /*

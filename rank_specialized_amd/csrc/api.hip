@@ -615,8 +615,9 @@ static int check_multi(const lora_multi_store* m) {
 }
 
 size_t lora_multi_workspace_bytes(const lora_multi_store* store_host, int T) {
-  if (check_multi(store_host) != LORA_OK) return 0;
-  return workspace_bytes(&store_host->stacked, T);
+  if (check_multi(store_host) != LORA_OK || T < 0) return 0;
+  const size_t base = workspace_bytes(&store_host->stacked, T);
+  return base ? base + slice_meta_bytes(T, store_host->stacked.n, store_host->n_slices) : 0;
 }
 
 static int multi_impl(const lora_multi_store* store_host, const void* x, int64_t ldx, void* const* y_host,
@@ -631,6 +632,7 @@ static int multi_impl(const lora_multi_store* store_host, const void* x, int64_t
   for (int k = 0; k < m.n_slices; ++k)
     if ((st = check_rows(y_host[k], ldy_host[k], m.slice[k].d_out, s.dtype, T)) != LORA_OK) return st;
   if ((st = check_ws(&s, T, ws, ws_bytes)) != LORA_OK) return st;
+  if (T > 0 && ws_bytes < lora_multi_workspace_bytes(store_host, T)) return LORA_ERR_INVALID_ARG;
   if (ids != nullptr && (T > LORA_SEGMENT_MAX_T || s.n > LORA_SEGMENT_MAX_N)) return LORA_ERR_UNSUPPORTED;
   if (T == 0) return LORA_OK;
   if (given_plan == nullptr && ids == nullptr && (st = check_grouping(&s, T, seg_off, perm)) != LORA_OK) return st;
@@ -638,9 +640,12 @@ static int multi_impl(const lora_multi_store* store_host, const void* x, int64_t
   hipError_t e = hipSuccess;
   const char* plan = reinterpret_cast<const char*>(given_plan);
   if (plan == nullptr) e = form_plan(s, s.n, T, ids, nullptr, 0, seg_off, perm, ws, &plan, strm);
-  if (e == hipSuccess) e = launch_shrink(s, plan, T, x, ldx, ws, strm);
+  // The slice records follow the stacked store's workspace.
+  SliceMeta* sl_meta = reinterpret_cast<SliceMeta*>(reinterpret_cast<char*>(ws) + workspace_bytes(&s, T));
+  const int64_t max_sub = plan_max_subtiles(T, s.n);
+  if (e == hipSuccess) e = launch_shrink_slices(m, sl_meta, plan, T, x, ldx, ws, strm);
   for (int k = 0; e == hipSuccess && k < m.n_slices; ++k)
-    e = launch_expand_slice(s, m.slice[k], m.hoff + (size_t)k * s.n, plan, T, ws, y_host[k], ldy_host[k], strm);
+    e = launch_expand_slice(s, m.slice[k], sl_meta + k * max_sub, plan, T, ws, y_host[k], ldy_host[k], strm);
   return e == hipSuccess ? LORA_OK : hip_fail(e);
 }
 

@@ -65,13 +65,11 @@ struct ExpandArgs {
   char* y;
   int64_t ldy_bytes;
   // Slice mode (multi-slice apply): the plan and partial sums come from the
-  // shrink of a stacked store (the bounds above are that store's); B, rank,
-  // row offset and scale come from the slice's store, and h from column
-  // sl_hoff[a] of the stacked h.  sl_rank == nullptr: ordinary mode.
-  const int32_t* sl_rank;
-  const int32_t* sl_row_off;
-  const float* sl_scale;
-  const int32_t* sl_hoff;
+  // shrink of a stacked store (the bounds above are that store's); B comes
+  // from the slice's store, and its rank, row offset, scale and h column
+  // (among the stacked ranks) from the records the stacked shrink wrote,
+  // checked against the slice store's bounds.
+  const SliceMeta* sl_meta;  // [max_sub]: this slice's records
   int sl_r_max, sl_R;
 };
 
@@ -353,6 +351,8 @@ __device__ __forceinline__ void expand_wave(const ExpandArgs& p) {
   const int count = *reinterpret_cast<const int32_t*>(p.plan);
   const int4 head = *reinterpret_cast<const int4*>(ent);  // a, pos0, m, j
   const TileMeta tm = p.meta[sc0];
+  SliceMeta sm{0, 0, 0.f, 0};
+  if constexpr (kSlice) sm = p.sl_meta[sc0];
   // Tokens 4g .. 4g + 3 in lane group g (an entry always holds 16).
   const int4 tk4 = *reinterpret_cast<const int4*>(ent->tok + 4 * ((threadIdx.x & 63) >> 4));
   const int m = head.z, pos0 = head.y;
@@ -361,13 +361,12 @@ __device__ __forceinline__ void expand_wave(const ExpandArgs& p) {
   int r = tm.r, ro = tm.row_off, hoff = 0;
   float sc = tm.scale;
   if constexpr (kSlice) {  // slice mode: this slice's rank, B rows, scale and h columns
-    const int a = head.x;
-    const int r2 = p.sl_rank[a], ro2 = p.sl_row_off[a], h2 = p.sl_hoff[a];
+    const int r2 = sm.r, ro2 = sm.row_off, h2 = sm.hoff;
     if (r2 <= 0 || r2 > p.sl_r_max || ro2 < 0 || ro2 > p.sl_R - r2 || h2 < 0 || h2 > r - r2) return;
     r = r2;
     ro = ro2;
     hoff = h2;
-    sc = p.sl_scale[a];
+    sc = sm.scale;
   }
   if (vector_expand<E, RUN>(r, m)) {
     const int fb = slot / kGroups, tg = slot - fb * kGroups;
@@ -434,7 +433,7 @@ static hipError_t launch_expand_kernel(int dtype, bool part, bool slice, dim3 gr
   return hipGetLastError();
 }
 
-static hipError_t launch_expand_impl(const lora_store& s, const lora_store* slice, const int32_t* hoff,
+static hipError_t launch_expand_impl(const lora_store& s, const lora_store* slice, const SliceMeta* sl_meta,
                                      const char* plan, int T, const void* ws, const float* h, int64_t ldh, void* y,
                                      int64_t ldy, hipStream_t stream) {
   const int64_t max_sub = plan_max_subtiles(T, s.n);
@@ -456,10 +455,7 @@ static hipError_t launch_expand_impl(const lora_store& s, const lora_store* slic
   a.S_max = shrink_split(s.d_in, s.dtype, max_sub).S;
   a.y = reinterpret_cast<char*>(y);
   a.ldy_bytes = ldy * elem_bytes(s.dtype);
-  a.sl_rank = slice ? slice->rank : nullptr;
-  a.sl_row_off = slice ? slice->row_off : nullptr;
-  a.sl_scale = slice ? slice->scale : nullptr;
-  a.sl_hoff = hoff;
+  a.sl_meta = sl_meta;
   a.sl_r_max = slice ? slice->r_max : 0;
   a.sl_R = slice ? slice->R : 0;
   const bool part = h == nullptr;
@@ -493,9 +489,9 @@ hipError_t launch_expand(const lora_store& s, const char* plan, int T, const voi
   return launch_expand_impl(s, nullptr, nullptr, plan, T, ws, h, ldh, y, ldy, stream);
 }
 
-hipError_t launch_expand_slice(const lora_store& stacked, const lora_store& slice, const int32_t* hoff,
+hipError_t launch_expand_slice(const lora_store& stacked, const lora_store& slice, const SliceMeta* sl_meta,
                                const char* plan, int T, const void* ws, void* y, int64_t ldy, hipStream_t stream) {
-  return launch_expand_impl(stacked, &slice, hoff, plan, T, ws, nullptr, 0, y, ldy, stream);
+  return launch_expand_impl(stacked, &slice, sl_meta, plan, T, ws, nullptr, 0, y, ldy, stream);
 }
 
 }  // namespace lora

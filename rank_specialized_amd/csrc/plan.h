@@ -107,6 +107,17 @@ struct TileMeta {
 };
 static_assert(sizeof(TileMeta) == 16, "one 16-byte load");
 
+// Multi-slice apply: per sub-tile and slice, the slice's rank, row offset and
+// scale for the sub-tile's adapter and the first column of its h among the
+// stacked ranks, written by the stacked store's shrink, so that a slice's
+// expand reads them with the plan entry (one round trip) instead of after it.
+struct SliceMeta {
+  int32_t r, row_off;
+  float scale;
+  int32_t hoff;
+};
+static_assert(sizeof(SliceMeta) == 16, "one 16-byte load");
+
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline int elem_bytes(int dtype) { return dtype == LORA_DTYPE_BF16 ? 2 : 4; }
 inline int vec_elems(int dtype) { return dtype == LORA_DTYPE_BF16 ? 8 : 4; }  // 16-byte vectors
@@ -171,6 +182,12 @@ inline WsLayout ws_layout(int T, int n, int d_in, int r_max, int dtype) {
   // The base-fused apply's s h as bf16 pairs hi, lo: [T][2][ldp].
   L.total = L.hs + align_up((size_t)T * (size_t)partial_ld(r_max) * 4, 256);
   return L;
+}
+
+// The multi-slice apply's workspace: the stacked store's, then the slice
+// records [n_slices][plan_max_subtiles].
+inline size_t slice_meta_bytes(int T, int n, int n_slices) {
+  return align_up(sizeof(SliceMeta) * (size_t)plan_max_subtiles(T, n) * (size_t)n_slices, 256);
 }
 
 // Meta buffer of a store: row_off[n+1] | rank[n] (stored) | scale[n] |

@@ -52,6 +52,19 @@ struct ShrinkArgs {
   TileMeta* meta;
 };
 
+// Multi-slice apply: each slice's rank, row offset and scale arrays and hoff
+// ([n_sl][n]); the records go to sl_meta[j * max_sub + st].  A separate
+// argument of the slice kernel only, so that the ordinary shrink's
+// arguments stay small.
+struct SliceSet {
+  int n_sl;
+  const int32_t* rank[LORA_MAX_SLICES];
+  const int32_t* row_off[LORA_MAX_SLICES];
+  const float* scale[LORA_MAX_SLICES];
+  const int32_t* hoff;
+  SliceMeta* meta;
+};
+
 // The plan's entry st checked against T and the store: every token, row
 // and partial it names lies inside the call's buffers.
 __device__ __forceinline__ bool entry_ok(int a, int m, int pos0, int n, int T) {
@@ -180,9 +193,8 @@ __device__ __forceinline__ void shrink_tile(const ShrinkArgs& p, int tok_l, int 
   for (int q = 0; q < NG; ++q) red_w[q][lane] = acc[q];
 }
 
-template <typename E>
-__global__ void __launch_bounds__(kShrinkThreads) __attribute__((amdgpu_waves_per_eu(4)))
-shrink_kernel(ShrinkArgs p) {
+template <typename E, bool kSl>
+__device__ __forceinline__ void shrink_body(const ShrinkArgs& p, const SliceSet& ss) {
   constexpr int kVecRank = kVecMaxRank * 2 / E::kBytes;  // 8 bf16, 4 float32
   __shared__ f32x4_t red[kShrinkWaves][4][64];             // matrix path: [wave][row group][lane]
   __shared__ float redg[kShrinkWaves][kGemvMaxProducts];   // reduction path: [wave][sum]
@@ -204,11 +216,31 @@ shrink_kernel(ShrinkArgs p) {
     const int tok_l = el->tok[lane & 15];
     int r_l = 0, ro_l = 0;
     float sc_l = 0.f;
+    // Multi-slice: lane 16 k + j also fetches slice j's record for item k's
+    // adapter (read with the metadata; written at the item's end).
+    const int jl = lane & 15;
+    SliceMeta sm_l{0, 0, 0.f, 0};
     if (vl && entry_ok(a_l, m_l, pos0_l, p.n, p.T)) {
       r_l = p.rank[a_l];
       ro_l = p.row_off[a_l];
       sc_l = p.scale[a_l];
       if (r_l < 0 || r_l > p.r_max || ro_l < 0 || ro_l > p.R - r_l) r_l = 0;  // not this store's metadata
+      if (kSl && jl < ss.n_sl) {
+        const int32_t* rk = ss.rank[0];
+        const int32_t* ok = ss.row_off[0];
+        const float* sk = ss.scale[0];
+#pragma unroll
+        for (int j = 1; j < LORA_MAX_SLICES; ++j)
+          if (jl == j) {
+            rk = ss.rank[j];
+            ok = ss.row_off[j];
+            sk = ss.scale[j];
+          }
+        sm_l.r = rk[a_l];
+        sm_l.row_off = ok[a_l];
+        sm_l.scale = sk[a_l];
+        sm_l.hoff = ss.hoff[(int64_t)jl * p.n + a_l];
+      }
     }
     for (int k = 0; k < kShrinkBatch; ++k) {
       const int it = b0 + k * G;
@@ -228,6 +260,8 @@ shrink_kernel(ShrinkArgs p) {
         tm.S = p.S;
         p.meta[st] = tm;
       }
+      if (kSl && kc == 0 && tid >= 16 * k && tid < 16 * k + ss.n_sl)  // lanes of wave 0 hold item k's records
+        ss.meta[(int64_t)(tid - 16 * k) * p.max_sub + st] = sm_l;
       if (r == 0) continue;  // the same in every wave: no barrier is skipped by some only
       const int k0 = kc * p.kchunk + w * p.span;
       const int kw = max(0, min(p.span, p.d_in - k0));
@@ -289,6 +323,23 @@ shrink_kernel(ShrinkArgs p) {
   }  // batches
 }
 
+template <typename E>
+__global__ void __launch_bounds__(kShrinkThreads) __attribute__((amdgpu_waves_per_eu(4)))
+shrink_kernel(ShrinkArgs p) {
+  shrink_body<E, false>(p, SliceSet{});
+}
+
+struct ShrinkSliceArgs {
+  ShrinkArgs p;
+  SliceSet ss;
+};
+
+template <typename E>
+__global__ void __launch_bounds__(kShrinkThreads) __attribute__((amdgpu_waves_per_eu(4)))
+shrink_slices_kernel(ShrinkSliceArgs a) {
+  shrink_body<E, true>(a.p, a.ss);
+}
+
 // ------------------------------------------------------------- reduce
 // h[pos, j] = partial 0 + partial 1 + ... (chunk order, as the expand sums
 // them), for every sub-tile of the plan.
@@ -314,8 +365,8 @@ reduce_partials_kernel(const char* __restrict__ plan, int max_sub, const TileMet
 }
 
 // --------------------------------------------------------------- host
-hipError_t launch_shrink(const lora_store& s, const char* plan, int T, const void* x, int64_t ldx, void* ws,
-                         hipStream_t stream) {
+static hipError_t shrink_impl(const lora_store& s, const lora_multi_store* multi, void* sl_meta, const char* plan,
+                              int T, const void* x, int64_t ldx, void* ws, hipStream_t stream) {
   const int64_t max_sub = plan_max_subtiles(T, s.n);
   if (max_sub == 0) return hipSuccess;
   const ShrinkSplit sp = shrink_split(s.d_in, s.dtype, max_sub);
@@ -350,11 +401,38 @@ hipError_t launch_shrink(const lora_store& s, const char* plan, int T, const voi
   const int64_t items = max_sub * sp.S;
   const int64_t cap = 1LL << 30;
   const int grid = (int)(items < cap ? items : cap);
-  if (s.dtype == LORA_DTYPE_BF16)
+  if (multi) {
+    ShrinkSliceArgs b;
+    b.p = a;
+    b.ss.n_sl = multi->n_slices;
+    for (int j = 0; j < LORA_MAX_SLICES; ++j) {
+      const bool in = j < multi->n_slices;
+      b.ss.rank[j] = in ? multi->slice[j].rank : nullptr;
+      b.ss.row_off[j] = in ? multi->slice[j].row_off : nullptr;
+      b.ss.scale[j] = in ? multi->slice[j].scale : nullptr;
+    }
+    b.ss.hoff = multi->hoff;
+    b.ss.meta = reinterpret_cast<SliceMeta*>(sl_meta);
+    if (s.dtype == LORA_DTYPE_BF16)
+      hipLaunchKernelGGL(shrink_slices_kernel<BF16>, dim3(grid), dim3(kShrinkThreads), 0, stream, b);
+    else
+      hipLaunchKernelGGL(shrink_slices_kernel<F32>, dim3(grid), dim3(kShrinkThreads), 0, stream, b);
+  } else if (s.dtype == LORA_DTYPE_BF16) {
     hipLaunchKernelGGL(shrink_kernel<BF16>, dim3(grid), dim3(kShrinkThreads), 0, stream, a);
-  else
+  } else {
     hipLaunchKernelGGL(shrink_kernel<F32>, dim3(grid), dim3(kShrinkThreads), 0, stream, a);
+  }
   return hipGetLastError();
+}
+
+hipError_t launch_shrink(const lora_store& s, const char* plan, int T, const void* x, int64_t ldx, void* ws,
+                         hipStream_t stream) {
+  return shrink_impl(s, nullptr, nullptr, plan, T, x, ldx, ws, stream);
+}
+
+hipError_t launch_shrink_slices(const lora_multi_store& m, void* sl_meta, const char* plan, int T, const void* x,
+                                int64_t ldx, void* ws, hipStream_t stream) {
+  return shrink_impl(m.stacked, &m, sl_meta, plan, T, x, ldx, ws, stream);
 }
 
 hipError_t launch_reduce_partials(const lora_store& s, const char* plan, int T, const void* ws, float* h,

@@ -568,8 +568,14 @@ def test_multi_bytes_and_rejects(lib):
 
 def test_multi_workspace_and_apply_rejects(lib):
     m = _multi()
-    assert lib.lora_multi_workspace_bytes(C.byref(m), 16) == lib.lora_workspace_bytes(C.byref(m.stacked), 16)
+    # The stacked store's workspace, then 16 bytes per slice and possible
+    # sub-tile of <= 16 tokens (the slice records), 256-byte aligned.
+    for T in (16, 1000):
+        max_sub = (T + 15 * min(4, T)) // 16
+        want = lib.lora_workspace_bytes(C.byref(m.stacked), T) + -(-(16 * max_sub * 2) // 256) * 256
+        assert lib.lora_multi_workspace_bytes(C.byref(m), T) == want
     assert lib.lora_multi_workspace_bytes(None, 16) == 0
+    assert lib.lora_multi_workspace_bytes(C.byref(m), -1) == 0
     big = 1 << 30
     ys = (C.c_void_p * 2)(FAKE, FAKE)
     lds = (C.c_int64 * 2)(32, 16)
@@ -588,6 +594,7 @@ def test_multi_workspace_and_apply_rejects(lib):
     assert call(y=(C.c_void_p * 2)(FAKE, FAKE + 2)) == 2
     assert call(ws=None) == 1
     assert call(wsb=64) == 1
+    assert call(wsb=lib.lora_multi_workspace_bytes(C.byref(_multi()), 16) - 1) == 1  # no room for the slice records
     assert call(T=L.LORA_SEGMENT_MAX_T + 1) == 2
     mm = _multi()
     mm.hoff = None
