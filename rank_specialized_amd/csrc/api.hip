@@ -35,7 +35,7 @@ const char* lora_status_string(int status) {
 
 int lora_last_hip_error(void) { return g_last_hip; }
 
-int lora_abi_version(void) { return 4; }
+int lora_abi_version(void) { return 5; }
 
 int lora_store_bytes(int n, int d_in, int d_out, int dtype, const int32_t* ranks_host, int pad_to,
                      size_t* a_bytes_host, size_t* b_bytes_host, size_t* meta_bytes_host) {

@@ -50,7 +50,7 @@ def test_status_strings(lib):
     assert b"invalid" in lib.lora_status_string(1)
     assert b"unsupported" in lib.lora_status_string(2)
     assert b"HIP" in lib.lora_status_string(3)
-    assert lib.lora_abi_version() == 4
+    assert lib.lora_abi_version() == 5
     assert lib.lora_last_hip_error() == 0
 
 
