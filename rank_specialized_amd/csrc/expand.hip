@@ -12,7 +12,10 @@
 // In calls of at least kExpandRunMinItems such items a wave takes a run of
 // kExpandRun consecutive feature blocks of its sub-tile instead: tokens and
 // h are read once, and each block's y rows are issued before the previous
-// block's products, so the next block's loads overlap this block's work.
+// block's products, so the next block's loads overlap this block's work.  In
+// that form two consecutive sub-tiles of one adapter (ranks of one K chunk)
+// pair up: their waves take one feature block each, for both sub-tiles, so
+// B's rows are read once for the two (prefill expand 120 -> 114 us).
 //   D[token, feature] = H[token, j] . B_a^T[j, feature]
 // on 16x16 MFMA tiles (bf16: 16x16x32, f32: 16x16x4), eight N blocks per
 // wave.  Column c of N block b is feature o0 + 8 c + b, so lane (c, g) ends
@@ -72,6 +75,56 @@ struct ExpandArgs {
   const SliceMeta* sl_meta;  // [max_sub]: this slice's records
   int sl_r_max, sl_R;
 };
+
+// The H operand chunk of one lane: h[hrow, j0 .. j0 + V) of the rows the
+// expand reads (the S partial sums added in chunk order, or h), zero past
+// the rank and for a row that is not valid.
+template <typename E, bool kPart>
+__device__ __forceinline__ HChunk<E> h_chunk(const ExpandArgs& p, int hrow, bool valid, int j0, int r, int S, int hoff) {
+  constexpr int V = E::kVec;
+  float f[V];
+#pragma unroll
+  for (int e = 0; e < V; ++e) f[e] = 0.f;
+  if (valid && hrow >= 0 && hrow < p.T && j0 < r) {
+    const float* src = p.hsrc + (int64_t)hrow * p.ldh + hoff + j0;
+    // A slice's columns (multi-slice apply) may start off a 16-byte
+    // boundary, or end so that a whole vector would run past the row of
+    // partial sums: those are read column by column, only below the rank.
+    const bool whole = (hoff & 3) == 0 && hoff + j0 + V <= p.ldh;
+    if (kPart && !whole) {
+#pragma unroll
+      for (int e = 0; e < V; ++e) f[e] = j0 + e < r ? src[e] : 0.f;
+#pragma unroll 4
+      for (int k = 1; k < S; ++k)
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+          if (j0 + e < r) f[e] += src[(int64_t)k * p.hstride + e];
+    } else if (kPart) {
+#pragma unroll
+      for (int v = 0; v < V / 4; ++v) {
+        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(src + 4 * v);
+        f[4 * v] = x[0]; f[4 * v + 1] = x[1]; f[4 * v + 2] = x[2]; f[4 * v + 3] = x[3];
+      }
+#pragma unroll 4
+      for (int k = 1; k < S; ++k) {
+#pragma unroll
+        for (int v = 0; v < V / 4; ++v) {
+          const f32x4_t x = *reinterpret_cast<const f32x4_t*>(src + (int64_t)k * p.hstride + 4 * v);
+          f[4 * v] += x[0]; f[4 * v + 1] += x[1]; f[4 * v + 2] += x[2]; f[4 * v + 3] += x[3];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        if (j0 + e >= r) f[e] = 0.f;
+    } else {
+#pragma unroll
+      for (int e = 0; e < V; ++e) f[e] = j0 + e < r ? src[e] : 0.f;
+    }
+  }
+  HChunk<E> h;
+  h.set(f);
+  return h;
+}
 
 template <typename E, bool kPart, int NQ, int RUN>
 __device__ __forceinline__ void expand_run(const ExpandArgs& p, const int4& tk4, int m, int r, int pos0,
@@ -142,52 +195,8 @@ __device__ __forceinline__ void expand_run(const ExpandArgs& p, const int4& tk4,
   for (int q = 0; q < NB; ++q) load_b(q, feat(0), bq[q]);
   // H chunks: token c of the sub-tile, ranks j0 .. j0 + V.
   HChunk<E> hc[NQ];
-  const int hrow = pos0 + c;
-  const bool hv = c < m && hrow >= 0 && hrow < p.T;
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    const int j0 = q * KSTEP + g * V;
-    float f[V];
-#pragma unroll
-    for (int e = 0; e < V; ++e) f[e] = 0.f;
-    if (hv && j0 < r) {
-      const float* src = p.hsrc + (int64_t)hrow * p.ldh + hoff + j0;
-      // A slice's columns (multi-slice apply) may start off a 16-byte
-      // boundary, or end so that a whole vector would run past the row of
-      // partial sums: those are read column by column, only below the rank.
-      const bool whole = (hoff & 3) == 0 && hoff + j0 + V <= p.ldh;
-      if (kPart && !whole) {
-#pragma unroll
-        for (int e = 0; e < V; ++e) f[e] = j0 + e < r ? src[e] : 0.f;
-#pragma unroll 4
-        for (int k = 1; k < S; ++k)
-#pragma unroll
-          for (int e = 0; e < V; ++e)
-            if (j0 + e < r) f[e] += src[(int64_t)k * p.hstride + e];
-      } else if (kPart) {
-#pragma unroll
-        for (int v = 0; v < V / 4; ++v) {
-          const f32x4_t x = *reinterpret_cast<const f32x4_t*>(src + 4 * v);
-          f[4 * v] = x[0]; f[4 * v + 1] = x[1]; f[4 * v + 2] = x[2]; f[4 * v + 3] = x[3];
-        }
-#pragma unroll 4
-        for (int k = 1; k < S; ++k) {
-#pragma unroll
-          for (int v = 0; v < V / 4; ++v) {
-            const f32x4_t x = *reinterpret_cast<const f32x4_t*>(src + (int64_t)k * p.hstride + 4 * v);
-            f[4 * v] += x[0]; f[4 * v + 1] += x[1]; f[4 * v + 2] += x[2]; f[4 * v + 3] += x[3];
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < V; ++e)
-          if (j0 + e >= r) f[e] = 0.f;
-      } else {
-#pragma unroll
-        for (int e = 0; e < V; ++e) f[e] = j0 + e < r ? src[e] : 0.f;
-      }
-    }
-    hc[q].set(f);
-  }
+  for (int q = 0; q < NQ; ++q) hc[q] = h_chunk<E, kPart>(p, pos0 + c, c < m, q * KSTEP + g * V, r, S, hoff);
   if constexpr (RUN > 1) load_y(feat(0), ya);
   // The run: block k's products and stores, with block k + 1's y rows
   // issued before block k is waited for (its B rows first: waits are in
@@ -235,6 +244,84 @@ __device__ __forceinline__ void expand_run(const ExpandArgs& p, const int4& tk4,
   }
 }
 
+// Run form, a pair: consecutive sub-tiles a and b of one adapter (ranks of
+// one K chunk) over one block of kExpandCols features.  B's rows of the block
+// are read once for both sub-tiles; the lane layout, the order of operations
+// and the results are those of the one-sub-tile form.
+template <typename E, bool kPart>
+__device__ __forceinline__ void expand_pair(const ExpandArgs& p, const int4& tka, const int4& tkb, int ma, int pa,
+                                            int mb, int pb, int r, int ro, float sc, int S, int fb) {
+  constexpr int V = E::kVec;
+  constexpr int YV = 8 / V;
+  const int lane = threadIdx.x & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+  const int o = fb * kExpandCols + 8 * c;
+  const int tkv[2][4] = {{tka.x, tka.y, tka.z, tka.w}, {tkb.x, tkb.y, tkb.z, tkb.w}};
+  const int mk[2] = {ma, mb};
+  const char* yrow[2][4];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int tok = 4 * g + e < mk[k] ? tkv[k][e] : -1;
+      yrow[k][e] = (unsigned)tok < (unsigned)p.T ? p.y + (int64_t)tok * p.ldy_bytes : nullptr;
+    }
+  // Both sub-tiles' y rows first (the longest wait), then B, then h.
+  uint4 yv[2][4][YV];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int v = 0; v < YV; ++v)
+        yv[k][e][v] = (yrow[k][e] && o + v * V < p.d_out) ? ld16_stream(yrow[k][e] + (size_t)(o + v * V) * E::kBytes)
+                                                          : zero;
+  const uint32_t row_bytes = (uint32_t)r * E::kBytes;
+  const rsrc_t br = make_rsrc(p.b_pack + (size_t)ro * p.d_out * E::kBytes, (uint32_t)p.d_out * row_bytes);
+  const bool odd_rows = E::kBytes == 2 && (r & 1);
+  const int j0 = g * V;
+  uint4 bq[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const bool ok = j0 < r && o + b < p.d_out;
+    const uint32_t off = (uint32_t)(o + b) * row_bytes + (uint32_t)j0 * E::kBytes;
+    if ((b & 1) && odd_rows) {
+      const uint32_t lo = ok ? off - 2 : kOutOfRange;
+      const uint4 d = buf_ld16(br, lo, 0);
+      const uint32_t t = buf_ld4(br, ok ? lo + 16 : kOutOfRange);
+      bq[b] = make_uint4(__builtin_amdgcn_alignbit(d.y, d.x, 16), __builtin_amdgcn_alignbit(d.z, d.y, 16),
+                         __builtin_amdgcn_alignbit(d.w, d.z, 16), __builtin_amdgcn_alignbit(t, d.w, 16));
+    } else {
+      bq[b] = buf_ld16(br, ok ? off : kOutOfRange, 0);
+    }
+  }
+  const HChunk<E> hc[2] = {h_chunk<E, kPart>(p, pa + c, c < ma, j0, r, S, 0),
+                           h_chunk<E, kPart>(p, pb + c, c < mb, j0, r, S, 0)};
+  const int nvalid = r - j0;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    f32x4_t acc[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[b] = hc[k].mma(keep_first<E>(bq[b], nvalid), f32x4_t{0.f, 0.f, 0.f, 0.f});
+    // acc[b][e] = feature o + b of token 4g + e of sub-tile k.
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (yrow[k][e] == nullptr) continue;
+      char* yp = const_cast<char*>(yrow[k][e]) + (size_t)o * E::kBytes;
+#pragma unroll
+      for (int v = 0; v < YV; ++v) {
+        if (o + v * V >= p.d_out) continue;
+        float f[V];
+        E::widen(yv[k][e][v], f);
+#pragma unroll
+        for (int kk = 0; kk < V; ++kk) f[kk] = f[kk] + sc * acc[v * V + kk][e];
+        st16_stream(yp + 16 * v, E::narrow(f));
+      }
+    }
+  }
+}
+
 // Sub-tile st checked against T and the store (metadata left in the
 // workspace by a call on another store is skipped): every token, B row and
 // partial sum it names then lies inside the call's buffers.
@@ -242,6 +329,15 @@ __device__ __forceinline__ bool entry_fits(const ExpandArgs& p, int a, int m, in
   return (unsigned)a < (unsigned)p.n && m > 0 && m <= kSubTile && pos0 >= 0 && pos0 <= p.T - m && tm.r > 0 &&
          tm.r <= p.r_max && tm.row_off >= 0 && tm.row_off <= p.R - tm.r && tm.S > 0 && tm.S <= p.S_max;
 }
+
+// Whether sub-tiles s and s + 1 (heads e0, e1, metadata t0, t1) make a pair
+// for the run form's matrix path: the adapter's sub-tiles j and j + 1 with j
+// even, both valid with the same metadata, both on the matrix path at rank r
+// of one K chunk.  The waves of both evaluate it on the same plan, so the
+// pair's feature blocks are split between them without overlap.
+template <typename E, int RUN>
+__device__ __forceinline__ bool pair_ok(const ExpandArgs& p, int lim, int s, const int4& e0, const int4& e1,
+                                        const TileMeta& t0, const TileMeta& t1, int r);
 
 // ------------------------------------------------------------ vector path
 // float32 B blocks are twice as large: that path stops at rank kVecMaxRank / 2.
@@ -252,6 +348,17 @@ constexpr int vec_rank_cap() {
 template <typename E, int RUN>
 __device__ __forceinline__ bool vector_expand(int r, int m) {
   return r <= vec_rank_cap<E, RUN>() && m <= kVecMaxTokens;
+}
+
+template <typename E, int RUN>
+__device__ __forceinline__ bool pair_ok(const ExpandArgs& p, int lim, int s, const int4& e0, const int4& e1,
+                                        const TileMeta& t0, const TileMeta& t1, int r) {
+  if (s < 0 || s + 1 >= lim) return false;
+  if (e1.x != e0.x || (e0.w & 1) || e1.w != e0.w + 1) return false;
+  if (!entry_fits(p, e0.x, e0.z, e0.y, t0) || !entry_fits(p, e1.x, e1.z, e1.y, t1)) return false;
+  if (t0.r != t1.r || t0.row_off != t1.row_off || t0.S != t1.S || __float_as_int(t0.scale) != __float_as_int(t1.scale))
+    return false;
+  return r <= 4 * E::kVec && !vector_expand<E, RUN>(r, e0.z) && !vector_expand<E, RUN>(r, e1.z);
 }
 
 template <typename E, bool kPart, int R>
@@ -354,7 +461,24 @@ __device__ __forceinline__ void expand_wave(const ExpandArgs& p) {
   SliceMeta sm{0, 0, 0.f, 0};
   if constexpr (kSlice) sm = p.sl_meta[sc0];
   // Tokens 4g .. 4g + 3 in lane group g (an entry always holds 16).
-  const int4 tk4 = *reinterpret_cast<const int4*>(ent->tok + 4 * ((threadIdx.x & 63) >> 4));
+  const int g4 = 4 * ((threadIdx.x & 63) >> 4);
+  const int4 tk4 = *reinterpret_cast<const int4*>(ent->tok + g4);
+  // Run form: the neighbours' heads, metadata and tokens too (a pair of
+  // sub-tiles needs its partner's), in the same round trip.
+  constexpr bool kPairs = RUN > 1 && !kSlice && E::kBytes == 2;
+  int4 hp{}, hn{}, tkp{}, tkn{};
+  TileMeta tp{}, tn{};
+  if constexpr (kPairs) {
+    const int sp = sc0 > 0 ? sc0 - 1 : sc0, sn = sc0 + 1 < p.max_sub ? sc0 + 1 : sc0;
+    const TileEntry* ep = ent + (sp - sc0);
+    const TileEntry* en = ent + (sn - sc0);
+    hp = *reinterpret_cast<const int4*>(ep);
+    hn = *reinterpret_cast<const int4*>(en);
+    tp = p.meta[sp];
+    tn = p.meta[sn];
+    tkp = *reinterpret_cast<const int4*>(ep->tok + g4);
+    tkn = *reinterpret_cast<const int4*>(en->tok + g4);
+  }
   const int m = head.z, pos0 = head.y;
   if ((st >= p.max_sub) | (st >= count) | !entry_fits(p, head.x, m, pos0, tm)) return;
   const int S = kPart ? tm.S : 1;
@@ -394,6 +518,19 @@ __device__ __forceinline__ void expand_wave(const ExpandArgs& p) {
   }
   const int runs = (p.fbn + RUN - 1) / RUN;
   if (slot >= runs) return;
+  if constexpr (kPairs) {
+    // Sub-tiles j and j + 1 (j even) of an adapter pair up: their 2 runs
+    // waves take one block each, for both, so that B's rows are read once.
+    const int lim = min(count, p.max_sub);
+    const bool odd = head.w & 1;
+    if (odd ? pair_ok<E, RUN>(p, lim, st - 1, hp, head, tp, tm, r) : pair_ok<E, RUN>(p, lim, st, head, hn, tm, tn, r)) {
+      const int fb = odd ? runs + slot : slot;
+      if (fb >= p.fbn) return;
+      if (odd) expand_pair<E, kPart>(p, tkp, tk4, hp.z, hp.y, m, pos0, r, ro, sc, S, fb);
+      else expand_pair<E, kPart>(p, tk4, tkn, m, pos0, hn.z, hn.y, r, ro, sc, S, fb);
+      return;
+    }
+  }
   const int fb0 = slot * RUN, nb = min(RUN, p.fbn - fb0);
   const int nq = (r + KSTEP - 1) / KSTEP;
   if (nq <= 1) {
