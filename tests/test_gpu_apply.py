@@ -648,7 +648,8 @@ def test_eight_partial_sums_integer_exact(dtype):
     assert np.array_equal(y_host(y2), want)
 
 
-def test_expand_h_split_per_element_bound():
+@pytest.mark.parametrize("case", ["small", "run_form_pairs"])
+def test_expand_h_split_per_element_bound(case):
     """The bf16 expand feeds h to the matrix cores as the pair hi + lo of bf16
     values (hi = nearest bf16 of h, lo = nearest bf16 of h - hi), so
     |h - (hi + lo)| <= 2^-16 |h| (two roundings of relative size 2^-8).
@@ -659,15 +660,27 @@ def test_expand_h_split_per_element_bound():
     element by element against the exact s B h (float64) on h with 24
     significant bits and on outputs that cancel: with B = [b, -b] pairs the
     exact sums are small next to sum |B h|, where a single bf16 copy of h
-    (error 2^-8 |h|) breaks the bound."""
+    (error 2^-8 |h|) breaks the bound.  Case run_form_pairs: a call large
+    enough for the expand's run form (1024 adapters, 2048 tokens, 6144
+    features) whose tokens all go to 4 adapters, so that consecutive
+    sub-tiles pair up (ranks 2, 8, 17; rank 40 takes two K chunks and stays
+    single)."""
     dev = device()
     rng = np.random.default_rng(77)
-    n, T, d_out = 4, 64, 256
-    ranks = [2, 8, 17, 40]
+    if case == "small":
+        n, T, d_out = 4, 64, 256
+        ranks = [2, 8, 17, 40]
+    else:
+        n, T, d_out = 1024, 2048, 6144
+        ranks = [2, 8, 17, 40] + [1] * (n - 4)
+        max_sub = (T + 15 * min(n, T)) // 16
+        assert max_sub * (d_out // 128) >= 48 * 1024  # the run form
     wl = make_random_workload(78, T, n, 64, d_out, ranks, dtype="bf16", id_mode="uniform")
+    if case != "small":
+        wl.ids = rng.integers(0, 4, size=T).astype(wl.ids.dtype)
     m = wl.module
     # B columns in cancelling pairs (column 2i+1 = -column 2i + small bf16 noise).
-    for a in range(n):
+    for a in range(4):
         B = m.B[a].astype(np.float64)
         for j in range(0, ranks[a] - 1, 2):
             B[:, j + 1] = -B[:, j] + 2.0 ** -10 * np.sign(rng.normal(size=d_out))
@@ -691,7 +704,7 @@ def test_expand_h_split_per_element_bound():
     torch.cuda.synchronize()
     got = y_host(y)
     worst, n_cancel = 0.0, 0
-    for a in range(n):
+    for a in range(4):
         r = ranks[a]
         s = float(m.scales[a])
         Ba = m.B[a].astype(np.float64)
