@@ -108,29 +108,40 @@ __device__ __forceinline__ void shrink_gemv(const ShrinkArgs& p, int tok_l, int 
   for (int j = 0; j < R; ++j)
 #pragma unroll
     for (int t = 0; t < M; ++t) acc[j][t] = 0.f;
+  // Two blocks per turn, all their loads issued before either is used: a
+  // wave's span is two blocks at most sizes, so the item takes one round
+  // trip instead of two (the sums keep their block order).
 #pragma nounroll
-  for (int kb = k0; kb < kend; kb += BLK) {
-    const int k = kb + lane * HV;
-    const bool kv = k < kend;
-    const size_t kk = (size_t)(kv ? k : k0) * E::kBytes;  // in bounds; masked below
-    uint2 xv[M], av[R];
+  for (int kb = k0; kb < kend; kb += 2 * BLK) {
+    uint2 xv[2][M], av[2][R];
+    bool kv[2];
 #pragma unroll
-    for (int t = 0; t < M; ++t) xv[t] = *reinterpret_cast<const uint2*>(p.x + xo[t] + kk);
+    for (int u = 0; u < 2; ++u) {
+      const int k = kb + u * BLK + lane * HV;
+      kv[u] = k < kend;
+      const size_t kk = (size_t)(kv[u] ? k : k0) * E::kBytes;  // in bounds; masked below
 #pragma unroll
-    for (int j = 0; j < R; ++j) av[j] = *reinterpret_cast<const uint2*>(ar + (size_t)j * p.d_in * E::kBytes + kk);
+      for (int t = 0; t < M; ++t) xv[u][t] = *reinterpret_cast<const uint2*>(p.x + xo[t] + kk);
 #pragma unroll
-    for (int t = 0; t < M; ++t)
-      if (!kv) xv[t] = make_uint2(0, 0);
+      for (int j = 0; j < R; ++j)
+        av[u][j] = *reinterpret_cast<const uint2*>(ar + (size_t)j * p.d_in * E::kBytes + kk);
+    }
 #pragma unroll
-    for (int j = 0; j < R; ++j) {
-      float af[HV];
-      widen8<E>(av[j], af);
+    for (int u = 0; u < 2; ++u) {
 #pragma unroll
-      for (int t = 0; t < M; ++t) {
-        float xf[HV];
-        widen8<E>(xv[t], xf);
+      for (int t = 0; t < M; ++t)
+        if (!kv[u]) xv[u][t] = make_uint2(0, 0);
 #pragma unroll
-        for (int e = 0; e < HV; ++e) acc[j][t] += af[e] * xf[e];
+      for (int j = 0; j < R; ++j) {
+        float af[HV];
+        widen8<E>(av[u][j], af);
+#pragma unroll
+        for (int t = 0; t < M; ++t) {
+          float xf[HV];
+          widen8<E>(xv[u][t], xf);
+#pragma unroll
+          for (int e = 0; e < HV; ++e) acc[j][t] += af[e] * xf[e];
+        }
       }
     }
   }
