@@ -642,10 +642,8 @@ static int multi_impl(const lora_multi_store* store_host, const void* x, int64_t
   if (plan == nullptr) e = form_plan(s, s.n, T, ids, nullptr, 0, seg_off, perm, ws, &plan, strm);
   // The slice records follow the stacked store's workspace.
   SliceMeta* sl_meta = reinterpret_cast<SliceMeta*>(reinterpret_cast<char*>(ws) + workspace_bytes(&s, T));
-  const int64_t max_sub = plan_max_subtiles(T, s.n);
   if (e == hipSuccess) e = launch_shrink_slices(m, sl_meta, plan, T, x, ldx, ws, strm);
-  for (int k = 0; e == hipSuccess && k < m.n_slices; ++k)
-    e = launch_expand_slice(s, m.slice[k], sl_meta + k * max_sub, plan, T, ws, y_host[k], ldy_host[k], strm);
+  if (e == hipSuccess) e = launch_expand_slices(m, sl_meta, plan, T, ws, y_host, ldy_host, strm);
   return e == hipSuccess ? LORA_OK : hip_fail(e);
 }
 

@@ -555,12 +555,9 @@ __attribute__((amdgpu_waves_per_eu(E::kBytes == 2 ? (RUN > 1 ? 3 : 4) : 1))) exp
 }
 
 template <int RUN>
-static hipError_t launch_expand_kernel(int dtype, bool part, bool slice, dim3 grid, dim3 block, hipStream_t stream,
+static hipError_t launch_expand_kernel(int dtype, bool part, dim3 grid, dim3 block, hipStream_t stream,
                                        const ExpandArgs& a) {
-  if (slice) {  // slice mode reads the shrink's partial sums
-    if (dtype == LORA_DTYPE_BF16) hipLaunchKernelGGL((expand_kernel<BF16, true, true, RUN>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((expand_kernel<F32, true, true, RUN>), grid, block, 0, stream, a);
-  } else if (dtype == LORA_DTYPE_BF16) {
+  if (dtype == LORA_DTYPE_BF16) {
     if (part) hipLaunchKernelGGL((expand_kernel<BF16, true, false, RUN>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((expand_kernel<BF16, false, false, RUN>), grid, block, 0, stream, a);
   } else {
@@ -570,11 +567,15 @@ static hipError_t launch_expand_kernel(int dtype, bool part, bool slice, dim3 gr
   return hipGetLastError();
 }
 
-static hipError_t launch_expand_impl(const lora_store& s, const lora_store* slice, const SliceMeta* sl_meta,
-                                     const char* plan, int T, const void* ws, const float* h, int64_t ldh, void* y,
-                                     int64_t ldy, hipStream_t stream) {
+// Whether a call uses the run form: the one-block form would launch many
+// times the waves the GPU holds.
+static bool expand_run_form(int64_t one_block_items) { return one_block_items >= kExpandRunMinItems; }
+
+// The arguments of one expand (slice: the multi-slice apply's slice store,
+// whose B is applied, with its records); `run`: the form the launch uses.
+static ExpandArgs expand_args(const lora_store& s, const lora_store* slice, const SliceMeta* sl_meta, const char* plan,
+                              int T, const void* ws, const float* h, int64_t ldh, void* y, int64_t ldy, bool run) {
   const int64_t max_sub = plan_max_subtiles(T, s.n);
-  if (max_sub == 0) return hipSuccess;
   const WsLayout L = ws_layout(T, s.n, s.d_in, s.r_max, s.dtype);
   const char* base = reinterpret_cast<const char*>(ws);
   const lora_store& out = slice ? *slice : s;  // the store whose B is applied
@@ -595,8 +596,7 @@ static hipError_t launch_expand_impl(const lora_store& s, const lora_store* slic
   a.sl_meta = sl_meta;
   a.sl_r_max = slice ? slice->r_max : 0;
   a.sl_R = slice ? slice->R : 0;
-  const bool part = h == nullptr;
-  if (part) {
+  if (h == nullptr) {
     a.hsrc = reinterpret_cast<const float*>(base + L.part);
     a.ldh = partial_ld(s.r_max);
     a.hstride = (int64_t)T * a.ldh;
@@ -607,28 +607,65 @@ static hipError_t launch_expand_impl(const lora_store& s, const lora_store* slic
   }
   a.fbv = (out.d_out + kVecCols - 1) / kVecCols;
   const int vec_waves = (kVecMaxTokens / kVecTokens) * a.fbv;
-  // Runs of kExpandRun feature blocks per wave when the one-block form would
-  // launch many times the waves the GPU holds; otherwise one block per wave
-  // (more waves in flight).
-  const bool run = max_sub * (int64_t)a.fbn >= kExpandRunMinItems;
   const int run_len = run ? kExpandRun : 1;
   const int runs = (a.fbn + run_len - 1) / run_len;
   a.slots = runs > vec_waves ? runs : vec_waves;
-  const int64_t items = max_sub * a.slots;
-  const dim3 block(kExpandWaves * 64);
-  const dim3 grid((unsigned)((items + kExpandWaves - 1) / kExpandWaves));
-  return run ? launch_expand_kernel<kExpandRun>(s.dtype, part, slice != nullptr, grid, block, stream, a)
-             : launch_expand_kernel<1>(s.dtype, part, slice != nullptr, grid, block, stream, a);
+  return a;
+}
+
+static dim3 expand_grid(const ExpandArgs& a) {
+  const int64_t items = (int64_t)a.max_sub * a.slots;
+  return dim3((unsigned)((items + kExpandWaves - 1) / kExpandWaves));
 }
 
 hipError_t launch_expand(const lora_store& s, const char* plan, int T, const void* ws, const float* h, int64_t ldh,
                          void* y, int64_t ldy, hipStream_t stream) {
-  return launch_expand_impl(s, nullptr, nullptr, plan, T, ws, h, ldh, y, ldy, stream);
+  const int64_t max_sub = plan_max_subtiles(T, s.n);
+  if (max_sub == 0) return hipSuccess;
+  const bool run = expand_run_form(max_sub * (int64_t)((s.d_out + kExpandCols - 1) / kExpandCols));
+  const ExpandArgs a = expand_args(s, nullptr, nullptr, plan, T, ws, h, ldh, y, ldy, run);
+  const dim3 block(kExpandWaves * 64);
+  return run ? launch_expand_kernel<kExpandRun>(s.dtype, h == nullptr, expand_grid(a), block, stream, a)
+             : launch_expand_kernel<1>(s.dtype, h == nullptr, expand_grid(a), block, stream, a);
 }
 
-hipError_t launch_expand_slice(const lora_store& stacked, const lora_store& slice, const SliceMeta* sl_meta,
-                               const char* plan, int T, const void* ws, void* y, int64_t ldy, hipStream_t stream) {
-  return launch_expand_impl(stacked, &slice, sl_meta, plan, T, ws, nullptr, 0, y, ldy, stream);
+// Every slice of a multi-slice apply in one launch: grid dimension y picks
+// the slice (one launch's ramp and tail instead of one per slice).
+struct ExpandSlices {
+  ExpandArgs s[LORA_MAX_SLICES];
+};
+
+template <typename E, int RUN>
+__global__ void __launch_bounds__(kExpandWaves * 64)
+__attribute__((amdgpu_waves_per_eu(E::kBytes == 2 ? (RUN > 1 ? 3 : 4) : 1))) expand_slices_kernel(ExpandSlices a) {
+  expand_wave<E, true, true, RUN>(a.s[blockIdx.y]);
+}
+
+hipError_t launch_expand_slices(const lora_multi_store& m, const SliceMeta* sl_meta, const char* plan, int T,
+                                const void* ws, void* const* y_host, const int64_t* ldy_host, hipStream_t stream) {
+  const lora_store& s = m.stacked;
+  const int64_t max_sub = plan_max_subtiles(T, s.n);
+  if (max_sub == 0) return hipSuccess;
+  // One form for the launch: the one-block items of all slices together.
+  int64_t one_block = 0;
+  for (int k = 0; k < m.n_slices; ++k) one_block += max_sub * (int64_t)((m.slice[k].d_out + kExpandCols - 1) / kExpandCols);
+  const bool run = expand_run_form(one_block);
+  ExpandSlices a;
+  unsigned gx = 0;
+  for (int k = 0; k < m.n_slices; ++k) {
+    a.s[k] = expand_args(s, &m.slice[k], sl_meta + (size_t)k * max_sub, plan, T, ws, nullptr, 0, y_host[k], ldy_host[k],
+                         run);
+    gx = expand_grid(a.s[k]).x > gx ? expand_grid(a.s[k]).x : gx;
+  }
+  const dim3 grid(gx, (unsigned)m.n_slices), block(kExpandWaves * 64);
+  if (s.dtype == LORA_DTYPE_BF16) {
+    if (run) hipLaunchKernelGGL((expand_slices_kernel<BF16, kExpandRun>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((expand_slices_kernel<BF16, 1>), grid, block, 0, stream, a);
+  } else {
+    if (run) hipLaunchKernelGGL((expand_slices_kernel<F32, kExpandRun>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((expand_slices_kernel<F32, 1>), grid, block, 0, stream, a);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace lora
