@@ -13,12 +13,18 @@ namespace lora {
 // order: one 16-wide block of a matrix-core tile.
 constexpr int kSubTile = 16;
 
-// The shrink's workgroup: 8 waves share one work item (a sub-tile and a chunk
+// The shrink's workgroup: W waves share one work item (a sub-tile and a chunk
 // of d_in), each wave taking an equal span of the chunk, and their float32
-// sums meet in LDS.  Two workgroups fit on a CU, so one's reduction overlaps
-// the other's loads.
-constexpr int kShrinkWaves = 8;
-constexpr int kShrinkThreads = kShrinkWaves * 64;
+// sums meet in LDS.  W = 8 (two workgroups per CU, so one's reduction
+// overlaps the other's loads), or 4 in calls of at least
+// kOneChunkMinSubtiles possible sub-tiles (shrink_split).  Measured on the
+// fleet's decode step, whose projections run on concurrent streams: 4 waves
+// took the step from 13.91 to 13.59 ms, while each shrink timed alone on one
+// stream stayed at 29.1 us on average; the smaller workgroups fit beside the
+// other streams' kernels.  In smaller calls (decode spectral, two chunks per
+// sub-tile) 4 waves were slower, 25.6 -> 28.2 us per shrink: each wave's span
+// doubles, and so do its batches of loads.
+constexpr int kShrinkWavesMax = 8;
 
 // The grouping kernel (one workgroup: a stable counting sort of the ids and
 // the sub-tile plan, in LDS) handles T <= kGroupMaxT and n <= kGroupMaxN;
@@ -123,10 +129,10 @@ inline int elem_bytes(int dtype) { return dtype == LORA_DTYPE_BF16 ? 2 : 4; }
 inline int vec_elems(int dtype) { return dtype == LORA_DTYPE_BF16 ? 8 : 4; }  // 16-byte vectors
 
 // The shrink cuts d_in into S <= kMaxChunks chunks, one workgroup item per
-// (sub-tile, chunk).  Each of its 8 waves takes an equal span of the chunk,
-// 8 matrix-core K steps of 64 bytes per row (256 bf16, 128 float32 values)
-// or a multiple for very wide inputs, so that one batch of loads covers it
-// at ranks up to 16 (two or three batches above).  Smaller chunks for
+// (sub-tile, chunk).  A unit is 8 waves x 8 matrix-core K steps of 64
+// bytes per row (256 bf16, 128 float32 values per wave); with 8 waves one
+// batch of loads covers a unit at ranks up to 16 (two or three batches
+// above).  Smaller chunks for
 // higher ranks, to even out the items' bytes, were measured slower (decode
 // spectral and prefill: more partial sums for the expand, no better
 // balance).  A call that can hold kOneChunkMinSubtiles sub-tiles or more
@@ -139,19 +145,22 @@ inline int vec_elems(int dtype) { return dtype == LORA_DTYPE_BF16 ? 8 : 4; }  //
 constexpr int kMaxChunks = 8;
 struct ShrinkSplit {
   int kchunk;  // K elements per chunk
-  int span;    // K elements per wave (kchunk / kShrinkWaves)
+  int waves;   // waves per workgroup (8, or 4 for one chunk per sub-tile)
+  int span;    // K elements per wave (kchunk / waves)
   int S;       // chunks (partial sums per h value)
 };
 constexpr int64_t kOneChunkMinSubtiles = 1024;
 inline ShrinkSplit shrink_split(int d_in, int dtype, int64_t max_sub) {
-  const int unit = kShrinkWaves * 8 * 4 * vec_elems(dtype);  // 2048 bf16, 1024 float32
+  const int unit = kShrinkWavesMax * 8 * 4 * vec_elems(dtype);  // 2048 bf16, 1024 float32
   const int units = (d_in + unit - 1) / unit;
   int mult = (units + kMaxChunks - 1) / kMaxChunks;
-  if (units <= 2 && max_sub >= kOneChunkMinSubtiles) mult = units;
+  const bool large = max_sub >= kOneChunkMinSubtiles;
+  if (units <= 2 && large) mult = units;
   if (mult < 1) mult = 1;
   ShrinkSplit sp;
   sp.kchunk = mult * unit;
-  sp.span = sp.kchunk / kShrinkWaves;
+  sp.waves = large ? 4 : kShrinkWavesMax;
+  sp.span = sp.kchunk / sp.waves;
   sp.S = (d_in + sp.kchunk - 1) / sp.kchunk;
   if (sp.S < 1) sp.S = 1;
   return sp;

@@ -9,11 +9,12 @@
 //
 // Work item = (sub-tile, K chunk of 2048 bf16 / 1024 float32 values, or a
 // multiple for very wide inputs), one workgroup of 8 waves each (two fit on
-// a CU).  No grouping work happens here:
+// a CU), or of 4 waves in calls of one chunk per sub-tile (four fit on a
+// CU).  No grouping work happens here:
 // the plan was formed before, once per grouping.  The workgroup reads its
 // sub-tile's entry, then the adapter's rank and row offset; each wave
-// streams its eighth of the chunk of the x rows and A rows in one batch of
-// loads (two or three for ranks above 16), the waves' float32 sums meet in
+// streams its share of the chunk of the x rows and A rows in batches of
+// loads, the waves' float32 sums meet in
 // LDS in wave order, and chunk kc's partial sums are written; the consumer
 // adds the S partials in chunk order.  No atomics: results are
 // deterministic.
@@ -204,11 +205,11 @@ __device__ __forceinline__ void shrink_tile(const ShrinkArgs& p, int tok_l, int 
   for (int q = 0; q < NG; ++q) red_w[q][lane] = acc[q];
 }
 
-template <typename E, bool kSl>
+template <typename E, bool kSl, int W>
 __device__ __forceinline__ void shrink_body(const ShrinkArgs& p, const SliceSet& ss) {
   constexpr int kVecRank = kVecMaxRank * 2 / E::kBytes;  // 8 bf16, 4 float32
-  __shared__ f32x4_t red[kShrinkWaves][4][64];             // matrix path: [wave][row group][lane]
-  __shared__ float redg[kShrinkWaves][kGemvMaxProducts];   // reduction path: [wave][sum]
+  __shared__ f32x4_t red[W][4][64];             // matrix path: [wave][row group][lane]
+  __shared__ float redg[W][kGemvMaxProducts];   // reduction path: [wave][sum]
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int n_sub = min(*reinterpret_cast<const int32_t*>(p.plan), p.max_sub);
   const int items = n_sub * p.S;
@@ -307,7 +308,7 @@ __device__ __forceinline__ void shrink_body(const ShrinkArgs& p, const SliceSet&
         if (tid < r * m) {
           float s = redg[0][tid];
 #pragma unroll
-          for (int ww = 1; ww < kShrinkWaves; ++ww) s += redg[ww][tid];
+          for (int ww = 1; ww < W; ++ww) s += redg[ww][tid];
           const int t = tid / r, j = tid - t * r;
           part[(int64_t)(pos0 + t) * p.ldp + j] = s;
         }
@@ -315,7 +316,7 @@ __device__ __forceinline__ void shrink_body(const ShrinkArgs& p, const SliceSet&
         const int q = tid >> 6, l = tid & 63;
         f32x4_t s = red[0][q][l];
 #pragma unroll
-        for (int ww = 1; ww < kShrinkWaves; ++ww) s += red[ww][q][l];
+        for (int ww = 1; ww < W; ++ww) s += red[ww][q][l];
         // Lane l of row group q: token l % 16, ranks 16 q + 4 (l / 16) + 0..3.
         const int c = l & 15, j0 = q * 16 + 4 * (l >> 4);
         if (c < m) {
@@ -334,10 +335,10 @@ __device__ __forceinline__ void shrink_body(const ShrinkArgs& p, const SliceSet&
   }  // batches
 }
 
-template <typename E>
-__global__ void __launch_bounds__(kShrinkThreads) __attribute__((amdgpu_waves_per_eu(4)))
+template <typename E, int W>
+__global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4)))
 shrink_kernel(ShrinkArgs p) {
-  shrink_body<E, false>(p, SliceSet{});
+  shrink_body<E, false, W>(p, SliceSet{});
 }
 
 struct ShrinkSliceArgs {
@@ -345,10 +346,25 @@ struct ShrinkSliceArgs {
   SliceSet ss;
 };
 
-template <typename E>
-__global__ void __launch_bounds__(kShrinkThreads) __attribute__((amdgpu_waves_per_eu(4)))
+template <typename E, int W>
+__global__ void __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4)))
 shrink_slices_kernel(ShrinkSliceArgs a) {
-  shrink_body<E, true>(a.p, a.ss);
+  shrink_body<E, true, W>(a.p, a.ss);
+}
+
+// The kernel of one element type and wave count.
+template <int W>
+static void launch_shrink_kernel(const lora_store& s, const lora_multi_store* multi, const ShrinkSliceArgs& b, int grid,
+                                 hipStream_t stream) {
+  const dim3 block(W * 64);
+  if (multi) {
+    if (s.dtype == LORA_DTYPE_BF16) hipLaunchKernelGGL((shrink_slices_kernel<BF16, W>), dim3(grid), block, 0, stream, b);
+    else hipLaunchKernelGGL((shrink_slices_kernel<F32, W>), dim3(grid), block, 0, stream, b);
+  } else if (s.dtype == LORA_DTYPE_BF16) {
+    hipLaunchKernelGGL((shrink_kernel<BF16, W>), dim3(grid), block, 0, stream, b.p);
+  } else {
+    hipLaunchKernelGGL((shrink_kernel<F32, W>), dim3(grid), block, 0, stream, b.p);
+  }
 }
 
 // ------------------------------------------------------------- reduce
@@ -412,9 +428,9 @@ static hipError_t shrink_impl(const lora_store& s, const lora_multi_store* multi
   const int64_t items = max_sub * sp.S;
   const int64_t cap = 1LL << 30;
   const int grid = (int)(items < cap ? items : cap);
+  ShrinkSliceArgs b{};
+  b.p = a;
   if (multi) {
-    ShrinkSliceArgs b;
-    b.p = a;
     b.ss.n_sl = multi->n_slices;
     for (int j = 0; j < LORA_MAX_SLICES; ++j) {
       const bool in = j < multi->n_slices;
@@ -424,15 +440,9 @@ static hipError_t shrink_impl(const lora_store& s, const lora_multi_store* multi
     }
     b.ss.hoff = multi->hoff;
     b.ss.meta = reinterpret_cast<SliceMeta*>(sl_meta);
-    if (s.dtype == LORA_DTYPE_BF16)
-      hipLaunchKernelGGL(shrink_slices_kernel<BF16>, dim3(grid), dim3(kShrinkThreads), 0, stream, b);
-    else
-      hipLaunchKernelGGL(shrink_slices_kernel<F32>, dim3(grid), dim3(kShrinkThreads), 0, stream, b);
-  } else if (s.dtype == LORA_DTYPE_BF16) {
-    hipLaunchKernelGGL(shrink_kernel<BF16>, dim3(grid), dim3(kShrinkThreads), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(shrink_kernel<F32>, dim3(grid), dim3(kShrinkThreads), 0, stream, a);
   }
+  if (sp.waves == 4) launch_shrink_kernel<4>(s, multi, b, grid, stream);
+  else launch_shrink_kernel<kShrinkWavesMax>(s, multi, b, grid, stream);
   return hipGetLastError();
 }
 
