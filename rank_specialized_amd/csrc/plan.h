@@ -35,7 +35,12 @@ constexpr int kGroupWaves = 8;
 
 // The expand's wave covers kExpandCols output features of one sub-tile.
 constexpr int kExpandCols = 128;
-constexpr int kExpandWaves = 4;  // waves per expand workgroup
+// Waves per expand workgroup.  The waves share nothing (no LDS, no
+// barriers), so this only sets the dispatch granularity.  Measured with 4,
+// 2 and 1: the fleet's 5S step took 13.59, 13.08 and 14.28 ms, the expand
+// averaged 45.4, 42.8 and 49.7 us over its 196 modules, and decode
+// spectral's expand took 28.8, 27.7 and 26.8 us.  Two waves are kept.
+constexpr int kExpandWaves = 2;
 // Feature blocks one matrix-path expand wave takes in turn (a run): its
 // sub-tile's tokens and h are read once, and each block's y rows are
 // issued before the previous block is computed.  Measured against 4 and 8
