@@ -590,7 +590,7 @@ static ExpandArgs expand_args(const lora_store& s, const lora_store* slice, cons
   a.n = s.n;
   a.r_max = s.r_max;
   a.R = s.R;
-  a.S_max = shrink_split(s.d_in, s.dtype, max_sub).S;
+  a.S_max = shrink_split(s.d_in, s.dtype, T, s.n).S;
   a.y = reinterpret_cast<char*>(y);
   a.ldy_bytes = ldy * elem_bytes(s.dtype);
   a.sl_meta = sl_meta;

@@ -518,7 +518,7 @@ hipError_t launch_base_fused(const lora_store& s, const void* w, int64_t ldw, co
     const int64_t work = (int64_t)T * (a.ldp / 8);
     hipLaunchKernelGGL(branch_h_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, stream, perm, ids, T, s.n,
                        s.rank, s.scale, reinterpret_cast<const float*>(base + L.part), a.ldp, (int64_t)T * a.ldp,
-                       shrink_split(s.d_in, s.dtype, plan_max_subtiles(T, s.n)).S, hs);
+                       shrink_split(s.d_in, s.dtype, T, s.n).S, hs);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -102,7 +102,7 @@ hipError_t launch_jd_sigma(const lora_store& basis, const char* plan, int T, con
   a.max_sub = (int)max_sub;
   a.k = basis.n;
   a.r = basis.r_max;
-  a.S_max = shrink_split(basis.d_in, basis.dtype, max_sub).S;
+  a.S_max = shrink_split(basis.d_in, basis.dtype, T, basis.n).S;
   a.part = reinterpret_cast<const float*>(base + L.part);
   a.ldp = partial_ld(basis.r_max);
   a.pstride = (int64_t)T * a.ldp;

@@ -16,8 +16,8 @@ constexpr int kSubTile = 16;
 // The shrink's workgroup: W waves share one work item (a sub-tile and a chunk
 // of d_in), each wave taking an equal span of the chunk, and their float32
 // sums meet in LDS.  W = 8 (two workgroups per CU, so one's reduction
-// overlaps the other's loads), or 4 in calls of at least
-// kOneChunkMinSubtiles possible sub-tiles (shrink_split).  Measured on the
+// overlaps the other's loads), or 4 in the calls that shrink_split gives one
+// chunk per sub-tile for their size or their shape.  Measured on the
 // fleet's decode step, whose projections run on concurrent streams: 4 waves
 // took the step from 13.91 to 13.59 ms, while each shrink timed alone on one
 // stream stayed at 29.1 us on average; the smaller workgroups fit beside the
@@ -155,11 +155,17 @@ struct ShrinkSplit {
   int S;       // chunks (partial sums per h value)
 };
 constexpr int64_t kOneChunkMinSubtiles = 1024;
-inline ShrinkSplit shrink_split(int d_in, int dtype, int64_t max_sub) {
+inline ShrinkSplit shrink_split(int d_in, int dtype, int T, int n) {
   const int unit = kShrinkWavesMax * 8 * 4 * vec_elems(dtype);  // 2048 bf16, 1024 float32
   const int units = (d_in + unit - 1) / unit;
   int mult = (units + kMaxChunks - 1) / kMaxChunks;
-  const bool large = max_sub >= kOneChunkMinSubtiles;
+  // Large calls, and calls with at least a full sub-tile per adapter on
+  // average (prefill: its sub-tiles are full, so its items are too): measured
+  // on prefill (T = 8192, 32 adapters), one chunk and 4 waves took the call
+  // from 159.0 to 153.3 us (the expand sums one partial, not two: 110.8 ->
+  // 106.4 us); on decode spectral (T = 2048, 512 adapters, mostly partial
+  // sub-tiles) the same split was slower, 61.9 -> 66.0 us.
+  const bool large = plan_max_subtiles(T, n) >= kOneChunkMinSubtiles || (int64_t)T >= (int64_t)kSubTile * n;
   if (units <= 2 && large) mult = units;
   if (mult < 1) mult = 1;
   ShrinkSplit sp;
@@ -186,7 +192,7 @@ struct WsLayout {
 };
 inline WsLayout ws_layout(int T, int n, int d_in, int r_max, int dtype) {
   WsLayout L;
-  const ShrinkSplit sp = shrink_split(d_in, dtype, plan_max_subtiles(T, n));
+  const ShrinkSplit sp = shrink_split(d_in, dtype, T, n);
   L.meta = 0;
   L.part = align_up(sizeof(TileMeta) * (size_t)plan_max_subtiles(T, n), 256);
   L.plan = L.part + align_up((size_t)sp.S * (size_t)T * (size_t)partial_ld(r_max) * 4, 256);

@@ -396,7 +396,7 @@ static hipError_t shrink_impl(const lora_store& s, const lora_multi_store* multi
                               int T, const void* x, int64_t ldx, void* ws, hipStream_t stream) {
   const int64_t max_sub = plan_max_subtiles(T, s.n);
   if (max_sub == 0) return hipSuccess;
-  const ShrinkSplit sp = shrink_split(s.d_in, s.dtype, max_sub);
+  const ShrinkSplit sp = shrink_split(s.d_in, s.dtype, T, s.n);
   const WsLayout L = ws_layout(T, s.n, s.d_in, s.r_max, s.dtype);
   char* base = reinterpret_cast<char*>(ws);
   ShrinkArgs a;
@@ -465,7 +465,7 @@ hipError_t launch_reduce_partials(const lora_store& s, const char* plan, int T, 
   const int64_t ldp = partial_ld(s.r_max);
   hipLaunchKernelGGL(reduce_partials_kernel, dim3((unsigned)max_sub), dim3(256), 0, stream, plan, (int)max_sub,
                      reinterpret_cast<const TileMeta*>(base + L.meta), reinterpret_cast<const float*>(base + L.part),
-                     ldp, (int64_t)T * ldp, T, s.n, s.r_max, shrink_split(s.d_in, s.dtype, max_sub).S, h, ldh);
+                     ldp, (int64_t)T * ldp, T, s.n, s.r_max, shrink_split(s.d_in, s.dtype, T, s.n).S, h, ldh);
   return hipGetLastError();
 }
 

@@ -273,7 +273,8 @@ def _layout_bytes(T, n, d_in, r_max, e):
     sub-tile of <= 16 tokens; float32 partial sums for the S chunks of d_in
     (a chunk is 8 waves x 8 K steps of 64 bytes, or the smallest multiple of
     that keeping S at most 8; one chunk for up to two units when the call can
-    hold 1024 sub-tiles) at row stride r_max rounded up to 8; the plan (256-byte
+    hold 1024 sub-tiles or has at least 16 tokens per adapter) at row stride
+    r_max rounded up to 8; the plan (256-byte
     header + one 128-byte entry per possible sub-tile); seg_off [n + 2] and
     perm [T]; s h as two bf16 values per rank for the base-fused apply
     ([T][2][ldp]); each part 256-byte aligned."""
@@ -282,7 +283,7 @@ def _layout_bytes(T, n, d_in, r_max, e):
     unit = 8 * 8 * 4 * (16 // e)  # 8 waves x 8 K steps of 64 bytes
     units = -(-d_in // unit)
     mult = max(1, -(-units // 8))
-    if units <= 2 and max_sub >= 1024:  # one chunk when the call has sub-tiles enough to fill the GPU
+    if units <= 2 and (max_sub >= 1024 or T >= 16 * n):  # one chunk: sub-tiles enough, or full ones
         mult = units
     S = max(1, -(-d_in // (mult * unit)))
     ldp = -(-max(r_max, 1) // 8) * 8
@@ -371,7 +372,9 @@ def test_apply_planned_rejects_before_launch(lib):
 @pytest.mark.parametrize("T,n,d_in,r_max,dtype", [(100, 4, 64, 6, 1), (2048, 512, 3584, 64, 1),
                                                   (4096, 1024, 18944, 16, 1), (4096, 1024, 3584, 16, 1),
                                                   (1024, 1024, 4096, 8, 1), (16, 4, 256, 4, 0),
-                                                  (300, 5000, 4096, 8, 1), (0, 3, 64, 4, 1)])
+                                                  (300, 5000, 4096, 8, 1), (0, 3, 64, 4, 1),
+                                                  (8192, 32, 4096, 32, 1), (8192, 512, 4096, 16, 1),
+                                                  (511, 32, 4096, 8, 1), (512, 32, 4096, 8, 1)])
 def test_workspace_bytes(lib, T, n, d_in, r_max, dtype):
     st = _store(n=n, d_in=d_in, r_max=r_max, dtype=dtype)
     assert lib.lora_workspace_bytes(C.byref(st), T) == _layout_bytes(T, n, d_in, r_max, 2 if dtype == 1 else 4)
