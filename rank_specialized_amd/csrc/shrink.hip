@@ -161,11 +161,18 @@ __device__ __forceinline__ void shrink_gemv(const ShrinkArgs& p, int tok_l, int 
 }
 
 // Token counts m with R m <= kGemvMaxProducts take the wavefront-reduction
-// path (their sums and loads stay within the registers of 4 waves per SIMD).
+// path (their sums and loads stay within the registers of 4 waves per SIMD):
+// ranks up to r_cap with up to kGemvMaxTokens tokens, and a single token at
+// any rank up to kGemvMaxProducts, which a 16 x 16 matrix tile would fill
+// with one row of sixteen.
 constexpr int kGemvMaxProducts = 16;
 // Items whose entries and metadata a workgroup fetches together.
 constexpr int kShrinkBatch = 4;
+// (The multi-slice shrink keeps single tokens at r_cap: its slice records
+// leave no registers for the wider instances.)
+template <bool kWideSingle>
 __device__ __forceinline__ bool gemv_fits(int r, int m, int r_cap) {
+  if (kWideSingle && m == 1) return r <= kGemvMaxProducts;
   return r <= r_cap && m <= kGemvMaxTokens && r * m <= kGemvMaxProducts;
 }
 
@@ -277,16 +284,18 @@ __device__ __forceinline__ void shrink_body(const ShrinkArgs& p, const SliceSet&
       if (r == 0) continue;  // the same in every wave: no barrier is skipped by some only
       const int k0 = kc * p.kchunk + w * p.span;
       const int kw = max(0, min(p.span, p.d_in - k0));
-      const bool gemv = gemv_fits(r, m, kVecRank);
+      const bool gemv = gemv_fits<!kSl>(r, m, kVecRank);
       if (gemv) {
         switch (r) {
 #define LORA_GEMV_CASE(RR) \
     case RR: shrink_gemv_m<E, RR>(p, tok_l, 16 * k, m, ro, k0, kw, redg[w]); break;
           LORA_GEMV_CASE(1) LORA_GEMV_CASE(2) LORA_GEMV_CASE(3) LORA_GEMV_CASE(4)
+          LORA_GEMV_CASE(5) LORA_GEMV_CASE(6) LORA_GEMV_CASE(7) LORA_GEMV_CASE(8)
           default:
-            if constexpr (kVecRank > 4) {
+            if constexpr (!kSl) {
               switch (r) {
-                LORA_GEMV_CASE(5) LORA_GEMV_CASE(6) LORA_GEMV_CASE(7) LORA_GEMV_CASE(8)
+                LORA_GEMV_CASE(9) LORA_GEMV_CASE(10) LORA_GEMV_CASE(11) LORA_GEMV_CASE(12)
+                LORA_GEMV_CASE(13) LORA_GEMV_CASE(14) LORA_GEMV_CASE(15) LORA_GEMV_CASE(16)
                 default: break;
               }
             }
