@@ -41,6 +41,29 @@ struct GroupArgs {
   int32_t* n_invalid;  // optional
 };
 
+// Inclusive prefix sum over the 64 lanes of a wave by DPP: shifts by 1, 2, 4
+// and 8 lanes within each row of 16, then row 0's total added into row 1
+// and row 2's into row 3 (row_bcast:15), then the first two rows' total
+// into rows 2 and 3 (row_bcast:31).  Lanes with no source read 0.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  int v = (int)x;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
+  return (uint32_t)v;
+}
+
+// The grouping scans, per group, its tokens and sub-tiles as one 32-bit
+// value, tokens << kSubBits | sub-tiles: with T <= kGroupMaxT and n <=
+// kGroupMaxN neither field of any prefix overflows.
+constexpr int kSubBits = 12;
+static_assert(((int64_t)kGroupMaxT + (int64_t)(kSubTile - 1) * kGroupMaxN) / kSubTile < (1 << kSubBits),
+              "sub-tile counts fit their field");
+static_assert(((int64_t)kGroupMaxT << kSubBits) < (1ll << 32), "token counts fit their field");
+
 // W waves: 16 where the per-wave histograms fit the LDS with the rest, else
 // kGroupWaves (8).
 template <int W>
@@ -61,7 +84,7 @@ __global__ void __launch_bounds__(W * 64) group_kernel(GroupArgs p) {
   int32_t* sub0 = hist + W * n1;       // [n1]: first sub-tile of each group
   int32_t* soff = sub0 + n1;           // [n1 + 1]: seg_off
   int32_t* permL = soff + n1 + 1;      // [T]
-  __shared__ uint64_t s_wsum[W];
+  __shared__ uint32_t s_wsum[W];
   __shared__ int s_inval;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   for (int i = tid; i < W * n1; i += kGroupThreads) hist[i] = 0;
@@ -116,28 +139,37 @@ __global__ void __launch_bounds__(W * 64) group_kernel(GroupArgs p) {
   __syncthreads();
 
   // 2. seg_off, first sub-tiles, and each wave's base position per group.
-  const int a0 = tid * kGroupPerThread;
-  uint64_t mine = 0;
+  //    Thread i takes the gpt consecutive groups from i gpt (gpt as small as
+  //    the groups allow, so that few threads loop); one 32-bit scan of
+  //    (tokens, sub-tiles) over the threads: a DPP scan per wave, the wave
+  //    totals through LDS, one barrier.
+  const int gpt = (n1 + kGroupThreads - 1) / kGroupThreads;  // 1 .. kGroupPerThread
+  const int a0 = tid * gpt;
+  uint32_t mine = 0;
 #pragma unroll
   for (int i = 0; i < kGroupPerThread; ++i) {
     const int a = a0 + i;
-    if (a < n1) {
+    if (i < gpt && a < n1) {
       int c = 0;
 #pragma unroll
       for (int ww = 0; ww < W; ++ww) c += hist[ww * n1 + a];
       const int st = a < n ? (c + kSubTile - 1) / kSubTile : 0;
-      mine += ((uint64_t)c << 32) | (uint64_t)st;
+      mine += ((uint32_t)c << kSubBits) | (uint32_t)st;
     }
   }
-  uint64_t tot;
-  uint64_t pre = block_exclusive_scan<W>(mine, s_wsum, &tot);
+  const uint32_t incl = wave_inclusive_scan(mine);
+  if (lane == 63) s_wsum[w] = incl;
+  __syncthreads();
+  uint32_t pre = incl - mine;
+#pragma unroll
+  for (int ww = 0; ww < W; ++ww) pre += ww < w ? (uint32_t)s_wsum[ww] : 0u;
 #pragma unroll
   for (int i = 0; i < kGroupPerThread; ++i) {
     const int a = a0 + i;
-    if (a < n1) {
-      int pos = (int)(pre >> 32);
+    if (i < gpt && a < n1) {
+      int pos = (int)(pre >> kSubBits);
       soff[a] = pos;
-      sub0[a] = (int)(pre & 0xffffffffu);
+      sub0[a] = (int)(pre & ((1u << kSubBits) - 1));
       int c = 0;
 #pragma unroll
       for (int ww = 0; ww < W; ++ww) {
@@ -146,7 +178,7 @@ __global__ void __launch_bounds__(W * 64) group_kernel(GroupArgs p) {
         c += cw;
       }
       const int st = a < n ? (c + kSubTile - 1) / kSubTile : 0;
-      pre += ((uint64_t)c << 32) | (uint64_t)st;
+      pre += ((uint32_t)c << kSubBits) | (uint32_t)st;
     }
   }
   if (tid == 0) soff[n1] = T;
@@ -160,8 +192,10 @@ __global__ void __launch_bounds__(W * 64) group_kernel(GroupArgs p) {
       const int g = gv[b];
       if (g >= 0) {
         const int pos = hist[w * n1 + g] + (rk[b] & 0xff);
-        permL[pos] = t;
-        if (p.perm) p.perm[pos] = t;
+        if ((unsigned)pos < (unsigned)T) {  // always, for a histogram of these tokens
+          permL[pos] = t;
+          if (p.perm) p.perm[pos] = t;
+        }
       }
       // every lane has read its base before the leaders move it
       if (g >= 0 && (rk[b] >> 16)) hist[w * n1 + g] += (rk[b] >> 8) & 0xff;
