@@ -137,11 +137,24 @@ def _segment_case(name):
         return rng.integers(-1, 1, size=129).astype(np.int32), 1
     if name == "sorted_desc":
         return np.sort(rng.integers(0, 50, size=2000))[::-1].astype(np.int32).copy(), 50
+    # The one-workgroup grouping at its limits (T = 8192, n = 2048):
+    if name == "max_subtiles":
+        # 384 adapters of 17 tokens and 1664 of one: 8192 tokens in 2432
+        # sub-tiles, the most any grouping of that size has.
+        ids = np.concatenate([np.repeat(np.arange(384), 17), np.arange(384, 2048)]).astype(np.int32)
+        return rng.permutation(ids).astype(np.int32), 2048
+    if name == "one_adapter_max_T":
+        ids = np.full(8192, 2047, np.int32)
+        ids[rng.random(8192) < 0.01] = -1
+        return ids, 2048
+    if name == "no_adapter_max_T":
+        return np.full(8192, -1, np.int32), 2048
     raise KeyError(name)
 
 
 SEGMENT_CASES = ["1", "2", "3", "4", "5", "all_same", "all_invalid", "out_of_range", "distinct",
-                 "max_T", "many_adapters", "one_token", "n1", "sorted_desc"]
+                 "max_T", "many_adapters", "one_token", "n1", "sorted_desc", "max_subtiles",
+                 "one_adapter_max_T", "no_adapter_max_T"]
 
 
 @pytest.mark.parametrize("name", SEGMENT_CASES)
@@ -177,7 +190,8 @@ def test_segment_repeatable():
 
 
 PLAN_CASES = ["1", "2", "3", "4", "5", "all_same", "all_invalid", "out_of_range", "distinct", "max_T",
-              "many_adapters", "one_token", "n1", "sorted_desc"]
+              "many_adapters", "one_token", "n1", "sorted_desc", "max_subtiles", "one_adapter_max_T",
+              "no_adapter_max_T"]
 
 
 def _plan_store(n, dev, seed):
