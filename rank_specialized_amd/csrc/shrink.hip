@@ -168,6 +168,8 @@ __device__ __forceinline__ void shrink_gemv(const ShrinkArgs& p, int tok_l, int 
 constexpr int kGemvMaxProducts = 16;
 // Items whose entries and metadata a workgroup fetches together.
 constexpr int kShrinkBatch = 4;
+constexpr int kXcds = 8;    // XCDs of the MI355X, which receive workgroups in turn
+constexpr int kXcdRun = 8;  // consecutive items of the plan dealt to one XCD
 // (The multi-slice shrink keeps single tokens at r_cap: its slice records
 // leave no registers for the wider instances.)
 template <bool kWideSingle>
@@ -226,7 +228,20 @@ __device__ __forceinline__ void shrink_body(const ShrinkArgs& p, const SliceSet&
   // Lanes 16 k .. 16 k + 15 of every wave fetch item k's entry, its 16
   // tokens and its adapter's metadata together (two round trips for the
   // batch), so that the items then run back to back on their data loads.
-  for (int b0 = blockIdx.x; b0 < items; b0 += kShrinkBatch * G) {  // uniform over the workgroup
+  // Workgroups are dealt to the 8 XCDs in turn (workgroup b to XCD b mod 8).
+  // When the grid holds every item, the items go to the XCDs in runs of
+  // kXcdRun consecutive items of the plan (run k to XCD k mod 8): an
+  // adapter's neighbouring sub-tiles then share one L2, so its A rows are
+  // fetched into one or two XCDs instead of each, while the runs of a
+  // heavy adapter still spread over the XCDs.
+  constexpr int kSpan = kXcds * kXcdRun;
+  const bool remap = G % kSpan == 0 && G >= items;
+  int first = (int)blockIdx.x;
+  if (remap) {
+    const int x = (int)(blockIdx.x % kXcds), j = (int)(blockIdx.x / kXcds);  // the XCD's j-th workgroup
+    first = ((j / kXcdRun) * kXcds + x) * kXcdRun + j % kXcdRun;
+  }
+  for (int b0 = first; b0 < items; b0 += kShrinkBatch * G) {  // uniform over the workgroup
     const int kl = lane >> 4;
     const int itl = b0 + kl * G;
     const bool vl = kl < kShrinkBatch && itl < items;
@@ -436,7 +451,10 @@ static hipError_t shrink_impl(const lora_store& s, const lora_multi_store* multi
   // count exit at once; past 2^31 items the workgroups loop.
   const int64_t items = max_sub * sp.S;
   const int64_t cap = 1LL << 30;
-  const int grid = (int)(items < cap ? items : cap);
+  // A multiple of 8 XCDs x kXcdRun items, so that the kernel can deal the
+  // items to the XCDs in runs.
+  constexpr int kSpan = kXcds * kXcdRun;
+  const int grid = (int)(((items < cap ? items : cap) + kSpan - 1) / kSpan * kSpan);
   ShrinkSliceArgs b{};
   b.p = a;
   if (multi) {
